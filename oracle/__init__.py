@@ -1,0 +1,40 @@
+"""fp64 CPU oracle for the DFlash/DSpark draft MLA attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute anything in this package: only the test suite, the smoke check of the
+entry module and the CPU-baseline leg of the bench use it.  It shares no code
+with the HIP library or its Python binding, and it never consumes a value the
+HIP path produced except as the thing being checked.
+
+What it computes, and the passages it follows:
+
+* ``attention.mla_attention`` -- the plain definition of the draft attention:
+  queries from the noise block, keys/values over [context | noise], key =
+  [k_nope (per head) | k_rope (head-shared, NoPE)], scale q_head_dim ** -0.5,
+  the dense additive mask added unchanged to the scores, softmax over keys,
+  weighted sum of v.  NeMo AutoModel pages: "dflash.draft_kimi_k3" --
+  KimiK3DFlashAttention (class text and forward: one K/V per query head, no GQA
+  repeat; the mask is passed through unchanged) and the module text on NoPE
+  (the rope slice is a plain head-shared extension of the key); "dspark.draft_kimi_k3"
+  -- KimiK3DSparkAttention attributes (q_head_dim, scaling) and forward
+  (context concatenated before the noise block).
+* ``expand.latent_expand`` -- kv_b_proj as a plain Linear: per head a slice of
+  qk_nope_head_dim + v_head_dim outputs.  Same class texts; latent width from the
+  Kimi K3 model page (MLA context-parallel forward: kv_lora_rank + qk_rope_head_dim
+  values per token).
+* ``occupancy.tile_classes`` / ``occupancy.tile_lists`` -- the integer tile
+  classification of an additive mask (all -inf / all zero / anything else)
+  that the method uses to skip fully masked tiles.  The pages only require
+  that the score matrix is never materialised (KimiK3DFlashAttention.forward);
+  the classification is defined here by its plain meaning.
+
+Readings where the pages are silent (also listed in the design notes):
+a row whose every score is -inf returns 0; a mask entry is "masked" only if it
+is exactly -inf, any finite value (including large negatives) is added as is.
+
+Pinned by tests/test_oracle_pins.py (closed forms, invariants, brute force,
+a library routine) -- nothing here is "parity unpinned".
+"""
+from .attention import mla_attention, softmax_weights  # noqa: F401
+from .expand import latent_expand  # noqa: F401
+from .occupancy import tile_classes, tile_lists  # noqa: F401

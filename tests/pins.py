@@ -1,0 +1,314 @@
+"""Checks that pin the fp64 oracle to things other than itself.
+
+Each check calls the oracle through the `oracle` package attributes, so a test
+can plant a mistake inside the oracle (monkeypatching one of its internals)
+and confirm that at least one check catches it.  None of these re-types the
+oracle's formula: they use closed forms derived by hand, invariants of the
+definition, a pure-Python brute force on tiny shapes, an explicit gather of
+the keys a DFlash block may see, and PyTorch's own fused attention routine.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle
+from oracle import attention as oatt
+from oracle import expand as oexp
+from oracle import occupancy as oocc
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+NINF = -np.inf
+
+
+def _rand(seed, B, H, Lq, Lk, dn=8, dr=4, dv=6):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, Lq, dn + dr))
+    kn = rng.standard_normal((B, H, Lk, dn))
+    kr = rng.standard_normal((B, Lk, dr))
+    v = rng.standard_normal((B, H, Lk, dv))
+    return q, kn, kr, v
+
+
+def _rand_mask(seed, B, Lq, Lk, p_masked=0.5, finite_noise=True, keep_one=True):
+    """Random additive mask with -inf entries; every row keeps >= 1 finite entry."""
+    rng = np.random.default_rng(seed + 1000)
+    m = rng.standard_normal((B, 1, Lq, Lk)) if finite_noise else np.zeros((B, 1, Lq, Lk))
+    hide = rng.random((B, 1, Lq, Lk)) < p_masked
+    if keep_one:
+        keep = rng.integers(0, Lk, size=(B, 1, Lq))
+        for b in range(B):
+            for i in range(Lq):
+                hide[b, 0, i, keep[b, 0, i]] = False
+    m[hide] = NINF
+    return m
+
+
+# ---------------------------------------------------------------- attention
+
+def pin_closed_form_golden():
+    """Hand-derived cases in tests/golden/closed_form_attention.json."""
+    with open(os.path.join(GOLDEN, "closed_form_attention.json")) as f:
+        data = json.load(f)
+    scale = 3.0 ** -0.5
+    conv = {"-inf": NINF, "ln2": math.log(2.0)}
+    for case in data["cases"]:
+        q = np.array(case["q"], dtype=np.float64)[None, None]          # [1,1,Lq,3]
+        a = np.log(np.array(case["k_nope_a"], dtype=np.float64) + 1.0) / (2.0 * scale)
+        kn = np.stack([a, np.zeros_like(a)], axis=1)[None, None]        # [1,1,3,2]
+        kr = a[:, None][None]                                           # [1,3,1]
+        v = np.array(case["v"], dtype=np.float64)[None, None]
+        mask = None
+        if case["mask"] is not None:
+            mask = np.array([[conv.get(x, x) if isinstance(x, str) else x for x in row]
+                             for row in case["mask"]], dtype=np.float64)[None, None]
+        out = oracle.mla_attention(q, kn, kr, v, mask, scale)[0, 0]
+        np.testing.assert_allclose(out, np.array(case["out"]), rtol=0, atol=1e-12,
+                                   err_msg=case["name"])
+
+
+def pin_rows_sum_to_one():
+    """Softmax weights: each row with a finite score sums to 1; -inf entries weigh 0."""
+    q, kn, kr, v = _rand(1, 2, 3, 7, 11)
+    mask = _rand_mask(1, 2, 7, 11)
+    for b in range(2):
+        for h in range(3):
+            p = oracle.softmax_weights(q, kn, kr, mask, 0.3, b, h)
+            np.testing.assert_allclose(p.sum(-1), 1.0, atol=1e-12)
+            assert np.all(p[mask[b, 0] == NINF] == 0.0)
+            assert np.all(p >= 0.0)
+
+
+def pin_zero_mask_equals_no_mask():
+    q, kn, kr, v = _rand(2, 1, 2, 5, 9)
+    a = oracle.mla_attention(q, kn, kr, v, np.zeros((1, 1, 5, 9)), 0.25)
+    b = oracle.mla_attention(q, kn, kr, v, None, 0.25)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+
+
+def pin_single_visible_key_returns_its_value():
+    q, kn, kr, v = _rand(3, 2, 2, 6, 10)
+    mask = np.full((2, 1, 6, 10), NINF)
+    rng = np.random.default_rng(3)
+    js = rng.integers(0, 10, size=(2, 6))
+    for b in range(2):
+        for i in range(6):
+            mask[b, 0, i, js[b, i]] = rng.standard_normal() * 5.0
+    out = oracle.mla_attention(q, kn, kr, v, mask, 0.7)
+    for b in range(2):
+        for h in range(2):
+            for i in range(6):
+                np.testing.assert_array_equal(out[b, h, i], v[b, h, js[b, i]])
+
+
+def pin_key_permutation_invariance():
+    q, kn, kr, v = _rand(4, 1, 3, 8, 13)
+    mask = _rand_mask(4, 1, 8, 13)
+    perm = np.random.default_rng(4).permutation(13)
+    a = oracle.mla_attention(q, kn, kr, v, mask, 0.4)
+    b = oracle.mla_attention(q, kn[:, :, perm], kr[:, perm], v[:, :, perm], mask[..., perm], 0.4)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
+def pin_row_shift_invariance():
+    """Adding c to every finite mask entry of a row leaves that row unchanged."""
+    q, kn, kr, v = _rand(5, 1, 2, 6, 9)
+    mask = _rand_mask(5, 1, 6, 9)
+    shifted = mask.copy()
+    c = np.array([3.0, -7.5, 0.25, 40.0, -1.0, 12.0])
+    shifted[0, 0] += c[:, None]          # -inf + c stays -inf
+    a = oracle.mla_attention(q, kn, kr, v, mask, 0.5)
+    b = oracle.mla_attention(q, kn, kr, v, shifted, 0.5)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
+def pin_zero_query_gives_mean_of_visible_values():
+    _, kn, kr, v = _rand(6, 2, 2, 5, 12)
+    q = np.zeros((2, 2, 5, 12))
+    vis = np.random.default_rng(6).random((2, 5, 12)) < 0.6
+    vis[:, :, 0] = True
+    mask = np.where(vis, 0.0, NINF)[:, None]
+    out = oracle.mla_attention(q, kn, kr, v, mask, 0.9)
+    for b in range(2):
+        for h in range(2):
+            for i in range(5):
+                np.testing.assert_allclose(out[b, h, i], v[b, h, vis[b, i]].mean(0), atol=1e-12)
+
+
+def pin_value_shift_adds_constant():
+    q, kn, kr, v = _rand(7, 1, 2, 4, 7)
+    mask = _rand_mask(7, 1, 4, 7)
+    c = 2.5
+    a = oracle.mla_attention(q, kn, kr, v, mask, 0.35)
+    b = oracle.mla_attention(q, kn, kr, v + c, mask, 0.35)
+    np.testing.assert_allclose(b, a + c, atol=1e-12)
+
+
+def pin_matches_torch_sdpa():
+    """PyTorch's scaled_dot_product_attention (fp64, CPU) on explicit keys
+    [k_nope | k_rope broadcast to every head] with the same float mask."""
+    import torch
+    import torch.nn.functional as F
+    q, kn, kr, v = _rand(8, 2, 3, 9, 14, dn=16, dr=8, dv=12)
+    mask = _rand_mask(8, 2, 9, 14)
+    scale = 24 ** -0.5
+    k = np.concatenate([kn, np.broadcast_to(kr[:, None], (2, 3, 14, 8))], axis=-1)
+    ref = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(np.ascontiguousarray(k)),
+                                         torch.from_numpy(v), attn_mask=torch.from_numpy(mask),
+                                         scale=scale).numpy()
+    out = oracle.mla_attention(q, kn, kr, v, mask, scale)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def pin_dflash_block_gather():
+    """With the DFlash block mask, block j's rows equal plain softmax attention
+    over the explicitly gathered keys context[0..anchor_j] + block j's own keys."""
+    from scipy.special import softmax
+    from dflash_block_draft_amd import workloads as W
+    rng = np.random.default_rng(9)
+    ctx, A, bs, H = 40, 3, 4, 2
+    anchors = W.draw_anchors(rng, 1, A, ctx)
+    vis = W.visibility(anchors, ctx, ctx, bs)
+    mask = np.where(vis, 0.0, NINF)[:, None]
+    Lq, Lk = A * bs, ctx + A * bs
+    q, kn, kr, v = _rand(9, 1, H, Lq, Lk)
+    scale = 12 ** -0.5
+    out = oracle.mla_attention(q, kn, kr, v, mask, scale)
+    for h in range(H):
+        for j in range(A):
+            keys = np.concatenate([np.arange(anchors[0, j] + 1), ctx + j * bs + np.arange(bs)])
+            kfull = np.concatenate([kn[0, h][keys], kr[0][keys]], axis=1)
+            for i in range(j * bs, (j + 1) * bs):
+                w = softmax(scale * (kfull @ q[0, h, i]))
+                np.testing.assert_allclose(out[0, h, i], w @ v[0, h][keys], atol=1e-12)
+
+
+def pin_brute_force_tiny():
+    """Pure-Python loops (math.exp, explicit sums) on tiny shapes."""
+    q, kn, kr, v = _rand(10, 2, 2, 3, 5, dn=3, dr=2, dv=2)
+    mask = _rand_mask(10, 2, 3, 5)
+    mask[1, 0, 2, :] = NINF                               # one dead row
+    scale = 0.6
+    out = oracle.mla_attention(q, kn, kr, v, mask, scale)
+    for b in range(2):
+        for h in range(2):
+            for i in range(3):
+                s = []
+                for j in range(5):
+                    acc = 0.0
+                    for d in range(3):
+                        acc += q[b, h, i, d] * kn[b, h, j, d]
+                    for d in range(2):
+                        acc += q[b, h, i, 3 + d] * kr[b, j, d]
+                    s.append(acc * scale + mask[b, 0, i, j])
+                fin = [x for x in s if x != -math.inf]
+                if not fin:
+                    exp_out = [0.0, 0.0]
+                else:
+                    mx = max(fin)
+                    e = [math.exp(x - mx) if x != -math.inf else 0.0 for x in s]
+                    z = sum(e)
+                    exp_out = [sum(e[j] * v[b, h, j, c] for j in range(5)) / z for c in range(2)]
+                np.testing.assert_allclose(out[b, h, i], exp_out, atol=1e-12)
+
+
+def pin_query_rows_subset():
+    """Restricting to a subset of query rows returns exactly those rows."""
+    q, kn, kr, v = _rand(11, 1, 2, 10, 8)
+    mask = _rand_mask(11, 1, 10, 8)
+    full = oracle.mla_attention(q, kn, kr, v, mask, 0.3)
+    rows = np.array([7, 0, 3])
+    sub = oracle.mla_attention(q, kn, kr, v, mask, 0.3, q_rows=rows)
+    np.testing.assert_array_equal(sub, full[:, :, rows])
+
+
+ATTENTION_PINS = [
+    pin_closed_form_golden, pin_rows_sum_to_one, pin_zero_mask_equals_no_mask,
+    pin_single_visible_key_returns_its_value, pin_key_permutation_invariance,
+    pin_row_shift_invariance, pin_zero_query_gives_mean_of_visible_values,
+    pin_value_shift_adds_constant, pin_matches_torch_sdpa, pin_dflash_block_gather,
+    pin_brute_force_tiny, pin_query_rows_subset,
+]
+
+
+# ---------------------------------------------------------------- expand
+
+def pin_expand_brute_force():
+    rng = np.random.default_rng(20)
+    B, Lk, R, H, Dn, Dv = 2, 3, 5, 2, 3, 2
+    lat = rng.standard_normal((B, Lk, R))
+    w = rng.standard_normal((H * (Dn + Dv), R))
+    kn, v = oracle.latent_expand(lat, w, H, Dn, Dv)
+    for b in range(B):
+        for t in range(Lk):
+            for h in range(H):
+                for e in range(Dn + Dv):
+                    acc = 0.0
+                    for r in range(R):
+                        acc += lat[b, t, r] * w[h * (Dn + Dv) + e, r]
+                    got = kn[b, h, t, e] if e < Dn else v[b, h, t, e - Dn]
+                    assert abs(got - acc) < 1e-12
+
+
+def pin_expand_one_hot_layout():
+    """A one-hot weight row copies one latent column to a known (head, slot)."""
+    B, Lk, R, H, Dn, Dv = 1, 4, 6, 3, 2, 2
+    lat = np.arange(B * Lk * R, dtype=np.float64).reshape(B, Lk, R) + 1.0
+    w = np.zeros((H * (Dn + Dv), R))
+    w[1 * (Dn + Dv) + 0, 4] = 1.0       # head 1, k_nope[0] <- latent[:, :, 4]
+    w[2 * (Dn + Dv) + Dn + 1, 2] = 1.0  # head 2, v[1]      <- latent[:, :, 2]
+    kn, v = oracle.latent_expand(lat, w, H, Dn, Dv)
+    np.testing.assert_array_equal(kn[0, 1, :, 0], lat[0, :, 4])
+    np.testing.assert_array_equal(v[0, 2, :, 1], lat[0, :, 2])
+    assert np.count_nonzero(kn) == Lk and np.count_nonzero(v) == Lk
+
+
+EXPAND_PINS = [pin_expand_brute_force, pin_expand_one_hot_layout]
+
+
+# ---------------------------------------------------------------- occupancy
+
+def pin_occupancy_brute_force():
+    rng = np.random.default_rng(30)
+    B, Lq, Lk, BM, BN = 2, 11, 23, 4, 5
+    m = np.zeros((B, 1, Lq, Lk))
+    m[rng.random(m.shape) < 0.7] = NINF
+    m[0, 0, 0:4, 0:5] = NINF                       # one tile all -inf
+    m[0, 0, 4:8, 5:10] = 0.0                       # one tile all zero
+    m[0, 0, 4:8, 10:15] = -0.0                     # negative zeros count as zero
+    m[1, 0, 8:11, 20:23] = NINF                    # a ragged corner tile, all -inf
+    m[1, 0, 4:8, 0:5] = NINF
+    m[1, 0, 5, 2] = np.nan                         # NaN alone in an otherwise -inf tile
+    m[1, 0, 0:4, 10:15] = 0.0
+    m[1, 0, 2, 11] = np.inf                        # +inf alone in an otherwise zero tile
+    m[1, 0, 1, 6] = -3.0e38                        # large finite negatives are values
+    cls = oracle.tile_classes(m, BM, BN)
+    assert cls.shape == (B, 3, 5)
+    for b in range(B):
+        for qt in range(3):
+            for kt in range(5):
+                vals = [m[b, 0, i, j] for i in range(qt * BM, min(qt * BM + BM, Lq))
+                        for j in range(kt * BN, min(kt * BN + BN, Lk))]
+                if all(x == -math.inf for x in vals):
+                    want = 0
+                elif all(x == 0.0 for x in vals):
+                    want = 1
+                else:
+                    want = 2
+                assert cls[b, qt, kt] == want, (b, qt, kt)
+    assert cls[0, 0, 0] == 0 and cls[0, 1, 1] == 1 and cls[0, 1, 2] == 1 and cls[1, 2, 4] == 0
+    assert cls[1, 1, 0] == 2 and cls[1, 0, 2] == 2
+    lists = oracle.tile_lists(cls)
+    for b in range(B):
+        for qt in range(3):
+            idx, c = lists[b][qt]
+            assert list(idx) == [kt for kt in range(5) if cls[b, qt, kt] != 0]
+            assert all(c == cls[b, qt, idx])
+
+
+OCCUPANCY_PINS = [pin_occupancy_brute_force]
+
+ALL_PINS = ATTENTION_PINS + EXPAND_PINS + OCCUPANCY_PINS

@@ -1,0 +1,145 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check a pin catches each.
+
+This is what makes the pins meaningful: a dropped term, a wrong sign, a wrong
+index or a transposed operand anywhere in the oracle must fail at least one.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import pins
+from oracle import attention as oatt
+from oracle import expand as oexp
+from oracle import occupancy as oocc
+from oracle._arrays import f64
+
+
+def _scores_no_rope(qb, kn, kr, mrow, scale, dn):
+    s = scale * (qb[:, :dn] @ kn.T)
+    return s if mrow is None else s + mrow
+
+
+def _scores_rope_sign(qb, kn, kr, mrow, scale, dn):
+    s = scale * (qb[:, :dn] @ kn.T - qb[:, dn:] @ kr.T)
+    return s if mrow is None else s + mrow
+
+
+def _scores_scale_after_mask(qb, kn, kr, mrow, scale, dn):
+    s = qb[:, :dn] @ kn.T + qb[:, dn:] @ kr.T
+    return scale * (s if mrow is None else s + mrow)
+
+
+def _scores_mask_ignored(qb, kn, kr, mrow, scale, dn):
+    return scale * (qb[:, :dn] @ kn.T + qb[:, dn:] @ kr.T)
+
+
+def _scores_rope_into_nope_slot(qb, kn, kr, mrow, scale, dn):
+    # pairs q_rope with the first Dr dims of k_nope instead of k_rope
+    dr = kr.shape[1]
+    s = scale * (qb[:, :dn] @ kn.T + qb[:, dn:] @ kn[:, :dr].T)
+    return s if mrow is None else s + mrow
+
+
+def _softmax_wrong_axis(s):
+    e = np.exp(s - np.max(np.where(np.isfinite(s), s, -1e300), axis=0, keepdims=True))
+    z = e.sum(axis=0, keepdims=True)
+    return np.where(z > 0, e / np.where(z > 0, z, 1.0), 0.0)
+
+
+def _softmax_uniform_dead_rows(s):
+    m = s.max(axis=-1, keepdims=True)
+    dead = m == -np.inf
+    e = np.where(dead, 1.0, np.exp(s - np.where(dead, 0.0, m)))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def _softmax_no_normalise(s):
+    m = s.max(axis=-1, keepdims=True)
+    dead = m == -np.inf
+    return np.where(dead, 0.0, np.exp(s - np.where(dead, 0.0, m)))
+
+
+def _attn_wrong_v_head(q, k_nope, k_rope, v, mask, scale, q_rows=None):
+    H = v.shape[1]
+    v2 = np.concatenate([f64(v)[:, 1:], f64(v)[:, :1]], axis=1) if H > 1 else f64(v)[..., ::-1]
+    return _orig_attn(q, k_nope, k_rope, v2, mask, scale, q_rows)
+
+
+def _attn_mask_transposed_rows(q, k_nope, k_rope, v, mask, scale, q_rows=None):
+    if mask is not None:
+        mask = f64(mask)[:, :, ::-1, :]
+    return _orig_attn(q, k_nope, k_rope, v, mask, scale, q_rows)
+
+
+def _expand_swapped_slices(latent, w, H, Dn, Dv):
+    lat, ww = f64(latent), f64(w)
+    B, Lk, R = lat.shape
+    kv = (lat @ ww.T).reshape(B, Lk, H, Dn + Dv)
+    return (np.ascontiguousarray(kv[..., Dv:].transpose(0, 2, 1, 3)),
+            np.ascontiguousarray(kv[..., :Dv].transpose(0, 2, 1, 3)))
+
+
+def _expand_slice_major(latent, w, H, Dn, Dv):
+    lat, ww = f64(latent), f64(w)
+    B, Lk, R = lat.shape
+    kv = (lat @ ww.T).reshape(B, Lk, Dn + Dv, H).transpose(0, 1, 3, 2)
+    return (np.ascontiguousarray(kv[..., :Dn].transpose(0, 2, 1, 3)),
+            np.ascontiguousarray(kv[..., Dn:].transpose(0, 2, 1, 3)))
+
+
+def _classes_positive_zero_only(mask, BM, BN):
+    m = f64(mask)
+    out = _orig_classes(m, BM, BN)
+    B, _, Lq, Lk = m.shape
+    for b in range(B):
+        for qt in range(out.shape[1]):
+            for kt in range(out.shape[2]):
+                t = m[b, 0, qt * BM:(qt + 1) * BM, kt * BN:(kt + 1) * BN]
+                if out[b, qt, kt] == 1 and np.any(np.signbit(t)):
+                    out[b, qt, kt] = 2
+    return out
+
+
+def _classes_nan_as_masked(mask, BM, BN):
+    m = f64(mask).copy()
+    m[np.isnan(m)] = -np.inf
+    return _orig_classes(m, BM, BN)
+
+
+def _classes_square_tiles(mask, BM, BN):
+    return _orig_classes(mask, BM, BM)
+
+
+_orig_attn = oracle.mla_attention
+_orig_classes = oracle.tile_classes
+
+MUTANTS = {
+    "drop_rope_term": [(oatt, "_scores", _scores_no_rope)],
+    "rope_sign": [(oatt, "_scores", _scores_rope_sign)],
+    "scale_after_mask": [(oatt, "_scores", _scores_scale_after_mask)],
+    "mask_ignored": [(oatt, "_scores", _scores_mask_ignored)],
+    "rope_paired_with_nope": [(oatt, "_scores", _scores_rope_into_nope_slot)],
+    "softmax_wrong_axis": [(oatt, "_softmax_rows", _softmax_wrong_axis)],
+    "dead_row_uniform": [(oatt, "_softmax_rows", _softmax_uniform_dead_rows)],
+    "no_normalisation": [(oatt, "_softmax_rows", _softmax_no_normalise)],
+    "wrong_v_head": [(oracle, "mla_attention", _attn_wrong_v_head)],
+    "mask_rows_reversed": [(oracle, "mla_attention", _attn_mask_transposed_rows)],
+    "expand_swapped_slices": [(oracle, "latent_expand", _expand_swapped_slices)],
+    "expand_slice_major": [(oracle, "latent_expand", _expand_slice_major)],
+    "occupancy_neg_zero": [(oracle, "tile_classes", _classes_positive_zero_only)],
+    "occupancy_nan_masked": [(oracle, "tile_classes", _classes_nan_as_masked)],
+    "occupancy_square_tiles": [(oracle, "tile_classes", _classes_square_tiles)],
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    for mod, attr, fn in MUTANTS[name]:
+        monkeypatch.setattr(mod, attr, fn)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake {name}"
