@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark of the DFlash/DSpark draft MLA attention hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: the mask-occupancy pass, then the fused bf16 MFMA
+attention (and, for the workload that has one, the kv_b_proj latent
+expansion before them).  The headline workload is the training-shaped one
+(batch 1, context 8192, 64 anchors x block 16, 64 heads, bf16 q/k/v, bf16
+mask); the long-context and block-size-sweep workloads and the expand
+workload are timed the same way and reported under "secondary".
+
+Metric: visible TFLOP/s = (finite-mask query-key pairs) x heads x (2*192 + 2*128)
+divided by the step time, and its fraction of MI355X's published dense bf16
+MFMA peak (2.5 PFLOP/s).  Prints one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+METRIC = "draft-attn visible TFLOP/s + % of MI355X bf16 MFMA peak (1 GPU)"
+ATTN_SRC = os.path.join(ROOT, "dflash_block_draft_amd", "csrc", "attn_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="2", help="headline workload: 0,1,2,3a,3b,4")
+    p.add_argument("--secondary", default="4,1,3a,3b", help="comma list, or 'none'")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration-mb", type=int, default=0,
+                   help="run one plain device copy of this size (for HBM counter calibration)")
+    return p.parse_args()
+
+
+def make_workload(key: str):
+    from dflash_block_draft_amd import workloads as W
+    if key == "3a":
+        return W.config(3, block_size=8)
+    if key == "3b":
+        return W.config(3, block_size=32)
+    return W.config(int(key))
+
+
+def describe(wl) -> str:
+    return (f"{wl.name}: B={wl.B} H={wl.H} ctx={wl.ctx} anchors={wl.num_anchors} "
+            f"block={wl.block_size} Lq={wl.Lq} Lk={wl.Lk} q/k/v={wl.dtype} mask={wl.mask_dtype}"
+            + (" +kv_b_proj expand R=512" if wl.latent is not None else ""))
+
+
+def kernel_sha() -> str:
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measure(wl, steps: int, warmup: int) -> dict:
+    import torch
+    from dflash_block_draft_amd import mla
+    from dflash_block_draft_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    q, kr, m = (t.to(dev) for t in (wl.q, wl.k_rope, wl.mask))
+    expand = wl.latent is not None
+    if expand:
+        lat, w = wl.latent.to(dev), wl.w_kv_b.to(dev)
+        kn = torch.empty((wl.B, wl.H, wl.Lk, wl.Dn), dtype=q.dtype, device=dev)
+        v = torch.empty((wl.B, wl.H, wl.Lk, wl.Dv), dtype=q.dtype, device=dev)
+    else:
+        kn, v = wl.k_nope.to(dev), wl.v.to(dev)
+    ws = mla.new_workspace(wl.B, wl.Lq, wl.Lk, dev)
+    out = torch.empty((wl.B, wl.H, wl.Lq, wl.Dv), dtype=q.dtype, device=dev)
+    vis_flops = W.visible_flops(wl.mask, wl.B, wl.H, wl.Lq, wl.Lk)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(marks):
+        if expand:
+            marks[0].record()
+            mla.latent_expand(lat, w, wl.H, k_nope=kn, v=v)
+        marks[1].record()
+        mla.mask_occupancy(m, ws)
+        marks[2].record()
+        mla.mla_attn(q, kn, kr, v, m, wl.scale, out=out, workspace=ws, reuse_tile_map=True)
+        marks[3].record()
+
+    scratch = [ev() for _ in range(4)]
+    for _ in range(warmup):
+        step(scratch)
+    torch.cuda.synchronize()
+    marks = [[ev() for _ in range(4)] for _ in range(steps)]
+    start, end = ev(), ev()
+    t0 = time.perf_counter()
+    start.record()
+    for k in range(steps):
+        step(marks[k])
+    end.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ms = start.elapsed_time(end) / steps
+    occ = sum(mk[1].elapsed_time(mk[2]) for mk in marks) / steps
+    att = sum(mk[2].elapsed_time(mk[3]) for mk in marks) / steps
+    att_min = min(mk[2].elapsed_time(mk[3]) for mk in marks)
+    exp_ms = sum(mk[0].elapsed_time(mk[1]) for mk in marks) / steps if expand else None
+
+    # tile statistics from the occupancy map of this mask
+    tm = mla.tile_map_view(ws, wl.B, wl.Lq, wl.Lk)
+    cls = tm["classes"].cpu()
+    n = cls.numel()
+    frac = {name: round(float((cls == c).sum()) / n, 4) for c, name in ((0, "empty"), (1, "zero"), (2, "mixed"))}
+    esz = 2 if wl.dtype == "bf16" else 4
+    mask_bytes = wl.mask.numel() * wl.mask.element_size()
+    attn_bytes = (wl.q.numel() + wl.B * wl.H * wl.Lk * (wl.Dn + wl.Dv) + wl.k_rope.numel()
+                  + wl.B * wl.H * wl.Lq * wl.Dv) * esz
+    res = {
+        "workload": wl.name,
+        "shape": {"B": wl.B, "H": wl.H, "Lq": wl.Lq, "Lk": wl.Lk, "ctx": wl.ctx,
+                  "anchors": wl.num_anchors, "block_size": wl.block_size},
+        "visible_gflop": round(vis_flops / 1e9, 3),
+        "ms_per_step": round(ms, 4),
+        "wall_ms_per_step": round(wall_ms, 4),
+        "tflops": round(vis_flops / (ms * 1e-3) / 1e12, 2),
+        "pct_bf16_peak": round(100.0 * vis_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "attn_kernel_ms": round(att, 4),
+        "attn_kernel_ms_min": round(att_min, 4),
+        "attn_kernel_tflops": round(vis_flops / (att * 1e-3) / 1e12, 2),
+        "occupancy_ms": round(occ, 4),
+        "occupancy_mask_GBs": round(mask_bytes / (occ * 1e-3) / 1e9, 1),
+        "tile_fractions_128x64": frac,
+        "attn_algorithmic_bytes": attn_bytes,
+        "mask_bytes": mask_bytes,
+    }
+    if expand:
+        xf = 2 * wl.B * wl.Lk * 512 * wl.H * (wl.Dn + wl.Dv)
+        res["expand_ms"] = round(exp_ms, 4)
+        res["expand_tflops"] = round(xf / (exp_ms * 1e-3) / 1e12, 2)
+    del q, kr, m, kn, v, ws, out
+    if expand:
+        del lat, w
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(wl, budget_s: float) -> dict:
+    """The fp64 oracle as it stands, timed on the host on a bounded sample:
+    batch row 0, heads 0, 1, ... (all query rows each) until the budget is used."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    import torch
+    q, kn, kr, v, m = wl.q[:1], wl.k_nope[:1], wl.k_rope[:1], wl.v[:1], wl.mask[:1]
+    pairs = int(torch.isfinite(m.float()).sum().item())
+    done = 0
+    t0 = time.perf_counter()
+    while done < wl.H and (time.perf_counter() - t0) < budget_s:
+        oracle.mla_attention(q[:, done:done + 1], kn[:, done:done + 1], kr, v[:, done:done + 1], m, wl.scale)
+        done += 1
+    dt = time.perf_counter() - t0
+    flops = pairs * done * 640
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{wl.name}: batch row 0, heads 0..{done - 1} ({done} of {wl.H}), all {wl.Lq} query rows; "
+                      f"{flops / 1e9:.1f} visible GFLOP in {dt:.1f} s (fp64 numpy)"}
+
+
+def traffic_for(wl_name: str):
+    """HBM bytes per attention launch from committed rocprofv3 counter runs, if the
+    kernel source is unchanged since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = data.get(wl_name)
+    if not rec or rec.get("kernel_sha") != kernel_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the draft attention "
+              "shards over heads/batch rows with no exchange, but no multi-GPU run is part of this build.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+    import torch
+    from dflash_block_draft_amd import mla
+    mla.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration_mb > 0:
+        nb = args.copy_calibration_mb << 20
+        src = torch.ones(nb // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {nb} bytes read, {nb} bytes written")
+        del src, dst
+
+    log(f"building workload {args.workload}")
+    wl = make_workload(args.workload)
+    log(describe(wl))
+    head = measure(wl, args.steps, args.warmup)
+    log(f"headline: {head['ms_per_step']} ms/step, {head['tflops']} TFLOP/s "
+        f"({head['pct_bf16_peak']}% of bf16 peak); attention kernel {head['attn_kernel_ms']} ms")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a bounded sample")
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+        log(f"oracle: {cpu['value']} TFLOP/s on {cpu['cores']} threads")
+
+    secondary = []
+    if args.secondary.strip().lower() != "none":
+        for key in [k.strip() for k in args.secondary.split(",") if k.strip()]:
+            if key == args.workload:
+                continue
+            log(f"building workload {key}")
+            w2 = make_workload(key)
+            log(describe(w2))
+            r = measure(w2, max(3, args.steps // 2), max(1, args.warmup // 2))
+            log(f"{key}: {r['ms_per_step']} ms/step, {r['tflops']} TFLOP/s ({r['pct_bf16_peak']}%)")
+            secondary.append(r)
+            del w2
+
+    att_s = head["attn_kernel_ms"] * 1e-3
+    achieved = head["visible_gflop"] * 1e9 / att_s / 1e12
+    line = {
+        "metric": METRIC,
+        "value": head["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 tensors, DFlash block mask from sorted random anchors)",
+        "config": {"workload": wl.name, "batch": wl.B, "heads": wl.H, "context": wl.ctx,
+                   "anchors": wl.num_anchors, "block_size": wl.block_size, "Lq": wl.Lq, "Lk": wl.Lk,
+                   "qk_nope": wl.Dn, "qk_rope_shared": wl.Dr, "v_head_dim": wl.Dv,
+                   "mask_dtype": wl.mask_dtype, "parallelism": "none (1 GPU)"},
+        "pct_bf16_peak": head["pct_bf16_peak"],
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_for(wl.name),
+                     "basis": "visible FLOPs (finite-mask pairs x heads x 640) / mean attention-kernel time (HIP events on its stream)"},
+        "cpu_baseline": cpu,
+        "headline": head,
+        "secondary": secondary,
+        "attn_kernel_sha": kernel_sha(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,300 @@
+// C ABI of the library (declared in include/dflash_mla.h): argument checks,
+// workspace layout and kernel dispatch.  Nothing here allocates device memory
+// or keeps state; every launch goes on the caller's stream.
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/dflash_mla.h"
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dflash_status fail(dflash_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+dflash_status fail(dflash_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+dflash_status ok() {
+  g_last_error.clear();
+  return DFLASH_OK;
+}
+
+dflash_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(DFLASH_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t dt_size(dflash_dtype d) { return d == DFLASH_BF16 ? 2 : 4; }
+
+bool valid_dtype(int d) { return d == DFLASH_F32 || d == DFLASH_BF16; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Range range_of(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return {a, a + bytes};
+}
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Multiply positive sizes, reporting overflow past 2^62.
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a <= 0 || b <= 0) return false;
+  if (a > (int64_t(1) << 62) / b) return false;
+  *out = a * b;
+  return true;
+}
+
+struct TileLayout {
+  int64_t nqt, nkt;
+  size_t classes, counts, lists, order, total;
+};
+
+bool tile_layout(int64_t B, int64_t Lq, int64_t Lk, TileLayout* t) {
+  if (B <= 0 || Lq <= 0 || Lk <= 0) return false;
+  t->nqt = (Lq + DFLASH_TILE_M - 1) / DFLASH_TILE_M;
+  t->nkt = (Lk + DFLASH_TILE_N - 1) / DFLASH_TILE_N;
+  int64_t rows, cells;
+  if (!mul_ok(B, t->nqt, &rows) || !mul_ok(rows, t->nkt, &cells)) return false;
+  t->classes = 0;
+  t->counts = align_up(static_cast<size_t>(cells), 256);
+  t->lists = t->counts + align_up(static_cast<size_t>(rows) * 4, 256);
+  t->order = t->lists + align_up(static_cast<size_t>(cells) * 4, 256);
+  t->total = t->order + align_up(static_cast<size_t>(rows) * 4, 256);
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dflash_status_string(dflash_status s) {
+  switch (s) {
+    case DFLASH_OK: return "DFLASH_OK";
+    case DFLASH_ERR_INVALID_ARG: return "DFLASH_ERR_INVALID_ARG";
+    case DFLASH_ERR_UNSUPPORTED: return "DFLASH_ERR_UNSUPPORTED";
+    case DFLASH_ERR_WORKSPACE: return "DFLASH_ERR_WORKSPACE";
+    case DFLASH_ERR_HIP: return "DFLASH_ERR_HIP";
+  }
+  return "DFLASH_ERR_UNKNOWN";
+}
+
+const char* dflash_last_error(void) { return g_last_error.c_str(); }
+
+size_t dflash_mla_attn_workspace_bytes(int64_t B, int64_t Lq, int64_t Lk) {
+  TileLayout t;
+  if (!tile_layout(B, Lq, Lk, &t)) return 0;
+  return t.total;
+}
+
+dflash_status dflash_mla_tile_map_layout(int64_t B, int64_t Lq, int64_t Lk, int64_t* n_q_tiles,
+                                         int64_t* n_k_tiles, size_t* classes_offset,
+                                         size_t* counts_offset, size_t* lists_offset,
+                                         size_t* order_offset) {
+  TileLayout t;
+  if (!tile_layout(B, Lq, Lk, &t)) return fail(DFLASH_ERR_INVALID_ARG, "B, Lq, Lk must be positive (got %lld, %lld, %lld)", (long long)B, (long long)Lq, (long long)Lk);
+  if (n_q_tiles) *n_q_tiles = t.nqt;
+  if (n_k_tiles) *n_k_tiles = t.nkt;
+  if (classes_offset) *classes_offset = t.classes;
+  if (counts_offset) *counts_offset = t.counts;
+  if (lists_offset) *lists_offset = t.lists;
+  if (order_offset) *order_offset = t.order;
+  return ok();
+}
+
+static dflash_status check_occupancy_args(const void* mask, int mask_dt, int64_t B, int64_t Lq,
+                                          int64_t Lk, const void* ws, size_t ws_bytes,
+                                          TileLayout* t) {
+  if (!mask) return fail(DFLASH_ERR_INVALID_ARG, "additive_mask is NULL");
+  if (!valid_dtype(mask_dt)) return fail(DFLASH_ERR_INVALID_ARG, "mask_dt %d is not a dflash_dtype", mask_dt);
+  if (!aligned16(mask)) return fail(DFLASH_ERR_INVALID_ARG, "additive_mask is not 16-byte aligned");
+  if (B <= 0 || Lq <= 0 || Lk <= 0)
+    return fail(DFLASH_ERR_INVALID_ARG, "B, Lq, Lk must be positive (got %lld, %lld, %lld)", (long long)B, (long long)Lq, (long long)Lk);
+  if (B > INT32_MAX || Lq > INT32_MAX || Lk > INT32_MAX)
+    return fail(DFLASH_ERR_UNSUPPORTED, "B, Lq, Lk must each fit in int32");
+  if (!tile_layout(B, Lq, Lk, t)) return fail(DFLASH_ERR_INVALID_ARG, "tile map size overflows");
+  if (t->nkt >= (int64_t(1) << 24)) return fail(DFLASH_ERR_UNSUPPORTED, "Lk too large for the tile lists");
+  if (B * t->nqt * t->nkt > INT32_MAX) return fail(DFLASH_ERR_UNSUPPORTED, "too many tiles");
+  if (!ws) return fail(DFLASH_ERR_WORKSPACE, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(DFLASH_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (ws_bytes < t->total)
+    return fail(DFLASH_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, t->total);
+  return ok();
+}
+
+static dflash::OccupancyArgs occupancy_args(const void* mask, int mask_dt, int64_t B, int64_t Lq,
+                                            int64_t Lk, void* ws, const TileLayout& t) {
+  dflash::OccupancyArgs o;
+  char* w = static_cast<char*>(ws);
+  o.mask = mask;
+  o.mask_bf16 = mask_dt == DFLASH_BF16;
+  o.B = static_cast<int>(B);
+  o.Lq = static_cast<int>(Lq);
+  o.Lk = static_cast<int>(Lk);
+  o.nqt = static_cast<int>(t.nqt);
+  o.nkt = static_cast<int>(t.nkt);
+  o.classes = reinterpret_cast<uint8_t*>(w + t.classes);
+  o.counts = reinterpret_cast<int32_t*>(w + t.counts);
+  o.lists = reinterpret_cast<int32_t*>(w + t.lists);
+  o.order = reinterpret_cast<int32_t*>(w + t.order);
+  return o;
+}
+
+dflash_status dflash_mla_mask_occupancy(const void* additive_mask, dflash_dtype mask_dt, int64_t B,
+                                        int64_t Lq, int64_t Lk, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  TileLayout t;
+  dflash_status st = check_occupancy_args(additive_mask, mask_dt, B, Lq, Lk, workspace, workspace_bytes, &t);
+  if (st != DFLASH_OK) return st;
+  const dflash::OccupancyArgs o = occupancy_args(additive_mask, mask_dt, B, Lq, Lk, workspace, t);
+  return hip_status(dflash::launch_occupancy(o, static_cast<hipStream_t>(stream)), "mask occupancy launch");
+}
+
+dflash_status dflash_mla_latent_expand(const void* latent, const void* w_kv_b, void* k_nope, void* v,
+                                       int64_t B, int64_t Lk, int64_t R, int64_t H, int64_t Dn,
+                                       int64_t Dv, dflash_dtype dt, void* stream) {
+  if (!latent || !w_kv_b || !k_nope || !v) return fail(DFLASH_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!aligned16(latent) || !aligned16(w_kv_b) || !aligned16(k_nope) || !aligned16(v))
+    return fail(DFLASH_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (B <= 0 || Lk <= 0 || R <= 0 || H <= 0 || Dn <= 0 || Dv <= 0)
+    return fail(DFLASH_ERR_INVALID_ARG, "sizes must be positive");
+  if (!valid_dtype(dt)) return fail(DFLASH_ERR_INVALID_ARG, "dt %d is not a dflash_dtype", (int)dt);
+  if (Dn != dflash::kDn || Dv != dflash::kDv)
+    return fail(DFLASH_ERR_UNSUPPORTED, "only Dn = 128 and Dv = 128 are built (got %lld, %lld)", (long long)Dn, (long long)Dv);
+  if (R % 32 != 0) return fail(DFLASH_ERR_UNSUPPORTED, "R must be a multiple of 32 (got %lld)", (long long)R);
+  int64_t M, tmp;
+  if (!mul_ok(B, Lk, &M) || M > INT32_MAX || H > 16384 || R > INT32_MAX || !mul_ok(M, R, &tmp))
+    return fail(DFLASH_ERR_UNSUPPORTED, "sizes too large");
+  const size_t es = dt_size(dt);
+  const Range rl = range_of(latent, static_cast<size_t>(M) * R * es);
+  const Range rw = range_of(w_kv_b, static_cast<size_t>(H) * 256 * R * es);
+  const Range rk = range_of(k_nope, static_cast<size_t>(M) * H * 128 * es);
+  const Range rv = range_of(v, static_cast<size_t>(M) * H * 128 * es);
+  if (overlaps(rk, rv) || overlaps(rk, rl) || overlaps(rk, rw) || overlaps(rv, rl) || overlaps(rv, rw))
+    return fail(DFLASH_ERR_INVALID_ARG, "outputs overlap each other or an input");
+  dflash::ExpandArgs a;
+  a.latent = latent;
+  a.w = w_kv_b;
+  a.kn = k_nope;
+  a.v = v;
+  a.B = static_cast<int>(B);
+  a.Lk = static_cast<int>(Lk);
+  a.R = static_cast<int>(R);
+  a.H = static_cast<int>(H);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(dt == DFLASH_BF16 ? dflash::launch_expand_bf16(a, s) : dflash::launch_expand_f32(a, s),
+                    "latent expand launch");
+}
+
+dflash_status dflash_mla_attn(const void* q, const void* k_nope, const void* k_rope_shared,
+                              const void* v, const void* additive_mask, void* out, int64_t B,
+                              int64_t H, int64_t Lq, int64_t Lk, int64_t Dn, int64_t Dr,
+                              int64_t Dv, float scale, dflash_dtype dt, dflash_dtype mask_dt,
+                              void* workspace, size_t workspace_bytes, uint32_t flags,
+                              void* stream) {
+  if (!q || !k_nope || !k_rope_shared || !v || !out) return fail(DFLASH_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!aligned16(q) || !aligned16(k_nope) || !aligned16(k_rope_shared) || !aligned16(v) || !aligned16(out) ||
+      (additive_mask && !aligned16(additive_mask)))
+    return fail(DFLASH_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0 || Dn <= 0 || Dr <= 0 || Dv <= 0)
+    return fail(DFLASH_ERR_INVALID_ARG, "sizes must be positive (B=%lld H=%lld Lq=%lld Lk=%lld)", (long long)B, (long long)H, (long long)Lq, (long long)Lk);
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(DFLASH_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (!valid_dtype(dt) || !valid_dtype(mask_dt)) return fail(DFLASH_ERR_INVALID_ARG, "dtype is not a dflash_dtype");
+  if (flags & ~(DFLASH_ATTN_REUSE_TILE_MAP | DFLASH_ATTN_NO_TILE_SKIP))
+    return fail(DFLASH_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  if (Dn != dflash::kDn || Dr != dflash::kDr || Dv != dflash::kDv)
+    return fail(DFLASH_ERR_UNSUPPORTED, "only Dn=128, Dr=64, Dv=128 are built (got %lld, %lld, %lld)", (long long)Dn, (long long)Dr, (long long)Dv);
+  if (additive_mask && dt == DFLASH_F32 && mask_dt != DFLASH_F32)
+    return fail(DFLASH_ERR_UNSUPPORTED, "an f32 attention takes an f32 mask");
+  if (B > INT32_MAX || H > INT32_MAX || Lq > INT32_MAX || Lk > INT32_MAX)
+    return fail(DFLASH_ERR_UNSUPPORTED, "sizes must each fit in int32");
+  int64_t bh, tmp;
+  if (!mul_ok(B, H, &bh) || !mul_ok(bh, Lq, &tmp) || !mul_ok(tmp, Dn + Dr, &tmp) || !mul_ok(bh, Lk, &tmp) ||
+      !mul_ok(tmp, Dn, &tmp) || !mul_ok(B * Lq, Lk, &tmp))
+    return fail(DFLASH_ERR_UNSUPPORTED, "sizes too large");
+  const size_t es = dt_size(dt);
+  const Range ro = range_of(out, static_cast<size_t>(bh) * Lq * Dv * es);
+  const Range ins[5] = {
+      range_of(q, static_cast<size_t>(bh) * Lq * (Dn + Dr) * es),
+      range_of(k_nope, static_cast<size_t>(bh) * Lk * Dn * es),
+      range_of(k_rope_shared, static_cast<size_t>(B) * Lk * Dr * es),
+      range_of(v, static_cast<size_t>(bh) * Lk * Dv * es),
+      additive_mask ? range_of(additive_mask, static_cast<size_t>(B) * Lq * Lk * dt_size(mask_dt)) : Range{0, 0},
+  };
+  for (const Range& r : ins)
+    if (overlaps(ro, r)) return fail(DFLASH_ERR_INVALID_ARG, "out overlaps an input");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  if (dt == DFLASH_F32) {
+    if (static_cast<int64_t>(B) > 65535 || H > 65535) return fail(DFLASH_ERR_UNSUPPORTED, "B and H must be <= 65535 for f32");
+    dflash::AttnF32Args a;
+    a.q = static_cast<const float*>(q);
+    a.kn = static_cast<const float*>(k_nope);
+    a.kr = static_cast<const float*>(k_rope_shared);
+    a.v = static_cast<const float*>(v);
+    a.mask = static_cast<const float*>(additive_mask);
+    a.out = static_cast<float*>(out);
+    a.B = static_cast<int>(B);
+    a.H = static_cast<int>(H);
+    a.Lq = static_cast<int>(Lq);
+    a.Lk = static_cast<int>(Lk);
+    a.scale = scale;
+    return hip_status(dflash::launch_attn_f32(a, s), "f32 attention launch");
+  }
+
+  dflash::AttnBf16Args a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kn = static_cast<const uint16_t*>(k_nope);
+  a.kr = static_cast<const uint16_t*>(k_rope_shared);
+  a.v = static_cast<const uint16_t*>(v);
+  a.mask = additive_mask;
+  a.out = static_cast<uint16_t*>(out);
+  a.B = static_cast<int>(B);
+  a.H = static_cast<int>(H);
+  a.Lq = static_cast<int>(Lq);
+  a.Lk = static_cast<int>(Lk);
+  a.nqt = static_cast<int>((Lq + DFLASH_TILE_M - 1) / DFLASH_TILE_M);
+  a.nkt = static_cast<int>((Lk + DFLASH_TILE_N - 1) / DFLASH_TILE_N);
+  a.scale = scale;
+  a.mask_bf16 = mask_dt == DFLASH_BF16;
+  a.no_skip = (flags & DFLASH_ATTN_NO_TILE_SKIP) ? 1 : 0;
+  if (static_cast<int64_t>(B) * a.nqt * H > INT32_MAX) return fail(DFLASH_ERR_UNSUPPORTED, "too many work items");
+  if (additive_mask) {
+    TileLayout t;
+    dflash_status st = check_occupancy_args(additive_mask, mask_dt, B, Lq, Lk, workspace, workspace_bytes, &t);
+    if (st != DFLASH_OK) return st;
+    const Range rw = range_of(workspace, t.total);
+    if (overlaps(ro, rw)) return fail(DFLASH_ERR_INVALID_ARG, "out overlaps the workspace");
+    for (const Range& r : ins)
+      if (overlaps(rw, r)) return fail(DFLASH_ERR_INVALID_ARG, "the workspace overlaps an input");
+    const dflash::OccupancyArgs o = occupancy_args(additive_mask, mask_dt, B, Lq, Lk, workspace, t);
+    if (!(flags & DFLASH_ATTN_REUSE_TILE_MAP)) {
+      st = hip_status(dflash::launch_occupancy(o, s), "mask occupancy launch");
+      if (st != DFLASH_OK) return st;
+    }
+    a.classes = o.classes;
+    a.counts = o.counts;
+    a.lists = o.lists;
+    a.order = o.order;
+  }
+  return hip_status(dflash::launch_attn_bf16(a, s), "bf16 attention launch");
+}
+
+}  // extern "C"

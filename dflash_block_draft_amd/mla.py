@@ -1,0 +1,219 @@
+"""Thin Python binding of the C ABI in include/dflash_mla.h.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, then their device pointers and the current HIP stream are passed
+to the library.  Every step of the computation runs in the HIP kernels; there
+is no fallback of any kind, and a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdflash_mla.so")
+
+TILE_M = 128
+TILE_N = 64
+DN, DR, DV = 128, 64, 128
+
+_F32, _BF16 = 0, 1
+_DT = {torch.float32: _F32, torch.bfloat16: _BF16}
+FLAG_REUSE_TILE_MAP = 0x1
+FLAG_NO_TILE_SKIP = 0x2
+
+EXPORTED = (
+    "dflash_status_string", "dflash_last_error", "dflash_mla_latent_expand",
+    "dflash_mla_attn_workspace_bytes", "dflash_mla_tile_map_layout",
+    "dflash_mla_mask_occupancy", "dflash_mla_attn",
+)
+
+
+class DflashError(ValueError):
+    """A non-OK status from the library (bad configuration raises ValueError,
+    as the pages' config builders do)."""
+
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__(f"{name}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libdflash_mla.so (built by dflash_block_draft_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                           "(run python -m dflash_block_draft_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, sz, u32, f32, i32 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t,
+                                  ctypes.c_uint32, ctypes.c_float, ctypes.c_int)
+    lib.dflash_status_string.argtypes = [i32]
+    lib.dflash_status_string.restype = ctypes.c_char_p
+    lib.dflash_last_error.argtypes = []
+    lib.dflash_last_error.restype = ctypes.c_char_p
+    lib.dflash_mla_latent_expand.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, vp]
+    lib.dflash_mla_latent_expand.restype = i32
+    lib.dflash_mla_attn_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.dflash_mla_attn_workspace_bytes.restype = sz
+    p64, psz = ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_size_t)
+    lib.dflash_mla_tile_map_layout.argtypes = [i64, i64, i64, p64, p64, psz, psz, psz, psz]
+    lib.dflash_mla_tile_map_layout.restype = i32
+    lib.dflash_mla_mask_occupancy.argtypes = [vp, i32, i64, i64, i64, vp, sz, vp]
+    lib.dflash_mla_mask_occupancy.restype = i32
+    lib.dflash_mla_attn.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32,
+                                    i32, i32, vp, sz, u32, vp]
+    lib.dflash_mla_attn.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        lib = load_library()
+        raise DflashError(status, lib.dflash_status_string(status).decode(),
+                          lib.dflash_last_error().decode())
+
+
+def _stream(t: torch.Tensor) -> Optional[int]:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if t.dtype not in _DT:
+        raise ValueError(f"{name}: unsupported dtype {t.dtype}")
+    return t
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def latent_expand(latent: torch.Tensor, w_kv_b: torch.Tensor, num_heads: int,
+                  qk_nope_head_dim: int = DN, v_head_dim: int = DV,
+                  k_nope: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None):
+    """kv_b_proj: latent [B, Lk, R] x w_kv_b [H*(Dn+Dv), R] -> (k_nope [B,H,Lk,Dn], v [B,H,Lk,Dv])."""
+    lib = load_library()
+    _dev(latent, "latent", ndim=3)
+    _dev(w_kv_b, "w_kv_b", dtype=latent.dtype, ndim=2)
+    B, Lk, R = latent.shape
+    H = int(num_heads)
+    if k_nope is None:
+        k_nope = torch.empty((B, H, Lk, qk_nope_head_dim), dtype=latent.dtype, device=latent.device)
+    if v is None:
+        v = torch.empty((B, H, Lk, v_head_dim), dtype=latent.dtype, device=latent.device)
+    _dev(k_nope, "k_nope", dtype=latent.dtype, ndim=4)
+    _dev(v, "v", dtype=latent.dtype, ndim=4)
+    if tuple(w_kv_b.shape) != (H * (qk_nope_head_dim + v_head_dim), R):
+        raise ValueError(f"w_kv_b must be [{H * (qk_nope_head_dim + v_head_dim)}, {R}], got {tuple(w_kv_b.shape)}")
+    if tuple(k_nope.shape) != (B, H, Lk, qk_nope_head_dim) or tuple(v.shape) != (B, H, Lk, v_head_dim):
+        raise ValueError("output shapes do not match [B, H, Lk, D]")
+    _check(lib.dflash_mla_latent_expand(_ptr(latent), _ptr(w_kv_b), _ptr(k_nope), _ptr(v),
+                                        B, Lk, R, H, qk_nope_head_dim, v_head_dim,
+                                        _DT[latent.dtype], _stream(latent)))
+    return k_nope, v
+
+
+def attn_workspace_bytes(B: int, Lq: int, Lk: int) -> int:
+    return int(load_library().dflash_mla_attn_workspace_bytes(B, Lq, Lk))
+
+
+def new_workspace(B: int, Lq: int, Lk: int, device) -> torch.Tensor:
+    n = attn_workspace_bytes(B, Lq, Lk)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def mask_occupancy(mask: torch.Tensor, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Run the occupancy pass alone; returns the workspace holding the tile map."""
+    lib = load_library()
+    _dev(mask, "mask", ndim=4)
+    B, one, Lq, Lk = mask.shape
+    if one != 1:
+        raise ValueError("mask must be [B, 1, Lq, Lk]")
+    if workspace is None:
+        workspace = new_workspace(B, Lq, Lk, mask.device)
+    _dev(workspace, "workspace", dtype=torch.uint8)
+    _check(lib.dflash_mla_mask_occupancy(_ptr(mask), _DT[mask.dtype], B, Lq, Lk, _ptr(workspace),
+                                         workspace.numel(), _stream(mask)))
+    return workspace
+
+
+def tile_map_view(workspace: torch.Tensor, B: int, Lq: int, Lk: int) -> dict:
+    """Views of the occupancy results inside a workspace (see dflash_mla_tile_map_layout)."""
+    lib = load_library()
+    nq, nk = ctypes.c_int64(), ctypes.c_int64()
+    offs = [ctypes.c_size_t() for _ in range(4)]
+    _check(lib.dflash_mla_tile_map_layout(B, Lq, Lk, ctypes.byref(nq), ctypes.byref(nk),
+                                          *[ctypes.byref(o) for o in offs]))
+    nq, nk = nq.value, nk.value
+    c_off, n_off, l_off, o_off = (o.value for o in offs)
+    ws = workspace
+    return {
+        "n_q_tiles": nq, "n_k_tiles": nk,
+        "classes": ws[c_off:c_off + B * nq * nk].view(B, nq, nk),
+        "counts": ws[n_off:n_off + 4 * B * nq].view(torch.int32).view(B, nq),
+        "lists": ws[l_off:l_off + 4 * B * nq * nk].view(torch.int32).view(B, nq, nk),
+        "order": ws[o_off:o_off + 4 * B * nq].view(torch.int32),
+    }
+
+
+def mla_attn(q: torch.Tensor, k_nope: torch.Tensor, k_rope: torch.Tensor, v: torch.Tensor,
+             mask: Optional[torch.Tensor] = None, scale: Optional[float] = None, *,
+             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+             reuse_tile_map: bool = False, tile_skip: bool = True) -> torch.Tensor:
+    """Draft MLA attention: q [B,H,Lq,Dn+Dr], k_nope [B,H,Lk,Dn], k_rope [B,Lk,Dr] (head-shared),
+    v [B,H,Lk,Dv], mask [B,1,Lq,Lk] or None -> out [B,H,Lq,Dv].  scale defaults to
+    q_head_dim ** -0.5."""
+    lib = load_library()
+    _dev(q, "q", ndim=4)
+    dt = q.dtype
+    _dev(k_nope, "k_nope", dtype=dt, ndim=4)
+    _dev(k_rope, "k_rope", dtype=dt, ndim=3)
+    _dev(v, "v", dtype=dt, ndim=4)
+    B, H, Lq, Dqk = q.shape
+    Lk, Dn = k_nope.shape[2], k_nope.shape[3]
+    Dr, Dv = k_rope.shape[2], v.shape[3]
+    if Dqk != Dn + Dr:
+        raise ValueError(f"q last dim {Dqk} != Dn + Dr = {Dn + Dr}")
+    if tuple(k_nope.shape[:2]) != (B, H) or tuple(v.shape[:3]) != (B, H, Lk) or tuple(k_rope.shape[:2]) != (B, Lk):
+        raise ValueError("q / k_nope / k_rope / v shapes are inconsistent")
+    if scale is None:
+        scale = float(Dn + Dr) ** -0.5
+    mask_dt = _F32
+    if mask is not None:
+        _dev(mask, "mask", ndim=4)
+        if tuple(mask.shape) != (B, 1, Lq, Lk):
+            raise ValueError(f"mask must be [{B}, 1, {Lq}, {Lk}], got {tuple(mask.shape)}")
+        mask_dt = _DT[mask.dtype]
+        if workspace is None:
+            if reuse_tile_map:
+                raise ValueError("reuse_tile_map needs the workspace that holds the map")
+            workspace = new_workspace(B, Lq, Lk, q.device)
+    if out is None:
+        out = torch.empty((B, H, Lq, Dv), dtype=dt, device=q.device)
+    _dev(out, "out", dtype=dt, ndim=4)
+    if workspace is not None:
+        _dev(workspace, "workspace", dtype=torch.uint8)
+    flags = (FLAG_REUSE_TILE_MAP if reuse_tile_map else 0) | (0 if tile_skip else FLAG_NO_TILE_SKIP)
+    _check(lib.dflash_mla_attn(_ptr(q), _ptr(k_nope), _ptr(k_rope), _ptr(v), _ptr(mask), _ptr(out),
+                               B, H, Lq, Lk, Dn, Dr, Dv, float(scale), _DT[dt], mask_dt,
+                               _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                               flags, _stream(q)))
+    return out

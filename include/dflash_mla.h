@@ -1,0 +1,186 @@
+/*
+ * dflash_mla.h -- C ABI of the MI355X (gfx950) DFlash/DSpark draft MLA attention.
+ *
+ * What the library computes (NeMo AutoModel documentation pages
+ * "speculative.dflash.draft_kimi_k3" and "speculative.dspark.draft_kimi_k3"):
+ * the draft's non-causal MLA attention.  Queries are the num_anchors*block_size
+ * noise-block tokens; keys and values span [target-hidden context | noise
+ * block] (KimiK3DSparkAttention.forward: the context is concatenated before the
+ * noise block).  Every query head has its own K/V, because kv_b_proj emits one
+ * qk_nope_head_dim + v_head_dim slice per head (KimiK3DFlashAttention class
+ * text: no GQA group repeat).  A key is [k_nope (per head) | k_rope (one per
+ * token, shared by all heads; NoPE, so no rotary -- module text of the DFlash
+ * page)].  The softmax scale is q_head_dim ** -0.5 (KimiK3DSparkAttention
+ * attributes).  The dense additive mask [batch, 1, Lq, ctx + Lq] is added to
+ * the scores unchanged (KimiK3DFlashAttention.forward); the Lq x Lk score
+ * matrix is never materialised (same passage: it is too large to afford).
+ *
+ * Conventions shared by every entry point
+ *  - Tensor pointers are device memory owned by the caller, contiguous, in the
+ *    layouts stated per call, and 16-byte aligned.  The library allocates no
+ *    memory and keeps no state between calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *    is enqueued asynchronously on it; a kernel fault surfaces at the caller's
+ *    next synchronisation.  Calls on different streams are independent as long
+ *    as they do not share a workspace.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    non-OK status means nothing was launched (except DFLASH_ERR_HIP, which
+ *    reports a failed launch).  dflash_last_error() gives a readable reason.
+ *  - No C++ exception crosses this interface.
+ *  - Results are bitwise deterministic from run to run (no atomics in any
+ *    reduction; the work schedule does not change which lane sums what).
+ */
+#ifndef DFLASH_MLA_H
+#define DFLASH_MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dflash_status {
+  DFLASH_OK = 0,
+  DFLASH_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, non-positive size, bad scale, aliasing, bad flags */
+  DFLASH_ERR_UNSUPPORTED = 2,  /* head dims or dtype combination this build does not implement */
+  DFLASH_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
+  DFLASH_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} dflash_status;
+
+typedef enum dflash_dtype {
+  DFLASH_F32 = 0,
+  DFLASH_BF16 = 1
+} dflash_dtype;
+
+/* Attention tile: queries per tile x keys per tile.  The mask-occupancy map
+ * classifies tiles of exactly this shape. */
+#define DFLASH_TILE_M 128
+#define DFLASH_TILE_N 64
+
+/* Tile classes stored in the occupancy map (one byte per tile). */
+#define DFLASH_TILE_EMPTY 0   /* every mask entry is exactly -inf: the tile is skipped      */
+#define DFLASH_TILE_ZERO 1    /* every mask entry is +0 or -0: no mask load, no mask add    */
+#define DFLASH_TILE_MIXED 2   /* anything else: the mask tile is loaded and added           */
+
+/* dflash_mla_attn flags */
+#define DFLASH_ATTN_REUSE_TILE_MAP 0x1u  /* skip the occupancy pass: the workspace already holds
+                                            the map of this same mask (e.g. the next draft layer,
+                                            which receives the same mask) */
+#define DFLASH_ATTN_NO_TILE_SKIP 0x2u    /* debug/verification: visit every tile, treating empty
+                                            tiles as mixed; the result is bitwise identical */
+
+/* Human-readable name of a status. Never NULL. */
+const char* dflash_status_string(dflash_status status);
+
+/* Reason for the last non-OK status returned on the calling thread ("" if none). */
+const char* dflash_last_error(void);
+
+/*
+ * kv_b_proj expansion of the compressed KV latent into per-head k_nope and v.
+ * Pages: DFlash page, KimiK3DFlashAttention class text ("kv_b_proj produces
+ * num_attention_heads slices of qk_nope_head_dim + v_head_dim"); DSpark page,
+ * KimiK3DSparkAttention (kv_b_proj, kv_lora_rank); Kimi K3 model page, MLA
+ * context-parallel forward (the latent is kv_lora_rank values per token besides
+ * the head-shared rope part, and is expanded locally).
+ *
+ *   k_nope[b,h,t,e] = sum_r latent[b,t,r] * w_kv_b[h*(Dn+Dv) + e,      r]   (e < Dn)
+ *   v     [b,h,t,e] = sum_r latent[b,t,r] * w_kv_b[h*(Dn+Dv) + Dn + e, r]   (e < Dv)
+ *
+ * latent  [B, Lk, R]          dtype dt   (the kv_b_proj input, already normed)
+ * w_kv_b  [H*(Dn+Dv), R]      dtype dt   (Linear weight, out x in, no bias)
+ * k_nope  [B, H, Lk, Dn]      dtype dt   (written)
+ * v       [B, H, Lk, Dv]      dtype dt   (written)
+ * Accumulation is fp32; bf16 outputs are rounded to nearest even.
+ * Supported: Dn == 128, Dv == 128, R a positive multiple of 32, dt F32 or BF16.
+ * Outputs must not overlap each other or the inputs.
+ */
+dflash_status dflash_mla_latent_expand(const void* latent, const void* w_kv_b,
+                                       void* k_nope, void* v,
+                                       int64_t B, int64_t Lk, int64_t R, int64_t H,
+                                       int64_t Dn, int64_t Dv, dflash_dtype dt,
+                                       void* stream);
+
+/*
+ * Bytes of device workspace dflash_mla_attn / dflash_mla_mask_occupancy need for
+ * a masked call of this shape (the occupancy map, the per-q-tile lists of
+ * non-empty k-tiles and the schedule).  0 if any size is not positive.
+ */
+size_t dflash_mla_attn_workspace_bytes(int64_t B, int64_t Lq, int64_t Lk);
+
+/*
+ * Where the occupancy results sit inside the workspace, so a caller can read
+ * them back (all offsets in bytes from the workspace start):
+ *   classes  uint8 [B, n_q_tiles, n_k_tiles]   DFLASH_TILE_* per tile
+ *   counts   int32 [B, n_q_tiles]              non-empty k-tiles per q-tile
+ *   lists    int32 [B, n_q_tiles, n_k_tiles]   first counts[] entries: k-tile index | class << 24,
+ *                                              in increasing k order
+ *   order    int32 [B * n_q_tiles]             (b * n_q_tiles + q-tile) by decreasing count,
+ *                                              ties by increasing index
+ * n_q_tiles = ceil(Lq / DFLASH_TILE_M), n_k_tiles = ceil(Lk / DFLASH_TILE_N).
+ */
+dflash_status dflash_mla_tile_map_layout(int64_t B, int64_t Lq, int64_t Lk,
+                                         int64_t* n_q_tiles, int64_t* n_k_tiles,
+                                         size_t* classes_offset, size_t* counts_offset,
+                                         size_t* lists_offset, size_t* order_offset);
+
+/*
+ * The mask-occupancy pass alone: classify every DFLASH_TILE_M x DFLASH_TILE_N
+ * tile of the additive mask and build the lists/schedule in the workspace.
+ * Tile of (b, qt, kt): rows [qt*M, min(qt*M+M, Lq)), columns [kt*N, min(kt*N+N, Lk))
+ * of mask[b, 0]; entries outside the mask do not count.  Classes compare bit
+ * patterns: exactly -inf is "masked"; +0/-0 is "zero"; everything else,
+ * including NaN, +inf and large finite negatives, is "mixed".
+ *
+ * additive_mask [B, 1, Lq, Lk] in mask_dt (F32 or BF16).
+ * The pages pass the same mask to every draft layer (DFlash page,
+ * KimiK3DFlashDecoderLayer.forward), so the result can be reused across layers
+ * with DFLASH_ATTN_REUSE_TILE_MAP.
+ */
+dflash_status dflash_mla_mask_occupancy(const void* additive_mask, dflash_dtype mask_dt,
+                                        int64_t B, int64_t Lq, int64_t Lk,
+                                        void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
+/*
+ * Non-causal draft MLA attention (DFlash page, KimiK3DFlashAttention.forward;
+ * DSpark page, KimiK3DSparkAttention.forward).  For batch b, head h, query i:
+ *
+ *   s_j = scale * (q[b,h,i,:Dn] . k_nope[b,h,j,:] + q[b,h,i,Dn:] . k_rope_shared[b,j,:])
+ *         + additive_mask[b,0,i,j]
+ *   out[b,h,i,:] = sum_j softmax_j(s) * v[b,h,j,:]
+ *
+ * q             [B, H, Lq, Dn+Dr]  dtype dt  (q_nope then q_rope)
+ * k_nope        [B, H, Lk, Dn]     dtype dt
+ * k_rope_shared [B, Lk, Dr]        dtype dt  (one per token, shared by every head)
+ * v             [B, H, Lk, Dv]     dtype dt
+ * additive_mask [B, 1, Lq, Lk]     mask_dt, or NULL (= every key visible)
+ * out           [B, H, Lq, Dv]     dtype dt  (written; must not overlap any input)
+ * scale         finite and > 0; the pages' value is (Dn + Dr) ** -0.5.
+ *
+ * Supported: Dn == 128, Dr == 64, Dv == 128;
+ *   (dt, mask_dt) in {(F32, F32), (BF16, F32), (BF16, BF16)}.
+ * BF16: QK^T and PV run as bf16 MFMA with fp32 accumulation and an online
+ *   softmax in fp32; the probabilities are rounded to bf16 for PV; out is
+ *   rounded to nearest even.  F32: fp32 arithmetic throughout.
+ * A query row whose every score is -inf returns 0 (the pages do not define it).
+ * Mask semantics: only exactly -inf hides a key; finite values, however large,
+ *   are added; +inf/NaN entries propagate NaN into that row as the plain
+ *   definition does.
+ * Workspace (BF16 with a mask): at least dflash_mla_attn_workspace_bytes(B, Lq, Lk)
+ *   bytes, 256-byte aligned; unused (may be NULL/0) when the mask is NULL or dt is F32.
+ * flags: 0 or DFLASH_ATTN_REUSE_TILE_MAP and/or DFLASH_ATTN_NO_TILE_SKIP.
+ */
+dflash_status dflash_mla_attn(const void* q, const void* k_nope, const void* k_rope_shared,
+                              const void* v, const void* additive_mask, void* out,
+                              int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                              int64_t Dn, int64_t Dr, int64_t Dv, float scale,
+                              dflash_dtype dt, dflash_dtype mask_dt,
+                              void* workspace, size_t workspace_bytes,
+                              uint32_t flags, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_MLA_H */

@@ -1,0 +1,130 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every
+function include/dflash_mla.h declares, and argument validation returns the
+documented status before anything touches a device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash_mla.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from dflash_block_draft_amd import mla
+    if not os.path.exists(mla.LIB_PATH):
+        from dflash_block_draft_amd import build
+        build.build(verbose=False)
+    return mla.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_documented_entry_points():
+    names = declared_functions()
+    for n in ("dflash_mla_latent_expand", "dflash_mla_attn", "dflash_mla_attn_workspace_bytes",
+              "dflash_mla_mask_occupancy", "dflash_mla_tile_map_layout", "dflash_status_string",
+              "dflash_last_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from dflash_block_draft_amd import mla
+    out = subprocess.run(["nm", "-D", "--defined-only", mla.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, f"{name} declared in the header but not exported"
+        assert getattr(lib, name) is not None
+    assert set(mla.EXPORTED) <= exported
+
+
+def test_status_strings(lib):
+    assert lib.dflash_status_string(0) == b"DFLASH_OK"
+    assert lib.dflash_status_string(3) == b"DFLASH_ERR_WORKSPACE"
+    assert lib.dflash_status_string(99) == b"DFLASH_ERR_UNKNOWN"
+
+
+def test_workspace_and_layout(lib):
+    assert lib.dflash_mla_attn_workspace_bytes(0, 1, 1) == 0
+    assert lib.dflash_mla_attn_workspace_bytes(1, -5, 1) == 0
+    n = lib.dflash_mla_attn_workspace_bytes(1, 4096, 36864)
+    nq, nk = ctypes.c_int64(), ctypes.c_int64()
+    offs = [ctypes.c_size_t() for _ in range(4)]
+    st = lib.dflash_mla_tile_map_layout(1, 4096, 36864, ctypes.byref(nq), ctypes.byref(nk),
+                                        *[ctypes.byref(o) for o in offs])
+    assert st == 0
+    assert (nq.value, nk.value) == (32, 576)
+    c, cnt, lst, order = (o.value for o in offs)
+    assert c == 0 and cnt >= 32 * 576 and lst >= cnt + 32 * 4 and order >= lst + 32 * 576 * 4
+    assert all(x % 256 == 0 for x in (c, cnt, lst, order))
+    assert n >= order + 32 * 4
+    assert lib.dflash_mla_tile_map_layout(1, 0, 5, None, None, None, None, None, None) == 1
+
+
+FAKE = 0x10000  # a 16-byte-aligned address that is never dereferenced (validation fails first)
+
+
+def _attn(lib, **kw):
+    args = dict(q=FAKE, kn=FAKE * 2, kr=FAKE * 3, v=FAKE * 4, mask=None, out=FAKE * 5,
+                B=1, H=2, Lq=32, Lk=96, Dn=128, Dr=64, Dv=128, scale=192 ** -0.5, dt=1, mdt=0,
+                ws=None, wsb=0, flags=0)
+    args.update(kw)
+    return lib.dflash_mla_attn(args["q"], args["kn"], args["kr"], args["v"], args["mask"], args["out"],
+                               args["B"], args["H"], args["Lq"], args["Lk"], args["Dn"], args["Dr"],
+                               args["Dv"], args["scale"], args["dt"], args["mdt"], args["ws"],
+                               args["wsb"], args["flags"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1),                      # null tensor
+    (dict(v=FAKE * 4 + 2), 1),              # misaligned
+    (dict(Lq=0), 1),                        # empty query axis (no zero-row drafts)
+    (dict(B=-1), 1),
+    (dict(scale=0.0), 1),
+    (dict(scale=float("nan")), 1),
+    (dict(scale=float("inf")), 1),
+    (dict(dt=7), 1),
+    (dict(flags=0x80), 1),
+    (dict(Dn=64), 2),                       # head dims this build does not implement
+    (dict(Dr=32), 2),
+    (dict(Dv=64), 2),
+    (dict(dt=0, mdt=1, mask=FAKE * 8), 2),  # f32 attention with a bf16 mask
+    (dict(out=FAKE * 4), 1),                # out aliases v
+    (dict(mask=FAKE * 100), 3),             # masked bf16 call without a workspace
+    (dict(mask=FAKE * 100, ws=FAKE * 400, wsb=16), 3),   # workspace too small
+    (dict(mask=FAKE * 100, ws=FAKE * 400 + 16, wsb=1 << 20), 3),  # workspace misaligned
+])
+def test_attn_validation(lib, kw, status):
+    assert _attn(lib, **kw) == status
+    assert lib.dflash_last_error() != b""
+
+
+def test_expand_validation(lib):
+    f = lib.dflash_mla_latent_expand
+    assert f(None, FAKE, FAKE * 2, FAKE * 3, 1, 4, 512, 2, 128, 128, 1, None) == 1
+    assert f(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, 1, 4, 500, 2, 128, 128, 1, None) == 2   # R % 32
+    assert f(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, 1, 4, 512, 2, 64, 128, 1, None) == 2    # Dn
+    assert f(FAKE, FAKE * 2, FAKE * 3, FAKE * 3, 1, 4, 512, 2, 128, 128, 1, None) == 1   # k_nope aliases v
+    assert f(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, 0, 4, 512, 2, 128, 128, 1, None) == 1
+
+
+def test_occupancy_validation(lib):
+    f = lib.dflash_mla_mask_occupancy
+    assert f(None, 0, 1, 32, 96, FAKE * 256, 1 << 20, None) == 1
+    assert f(FAKE, 0, 1, 32, 96, None, 0, None) == 3
+    assert f(FAKE, 5, 1, 32, 96, FAKE * 256, 1 << 20, None) == 1
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    from dflash_block_draft_amd import mla
+    x = torch.zeros(1, 1, 4, 192)
+    with pytest.raises((ValueError, RuntimeError)):
+        mla.mla_attn(x, x, x, x)

@@ -1,0 +1,286 @@
+"""HIP path vs the fp64 oracle, through the C ABI (gfx950 GPU required).
+
+Tolerances (absolute, on the output): fp32 inputs max|err| <= 1e-5; bf16
+inputs max|err| <= 1.5e-2 and mean|err| <= 1e-3.  The oracle always runs on
+exactly the values the GPU consumed (bf16/f32 upcast to fp64).  Full-size
+workloads are checked on sampled query rows (every q-tile's first and last
+row plus random rows, all heads), which the oracle computes one by one.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dflash_block_draft_amd import mla
+from dflash_block_draft_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_BF16_MAX = 1.5e-2
+TOL_BF16_MEAN = 1e-3
+
+
+def say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    mla.load_library()
+    return torch.device("cuda:0")
+
+
+def _to(dev, *ts):
+    return [None if t is None else t.to(dev) for t in ts]
+
+
+def _err(out_gpu, ref):
+    d = np.abs(out_gpu.detach().to("cpu", torch.float64).numpy() - ref)
+    return float(d.max()), float(d.mean())
+
+
+def _check(out_gpu, ref, dtype, what):
+    mx, mean = _err(out_gpu, ref)
+    say(f"{what}: max|err|={mx:.3e} mean|err|={mean:.3e}")
+    if dtype == "f32":
+        assert mx <= TOL_F32, what
+    else:
+        assert mx <= TOL_BF16_MAX and mean <= TOL_BF16_MEAN, what
+
+
+def _sample_rows(Lq, seed, extra=24):
+    rng = np.random.default_rng(seed)
+    rows = set([0, Lq - 1])
+    for qt in range(0, Lq, mla.TILE_M):
+        rows.update([qt, min(qt + mla.TILE_M - 1, Lq - 1)])
+    rows.update(rng.integers(0, Lq, size=extra).tolist())
+    return np.array(sorted(rows))
+
+
+def _attn_case(dev, wl, rows=None, **kw):
+    say(f"{wl.name}: B={wl.B} H={wl.H} Lq={wl.Lq} Lk={wl.Lk} dtype={wl.dtype} mask={wl.mask_dtype}")
+    q, kn, kr, v, m = _to(dev, wl.q, wl.k_nope, wl.k_rope, wl.v, wl.mask)
+    out = mla.mla_attn(q, kn, kr, v, m, wl.scale, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.mla_attention(wl.q, wl.k_nope, wl.k_rope, wl.v, wl.mask, wl.scale, q_rows=rows)
+    got = out if rows is None else out[:, :, torch.as_tensor(rows, device=dev)]
+    _check(got, ref, wl.dtype, wl.name)
+    return out
+
+
+# ------------------------------------------------------------- the five workloads
+
+def test_config0_f32(dev):
+    _attn_case(dev, W.config(0))
+
+
+def test_config1_expand_then_attention(dev):
+    wl = W.config(1)
+    lat, w, q, kr, m = _to(dev, wl.latent, wl.w_kv_b, wl.q, wl.k_rope, wl.mask)
+    say("config1 expand")
+    kn, v = mla.latent_expand(lat, w, wl.H)
+    torch.cuda.synchronize()
+    ref_kn, ref_v = oracle.latent_expand(wl.latent, wl.w_kv_b, wl.H, wl.Dn, wl.Dv)
+    for name, got, ref in (("k_nope", kn, ref_kn), ("v", v, ref_v)):
+        g = got.to("cpu", torch.float64).numpy()
+        # within one bf16 rounding of the fp64 value: |g - ref| <= 2^-8 |ref| (+ tiny abs)
+        bound = np.abs(ref) * 2.0 ** -8 + 1e-6
+        assert np.all(np.abs(g - ref) <= bound), name
+        say(f"expand {name}: max|err|={np.abs(g - ref).max():.3e}")
+    say("config1 attention on the expanded k/v")
+    out = mla.mla_attn(q, kn, kr, v, m, wl.scale)
+    torch.cuda.synchronize()
+    wl.k_nope, wl.v = kn.cpu(), v.cpu()
+    ref = oracle.mla_attention(wl.q, wl.k_nope, wl.k_rope, wl.v, wl.mask, wl.scale)
+    _check(out, ref, "bf16", "config1 attention")
+    # end to end against the fp64 expansion as well
+    ref_e2e = oracle.mla_attention(wl.q, ref_kn, wl.k_rope, ref_v, wl.mask, wl.scale)
+    _check(out, ref_e2e, "bf16", "config1 end-to-end (fp64 expand)")
+
+
+def test_config2_sampled(dev):
+    wl = W.config(2)
+    _attn_case(dev, wl, rows=_sample_rows(wl.Lq, 2))
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+def test_config3_sampled(dev, bs):
+    wl = W.config(3, block_size=bs)
+    _attn_case(dev, wl, rows=_sample_rows(wl.Lq, 3))
+
+
+def test_config4_sampled(dev):
+    wl = W.config(4)
+    _attn_case(dev, wl, rows=_sample_rows(wl.Lq, 4, extra=16))
+
+
+# ------------------------------------------------------------- ragged and edge cases
+
+@pytest.mark.parametrize("dtype,mdt", [("bf16", "f32"), ("bf16", "bf16"), ("f32", "f32")])
+def test_ragged_tiles(dev, dtype, mdt):
+    # Lq = 35 (one partial q-tile), Lk = 100 + 35 = 135 (three k-tiles, the last partial)
+    wl = W.custom(seed=11, B=2, H=3, ctx=100, A=5, bs=7, dtype=dtype, mask_dtype=mdt)
+    _attn_case(dev, wl)
+
+
+def test_several_tiles_and_ragged_tail(dev):
+    # Lq = 300 (3 q-tiles), Lk = 700 + 300 = 1000 (16 k-tiles, last one 40 wide)
+    wl = W.custom(seed=12, B=1, H=4, ctx=700, A=20, bs=15, dtype="bf16", mask_dtype="f32")
+    _attn_case(dev, wl)
+
+
+def test_odd_lk_scalar_mask_path(dev):
+    # Lk odd: mask rows are not 16-byte aligned -> scalar classification and loads
+    wl = W.custom(seed=13, B=2, H=2, ctx=101, A=4, bs=8, dtype="bf16", mask_dtype="bf16")
+    assert wl.Lk % 2 == 1
+    _attn_case(dev, wl)
+
+
+def test_no_mask_equals_zero_mask_and_oracle(dev):
+    q, kn, kr, v = W.random_attention_inputs(14, 2, 3, 200, 333, dtype="bf16")
+    zero = torch.zeros(2, 1, 200, 333, dtype=torch.float32)
+    qd, knd, krd, vd, zd = _to(dev, q, kn, kr, v, zero)
+    a = mla.mla_attn(qd, knd, krd, vd, None)
+    b = mla.mla_attn(qd, knd, krd, vd, zd)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    ref = oracle.mla_attention(q, kn, kr, v, None, 192 ** -0.5)
+    _check(a, ref, "bf16", "no-mask")
+
+
+def test_general_additive_mask(dev):
+    """Finite non-zero mask values (class-2 tiles everywhere) plus -inf holes."""
+    B, H, Lq, Lk = 2, 2, 160, 300
+    q, kn, kr, v = W.random_attention_inputs(15, B, H, Lq, Lk, dtype="bf16")
+    rng = np.random.default_rng(15)
+    m = rng.standard_normal((B, 1, Lq, Lk)).astype(np.float32) * 3.0
+    m[rng.random(m.shape) < 0.3] = -np.inf
+    m[..., 0] = 0.0
+    for mdt in (torch.float32, torch.bfloat16):
+        mask = torch.from_numpy(m).to(mdt)
+        qd, knd, krd, vd, md = _to(dev, q, kn, kr, v, mask)
+        out = mla.mla_attn(qd, knd, krd, vd, md)
+        torch.cuda.synchronize()
+        ref = oracle.mla_attention(q, kn, kr, v, mask, 192 ** -0.5)
+        _check(out, ref, "bf16", f"general mask {mdt}")
+
+
+def test_fully_masked_rows_and_huge_negatives(dev):
+    B, H, Lq, Lk = 1, 2, 140, 200
+    q, kn, kr, v = W.random_attention_inputs(16, B, H, Lq, Lk, dtype="bf16")
+    m = np.zeros((B, 1, Lq, Lk), dtype=np.float32)
+    m[0, 0, 3, :] = -np.inf                          # fully masked row -> 0
+    m[0, 0, 130:140, :] = -np.inf                    # rows in the partial q-tile, fully masked
+    fmin = np.finfo(np.float32).min
+    m[0, 0, 5, :] = fmin                             # every entry a huge finite negative
+    m[0, 0, 7, 100:] = fmin                          # half visible, half huge negative
+    mask = torch.from_numpy(m)
+    qd, knd, krd, vd, md = _to(dev, q, kn, kr, v, mask)
+    out = mla.mla_attn(qd, knd, krd, vd, md)
+    torch.cuda.synchronize()
+    o = out.cpu()
+    assert torch.all(o[0, :, 3] == 0) and torch.all(o[0, :, 130:140] == 0)
+    ref = oracle.mla_attention(q, kn, kr, v, mask, 192 ** -0.5)
+    _check(out, ref, "bf16", "dead rows / finfo.min rows")
+
+
+def test_single_visible_key_returns_its_value(dev):
+    B, H, Lq, Lk = 2, 3, 64, 130
+    q, kn, kr, v = W.random_attention_inputs(17, B, H, Lq, Lk, dtype="bf16")
+    rng = np.random.default_rng(17)
+    js = rng.integers(0, Lk, size=(B, Lq))
+    m = np.full((B, 1, Lq, Lk), -np.inf, dtype=np.float32)
+    for b in range(B):
+        m[b, 0, np.arange(Lq), js[b]] = 0.0
+    qd, knd, krd, vd, md = _to(dev, q, kn, kr, v, torch.from_numpy(m))
+    out = mla.mla_attn(qd, knd, krd, vd, md)
+    torch.cuda.synchronize()
+    o = out.cpu()
+    for b in range(B):
+        want = v[b][:, torch.as_tensor(js[b])]
+        assert torch.equal(o[b], want)
+
+
+# ------------------------------------------------------------- occupancy, skip, determinism
+
+def test_tile_map_exact(dev):
+    for wl in (W.config(2), W.custom(seed=18, B=3, H=1, ctx=450, A=9, bs=16, mask_dtype="f32")):
+        say(f"tile map {wl.name}")
+        md = wl.mask.to(dev)
+        ws = mla.mask_occupancy(md)
+        torch.cuda.synchronize()
+        tm = mla.tile_map_view(ws, wl.B, wl.Lq, wl.Lk)
+        want = oracle.tile_classes(wl.mask, mla.TILE_M, mla.TILE_N)
+        got = tm["classes"].cpu().numpy()
+        assert np.array_equal(got, want)
+        counts = tm["counts"].cpu().numpy()
+        lists = tm["lists"].cpu().numpy()
+        for b, row in enumerate(oracle.tile_lists(want)):
+            for qt, (idx, cls) in enumerate(row):
+                assert counts[b, qt] == len(idx)
+                ent = lists[b, qt, :len(idx)]
+                assert np.array_equal(ent & 0xFFFFFF, idx) and np.array_equal(ent >> 24, cls)
+        flat = counts.reshape(-1)
+        order = tm["order"].cpu().numpy()
+        want_order = sorted(range(flat.size), key=lambda i: (-flat[i], i))
+        assert list(order) == want_order
+
+
+def test_skip_on_equals_skip_off_bitwise(dev):
+    wl = W.custom(seed=19, B=2, H=4, ctx=900, A=12, bs=16, dtype="bf16", mask_dtype="bf16")
+    q, kn, kr, v, m = _to(dev, wl.q, wl.k_nope, wl.k_rope, wl.v, wl.mask)
+    a = mla.mla_attn(q, kn, kr, v, m, tile_skip=True)
+    b = mla.mla_attn(q, kn, kr, v, m, tile_skip=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_deterministic_and_reuse_tile_map(dev):
+    wl = W.custom(seed=20, B=1, H=8, ctx=1500, A=24, bs=16, dtype="bf16", mask_dtype="f32")
+    q, kn, kr, v, m = _to(dev, wl.q, wl.k_nope, wl.k_rope, wl.v, wl.mask)
+    ws = mla.new_workspace(wl.B, wl.Lq, wl.Lk, dev)
+    a = mla.mla_attn(q, kn, kr, v, m, workspace=ws)
+    b = mla.mla_attn(q, kn, kr, v, m, workspace=ws)
+    q2 = torch.flip(q, dims=[1]).contiguous()               # "next layer": new q, same mask
+    c = mla.mla_attn(q2, kn, kr, v, m, workspace=ws, reuse_tile_map=True)
+    d = mla.mla_attn(q2, kn, kr, v, m)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.equal(c, d)
+
+
+def test_non_default_stream(dev):
+    wl = W.custom(seed=21, B=1, H=2, ctx=300, A=6, bs=16, dtype="bf16", mask_dtype="f32")
+    q, kn, kr, v, m = _to(dev, wl.q, wl.k_nope, wl.k_rope, wl.v, wl.mask)
+    ref = mla.mla_attn(q, kn, kr, v, m)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out = mla.mla_attn(q, kn, kr, v, m)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
+# ------------------------------------------------------------- expand
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_expand_ragged(dev, dtype):
+    rng = np.random.default_rng(22)
+    B, Lk, R, H = 2, 77, 96, 3
+    lat = W.normal(rng, (B, Lk, R), 1.0, dtype)
+    w = W.normal(rng, (H * 256, R), 0.05, dtype)
+    ld, wd = _to(dev, lat, w)
+    kn, v = mla.latent_expand(ld, wd, H)
+    torch.cuda.synchronize()
+    ref_kn, ref_v = oracle.latent_expand(lat, w, H, 128, 128)
+    for got, ref in ((kn, ref_kn), (v, ref_v)):
+        g = got.to("cpu", torch.float64).numpy()
+        if dtype == "f32":
+            assert np.abs(g - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max())
+        else:
+            assert np.all(np.abs(g - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6)
