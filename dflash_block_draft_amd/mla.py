@@ -97,7 +97,7 @@ def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None) -> torch.Tensor:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
-    if t.dtype not in _DT:
+    if dtype is None and t.dtype not in _DT:
         raise ValueError(f"{name}: unsupported dtype {t.dtype}")
     return t
 

@@ -153,7 +153,15 @@ def test_no_mask_equals_zero_mask_and_oracle(dev):
 
 
 def test_general_additive_mask(dev):
-    """Finite non-zero mask values (class-2 tiles everywhere) plus -inf holes."""
+    """Finite non-zero mask values (class-2 tiles everywhere) plus -inf holes.
+
+    Mask values ~ N(0, 3^2) make the softmax far peakier than the DFlash
+    workloads, so the fixed 1.5e-2 bound is replaced by one derived from the
+    arithmetic: rounding each probability to bf16 perturbs a weight by at most
+    2^-9 of itself, moving the output by at most 2^-9 * sum_j p_j |v_j - out|
+    <= 2^-9 * 2 max|v|, and the bf16 output adds 2^-9 |out|.  Bound: 2^-9 *
+    (max|out| + 2 max|v|) * 1.25 (the factor covers fp32 accumulation); the mean
+    bound stays 1e-3."""
     B, H, Lq, Lk = 2, 2, 160, 300
     q, kn, kr, v = W.random_attention_inputs(15, B, H, Lq, Lk, dtype="bf16")
     rng = np.random.default_rng(15)
@@ -166,7 +174,11 @@ def test_general_additive_mask(dev):
         out = mla.mla_attn(qd, knd, krd, vd, md)
         torch.cuda.synchronize()
         ref = oracle.mla_attention(q, kn, kr, v, mask, 192 ** -0.5)
-        _check(out, ref, "bf16", f"general mask {mdt}")
+        mx, mean = _err(out, ref)
+        vmax = float(v.float().abs().max())
+        bound = 2.0 ** -9 * (float(np.abs(ref).max()) + 2.0 * vmax) * 1.25
+        say(f"general mask {mdt}: max|err|={mx:.3e} (derived bound {bound:.3e}) mean|err|={mean:.3e}")
+        assert mx <= bound and mean <= TOL_BF16_MEAN
 
 
 def test_fully_masked_rows_and_huge_negatives(dev):
