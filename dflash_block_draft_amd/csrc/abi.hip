@@ -64,7 +64,7 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 
 struct TileLayout {
   int64_t nqt, nkt;
-  size_t classes, counts, lists, order, total;
+  size_t classes, counts, lists, order, bits, total;
 };
 
 bool tile_layout(int64_t B, int64_t Lq, int64_t Lk, TileLayout* t) {
@@ -77,7 +77,8 @@ bool tile_layout(int64_t B, int64_t Lq, int64_t Lk, TileLayout* t) {
   t->counts = align_up(static_cast<size_t>(cells), 256);
   t->lists = t->counts + align_up(static_cast<size_t>(rows) * 4, 256);
   t->order = t->lists + align_up(static_cast<size_t>(cells) * 4, 256);
-  t->total = t->order + align_up(static_cast<size_t>(rows) * 4, 256);
+  t->bits = t->order + align_up(static_cast<size_t>(rows) * 4, 256);
+  t->total = t->bits + static_cast<size_t>(cells) * DFLASH_TILE_M * 8;
   return true;
 }
 
@@ -107,7 +108,7 @@ size_t dflash_mla_attn_workspace_bytes(int64_t B, int64_t Lq, int64_t Lk) {
 dflash_status dflash_mla_tile_map_layout(int64_t B, int64_t Lq, int64_t Lk, int64_t* n_q_tiles,
                                          int64_t* n_k_tiles, size_t* classes_offset,
                                          size_t* counts_offset, size_t* lists_offset,
-                                         size_t* order_offset) {
+                                         size_t* order_offset, size_t* bits_offset) {
   TileLayout t;
   if (!tile_layout(B, Lq, Lk, &t)) return fail(DFLASH_ERR_INVALID_ARG, "B, Lq, Lk must be positive (got %lld, %lld, %lld)", (long long)B, (long long)Lq, (long long)Lk);
   if (n_q_tiles) *n_q_tiles = t.nqt;
@@ -116,6 +117,7 @@ dflash_status dflash_mla_tile_map_layout(int64_t B, int64_t Lq, int64_t Lk, int6
   if (counts_offset) *counts_offset = t.counts;
   if (lists_offset) *lists_offset = t.lists;
   if (order_offset) *order_offset = t.order;
+  if (bits_offset) *bits_offset = t.bits;
   return ok();
 }
 
@@ -154,6 +156,7 @@ static dflash::OccupancyArgs occupancy_args(const void* mask, int mask_dt, int64
   o.counts = reinterpret_cast<int32_t*>(w + t.counts);
   o.lists = reinterpret_cast<int32_t*>(w + t.lists);
   o.order = reinterpret_cast<int32_t*>(w + t.order);
+  o.bits = reinterpret_cast<uint64_t*>(w + t.bits);
   return o;
 }
 
@@ -293,6 +296,7 @@ dflash_status dflash_mla_attn(const void* q, const void* k_nope, const void* k_r
     a.counts = o.counts;
     a.lists = o.lists;
     a.order = o.order;
+    a.bits = o.bits;
   }
   return hip_status(dflash::launch_attn_bf16(a, s), "bf16 attention launch");
 }

@@ -19,6 +19,7 @@ struct AttnBf16Args {
   const int32_t* counts;  // [B*nqt]
   const int32_t* lists;   // [B*nqt, nkt]
   const int32_t* order;   // [B*nqt]
+  const uint64_t* bits;   // [B*nqt*nkt, 128] visibility words of class-2 tiles
   int B, H, Lq, Lk, nqt, nkt;
   float scale;            // softmax scale (natural units)
   int mask_bf16;          // 1: mask is bf16, 0: f32
@@ -37,6 +38,7 @@ struct OccupancyArgs {
   const void* mask; int mask_bf16;
   int B, Lq, Lk, nqt, nkt;
   uint8_t* classes; int32_t* counts; int32_t* lists; int32_t* order;
+  uint64_t* bits;   // [B*nqt*nkt, kTileM]: bit k of row r = entry (r, k) is +-0 (class-2 tiles only)
 };
 
 struct ExpandArgs {

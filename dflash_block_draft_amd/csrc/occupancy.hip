@@ -3,9 +3,16 @@
 // mask [batch, 1, Lq, ctx+Lq] is added to the scores unchanged) and build, per
 // (batch, q-tile), the ordered list of tiles that contribute anything.
 //
+// Classes: 0 every entry exactly -inf (skipped), 1 every entry +-0 (no mask
+// work), 2 only +-0 and -inf (a 64-bit visibility word per row is written so
+// the attention kernel reads 8 bytes per query instead of the values),
+// 3 anything else (the attention kernel adds the values).
+//
 // The mask is head-independent, so this runs once per call (or once for every
 // draft layer, which all receive the same mask) and is pure HBM streaming:
-// each mask byte is read exactly once with 16-byte loads.
+// each mask row segment is read exactly once, one element per lane, so a wave
+// load covers a full 256 B (f32) / 128 B (bf16) row segment and a ballot of the
+// lanes is directly that row's visibility word.
 #include "common.h"
 #include "launch.h"
 
@@ -13,21 +20,13 @@ namespace dflash {
 namespace {
 
 constexpr int kClassifyThreads = 256;
+constexpr int kClassifyWaves = kClassifyThreads / 64;
 
-// Bit-pattern tests: only exactly -inf is "masked"; +0 and -0 are "zero".
-__device__ __forceinline__ void scan_f32(uint32_t w, bool& all_ninf, bool& all_zero) {
-  all_ninf &= (w == 0xFF800000u);
-  all_zero &= ((w & 0x7FFFFFFFu) == 0u);
-}
-__device__ __forceinline__ void scan_bf16x2(uint32_t w, bool& all_ninf, bool& all_zero) {
-  all_ninf &= (w == 0xFF80FF80u);
-  all_zero &= ((w & 0x7FFF7FFFu) == 0u);
-}
-
-// One workgroup per tile.  Grid x enumerates (b, qt, kt) with kt fastest, so
-// neighbouring workgroups stream neighbouring 256 B (f32) / 128 B (bf16) row segments.
+// One workgroup per tile; grid x enumerates (b, qt, kt) with kt fastest.
 template <bool BF16>
-__global__ void __launch_bounds__(kClassifyThreads) classify_tiles(OccupancyArgs a, int vec_ok) {
+__global__ void __launch_bounds__(kClassifyThreads) classify_tiles(OccupancyArgs a) {
+  __shared__ uint64_t s_vis[kTileM];
+  __shared__ int s_flags[kClassifyWaves];
   const int64_t tile = blockIdx.x;
   const int kt = static_cast<int>(tile % a.nkt);
   const int64_t rest = tile / a.nkt;
@@ -36,50 +35,51 @@ __global__ void __launch_bounds__(kClassifyThreads) classify_tiles(OccupancyArgs
   const int r0 = qt * kTileM, c0 = kt * kTileN;
   const int rows = min(kTileM, a.Lq - r0);
   const int cols = min(kTileN, a.Lk - c0);
-  const int t = threadIdx.x;
-  bool all_ninf = true, all_zero = true;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bool col_ok = lane < cols;
+  const uint64_t valid = cols == 64 ? ~0ull : ((1ull << cols) - 1ull);
 
-  const size_t esz = BF16 ? 2 : 4;
-  const char* base = static_cast<const char*>(a.mask) +
-                     ((static_cast<size_t>(b) * a.Lq + r0) * a.Lk + c0) * esz;
-  const size_t row_bytes = static_cast<size_t>(a.Lk) * esz;
-
-  if (vec_ok && cols == kTileN) {
-    // 16-byte chunks: a 64-wide row is 16 chunks (f32) or 8 chunks (bf16).
-    constexpr int kChunksPerRow = BF16 ? 8 : 16;
-    constexpr int kShift = BF16 ? 3 : 4;
-    constexpr int kChunks = kTileM * kChunksPerRow;
+  // flag bits: 1 = some entry is not -inf, 2 = some entry is not +-0, 4 = some entry is neither
+  int flags = 0;
+  const size_t row0 = (static_cast<size_t>(b) * a.Lq + r0) * a.Lk + c0 + lane;
+  constexpr int kRowsPerWave = kTileM / kClassifyWaves;
+  uint32_t w[kRowsPerWave];
 #pragma unroll
-    for (int i = 0; i < kChunks / kClassifyThreads; ++i) {
-      const int ch = t + i * kClassifyThreads;
-      const int row = ch >> kShift;
-      const int c = ch & (kChunksPerRow - 1);
-      if (row < rows) {
-        const u32x4_t w = ldg16(base + row * row_bytes + c * 16);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (BF16) scan_bf16x2(w[j], all_ninf, all_zero);
-          else scan_f32(w[j], all_ninf, all_zero);
-        }
-      }
-    }
-  } else {
-    const int n = rows * cols;
-    for (int e = t; e < n; e += kClassifyThreads) {
-      const int row = e / cols, col = e % cols;
-      const char* p = base + row * row_bytes + col * esz;
-      if (BF16) {
-        const uint32_t h = *reinterpret_cast<const uint16_t*>(p);
-        all_ninf &= (h == 0xFF80u);
-        all_zero &= ((h & 0x7FFFu) == 0u);
-      } else {
-        scan_f32(*reinterpret_cast<const uint32_t*>(p), all_ninf, all_zero);
-      }
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int r = wave + kClassifyWaves * i;
+    w[i] = 0xFF800000u;  // rows/cols outside the mask read as -inf and are excluded below
+    if (r < rows && col_ok) {
+      const size_t idx = row0 + static_cast<size_t>(r) * a.Lk;
+      w[i] = BF16 ? (static_cast<uint32_t>(static_cast<const uint16_t*>(a.mask)[idx]) << 16)
+                  : static_cast<const uint32_t*>(a.mask)[idx];
     }
   }
-  const int any_not_ninf = __syncthreads_or(!all_ninf);
-  const int any_not_zero = __syncthreads_or(!all_zero);
-  if (t == 0) a.classes[tile] = any_not_ninf ? (any_not_zero ? 2 : 1) : 0;
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int r = wave + kClassifyWaves * i;
+    const bool zero = (w[i] & 0x7FFFFFFFu) == 0u;  // bf16 was shifted into the f32 position
+    const bool ninf = w[i] == 0xFF800000u;
+    const uint64_t vz = __ballot(zero) & valid;
+    const uint64_t vn = __ballot(ninf) & valid;
+    if (r < rows) {
+      const uint64_t other = valid & ~(vz | vn);
+      if ((vz | other) != 0) flags |= 1;
+      if ((vn | other) != 0) flags |= 2;
+      if (other != 0) flags |= 4;
+      if (lane == 0) s_vis[r] = vz;
+    }
+  }
+  if (lane == 0) s_flags[wave] = flags;
+  __syncthreads();
+  int f = 0;
+#pragma unroll
+  for (int i = 0; i < kClassifyWaves; ++i) f |= s_flags[i];
+  const int cls = !(f & 1) ? 0 : (!(f & 2) ? 1 : ((f & 4) ? 3 : 2));
+  if (threadIdx.x == 0) a.classes[tile] = static_cast<uint8_t>(cls);
+  if (cls == 2) {
+    uint64_t* dst = a.bits + static_cast<size_t>(tile) * kTileM;
+    for (int r = threadIdx.x; r < kTileM; r += kClassifyThreads) dst[r] = r < rows ? s_vis[r] : 0ull;
+  }
 }
 
 // One workgroup: (1) each wave compacts the non-empty k-tiles of its
@@ -130,13 +130,10 @@ __global__ void __launch_bounds__(kListThreads) build_lists(OccupancyArgs a) {
 
 hipError_t launch_occupancy(const OccupancyArgs& a, hipStream_t s) {
   const int64_t ntiles = static_cast<int64_t>(a.B) * a.nqt * a.nkt;
-  const size_t esz = a.mask_bf16 ? 2 : 4;
-  const int vec_ok = ((static_cast<size_t>(a.Lk) * esz) % 16 == 0) &&
-                     (reinterpret_cast<uintptr_t>(a.mask) % 16 == 0);
   if (a.mask_bf16)
-    hipLaunchKernelGGL(classify_tiles<true>, dim3(static_cast<unsigned>(ntiles)), dim3(kClassifyThreads), 0, s, a, vec_ok);
+    hipLaunchKernelGGL(classify_tiles<true>, dim3(static_cast<unsigned>(ntiles)), dim3(kClassifyThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(classify_tiles<false>, dim3(static_cast<unsigned>(ntiles)), dim3(kClassifyThreads), 0, s, a, vec_ok);
+    hipLaunchKernelGGL(classify_tiles<false>, dim3(static_cast<unsigned>(ntiles)), dim3(kClassifyThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(build_lists, dim3(1), dim3(kListThreads), 0, s, a);

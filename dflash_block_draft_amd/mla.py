@@ -64,7 +64,7 @@ def load_library() -> ctypes.CDLL:
     lib.dflash_mla_attn_workspace_bytes.argtypes = [i64, i64, i64]
     lib.dflash_mla_attn_workspace_bytes.restype = sz
     p64, psz = ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_size_t)
-    lib.dflash_mla_tile_map_layout.argtypes = [i64, i64, i64, p64, p64, psz, psz, psz, psz]
+    lib.dflash_mla_tile_map_layout.argtypes = [i64, i64, i64, p64, p64, psz, psz, psz, psz, psz]
     lib.dflash_mla_tile_map_layout.restype = i32
     lib.dflash_mla_mask_occupancy.argtypes = [vp, i32, i64, i64, i64, vp, sz, vp]
     lib.dflash_mla_mask_occupancy.restype = i32
@@ -159,11 +159,11 @@ def tile_map_view(workspace: torch.Tensor, B: int, Lq: int, Lk: int) -> dict:
     """Views of the occupancy results inside a workspace (see dflash_mla_tile_map_layout)."""
     lib = load_library()
     nq, nk = ctypes.c_int64(), ctypes.c_int64()
-    offs = [ctypes.c_size_t() for _ in range(4)]
+    offs = [ctypes.c_size_t() for _ in range(5)]
     _check(lib.dflash_mla_tile_map_layout(B, Lq, Lk, ctypes.byref(nq), ctypes.byref(nk),
                                           *[ctypes.byref(o) for o in offs]))
     nq, nk = nq.value, nk.value
-    c_off, n_off, l_off, o_off = (o.value for o in offs)
+    c_off, n_off, l_off, o_off, b_off = (o.value for o in offs)
     ws = workspace
     return {
         "n_q_tiles": nq, "n_k_tiles": nk,
@@ -171,6 +171,7 @@ def tile_map_view(workspace: torch.Tensor, B: int, Lq: int, Lk: int) -> dict:
         "counts": ws[n_off:n_off + 4 * B * nq].view(torch.int32).view(B, nq),
         "lists": ws[l_off:l_off + 4 * B * nq * nk].view(torch.int32).view(B, nq, nk),
         "order": ws[o_off:o_off + 4 * B * nq].view(torch.int32),
+        "bits": ws[b_off:b_off + 8 * B * nq * nk * TILE_M].view(torch.int64).view(B, nq, nk, TILE_M),
     }
 
 

@@ -59,9 +59,11 @@ typedef enum dflash_dtype {
 #define DFLASH_TILE_N 64
 
 /* Tile classes stored in the occupancy map (one byte per tile). */
-#define DFLASH_TILE_EMPTY 0   /* every mask entry is exactly -inf: the tile is skipped      */
-#define DFLASH_TILE_ZERO 1    /* every mask entry is +0 or -0: no mask load, no mask add    */
-#define DFLASH_TILE_MIXED 2   /* anything else: the mask tile is loaded and added           */
+#define DFLASH_TILE_EMPTY 0   /* every mask entry is exactly -inf: the tile is skipped            */
+#define DFLASH_TILE_ZERO 1    /* every mask entry is +0 or -0: no mask load, no mask add          */
+#define DFLASH_TILE_BINARY 2  /* only +-0 and -inf, both present: a 64-bit visibility word per    */
+                              /* row is stored in the workspace and applied instead of the values */
+#define DFLASH_TILE_MIXED 3   /* anything else: the mask values are loaded and added              */
 
 /* dflash_mla_attn flags */
 #define DFLASH_ATTN_REUSE_TILE_MAP 0x1u  /* skip the occupancy pass: the workspace already holds
@@ -110,19 +112,25 @@ size_t dflash_mla_attn_workspace_bytes(int64_t B, int64_t Lq, int64_t Lk);
 
 /*
  * Where the occupancy results sit inside the workspace, so a caller can read
- * them back (all offsets in bytes from the workspace start):
- *   classes  uint8 [B, n_q_tiles, n_k_tiles]   DFLASH_TILE_* per tile
- *   counts   int32 [B, n_q_tiles]              non-empty k-tiles per q-tile
- *   lists    int32 [B, n_q_tiles, n_k_tiles]   first counts[] entries: k-tile index | class << 24,
- *                                              in increasing k order
- *   order    int32 [B * n_q_tiles]             (b * n_q_tiles + q-tile) by decreasing count,
- *                                              ties by increasing index
+ * them back (all offsets in bytes from the workspace start; any output pointer
+ * may be NULL):
+ *   classes  uint8  [B, n_q_tiles, n_k_tiles]   DFLASH_TILE_* per tile
+ *   counts   int32  [B, n_q_tiles]              non-empty k-tiles per q-tile
+ *   lists    int32  [B, n_q_tiles, n_k_tiles]   first counts[] entries: k-tile index | class << 24,
+ *                                               in increasing k order
+ *   order    int32  [B * n_q_tiles]             (b * n_q_tiles + q-tile) by decreasing count,
+ *                                               ties by increasing index
+ *   bits     uint64 [B, n_q_tiles, n_k_tiles, DFLASH_TILE_M]   for DFLASH_TILE_BINARY tiles only:
+ *                                               bit k of row r is set iff mask entry
+ *                                               (qt*M + r, kt*N + k) is +-0 (rows/columns past
+ *                                               the mask read 0); other tiles' words are unspecified
  * n_q_tiles = ceil(Lq / DFLASH_TILE_M), n_k_tiles = ceil(Lk / DFLASH_TILE_N).
  */
 dflash_status dflash_mla_tile_map_layout(int64_t B, int64_t Lq, int64_t Lk,
                                          int64_t* n_q_tiles, int64_t* n_k_tiles,
                                          size_t* classes_offset, size_t* counts_offset,
-                                         size_t* lists_offset, size_t* order_offset);
+                                         size_t* lists_offset, size_t* order_offset,
+                                         size_t* bits_offset);
 
 /*
  * The mask-occupancy pass alone: classify every DFLASH_TILE_M x DFLASH_TILE_N
@@ -130,7 +138,8 @@ dflash_status dflash_mla_tile_map_layout(int64_t B, int64_t Lq, int64_t Lk,
  * Tile of (b, qt, kt): rows [qt*M, min(qt*M+M, Lq)), columns [kt*N, min(kt*N+N, Lk))
  * of mask[b, 0]; entries outside the mask do not count.  Classes compare bit
  * patterns: exactly -inf is "masked"; +0/-0 is "zero"; everything else,
- * including NaN, +inf and large finite negatives, is "mixed".
+ * including NaN, +inf and large finite negatives, is a "value" and makes the
+ * tile DFLASH_TILE_MIXED.
  *
  * additive_mask [B, 1, Lq, Lk] in mask_dt (F32 or BF16).
  * The pages pass the same mask to every draft layer (DFlash page,

@@ -22,8 +22,9 @@ What it computes, and the passages it follows:
   qk_nope_head_dim + v_head_dim outputs.  Same class texts; latent width from the
   Kimi K3 model page (MLA context-parallel forward: kv_lora_rank + qk_rope_head_dim
   values per token).
-* ``occupancy.tile_classes`` / ``occupancy.tile_lists`` -- the integer tile
-  classification of an additive mask (all -inf / all zero / anything else)
+* ``occupancy.tile_classes`` / ``tile_lists`` / ``tile_bits`` -- the integer tile
+  classification of an additive mask (all -inf / all zero / only zeros and
+  -inf / anything else) and the per-row visibility words of binary tiles
   that the method uses to skip fully masked tiles.  The pages only require
   that the score matrix is never materialised (KimiK3DFlashAttention.forward);
   the classification is defined here by its plain meaning.
@@ -37,4 +38,4 @@ a library routine) -- nothing here is "parity unpinned".
 """
 from .attention import mla_attention, softmax_weights  # noqa: F401
 from .expand import latent_expand  # noqa: F401
-from .occupancy import tile_classes, tile_lists  # noqa: F401
+from .occupancy import tile_bits, tile_classes, tile_lists  # noqa: F401

@@ -296,11 +296,25 @@ def pin_occupancy_brute_force():
                     want = 0
                 elif all(x == 0.0 for x in vals):
                     want = 1
-                else:
+                elif all(x == 0.0 or x == -math.inf for x in vals):
                     want = 2
+                else:
+                    want = 3
                 assert cls[b, qt, kt] == want, (b, qt, kt)
     assert cls[0, 0, 0] == 0 and cls[0, 1, 1] == 1 and cls[0, 1, 2] == 1 and cls[1, 2, 4] == 0
-    assert cls[1, 1, 0] == 2 and cls[1, 0, 2] == 2
+    assert cls[1, 1, 0] == 3 and cls[1, 0, 2] == 3            # NaN / +inf make a tile "values"
+    assert (cls == 2).sum() > 0                                # the random 0/-inf tiles are binary
+    bits = oracle.tile_bits(m, BM, BN, cls)
+    for b, qt, kt in zip(*np.nonzero(cls == 2)):
+        for r in range(BM):
+            i = qt * BM + r
+            want = 0
+            if i < Lq:
+                for k in range(BN):
+                    j = kt * BN + k
+                    if j < Lk and m[b, 0, i, j] == 0.0:
+                        want += 2 ** k
+            assert int(bits[b, qt, kt, r]) == want, (b, qt, kt, r)
     lists = oracle.tile_lists(cls)
     for b in range(B):
         for qt in range(3):

@@ -56,16 +56,17 @@ def test_workspace_and_layout(lib):
     assert lib.dflash_mla_attn_workspace_bytes(1, -5, 1) == 0
     n = lib.dflash_mla_attn_workspace_bytes(1, 4096, 36864)
     nq, nk = ctypes.c_int64(), ctypes.c_int64()
-    offs = [ctypes.c_size_t() for _ in range(4)]
+    offs = [ctypes.c_size_t() for _ in range(5)]
     st = lib.dflash_mla_tile_map_layout(1, 4096, 36864, ctypes.byref(nq), ctypes.byref(nk),
                                         *[ctypes.byref(o) for o in offs])
     assert st == 0
     assert (nq.value, nk.value) == (32, 576)
-    c, cnt, lst, order = (o.value for o in offs)
+    c, cnt, lst, order, bits = (o.value for o in offs)
     assert c == 0 and cnt >= 32 * 576 and lst >= cnt + 32 * 4 and order >= lst + 32 * 576 * 4
-    assert all(x % 256 == 0 for x in (c, cnt, lst, order))
-    assert n >= order + 32 * 4
-    assert lib.dflash_mla_tile_map_layout(1, 0, 5, None, None, None, None, None, None) == 1
+    assert bits >= order + 32 * 4
+    assert all(x % 256 == 0 for x in (c, cnt, lst, order, bits))
+    assert n >= bits + 32 * 576 * 128 * 8
+    assert lib.dflash_mla_tile_map_layout(1, 0, 5, None, None, None, None, None, None, None) == 1
 
 
 FAKE = 0x10000  # a 16-byte-aligned address that is never dereferenced (validation fails first)

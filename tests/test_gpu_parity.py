@@ -240,6 +240,11 @@ def test_tile_map_exact(dev):
         order = tm["order"].cpu().numpy()
         want_order = sorted(range(flat.size), key=lambda i: (-flat[i], i))
         assert list(order) == want_order
+        want_bits = oracle.tile_bits(wl.mask, mla.TILE_M, mla.TILE_N, want)
+        got_bits = tm["bits"].cpu().numpy().view(np.uint64)
+        sel = want == 2
+        assert sel.sum() > 0
+        assert np.array_equal(got_bits[sel], want_bits[sel])
 
 
 def test_skip_on_equals_skip_off_bitwise(dev):

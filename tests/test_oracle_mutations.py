@@ -110,8 +110,23 @@ def _classes_square_tiles(mask, BM, BN):
     return _orig_classes(mask, BM, BM)
 
 
+def _classes_binary_as_values(mask, BM, BN):
+    out = _orig_classes(mask, BM, BN)
+    out[out == 2] = 3
+    return out
+
+
+def _bits_transposed(mask, BM, BN, classes):
+    out = _orig_bits(mask, BM, BN, classes)
+    rev = np.zeros_like(out)
+    for k in range(BN):
+        rev |= ((out >> np.uint64(k)) & np.uint64(1)) << np.uint64(BN - 1 - k)
+    return rev
+
+
 _orig_attn = oracle.mla_attention
 _orig_classes = oracle.tile_classes
+_orig_bits = oracle.tile_bits
 
 MUTANTS = {
     "drop_rope_term": [(oatt, "_scores", _scores_no_rope)],
@@ -129,6 +144,8 @@ MUTANTS = {
     "occupancy_neg_zero": [(oracle, "tile_classes", _classes_positive_zero_only)],
     "occupancy_nan_masked": [(oracle, "tile_classes", _classes_nan_as_masked)],
     "occupancy_square_tiles": [(oracle, "tile_classes", _classes_square_tiles)],
+    "occupancy_binary_as_values": [(oracle, "tile_classes", _classes_binary_as_values)],
+    "occupancy_bits_reversed": [(oracle, "tile_bits", _bits_transposed)],
 }
 
 
