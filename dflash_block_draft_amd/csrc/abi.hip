@@ -277,8 +277,10 @@ dflash_status dflash_mla_attn(const void* q, const void* k_nope, const void* k_r
   a.nkt = static_cast<int>((Lk + DFLASH_TILE_N - 1) / DFLASH_TILE_N);
   a.scale = scale;
   a.mask_bf16 = mask_dt == DFLASH_BF16;
-  a.no_skip = (flags & DFLASH_ATTN_NO_TILE_SKIP) ? 1 : 0;
   if (static_cast<int64_t>(B) * a.nqt * H > INT32_MAX) return fail(DFLASH_ERR_UNSUPPORTED, "too many work items");
+  if (additive_mask && a.nkt > dflash::kLdsListMax)
+    return fail(DFLASH_ERR_UNSUPPORTED, "a masked bf16 call supports at most %d key tiles (Lk <= %d), got Lk = %lld",
+                dflash::kLdsListMax, dflash::kLdsListMax * DFLASH_TILE_N, (long long)Lk);
   if (additive_mask) {
     TileLayout t;
     dflash_status st = check_occupancy_args(additive_mask, mask_dt, B, Lq, Lk, workspace, workspace_bytes, &t);
@@ -290,6 +292,10 @@ dflash_status dflash_mla_attn(const void* q, const void* k_nope, const void* k_r
     const dflash::OccupancyArgs o = occupancy_args(additive_mask, mask_dt, B, Lq, Lk, workspace, t);
     if (!(flags & DFLASH_ATTN_REUSE_TILE_MAP)) {
       st = hip_status(dflash::launch_occupancy(o, s), "mask occupancy launch");
+      if (st != DFLASH_OK) return st;
+    }
+    if (flags & DFLASH_ATTN_NO_TILE_SKIP) {
+      st = hip_status(dflash::launch_lists_all_tiles(o, s), "tile list rewrite launch");
       if (st != DFLASH_OK) return st;
     }
     a.classes = o.classes;

@@ -7,23 +7,26 @@
 // over the keys [context | noise block], with no materialised score matrix.
 //
 // Decomposition (one workgroup = one (batch, head, 128-query tile)):
-//  * 8 waves: wave w owns queries 32*(w&3) .. +31 of the tile and keys
-//    32*(w>>2) .. +31 of every 64-key tile; the two waves of a query group
-//    merge (m, l, O) once at the end.  Two waves per SIMD, so one wave's
-//    softmax overlaps the other's MFMAs.
+//  * 8 waves, two per SIMD: wave w owns queries 32*(w&3) .. +31 of the tile
+//    and keys 32*(w>>2) .. +31 of every 64-key tile; the two waves of a query
+//    group share a SIMD and merge (m, l, O) once at the end.
+//  * The two waves of a SIMD run half an iteration apart: the key-half-1 wave
+//    computes the scores of tile i+1 at the end of iteration i, so while one
+//    wave runs its score MFMAs the other runs its softmax on the VALU.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
-//    a lane then holds one query and 16 of its keys, so row max / row sum are
+//    a lane holds one query and 16 of its keys, so row max / row sum are
 //    in-lane (plus one v_permlane32_swap), and the lane's P^T values are
 //    already the B operand of O^T = V^T P^T for the same key order (the order
 //    of the key contraction is free, so keys are relabelled to match the
 //    accumulator layout).
-//  * V^T operands come straight from the row-major V tile with the gfx950
-//    transposing LDS read (ds_read_b64_tr_b16); V rows are padded to 320 B so
-//    those reads are bank-conflict free, K rows to 400 B for the b128 reads.
+//  * V^T operands come straight from the V tile with the gfx950 transposing
+//    LDS read (ds_read_b64_tr_b16).
+//  * K = [k_nope | head-shared k_rope] and V tiles go global -> LDS with
+//    buffer_load ... lds (no VGPR staging, rows past Lk read as zero), into
+//    three rotating stages so one barrier per tile suffices.  LDS tiles are
+//    blocks of 16 rows x 64 B, the K chunks XOR-swizzled so the MFMA operand
+//    reads are bank-conflict free while the loads stay 64-byte coalesced.
 //  * Q (32 x 192 bf16 per wave) stays in registers for the whole key loop.
-//  * K = [k_nope | k_rope] and V tiles are staged in LDS, double-buffered,
-//    with 16-byte coalesced loads; the head-shared k_rope tile is stored next
-//    to this head's k_nope so one LDS row feeds the whole 192-wide contraction.
 //  * Online softmax in fp32 with the hardware exp2; the running max is only
 //    raised when a new score exceeds it by more than 2^8 in probability space
 //    ("lazy rescale"), exact because the same max scales both O and l.
@@ -38,16 +41,18 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kKsStride = kDqk + 8;               // bf16 per LDS K row (400 B)
-constexpr int kVsStride = kDv + 32;               // bf16 per LDS V row (320 B)
-constexpr int kKsTile = kTileN * kKsStride;
-constexpr int kVsTile = kTileN * kVsStride;
-constexpr int kStageElems = kKsTile + kVsTile;     // one buffer
-constexpr float kLazyTau = 8.0f / kLog2e;          // natural-units slack before a rescale
+constexpr int kKTileBytes = kTileN * kDqk * 2;      // 24 KiB: 4 row blocks x 6 chunk quads x 1 KiB
+constexpr int kVTileBytes = kTileN * kDv * 2;       // 16 KiB: 4 row blocks x 4 chunk quads x 1 KiB
+constexpr int kStageBytes = kKTileBytes + kVTileBytes;
+constexpr int kStages = 3;
+constexpr float kLazyTau = 8.0f / kLog2e;            // natural-units slack before a rescale
 constexpr uint32_t kNegInfBits = 0xFF800000u;
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
 
 // max / sum of x over lanes l and l ^ 32
 __device__ __forceinline__ float halves_max(float x) {
@@ -61,52 +66,55 @@ __device__ __forceinline__ float halves_sum(float x) {
 
 // Transposing LDS read: within each 16-lane group, lane i receives element i%4
 // of the 8-byte rows addressed by lanes i/4, 4+i/4, 8+i/4, 12+i/4.
-__device__ __forceinline__ s16x4_t ds_read_tr(const uint16_t* p) {
+__device__ __forceinline__ s16x4_t ds_read_tr(const lds_char_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
 }
 
-struct Stage {
-  u32x4_t kn0, kn1, kr, v0, v1;
-};
+// s_waitcnt vmcnt(0) (expcnt/lgkmcnt fields left at their no-wait maxima).  The
+// builtin, unlike inline asm, also tells the compiler's wait-count model that its
+// own vector loads are complete, so it does not wait for them again later.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Global -> registers for the key tile starting at k0 (zero rows past Lk).
-__device__ __forceinline__ void load_stage(Stage& st, const uint16_t* kn_bh, const uint16_t* kr_b,
-                                           const uint16_t* v_bh, int k0, int Lk, int t) {
-  const u32x4_t z = {0u, 0u, 0u, 0u};
-  {
-    const int row = t >> 4, c = t & 15;
-    const bool ok = k0 + row < Lk;
-    st.kn0 = ok ? ldg16(kn_bh + static_cast<size_t>(k0 + row) * kDn + c * 8) : z;
-    st.v0 = ok ? ldg16(v_bh + static_cast<size_t>(k0 + row) * kDv + c * 8) : z;
-  }
-  {
-    const int row = 32 + (t >> 4), c = t & 15;
-    const bool ok = k0 + row < Lk;
-    st.kn1 = ok ? ldg16(kn_bh + static_cast<size_t>(k0 + row) * kDn + c * 8) : z;
-    st.v1 = ok ? ldg16(v_bh + static_cast<size_t>(k0 + row) * kDv + c * 8) : z;
-  }
-  {
-    const int row = t >> 3, c = t & 7;
-    st.kr = (k0 + row < Lk) ? ldg16(kr_b + static_cast<size_t>(k0 + row) * kDr + c * 8) : z;
-  }
+// 16 bytes per lane from a buffer straight into LDS at lds_addr + 16*lane; reads past
+// the descriptor's num_records return zeros.  Issued as inline asm so the compiler
+// does not treat the in-flight LDS write as a dependency of unrelated LDS reads
+// (it would otherwise wait for it before every ds_read); completion is awaited
+// explicitly with wait_vmem() before the barrier that publishes the stage.  No
+// memory clobber: the stage it writes is not read before that barrier, and a
+// clobber would stop the compiler from using scalar loads for the tile lists.
+__device__ __forceinline__ void dma16(u32x4_t rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr));
 }
 
-__device__ __forceinline__ void store_stage(const Stage& st, uint16_t* buf, int t) {
-  uint16_t* Ks = buf;
-  uint16_t* Vs = buf + kKsTile;
-  {
-    const int row = t >> 4, c = t & 15;
-    stg16(Ks + row * kKsStride + c * 8, st.kn0);
-    stg16(Vs + row * kVsStride + c * 8, st.v0);
-  }
-  {
-    const int row = 32 + (t >> 4), c = t & 15;
-    stg16(Ks + row * kKsStride + c * 8, st.kn1);
-    stg16(Vs + row * kVsStride + c * 8, st.v1);
-  }
-  {
-    const int row = t >> 3, c = t & 7;
-    stg16(Ks + row * kKsStride + kDn + c * 8, st.kr);
+__device__ __forceinline__ u32x4_t buffer_desc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  u32x4_t d = {static_cast<uint32_t>(p), static_cast<uint32_t>(p >> 32) & 0xFFFFu, bytes, 0x00020000u};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[i] = __builtin_amdgcn_readfirstlane(d[i]);
+  return d;
+}
+
+// LDS tile layout (both K and V): row block rb (16 rows), chunk quad cq (4 x 16 B
+// chunks) -> 1 KiB block (rb * nq + cq); inside it row r%16 takes 64 B, and
+// 16-byte chunk c%4 of that row sits at slot (c%4) ^ swz(r), with
+// swz(r) = (r >> 2) & 3 for K and 0 for V.
+//
+// Per-wave global -> LDS copy of one 64-key tile: 3 K blocks and 2 V blocks,
+// lane l of a block covers row rb*16 + l/4 and slot l%4.
+struct TileCopy {
+  u32x4_t kn, kr, v;
+  uint32_t voff[5];      // per-lane byte offset inside the source slice (tile start excluded)
+  int lds_off[5];        // block offset inside a stage
+  int kind[5];           // 0 k_nope, 1 k_rope, 2 v
+};
+
+__device__ __forceinline__ void issue_tile(const TileCopy& tc, uint32_t stage, int k0) {
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const u32x4_t rs = tc.kind[i] == 0 ? tc.kn : (tc.kind[i] == 1 ? tc.kr : tc.v);
+    const int row_bytes = tc.kind[i] == 1 ? kDr * 2 : kDn * 2;
+    dma16(rs, stage + tc.lds_off[i], tc.voff[i], k0 * row_bytes);
   }
 }
 
@@ -118,11 +126,14 @@ __device__ __forceinline__ float load_mask(const void* mask, size_t idx) {
 
 template <bool MASK_BF16>
 __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStageElems];
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
+  __shared__ int s_list[kLdsListMax];
+  lds_char_t* const lds = (lds_char_t*)smem;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
 
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: keeps buffer descriptors scalar
   const int qg = wave & 3;      // query group: 32 queries
   const int kh = wave >> 2;     // key half of each 64-key tile
   const int li = lane & 31;
@@ -134,16 +145,52 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
   const int bq = a.order ? a.order[rank] : rank;
   const int b = bq / a.nqt;
   const int qt = bq % a.nqt;
-  const int ntiles = a.counts ? (a.no_skip ? a.nkt : a.counts[bq]) : a.nkt;
+  const int ntiles = a.counts ? a.counts[bq] : a.nkt;
 
   const size_t bh = static_cast<size_t>(b) * a.H + h;
-  const uint16_t* kn_bh = a.kn + bh * a.Lk * kDn;
-  const uint16_t* v_bh = a.v + bh * a.Lk * kDv;
-  const uint16_t* kr_b = a.kr + static_cast<size_t>(b) * a.Lk * kDr;
-
   const int q_local = qg * 32 + li;               // this lane's query within the tile
   const int q_row = qt * kTileM + q_local;
   const bool q_ok = q_row < a.Lq;
+
+  // ---- global -> LDS copy plan of this wave
+  TileCopy tc;
+  tc.kn = buffer_desc(a.kn + bh * a.Lk * kDn, a.Lk * kDn * 2);
+  tc.kr = buffer_desc(a.kr + static_cast<size_t>(b) * a.Lk * kDr, a.Lk * kDr * 2);
+  tc.v = buffer_desc(a.v + bh * a.Lk * kDv, a.Lk * kDv * 2);
+  {
+    const int r16 = lane >> 2, s4 = lane & 3;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {            // K blocks 3w .. 3w+2 of 24 (4 row blocks x 6 quads)
+      const int blk = 3 * wave + i, rb = blk / 6, cq = blk % 6;
+      const int row = rb * 16 + r16;
+      const int chunk = cq * 4 + (s4 ^ ((r16 >> 2) & 3));
+      tc.lds_off[i] = blk * 1024;
+      if (cq < 4) { tc.kind[i] = 0; tc.voff[i] = row * (kDn * 2) + chunk * 16; }        // k_nope dims
+      else { tc.kind[i] = 1; tc.voff[i] = row * (kDr * 2) + (chunk - 16) * 16; }      // k_rope dims
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {            // V blocks 2w, 2w+1 of 16 (4 row blocks x 4 quads)
+      const int blk = 2 * wave + i, rb = blk / 4, cq = blk % 4;
+      const int row = rb * 16 + r16;
+      tc.lds_off[3 + i] = kKTileBytes + blk * 1024;
+      tc.kind[3 + i] = 2;
+      tc.voff[3 + i] = row * (kDv * 2) + (cq * 4 + s4) * 16;
+    }
+  }
+
+  // ---- per-lane LDS read offsets (bytes inside a stage)
+  // K operand of chunk c (dims 16c .. 16c+15): lane reads 16-dim row kh*32+li, 16-byte
+  // chunk 2c+hi -> block (rb*6 + c/2), slot (2*(c&1) + hi) ^ swz(row).
+  const int krow = kh * 32 + li;
+  const int kq = (li >> 2) & 3;
+  const int k_even = ((krow >> 4) * 6) * 1024 + (krow & 15) * 64 + ((hi) ^ kq) * 16;
+  const int k_odd = ((krow >> 4) * 6) * 1024 + (krow & 15) * 64 + ((2 + hi) ^ kq) * 16;
+  // V^T operand (transposing read): lane i of 16-lane group G addresses row
+  // kh*32 + 16*step + 4*hi + i/4 (+8), dims 32*j + 16*(G&1) + 4*(i&3).
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int vrow = kh * 32 + 4 * hi + (i16 >> 2);
+  const int v_base = kKTileBytes + ((vrow >> 4) * 4) * 1024 + (vrow & 15) * 64 + (2 * (g16 & 1) + ((i16 & 3) >> 1)) * 16 +
+                     (i16 & 1) * 8;
 
   // ---- Q fragments (B operand of S^T = K Q^T): 12 chunks of 16 dims
   bf16x8_t qf[kDqk / 16];
@@ -169,84 +216,91 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
   const size_t mask_row = (static_cast<size_t>(b) * a.Lq + (q_ok ? q_row : 0)) * a.Lk;
   const size_t tile_row0 = static_cast<size_t>(bq) * a.nkt;
 
-  auto tile_at = [&](int i, int& kt, int& cls) {
-    if (!a.counts) { kt = i; cls = 1; return; }
-    if (a.no_skip) {
-      kt = i;
-      const int c = a.classes[tile_row0 + i];
-      cls = c == 0 ? 3 : c;
-      return;
-    }
-    const int e = a.lists[tile_row0 + i];
-    kt = e & 0xFFFFFF;
-    cls = e >> 24;
+  // list entry of tile i: k-tile index | class << 24 (all zero-class when there is no mask).
+  // The q-tile's list is copied to LDS once (published by the prologue barrier).
+  // (The host rejects masked calls with more than kLdsListMax k-tiles.)
+  const int32_t* list = a.counts ? a.lists + tile_row0 : nullptr;
+  if (list)
+    for (int i = t; i < ntiles; i += kThreads) s_list[i] = list[i];
+  auto entry = [&](int i) -> int {
+    if (i >= ntiles) return 0;
+    if (!list) return i | (1 << 24);
+    return __builtin_amdgcn_readfirstlane(s_list[i]);
   };
-  auto load_bits = [&](int kt, int cls) -> uint32_t {
-    if (cls != 2) return 0u;
-    const uint64_t w = a.bits[(tile_row0 + kt) * kTileM + q_local];
-    return static_cast<uint32_t>(w >> (kh * 32 + 4 * hi));   // bit 8g+c <-> key kh*32 + 8g + 4hi + c
+  // visibility word of this lane's query in a class-2 tile (raw; shifted where it is used
+  // so the load stays in flight until then)
+  auto load_bits = [&](int e) -> uint64_t {
+    if ((e >> 24) != 2) return 0ull;
+    return a.bits[(tile_row0 + (e & 0xFFFFFF)) * kTileM + q_local];
   };
-
-  // per-lane LDS offsets (elements)
-  const int k_off = (kh * 32 + li) * kKsStride + 8 * hi;
-  const int g16 = lane >> 4, i16 = lane & 15;
-  const int v_off = (kh * 32 + 4 * hi + (i16 >> 2)) * kVsStride + 16 * (g16 & 1) + 4 * (i16 & 3);
-
-  Stage st;
-  int kt_cur = 0, cls_cur = 1;
-  uint32_t bits_cur = 0u;
-  if (ntiles > 0) {
-    tile_at(0, kt_cur, cls_cur);
-    load_stage(st, kn_bh, kr_b, v_bh, kt_cur * kTileN, a.Lk, t);
-    bits_cur = load_bits(kt_cur, cls_cur);
-    store_stage(st, smem, t);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int k0 = kt_cur * kTileN;
-    const bool has_next = it + 1 < ntiles;
-    int kt_nxt = 0, cls_nxt = 1;
-    uint32_t bits_nxt = 0u;
-    if (has_next) {
-      tile_at(it + 1, kt_nxt, cls_nxt);
-      load_stage(st, kn_bh, kr_b, v_bh, kt_nxt * kTileN, a.Lk, t);
-      bits_nxt = load_bits(kt_nxt, cls_nxt);
-    }
-    const uint16_t* Ks = smem + (it & 1) * kStageElems;
-    const uint16_t* Vs = Ks + kKsTile;
-
-    // ---- S^T block: keys kh*32 + (rows), queries qg*32 + li
+  auto scores = [&](const lds_char_t* stage) {
+    const lds_char_t* ke = stage + k_even;
+    const lds_char_t* ko = stage + k_odd;
     f32x16_t s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
     for (int c = 0; c < kDqk / 16; ++c) {
-      const bf16x8_t kf = as_bf16x8(*reinterpret_cast<const u32x4_t*>(Ks + k_off + 16 * c));
+      const lds_char_t* kp = ((c & 1) ? ko : ke) + (c >> 1) * 1024;
+      const bf16x8_t kf = as_bf16x8(*reinterpret_cast<const lds_u32x4_t*>(kp));
       s = mfma32(kf, qf[c], s);
     }
+    return s;
+  };
+
+  // ---- prologue: tiles 0 and 1 in flight, key-half-1 waves score tile 0
+  __syncthreads();                                              // s_list visible
+  int e_cur = entry(0), e_nxt = entry(1), e_nxt2 = entry(2);   // tiles it, it+1, it+2
+  uint64_t bits_cur = load_bits(e_cur);
+  if (ntiles > 0) issue_tile(tc, lds0, (e_cur & 0xFFFFFF) * kTileN);
+  if (ntiles > 1) issue_tile(tc, lds0 + kStageBytes, (e_nxt & 0xFFFFFF) * kTileN);
+  wait_vmem();
+  __syncthreads();
+  f32x16_t s;
+  if (kh == 1 && ntiles > 0) s = scores(lds);
+
+  int st_i = 0;                                       // stage of tile it (it % 3)
+  for (int it = 0; it < ntiles; ++it) {
+    const int st_n = st_i == 2 ? 0 : st_i + 1;
+    const int st_n2 = st_n == 2 ? 0 : st_n + 1;
+    const lds_char_t* st_cur = lds + st_i * kStageBytes;
+    const lds_char_t* st_nxt = lds + st_n * kStageBytes;
+    const int e_nxt3 = entry(it + 3);                 // scalar load, used next iteration
+    const uint64_t bits_nxt = load_bits(e_nxt);       // in flight until next iteration
+    if (it + 2 < ntiles) issue_tile(tc, lds0 + st_n2 * kStageBytes, (e_nxt2 & 0xFFFFFF) * kTileN);
+
+    if (kh == 0) s = scores(st_cur);
 
     // accumulator r <-> key k0 + kh*32 + 8*(r>>2) + 4*hi + (r&3)
+    const int cls_cur = e_cur >> 24;
+    const int k0 = (e_cur & 0xFFFFFF) * kTileN;
     const int kbase = k0 + kh * 32 + 4 * hi;
     float tile_max;
     if (cls_cur == 3) {
       // general mask values: s <- scale*qk + mask (natural units)
+      float mv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {   // all 16 loads in flight together (clamped index, fixed below)
+        const int kk = kbase + 8 * (r >> 2) + (r & 3);
+        mv[r] = load_mask<MASK_BF16>(a.mask, mask_row + min(kk, a.Lk - 1));
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kk = kbase + 8 * (r >> 2) + (r & 3);
-        float mv = -INFINITY;
-        if (kk < a.Lk) mv = q_ok ? load_mask<MASK_BF16>(a.mask, mask_row + kk) : 0.f;
-        s[r] = __builtin_fmaf(s[r], scale, mv);
+        const float m = kk < a.Lk ? (q_ok ? mv[r] : 0.f) : -INFINITY;
+        s[r] = __builtin_fmaf(s[r], scale, m);
       }
       tile_max = s[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) tile_max = fmaxf(tile_max, s[r]);
     } else {
       if (cls_cur == 2) {
+        // bit 8g+c of w <-> key kh*32 + 8g + 4hi + c
+        const uint32_t w = static_cast<uint32_t>(bits_cur >> (kh * 32 + 4 * hi));
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int bit = 8 * (r >> 2) + (r & 3);
-          const uint32_t keep = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(bits_cur), bit, 1));
+          const uint32_t keep = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(w), bit, 1));
           s[r] = __uint_as_float((__float_as_uint(s[r]) & keep) | (kNegInfBits & ~keep));
         }
       }
@@ -302,19 +356,22 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
       const bf16x8_t bfr = as_bf16x8(pb);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint16_t* vp = Vs + v_off + 16 * step * kVsStride + 32 * j;
+        const lds_char_t* vp = st_cur + v_base + step * 4096 + j * 1024;
         const s16x4_t lo = ds_read_tr(vp);
-        const s16x4_t hi4 = ds_read_tr(vp + 8 * kVsStride);
-        typedef short s16x8_t __attribute__((ext_vector_type(8)));
+        const s16x4_t hi4 = ds_read_tr(vp + 512);
         const s16x8_t av = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
         o[j] = mfma32(__builtin_bit_cast(bf16x8_t, av), bfr, o[j]);
       }
     }
 
-    if (has_next) store_stage(st, smem + ((it + 1) & 1) * kStageElems, t);
-    kt_cur = kt_nxt;
-    cls_cur = cls_nxt;
+    if (kh == 1 && it + 1 < ntiles) s = scores(st_nxt);
+
+    e_cur = e_nxt;
+    e_nxt = e_nxt2;
+    e_nxt2 = e_nxt3;
     bits_cur = bits_nxt;
+    st_i = st_n;
+    wait_vmem();
     __syncthreads();
   }
 

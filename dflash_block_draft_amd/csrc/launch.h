@@ -23,7 +23,6 @@ struct AttnBf16Args {
   int B, H, Lq, Lk, nqt, nkt;
   float scale;            // softmax scale (natural units)
   int mask_bf16;          // 1: mask is bf16, 0: f32
-  int no_skip;            // visit every tile (empty ones treated as mixed)
 };
 
 struct AttnF32Args {
@@ -50,6 +49,8 @@ struct ExpandArgs {
 hipError_t launch_attn_bf16(const AttnBf16Args& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnF32Args& a, hipStream_t s);
 hipError_t launch_occupancy(const OccupancyArgs& a, hipStream_t s);
+// Rewrite the lists so every k-tile is visited (empty tiles as class 3); debug/verification mode.
+hipError_t launch_lists_all_tiles(const OccupancyArgs& a, hipStream_t s);
 hipError_t launch_expand_bf16(const ExpandArgs& a, hipStream_t s);
 hipError_t launch_expand_f32(const ExpandArgs& a, hipStream_t s);
 

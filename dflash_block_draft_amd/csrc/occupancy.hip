@@ -126,7 +126,25 @@ __global__ void __launch_bounds__(kListThreads) build_lists(OccupancyArgs a) {
   }
 }
 
+// Every k-tile of every (b, q-tile), empty ones relabelled class 3 (their -inf
+// values are then added like any other mask values and contribute exp(-inf) = 0).
+__global__ void __launch_bounds__(256) lists_all_tiles(OccupancyArgs a) {
+  const int row = blockIdx.x;
+  const uint8_t* cls = a.classes + static_cast<size_t>(row) * a.nkt;
+  int32_t* list = a.lists + static_cast<size_t>(row) * a.nkt;
+  for (int kt = threadIdx.x; kt < a.nkt; kt += 256) {
+    const int c = cls[kt];
+    list[kt] = kt | ((c == 0 ? 3 : c) << 24);
+  }
+  if (threadIdx.x == 0) a.counts[row] = a.nkt;
+}
+
 }  // namespace
+
+hipError_t launch_lists_all_tiles(const OccupancyArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(lists_all_tiles, dim3(static_cast<unsigned>(a.B * a.nqt)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_occupancy(const OccupancyArgs& a, hipStream_t s) {
   const int64_t ntiles = static_cast<int64_t>(a.B) * a.nqt * a.nkt;

@@ -70,7 +70,9 @@ typedef enum dflash_dtype {
                                             the map of this same mask (e.g. the next draft layer,
                                             which receives the same mask) */
 #define DFLASH_ATTN_NO_TILE_SKIP 0x2u    /* debug/verification: visit every tile, treating empty
-                                            tiles as mixed; the result is bitwise identical */
+                                            tiles as mixed; the result is bitwise identical.  The
+                                            workspace lists are left covering every tile, so a later
+                                            REUSE_TILE_MAP call on it also visits every tile */
 
 /* Human-readable name of a status. Never NULL. */
 const char* dflash_status_string(dflash_status status);
@@ -168,7 +170,8 @@ dflash_status dflash_mla_mask_occupancy(const void* additive_mask, dflash_dtype 
  * scale         finite and > 0; the pages' value is (Dn + Dr) ** -0.5.
  *
  * Supported: Dn == 128, Dr == 64, Dv == 128;
- *   (dt, mask_dt) in {(F32, F32), (BF16, F32), (BF16, BF16)}.
+ *   (dt, mask_dt) in {(F32, F32), (BF16, F32), (BF16, BF16)};
+ *   a masked BF16 call takes Lk <= 655360 (10240 key tiles), else UNSUPPORTED.
  * BF16: QK^T and PV run as bf16 MFMA with fp32 accumulation and an online
  *   softmax in fp32; the probabilities are rounded to bf16 for PV; out is
  *   rounded to nearest even.  F32: fp32 arithmetic throughout.
