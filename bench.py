@@ -48,6 +48,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="run one plain device copy of this size (for HBM counter calibration)")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="offline: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE run, "
+                        "WRITE_SIZE run, both with --copy-calibration-mb) into HBM bytes per attention "
+                        "launch for --workload, stored in profiles/attn_traffic.json; no GPU needed")
     return p.parse_args()
 
 
@@ -123,7 +127,8 @@ def measure(wl, steps: int, warmup: int) -> dict:
     tm = mla.tile_map_view(ws, wl.B, wl.Lq, wl.Lk)
     cls = tm["classes"].cpu()
     n = cls.numel()
-    frac = {name: round(float((cls == c).sum()) / n, 4) for c, name in ((0, "empty"), (1, "zero"), (2, "mixed"))}
+    frac = {name: round(float((cls == c).sum()) / n, 4)
+            for c, name in ((0, "empty"), (1, "zero"), (2, "binary"), (3, "general"))}
     esz = 2 if wl.dtype == "bf16" else 4
     mask_bytes = wl.mask.numel() * wl.mask.element_size()
     attn_bytes = (wl.q.numel() + wl.B * wl.H * wl.Lk * (wl.Dn + wl.Dv) + wl.k_rope.numel()
@@ -197,8 +202,55 @@ def traffic_for(wl_name: str):
     return rec.get("bytes_per_launch")
 
 
+def _counter_rows(path: str, counter: str):
+    import csv
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") == counter:
+                yield row.get("Kernel_Name", ""), float(row["Counter_Value"])
+
+
+def traffic_from(args) -> None:
+    """HBM bytes per launch of the attention kernel from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled so that the calibration copy of known size
+    reads and writes exactly its own bytes."""
+    nb = args.copy_calibration_mb << 20
+    if nb <= 0:
+        raise SystemExit("--traffic-from needs --copy-calibration-mb (the size used in the counter runs)")
+    out = {}
+    for path, counter in zip(args.traffic_from, ("FETCH_SIZE", "WRITE_SIZE")):
+        rows = list(_counter_rows(path, counter))
+        copies = [v for k, v in rows if "copy" in k.lower()]
+        attn = [v for k, v in rows if "attn_fwd_bf16" in k]
+        if not copies or not attn:
+            raise SystemExit(f"{path}: no calibration copy or attention dispatch with {counter}")
+        factor = nb / (max(copies) * 1024.0)
+        out[counter] = {"kib_per_launch_raw": sum(attn) / len(attn), "calibration_factor": factor,
+                        "bytes_per_launch": sum(attn) / len(attn) * 1024.0 * factor, "launches": len(attn)}
+    wl = make_workload(args.workload)
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        data = {}
+    data[wl.name] = {"kernel_sha": kernel_sha(),
+                     "bytes_per_launch": round(out["FETCH_SIZE"]["bytes_per_launch"]
+                                               + out["WRITE_SIZE"]["bytes_per_launch"]),
+                     "read_bytes": round(out["FETCH_SIZE"]["bytes_per_launch"]),
+                     "write_bytes": round(out["WRITE_SIZE"]["bytes_per_launch"]),
+                     "calibration": {k: round(v["calibration_factor"], 4) for k, v in out.items()},
+                     "calibration_copy_bytes": nb}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    print(json.dumps(data[wl.name]))
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the draft attention "
               "shards over heads/batch rows with no exchange, but no multi-GPU run is part of this build.",

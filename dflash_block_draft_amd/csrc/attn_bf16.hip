@@ -34,7 +34,9 @@
 //    mask; general masks add their values to the scaled scores.
 //  * Online softmax in fp32 with the hardware exp2; the running max is only
 //    raised when a new score exceeds it by more than 2^8 in probability space
-//    ("lazy rescale"), exact because the same max scales both O and l.
+//    ("lazy rescale"), exact because the same max scales both O and l.  The
+//    row sum adds the bf16-rounded probabilities (v_dot2), the same values the
+//    PV MFMA consumes.
 #include "common.h"
 #include "launch.h"
 
@@ -250,8 +252,13 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
   auto k0_of = [&](int i, int e) -> int { return i < ntiles ? (e & 0xFFFFFF) * kTileN : a.Lk; };
   auto bits_kt = [&](int i, int e) -> int { return (i < ntiles && (e >> 24) == 2) ? (e & 0xFFFFFF) : a.nkt; };
 
-  // score accumulator initial value: 0, or -inf for keys a binary mask hides
-  auto score_init = [&](int e, int slot) {
+  // Scores of the tile in ring slot `slot`: S^T = K Q^T over the 12 16-dim chunks.
+  // A binary-mask tile starts the accumulator at 0 / -inf for visible / hidden keys
+  // (the MFMA then applies the mask); other tiles start from an inline zero.
+  auto scores = [&](int e, int slot) {
+    const lds_char_t* ke = lds + kKRing + slot * kKBytes + k_even;
+    const lds_char_t* ko = lds + kKRing + slot * kKBytes + k_odd;
+    const bf16x8_t k_first = as_bf16x8(*reinterpret_cast<const lds_u32x4_t*>(ke));
     f32x16_t s;
     if ((e >> 24) == 2) {
       const uint64_t w64 = *reinterpret_cast<const lds_u64_t*>(lds + kBitsRing + slot * kBitsBytes + q_local * 8);
@@ -261,17 +268,13 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
         const uint32_t keep = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(w), 8 * (r >> 2) + (r & 3), 1));
         s[r] = __uint_as_float(kNegInfBits & ~keep);
       }
+      s = mfma32(k_first, qf[0], s);
     } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+      const f32x16_t z = {};
+      s = mfma32(k_first, qf[0], z);
     }
-    return s;
-  };
-  auto scores = [&](f32x16_t s, int slot) {
-    const lds_char_t* ke = lds + kKRing + slot * kKBytes + k_even;
-    const lds_char_t* ko = lds + kKRing + slot * kKBytes + k_odd;
 #pragma unroll
-    for (int c = 0; c < kDqk / 16; ++c) {
+    for (int c = 1; c < kDqk / 16; ++c) {
       const lds_char_t* kp = ((c & 1) ? ko : ke) + (c >> 1) * 1024;
       const bf16x8_t kf = as_bf16x8(*reinterpret_cast<const lds_u32x4_t*>(kp));
       s = mfma32(kf, qf[c], s);
@@ -292,7 +295,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
   issue_bits(2, bits_kt(2, e2));
   wait_vmem<0>();
   __syncthreads();
-  f32x16_t s = scores(score_init(e0, 0), 0);   // S(0)
+  f32x16_t s = scores(e0, 0);                  // S(0)
 
   int e_cur = e0, e_nxt = e1, e_nxt2 = e2;     // tiles it, it+1, it+2
   int slot = 0;                                // ring slot of tile it
@@ -359,19 +362,36 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
       ca = kLog2e;
       cb = 0.f;
     }
-    // initial value of S(it+1) (binary mask of tile it+1 applied here)
-    const f32x16_t s_init = score_init(e_nxt, slot1);
+    // ---- copies for later tiles: K(it+3) and bits(it+3) into the slots of tile it,
+    // V(it+2) into the V slot of tile it-1 (all last read before the previous barrier).
+    // Issued here so their scalar work overlaps the MFMAs below.
+    issue_k(slot, k0_of(it + 3, e_nxt3));
+    issue_bits(slot, bits_kt(it + 3, e_nxt3));
+    issue_v(slot2, k0_of(it + 2, e_nxt2));
 
-    // ---- part 2 (one basic block): S(it+1) MFMAs, probabilities of tile it, PV(it)
-    const f32x16_t s_next = scores(s_init, slot1);
+    // ---- part 2: S(it+1) MFMAs interleaved with the probabilities of tile it, then
+    // PV(it).  The sched barrier keeps the score chain ahead of the PV MFMAs, so the
+    // next iteration's tile max does not wait behind them.
+    const f32x16_t s_next = scores(e_nxt, slot1);
     float p[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], ca, cb));
-#pragma unroll
-    for (int r = 0; r < 16; ++r) l_run += p[r];
     uint32_t pk[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) pk[u] = pack_bf16x2(p[2 * u], p[2 * u + 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    // row sum of the rounded probabilities, the values the PV MFMA consumes
+    {
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+      float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; u += 2) {
+        l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[u]), one2, l0, false);
+        l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[u + 1]), one2, l1, false);
+      }
+      l_run += l0 + l1;
+    }
     // O^T += V^T P^T over this wave's 32 keys (two 16-key MFMA steps).  B operand
     // element e of lane (li, hi) is key 8*(e>>2) + 4*hi + (e&3) of the step; the
     // transposing reads deliver V[that key][32*j + li] as A operand.
@@ -390,11 +410,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
       }
     }
 
-    // ---- copies for later tiles: K(it+3) and bits(it+3) into the slots of tile it,
-    // V(it+2) into the V slot of tile it-1 (all last read before the previous barrier)
-    issue_k(slot, k0_of(it + 3, e_nxt3));
-    issue_bits(slot, bits_kt(it + 3, e_nxt3));
-    issue_v(slot2, k0_of(it + 2, e_nxt2));
     s = s_next;
     e_cur = e_nxt;
     e_nxt = e_nxt2;
