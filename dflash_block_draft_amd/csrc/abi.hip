@@ -278,9 +278,9 @@ dflash_status dflash_mla_attn(const void* q, const void* k_nope, const void* k_r
   a.scale = scale;
   a.mask_bf16 = mask_dt == DFLASH_BF16;
   if (static_cast<int64_t>(B) * a.nqt * H > INT32_MAX) return fail(DFLASH_ERR_UNSUPPORTED, "too many work items");
-  if (additive_mask && a.nkt > dflash::kLdsListMax)
-    return fail(DFLASH_ERR_UNSUPPORTED, "a masked bf16 call supports at most %d key tiles (Lk <= %d), got Lk = %lld",
-                dflash::kLdsListMax, dflash::kLdsListMax * DFLASH_TILE_N, (long long)Lk);
+  if (a.nkt > dflash::kMaxKeyTiles)
+    return fail(DFLASH_ERR_UNSUPPORTED, "a bf16 call supports at most %d key tiles (Lk <= %d), got Lk = %lld",
+                dflash::kMaxKeyTiles, dflash::kMaxKeyTiles * DFLASH_TILE_N, (long long)Lk);
   if (additive_mask) {
     TileLayout t;
     dflash_status st = check_occupancy_args(additive_mask, mask_dt, B, Lq, Lk, workspace, workspace_bytes, &t);

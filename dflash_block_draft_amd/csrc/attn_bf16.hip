@@ -8,37 +8,43 @@
 //
 // Decomposition (one workgroup = one (batch, head, 128-query tile)):
 //  * 8 waves, two per SIMD: wave w owns queries 32*(w&3) .. +31 of the tile
-//    and keys 32*(w>>2) .. +31 of every 64-key tile; the two waves of a query
-//    group merge (m, l, O) once at the end.
-//  * Each wave is software-pipelined: in iteration i it runs the score MFMAs of
-//    tile i+1 in the same basic block as the softmax and PV of tile i, so the
-//    MFMA pipe and the VALU work at the same time within a wave (and across
-//    the two waves of a SIMD).
-//  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
-//    a lane holds one query and 16 of its keys, so row max / row sum are
-//    in-lane (plus one v_permlane32_swap), and the lane's P^T values are
-//    already the B operand of O^T = V^T P^T for the same key order (the order
-//    of the key contraction is free, so keys are relabelled to match the
-//    accumulator layout).  V^T operands come straight from the V tile with the
-//    gfx950 transposing LDS read (ds_read_b64_tr_b16).
+//    and keys 32*(w>>2) .. +31 of every 64-key tile; the two key-half waves of
+//    a query group keep separate (m, l, O) and merge them once at the end.
+//  * Ping-pong: each wave alternates a matrix phase (score MFMAs of the next
+//    tile + PV MFMAs of the current one) and a vector phase (softmax of the
+//    next tile), with a workgroup barrier after every phase.  The key-half-1
+//    waves run one phase behind the key-half-0 waves, so on every SIMD (waves
+//    w and w+4) one wave feeds the matrix core while the other does its
+//    exponentials.
+//  * Scores are computed transposed, S^T = K Q^T with v_mfma_f32_32x32x16_bf16:
+//    a lane holds one query and 16 of its keys, so row sums are in-lane, and
+//    the packed bf16 P^T values are directly the B operand of O^T = V^T P^T
+//    (the key order of the contraction is free, so keys are relabelled to
+//    match the accumulator layout).  V^T operands come from the V tile with
+//    the gfx950 transposing LDS read (ds_read_b64_tr_b16).
 //  * K = [k_nope | head-shared k_rope], V and the visibility words go global ->
 //    LDS with buffer_load ... lds (no VGPR staging; out-of-range reads give
-//    zeros).  K and V have separate three-slot rings: K of tile i+1 is read in
-//    iteration i, V of tile i too, so issuing K(i+3) and V(i+2) in iteration i
-//    gives every copy two iterations to land, with one barrier per tile.  LDS
+//    zeros) into three-slot rings; every copy has two phases of slack before
+//    the barrier that publishes it.  The key loop is unrolled by the ring
+//    length so every LDS address and copy destination is a constant.  LDS
 //    tiles are 16-row x 64 B blocks with XOR-swizzled K chunks: conflict-free
-//    operand reads, 64-byte coalesced loads, immediate offsets.
-//  * Q (32 x 192 bf16 per wave) stays in registers for the whole key loop.
+//    operand reads, 64-byte coalesced loads.
+//  * Q (32 x 192 bf16 per wave) stays in registers for the whole key loop; the
+//    K operands of the next score tile are read into registers at the end of
+//    the vector phase, so the matrix phase starts on data already there.
 //  * Binary-mask tiles (only 0 / -inf) initialise the score accumulator to
 //    0 / -inf from a 64-bit visibility word per query, so the MFMA applies the
 //    mask; general masks add their values to the scaled scores.
-//  * Online softmax in fp32 with the hardware exp2; the running max is only
-//    raised when a new score exceeds it by more than 2^8 in probability space
-//    ("lazy rescale"), exact because the same max scales both O and l.  The
-//    row sum adds the bf16-rounded probabilities (v_dot2), the same values the
-//    PV MFMA consumes.
+//  * Online softmax in fp32 with the hardware exp2 and a stabiliser m that is
+//    only raised when needed: the probabilities of a tile are first formed
+//    with the current m; if some lane's tile sum exceeds 2^8 (or m is still
+//    -inf) the wave takes the exact path (tile max, rescale of O and l by
+//    exp(m_old - m_new), recompute).  Any stabiliser gives the same result in
+//    exact arithmetic because it scales O and l alike.
 #include "common.h"
 #include "launch.h"
+
+#include <type_traits>
 
 namespace dflash {
 namespace {
@@ -53,8 +59,9 @@ constexpr int kKRing = 0;
 constexpr int kVRing = kKRing + kRing * kKBytes;
 constexpr int kBitsRing = kVRing + kRing * kVBytes;
 constexpr int kRingBytes = kBitsRing + kRing * kBitsBytes;
-static_assert(kRingBytes + 4 * kLdsListMax <= 160 * 1024, "LDS budget");
-constexpr float kLazyTau = 8.0f / kLog2e;            // natural-units slack before a rescale
+static_assert(kRingBytes + 4 * kLdsListEntries <= 160 * 1024, "LDS budget");
+constexpr int kPrefetchK = 8;                        // K operand chunks read before the matrix phase
+constexpr float kSumLimit = 256.0f;                  // fast path keeps every probability <= 2^8
 constexpr uint32_t kNegInfBits = 0xFF800000u;
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -87,15 +94,17 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
-// 16 bytes per lane from a buffer straight into LDS at lds_addr + 16*lane; reads past
+// 16 bytes per lane from a buffer straight into LDS at lds_base + OFF + 16*lane; reads past
 // the descriptor's num_records return zeros.  Issued as inline asm so the compiler
 // does not treat the in-flight LDS write as a dependency of unrelated LDS reads
 // (it would otherwise wait for it before every ds_read); completion is awaited
 // explicitly (wait_vmem) before the barrier that publishes the slot.  No memory
 // clobber: the slot it writes is not read before that barrier.
-__device__ __forceinline__ void dma16(u32x4_t rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr));
+template <int OFF>
+__device__ __forceinline__ void dma16(u32x4_t rsrc, uint32_t lds_base, uint32_t voff, uint32_t soff) {
+  asm volatile("s_add_u32 m0, %3, %4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                  "s"(__builtin_amdgcn_readfirstlane(lds_base)), "i"(OFF) : "scc");
 }
 
 __device__ __forceinline__ u32x4_t buffer_desc(const void* base, uint32_t bytes) {
@@ -109,13 +118,13 @@ __device__ __forceinline__ u32x4_t buffer_desc(const void* base, uint32_t bytes)
 // LDS tile layout (K and V): row block rb (16 rows) x chunk quad cq (4 x 16 B
 // chunks) -> 1 KiB block (rb * nq + cq); inside it row r%16 takes 64 B and the
 // 16-byte chunk c%4 of that row sits at slot (c%4) ^ swz(r), swz(r) = (r>>2)&3
-// for K and 0 for V.  A wave copies 3 K blocks and 2 V blocks of each tile;
-// lane l of a block covers row rb*16 + l/4 and slot l%4.
+// for K and 0 for V.  Wave w copies, of each tile, row block w/2 of K: the
+// k_nope quads 2(w%2), 2(w%2)+1 (adjacent blocks) and the k_rope quad 4 + w%2,
+// and V blocks 2w, 2w+1; lane l of a block covers row rb*16 + l/4, slot l%4.
 struct TileCopy {
-  u32x4_t kdesc[3], v, bits;   // descriptors (k_nope or k_rope slice per K block)
-  uint32_t voff[5];            // per-lane byte offset inside the source slice (tile start excluded)
-  uint32_t lds_off[5];         // block offset inside a K / V slot
-  int krow_bytes[3];           // source row pitch of each K block (k_nope 256 B, k_rope 128 B)
+  u32x4_t kn, kr, v, bits;     // descriptors: this (b, h)'s k_nope, the shared k_rope, v, visibility words
+  uint32_t voff[4];            // per-lane byte offset inside the source rows (tile start excluded)
+  uint32_t kn_lds, kr_lds, v_lds;   // LDS address of this wave's k_nope pair / k_rope / V pair in slot 0
 };
 
 __device__ __forceinline__ u32x4_t uniform4(u32x4_t d) {
@@ -130,10 +139,13 @@ __device__ __forceinline__ float load_mask(const void* mask, size_t idx) {
   return static_cast<const float*>(mask)[idx];
 }
 
+template <int N>
+using IC = std::integral_constant<int, N>;
+
 template <bool MASK_BF16>
 __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
   __shared__ __attribute__((aligned(1024))) char smem[kRingBytes];
-  __shared__ int s_list[kLdsListMax];
+  __shared__ int s_list[kLdsListEntries];
   lds_char_t* const lds = (lds_char_t*)smem;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
 
@@ -141,7 +153,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: keeps descriptors scalar
   const int qg = wave & 3;      // query group: 32 queries
-  const int kh = wave >> 2;     // key half of each 64-key tile
+  const int kh = wave >> 2;     // key half of each 64-key tile; also the ping-pong group
   const int li = lane & 31;
   const int hi = lane >> 5;
 
@@ -159,53 +171,55 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
   const bool q_ok = q_row < a.Lq;
   const size_t tile_row0 = static_cast<size_t>(bq) * a.nkt;
 
-  // ---- tile list of this q-tile -> LDS (entry: k-tile | class << 24); host caps ntiles
+  // ---- tile list of this q-tile -> LDS (entry: k-tile | class << 24, class 0 =
+  // no tile), kListPad zero entries after it; without a mask every k-tile is
+  // class 1.  The host caps ntiles at kMaxKeyTiles.
   const int32_t* list = a.counts ? a.lists + tile_row0 : nullptr;
-  if (list)
-    for (int i = t; i < ntiles; i += kThreads) s_list[i] = list[i];
+  for (int i = t; i < ntiles + kListPad; i += kThreads)
+    s_list[i] = i >= ntiles ? 0 : (list ? list[i] : (i | (1 << 24)));
 
   // ---- global -> LDS copy plan of this wave
   TileCopy tc;
-  const u32x4_t kn_desc = buffer_desc(a.kn + bh * a.Lk * kDn, a.Lk * kDn * 2);
-  const u32x4_t kr_desc = buffer_desc(a.kr + static_cast<size_t>(b) * a.Lk * kDr, a.Lk * kDr * 2);
+  tc.kn = buffer_desc(a.kn + bh * a.Lk * kDn, a.Lk * kDn * 2);
+  tc.kr = buffer_desc(a.kr + static_cast<size_t>(b) * a.Lk * kDr, a.Lk * kDr * 2);
   tc.v = buffer_desc(a.v + bh * a.Lk * kDv, a.Lk * kDv * 2);
   tc.bits = buffer_desc(a.bits ? a.bits + tile_row0 * kTileM : nullptr, a.bits ? a.nkt * kBitsBytes : 0);
   {
     const int r16 = lane >> 2, s4 = lane & 3;
+    const int krb = wave >> 1;                                   // K row block of this wave
+    const int krow = krb * 16 + r16;
+    const int kslot = s4 ^ ((r16 >> 2) & 3);                     // swizzled 16-byte chunk in the quad
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {            // K blocks 3w .. 3w+2 of 24 (4 row blocks x 6 quads)
-      const int blk = 3 * wave + i, rb = blk / 6, cq = blk % 6;
-      const int row = rb * 16 + r16;
-      const int chunk = cq * 4 + (s4 ^ ((r16 >> 2) & 3));
-      const bool rope = cq >= 4;                                  // chunks 16..23: k_rope dims
-      tc.lds_off[i] = blk * 1024;
-      tc.kdesc[i] = uniform4(rope ? kr_desc : kn_desc);
-      tc.krow_bytes[i] = rope ? kDr * 2 : kDn * 2;
-      tc.voff[i] = rope ? row * (kDr * 2) + (chunk - 16) * 16 : row * (kDn * 2) + chunk * 16;
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {            // V blocks 2w, 2w+1 of 16 (4 row blocks x 4 quads)
-      const int blk = 2 * wave + i, rb = blk / 4, cq = blk % 4;
-      const int row = rb * 16 + r16;
-      tc.lds_off[3 + i] = blk * 1024;
-      tc.voff[3 + i] = row * (kDv * 2) + (cq * 4 + s4) * 16;
-    }
+    for (int i = 0; i < 2; ++i)                                  // k_nope quads 2(w%2) + i: dims 64(w%2) + 32i ..
+      tc.voff[i] = krow * (kDn * 2) + ((2 * (wave & 1) + i) * 4 + kslot) * 16;
+    tc.voff[2] = krow * (kDr * 2) + ((wave & 1) * 4 + kslot) * 16;   // k_rope quad 4 + w%2
+    tc.kn_lds = lds0 + kKRing + (krb * 6 + 2 * (wave & 1)) * 1024;
+    tc.kr_lds = lds0 + kKRing + (krb * 6 + 4 + (wave & 1)) * 1024;
+    // V blocks 2w, 2w+1 of 16 (4 row blocks x 4 quads): row block w/2, quads 2(w%2) + i
+    const int vrow0 = (wave >> 1) * 16 + r16;
+    tc.voff[3] = vrow0 * (kDv * 2) + (2 * (wave & 1) * 4 + s4) * 16;   // second block is +64 B in the row
+    tc.v_lds = lds0 + kVRing + 2 * wave * 1024;
   }
-  // k0 = Lk makes every lane's read out of range (zeros, no traffic): used for
-  // ring slots whose tile does not exist, so every wave always issues the same
-  // number of copies and the wait count is a constant.
-  auto issue_k = [&](int slot, int k0) {
-#pragma unroll
-    for (int i = 0; i < 3; ++i)
-      dma16(tc.kdesc[i], lds0 + kKRing + slot * kKBytes + tc.lds_off[i], tc.voff[i], k0 * tc.krow_bytes[i]);
+  // Tiles past the end use k0 = Lk: every lane's read is out of range (zeros, no
+  // traffic), so every wave always issues the same number of copies and the
+  // wait counts are constants.
+  auto k0_of = [&](int e) __attribute__((always_inline)) -> int { return (e >> 24) ? (e & 0xFFFFFF) * kTileN : a.Lk; };
+  auto bits_kt = [&](int e) __attribute__((always_inline)) -> int { return (e >> 24) == 2 ? (e & 0xFFFFFF) : a.nkt; };
+  auto issue_k = [&](auto SL, int k0) __attribute__((always_inline)) {
+    constexpr int sl = decltype(SL)::value;
+    dma16<sl * kKBytes>(tc.kn, tc.kn_lds, tc.voff[0], k0 * (kDn * 2));
+    dma16<sl * kKBytes + 1024>(tc.kn, tc.kn_lds, tc.voff[1], k0 * (kDn * 2));
+    dma16<sl * kKBytes>(tc.kr, tc.kr_lds, tc.voff[2], k0 * (kDr * 2));
   };
-  auto issue_v = [&](int slot, int k0) {
-#pragma unroll
-    for (int i = 3; i < 5; ++i) dma16(tc.v, lds0 + kVRing + slot * kVBytes + tc.lds_off[i], tc.voff[i], k0 * (kDv * 2));
+  auto issue_v = [&](auto SL, int k0) __attribute__((always_inline)) {
+    constexpr int sl = decltype(SL)::value;
+    dma16<sl * kVBytes>(tc.v, tc.v_lds, tc.voff[3], k0 * (kDv * 2));
+    dma16<sl * kVBytes + 1024>(tc.v, tc.v_lds, tc.voff[3] + 64, k0 * (kDv * 2));
   };
   // visibility words of a class-2 tile (1 KiB, copied by wave 0); kt = nkt reads zeros
-  auto issue_bits = [&](int slot, int kt) {
-    if (wave == 0) dma16(tc.bits, lds0 + kBitsRing + slot * kBitsBytes, lane * 16, kt * kBitsBytes);
+  auto issue_bits = [&](auto SL, int kt) __attribute__((always_inline)) {
+    constexpr int sl = decltype(SL)::value;
+    if (wave == 0) dma16<kBitsRing + sl * kBitsBytes>(tc.bits, lds0, lane * 16, kt * kBitsBytes);
   };
 
   // ---- per-lane LDS read offsets (bytes inside a slot)
@@ -220,6 +234,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
   const int g16 = lane >> 4, i16 = lane & 15;
   const int vrow = kh * 32 + 4 * hi + (i16 >> 2);
   const int v_base = ((vrow >> 4) * 4) * 1024 + (vrow & 15) * 64 + (2 * (g16 & 1) + ((i16 & 3) >> 1)) * 16 + (i16 & 1) * 8;
+  const lds_char_t* const ke_ptr = lds + kKRing + k_even;
+  const lds_char_t* const ko_ptr = lds + kKRing + k_odd;
+  const lds_char_t* const v_ptr = lds + kVRing + v_base;
+  const lds_u64_t* const bits_ptr = reinterpret_cast<const lds_u64_t*>(lds + kBitsRing + q_local * 8);
 
   // ---- Q fragments (B operand of S^T = K Q^T): 12 chunks of 16 dims
   bf16x8_t qf[kDqk / 16];
@@ -237,190 +255,243 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[j][r] = 0.f;
-  float m_run = -INFINITY;   // running max (natural units), same in both halves
+  float m_run = -INFINITY;   // stabiliser (natural units), same in both lane halves
   float l_run = 0.f;         // this lane's partial row sum
 
   const float scale = a.scale;
   const float scale_log2 = a.scale * kLog2e;
   const size_t mask_row = (static_cast<size_t>(b) * a.Lq + (q_ok ? q_row : 0)) * a.Lk;
 
-  auto entry = [&](int i) -> int {
-    if (i >= ntiles) return 0;
-    if (!list) return i | (1 << 24);
-    return __builtin_amdgcn_readfirstlane(s_list[i]);
-  };
-  auto k0_of = [&](int i, int e) -> int { return i < ntiles ? (e & 0xFFFFFF) * kTileN : a.Lk; };
-  auto bits_kt = [&](int i, int e) -> int { return (i < ntiles && (e >> 24) == 2) ? (e & 0xFFFFFF) : a.nkt; };
+  // list entry i (0 past the end), wave-uniform
+  auto entry = [&](int i) __attribute__((always_inline)) -> int { return __builtin_amdgcn_readfirstlane(s_list[i]); };
 
-  // Scores of the tile in ring slot `slot`: S^T = K Q^T over the 12 16-dim chunks.
-  // A binary-mask tile starts the accumulator at 0 / -inf for visible / hidden keys
-  // (the MFMA then applies the mask); other tiles start from an inline zero.
-  auto scores = [&](int e, int slot) {
-    const lds_char_t* ke = lds + kKRing + slot * kKBytes + k_even;
-    const lds_char_t* ko = lds + kKRing + slot * kKBytes + k_odd;
-    const bf16x8_t k_first = as_bf16x8(*reinterpret_cast<const lds_u32x4_t*>(ke));
-    f32x16_t s;
+  f32x16_t s;                    // scores of the tile between its matrix and vector phases
+  bf16x8_t kf[kDqk / 16];        // K operands of the next score tile
+  uint32_t pk[8];                // P^T of the tile awaiting PV, bf16 pairs
+
+  // K operand chunks [C0, C1) of ring slot SL into registers
+  auto read_k = [&](auto SL, auto C0, auto C1) __attribute__((always_inline)) {
+    constexpr int sl = decltype(SL)::value;
+#pragma unroll
+    for (int c = decltype(C0)::value; c < decltype(C1)::value; ++c) {
+      const lds_char_t* kp = ((c & 1) ? ko_ptr : ke_ptr) + sl * kKBytes + (c >> 1) * 1024;
+      kf[c] = as_bf16x8(*reinterpret_cast<const lds_u32x4_t*>(kp));
+    }
+  };
+  // First K operands of ring slot SL (the rest are read in the matrix phase, behind
+  // the first MFMAs); for a binary tile also its hidden-key word, applied to the
+  // scores in the vector phase.
+  uint32_t hid_next = 0, hid = 0;   // bit 8g+c <-> key kh*32+8g+4hi+c of the tile is hidden
+  auto load_k = [&](auto SL, int e) __attribute__((always_inline)) {
+    constexpr int sl = decltype(SL)::value;
+    read_k(SL, IC<0>{}, IC<kPrefetchK>{});
     if ((e >> 24) == 2) {
-      const uint64_t w64 = *reinterpret_cast<const lds_u64_t*>(lds + kBitsRing + slot * kBitsBytes + q_local * 8);
-      const uint32_t w = static_cast<uint32_t>(w64 >> (kh * 32 + 4 * hi));   // bit 8g+c <-> key kh*32+8g+4hi+c
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t keep = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(w), 8 * (r >> 2) + (r & 3), 1));
-        s[r] = __uint_as_float(kNegInfBits & ~keep);
-      }
-      s = mfma32(k_first, qf[0], s);
-    } else {
-      const f32x16_t z = {};
-      s = mfma32(k_first, qf[0], z);
+      const uint64_t w64 = bits_ptr[sl * (kBitsBytes / 8)];
+      hid_next = ~static_cast<uint32_t>(w64 >> (kh * 32 + 4 * hi));
     }
-#pragma unroll
-    for (int c = 1; c < kDqk / 16; ++c) {
-      const lds_char_t* kp = ((c & 1) ? ko : ke) + (c >> 1) * 1024;
-      const bf16x8_t kf = as_bf16x8(*reinterpret_cast<const lds_u32x4_t*>(kp));
-      s = mfma32(kf, qf[c], s);
-    }
-    return s;
   };
-
-  // ---- prologue: K(0..2), bits(0..2), V(0..1) in flight; everyone scores tile 0
-  __syncthreads();                                              // s_list visible
-  int e0 = entry(0), e1 = entry(1), e2 = entry(2);
-  issue_k(0, k0_of(0, e0));
-  issue_k(1, k0_of(1, e1));
-  issue_k(2, k0_of(2, e2));
-  issue_v(0, k0_of(0, e0));
-  issue_v(1, k0_of(1, e1));
-  issue_bits(0, bits_kt(0, e0));
-  issue_bits(1, bits_kt(1, e1));
-  issue_bits(2, bits_kt(2, e2));
-  wait_vmem<0>();
-  __syncthreads();
-  f32x16_t s = scores(e0, 0);                  // S(0)
-
-  int e_cur = e0, e_nxt = e1, e_nxt2 = e2;     // tiles it, it+1, it+2
-  int slot = 0;                                // ring slot of tile it
-  for (int it = 0; it < ntiles; ++it) {
-    const int slot1 = slot == 2 ? 0 : slot + 1;        // tile it+1
-    const int slot2 = slot1 == 2 ? 0 : slot1 + 1;      // tile it+2 (and it-1)
-    const int e_nxt3 = entry(it + 3);
-    const int cls = e_cur >> 24;
-    const int k0 = (e_cur & 0xFFFFFF) * kTileN;
-    // accumulator r <-> key k0 + kh*32 + 8*(r>>2) + 4*hi + (r&3)
-    const int kbase = k0 + kh * 32 + 4 * hi;
-
-    // ---- part 1: tile max of S(it)
-    float tile_max;
-    if (cls == 3) {
-      // general mask values: s <- scale*qk + mask (natural units)
-      float mv[16];
+  auto score_mfma = [&]() __attribute__((always_inline)) {
+    const f32x16_t z = {};
+    s = mfma32(kf[0], qf[0], z);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {   // all 16 loads in flight together (clamped index, fixed below)
-        const int kk = kbase + 8 * (r >> 2) + (r & 3);
-        mv[r] = load_mask<MASK_BF16>(a.mask, mask_row + min(kk, a.Lk - 1));
+    for (int c = 1; c < kDqk / 16; ++c) s = mfma32(kf[c], qf[c], s);
+  };
+  // O^T += V^T P^T over this wave's 32 keys (two 16-key MFMA steps).  B operand
+  // element e of lane (li, hi) is key 8*(e>>2) + 4*hi + (e&3) of the step; the
+  // transposing reads deliver V[that key][32*j + li] as A operand.
+  s16x8_t av[2][4];              // V^T operands of the tile awaiting PV
+  auto read_v = [&](auto SL) __attribute__((always_inline)) {
+    constexpr int sl = decltype(SL)::value;
+#pragma unroll
+    for (int step = 0; step < 2; ++step)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const lds_char_t* vp = v_ptr + sl * kVBytes + step * 4096 + j * 1024;
+        const s16x4_t lo = ds_read_tr(vp);
+        const s16x4_t hi4 = ds_read_tr(vp + 512);
+        av[step][j] = s16x8_t{lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = kbase + 8 * (r >> 2) + (r & 3);
-        const float m = kk < a.Lk ? (q_ok ? mv[r] : 0.f) : -INFINITY;
-        s[r] = __builtin_fmaf(s[r], scale, m);
-      }
-      tile_max = s[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) tile_max = fmaxf(tile_max, s[r]);
-    } else {
-      if (k0 + kTileN > a.Lk) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kbase + 8 * (r >> 2) + (r & 3) >= a.Lk) s[r] = -INFINITY;
-      }
-      tile_max = s[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) tile_max = fmaxf(tile_max, s[r]);
-      tile_max *= scale;
-    }
-    tile_max = halves_max(tile_max);
-
-    // ---- lazy rescale (wave-uniform decision)
-    const bool need = (tile_max > m_run + kLazyTau) || (m_run == -INFINITY && tile_max > -INFINITY);
-    if (__any(need)) {
-      const float m_new = fmaxf(m_run, tile_max);
-      const float alpha = (m_run == -INFINITY || m_new == -INFINITY) ? (m_run == m_new ? 1.f : 0.f)
-                                                                     : __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e);
-      l_run *= alpha;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[j][r] *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    // p = exp2(fma(x, ca, cb)): raw scores for zero/binary tiles, s - m for general ones
-    float ca = scale_log2, cb = -m_use * kLog2e;
-    if (cls == 3) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] -= m_use;
-      ca = kLog2e;
-      cb = 0.f;
-    }
-    // ---- copies for later tiles: K(it+3) and bits(it+3) into the slots of tile it,
-    // V(it+2) into the V slot of tile it-1 (all last read before the previous barrier).
-    // Issued here so their scalar work overlaps the MFMAs below.
-    issue_k(slot, k0_of(it + 3, e_nxt3));
-    issue_bits(slot, bits_kt(it + 3, e_nxt3));
-    issue_v(slot2, k0_of(it + 2, e_nxt2));
-
-    // ---- part 2: S(it+1) MFMAs interleaved with the probabilities of tile it, then
-    // PV(it).  The sched barrier keeps the score chain ahead of the PV MFMAs, so the
-    // next iteration's tile max does not wait behind them.
-    const f32x16_t s_next = scores(e_nxt, slot1);
-    float p[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], ca, cb));
-    uint32_t pk[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) pk[u] = pack_bf16x2(p[2 * u], p[2 * u + 1]);
-    __builtin_amdgcn_sched_barrier(0);
-    // row sum of the rounded probabilities, the values the PV MFMA consumes
-    {
-      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-      const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
-      float l0 = 0.f, l1 = 0.f;
-#pragma unroll
-      for (int u = 0; u < 8; u += 2) {
-        l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[u]), one2, l0, false);
-        l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[u + 1]), one2, l1, false);
-      }
-      l_run += l0 + l1;
-    }
-    // O^T += V^T P^T over this wave's 32 keys (two 16-key MFMA steps).  B operand
-    // element e of lane (li, hi) is key 8*(e>>2) + 4*hi + (e&3) of the step; the
-    // transposing reads deliver V[that key][32*j + li] as A operand.
-    const lds_char_t* vs = lds + kVRing + slot * kVBytes + v_base;
+  };
+  auto pv_mfma = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int step = 0; step < 2; ++step) {
       const u32x4_t pb = {pk[4 * step + 0], pk[4 * step + 1], pk[4 * step + 2], pk[4 * step + 3]};
       const bf16x8_t bfr = as_bf16x8(pb);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const lds_char_t* vp = vs + step * 4096 + j * 1024;
-        const s16x4_t lo = ds_read_tr(vp);
-        const s16x4_t hi4 = ds_read_tr(vp + 512);
-        const s16x8_t av = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-        o[j] = mfma32(__builtin_bit_cast(bf16x8_t, av), bfr, o[j]);
-      }
+      for (int j = 0; j < 4; ++j) o[j] = mfma32(__builtin_bit_cast(bf16x8_t, av[step][j]), bfr, o[j]);
     }
+  };
+  // p = exp2(fma(x, ca, cb)) -> pk (bf16 pairs); returns the lane's sum of p.  The sum
+  // uses plain fp32 adds: v_dot2 would wait for the matrix core, which the other
+  // wave of the SIMD keeps busy during this phase.
+  auto probs = [&](const float* x, float ca, float cb) __attribute__((always_inline)) -> float {
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], ca, cb));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) pk[u] = pack_bf16x2(p[2 * u], p[2 * u + 1]);
+    float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      l0 += p[r];
+      l1 += p[r + 1];
+    }
+    return l0 + l1;
+  };
+  // Vector phase: softmax of the raw scores in s (tile entry e) -> pk, m_run, l_run, o.
+  // Fast path (zero-mask tile, no ragged end): probabilities with the current
+  // stabiliser.  Exact path (binary or general mask, ragged end, no stabiliser
+  // yet, or a probability that may exceed 2^8): masked natural-unit scores, tile
+  // max, rescale of O and l when the stabiliser rises, probabilities.
+  auto softmax = [&](int e) __attribute__((always_inline)) {
+    const int cls = e >> 24;
+    const int k0 = (e & 0xFFFFFF) * kTileN;
+    const bool ragged = k0 + kTileN > a.Lk;
+    float lsum = 0.f;
+    bool exact = true;
+    if (cls == 1 && !ragged) {
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = s[r];
+      lsum = probs(x, scale_log2, -(m_run == -INFINITY ? 0.f : m_run) * kLog2e);
+      exact = __any(!(lsum <= kSumLimit) || (m_run == -INFINITY));   // NaN sums too
+    }
+    if (__builtin_expect(exact, 0)) {
+      // accumulator r <-> key k0 + kh*32 + 8*(r>>2) + 4*hi + (r&3)
+      const int kbase = k0 + kh * 32 + 4 * hi;
+      float x[16];
+      if (cls == 3) {
+        // general mask values: x = scale*qk + mask
+        float mv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {   // all 16 loads in flight together (clamped index, fixed below)
+          const int kk = kbase + 8 * (r >> 2) + (r & 3);
+          mv[r] = load_mask<MASK_BF16>(a.mask, mask_row + min(kk, a.Lk - 1));
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = __builtin_fmaf(s[r], scale, q_ok ? mv[r] : 0.f);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = s[r] * scale;
+        if (cls == 2) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int h1 = __builtin_amdgcn_sbfe(static_cast<int>(hid), 8 * (r >> 2) + (r & 3), 1);   // -1: hidden
+            x[r] = __int_as_float((h1 & static_cast<int>(kNegInfBits)) | (~h1 & __float_as_int(x[r])));
+          }
+        }
+      }
+      if (ragged) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kbase + 8 * (r >> 2) + (r & 3) >= a.Lk) x[r] = -INFINITY;
+      }
+      float tmax = x[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, x[r]);
+      const float m_new = fmaxf(m_run, halves_max(tmax));
+      if (__any(m_new != m_run)) {
+        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e);
+        l_run *= alpha;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[j][r] *= alpha;
+        m_run = m_new;
+      }
+      // subtract before scaling: m * log2e can overflow where x - m does not (mask values near -FLT_MAX)
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] -= m_use;
+      lsum = probs(x, kLog2e, 0.f);
+    }
+    l_run += lsum;
+  };
 
-    s = s_next;
-    e_cur = e_nxt;
-    e_nxt = e_nxt2;
-    e_nxt2 = e_nxt3;
-    slot = slot1;
-    // copies issued one iteration ago (K(it+2), bits(it+2), V(it+1)) must have
-    // landed; this iteration's (5 per wave, 6 for wave 0) stay in flight.
-    if (wave == 0) wait_vmem<6>();
-    else wait_vmem<5>();
+  // ---- prologue: K(0..2), bits(0..2), V(0..1) land before anyone reads
+  __syncthreads();                                              // s_list visible
+  int e0 = entry(0), e1 = entry(1), e2 = entry(2), e3 = entry(3);   // tiles t .. t+3
+  issue_k(IC<0>{}, k0_of(e0));
+  issue_k(IC<1>{}, k0_of(e1));
+  issue_k(IC<2>{}, k0_of(e2));
+  issue_v(IC<0>{}, k0_of(e0));
+  issue_v(IC<1>{}, k0_of(e1));
+  issue_bits(IC<0>{}, bits_kt(e0));
+  issue_bits(IC<1>{}, bits_kt(e1));
+  issue_bits(IC<2>{}, bits_kt(e2));
+  wait_vmem<0>();
+  __syncthreads();
+
+  // Phase schedule (every phase ends with a workgroup barrier):
+  //   key half 0:  S(0) | V(0) | M(0) | V(1) | M(1) | ... | M(T-1) | idle
+  //   key half 1:  idle | S(0) | V(0) | M(0) | V(1) | ... | V(T-1) | M(T-1)
+  // M(t) = scores of tile t+1 and PV of tile t; V(t) = softmax of tile t.
+  // Copies of K(t+3), bits(t+3), V(t+2) are issued at the start of the phase
+  // both halves run in slot 2t+2 (half 0: M(t), half 1: V(t)); each wave waits
+  // for its own copies two phases before the first read, then the barrier
+  // publishes them.
+  if (kh == 1) __syncthreads();
+  load_k(IC<0>{}, e0);
+  read_k(IC<0>{}, IC<kPrefetchK>{}, IC<kDqk / 16>{});
+  score_mfma();
+  hid = hid_next;
+  __syncthreads();
+
+  auto issue_copies = [&](auto R, int it) __attribute__((always_inline)) {
+    constexpr int r = decltype(R)::value;
+    issue_k(IC<r>{}, k0_of(e3));
+    issue_bits(IC<r>{}, bits_kt(e3));
+    issue_v(IC<(r + 2) % 3>{}, k0_of(e2));
+  };
+  // list entry it+4 is read into a VGPR one iteration ahead of its readfirstlane
+  int ev = s_list[4];
+  auto iteration = [&](auto R, int it) __attribute__((always_inline)) {
+    constexpr int r = decltype(R)::value;          // it % 3: ring slot of tile it
+    const int e_next = __builtin_amdgcn_readfirstlane(ev);
+    ev = s_list[it + 5];
+    // ---- vector phase: K operands of tile it+1, softmax of tile it
+    if (it + 1 < ntiles) load_k(IC<(r + 1) % 3>{}, e1);
+    if (kh == 1) issue_copies(R, it);
+    softmax(e0);
+    if (kh == 0) {            // V(it) must have landed (issued two matrix phases ago)
+      if (wave == 0) wait_vmem<6>(); else wait_vmem<5>();
+    } else {                  // K(it+2), bits(it+2)
+      wait_vmem<7>();
+    }
     __syncthreads();
+    // ---- matrix phase: scores of tile it+1 (after the last tile they score stale
+    // data and are never used), PV of tile it.  The remaining K operands and the V
+    // operands are requested two at a time between the score MFMAs, so the wave
+    // never stalls on a full LDS queue while it could feed the matrix core.
+    if (kh == 0) issue_copies(R, it);
+    read_k(IC<(r + 1) % 3>{}, IC<kPrefetchK>{}, IC<kDqk / 16>{});
+    read_v(IC<r>{});
+    score_mfma();
+    pv_mfma();
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
+    if (kh == 0) {            // K(it+2), bits(it+2)
+      if (wave == 0) wait_vmem<8>(); else wait_vmem<7>();
+    } else {                  // V(it+1)
+      wait_vmem<5>();
+    }
+    __syncthreads();
+    e0 = e1; e1 = e2; e2 = e3; e3 = e_next;
+    hid = hid_next;
+  };
+  for (int it = 0; ntiles > 0;) {
+    iteration(IC<0>{}, it);
+    if (++it >= ntiles) break;
+    iteration(IC<1>{}, it);
+    if (++it >= ntiles) break;
+    iteration(IC<2>{}, it);
+    if (++it >= ntiles) break;
   }
+  if (kh == 0) __syncthreads();
   wait_vmem<0>();
 
   // ---- merge the two key halves of each query group, normalise, store
