@@ -279,8 +279,8 @@ dflash_status dflash_mla_attn(const void* q, const void* k_nope, const void* k_r
   a.mask_bf16 = mask_dt == DFLASH_BF16;
   if (static_cast<int64_t>(B) * a.nqt * H > INT32_MAX) return fail(DFLASH_ERR_UNSUPPORTED, "too many work items");
   if (a.nkt > dflash::kMaxKeyTiles)
-    return fail(DFLASH_ERR_UNSUPPORTED, "a bf16 call supports at most %d key tiles (Lk <= %d), got Lk = %lld",
-                dflash::kMaxKeyTiles, dflash::kMaxKeyTiles * DFLASH_TILE_N, (long long)Lk);
+    return fail(DFLASH_ERR_UNSUPPORTED, "a bf16 call supports at most %d key tiles, got Lk = %lld",
+                dflash::kMaxKeyTiles, (long long)Lk);
   if (additive_mask) {
     TileLayout t;
     dflash_status st = check_occupancy_args(additive_mask, mask_dt, B, Lq, Lk, workspace, workspace_bytes, &t);

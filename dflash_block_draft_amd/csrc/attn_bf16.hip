@@ -54,12 +54,13 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kKBytes = kTileN * kDqk * 2;          // 24 KiB: 4 row blocks x 6 chunk quads x 1 KiB
 constexpr int kVBytes = kTileN * kDv * 2;           // 16 KiB: 4 row blocks x 4 chunk quads x 1 KiB
 constexpr int kBitsBytes = kTileM * 8;              // 1 KiB: one visibility word per query
-constexpr int kRing = 3;
+constexpr int kKRingN = 4;                           // K and visibility-word rings: copies lead by 2.5 tiles
+constexpr int kVRingN = 3;                           // V ring: copies lead by 2 tiles
 constexpr int kKRing = 0;
-constexpr int kVRing = kKRing + kRing * kKBytes;
-constexpr int kBitsRing = kVRing + kRing * kVBytes;
-constexpr int kRingBytes = kBitsRing + kRing * kBitsBytes;
-static_assert(kRingBytes + 4 * kLdsListEntries <= 160 * 1024, "LDS budget");
+constexpr int kVRing = kKRing + kKRingN * kKBytes;
+constexpr int kBitsRing = kVRing + kVRingN * kVBytes;
+constexpr int kRingBytes = kBitsRing + kKRingN * kBitsBytes;
+static_assert(kRingBytes <= 160 * 1024, "LDS budget");
 constexpr int kPrefetchK = 8;                        // K operand chunks read before the matrix phase
 constexpr float kSumLimit = 256.0f;                  // fast path keeps every probability <= 2^8
 constexpr uint32_t kNegInfBits = 0xFF800000u;
@@ -145,7 +146,6 @@ using IC = std::integral_constant<int, N>;
 template <bool MASK_BF16>
 __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
   __shared__ __attribute__((aligned(1024))) char smem[kRingBytes];
-  __shared__ int s_list[kLdsListEntries];
   lds_char_t* const lds = (lds_char_t*)smem;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
 
@@ -171,12 +171,16 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
   const bool q_ok = q_row < a.Lq;
   const size_t tile_row0 = static_cast<size_t>(bq) * a.nkt;
 
-  // ---- tile list of this q-tile -> LDS (entry: k-tile | class << 24, class 0 =
-  // no tile), kListPad zero entries after it; without a mask every k-tile is
-  // class 1.  The host caps ntiles at kMaxKeyTiles.
+  // ---- tile list of this q-tile (entry: k-tile | class << 24), read with scalar
+  // loads; past the end an entry is 0 (no tile); without a mask every k-tile is class 1
+  typedef __attribute__((address_space(4))) const int32_t const_i32;
   const int32_t* list = a.counts ? a.lists + tile_row0 : nullptr;
-  for (int i = t; i < ntiles + kListPad; i += kThreads)
-    s_list[i] = i >= ntiles ? 0 : (list ? list[i] : (i | (1 << 24)));
+  const const_i32* clist = (const const_i32*)(uintptr_t)(list);
+  auto entry = [&](int i) __attribute__((always_inline)) -> int {
+    if (i >= ntiles) return 0;
+    if (!list) return i | (1 << 24);
+    return clist[i];
+  };
 
   // ---- global -> LDS copy plan of this wave
   TileCopy tc;
@@ -205,21 +209,18 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
   // wait counts are constants.
   auto k0_of = [&](int e) __attribute__((always_inline)) -> int { return (e >> 24) ? (e & 0xFFFFFF) * kTileN : a.Lk; };
   auto bits_kt = [&](int e) __attribute__((always_inline)) -> int { return (e >> 24) == 2 ? (e & 0xFFFFFF) : a.nkt; };
-  auto issue_k = [&](auto SL, int k0) __attribute__((always_inline)) {
-    constexpr int sl = decltype(SL)::value;
-    dma16<sl * kKBytes>(tc.kn, tc.kn_lds, tc.voff[0], k0 * (kDn * 2));
-    dma16<sl * kKBytes + 1024>(tc.kn, tc.kn_lds, tc.voff[1], k0 * (kDn * 2));
-    dma16<sl * kKBytes>(tc.kr, tc.kr_lds, tc.voff[2], k0 * (kDr * 2));
+  auto issue_k = [&](uint32_t slot_off, int k0) __attribute__((always_inline)) {
+    dma16<0>(tc.kn, tc.kn_lds + slot_off, tc.voff[0], k0 * (kDn * 2));
+    dma16<1024>(tc.kn, tc.kn_lds + slot_off, tc.voff[1], k0 * (kDn * 2));
+    dma16<0>(tc.kr, tc.kr_lds + slot_off, tc.voff[2], k0 * (kDr * 2));
   };
-  auto issue_v = [&](auto SL, int k0) __attribute__((always_inline)) {
-    constexpr int sl = decltype(SL)::value;
-    dma16<sl * kVBytes>(tc.v, tc.v_lds, tc.voff[3], k0 * (kDv * 2));
-    dma16<sl * kVBytes + 1024>(tc.v, tc.v_lds, tc.voff[3] + 64, k0 * (kDv * 2));
+  auto issue_v = [&](uint32_t slot_off, int k0) __attribute__((always_inline)) {
+    dma16<0>(tc.v, tc.v_lds + slot_off, tc.voff[3], k0 * (kDv * 2));
+    dma16<1024>(tc.v, tc.v_lds + slot_off, tc.voff[3] + 64, k0 * (kDv * 2));
   };
   // visibility words of a class-2 tile (1 KiB, copied by wave 0); kt = nkt reads zeros
-  auto issue_bits = [&](auto SL, int kt) __attribute__((always_inline)) {
-    constexpr int sl = decltype(SL)::value;
-    if (wave == 0) dma16<kBitsRing + sl * kBitsBytes>(tc.bits, lds0, lane * 16, kt * kBitsBytes);
+  auto issue_bits = [&](uint32_t slot_off, int kt) __attribute__((always_inline)) {
+    if (wave == 0) dma16<kBitsRing>(tc.bits, lds0 + slot_off, lane * 16, kt * kBitsBytes);
   };
 
   // ---- per-lane LDS read offsets (bytes inside a slot)
@@ -262,19 +263,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
   const float scale_log2 = a.scale * kLog2e;
   const size_t mask_row = (static_cast<size_t>(b) * a.Lq + (q_ok ? q_row : 0)) * a.Lk;
 
-  // list entry i (0 past the end), wave-uniform
-  auto entry = [&](int i) __attribute__((always_inline)) -> int { return __builtin_amdgcn_readfirstlane(s_list[i]); };
-
   f32x16_t s;                    // scores of the tile between its matrix and vector phases
   bf16x8_t kf[kDqk / 16];        // K operands of the next score tile
   uint32_t pk[8];                // P^T of the tile awaiting PV, bf16 pairs
 
   // K operand chunks [C0, C1) of ring slot SL into registers
-  auto read_k = [&](auto SL, auto C0, auto C1) __attribute__((always_inline)) {
-    constexpr int sl = decltype(SL)::value;
+  auto read_k = [&](uint32_t slot_off, auto C0, auto C1) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = decltype(C0)::value; c < decltype(C1)::value; ++c) {
-      const lds_char_t* kp = ((c & 1) ? ko_ptr : ke_ptr) + sl * kKBytes + (c >> 1) * 1024;
+      const lds_char_t* kp = ((c & 1) ? ko_ptr : ke_ptr) + slot_off + (c >> 1) * 1024;
       kf[c] = as_bf16x8(*reinterpret_cast<const lds_u32x4_t*>(kp));
     }
   };
@@ -282,11 +279,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
   // the first MFMAs); for a binary tile also its hidden-key word, applied to the
   // scores in the vector phase.
   uint32_t hid_next = 0, hid = 0;   // bit 8g+c <-> key kh*32+8g+4hi+c of the tile is hidden
-  auto load_k = [&](auto SL, int e) __attribute__((always_inline)) {
-    constexpr int sl = decltype(SL)::value;
-    read_k(SL, IC<0>{}, IC<kPrefetchK>{});
+  auto load_k = [&](int slot, int e) __attribute__((always_inline)) {
+    read_k(slot * kKBytes, IC<0>{}, IC<kPrefetchK>{});
     if ((e >> 24) == 2) {
-      const uint64_t w64 = bits_ptr[sl * (kBitsBytes / 8)];
+      const uint64_t w64 = bits_ptr[slot * (kBitsBytes / 8)];
       hid_next = ~static_cast<uint32_t>(w64 >> (kh * 32 + 4 * hi));
     }
   };
@@ -300,13 +296,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
   // element e of lane (li, hi) is key 8*(e>>2) + 4*hi + (e&3) of the step; the
   // transposing reads deliver V[that key][32*j + li] as A operand.
   s16x8_t av[2][4];              // V^T operands of the tile awaiting PV
-  auto read_v = [&](auto SL) __attribute__((always_inline)) {
-    constexpr int sl = decltype(SL)::value;
+  auto read_v = [&](uint32_t slot_off) __attribute__((always_inline)) {
 #pragma unroll
     for (int step = 0; step < 2; ++step)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const lds_char_t* vp = v_ptr + sl * kVBytes + step * 4096 + j * 1024;
+        const lds_char_t* vp = v_ptr + slot_off + step * 4096 + j * 1024;
         const s16x4_t lo = ds_read_tr(vp);
         const s16x4_t hi4 = ds_read_tr(vp + 512);
         av[step][j] = s16x8_t{lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
@@ -408,17 +403,19 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
     l_run += lsum;
   };
 
-  // ---- prologue: K(0..2), bits(0..2), V(0..1) land before anyone reads
-  __syncthreads();                                              // s_list visible
-  int e0 = entry(0), e1 = entry(1), e2 = entry(2), e3 = entry(3);   // tiles t .. t+3
-  issue_k(IC<0>{}, k0_of(e0));
-  issue_k(IC<1>{}, k0_of(e1));
-  issue_k(IC<2>{}, k0_of(e2));
-  issue_v(IC<0>{}, k0_of(e0));
-  issue_v(IC<1>{}, k0_of(e1));
-  issue_bits(IC<0>{}, bits_kt(e0));
-  issue_bits(IC<1>{}, bits_kt(e1));
-  issue_bits(IC<2>{}, bits_kt(e2));
+  // ---- prologue: K(0..3), bits(0..3), V(0..1) land before anyone reads
+  int e0 = entry(0), e1 = entry(1), e2 = entry(2), e3 = entry(3), e4 = entry(4);   // tiles t .. t+4
+  int e5 = entry(5);
+  issue_k(0 * kKBytes, k0_of(e0));
+  issue_k(1 * kKBytes, k0_of(e1));
+  issue_k(2 * kKBytes, k0_of(e2));
+  issue_k(3 * kKBytes, k0_of(e3));
+  issue_v(0 * kVBytes, k0_of(e0));
+  issue_v(1 * kVBytes, k0_of(e1));
+  issue_bits(0 * kBitsBytes, bits_kt(e0));
+  issue_bits(1 * kBitsBytes, bits_kt(e1));
+  issue_bits(2 * kBitsBytes, bits_kt(e2));
+  issue_bits(3 * kBitsBytes, bits_kt(e3));
   wait_vmem<0>();
   __syncthreads();
 
@@ -426,46 +423,48 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
   //   key half 0:  S(0) | V(0) | M(0) | V(1) | M(1) | ... | M(T-1) | idle
   //   key half 1:  idle | S(0) | V(0) | M(0) | V(1) | ... | V(T-1) | M(T-1)
   // M(t) = scores of tile t+1 and PV of tile t; V(t) = softmax of tile t.
-  // Copies of K(t+3), bits(t+3), V(t+2) are issued at the start of the phase
-  // both halves run in slot 2t+2 (half 0: M(t), half 1: V(t)); each wave waits
-  // for its own copies two phases before the first read, then the barrier
-  // publishes them.
+  // Tile u lives in K / bits slot u%4 and V slot u%3.  Copies of K(t+4),
+  // bits(t+4) and V(t+2) are issued at the start of the phase both halves run
+  // in slot 2t+2 (half 0: M(t), half 1: V(t)): the slots they overwrite were
+  // last read in slot 2t+1.  Each wave waits for its own copies before the
+  // barrier that precedes their first read: K(t+2), bits(t+2) at the end of
+  // slot 2t+2 (first read in slot 2t+3), V(t+1) at the end of slot 2t+3.
   if (kh == 1) __syncthreads();
-  load_k(IC<0>{}, e0);
-  read_k(IC<0>{}, IC<kPrefetchK>{}, IC<kDqk / 16>{});
+  load_k(0, e0);
+  read_k(0, IC<kPrefetchK>{}, IC<kDqk / 16>{});
   score_mfma();
   hid = hid_next;
   __syncthreads();
 
-  auto issue_copies = [&](auto R, int it) __attribute__((always_inline)) {
-    constexpr int r = decltype(R)::value;
-    issue_k(IC<r>{}, k0_of(e3));
-    issue_bits(IC<r>{}, bits_kt(e3));
-    issue_v(IC<(r + 2) % 3>{}, k0_of(e2));
-  };
-  // list entry it+4 is read into a VGPR one iteration ahead of its readfirstlane
-  int ev = s_list[4];
-  auto iteration = [&](auto R, int it) __attribute__((always_inline)) {
-    constexpr int r = decltype(R)::value;          // it % 3: ring slot of tile it
-    const int e_next = __builtin_amdgcn_readfirstlane(ev);
-    ev = s_list[it + 5];
+  int v3 = 0;                                      // t % 3
+  for (int it = 0; it < ntiles; ++it) {
+    const int k4 = it & 3;                         // K / bits slot of tile it (and it+4)
+    const int k4n = (it + 1) & 3;                  // K / bits slot of tile it+1
+    const int v3n2 = v3 == 0 ? 2 : v3 - 1;         // V slot of tile it+2
+    const int e_next = e5;
+    e5 = entry(it + 6);
+    auto issue_copies = [&]() __attribute__((always_inline)) {
+      issue_k(k4 * kKBytes, k0_of(e4));
+      issue_bits(k4 * kBitsBytes, bits_kt(e4));
+      issue_v(v3n2 * kVBytes, k0_of(e2));
+    };
     // ---- vector phase: K operands of tile it+1, softmax of tile it
-    if (it + 1 < ntiles) load_k(IC<(r + 1) % 3>{}, e1);
-    if (kh == 1) issue_copies(R, it);
+    if (it + 1 < ntiles) load_k(k4n, e1);
+    if (kh == 1) issue_copies();
     softmax(e0);
-    if (kh == 0) {            // V(it) must have landed (issued two matrix phases ago)
+    if (kh == 0) {            // V(it): issued three phases ago, five (six) copies since
       if (wave == 0) wait_vmem<6>(); else wait_vmem<5>();
-    } else {                  // K(it+2), bits(it+2)
-      wait_vmem<7>();
+    } else {                  // K(it+2): twelve copies since
+      wait_vmem<12>();
     }
     __syncthreads();
     // ---- matrix phase: scores of tile it+1 (after the last tile they score stale
     // data and are never used), PV of tile it.  The remaining K operands and the V
     // operands are requested two at a time between the score MFMAs, so the wave
     // never stalls on a full LDS queue while it could feed the matrix core.
-    if (kh == 0) issue_copies(R, it);
-    read_k(IC<(r + 1) % 3>{}, IC<kPrefetchK>{}, IC<kDqk / 16>{});
-    read_v(IC<r>{});
+    if (kh == 0) issue_copies();
+    read_k(k4n * kKBytes, IC<kPrefetchK>{}, IC<kDqk / 16>{});
+    read_v(v3 * kVBytes);
     score_mfma();
     pv_mfma();
 #pragma unroll
@@ -474,22 +473,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
-    if (kh == 0) {            // K(it+2), bits(it+2)
-      if (wave == 0) wait_vmem<8>(); else wait_vmem<7>();
-    } else {                  // V(it+1)
+    if (kh == 0) {            // K(it+2), bits(it+2): twelve (fourteen) copies since
+      if (wave == 0) wait_vmem<14>(); else wait_vmem<12>();
+    } else {                  // V(it+1): five copies since
       wait_vmem<5>();
     }
     __syncthreads();
-    e0 = e1; e1 = e2; e2 = e3; e3 = e_next;
+    e0 = e1; e1 = e2; e2 = e3; e3 = e4; e4 = e_next;
     hid = hid_next;
-  };
-  for (int it = 0; ntiles > 0;) {
-    iteration(IC<0>{}, it);
-    if (++it >= ntiles) break;
-    iteration(IC<1>{}, it);
-    if (++it >= ntiles) break;
-    iteration(IC<2>{}, it);
-    if (++it >= ntiles) break;
+    v3 = v3 == 2 ? 0 : v3 + 1;
   }
   if (kh == 0) __syncthreads();
   wait_vmem<0>();

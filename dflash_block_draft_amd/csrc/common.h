@@ -19,13 +19,8 @@ constexpr int kTileN = 64;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// The bf16 attention keeps a q-tile's k-tile list in LDS next to its three-slot
-// K, V and visibility-word rings.  kLdsListEntries is that capacity; eight
-// entries past the end of a list are zero padding (read ahead), so a call takes
-// at most kMaxKeyTiles k-tiles (Lk <= 605696).
-constexpr int kLdsListEntries = (160 * 1024 - 3 * (kTileN * (kDqk + kDv) * 2 + kTileM * 8)) / 4;
-constexpr int kListPad = 8;
-constexpr int kMaxKeyTiles = kLdsListEntries - kListPad;
+// A tile-list entry packs the k-tile index in its low 24 bits and the class above.
+constexpr int kMaxKeyTiles = (1 << 24) - 1;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));

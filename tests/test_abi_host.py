@@ -101,9 +101,9 @@ def _attn(lib, **kw):
     (dict(mask=FAKE * 100), 3),             # masked bf16 call without a workspace
     (dict(mask=FAKE * 100, ws=FAKE * 400, wsb=16), 3),   # workspace too small
     (dict(mask=FAKE * 100, ws=FAKE * 400 + 16, wsb=1 << 20), 3),  # workspace misaligned
-    (dict(q=1 << 36, kn=2 << 36, kr=3 << 36, v=4 << 36, out=5 << 36, mask=6 << 36, Lk=700000,
-          ws=7 << 36, wsb=1 << 34), 2),     # masked bf16 call with Lk > 605696
-    (dict(q=1 << 36, kn=2 << 36, kr=3 << 36, v=4 << 36, out=5 << 36, Lk=700000), 2),   # unmasked, same limit
+    (dict(q=1 << 44, kn=2 << 44, kr=3 << 44, v=4 << 44, out=5 << 44, mask=6 << 44, Lk=1 << 30,
+          ws=7 << 44, wsb=1 << 40), 2),     # masked bf16 call with 2^24 key tiles
+    (dict(q=1 << 44, kn=2 << 44, kr=3 << 44, v=4 << 44, out=5 << 44, Lk=1 << 30), 2),   # unmasked, same limit
 ])
 def test_attn_validation(lib, kw, status):
     assert _attn(lib, **kw) == status
