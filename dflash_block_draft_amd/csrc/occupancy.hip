@@ -10,9 +10,10 @@
 //
 // The mask is head-independent, so this runs once per call (or once for every
 // draft layer, which all receive the same mask) and is pure HBM streaming:
-// each mask row segment is read exactly once, one element per lane, so a wave
-// load covers a full 256 B (f32) / 128 B (bf16) row segment and a ballot of the
-// lanes is directly that row's visibility word.
+// each mask entry is read exactly once.  Masks whose rows start 16-byte aligned
+// are read 16 bytes per lane; others one entry per lane, where a wave load
+// covers a 64-entry row segment and a ballot of the lanes is that row's
+// visibility word.
 #include "common.h"
 #include "launch.h"
 
@@ -82,40 +83,112 @@ __global__ void __launch_bounds__(kClassifyThreads) classify_tiles(OccupancyArgs
   }
 }
 
-// One workgroup: (1) each wave compacts the non-empty k-tiles of its
-// (b, q-tile) rows into an increasing list; (2) the q-tiles are ranked by
-// decreasing list length (ties: lower index first) so the attention launch can
-// start the longest work first.
-constexpr int kListThreads = 1024;
-constexpr int kMaxRankItems = 4096;
+// Same classification with 16-byte loads, for masks whose rows start 16-byte
+// aligned (Lk a multiple of 8 for bf16, of 4 for f32): lane t reads chunk t % CH
+// (EPL consecutive entries) of rows t / CH + (256 / CH) * i.  A chunk's
+// visibility bits are assembled into the row words through LDS.
+template <bool BF16>
+__global__ void __launch_bounds__(kClassifyThreads) classify_tiles_vec(OccupancyArgs a) {
+  constexpr int EPL = BF16 ? 8 : 4;                 // entries per 16-byte chunk
+  constexpr int CH = kTileN / EPL;                  // chunks per tile row
+  constexpr int RPB = kClassifyThreads / CH;        // rows per block-wide load
+  constexpr int NIT = kTileM / RPB;
+  __shared__ uint8_t s_vis[kTileM][CH];
+  __shared__ int s_flags[kClassifyWaves];
+  const int64_t tile = blockIdx.x;
+  const int kt = static_cast<int>(tile % a.nkt);
+  const int64_t rest = tile / a.nkt;
+  const int qt = static_cast<int>(rest % a.nqt);
+  const int b = static_cast<int>(rest / a.nqt);
+  const int r0 = qt * kTileM, c0 = kt * kTileN;
+  const int rows = min(kTileM, a.Lq - r0);
+  const int cols = min(kTileN, a.Lk - c0);          // a multiple of EPL here
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int c = t % CH, rr = t / CH;
+  const bool col_ok = c * EPL < cols;
+  const size_t esz = BF16 ? 2 : 4;
+  const char* base = static_cast<const char*>(a.mask) + ((static_cast<size_t>(b) * a.Lq + r0) * a.Lk + c0 + c * EPL) * esz;
 
-__global__ void __launch_bounds__(kListThreads) build_lists(OccupancyArgs a) {
-  __shared__ int s_counts[kMaxRankItems];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int nrows = a.B * a.nqt;
-  for (int row = wave; row < nrows; row += kListThreads / 64) {
-    const uint8_t* cls = a.classes + static_cast<size_t>(row) * a.nkt;
-    int32_t* list = a.lists + static_cast<size_t>(row) * a.nkt;
-    int base = 0;
-    for (int k0 = 0; k0 < a.nkt; k0 += 64) {
-      const int kt = k0 + lane;
-      const int c = kt < a.nkt ? cls[kt] : 0;
-      const uint64_t bal = __ballot(c != 0);
-      const int pre = __popcll(bal & ((1ull << lane) - 1ull));
-      if (c != 0) list[base + pre] = kt | (c << 24);
-      base += __popcll(bal);
-    }
-    if (lane == 0) a.counts[row] = base;
+  u32x4_t w[NIT];
+#pragma unroll
+  for (int i = 0; i < NIT; ++i) {                   // all loads in flight together
+    const int r = rr + RPB * i;
+    const u32x4_t ninf = BF16 ? u32x4_t{0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u}
+                              : u32x4_t{0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u};
+    w[i] = (r < rows && col_ok) ? ldg16(base + static_cast<size_t>(r) * a.Lk * esz) : ninf;
   }
+  bool any_vis = false, any_nonzero = false, any_other = false;
+#pragma unroll
+  for (int i = 0; i < NIT; ++i) {
+    const int r = rr + RPB * i;
+    uint32_t vis = 0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const uint32_t x = BF16 ? ((w[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu) : w[i][e];
+      const bool zero = BF16 ? (x & 0x7FFFu) == 0u : (x & 0x7FFFFFFFu) == 0u;
+      const bool ninf = BF16 ? x == 0xFF80u : x == 0xFF800000u;
+      vis |= static_cast<uint32_t>(zero) << e;
+      if (r < rows && col_ok) {                     // entries outside the mask do not count
+        any_vis |= !ninf;
+        any_nonzero |= !zero;
+        any_other |= !zero && !ninf;
+      }
+    }
+    s_vis[r][c] = static_cast<uint8_t>(vis);        // outside the mask: loaded as -inf, bits 0
+  }
+  int flags = (__ballot(any_vis) ? 1 : 0) | (__ballot(any_nonzero) ? 2 : 0) | (__ballot(any_other) ? 4 : 0);
+  if (lane == 0) s_flags[wave] = flags;
   __syncthreads();
-  if (nrows > kMaxRankItems) {  // too many q-tiles to rank here: natural order
-    for (int i = threadIdx.x; i < nrows; i += kListThreads) a.order[i] = i;
+  int f = 0;
+#pragma unroll
+  for (int i = 0; i < kClassifyWaves; ++i) f |= s_flags[i];
+  const int cls = !(f & 1) ? 0 : (!(f & 2) ? 1 : ((f & 4) ? 3 : 2));
+  if (t == 0) a.classes[tile] = static_cast<uint8_t>(cls);
+  if (cls == 2 && t < kTileM) {
+    uint64_t word = 0;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) word |= static_cast<uint64_t>(s_vis[t][k]) << (EPL * k);
+    a.bits[static_cast<size_t>(tile) * kTileM + t] = t < rows ? word : 0ull;
+  }
+}
+
+// One workgroup per (b, q-tile) row: compact its non-empty k-tiles into an
+// increasing list (ballot prefix counts, 256 candidates per step).
+constexpr int kRowThreads = 256;
+__global__ void __launch_bounds__(kRowThreads) build_row_lists(OccupancyArgs a) {
+  __shared__ int s_wave[kRowThreads / 64];
+  const int row = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const uint8_t* cls = a.classes + static_cast<size_t>(row) * a.nkt;
+  int32_t* list = a.lists + static_cast<size_t>(row) * a.nkt;
+  int base = 0;
+  for (int k0 = 0; k0 < a.nkt; k0 += kRowThreads) {
+    const int kt = k0 + t;
+    const int c = kt < a.nkt ? cls[kt] : 0;
+    const uint64_t bal = __ballot(c != 0);
+    if (lane == 0) s_wave[wave] = __popcll(bal);
+    __syncthreads();
+    int before = base;
+    for (int i = 0; i < wave; ++i) before += s_wave[i];
+    if (c != 0) list[before + __popcll(bal & ((1ull << lane) - 1ull))] = kt | (c << 24);
+    for (int i = 0; i < kRowThreads / 64; ++i) base += s_wave[i];
+    __syncthreads();
+  }
+  if (t == 0) a.counts[row] = base;
+}
+
+// One workgroup: rank the (b, q-tile) rows by decreasing list length (ties:
+// lower index first) so the attention launch starts the longest work first.
+__global__ void __launch_bounds__(1024) rank_rows(OccupancyArgs a) {
+  __shared__ int s_counts[4096];
+  const int nrows = a.B * a.nqt;
+  if (nrows > 4096) {  // too many q-tiles to rank here: natural order
+    for (int i = threadIdx.x; i < nrows; i += 1024) a.order[i] = i;
     return;
   }
-  for (int i = threadIdx.x; i < nrows; i += kListThreads) s_counts[i] = a.counts[i];
+  for (int i = threadIdx.x; i < nrows; i += 1024) s_counts[i] = a.counts[i];
   __syncthreads();
-  for (int i = threadIdx.x; i < nrows; i += kListThreads) {
+  for (int i = threadIdx.x; i < nrows; i += 1024) {
     const int c = s_counts[i];
     int rank = 0;
     for (int j = 0; j < nrows; ++j) {
@@ -148,13 +221,21 @@ hipError_t launch_lists_all_tiles(const OccupancyArgs& a, hipStream_t s) {
 
 hipError_t launch_occupancy(const OccupancyArgs& a, hipStream_t s) {
   const int64_t ntiles = static_cast<int64_t>(a.B) * a.nqt * a.nkt;
-  if (a.mask_bf16)
-    hipLaunchKernelGGL(classify_tiles<true>, dim3(static_cast<unsigned>(ntiles)), dim3(kClassifyThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(classify_tiles<false>, dim3(static_cast<unsigned>(ntiles)), dim3(kClassifyThreads), 0, s, a);
+  const dim3 grid(static_cast<unsigned>(ntiles)), block(kClassifyThreads);
+  const bool vec = a.Lk % (a.mask_bf16 ? 8 : 4) == 0;   // rows start 16-byte aligned (the base is)
+  if (a.mask_bf16) {
+    if (vec) hipLaunchKernelGGL(classify_tiles_vec<true>, grid, block, 0, s, a);
+    else hipLaunchKernelGGL(classify_tiles<true>, grid, block, 0, s, a);
+  } else {
+    if (vec) hipLaunchKernelGGL(classify_tiles_vec<false>, grid, block, 0, s, a);
+    else hipLaunchKernelGGL(classify_tiles<false>, grid, block, 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(build_lists, dim3(1), dim3(kListThreads), 0, s, a);
+  hipLaunchKernelGGL(build_row_lists, dim3(static_cast<unsigned>(a.B * a.nqt)), dim3(kRowThreads), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(rank_rows, dim3(1), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 

@@ -219,14 +219,33 @@ def test_single_visible_key_returns_its_value(dev):
 
 # ------------------------------------------------------------- occupancy, skip, determinism
 
+def _tile_map_masks():
+    """Masks for the occupancy pass: 16-byte-aligned rows (Lk % 8 == 0 for bf16,
+    % 4 == 0 for f32; the vectorised path) and unaligned rows (the per-entry path),
+    with ragged last tiles, plus one with general values, NaN and +inf entries."""
+    yield W.config(2).mask
+    yield W.custom(seed=18, B=3, H=1, ctx=450, A=9, bs=16, mask_dtype="f32").mask      # Lk 594: per-entry f32
+    yield W.custom(seed=21, B=2, H=1, ctx=452, A=9, bs=16, mask_dtype="f32").mask      # Lk 596: vector f32, ragged
+    yield W.custom(seed=22, B=2, H=1, ctx=456, A=9, bs=16, mask_dtype="bf16").mask     # Lk 600: vector bf16, ragged
+    yield W.custom(seed=23, B=1, H=1, ctx=455, A=9, bs=16, mask_dtype="bf16").mask     # Lk 599: per-entry bf16
+    for dt in ("f32", "bf16"):
+        m = W.custom(seed=24, B=1, H=1, ctx=504, A=8, bs=16, mask_dtype=dt).mask.clone()   # Lk 632
+        m[0, 0, 3, 5] = 0.5           # general value inside an otherwise binary tile
+        m[0, 0, 70, 200] = float("nan")
+        m[0, 0, 100, 400] = float("inf")
+        m[0, 0, 1, 600:632] = -2.0    # general values in the ragged last tile
+        yield m
+
+
 def test_tile_map_exact(dev):
-    for wl in (W.config(2), W.custom(seed=18, B=3, H=1, ctx=450, A=9, bs=16, mask_dtype="f32")):
-        say(f"tile map {wl.name}")
-        md = wl.mask.to(dev)
+    for mask in _tile_map_masks():
+        B, _, Lq, Lk = mask.shape
+        say(f"tile map {tuple(mask.shape)} {mask.dtype}")
+        md = mask.to(dev)
         ws = mla.mask_occupancy(md)
         torch.cuda.synchronize()
-        tm = mla.tile_map_view(ws, wl.B, wl.Lq, wl.Lk)
-        want = oracle.tile_classes(wl.mask, mla.TILE_M, mla.TILE_N)
+        tm = mla.tile_map_view(ws, B, Lq, Lk)
+        want = oracle.tile_classes(mask, mla.TILE_M, mla.TILE_N)
         got = tm["classes"].cpu().numpy()
         assert np.array_equal(got, want)
         counts = tm["counts"].cpu().numpy()
@@ -240,7 +259,7 @@ def test_tile_map_exact(dev):
         order = tm["order"].cpu().numpy()
         want_order = sorted(range(flat.size), key=lambda i: (-flat[i], i))
         assert list(order) == want_order
-        want_bits = oracle.tile_bits(wl.mask, mla.TILE_M, mla.TILE_N, want)
+        want_bits = oracle.tile_bits(mask, mla.TILE_M, mla.TILE_N, want)
         got_bits = tm["bits"].cpu().numpy().view(np.uint64)
         sel = want == 2
         assert sel.sum() > 0
