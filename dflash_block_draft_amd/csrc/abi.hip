@@ -64,7 +64,7 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 
 struct TileLayout {
   int64_t nqt, nkt;
-  size_t classes, counts, lists, order, bits, total;
+  size_t classes, counts, lists, order, bits, sync, total;
 };
 
 bool tile_layout(int64_t B, int64_t Lq, int64_t Lk, TileLayout* t) {
@@ -78,7 +78,8 @@ bool tile_layout(int64_t B, int64_t Lq, int64_t Lk, TileLayout* t) {
   t->lists = t->counts + align_up(static_cast<size_t>(rows) * 4, 256);
   t->order = t->lists + align_up(static_cast<size_t>(cells) * 4, 256);
   t->bits = t->order + align_up(static_cast<size_t>(rows) * 4, 256);
-  t->total = t->bits + static_cast<size_t>(cells) * DFLASH_TILE_M * 8;
+  t->sync = align_up(t->bits + static_cast<size_t>(cells) * DFLASH_TILE_M * 8, 256);
+  t->total = t->sync + 256;
   return true;
 }
 
@@ -157,6 +158,7 @@ static dflash::OccupancyArgs occupancy_args(const void* mask, int mask_dt, int64
   o.lists = reinterpret_cast<int32_t*>(w + t.lists);
   o.order = reinterpret_cast<int32_t*>(w + t.order);
   o.bits = reinterpret_cast<uint64_t*>(w + t.bits);
+  o.sync = reinterpret_cast<uint32_t*>(w + t.sync);
   return o;
 }
 

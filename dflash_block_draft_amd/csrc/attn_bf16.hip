@@ -459,20 +459,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
     }
     __syncthreads();
     // ---- matrix phase: scores of tile it+1 (after the last tile they score stale
-    // data and are never used), PV of tile it.  The remaining K operands and the V
-    // operands are requested two at a time between the score MFMAs, so the wave
-    // never stalls on a full LDS queue while it could feed the matrix core.
+    // data and are never used), PV of tile it.  The remaining K operands and all V
+    // operands are requested before the first MFMA; the first eight score MFMAs run
+    // on operands already in registers while they arrive.
     if (kh == 0) issue_copies();
     read_k(k4n * kKBytes, IC<kPrefetchK>{}, IC<kDqk / 16>{});
     read_v(v3 * kVBytes);
+    __builtin_amdgcn_sched_barrier(0);
     score_mfma();
     pv_mfma();
-#pragma unroll
-    for (int i = 0; i < 10; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
     if (kh == 0) {            // K(it+2), bits(it+2): twelve (fourteen) copies since
       if (wave == 0) wait_vmem<14>(); else wait_vmem<12>();
     } else {                  // V(it+1): five copies since

@@ -38,6 +38,7 @@ struct OccupancyArgs {
   int B, Lq, Lk, nqt, nkt;
   uint8_t* classes; int32_t* counts; int32_t* lists; int32_t* order;
   uint64_t* bits;   // [B*nqt*nkt, kTileM]: bit k of row r = entry (r, k) is +-0 (class-2 tiles only)
+  uint32_t* sync;   // one counter: list workgroups done (zeroed by the classify pass)
 };
 
 struct ExpandArgs {

@@ -38,6 +38,7 @@ __global__ void __launch_bounds__(kClassifyThreads) classify_tiles(OccupancyArgs
   const int cols = min(kTileN, a.Lk - c0);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool col_ok = lane < cols;
+  if (tile == 0 && threadIdx.x == 0) *a.sync = 0u;   // the list pass that follows counts its workgroups
   const uint64_t valid = cols == 64 ? ~0ull : ((1ull << cols) - 1ull);
 
   // flag bits: 1 = some entry is not -inf, 2 = some entry is not +-0, 4 = some entry is neither
@@ -105,6 +106,7 @@ __global__ void __launch_bounds__(kClassifyThreads) classify_tiles_vec(Occupancy
   const int cols = min(kTileN, a.Lk - c0);          // a multiple of EPL here
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int c = t % CH, rr = t / CH;
+  if (tile == 0 && t == 0) *a.sync = 0u;              // the list pass that follows counts its workgroups
   const bool col_ok = c * EPL < cols;
   const size_t esz = BF16 ? 2 : 4;
   const char* base = static_cast<const char*>(a.mask) + ((static_cast<size_t>(b) * a.Lq + r0) * a.Lk + c0 + c * EPL) * esz;
@@ -152,11 +154,33 @@ __global__ void __launch_bounds__(kClassifyThreads) classify_tiles_vec(Occupancy
   }
 }
 
-// One workgroup per (b, q-tile) row: compact its non-empty k-tiles into an
-// increasing list (ballot prefix counts, 256 candidates per step).
+// Rank rows by decreasing list length (ties: lower index first) so the attention
+// launch starts the longest work first: order[rank] = row.  n <= kMaxFusedRank.
 constexpr int kRowThreads = 256;
-__global__ void __launch_bounds__(kRowThreads) build_row_lists(OccupancyArgs a) {
+constexpr int kMaxFusedRank = 512;
+__device__ void rank_rows_block(const OccupancyArgs& a, int* s_counts, int nthreads) {
+  const int nrows = a.B * a.nqt;
+  for (int i = threadIdx.x; i < nrows; i += nthreads)
+    s_counts[i] = __hip_atomic_load(a.counts + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  for (int i = threadIdx.x; i < nrows; i += nthreads) {
+    const int c = s_counts[i];
+    int rank = 0;
+    for (int j = 0; j < nrows; ++j) {
+      const int cj = s_counts[j];
+      rank += (cj > c) || (cj == c && j < i);
+    }
+    a.order[rank] = i;
+  }
+}
+
+// One workgroup per (b, q-tile) row: compact its non-empty k-tiles into an
+// increasing list (ballot prefix counts, 256 candidates per step).  With few
+// rows, the last workgroup to finish (counted in a.sync) also ranks the rows.
+__global__ void __launch_bounds__(kRowThreads) build_row_lists(OccupancyArgs a, int fuse_rank) {
   __shared__ int s_wave[kRowThreads / 64];
+  __shared__ int s_counts[kMaxFusedRank];
+  __shared__ int s_last;
   const int row = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const uint8_t* cls = a.classes + static_cast<size_t>(row) * a.nkt;
@@ -174,11 +198,23 @@ __global__ void __launch_bounds__(kRowThreads) build_row_lists(OccupancyArgs a) 
     for (int i = 0; i < kRowThreads / 64; ++i) base += s_wave[i];
     __syncthreads();
   }
-  if (t == 0) a.counts[row] = base;
+  if (!fuse_rank) {
+    if (t == 0) a.counts[row] = base;
+    return;
+  }
+  if (t == 0) {
+    __hip_atomic_store(a.counts + row, base, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned done = __hip_atomic_fetch_add(a.sync, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = done == static_cast<unsigned>(a.B * a.nqt - 1);
+  }
+  __syncthreads();
+  if (s_last) {
+    __atomic_thread_fence(__ATOMIC_ACQUIRE);
+    rank_rows_block(a, s_counts, kRowThreads);
+  }
 }
 
-// One workgroup: rank the (b, q-tile) rows by decreasing list length (ties:
-// lower index first) so the attention launch starts the longest work first.
+// One workgroup ranks many rows (more than kMaxFusedRank).
 __global__ void __launch_bounds__(1024) rank_rows(OccupancyArgs a) {
   __shared__ int s_counts[4096];
   const int nrows = a.B * a.nqt;
@@ -186,17 +222,7 @@ __global__ void __launch_bounds__(1024) rank_rows(OccupancyArgs a) {
     for (int i = threadIdx.x; i < nrows; i += 1024) a.order[i] = i;
     return;
   }
-  for (int i = threadIdx.x; i < nrows; i += 1024) s_counts[i] = a.counts[i];
-  __syncthreads();
-  for (int i = threadIdx.x; i < nrows; i += 1024) {
-    const int c = s_counts[i];
-    int rank = 0;
-    for (int j = 0; j < nrows; ++j) {
-      const int cj = s_counts[j];
-      rank += (cj > c) || (cj == c && j < i);
-    }
-    a.order[rank] = i;
-  }
+  rank_rows_block(a, s_counts, 1024);
 }
 
 // Every k-tile of every (b, q-tile), empty ones relabelled class 3 (their -inf
@@ -232,9 +258,11 @@ hipError_t launch_occupancy(const OccupancyArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(build_row_lists, dim3(static_cast<unsigned>(a.B * a.nqt)), dim3(kRowThreads), 0, s, a);
+  const int nrows = a.B * a.nqt;
+  const int fuse = nrows <= kMaxFusedRank;
+  hipLaunchKernelGGL(build_row_lists, dim3(static_cast<unsigned>(nrows)), dim3(kRowThreads), 0, s, a, fuse);
   e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || fuse) return e;
   hipLaunchKernelGGL(rank_rows, dim3(1), dim3(1024), 0, s, a);
   return hipGetLastError();
 }

@@ -126,6 +126,7 @@ size_t dflash_mla_attn_workspace_bytes(int64_t B, int64_t Lq, int64_t Lk);
  *                                               bit k of row r is set iff mask entry
  *                                               (qt*M + r, kt*N + k) is +-0 (rows/columns past
  *                                               the mask read 0); other tiles' words are unspecified
+ * After bits the workspace holds one private counter the occupancy pass uses.
  * n_q_tiles = ceil(Lq / DFLASH_TILE_M), n_k_tiles = ceil(Lk / DFLASH_TILE_N).
  */
 dflash_status dflash_mla_tile_map_layout(int64_t B, int64_t Lq, int64_t Lk,

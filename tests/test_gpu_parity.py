@@ -266,6 +266,28 @@ def test_tile_map_exact(dev):
         assert np.array_equal(got_bits[sel], want_bits[sel])
 
 
+def test_tile_map_many_rows_order(dev):
+    """More (b, q-tile) rows than the list pass ranks itself: the separate ranking
+    kernel orders them (decreasing count, ties by index)."""
+    rng = np.random.default_rng(25)
+    B, Lq, Lk = 3, 128 * 200, 130                       # 600 rows, 3 k-tiles (one ragged)
+    m = np.full((B, 1, Lq, Lk), -np.inf, dtype=np.float32)
+    vis = rng.random((B, Lq // 128, 3)) < 0.5
+    for b, qt, kt in zip(*np.nonzero(vis)):
+        r = qt * 128 + rng.integers(0, 128)
+        m[b, 0, r, kt * 64 + rng.integers(0, min(64, Lk - kt * 64))] = 0.0
+    mask = torch.from_numpy(m).to(torch.bfloat16)
+    ws = mla.mask_occupancy(mask.to(dev))
+    torch.cuda.synchronize()
+    tm = mla.tile_map_view(ws, B, Lq, Lk)
+    want = oracle.tile_classes(mask, mla.TILE_M, mla.TILE_N)
+    assert np.array_equal(tm["classes"].cpu().numpy(), want)
+    flat = tm["counts"].cpu().numpy().reshape(-1)
+    assert np.array_equal(flat, (want != 0).sum(-1).reshape(-1))
+    want_order = sorted(range(flat.size), key=lambda i: (-flat[i], i))
+    assert list(tm["order"].cpu().numpy()) == want_order
+
+
 def test_skip_on_equals_skip_off_bitwise(dev):
     wl = W.custom(seed=19, B=2, H=4, ctx=900, A=12, bs=16, dtype="bf16", mask_dtype="bf16")
     q, kn, kr, v, m = _to(dev, wl.q, wl.k_nope, wl.k_rope, wl.v, wl.mask)
