@@ -43,7 +43,9 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="2", help="headline workload: 0,1,2,3a,3b,4")
-    p.add_argument("--secondary", default="4,1,3a,3b", help="comma list, or 'none'")
+    p.add_argument("--secondary", default="4,1,3a,3b,2s,4s",
+                   help="comma list, or 'none'; a trailing 's' takes the mask from the block "
+                        "structure (anchors) instead of the dense tensor")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -57,6 +59,7 @@ def parse():
 
 def make_workload(key: str):
     from dflash_block_draft_amd import workloads as W
+    key = key.rstrip("s")
     if key == "3a":
         return W.config(3, block_size=8)
     if key == "3b":
@@ -75,7 +78,7 @@ def kernel_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measure(wl, steps: int, warmup: int) -> dict:
+def measure(wl, steps: int, warmup: int, structured: bool = False) -> dict:
     import torch
     from dflash_block_draft_amd import mla
     from dflash_block_draft_amd import workloads as W
@@ -90,6 +93,8 @@ def measure(wl, steps: int, warmup: int) -> dict:
     else:
         kn, v = wl.k_nope.to(dev), wl.v.to(dev)
     ws = mla.new_workspace(wl.B, wl.Lq, wl.Lk, dev)
+    anchors = torch.as_tensor(wl.anchors.astype("int32")).to(dev)
+    ctx_valid = torch.full((wl.B,), wl.ctx_valid, dtype=torch.int32, device=dev)
     out = torch.empty((wl.B, wl.H, wl.Lq, wl.Dv), dtype=q.dtype, device=dev)
     vis_flops = W.visible_flops(wl.mask, wl.B, wl.H, wl.Lq, wl.Lk)
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -99,9 +104,15 @@ def measure(wl, steps: int, warmup: int) -> dict:
             marks[0].record()
             mla.latent_expand(lat, w, wl.H, k_nope=kn, v=v)
         marks[1].record()
-        mla.mask_occupancy(m, ws)
-        marks[2].record()
-        mla.mla_attn(q, kn, kr, v, m, wl.scale, out=out, workspace=ws, reuse_tile_map=True)
+        if structured:
+            mla.block_occupancy(anchors, wl.block_size, wl.ctx, ctx_valid, ws)
+            marks[2].record()
+            mla.mla_attn_blocks(q, kn, kr, v, anchors, wl.block_size, wl.ctx, ctx_valid, wl.scale,
+                                out=out, workspace=ws, reuse_tile_map=True)
+        else:
+            mla.mask_occupancy(m, ws)
+            marks[2].record()
+            mla.mla_attn(q, kn, kr, v, m, wl.scale, out=out, workspace=ws, reuse_tile_map=True)
         marks[3].record()
 
     scratch = [ev() for _ in range(4)]
@@ -135,6 +146,7 @@ def measure(wl, steps: int, warmup: int) -> dict:
                   + wl.B * wl.H * wl.Lq * wl.Dv) * esz
     res = {
         "workload": wl.name,
+        "mask_from": "block structure (anchors, ctx_valid)" if structured else "dense tensor",
         "shape": {"B": wl.B, "H": wl.H, "Lq": wl.Lq, "Lk": wl.Lk, "ctx": wl.ctx,
                   "anchors": wl.num_anchors, "block_size": wl.block_size},
         "visible_gflop": round(vis_flops / 1e9, 3),
@@ -146,7 +158,7 @@ def measure(wl, steps: int, warmup: int) -> dict:
         "attn_kernel_ms_min": round(att_min, 4),
         "attn_kernel_tflops": round(vis_flops / (att * 1e-3) / 1e12, 2),
         "occupancy_ms": round(occ, 4),
-        "occupancy_mask_GBs": round(mask_bytes / (occ * 1e-3) / 1e9, 1),
+        "occupancy_mask_GBs": None if structured else round(mask_bytes / (occ * 1e-3) / 1e9, 1),
         "tile_fractions_128x64": frac,
         "attn_algorithmic_bytes": attn_bytes,
         "mask_bytes": mask_bytes,
@@ -155,7 +167,7 @@ def measure(wl, steps: int, warmup: int) -> dict:
         xf = 2 * wl.B * wl.Lk * 512 * wl.H * (wl.Dn + wl.Dv)
         res["expand_ms"] = round(exp_ms, 4)
         res["expand_tflops"] = round(xf / (exp_ms * 1e-3) / 1e12, 2)
-    del q, kr, m, kn, v, ws, out
+    del q, kr, m, kn, v, ws, out, anchors, ctx_valid
     if expand:
         del lat, w
     torch.cuda.empty_cache()
@@ -292,7 +304,7 @@ def main():
             log(f"building workload {key}")
             w2 = make_workload(key)
             log(describe(w2))
-            r = measure(w2, max(3, args.steps // 2), max(1, args.warmup // 2))
+            r = measure(w2, max(3, args.steps // 2), max(1, args.warmup // 2), structured=key.endswith("s"))
             log(f"{key}: {r['ms_per_step']} ms/step, {r['tflops']} TFLOP/s ({r['pct_bf16_peak']}%)")
             secondary.append(r)
             del w2

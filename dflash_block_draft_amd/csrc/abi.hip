@@ -159,6 +159,52 @@ static dflash::OccupancyArgs occupancy_args(const void* mask, int mask_dt, int64
   o.order = reinterpret_cast<int32_t*>(w + t.order);
   o.bits = reinterpret_cast<uint64_t*>(w + t.bits);
   o.sync = reinterpret_cast<uint32_t*>(w + t.sync);
+  o.anchors = nullptr;
+  o.ctx_valid = nullptr;
+  o.A = o.bs = o.ctx = 0;
+  return o;
+}
+
+// Validation shared by the block-structure entry points: Lq = A * block_size,
+// Lk = ctx + Lq; returns the tile layout.
+static dflash_status check_block_args(const int32_t* anchors, const int32_t* ctx_valid, int64_t B, int64_t A,
+                                      int64_t block_size, int64_t ctx, const void* ws, size_t ws_bytes,
+                                      TileLayout* t, int64_t* Lq, int64_t* Lk) {
+  if (!anchors) return fail(DFLASH_ERR_INVALID_ARG, "anchors is NULL");
+  if ((reinterpret_cast<uintptr_t>(anchors) & 3u) != 0 || (reinterpret_cast<uintptr_t>(ctx_valid) & 3u) != 0)
+    return fail(DFLASH_ERR_INVALID_ARG, "anchors / ctx_valid must be 4-byte aligned");
+  if (B <= 0 || A <= 0 || block_size <= 0 || ctx < 0)
+    return fail(DFLASH_ERR_INVALID_ARG, "B, A, block_size must be positive and ctx >= 0 (got %lld, %lld, %lld, %lld)",
+                (long long)B, (long long)A, (long long)block_size, (long long)ctx);
+  int64_t lq;
+  if (!mul_ok(A, block_size, &lq) || lq > INT32_MAX || ctx > INT32_MAX - lq)
+    return fail(DFLASH_ERR_UNSUPPORTED, "A * block_size + ctx must fit in int32");
+  *Lq = lq;
+  *Lk = ctx + lq;
+  if (!tile_layout(B, *Lq, *Lk, t)) return fail(DFLASH_ERR_INVALID_ARG, "tile map size overflows");
+  if (B > INT32_MAX) return fail(DFLASH_ERR_UNSUPPORTED, "B must fit in int32");
+  if (t->nkt >= (int64_t(1) << 24)) return fail(DFLASH_ERR_UNSUPPORTED, "Lk too large for the tile lists");
+  if (B * t->nqt * t->nkt > INT32_MAX) return fail(DFLASH_ERR_UNSUPPORTED, "too many tiles");
+  if (!ws) return fail(DFLASH_ERR_WORKSPACE, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(DFLASH_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (ws_bytes < t->total)
+    return fail(DFLASH_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, t->total);
+  const Range rw = range_of(ws, t->total);
+  if (overlaps(rw, range_of(anchors, static_cast<size_t>(B) * A * 4)) ||
+      (ctx_valid && overlaps(rw, range_of(ctx_valid, static_cast<size_t>(B) * 4))))
+    return fail(DFLASH_ERR_INVALID_ARG, "the workspace overlaps anchors / ctx_valid");
+  return ok();
+}
+
+static dflash::OccupancyArgs block_args(const int32_t* anchors, const int32_t* ctx_valid, int64_t B, int64_t A,
+                                        int64_t block_size, int64_t ctx, int64_t Lq, int64_t Lk, void* ws,
+                                        const TileLayout& t) {
+  dflash::OccupancyArgs o = occupancy_args(nullptr, DFLASH_F32, B, Lq, Lk, ws, t);
+  o.anchors = anchors;
+  o.ctx_valid = ctx_valid;
+  o.A = static_cast<int>(A);
+  o.bs = static_cast<int>(block_size);
+  o.ctx = static_cast<int>(ctx);
   return o;
 }
 
@@ -222,7 +268,7 @@ dflash_status dflash_mla_attn(const void* q, const void* k_nope, const void* k_r
     return fail(DFLASH_ERR_INVALID_ARG, "sizes must be positive (B=%lld H=%lld Lq=%lld Lk=%lld)", (long long)B, (long long)H, (long long)Lq, (long long)Lk);
   if (!std::isfinite(scale) || !(scale > 0.f)) return fail(DFLASH_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (!valid_dtype(dt) || !valid_dtype(mask_dt)) return fail(DFLASH_ERR_INVALID_ARG, "dtype is not a dflash_dtype");
-  if (flags & ~(DFLASH_ATTN_REUSE_TILE_MAP | DFLASH_ATTN_NO_TILE_SKIP))
+  if (flags & ~(DFLASH_ATTN_REUSE_TILE_MAP | DFLASH_ATTN_NO_TILE_SKIP | DFLASH_ATTN_CHECK_ONLY))
     return fail(DFLASH_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   if (Dn != dflash::kDn || Dr != dflash::kDr || Dv != dflash::kDv)
     return fail(DFLASH_ERR_UNSUPPORTED, "only Dn=128, Dr=64, Dv=128 are built (got %lld, %lld, %lld)", (long long)Dn, (long long)Dr, (long long)Dv);
@@ -245,6 +291,10 @@ dflash_status dflash_mla_attn(const void* q, const void* k_nope, const void* k_r
   };
   for (const Range& r : ins)
     if (overlaps(ro, r)) return fail(DFLASH_ERR_INVALID_ARG, "out overlaps an input");
+  if (dt == DFLASH_BF16 && (Lk + DFLASH_TILE_N - 1) / DFLASH_TILE_N > dflash::kMaxKeyTiles)
+    return fail(DFLASH_ERR_UNSUPPORTED, "a bf16 call supports at most %d key tiles, got Lk = %lld",
+                dflash::kMaxKeyTiles, (long long)Lk);
+  if (flags & DFLASH_ATTN_CHECK_ONLY) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   if (dt == DFLASH_F32) {
@@ -306,6 +356,72 @@ dflash_status dflash_mla_attn(const void* q, const void* k_nope, const void* k_r
     a.order = o.order;
     a.bits = o.bits;
   }
+  return hip_status(dflash::launch_attn_bf16(a, s), "bf16 attention launch");
+}
+
+dflash_status dflash_mla_block_occupancy(const int32_t* anchors, const int32_t* ctx_valid, int64_t B, int64_t A,
+                                         int64_t block_size, int64_t ctx, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  TileLayout t;
+  int64_t Lq, Lk;
+  dflash_status st = check_block_args(anchors, ctx_valid, B, A, block_size, ctx, workspace, workspace_bytes, &t, &Lq, &Lk);
+  if (st != DFLASH_OK) return st;
+  const dflash::OccupancyArgs o = block_args(anchors, ctx_valid, B, A, block_size, ctx, Lq, Lk, workspace, t);
+  return hip_status(dflash::launch_block_occupancy(o, static_cast<hipStream_t>(stream)), "block occupancy launch");
+}
+
+dflash_status dflash_mla_attn_blocks(const void* q, const void* k_nope, const void* k_rope_shared, const void* v,
+                                     const int32_t* anchors, const int32_t* ctx_valid, void* out, int64_t B,
+                                     int64_t H, int64_t A, int64_t block_size, int64_t ctx, int64_t Dn, int64_t Dr,
+                                     int64_t Dv, float scale, dflash_dtype dt, void* workspace,
+                                     size_t workspace_bytes, uint32_t flags, void* stream) {
+  if (flags & ~DFLASH_ATTN_REUSE_TILE_MAP) return fail(DFLASH_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  if (valid_dtype(dt) && dt != DFLASH_BF16) return fail(DFLASH_ERR_UNSUPPORTED, "the block-structure path is BF16 only");
+  TileLayout t;
+  int64_t Lq, Lk;
+  dflash_status st = check_block_args(anchors, ctx_valid, B, A, block_size, ctx, workspace, workspace_bytes, &t, &Lq, &Lk);
+  if (st != DFLASH_OK) return st;
+  // the shape / pointer checks of the dense-mask call (no mask, no workspace there)
+  st = dflash_mla_attn(q, k_nope, k_rope_shared, v, nullptr, out, B, H, Lq, Lk, Dn, Dr, Dv, scale, dt,
+                       DFLASH_F32, nullptr, 0, DFLASH_ATTN_CHECK_ONLY, stream);
+  if (st != DFLASH_OK) return st;
+  const Range rw = range_of(workspace, t.total);
+  const int64_t bh = B * H;
+  const Range io[5] = {
+      range_of(out, static_cast<size_t>(bh) * Lq * Dv * 2), range_of(q, static_cast<size_t>(bh) * Lq * (Dn + Dr) * 2),
+      range_of(k_nope, static_cast<size_t>(bh) * Lk * Dn * 2), range_of(k_rope_shared, static_cast<size_t>(B) * Lk * Dr * 2),
+      range_of(v, static_cast<size_t>(bh) * Lk * Dv * 2)};
+  for (const Range& r : io)
+    if (overlaps(rw, r)) return fail(DFLASH_ERR_INVALID_ARG, "the workspace overlaps a tensor");
+  if (overlaps(io[0], range_of(anchors, static_cast<size_t>(B) * A * 4)) ||
+      (ctx_valid && overlaps(io[0], range_of(ctx_valid, static_cast<size_t>(B) * 4))))
+    return fail(DFLASH_ERR_INVALID_ARG, "out overlaps anchors / ctx_valid");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dflash::OccupancyArgs o = block_args(anchors, ctx_valid, B, A, block_size, ctx, Lq, Lk, workspace, t);
+  if (!(flags & DFLASH_ATTN_REUSE_TILE_MAP)) {
+    st = hip_status(dflash::launch_block_occupancy(o, s), "block occupancy launch");
+    if (st != DFLASH_OK) return st;
+  }
+  dflash::AttnBf16Args a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kn = static_cast<const uint16_t*>(k_nope);
+  a.kr = static_cast<const uint16_t*>(k_rope_shared);
+  a.v = static_cast<const uint16_t*>(v);
+  a.mask = nullptr;                 // a block-structure map has no class-3 tiles
+  a.out = static_cast<uint16_t*>(out);
+  a.B = static_cast<int>(B);
+  a.H = static_cast<int>(H);
+  a.Lq = static_cast<int>(Lq);
+  a.Lk = static_cast<int>(Lk);
+  a.nqt = static_cast<int>(t.nqt);
+  a.nkt = static_cast<int>(t.nkt);
+  a.scale = scale;
+  a.mask_bf16 = 0;
+  a.classes = o.classes;
+  a.counts = o.counts;
+  a.lists = o.lists;
+  a.order = o.order;
+  a.bits = o.bits;
   return hip_status(dflash::launch_attn_bf16(a, s), "bf16 attention launch");
 }
 

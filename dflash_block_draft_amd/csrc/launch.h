@@ -39,6 +39,10 @@ struct OccupancyArgs {
   uint8_t* classes; int32_t* counts; int32_t* lists; int32_t* order;
   uint64_t* bits;   // [B*nqt*nkt, kTileM]: bit k of row r = entry (r, k) is +-0 (class-2 tiles only)
   uint32_t* sync;   // one counter: list workgroups done (zeroed by the classify pass)
+  // DFlash block structure (block occupancy only): row b, query i in block j = i / bs
+  // sees context key k <= anchors[b*A + j], k < ctx_valid[b], and noise keys of block j
+  const int32_t* anchors; const int32_t* ctx_valid;  // [B, A], [B] or null (= ctx)
+  int A, bs, ctx;
 };
 
 struct ExpandArgs {
@@ -50,6 +54,8 @@ struct ExpandArgs {
 hipError_t launch_attn_bf16(const AttnBf16Args& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnF32Args& a, hipStream_t s);
 hipError_t launch_occupancy(const OccupancyArgs& a, hipStream_t s);
+// The same tile map from the block structure (anchors, ctx_valid, bs) instead of a dense mask.
+hipError_t launch_block_occupancy(const OccupancyArgs& a, hipStream_t s);
 // Rewrite the lists so every k-tile is visited (empty tiles as class 3); debug/verification mode.
 hipError_t launch_lists_all_tiles(const OccupancyArgs& a, hipStream_t s);
 hipError_t launch_expand_bf16(const ExpandArgs& a, hipStream_t s);

@@ -154,6 +154,52 @@ __global__ void __launch_bounds__(kClassifyThreads) classify_tiles_vec(Occupancy
   }
 }
 
+// Bits [c0, c0 + cols) of the key range [lo, hi] (inclusive), relative to c0.
+__device__ __forceinline__ uint64_t range_bits(int c0, int cols, int lo, int hi) {
+  const int a = max(lo, c0) - c0, b = min(hi, c0 + cols - 1) - c0;
+  if (b < a) return 0ull;
+  const uint64_t upto = b >= 63 ? ~0ull : ((1ull << (b + 1)) - 1ull);
+  const uint64_t below = a == 0 ? 0ull : ((1ull << a) - 1ull);
+  return upto & ~below;
+}
+
+// Tile classes and visibility words of the DFlash block mask straight from its
+// definition (no mask bytes are read): one workgroup per tile, one thread per
+// tile row, whose visible keys are two ranges -- context [0, min(anchor, ctx_valid - 1)]
+// and its own noise block [ctx + j*bs, ctx + (j+1)*bs).  Same output as the
+// dense-mask classification of the 0 / -inf mask with that visibility.
+__global__ void __launch_bounds__(kTileM) classify_blocks(OccupancyArgs a) {
+  __shared__ int s_flags[kTileM / 64];
+  const int64_t tile = blockIdx.x;
+  const int kt = static_cast<int>(tile % a.nkt);
+  const int64_t rest = tile / a.nkt;
+  const int qt = static_cast<int>(rest % a.nqt);
+  const int b = static_cast<int>(rest / a.nqt);
+  const int r = threadIdx.x, lane = r & 63, wave = r >> 6;
+  if (tile == 0 && r == 0) *a.sync = 0u;             // the list pass that follows counts its workgroups
+  const int i = qt * kTileM + r;
+  const int c0 = kt * kTileN;
+  const int cols = min(kTileN, a.Lk - c0);
+  const uint64_t valid = cols == 64 ? ~0ull : ((1ull << cols) - 1ull);
+  const bool row_ok = i < a.Lq;
+  uint64_t word = 0;
+  if (row_ok) {
+    const int j = i / a.bs;
+    // anchors below -1 are clamped there so range_bits never subtracts from INT_MIN
+    const int anchor = max(a.anchors[static_cast<size_t>(b) * a.A + j], -1);
+    const int cv = a.ctx_valid ? min(max(a.ctx_valid[b], 0), a.ctx) : a.ctx;
+    word = range_bits(c0, cols, 0, min(anchor, cv - 1)) |
+           range_bits(c0, cols, a.ctx + j * a.bs, a.ctx + (j + 1) * a.bs - 1);
+  }
+  const int flags = (__ballot(row_ok && word != 0ull) ? 1 : 0) | (__ballot(row_ok && word != valid) ? 2 : 0);
+  if (lane == 0) s_flags[wave] = flags;
+  __syncthreads();
+  const int f = s_flags[0] | s_flags[1];
+  const int cls = !(f & 1) ? 0 : (!(f & 2) ? 1 : 2);
+  if (r == 0) a.classes[tile] = static_cast<uint8_t>(cls);
+  if (cls == 2) a.bits[static_cast<size_t>(tile) * kTileM + r] = word;
+}
+
 // Rank rows by decreasing list length (ties: lower index first) so the attention
 // launch starts the longest work first: order[rank] = row.  n <= kMaxFusedRank.
 constexpr int kRowThreads = 256;
@@ -245,6 +291,24 @@ hipError_t launch_lists_all_tiles(const OccupancyArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+static hipError_t launch_lists(const OccupancyArgs& a, hipStream_t s) {
+  const int nrows = a.B * a.nqt;
+  const int fuse = nrows <= kMaxFusedRank;
+  hipLaunchKernelGGL(build_row_lists, dim3(static_cast<unsigned>(nrows)), dim3(kRowThreads), 0, s, a, fuse);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || fuse) return e;
+  hipLaunchKernelGGL(rank_rows, dim3(1), dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_occupancy(const OccupancyArgs& a, hipStream_t s) {
+  const int64_t ntiles = static_cast<int64_t>(a.B) * a.nqt * a.nkt;
+  hipLaunchKernelGGL(classify_blocks, dim3(static_cast<unsigned>(ntiles)), dim3(kTileM), 0, s, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_lists(a, s);
+}
+
 hipError_t launch_occupancy(const OccupancyArgs& a, hipStream_t s) {
   const int64_t ntiles = static_cast<int64_t>(a.B) * a.nqt * a.nkt;
   const dim3 grid(static_cast<unsigned>(ntiles)), block(kClassifyThreads);
@@ -256,15 +320,9 @@ hipError_t launch_occupancy(const OccupancyArgs& a, hipStream_t s) {
     if (vec) hipLaunchKernelGGL(classify_tiles_vec<false>, grid, block, 0, s, a);
     else hipLaunchKernelGGL(classify_tiles<false>, grid, block, 0, s, a);
   }
-  hipError_t e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nrows = a.B * a.nqt;
-  const int fuse = nrows <= kMaxFusedRank;
-  hipLaunchKernelGGL(build_row_lists, dim3(static_cast<unsigned>(nrows)), dim3(kRowThreads), 0, s, a, fuse);
-  e = hipGetLastError();
-  if (e != hipSuccess || fuse) return e;
-  hipLaunchKernelGGL(rank_rows, dim3(1), dim3(1024), 0, s, a);
-  return hipGetLastError();
+  return launch_lists(a, s);
 }
 
 }  // namespace dflash

@@ -24,11 +24,13 @@ _F32, _BF16 = 0, 1
 _DT = {torch.float32: _F32, torch.bfloat16: _BF16}
 FLAG_REUSE_TILE_MAP = 0x1
 FLAG_NO_TILE_SKIP = 0x2
+FLAG_CHECK_ONLY = 0x4
 
 EXPORTED = (
     "dflash_status_string", "dflash_last_error", "dflash_mla_latent_expand",
     "dflash_mla_attn_workspace_bytes", "dflash_mla_tile_map_layout",
-    "dflash_mla_mask_occupancy", "dflash_mla_attn",
+    "dflash_mla_mask_occupancy", "dflash_mla_attn", "dflash_mla_block_occupancy",
+    "dflash_mla_attn_blocks",
 )
 
 
@@ -71,6 +73,11 @@ def load_library() -> ctypes.CDLL:
     lib.dflash_mla_attn.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32,
                                     i32, i32, vp, sz, u32, vp]
     lib.dflash_mla_attn.restype = i32
+    lib.dflash_mla_block_occupancy.argtypes = [vp, vp, i64, i64, i64, i64, vp, sz, vp]
+    lib.dflash_mla_block_occupancy.restype = i32
+    lib.dflash_mla_attn_blocks.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64,
+                                           f32, i32, vp, sz, u32, vp]
+    lib.dflash_mla_attn_blocks.restype = i32
     _lib = lib
     return lib
 
@@ -217,4 +224,64 @@ def mla_attn(q: torch.Tensor, k_nope: torch.Tensor, k_rope: torch.Tensor, v: tor
                                B, H, Lq, Lk, Dn, Dr, Dv, float(scale), _DT[dt], mask_dt,
                                _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                flags, _stream(q)))
+    return out
+
+
+def _block_tensors(anchors: torch.Tensor, ctx_valid: Optional[torch.Tensor]):
+    _dev(anchors, "anchors", dtype=torch.int32, ndim=2)
+    if ctx_valid is not None:
+        _dev(ctx_valid, "ctx_valid", dtype=torch.int32, ndim=1)
+        if ctx_valid.shape[0] != anchors.shape[0]:
+            raise ValueError("ctx_valid must be [B]")
+    return anchors.shape
+
+
+def block_occupancy(anchors: torch.Tensor, block_size: int, ctx: int, ctx_valid: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Tile map of the DFlash block mask from anchors [B, A] (int32) and ctx_valid [B]
+    (int32, or None = ctx); returns the workspace holding it."""
+    lib = load_library()
+    B, A = _block_tensors(anchors, ctx_valid)
+    Lq = A * int(block_size)
+    if workspace is None:
+        workspace = new_workspace(B, Lq, int(ctx) + Lq, anchors.device)
+    _dev(workspace, "workspace", dtype=torch.uint8)
+    _check(lib.dflash_mla_block_occupancy(_ptr(anchors), _ptr(ctx_valid), B, A, int(block_size), int(ctx),
+                                          _ptr(workspace), workspace.numel(), _stream(anchors)))
+    return workspace
+
+
+def mla_attn_blocks(q: torch.Tensor, k_nope: torch.Tensor, k_rope: torch.Tensor, v: torch.Tensor,
+                    anchors: torch.Tensor, block_size: int, ctx: int, ctx_valid: Optional[torch.Tensor] = None,
+                    scale: Optional[float] = None, *, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, reuse_tile_map: bool = False) -> torch.Tensor:
+    """mla_attn with the DFlash block mask given by anchors [B, A] (int32), block_size,
+    ctx and ctx_valid [B] (int32, or None = ctx) instead of a dense mask."""
+    lib = load_library()
+    _dev(q, "q", dtype=torch.bfloat16, ndim=4)
+    _dev(k_nope, "k_nope", dtype=torch.bfloat16, ndim=4)
+    _dev(k_rope, "k_rope", dtype=torch.bfloat16, ndim=3)
+    _dev(v, "v", dtype=torch.bfloat16, ndim=4)
+    B, A = _block_tensors(anchors, ctx_valid)
+    Bq, H, Lq, Dqk = q.shape
+    Dn, Dr, Dv = k_nope.shape[3], k_rope.shape[2], v.shape[3]
+    if Bq != B or Lq != A * int(block_size):
+        raise ValueError(f"q must be [{B}, H, {A * int(block_size)}, D], got {tuple(q.shape)}")
+    Lk = int(ctx) + Lq
+    if tuple(k_nope.shape[:3]) != (B, H, Lk) or tuple(v.shape[:3]) != (B, H, Lk) or tuple(k_rope.shape[:2]) != (B, Lk):
+        raise ValueError("k_nope / k_rope / v shapes must use Lk = ctx + A * block_size")
+    if scale is None:
+        scale = float(Dn + Dr) ** -0.5
+    if workspace is None:
+        if reuse_tile_map:
+            raise ValueError("reuse_tile_map needs the workspace that holds the map")
+        workspace = new_workspace(B, Lq, Lk, q.device)
+    _dev(workspace, "workspace", dtype=torch.uint8)
+    if out is None:
+        out = torch.empty((B, H, Lq, Dv), dtype=q.dtype, device=q.device)
+    _dev(out, "out", dtype=q.dtype, ndim=4)
+    _check(lib.dflash_mla_attn_blocks(_ptr(q), _ptr(k_nope), _ptr(k_rope), _ptr(v), _ptr(anchors), _ptr(ctx_valid),
+                                      _ptr(out), B, H, A, int(block_size), int(ctx), Dn, Dr, Dv, float(scale),
+                                      _BF16, _ptr(workspace), workspace.numel(),
+                                      FLAG_REUSE_TILE_MAP if reuse_tile_map else 0, _stream(q)))
     return out

@@ -92,9 +92,11 @@ def draw_anchors(rng: np.random.Generator, B: int, A: int, ctx_valid: int) -> np
     return out
 
 
-def visibility(anchors: np.ndarray, ctx: int, ctx_valid: int, block_size: int) -> np.ndarray:
-    """Boolean [B, Lq, Lk]: True where query i may see key k (reading stated above)."""
+def visibility(anchors: np.ndarray, ctx: int, ctx_valid, block_size: int) -> np.ndarray:
+    """Boolean [B, Lq, Lk]: True where query i may see key k (reading stated above).
+    ctx_valid is one int or one per batch row."""
     B, A = anchors.shape
+    cv = np.broadcast_to(np.asarray(ctx_valid, dtype=np.int64), (B,))
     Lq = A * block_size
     Lk = ctx + Lq
     blk = np.arange(Lq) // block_size                        # block of each query
@@ -103,7 +105,7 @@ def visibility(anchors: np.ndarray, ctx: int, ctx_valid: int, block_size: int) -
     ctx_k = k[:ctx]
     for b in range(B):
         anc = anchors[b][blk]                                 # anchor of each query's block
-        vis[b, :, :ctx] = (ctx_k[None, :] <= anc[:, None]) & (ctx_k[None, :] < ctx_valid)
+        vis[b, :, :ctx] = (ctx_k[None, :] <= anc[:, None]) & (ctx_k[None, :] < cv[b])
     noise_blk = (k[ctx:] - ctx) // block_size
     vis[:, :, ctx:] = (noise_blk[None, :] == blk[:, None])[None]
     return vis

@@ -73,6 +73,7 @@ typedef enum dflash_dtype {
                                             tiles as mixed; the result is bitwise identical.  The
                                             workspace lists are left covering every tile, so a later
                                             REUSE_TILE_MAP call on it also visits every tile */
+#define DFLASH_ATTN_CHECK_ONLY 0x4u      /* validate the arguments and return; launch nothing */
 
 /* Human-readable name of a status. Never NULL. */
 const char* dflash_status_string(dflash_status status);
@@ -182,7 +183,7 @@ dflash_status dflash_mla_mask_occupancy(const void* additive_mask, dflash_dtype 
  *   definition does.
  * Workspace (BF16 with a mask): at least dflash_mla_attn_workspace_bytes(B, Lq, Lk)
  *   bytes, 256-byte aligned; unused (may be NULL/0) when the mask is NULL or dt is F32.
- * flags: 0 or DFLASH_ATTN_REUSE_TILE_MAP and/or DFLASH_ATTN_NO_TILE_SKIP.
+ * flags: any of DFLASH_ATTN_REUSE_TILE_MAP, DFLASH_ATTN_NO_TILE_SKIP, DFLASH_ATTN_CHECK_ONLY.
  */
 dflash_status dflash_mla_attn(const void* q, const void* k_nope, const void* k_rope_shared,
                               const void* v, const void* additive_mask, void* out,
@@ -191,6 +192,44 @@ dflash_status dflash_mla_attn(const void* q, const void* k_nope, const void* k_r
                               dflash_dtype dt, dflash_dtype mask_dt,
                               void* workspace, size_t workspace_bytes,
                               uint32_t flags, void* stream);
+
+/*
+ * The tile map of the DFlash block mask computed from the block structure itself
+ * instead of a dense mask: no mask bytes are read.  Row b, query i belongs to
+ * block j = i / block_size and sees context key k (k < ctx) iff
+ * k <= anchors[b, j] and k < ctx_valid[b], and noise key ctx + m iff
+ * m / block_size == j (its own block, non-causally).  This is the block
+ * structure the dense additive mask of the DFlash page (KimiK3DFlashAttention.forward)
+ * carries; the resulting map equals dflash_mla_mask_occupancy of the 0 / -inf
+ * mask with that visibility.
+ *
+ * anchors    int32 [B, A], device, 4-byte aligned: the context position each block
+ *            is anchored at (any value; one below 0 hides the whole context)
+ * ctx_valid  int32 [B], device, or NULL (= ctx); values are clamped to [0, ctx]
+ * Lq = A * block_size, Lk = ctx + Lq; the workspace is sized and laid out as for
+ * dflash_mla_attn_workspace_bytes(B, Lq, Lk) / dflash_mla_tile_map_layout.
+ * Errors: INVALID_ARG (NULL or misaligned anchors, B/A/block_size <= 0, ctx < 0,
+ * workspace overlapping anchors/ctx_valid), UNSUPPORTED (Lk beyond int32 or
+ * 2^24 - 1 key tiles), WORKSPACE, HIP.
+ */
+dflash_status dflash_mla_block_occupancy(const int32_t* anchors, const int32_t* ctx_valid,
+                                         int64_t B, int64_t A, int64_t block_size, int64_t ctx,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dflash_mla_attn for the DFlash block mask given by its structure (see
+ * dflash_mla_block_occupancy): out equals dflash_mla_attn with the dense 0 / -inf
+ * additive mask of that structure, bitwise.  Lq = A * block_size, Lk = ctx + Lq;
+ * tensors as for dflash_mla_attn.  BF16 only (F32 returns UNSUPPORTED).  The
+ * workspace is required.  flags: 0 or DFLASH_ATTN_REUSE_TILE_MAP (the workspace
+ * holds the map of this same structure, e.g. for the next draft layer).
+ */
+dflash_status dflash_mla_attn_blocks(const void* q, const void* k_nope, const void* k_rope_shared,
+                                     const void* v, const int32_t* anchors, const int32_t* ctx_valid,
+                                     void* out, int64_t B, int64_t H, int64_t A, int64_t block_size,
+                                     int64_t ctx, int64_t Dn, int64_t Dr, int64_t Dv, float scale,
+                                     dflash_dtype dt, void* workspace, size_t workspace_bytes,
+                                     uint32_t flags, void* stream);
 
 #ifdef __cplusplus
 }

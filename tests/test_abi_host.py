@@ -30,6 +30,7 @@ def declared_functions():
 def test_header_declares_the_documented_entry_points():
     names = declared_functions()
     for n in ("dflash_mla_latent_expand", "dflash_mla_attn", "dflash_mla_attn_workspace_bytes",
+              "dflash_mla_block_occupancy", "dflash_mla_attn_blocks",
               "dflash_mla_mask_occupancy", "dflash_mla_tile_map_layout", "dflash_status_string",
               "dflash_last_error"):
         assert n in names
@@ -132,3 +133,61 @@ def test_python_binding_rejects_host_tensors():
     x = torch.zeros(1, 1, 4, 192)
     with pytest.raises((ValueError, RuntimeError)):
         mla.mla_attn(x, x, x, x)
+
+
+def _blocks(lib, **kw):
+    args = dict(q=FAKE, kn=FAKE * 2, kr=FAKE * 3, v=FAKE * 4, anchors=FAKE * 6, cv=None, out=FAKE * 5,
+                B=1, H=2, A=2, bs=16, ctx=64, Dn=128, Dr=64, Dv=128, scale=192 ** -0.5, dt=1,
+                ws=FAKE * 256, wsb=1 << 20, flags=0)
+    args.update(kw)
+    return lib.dflash_mla_attn_blocks(args["q"], args["kn"], args["kr"], args["v"], args["anchors"], args["cv"],
+                                      args["out"], args["B"], args["H"], args["A"], args["bs"], args["ctx"],
+                                      args["Dn"], args["Dr"], args["Dv"], args["scale"], args["dt"], args["ws"],
+                                      args["wsb"], args["flags"], None)
+
+
+# every case fails validation, so nothing is launched
+@pytest.mark.parametrize("kw,status", [
+    (dict(anchors=None), 1),
+    (dict(anchors=FAKE * 6 + 2), 1),        # misaligned anchors
+    (dict(cv=FAKE * 7 + 1), 1),             # misaligned ctx_valid
+    (dict(A=0), 1),
+    (dict(bs=0), 1),
+    (dict(ctx=-1), 1),
+    (dict(flags=0x2), 1),                   # tile-skip switch is not offered here
+    (dict(flags=0x4), 1),
+    (dict(dt=0), 2),                        # f32: the block path is bf16 only
+    (dict(ws=None, wsb=0), 3),
+    (dict(wsb=16), 3),
+    (dict(ws=FAKE * 256 + 16), 3),
+    (dict(ws=FAKE * 6), 1),                 # workspace overlaps anchors
+    (dict(ws=FAKE * 4), 1),                 # workspace overlaps v
+    (dict(out=FAKE * 6), 1),                # out overlaps anchors
+    (dict(out=FAKE * 4), 1),                # out aliases v
+    (dict(Dv=64), 2),
+    (dict(scale=0.0), 1),
+    (dict(A=1 << 20, bs=1 << 12), 2),       # Lq beyond int32
+    (dict(q=1 << 44, kn=2 << 44, kr=3 << 44, v=4 << 44, out=5 << 44, anchors=6 << 44, ws=7 << 44,
+          wsb=1 << 40, ctx=1 << 30), 2),    # 2^24 key tiles
+])
+def test_attn_blocks_validation(lib, kw, status):
+    assert _blocks(lib, **kw) == status
+    assert lib.dflash_last_error() != b""
+
+
+def test_block_occupancy_validation(lib):
+    f = lib.dflash_mla_block_occupancy
+    assert f(None, None, 1, 2, 16, 64, FAKE * 256, 1 << 20, None) == 1
+    assert f(FAKE + 1, None, 1, 2, 16, 64, FAKE * 256, 1 << 20, None) == 1
+    assert f(FAKE, None, 0, 2, 16, 64, FAKE * 256, 1 << 20, None) == 1
+    assert f(FAKE, None, 1, 2, 16, -3, FAKE * 256, 1 << 20, None) == 1
+    assert f(FAKE, None, 1, 2, 16, 64, None, 0, None) == 3
+    assert f(FAKE, None, 1, 2, 16, 64, FAKE * 256, 64, None) == 3
+    assert f(FAKE * 256, None, 1, 2, 16, 64, FAKE * 256, 1 << 20, None) == 1   # overlap
+
+
+def test_block_binding_rejects_bad_tensors():
+    import torch
+    from dflash_block_draft_amd import mla
+    with pytest.raises(ValueError):
+        mla.block_occupancy(torch.zeros(1, 2, dtype=torch.int32), 16, 64)        # host tensor
