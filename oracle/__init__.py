@@ -29,6 +29,12 @@ What it computes, and the passages it follows:
   that the score matrix is never materialised (KimiK3DFlashAttention.forward);
   the classification is defined here by its plain meaning.
 
+* ``backward.mla_attention_backward`` / ``logsumexp_rows`` -- the gradients of
+  that attention with respect to q, k_nope, the head-shared k_rope (summed over
+  heads) and v, and the per-row log normaliser a forward pass saves for them.
+  The draft is trained (DFlash page, KimiK3DFlashDraftModel class text: the
+  DFlash trainer; DSpark page, module text: speculative-decoding training).
+
 Readings where the pages are silent (also listed in the design notes):
 a row whose every score is -inf returns 0; a mask entry is "masked" only if it
 is exactly -inf, any finite value (including large negatives) is added as is.
@@ -37,5 +43,6 @@ Pinned by tests/test_oracle_pins.py (closed forms, invariants, brute force,
 a library routine) -- nothing here is "parity unpinned".
 """
 from .attention import mla_attention, softmax_weights  # noqa: F401
+from .backward import logsumexp_rows, mla_attention_backward  # noqa: F401
 from .expand import latent_expand  # noqa: F401
 from .occupancy import tile_bits, tile_classes, tile_lists  # noqa: F401

@@ -325,4 +325,105 @@ def pin_occupancy_brute_force():
 
 OCCUPANCY_PINS = [pin_occupancy_brute_force]
 
-ALL_PINS = ATTENTION_PINS + EXPAND_PINS + OCCUPANCY_PINS
+
+# ---------------------------------------------------------------- backward
+
+def _mask_with_dead_row(seed, B, Lq, Lk):
+    m = _rand_mask(seed, B, Lq, Lk, p_masked=0.45)
+    m[0, 0, Lq - 1, :] = NINF                      # one row sees nothing: constant 0 output
+    return m
+
+
+def pin_backward_finite_differences():
+    """Central differences of the (separately pinned) forward oracle: for
+    f = sum(dout * out), df/dx at every entry of q, k_nope, k_rope and v."""
+    q, kn, kr, v = _rand(40, 2, 2, 3, 5, dn=4, dr=3, dv=3)
+    mask = _mask_with_dead_row(40, 2, 3, 5)
+    dout = np.random.default_rng(41).standard_normal((2, 2, 3, 3))
+    scale = 0.41
+    grads = oracle.mla_attention_backward(q, kn, kr, v, mask, dout, scale)
+    args = [q, kn, kr, v]
+    eps = 1e-6
+    for slot, g in enumerate(grads):
+        x = args[slot]
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            ap, am = list(args), list(args)
+            ap[slot], am[slot] = xp, xm
+            fp = (dout * oracle.mla_attention(*ap, mask, scale)).sum()
+            fm = (dout * oracle.mla_attention(*am, mask, scale)).sum()
+            num[idx] = (fp - fm) / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=0, atol=2e-8, err_msg=f"input {slot}")
+
+
+def pin_backward_matches_torch_autograd():
+    """torch.autograd (fp64, CPU) through scaled_dot_product_attention on explicit
+    keys [k_nope | k_rope broadcast to every head]; rows with a finite score only
+    (the library's softmax of an all -inf row is NaN, not the 0 this reading uses)."""
+    import torch
+    import torch.nn.functional as F
+    B, H, Lq, Lk, dn, dr, dv = 2, 3, 9, 14, 16, 8, 12
+    q, kn, kr, v = _rand(42, B, H, Lq, Lk, dn=dn, dr=dr, dv=dv)
+    mask = _rand_mask(42, B, Lq, Lk)
+    dout = np.random.default_rng(43).standard_normal((B, H, Lq, dv))
+    scale = 24 ** -0.5
+    tq, tkn, tkr, tv = (torch.tensor(a, requires_grad=True) for a in (q, kn, kr, v))
+    k = torch.cat([tkn, tkr[:, None].expand(B, H, Lk, dr)], dim=-1)
+    out = F.scaled_dot_product_attention(tq, k, tv, attn_mask=torch.from_numpy(mask), scale=scale)
+    out.backward(torch.from_numpy(dout))
+    got = oracle.mla_attention_backward(q, kn, kr, v, mask, dout, scale)
+    for g, t in zip(got, (tq, tkn, tkr, tv)):
+        np.testing.assert_allclose(g, t.grad.numpy(), rtol=0, atol=1e-11)
+
+
+def pin_backward_invariants():
+    """Softmax rows sum to 1, so the gradient rows of s sum to 0: the key
+    gradients sum to 0 over the keys, and the value gradients sum to the
+    output gradient of the rows that see anything.  A dead row passes nothing."""
+    B, H, Lq, Lk = 2, 2, 6, 11
+    q, kn, kr, v = _rand(44, B, H, Lq, Lk)
+    mask = _mask_with_dead_row(44, B, Lq, Lk)
+    dout = np.random.default_rng(45).standard_normal((B, H, Lq, v.shape[-1]))
+    dq, dkn, dkr, dv = oracle.mla_attention_backward(q, kn, kr, v, mask, dout, 0.3)
+    np.testing.assert_allclose(dkn.sum(axis=2), 0.0, atol=1e-12)
+    np.testing.assert_allclose(dkr.sum(axis=1), 0.0, atol=1e-12)
+    live = np.isfinite(mask).any(axis=-1)[:, 0]                  # [B, Lq]
+    want_dv = (dout * live[:, None, :, None]).sum(axis=2)
+    np.testing.assert_allclose(dv.sum(axis=2), want_dv, atol=1e-12)
+    assert not live[0, Lq - 1] and np.all(dq[0, :, Lq - 1] == 0.0)
+    # per-head restriction: the same slices, and the rope gradient of one head
+    one = oracle.mla_attention_backward(q, kn, kr, v, mask, dout, 0.3, heads=[1])
+    np.testing.assert_allclose(one[0][:, 1], dq[:, 1], atol=0)
+    np.testing.assert_allclose(one[3][:, 1], dv[:, 1], atol=0)
+    zero = oracle.mla_attention_backward(q, kn, kr, v, mask, dout, 0.3, heads=[0])
+    np.testing.assert_allclose(one[2] + zero[2], dkr, atol=1e-12)
+
+
+def pin_logsumexp_normalises_the_forward():
+    """exp(s - lse) over explicitly formed scores sums to 1 per live row and,
+    applied to v, reproduces the forward oracle; dead rows have lse = -inf."""
+    B, H, Lq, Lk, dn = 2, 2, 5, 9, 8
+    q, kn, kr, v = _rand(46, B, H, Lq, Lk, dn=dn)
+    mask = _mask_with_dead_row(46, B, Lq, Lk)
+    lse = oracle.logsumexp_rows(q, kn, kr, mask, 0.37)
+    out = oracle.mla_attention(q, kn, kr, v, mask, 0.37)
+    for b in range(B):
+        for h in range(H):
+            for i in range(Lq):
+                s = [0.37 * (float(np.dot(q[b, h, i, :dn], kn[b, h, j])) + float(np.dot(q[b, h, i, dn:], kr[b, j])))
+                     + mask[b, 0, i, j] for j in range(Lk)]
+                if all(x == NINF for x in s):
+                    assert lse[b, h, i] == NINF
+                    continue
+                p = [math.exp(x - lse[b, h, i]) for x in s]
+                assert abs(sum(p) - 1.0) < 1e-12
+                np.testing.assert_allclose(np.dot(p, v[b, h]), out[b, h, i], atol=1e-12)
+
+
+BACKWARD_PINS = [pin_backward_finite_differences, pin_backward_matches_torch_autograd,
+                 pin_backward_invariants, pin_logsumexp_normalises_the_forward]
+
+ALL_PINS = ATTENTION_PINS + EXPAND_PINS + OCCUPANCY_PINS + BACKWARD_PINS

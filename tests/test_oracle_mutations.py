@@ -3,6 +3,8 @@
 This is what makes the pins meaningful: a dropped term, a wrong sign, a wrong
 index or a transposed operand anywhere in the oracle must fail at least one.
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -124,6 +126,39 @@ def _bits_transposed(mask, BM, BN, classes):
     return rev
 
 
+def _bwd_variant(kind):
+    """The backward with one planted mistake (test code, not the oracle)."""
+    def f(q, k_nope, k_rope, v, mask, dout, scale, heads=None):
+        from oracle._arrays import f64
+        B, H = q.shape[:2]
+        dn = k_nope.shape[-1]
+        dq, dkn = np.zeros(q.shape), np.zeros(k_nope.shape)
+        dkr, dv = np.zeros(k_rope.shape), np.zeros(v.shape)
+        for b in range(B):
+            for h in range(H) if heads is None else heads:
+                p = oracle.softmax_weights(q, k_nope, k_rope, mask, scale, b, h)
+                qb, kn, kr = f64(q[b, h]), f64(k_nope[b, h]), f64(k_rope[b])
+                do, vb = f64(dout[b, h]), f64(v[b, h])
+                dp = do @ vb.T
+                D = 0.0 if kind == "no_D" else (p * dp).sum(axis=-1, keepdims=True)
+                ds = p * (dp - D)
+                dv[b, h] = (ds if kind == "dv_from_ds" else p).T @ do
+                dq[b, h, :, :dn] = scale * (ds @ kn)
+                dq[b, h, :, dn:] = (-scale if kind == "dq_rope_sign" else scale) * (ds @ kr)
+                dkn[b, h] = (1.0 if kind == "dk_unscaled" else scale) * (ds.T @ qb[:, :dn])
+                if kind == "rope_last_head":
+                    dkr[b] = scale * (ds.T @ qb[:, dn:])
+                else:
+                    dkr[b] += scale * (ds.T @ qb[:, dn:])
+        return dq, dkn, dkr, dv
+    return f
+
+
+def _lse_log2(q, k_nope, k_rope, mask, scale):
+    return _orig_lse(q, k_nope, k_rope, mask, scale) / math.log(2.0)
+
+
+_orig_lse = oracle.logsumexp_rows
 _orig_attn = oracle.mla_attention
 _orig_classes = oracle.tile_classes
 _orig_bits = oracle.tile_bits
@@ -146,6 +181,12 @@ MUTANTS = {
     "occupancy_square_tiles": [(oracle, "tile_classes", _classes_square_tiles)],
     "occupancy_binary_as_values": [(oracle, "tile_classes", _classes_binary_as_values)],
     "occupancy_bits_reversed": [(oracle, "tile_bits", _bits_transposed)],
+    "backward_no_D": [(oracle, "mla_attention_backward", _bwd_variant("no_D"))],
+    "backward_dv_from_ds": [(oracle, "mla_attention_backward", _bwd_variant("dv_from_ds"))],
+    "backward_dq_rope_sign": [(oracle, "mla_attention_backward", _bwd_variant("dq_rope_sign"))],
+    "backward_dk_unscaled": [(oracle, "mla_attention_backward", _bwd_variant("dk_unscaled"))],
+    "backward_rope_last_head": [(oracle, "mla_attention_backward", _bwd_variant("rope_last_head"))],
+    "lse_in_log2": [(oracle, "logsumexp_rows", _lse_log2)],
 }
 
 
