@@ -26,6 +26,15 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-source device flags.  The backward kernels keep 160 accumulator registers
+# (dK, dV or dQ) plus register-resident operands; letting the MFMAs write their
+# score tiles to ordinary VGPRs (which the softmax reads anyway) instead of
+# accumulator registers avoids spilling.
+FILE_FLAGS = {
+    "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _hipcc() -> str:
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -39,7 +48,7 @@ def sources():
 
 def _compile(hipcc: str, src: str, extra) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc, *COMMON_FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [hipcc, *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature"
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)

@@ -254,12 +254,16 @@ dflash_status dflash_mla_latent_expand(const void* latent, const void* w_kv_b, v
                     "latent expand launch");
 }
 
-dflash_status dflash_mla_attn(const void* q, const void* k_nope, const void* k_rope_shared,
-                              const void* v, const void* additive_mask, void* out, int64_t B,
-                              int64_t H, int64_t Lq, int64_t Lk, int64_t Dn, int64_t Dr,
-                              int64_t Dv, float scale, dflash_dtype dt, dflash_dtype mask_dt,
-                              void* workspace, size_t workspace_bytes, uint32_t flags,
-                              void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward of dflash_mla_attn / dflash_mla_attn_lse (lse may be null).
+dflash_status attn_impl(const void* q, const void* k_nope, const void* k_rope_shared, const void* v,
+                        const void* additive_mask, void* out, float* lse, int64_t B, int64_t H, int64_t Lq,
+                        int64_t Lk, int64_t Dn, int64_t Dr, int64_t Dv, float scale, dflash_dtype dt,
+                        dflash_dtype mask_dt, void* workspace, size_t workspace_bytes, uint32_t flags,
+                        void* stream) {
   if (!q || !k_nope || !k_rope_shared || !v || !out) return fail(DFLASH_ERR_INVALID_ARG, "a tensor pointer is NULL");
   if (!aligned16(q) || !aligned16(k_nope) || !aligned16(k_rope_shared) || !aligned16(v) || !aligned16(out) ||
       (additive_mask && !aligned16(additive_mask)))
@@ -291,6 +295,13 @@ dflash_status dflash_mla_attn(const void* q, const void* k_nope, const void* k_r
   };
   for (const Range& r : ins)
     if (overlaps(ro, r)) return fail(DFLASH_ERR_INVALID_ARG, "out overlaps an input");
+  const Range rl = lse ? range_of(lse, static_cast<size_t>(bh) * Lq * 4) : Range{0, 0};
+  if (lse) {
+    if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return fail(DFLASH_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    if (overlaps(rl, ro)) return fail(DFLASH_ERR_INVALID_ARG, "lse overlaps out");
+    for (const Range& r : ins)
+      if (overlaps(rl, r)) return fail(DFLASH_ERR_INVALID_ARG, "lse overlaps an input");
+  }
   if (dt == DFLASH_BF16 && (Lk + DFLASH_TILE_N - 1) / DFLASH_TILE_N > dflash::kMaxKeyTiles)
     return fail(DFLASH_ERR_UNSUPPORTED, "a bf16 call supports at most %d key tiles, got Lk = %lld",
                 dflash::kMaxKeyTiles, (long long)Lk);
@@ -311,6 +322,7 @@ dflash_status dflash_mla_attn(const void* q, const void* k_nope, const void* k_r
     a.Lq = static_cast<int>(Lq);
     a.Lk = static_cast<int>(Lk);
     a.scale = scale;
+    a.lse = lse;
     return hip_status(dflash::launch_attn_f32(a, s), "f32 attention launch");
   }
 
@@ -329,6 +341,7 @@ dflash_status dflash_mla_attn(const void* q, const void* k_nope, const void* k_r
   a.nkt = static_cast<int>((Lk + DFLASH_TILE_N - 1) / DFLASH_TILE_N);
   a.scale = scale;
   a.mask_bf16 = mask_dt == DFLASH_BF16;
+  a.lse = lse;
   if (static_cast<int64_t>(B) * a.nqt * H > INT32_MAX) return fail(DFLASH_ERR_UNSUPPORTED, "too many work items");
   if (a.nkt > dflash::kMaxKeyTiles)
     return fail(DFLASH_ERR_UNSUPPORTED, "a bf16 call supports at most %d key tiles, got Lk = %lld",
@@ -338,7 +351,7 @@ dflash_status dflash_mla_attn(const void* q, const void* k_nope, const void* k_r
     dflash_status st = check_occupancy_args(additive_mask, mask_dt, B, Lq, Lk, workspace, workspace_bytes, &t);
     if (st != DFLASH_OK) return st;
     const Range rw = range_of(workspace, t.total);
-    if (overlaps(ro, rw)) return fail(DFLASH_ERR_INVALID_ARG, "out overlaps the workspace");
+    if (overlaps(ro, rw) || overlaps(rl, rw)) return fail(DFLASH_ERR_INVALID_ARG, "out / lse overlap the workspace");
     for (const Range& r : ins)
       if (overlaps(rw, r)) return fail(DFLASH_ERR_INVALID_ARG, "the workspace overlaps an input");
     const dflash::OccupancyArgs o = occupancy_args(additive_mask, mask_dt, B, Lq, Lk, workspace, t);
@@ -357,6 +370,158 @@ dflash_status dflash_mla_attn(const void* q, const void* k_nope, const void* k_r
     a.bits = o.bits;
   }
   return hip_status(dflash::launch_attn_bf16(a, s), "bf16 attention launch");
+}
+
+// Backward workspace: the forward's tile map, then the backward's own arrays.
+struct BwdLayout {
+  TileLayout t;
+  int64_t Lqp, Lkp;
+  size_t lse2, dd, qT, doT, knT, krT, rope, total;
+};
+
+bool bwd_layout(int64_t B, int64_t H, int64_t Lq, int64_t Lk, BwdLayout* L) {
+  if (H <= 0 || !tile_layout(B, Lq, Lk, &L->t)) return false;
+  L->Lqp = L->t.nqt * DFLASH_TILE_M;
+  L->Lkp = L->t.nkt * DFLASH_TILE_N;
+  int64_t bh, a, c, d, e, f, g;
+  if (!mul_ok(B, H, &bh) || !mul_ok(bh, L->Lqp, &a) || !mul_ok(a, 4, &c) || !mul_ok(a, 2 * 192, &d) ||
+      !mul_ok(bh, L->Lkp, &e) || !mul_ok(e, 2 * 128, &e) || !mul_ok(B, L->Lkp * 2 * 64, &f) ||
+      !mul_ok(bh, Lk, &g) || !mul_ok(g, 64 * 4, &g))
+    return false;
+  L->lse2 = align_up(L->t.total, 256);
+  L->dd = L->lse2 + align_up(static_cast<size_t>(c), 256);
+  L->qT = L->dd + align_up(static_cast<size_t>(c), 256);
+  L->doT = L->qT + align_up(static_cast<size_t>(d), 256);
+  L->knT = L->doT + align_up(static_cast<size_t>(a) * 2 * 128, 256);
+  L->krT = L->knT + align_up(static_cast<size_t>(e), 256);
+  L->rope = L->krT + align_up(static_cast<size_t>(f), 256);
+  L->total = L->rope + align_up(static_cast<size_t>(g), 256);
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+dflash_status dflash_mla_attn(const void* q, const void* k_nope, const void* k_rope_shared,
+                              const void* v, const void* additive_mask, void* out, int64_t B,
+                              int64_t H, int64_t Lq, int64_t Lk, int64_t Dn, int64_t Dr,
+                              int64_t Dv, float scale, dflash_dtype dt, dflash_dtype mask_dt,
+                              void* workspace, size_t workspace_bytes, uint32_t flags,
+                              void* stream) {
+  return attn_impl(q, k_nope, k_rope_shared, v, additive_mask, out, nullptr, B, H, Lq, Lk, Dn, Dr, Dv, scale, dt,
+                   mask_dt, workspace, workspace_bytes, flags, stream);
+}
+
+dflash_status dflash_mla_attn_lse(const void* q, const void* k_nope, const void* k_rope_shared,
+                                  const void* v, const void* additive_mask, void* out, float* lse,
+                                  int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t Dn, int64_t Dr,
+                                  int64_t Dv, float scale, dflash_dtype dt, dflash_dtype mask_dt,
+                                  void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+  if (!lse) return fail(DFLASH_ERR_INVALID_ARG, "lse is NULL");
+  return attn_impl(q, k_nope, k_rope_shared, v, additive_mask, out, lse, B, H, Lq, Lk, Dn, Dr, Dv, scale, dt,
+                   mask_dt, workspace, workspace_bytes, flags, stream);
+}
+
+size_t dflash_mla_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Lq, int64_t Lk) {
+  BwdLayout L;
+  return bwd_layout(B, H, Lq, Lk, &L) ? L.total : 0;
+}
+
+dflash_status dflash_mla_attn_bwd(const void* q, const void* k_nope, const void* k_rope_shared, const void* v,
+                                  const void* additive_mask, const void* out, const void* dout, const float* lse,
+                                  void* dq, void* dk_nope, void* dk_rope_shared, void* dv, int64_t B, int64_t H,
+                                  int64_t Lq, int64_t Lk, int64_t Dn, int64_t Dr, int64_t Dv, float scale,
+                                  dflash_dtype dt, dflash_dtype mask_dt, void* workspace, size_t workspace_bytes,
+                                  uint32_t flags, void* stream) {
+  if (!q || !k_nope || !k_rope_shared || !v || !out || !dout || !lse || !dq || !dk_nope || !dk_rope_shared || !dv)
+    return fail(DFLASH_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!aligned16(q) || !aligned16(k_nope) || !aligned16(k_rope_shared) || !aligned16(v) || !aligned16(out) ||
+      !aligned16(dout) || !aligned16(dq) || !aligned16(dk_nope) || !aligned16(dk_rope_shared) || !aligned16(dv) ||
+      (additive_mask && !aligned16(additive_mask)) || (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+    return fail(DFLASH_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned (lse: 4-byte)");
+  if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0 || Dn <= 0 || Dr <= 0 || Dv <= 0)
+    return fail(DFLASH_ERR_INVALID_ARG, "sizes must be positive (B=%lld H=%lld Lq=%lld Lk=%lld)", (long long)B,
+                (long long)H, (long long)Lq, (long long)Lk);
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(DFLASH_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (!valid_dtype(dt) || !valid_dtype(mask_dt)) return fail(DFLASH_ERR_INVALID_ARG, "dtype is not a dflash_dtype");
+  if (flags & ~DFLASH_ATTN_REUSE_TILE_MAP) return fail(DFLASH_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  if (Dn != dflash::kDn || Dr != dflash::kDr || Dv != dflash::kDv)
+    return fail(DFLASH_ERR_UNSUPPORTED, "only Dn=128, Dr=64, Dv=128 are built (got %lld, %lld, %lld)", (long long)Dn,
+                (long long)Dr, (long long)Dv);
+  if (dt != DFLASH_BF16) return fail(DFLASH_ERR_UNSUPPORTED, "the backward is built for bf16 tensors only");
+  if (Lq > INT32_MAX || Lk > INT32_MAX) return fail(DFLASH_ERR_UNSUPPORTED, "Lq and Lk must each fit in int32");
+  int64_t bh;
+  if (!mul_ok(B, H, &bh) || bh > 65535) return fail(DFLASH_ERR_UNSUPPORTED, "B * H must be at most 65535");
+  BwdLayout L;
+  if (!bwd_layout(B, H, Lq, Lk, &L)) return fail(DFLASH_ERR_UNSUPPORTED, "sizes too large");
+  if (L.t.nkt > dflash::kMaxKeyTiles || bh * L.t.nqt > INT32_MAX || L.Lqp > INT32_MAX || L.Lkp > INT32_MAX)
+    return fail(DFLASH_ERR_UNSUPPORTED, "sizes too large for the backward launches");
+  if (!workspace) return fail(DFLASH_ERR_WORKSPACE, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(DFLASH_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(DFLASH_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+  const size_t nq = static_cast<size_t>(bh) * Lq, nk = static_cast<size_t>(bh) * Lk;
+  const Range ins[8] = {
+      range_of(q, nq * 192 * 2), range_of(k_nope, nk * 128 * 2), range_of(k_rope_shared, static_cast<size_t>(B) * Lk * 64 * 2),
+      range_of(v, nk * 128 * 2), range_of(out, nq * 128 * 2), range_of(dout, nq * 128 * 2), range_of(lse, nq * 4),
+      additive_mask ? range_of(additive_mask, static_cast<size_t>(B) * Lq * Lk * dt_size(mask_dt)) : Range{0, 0}};
+  const Range outs[5] = {range_of(dq, nq * 192 * 2), range_of(dk_nope, nk * 128 * 2),
+                         range_of(dk_rope_shared, static_cast<size_t>(B) * Lk * 64 * 2), range_of(dv, nk * 128 * 2),
+                         range_of(workspace, L.total)};
+  for (int i = 0; i < 5; ++i) {
+    for (const Range& r : ins)
+      if (overlaps(outs[i], r)) return fail(DFLASH_ERR_INVALID_ARG, "an output or the workspace overlaps an input");
+    for (int j = i + 1; j < 5; ++j)
+      if (overlaps(outs[i], outs[j])) return fail(DFLASH_ERR_INVALID_ARG, "outputs / workspace overlap each other");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  dflash::AttnBwdArgs a = {};
+  if (additive_mask) {
+    dflash_status st = check_occupancy_args(additive_mask, mask_dt, B, Lq, Lk, workspace, workspace_bytes, &L.t);
+    if (st != DFLASH_OK) return st;
+    const dflash::OccupancyArgs o = occupancy_args(additive_mask, mask_dt, B, Lq, Lk, workspace, L.t);
+    if (!(flags & DFLASH_ATTN_REUSE_TILE_MAP)) {
+      st = hip_status(dflash::launch_occupancy(o, s), "mask occupancy launch");
+      if (st != DFLASH_OK) return st;
+    }
+    a.classes = o.classes;
+    a.counts = o.counts;
+    a.lists = o.lists;
+    a.order = o.order;
+    a.bits = o.bits;
+  }
+  a.q = static_cast<const uint16_t*>(q);
+  a.kn = static_cast<const uint16_t*>(k_nope);
+  a.kr = static_cast<const uint16_t*>(k_rope_shared);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out = static_cast<const uint16_t*>(out);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.mask = additive_mask;
+  a.mask_bf16 = mask_dt == DFLASH_BF16;
+  a.lse = lse;
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dkn = static_cast<uint16_t*>(dk_nope);
+  a.dkr = static_cast<uint16_t*>(dk_rope_shared);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.lse2 = reinterpret_cast<float*>(ws + L.lse2);
+  a.dd = reinterpret_cast<float*>(ws + L.dd);
+  a.qT = reinterpret_cast<uint16_t*>(ws + L.qT);
+  a.doT = reinterpret_cast<uint16_t*>(ws + L.doT);
+  a.knT = reinterpret_cast<uint16_t*>(ws + L.knT);
+  a.krT = reinterpret_cast<uint16_t*>(ws + L.krT);
+  a.rope_part = reinterpret_cast<float*>(ws + L.rope);
+  a.B = static_cast<int>(B);
+  a.H = static_cast<int>(H);
+  a.Lq = static_cast<int>(Lq);
+  a.Lk = static_cast<int>(Lk);
+  a.nqt = static_cast<int>(L.t.nqt);
+  a.nkt = static_cast<int>(L.t.nkt);
+  a.Lqp = static_cast<int>(L.Lqp);
+  a.Lkp = static_cast<int>(L.Lkp);
+  a.scale = scale;
+  return hip_status(dflash::launch_attn_bwd_bf16(a, s), "attention backward launch");
 }
 
 dflash_status dflash_mla_block_occupancy(const int32_t* anchors, const int32_t* ctx_valid, int64_t B, int64_t A,

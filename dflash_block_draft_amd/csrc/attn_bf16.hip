@@ -502,6 +502,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
     const float a1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * kLog2e);
     const float l = l_run * a0 + l1 * a1;
     const float inv = l > 0.f ? 1.f / l : 0.f;
+    if (a.lse && q_ok && hi == 0) a.lse[bh * a.Lq + q_row] = l > 0.f ? m + __logf(l) : -INFINITY;
     if (q_ok) {
       uint16_t* op = a.out + (bh * a.Lq + q_row) * kDv;
       // o[j][r] holds dv = 32*j + 8*(r>>2) + 4*hi + (r&3)

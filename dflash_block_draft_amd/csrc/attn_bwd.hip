@@ -1,0 +1,616 @@
+// Backward of the fused draft MLA attention, bf16 MFMA on gfx950.
+//
+// The draft is trained (NeMo AutoModel DFlash page, KimiK3DFlashDraftModel: the
+// DFlash trainer drives it; DSpark page, module text: speculative-decoding
+// training), so the attention of the forward kernel needs its gradients.  With
+// p = exp(s - lse) recomputed from the saved per-row normaliser lse,
+//   dp = dout . v_j,  D = rowsum(dout * out),  ds = p * (dp - D)
+//   dv_j = sum_i p_ij dout_i          dk_j = scale * sum_i ds_ij q_i
+//   dq_i = scale * sum_j ds_ij k_j    dk_rope_j = sum over heads of dk_j[Dn:]
+// and the score matrix is never stored: both passes recompute their tile of p.
+//
+// Four launches (one ordered stream, no atomics, bitwise deterministic):
+//  1. prep_q: D, lse in log2 units (+inf for dead or padded rows, so their p is
+//     exactly 0), and transposed copies of q and dout.
+//  2. prep_k: transposed copies of k_nope (per head) and k_rope (per row).
+//  3. dkdv: one workgroup per (b, h, 128 keys); wave w owns 32 keys, keeps their
+//     K and V operands in registers and dK (32 x 192) and dV (32 x 128) in
+//     accumulators, and walks the 32-query chunks of every q-tile whose tiles
+//     with these keys are not empty.  S = Q K^T and dP = dO V^T put one key per
+//     lane, which is the A-operand layout of dV += P^T dO and dK += dS^T Q, so
+//     P and dS go from accumulator to operand without moving; the other
+//     operands (q and dout, reduction over queries) come from the transposed
+//     copies with 16-byte LDS reads.  dk_rope is written per head (fp32).
+//  4. dq: one workgroup per (b, q-tile, h) in the forward's ranked order; wave w
+//     owns 32 queries, keeps Q and dO in registers and walks the tile list:
+//     S^T = K Q^T and dP^T = V dO^T put one query per lane, and dS^T is the
+//     B operand of dQ^T += K^T dS^T, with K^T from the transposed copy.
+//  5. rope_reduce: dk_rope = sum over heads of the per-head parts, in head order.
+//
+// Operand staging is plain: 16-byte global loads into registers one chunk /
+// tile ahead, then 16-byte LDS stores into the other half of a double buffer,
+// with LDS rows padded by 16 bytes so the 16-byte column reads of 16 lanes hit
+// distinct banks.  Masks: class-0 tiles are skipped, class-1 tiles need no
+// mask work, class-2 tiles zero p for keys whose visibility bit is clear,
+// class-3 tiles add the mask values; keys past Lk get p = 0.
+#include "common.h"
+#include "launch.h"
+
+namespace dflash {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kQC = 32;                         // queries per dK/dV chunk
+constexpr int kKB = 128;                        // keys per dK/dV workgroup
+// LDS row strides (bytes): row + 16
+constexpr int kSQ = kDqk * 2 + 16;              // 400: q / k rows
+constexpr int kSO = kDv * 2 + 16;               // 272: dout / v rows
+constexpr int kSQT = kQC * 2 + 16;              // 80:  transposed q / dout rows (32 queries)
+constexpr int kSKT = kTileN * 2 + 16;           // 144: transposed k rows (64 keys)
+
+// dK/dV stage: Q, dO, Q^T, dO^T, lse2, D, visibility words (32 rows x 2 k-tiles)
+constexpr int kA_Q = 0;
+constexpr int kA_O = kA_Q + kQC * kSQ;
+constexpr int kA_QT = kA_O + kQC * kSO;
+constexpr int kA_OT = kA_QT + kDqk * kSQT;
+constexpr int kA_L = kA_OT + kDv * kSQT;
+constexpr int kA_D = kA_L + kQC * 4;
+constexpr int kA_B = kA_D + kQC * 4;
+constexpr int kA_Stage = kA_B + kQC * 2 * 8;
+static_assert(kA_Stage % 16 == 0, "stage alignment");
+
+// dQ stage: K, V, K^T
+constexpr int kB_K = 0;
+constexpr int kB_V = kB_K + kTileN * kSQ;
+constexpr int kB_KT = kB_V + kTileN * kSO;
+constexpr int kB_Stage = kB_KT + kDqk * kSKT;
+static_assert(2 * kB_Stage <= 160 * 1024, "LDS budget");
+
+// Position k of a 16-entry group holds entry relabel16(k): bits 2 and 3 swapped.
+__device__ __forceinline__ int relabel16(int k) { return (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
+__device__ __forceinline__ u32x4_t zero4() { return u32x4_t{0u, 0u, 0u, 0u}; }
+
+__device__ __forceinline__ bf16x8_t lds_frag(const char* p) { return as_bf16x8(*reinterpret_cast<const u32x4_t*>(p)); }
+
+// 8 floats -> one bf16x8 operand (round to nearest even)
+__device__ __forceinline__ bf16x8_t pack8(const float* x) {
+  const u32x4_t w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                     pack_bf16x2(x[6], x[7])};
+  return as_bf16x8(w);
+}
+
+__device__ __forceinline__ f32x16_t zero16() {
+  f32x16_t z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  return z;
+}
+
+template <bool MASK_BF16>
+__device__ __forceinline__ float mask_value(const void* mask, size_t idx) {
+  if (MASK_BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(mask)[idx]);
+  return static_cast<const float*>(mask)[idx];
+}
+
+// ---------------------------------------------------------------- 1. prep_q
+// grid (Lqp / 32, B*H): D, lse2 and the transposed q / dout of 32 queries.
+__global__ void __launch_bounds__(kThreads) bwd_prep_q(AttnBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char sq[kQC * kSQ];
+  __shared__ __attribute__((aligned(16))) char so[kQC * kSO];
+  const int t = threadIdx.x;
+  const int q0 = blockIdx.x * kQC;
+  const size_t bh = blockIdx.y;
+  for (int i = t; i < kQC * 24; i += kThreads) {
+    const int r = i / 24, c = i % 24, qi = q0 + r;
+    *reinterpret_cast<u32x4_t*>(sq + r * kSQ + c * 16) =
+        qi < a.Lq ? ldg16(a.q + (bh * a.Lq + qi) * kDqk + c * 8) : zero4();
+  }
+  for (int i = t; i < kQC * 16; i += kThreads) {
+    const int r = i / 16, c = i % 16, qi = q0 + r;
+    *reinterpret_cast<u32x4_t*>(so + r * kSO + c * 16) =
+        qi < a.Lq ? ldg16(a.dout + (bh * a.Lq + qi) * kDv + c * 8) : zero4();
+  }
+  {  // D: 8 lanes per row, 16 dims each
+    const int r = t >> 3, part = t & 7, qi = q0 + r;
+    float acc = 0.f;
+    if (qi < a.Lq) {
+      const uint16_t* op = a.out + (bh * a.Lq + qi) * kDv + part * 16;
+      const uint16_t* gp = a.dout + (bh * a.Lq + qi) * kDv + part * 16;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const u32x4_t o = ldg16(op + 8 * h2), g = ldg16(gp + 8 * h2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc += bf16_bits_to_f32(o[j] & 0xFFFFu) * bf16_bits_to_f32(g[j] & 0xFFFFu);
+          acc += bf16_bits_to_f32(o[j] >> 16) * bf16_bits_to_f32(g[j] >> 16);
+        }
+      }
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 4);
+    if (part == 0) {
+      a.dd[bh * a.Lqp + qi] = acc;
+      const float l = qi < a.Lq ? a.lse[bh * a.Lq + qi] : -INFINITY;
+      a.lse2[bh * a.Lqp + qi] = l == -INFINITY ? INFINITY : l * kLog2e;
+    }
+  }
+  __syncthreads();
+  const uint16_t* sq16 = reinterpret_cast<const uint16_t*>(sq);
+  const uint16_t* so16 = reinterpret_cast<const uint16_t*>(so);
+  // transposed rows: 4 chunks of 8 positions per 32-query row
+  for (int i = t; i < (kDqk + kDv) * 4; i += kThreads) {
+    const int d = i >> 2, g = i & 3;
+    const bool isq = d < kDqk;
+    const int dd = isq ? d : d - kDqk;
+    const uint16_t* src = isq ? sq16 : so16;
+    const int stride = (isq ? kSQ : kSO) / 2;
+    uint32_t w[4];
+#pragma unroll
+    for (int p = 0; p < 8; p += 2) {
+      const int k0 = 8 * g + p, k1 = k0 + 1;
+      const int r0 = (k0 & 16) | relabel16(k0 & 15), r1 = (k1 & 16) | relabel16(k1 & 15);
+      w[p >> 1] = static_cast<uint32_t>(src[r0 * stride + dd]) | (static_cast<uint32_t>(src[r1 * stride + dd]) << 16);
+    }
+    uint16_t* dst = isq ? a.qT + (bh * kDqk + dd) * a.Lqp : a.doT + (bh * kDv + dd) * a.Lqp;
+    stg16(dst + q0 + 8 * g, u32x4_t{w[0], w[1], w[2], w[3]});
+  }
+}
+
+// ---------------------------------------------------------------- 2. prep_k
+// grid (Lkp / 64, B*H): transposed k_nope of 64 keys; the h == 0 workgroups also
+// transpose the batch row's k_rope.
+__global__ void __launch_bounds__(kThreads) bwd_prep_k(AttnBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sk[kTileN * (kDn + 8)];
+  __shared__ __attribute__((aligned(16))) uint16_t sr[kTileN * (kDr + 8)];
+  const int t = threadIdx.x;
+  const int k0 = blockIdx.x * kTileN;
+  const size_t bh = blockIdx.y;
+  const int b = static_cast<int>(bh / a.H), h = static_cast<int>(bh % a.H);
+  const bool rope = h == 0;
+  for (int i = t; i < kTileN * 16; i += kThreads) {
+    const int r = i >> 4, c = i & 15, kj = k0 + r;
+    *reinterpret_cast<u32x4_t*>(sk + r * (kDn + 8) + c * 8) =
+        kj < a.Lk ? ldg16(a.kn + (bh * a.Lk + kj) * kDn + c * 8) : zero4();
+  }
+  if (rope) {
+    for (int i = t; i < kTileN * 8; i += kThreads) {
+      const int r = i >> 3, c = i & 7, kj = k0 + r;
+      *reinterpret_cast<u32x4_t*>(sr + r * (kDr + 8) + c * 8) =
+          kj < a.Lk ? ldg16(a.kr + (static_cast<size_t>(b) * a.Lk + kj) * kDr + c * 8) : zero4();
+    }
+  }
+  __syncthreads();
+  const int rows = rope ? kDn + kDr : kDn;
+  for (int i = t; i < rows * 8; i += kThreads) {
+    const int d = i >> 3, g = i & 7;
+    const bool isn = d < kDn;
+    const int dd = isn ? d : d - kDn;
+    const uint16_t* src = isn ? sk : sr;
+    const int stride = isn ? kDn + 8 : kDr + 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int p = 0; p < 8; p += 2) {
+      const int j0 = 8 * g + p, j1 = j0 + 1;
+      const int r0 = (j0 & 48) | relabel16(j0 & 15), r1 = (j1 & 48) | relabel16(j1 & 15);
+      w[p >> 1] = static_cast<uint32_t>(src[r0 * stride + dd]) | (static_cast<uint32_t>(src[r1 * stride + dd]) << 16);
+    }
+    uint16_t* dst = isn ? a.knT + (bh * kDn + dd) * a.Lkp : a.krT + (static_cast<size_t>(b) * kDr + dd) * a.Lkp;
+    stg16(dst + k0 + 8 * g, u32x4_t{w[0], w[1], w[2], w[3]});
+  }
+}
+
+// ---------------------------------------------------------------- 3. dK / dV
+template <bool MASK_BF16>
+__global__ void __launch_bounds__(kThreads) bwd_dkdv(AttnBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kA_Stage];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int li = lane & 31, hi = lane >> 5;
+  const int kb = blockIdx.x;
+  const size_t bh = blockIdx.y;
+  const int b = static_cast<int>(bh / a.H);
+  const int kt0 = 2 * kb;                              // this workgroup's k-tiles: kt0, kt0 + 1
+  const bool has_kt1 = kt0 + 1 < a.nkt;
+  const int key = kb * kKB + 32 * w + li;              // this lane's key (operands, p column)
+  const bool key_ok = key < a.Lk;
+  const int bit = (w & 1) * 32 + li;                   // its bit in the k-tile's visibility words
+
+  bf16x8_t kreg[12], vreg[8];
+#pragma unroll
+  for (int s = 0; s < 12; ++s) {
+    u32x4_t x = zero4();
+    if (key_ok) x = s < 8 ? ldg16(a.kn + (bh * a.Lk + key) * kDn + 16 * s + 8 * hi)
+                          : ldg16(a.kr + (static_cast<size_t>(b) * a.Lk + key) * kDr + 16 * (s - 8) + 8 * hi);
+    kreg[s] = as_bf16x8(x);
+  }
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    vreg[s] = as_bf16x8(key_ok ? ldg16(a.v + (bh * a.Lk + key) * kDv + 16 * s + 8 * hi) : zero4());
+
+  f32x16_t dk[6], dv[4];
+#pragma unroll
+  for (int i = 0; i < 6; ++i) dk[i] = zero16();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dv[i] = zero16();
+
+  // chunk iterator over (q-tile, 32-query chunk) with a non-empty tile in kt0 / kt0+1
+  auto tile_cls = [&](int qt, int kt) -> int {
+    if (!a.classes) return 1;
+    return a.classes[(static_cast<size_t>(b) * a.nqt + qt) * a.nkt + kt];
+  };
+  auto next_qt = [&](int qt) -> int {
+    for (++qt; qt < a.nqt; ++qt)
+      if (tile_cls(qt, kt0) != 0 || (has_kt1 && tile_cls(qt, kt0 + 1) != 0)) break;
+    return qt;
+  };
+  auto advance = [&](int& qt, int& c) {
+    ++c;
+    if (c == kTileM / kQC || qt * kTileM + c * kQC >= a.Lq) {
+      c = 0;
+      qt = next_qt(qt);
+    }
+  };
+
+  u32x4_t pre[11];
+  auto prefetch = [&](int qt, int c, int cls0, int cls1) {
+    const int q0 = qt * kTileM + c * kQC;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {                     // q rows: 32 x 24 chunks
+      const int ci = t + kThreads * i, r = ci / 24, ch = ci % 24, qi = q0 + r;
+      pre[i] = qi < a.Lq ? ldg16(a.q + (bh * a.Lq + qi) * kDqk + ch * 8) : zero4();
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {                     // dout rows: 32 x 16 chunks
+      const int ci = t + kThreads * i, r = ci >> 4, ch = ci & 15, qi = q0 + r;
+      pre[3 + i] = qi < a.Lq ? ldg16(a.dout + (bh * a.Lq + qi) * kDv + ch * 8) : zero4();
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {                     // q^T: 192 rows x 4 chunks
+      const int ci = t + kThreads * i, d = ci >> 2, ch = ci & 3;
+      pre[5 + i] = ldg16(a.qT + (bh * kDqk + d) * a.Lqp + q0 + ch * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {                     // dout^T: 128 rows x 4 chunks
+      const int ci = t + kThreads * i, d = ci >> 2, ch = ci & 3;
+      pre[8 + i] = ldg16(a.doT + (bh * kDv + d) * a.Lqp + q0 + ch * 8);
+    }
+    pre[10] = zero4();
+    if (t < 16) {                                     // lse2 (t < 8), D (8 <= t < 16)
+      const float* src = t < 8 ? a.lse2 : a.dd;
+      pre[10] = *reinterpret_cast<const u32x4_t*>(src + bh * a.Lqp + q0 + 4 * (t & 7));
+    } else if (t < 16 + 2 * kQC) {                    // visibility words of class-2 tiles
+      const int j = t - 16, r = j >> 1, th = j & 1;
+      const int cls = th ? cls1 : cls0;
+      if (cls == 2 && q0 + r < a.Lq) {
+        const size_t tile = (static_cast<size_t>(b) * a.nqt + qt) * a.nkt + kt0 + th;
+        const uint64_t word = a.bits[tile * kTileM + c * kQC + r];
+        pre[10] = u32x4_t{static_cast<uint32_t>(word), static_cast<uint32_t>(word >> 32), 0u, 0u};
+      }
+    }
+  };
+  auto commit = [&](char* st) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int ci = t + kThreads * i;
+      *reinterpret_cast<u32x4_t*>(st + kA_Q + (ci / 24) * kSQ + (ci % 24) * 16) = pre[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ci = t + kThreads * i;
+      *reinterpret_cast<u32x4_t*>(st + kA_O + (ci >> 4) * kSO + (ci & 15) * 16) = pre[3 + i];
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int ci = t + kThreads * i;
+      *reinterpret_cast<u32x4_t*>(st + kA_QT + (ci >> 2) * kSQT + (ci & 3) * 16) = pre[5 + i];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ci = t + kThreads * i;
+      *reinterpret_cast<u32x4_t*>(st + kA_OT + (ci >> 2) * kSQT + (ci & 3) * 16) = pre[8 + i];
+    }
+    if (t < 16) {
+      *reinterpret_cast<u32x4_t*>(st + (t < 8 ? kA_L : kA_D) + 16 * (t & 7)) = pre[10];
+    } else if (t < 16 + 2 * kQC) {
+      const int j = t - 16;
+      *reinterpret_cast<u32x2_t*>(st + kA_B + 8 * j) = u32x2_t{pre[10][0], pre[10][1]};
+    }
+  };
+
+  const float scale_log2 = a.scale * kLog2e;
+  auto compute = [&](const char* st, int qt, int c, int cls) {
+    if (cls == 0) return;
+    f32x16_t S = zero16(), dP = zero16();
+#pragma unroll
+    for (int s = 0; s < 12; ++s) S = mfma32(lds_frag(st + kA_Q + li * kSQ + (16 * s + 8 * hi) * 2), kreg[s], S);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) dP = mfma32(lds_frag(st + kA_O + li * kSO + (16 * s + 8 * hi) * 2), vreg[s], dP);
+    __builtin_amdgcn_sched_barrier(0);
+    const int q0 = qt * kTileM + c * kQC;
+    float madd[16];                                   // log2(e) * mask values (general tiles only)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) madd[r] = 0.f;
+    if (cls == 3) {
+      for (int r = 0; r < 16; ++r) {
+        const int qr = 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (key_ok && q0 + qr < a.Lq)
+          madd[r] = mask_value<MASK_BF16>(a.mask, (static_cast<size_t>(b) * a.Lq + q0 + qr) * a.Lk + key) * kLog2e;
+      }
+    }
+    float p[16], ds[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(st + kA_L + (8 * g + 4 * hi) * 4);
+      const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(st + kA_D + (8 * g + 4 * hi) * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e, qr = 8 * g + 4 * hi + e;   // accumulator row r <-> chunk query qr
+        bool vis = key_ok;
+        if (cls == 2) {
+          const uint64_t word = *reinterpret_cast<const uint64_t*>(st + kA_B + (2 * qr + (w >> 1)) * 8);
+          vis = vis && ((word >> bit) & 1ull);
+        }
+        const float pr = vis ? __builtin_amdgcn_exp2f(S[r] * scale_log2 - l4[e] + madd[r]) : 0.f;
+        p[r] = pr;
+        ds[r] = pr * (dP[r] - d4[e]);
+      }
+    }
+    const bf16x8_t aP0 = pack8(p), aP1 = pack8(p + 8);
+    const bf16x8_t aS0 = pack8(ds), aS1 = pack8(ds + 8);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const char* rowp = st + kA_OT + (32 * nt + li) * kSQT + 16 * hi;
+      dv[nt] = mfma32(aP0, lds_frag(rowp), dv[nt]);
+      dv[nt] = mfma32(aP1, lds_frag(rowp + 32), dv[nt]);
+    }
+#pragma unroll
+    for (int nt = 0; nt < 6; ++nt) {
+      const char* rowp = st + kA_QT + (32 * nt + li) * kSQT + 16 * hi;
+      dk[nt] = mfma32(aS0, lds_frag(rowp), dk[nt]);
+      dk[nt] = mfma32(aS1, lds_frag(rowp + 32), dk[nt]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  int qt = next_qt(-1), c = 0;
+  if (qt < a.nqt) {
+    int cls0 = tile_cls(qt, kt0), cls1 = has_kt1 ? tile_cls(qt, kt0 + 1) : 0;
+    prefetch(qt, c, cls0, cls1);
+    commit(smem);
+    __syncthreads();
+    for (int it = 0;; ++it) {
+      int nqt_ = qt, nc = c;
+      advance(nqt_, nc);
+      const bool more = nqt_ < a.nqt;
+      int ncls0 = 0, ncls1 = 0;
+      if (more) {
+        ncls0 = tile_cls(nqt_, kt0);
+        ncls1 = has_kt1 ? tile_cls(nqt_, kt0 + 1) : 0;
+        prefetch(nqt_, nc, ncls0, ncls1);
+      }
+      compute(smem + (it & 1) * kA_Stage, qt, c, (w >> 1) ? cls1 : cls0);
+      if (!more) break;
+      commit(smem + ((it + 1) & 1) * kA_Stage);
+      __syncthreads();
+      qt = nqt_;
+      c = nc;
+      cls0 = ncls0;
+      cls1 = ncls1;
+    }
+  }
+
+  // accumulator row r <-> key 8*(r/4) + 4*hi + r%4 of the wave's 32, column <-> dim
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int kj = kb * kKB + 32 * w + 8 * (r >> 2) + 4 * hi + (r & 3);
+    if (kj >= a.Lk) continue;
+    const size_t row = bh * a.Lk + kj;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const uint32_t kv = pack_bf16x2(dk[nt][r] * a.scale, dv[nt][r]);
+      a.dkn[row * kDn + 32 * nt + li] = static_cast<uint16_t>(kv & 0xFFFFu);
+      a.dv[row * kDv + 32 * nt + li] = static_cast<uint16_t>(kv >> 16);
+    }
+#pragma unroll
+    for (int nt = 4; nt < 6; ++nt) a.rope_part[row * kDr + 32 * (nt - 4) + li] = dk[nt][r] * a.scale;
+  }
+}
+
+// ---------------------------------------------------------------- 4. dQ
+template <bool MASK_BF16>
+__global__ void __launch_bounds__(kThreads) bwd_dq(AttnBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kB_Stage];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int li = lane & 31, hi = lane >> 5;
+  const int rank = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int row = a.order ? a.order[rank] : rank;      // b * nqt + qt
+  const int b = row / a.nqt, qt = row % a.nqt;
+  const size_t bh = static_cast<size_t>(b) * a.H + h;
+  const int qi = qt * kTileM + 32 * w + li;            // this lane's query
+  const bool q_ok = qi < a.Lq;
+
+  bf16x8_t qreg[12], oreg[8];
+#pragma unroll
+  for (int s = 0; s < 12; ++s)
+    qreg[s] = as_bf16x8(q_ok ? ldg16(a.q + (bh * a.Lq + qi) * kDqk + 16 * s + 8 * hi) : zero4());
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    oreg[s] = as_bf16x8(q_ok ? ldg16(a.dout + (bh * a.Lq + qi) * kDv + 16 * s + 8 * hi) : zero4());
+  const float lse2 = a.lse2[bh * a.Lqp + qi];
+  const float dd = a.dd[bh * a.Lqp + qi];
+
+  f32x16_t dq[6];
+#pragma unroll
+  for (int i = 0; i < 6; ++i) dq[i] = zero16();
+
+  const int n = a.lists ? a.counts[row] : a.nkt;
+  const int32_t* list = a.lists ? a.lists + static_cast<size_t>(row) * a.nkt : nullptr;
+  auto entry = [&](int e) -> int { return list ? list[e] : (e | (1 << 24)); };
+
+  u32x4_t pre[16];
+  auto prefetch = [&](int kt) {
+    const int k0 = kt * kTileN;
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {                     // K rows: 64 x (16 nope + 8 rope) chunks
+      const int ci = t + kThreads * i, r = ci / 24, ch = ci % 24, kj = k0 + r;
+      u32x4_t x = zero4();
+      if (kj < a.Lk)
+        x = ch < 16 ? ldg16(a.kn + (bh * a.Lk + kj) * kDn + ch * 8)
+                    : ldg16(a.kr + (static_cast<size_t>(b) * a.Lk + kj) * kDr + (ch - 16) * 8);
+      pre[i] = x;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {                     // V rows: 64 x 16 chunks
+      const int ci = t + kThreads * i, r = ci >> 4, ch = ci & 15, kj = k0 + r;
+      pre[6 + i] = kj < a.Lk ? ldg16(a.v + (bh * a.Lk + kj) * kDv + ch * 8) : zero4();
+    }
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {                     // K^T: 192 rows x 8 chunks
+      const int ci = t + kThreads * i, d = ci >> 3, ch = ci & 7;
+      const uint16_t* src = d < kDn ? a.knT + (bh * kDn + d) * a.Lkp
+                                    : a.krT + (static_cast<size_t>(b) * kDr + d - kDn) * a.Lkp;
+      pre[10 + i] = ldg16(src + k0 + ch * 8);
+    }
+  };
+  auto commit = [&](char* st) {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int ci = t + kThreads * i;
+      *reinterpret_cast<u32x4_t*>(st + kB_K + (ci / 24) * kSQ + (ci % 24) * 16) = pre[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ci = t + kThreads * i;
+      *reinterpret_cast<u32x4_t*>(st + kB_V + (ci >> 4) * kSO + (ci & 15) * 16) = pre[6 + i];
+    }
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int ci = t + kThreads * i;
+      *reinterpret_cast<u32x4_t*>(st + kB_KT + (ci >> 3) * kSKT + (ci & 7) * 16) = pre[10 + i];
+    }
+  };
+
+  const float scale_log2 = a.scale * kLog2e;
+  auto compute = [&](const char* st, int kt, int cls) {
+    uint64_t word = 0;
+    if (cls == 2 && q_ok) word = a.bits[((static_cast<size_t>(row) * a.nkt + kt) * kTileM) + 32 * w + li];
+    bf16x8_t bS[4];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      f32x16_t S = zero16(), dP = zero16();
+#pragma unroll
+      for (int s = 0; s < 12; ++s)
+        S = mfma32(lds_frag(st + kB_K + (32 * half + li) * kSQ + (16 * s + 8 * hi) * 2), qreg[s], S);
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        dP = mfma32(lds_frag(st + kB_V + (32 * half + li) * kSO + (16 * s + 8 * hi) * 2), oreg[s], dP);
+      __builtin_amdgcn_sched_barrier(0);
+      float madd[16];                                 // log2(e) * mask values (general tiles only)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) madd[r] = 0.f;
+      if (cls == 3) {
+        for (int r = 0; r < 16; ++r) {
+          const int kj = kt * kTileN + 32 * half + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (kj < a.Lk && q_ok)
+            madd[r] = mask_value<MASK_BF16>(a.mask, (static_cast<size_t>(b) * a.Lq + qi) * a.Lk + kj) * kLog2e;
+        }
+      }
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kl = 32 * half + 8 * (r >> 2) + 4 * hi + (r & 3);   // key within the tile
+        bool vis = kt * kTileN + kl < a.Lk;
+        if (cls == 2) vis = vis && ((word >> kl) & 1ull);
+        const float pr = vis ? __builtin_amdgcn_exp2f(S[r] * scale_log2 - lse2 + madd[r]) : 0.f;
+        ds[r] = pr * (dP[r] - dd);
+      }
+      bS[2 * half] = pack8(ds);
+      bS[2 * half + 1] = pack8(ds + 8);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 6; ++mt) {
+      const char* rowp = st + kB_KT + (32 * mt + li) * kSKT + 16 * hi;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) dq[mt] = mfma32(lds_frag(rowp + 32 * kk), bS[kk], dq[mt]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  if (n > 0) {
+    int e0 = entry(0);
+    prefetch(e0 & 0xFFFFFF);
+    commit(smem);
+    __syncthreads();
+    for (int e = 0; e < n; ++e) {
+      const bool more = e + 1 < n;
+      int e1 = 0;
+      if (more) {
+        e1 = entry(e + 1);
+        prefetch(e1 & 0xFFFFFF);
+      }
+      compute(smem + (e & 1) * kB_Stage, e0 & 0xFFFFFF, e0 >> 24);
+      if (!more) break;
+      commit(smem + ((e + 1) & 1) * kB_Stage);
+      __syncthreads();
+      e0 = e1;
+    }
+  }
+
+  // accumulator row r <-> dim 32*mt + 8*(r/4) + 4*hi + r%4, column <-> this lane's query
+  if (q_ok) {
+    uint16_t* op = a.dq + (bh * a.Lq + qi) * kDqk;
+#pragma unroll
+    for (int mt = 0; mt < 6; ++mt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x2_t w2 = {pack_bf16x2(dq[mt][4 * g] * a.scale, dq[mt][4 * g + 1] * a.scale),
+                            pack_bf16x2(dq[mt][4 * g + 2] * a.scale, dq[mt][4 * g + 3] * a.scale)};
+        *reinterpret_cast<u32x2_t*>(op + 32 * mt + 8 * g + 4 * hi) = w2;
+      }
+  }
+}
+
+// ---------------------------------------------------------------- 5. dk_rope
+// One thread per 4 consecutive dims of one (b, key): sum over heads in order.
+__global__ void __launch_bounds__(kThreads) bwd_rope_reduce(AttnBwdArgs a) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(a.B) * a.Lk * (kDr / 4);
+  if (i >= total) return;
+  const int d4 = static_cast<int>(i % (kDr / 4));
+  const int64_t bk = i / (kDr / 4);
+  const int b = static_cast<int>(bk / a.Lk), kj = static_cast<int>(bk % a.Lk);
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int h = 0; h < a.H; ++h) {
+    const size_t row = (static_cast<size_t>(b) * a.H + h) * a.Lk + kj;
+    acc += *reinterpret_cast<const f32x4_t*>(a.rope_part + row * kDr + 4 * d4);
+  }
+  const u32x2_t w2 = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+  *reinterpret_cast<u32x2_t*>(a.dkr + (static_cast<size_t>(b) * a.Lk + kj) * kDr + 4 * d4) = w2;
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
+  const unsigned bh = static_cast<unsigned>(a.B) * a.H;
+  hipLaunchKernelGGL(bwd_prep_q, dim3(a.Lqp / kQC, bh), dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_prep_k, dim3(a.Lkp / kTileN, bh), dim3(kThreads), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const dim3 gkv((a.Lk + kKB - 1) / kKB, bh);
+  if (a.mask && a.mask_bf16) hipLaunchKernelGGL(bwd_dkdv<true>, gkv, dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL(bwd_dkdv<false>, gkv, dim3(kThreads), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const dim3 gq(static_cast<unsigned>(a.B) * a.nqt * a.H);
+  if (a.mask && a.mask_bf16) hipLaunchKernelGGL(bwd_dq<true>, gq, dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL(bwd_dq<false>, gq, dim3(kThreads), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t n4 = static_cast<int64_t>(a.B) * a.Lk * (kDr / 4);
+  hipLaunchKernelGGL(bwd_rope_reduce, dim3(static_cast<unsigned>((n4 + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace dflash

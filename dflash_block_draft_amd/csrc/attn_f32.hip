@@ -84,6 +84,7 @@ __global__ void __launch_bounds__(64) attn_fwd_f32(AttnF32Args a) {
   }
   if (!q_ok) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (a.lse) a.lse[bh * a.Lq + qi] = l > 0.f ? m + logf(l) : -INFINITY;
   float* op = a.out + (bh * a.Lq + qi) * kDv;
 #pragma unroll
   for (int d = 0; d < kDv; ++d) op[d] = o[d] * inv;

@@ -23,12 +23,14 @@ struct AttnBf16Args {
   int B, H, Lq, Lk, nqt, nkt;
   float scale;            // softmax scale (natural units)
   int mask_bf16;          // 1: mask is bf16, 0: f32
+  float* lse;             // [B,H,Lq] f32 natural-log row normaliser (-inf: dead row), or null
 };
 
 struct AttnF32Args {
   const float* q; const float* kn; const float* kr; const float* v;
   const float* mask;      // [B,1,Lq,Lk] f32 or null
   float* out;
+  float* lse;             // [B,H,Lq] or null
   int B, H, Lq, Lk;
   float scale;
 };
@@ -45,6 +47,29 @@ struct OccupancyArgs {
   int A, bs, ctx;
 };
 
+// Attention backward (bf16).  Workspace arrays are padded: Lqp = nqt*128 queries,
+// Lkp = nkt*64 keys.  The transposed copies hold, per 16-entry group, entry
+// 16g + k at position 16g + k with bits 2 and 3 of k swapped (the order in which
+// an MFMA accumulator's rows become the next MFMA's reduction index).
+struct AttnBwdArgs {
+  const uint16_t* q; const uint16_t* kn; const uint16_t* kr; const uint16_t* v;
+  const uint16_t* out; const uint16_t* dout;
+  const void* mask; int mask_bf16;
+  const float* lse;                       // [B,H,Lq]
+  uint16_t* dq; uint16_t* dkn; uint16_t* dkr; uint16_t* dv;
+  const uint8_t* classes; const int32_t* counts; const int32_t* lists; const int32_t* order;
+  const uint64_t* bits;                   // tile map (null classes: every tile visible, no lists)
+  float* lse2;                            // [B*H, Lqp] lse * log2(e); +inf for dead / padded rows
+  float* dd;                              // [B*H, Lqp] rowsum(dout * out)
+  uint16_t* qT;                           // [B*H, 192, Lqp]
+  uint16_t* doT;                          // [B*H, 128, Lqp]
+  uint16_t* knT;                          // [B*H, 128, Lkp]
+  uint16_t* krT;                          // [B, 64, Lkp]
+  float* rope_part;                       // [B*H, Lk, 64] per-head k_rope gradients
+  int B, H, Lq, Lk, nqt, nkt, Lqp, Lkp;
+  float scale;
+};
+
 struct ExpandArgs {
   const void* latent; const void* w;  // [B,Lk,R], [H*256,R]
   void* kn; void* v;                  // [B,H,Lk,128] each
@@ -58,6 +83,7 @@ hipError_t launch_occupancy(const OccupancyArgs& a, hipStream_t s);
 hipError_t launch_block_occupancy(const OccupancyArgs& a, hipStream_t s);
 // Rewrite the lists so every k-tile is visited (empty tiles as class 3); debug/verification mode.
 hipError_t launch_lists_all_tiles(const OccupancyArgs& a, hipStream_t s);
+hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s);
 hipError_t launch_expand_bf16(const ExpandArgs& a, hipStream_t s);
 hipError_t launch_expand_f32(const ExpandArgs& a, hipStream_t s);
 

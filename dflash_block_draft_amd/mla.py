@@ -30,7 +30,8 @@ EXPORTED = (
     "dflash_status_string", "dflash_last_error", "dflash_mla_latent_expand",
     "dflash_mla_attn_workspace_bytes", "dflash_mla_tile_map_layout",
     "dflash_mla_mask_occupancy", "dflash_mla_attn", "dflash_mla_block_occupancy",
-    "dflash_mla_attn_blocks",
+    "dflash_mla_attn_blocks", "dflash_mla_attn_lse", "dflash_mla_attn_bwd_workspace_bytes",
+    "dflash_mla_attn_bwd",
 )
 
 
@@ -73,6 +74,14 @@ def load_library() -> ctypes.CDLL:
     lib.dflash_mla_attn.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32,
                                     i32, i32, vp, sz, u32, vp]
     lib.dflash_mla_attn.restype = i32
+    lib.dflash_mla_attn_lse.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32,
+                                        i32, i32, vp, sz, u32, vp]
+    lib.dflash_mla_attn_lse.restype = i32
+    lib.dflash_mla_attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.dflash_mla_attn_bwd_workspace_bytes.restype = sz
+    lib.dflash_mla_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                        i64, i64, i64, f32, i32, i32, vp, sz, u32, vp]
+    lib.dflash_mla_attn_bwd.restype = i32
     lib.dflash_mla_block_occupancy.argtypes = [vp, vp, i64, i64, i64, i64, vp, sz, vp]
     lib.dflash_mla_block_occupancy.restype = i32
     lib.dflash_mla_attn_blocks.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64,
@@ -185,10 +194,11 @@ def tile_map_view(workspace: torch.Tensor, B: int, Lq: int, Lk: int) -> dict:
 def mla_attn(q: torch.Tensor, k_nope: torch.Tensor, k_rope: torch.Tensor, v: torch.Tensor,
              mask: Optional[torch.Tensor] = None, scale: Optional[float] = None, *,
              out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-             reuse_tile_map: bool = False, tile_skip: bool = True) -> torch.Tensor:
+             reuse_tile_map: bool = False, tile_skip: bool = True, lse: Optional[torch.Tensor] = None):
     """Draft MLA attention: q [B,H,Lq,Dn+Dr], k_nope [B,H,Lk,Dn], k_rope [B,Lk,Dr] (head-shared),
     v [B,H,Lk,Dv], mask [B,1,Lq,Lk] or None -> out [B,H,Lq,Dv].  scale defaults to
-    q_head_dim ** -0.5."""
+    q_head_dim ** -0.5.  With `lse` (a float32 [B,H,Lq] device tensor) the row
+    log-normalisers are written there too (dflash_mla_attn_lse)."""
     lib = load_library()
     _dev(q, "q", ndim=4)
     dt = q.dtype
@@ -220,11 +230,72 @@ def mla_attn(q: torch.Tensor, k_nope: torch.Tensor, k_rope: torch.Tensor, v: tor
     if workspace is not None:
         _dev(workspace, "workspace", dtype=torch.uint8)
     flags = (FLAG_REUSE_TILE_MAP if reuse_tile_map else 0) | (0 if tile_skip else FLAG_NO_TILE_SKIP)
-    _check(lib.dflash_mla_attn(_ptr(q), _ptr(k_nope), _ptr(k_rope), _ptr(v), _ptr(mask), _ptr(out),
-                               B, H, Lq, Lk, Dn, Dr, Dv, float(scale), _DT[dt], mask_dt,
-                               _ptr(workspace), 0 if workspace is None else workspace.numel(),
-                               flags, _stream(q)))
+    wsb = 0 if workspace is None else workspace.numel()
+    if lse is None:
+        _check(lib.dflash_mla_attn(_ptr(q), _ptr(k_nope), _ptr(k_rope), _ptr(v), _ptr(mask), _ptr(out),
+                                   B, H, Lq, Lk, Dn, Dr, Dv, float(scale), _DT[dt], mask_dt,
+                                   _ptr(workspace), wsb, flags, _stream(q)))
+    else:
+        _dev(lse, "lse", dtype=torch.float32, ndim=3)
+        if tuple(lse.shape) != (B, H, Lq):
+            raise ValueError(f"lse must be [{B}, {H}, {Lq}]")
+        _check(lib.dflash_mla_attn_lse(_ptr(q), _ptr(k_nope), _ptr(k_rope), _ptr(v), _ptr(mask), _ptr(out),
+                                       _ptr(lse), B, H, Lq, Lk, Dn, Dr, Dv, float(scale), _DT[dt], mask_dt,
+                                       _ptr(workspace), wsb, flags, _stream(q)))
     return out
+
+
+def attn_bwd_workspace_bytes(B: int, H: int, Lq: int, Lk: int) -> int:
+    return int(load_library().dflash_mla_attn_bwd_workspace_bytes(B, H, Lq, Lk))
+
+
+def new_bwd_workspace(B: int, H: int, Lq: int, Lk: int, device) -> torch.Tensor:
+    """A workspace for the backward; it also serves the forward (the tile map comes first)."""
+    n = attn_bwd_workspace_bytes(B, H, Lq, Lk)
+    if n == 0:
+        raise ValueError("invalid sizes for the backward workspace")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def mla_attn_bwd(q: torch.Tensor, k_nope: torch.Tensor, k_rope: torch.Tensor, v: torch.Tensor,
+                 mask: Optional[torch.Tensor], out: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor,
+                 scale: Optional[float] = None, *, workspace: Optional[torch.Tensor] = None,
+                 reuse_tile_map: bool = False, grads=None):
+    """Gradients (dq, dk_nope, dk_rope, dv) of mla_attn (bf16); out and lse from the
+    forward with lse.  `grads` may supply the four output tensors."""
+    lib = load_library()
+    for t, n, nd in ((q, "q", 4), (k_nope, "k_nope", 4), (k_rope, "k_rope", 3), (v, "v", 4), (out, "out", 4),
+                     (dout, "dout", 4)):
+        _dev(t, n, dtype=torch.bfloat16, ndim=nd)
+    _dev(lse, "lse", dtype=torch.float32, ndim=3)
+    B, H, Lq, _ = q.shape
+    Lk, Dn, Dr, Dv = k_nope.shape[2], k_nope.shape[3], k_rope.shape[2], v.shape[3]
+    if tuple(out.shape) != (B, H, Lq, Dv) or tuple(dout.shape) != (B, H, Lq, Dv) or tuple(lse.shape) != (B, H, Lq):
+        raise ValueError("out / dout / lse shapes are inconsistent with q and v")
+    if scale is None:
+        scale = float(Dn + Dr) ** -0.5
+    mask_dt = _F32
+    if mask is not None:
+        _dev(mask, "mask", ndim=4)
+        mask_dt = _DT[mask.dtype]
+    if workspace is None:
+        if reuse_tile_map:
+            raise ValueError("reuse_tile_map needs the workspace that holds the map")
+        workspace = new_bwd_workspace(B, H, Lq, Lk, q.device)
+    _dev(workspace, "workspace", dtype=torch.uint8)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k_nope), torch.empty_like(k_rope), torch.empty_like(v))
+    dq, dkn, dkr, dv = grads
+    for t, ref, n in ((dq, q, "dq"), (dkn, k_nope, "dk_nope"), (dkr, k_rope, "dk_rope"), (dv, v, "dv")):
+        _dev(t, n, dtype=torch.bfloat16)
+        if t.shape != ref.shape:
+            raise ValueError(f"{n} must have shape {tuple(ref.shape)}")
+    _check(lib.dflash_mla_attn_bwd(_ptr(q), _ptr(k_nope), _ptr(k_rope), _ptr(v), _ptr(mask), _ptr(out),
+                                   _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dkn), _ptr(dkr), _ptr(dv),
+                                   B, H, Lq, Lk, Dn, Dr, Dv, float(scale), _BF16, mask_dt,
+                                   _ptr(workspace), workspace.numel(),
+                                   FLAG_REUSE_TILE_MAP if reuse_tile_map else 0, _stream(q)))
+    return dq, dkn, dkr, dv
 
 
 def _block_tensors(anchors: torch.Tensor, ctx_valid: Optional[torch.Tensor]):

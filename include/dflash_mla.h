@@ -194,6 +194,69 @@ dflash_status dflash_mla_attn(const void* q, const void* k_nope, const void* k_r
                               uint32_t flags, void* stream);
 
 /*
+ * dflash_mla_attn that also writes, for every (b, h, i), the natural-log row
+ * normaliser lse[b,h,i] = log(sum_j exp(s_j)) (f32, [B, H, Lq]; -inf for a row
+ * with no finite score), which the backward takes instead of recomputing the
+ * softmax statistics.  In the BF16 path the sum is that of the bf16-rounded
+ * probabilities the kernel uses for PV, so exp(s_j - lse) are the weights that
+ * produced out.  lse must be 4-byte aligned and overlap nothing else; other
+ * arguments, limits and errors as dflash_mla_attn.
+ */
+dflash_status dflash_mla_attn_lse(const void* q, const void* k_nope, const void* k_rope_shared,
+                                  const void* v, const void* additive_mask, void* out, float* lse,
+                                  int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                                  int64_t Dn, int64_t Dr, int64_t Dv, float scale,
+                                  dflash_dtype dt, dflash_dtype mask_dt,
+                                  void* workspace, size_t workspace_bytes, uint32_t flags,
+                                  void* stream);
+
+/*
+ * Bytes of device workspace dflash_mla_attn_bwd needs (0 for invalid sizes).  It
+ * begins with the forward's tile map in the dflash_mla_tile_map_layout layout,
+ * so one workspace of this size serves the forward (dflash_mla_attn_lse) and then
+ * the backward with DFLASH_ATTN_REUSE_TILE_MAP.
+ */
+size_t dflash_mla_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Lq, int64_t Lk);
+
+/*
+ * Gradients of dflash_mla_attn with respect to q, k_nope, k_rope_shared and v.
+ * The draft is trained (DFlash page, KimiK3DFlashDraftModel: the DFlash trainer;
+ * DSpark page, module text: speculative-decoding training).  With
+ * p_ij = exp(s_ij - lse_i) and D_i = sum_d dout[i,d] * out[i,d]:
+ *
+ *   ds_ij = p_ij * (dout_i . v_j - D_i)
+ *   dq_i = scale * sum_j ds_ij [k_nope_j | k_rope_j]    dv_j = sum_i p_ij dout_i
+ *   dk_nope_j = scale * sum_i ds_ij q_i[:Dn]
+ *   dk_rope_shared[b,j] = scale * sum_h sum_i ds_ij q_i[Dn:]   (summed over heads)
+ *
+ * Inputs (not modified): q, k_nope, k_rope_shared, v, additive_mask as in
+ * dflash_mla_attn; out [B,H,Lq,Dv] and lse [B,H,Lq] f32 as written by
+ * dflash_mla_attn_lse for the same inputs; dout [B,H,Lq,Dv] (gradient of out).
+ * Outputs (written): dq [B,H,Lq,Dn+Dr], dk_nope [B,H,Lk,Dn], dk_rope_shared
+ * [B,Lk,Dr], dv [B,H,Lk,Dv], all dtype dt.  Rows with lse = -inf (no visible
+ * key) pass no gradient; hidden entries (mask -inf) have p = 0.  The mask gets
+ * no gradient.
+ * Supported: dt = BF16 (F32 returns UNSUPPORTED), mask_dt F32 or BF16, Dn 128,
+ *   Dr 64, Dv 128, B * H <= 65535, at most 2^24 - 1 key tiles.  bf16 MFMA with
+ *   fp32 accumulation; p and ds are rounded to bf16 as MFMA operands; outputs
+ *   rounded to nearest even.  Deterministic: no atomics, dk_rope summed over
+ *   heads in head order.
+ * Workspace: at least dflash_mla_attn_bwd_workspace_bytes(B, H, Lq, Lk) bytes,
+ *   256-byte aligned, not overlapping any tensor.  flags: 0, or
+ *   DFLASH_ATTN_REUSE_TILE_MAP when the workspace already holds the tile map of
+ *   this mask (a forward call on the same workspace).
+ * Errors: INVALID_ARG (NULL or misaligned pointers, sizes <= 0, bad scale, unknown
+ *   flags, overlapping buffers), UNSUPPORTED, WORKSPACE, HIP.
+ */
+dflash_status dflash_mla_attn_bwd(const void* q, const void* k_nope, const void* k_rope_shared,
+                                  const void* v, const void* additive_mask, const void* out,
+                                  const void* dout, const float* lse, void* dq, void* dk_nope,
+                                  void* dk_rope_shared, void* dv, int64_t B, int64_t H, int64_t Lq,
+                                  int64_t Lk, int64_t Dn, int64_t Dr, int64_t Dv, float scale,
+                                  dflash_dtype dt, dflash_dtype mask_dt, void* workspace,
+                                  size_t workspace_bytes, uint32_t flags, void* stream);
+
+/*
  * The tile map of the DFlash block mask computed from the block structure itself
  * instead of a dense mask: no mask bytes are read.  Row b, query i belongs to
  * block j = i / block_size and sees context key k (k < ctx) iff
