@@ -43,9 +43,10 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="2", help="headline workload: 0,1,2,3a,3b,4")
-    p.add_argument("--secondary", default="4,1,3a,3b,2s,4s",
+    p.add_argument("--secondary", default="4,1,3a,3b,2s,4s,2b,4b",
                    help="comma list, or 'none'; a trailing 's' takes the mask from the block "
-                        "structure (anchors) instead of the dense tensor")
+                        "structure (anchors) instead of the dense tensor, a trailing 'b' times "
+                        "the backward")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -59,7 +60,7 @@ def parse():
 
 def make_workload(key: str):
     from dflash_block_draft_amd import workloads as W
-    key = key.rstrip("s")
+    key = key.rstrip("sb")
     if key == "3a":
         return W.config(3, block_size=8)
     if key == "3b":
@@ -170,6 +171,54 @@ def measure(wl, steps: int, warmup: int, structured: bool = False) -> dict:
     del q, kr, m, kn, v, ws, out, anchors, ctx_valid
     if expand:
         del lat, w
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure_bwd(wl, steps: int, warmup: int) -> dict:
+    """One step = the attention backward (prep, dK/dV, dQ, dk_rope reduction) given
+    out and lse from a forward on the same workspace (its tile map is reused)."""
+    import numpy as np
+    import torch
+    from dflash_block_draft_amd import mla
+    from dflash_block_draft_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    q, kn, kr, v, m = (t.to(dev) for t in (wl.q, wl.k_nope, wl.k_rope, wl.v, wl.mask))
+    dout = W.normal(np.random.default_rng(1000 + wl.seed), (wl.B, wl.H, wl.Lq, wl.Dv), 1.0, wl.dtype).to(dev)
+    ws = mla.new_bwd_workspace(wl.B, wl.H, wl.Lq, wl.Lk, dev)
+    lse = torch.empty((wl.B, wl.H, wl.Lq), dtype=torch.float32, device=dev)
+    out = mla.mla_attn(q, kn, kr, v, m, wl.scale, workspace=ws, lse=lse)
+    grads = (torch.empty_like(q), torch.empty_like(kn), torch.empty_like(kr), torch.empty_like(v))
+
+    def step():
+        mla.mla_attn_bwd(q, kn, kr, v, m, out, dout, lse, wl.scale, workspace=ws, reuse_tile_map=True,
+                         grads=grads)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    times = [a.elapsed_time(b) for a, b in evs]
+    ms = sum(times) / steps
+    pairs = W.visible_pairs(wl.mask)
+    flops = pairs * wl.H * (2 * (wl.Dn + wl.Dr) * 3 + 2 * wl.Dv * 2)   # QK^T, dQ, dK (192) + dP, dV (128)
+    res = {
+        "workload": wl.name,
+        "pass": "backward (dq, dk_nope, dk_rope, dv)",
+        "visible_gflop": round(flops / 1e9, 3),
+        "flop_basis": "visible pairs x heads x 1664 (QK^T, dP, dV, dK, dQ once each)",
+        "ms_per_step": round(ms, 4),
+        "ms_min": round(min(times), 4),
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        "pct_bf16_peak": round(100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+    }
+    del q, kn, kr, v, m, dout, ws, lse, out, grads
     torch.cuda.empty_cache()
     return res
 
@@ -304,7 +353,10 @@ def main():
             log(f"building workload {key}")
             w2 = make_workload(key)
             log(describe(w2))
-            r = measure(w2, max(3, args.steps // 2), max(1, args.warmup // 2), structured=key.endswith("s"))
+            if key.endswith("b"):
+                r = measure_bwd(w2, max(3, args.steps // 2), max(1, args.warmup // 2))
+            else:
+                r = measure(w2, max(3, args.steps // 2), max(1, args.warmup // 2), structured=key.endswith("s"))
             log(f"{key}: {r['ms_per_step']} ms/step, {r['tflops']} TFLOP/s ({r['pct_bf16_peak']}%)")
             secondary.append(r)
             del w2

@@ -191,3 +191,54 @@ def test_block_binding_rejects_bad_tensors():
     from dflash_block_draft_amd import mla
     with pytest.raises(ValueError):
         mla.block_occupancy(torch.zeros(1, 2, dtype=torch.int32), 16, 64)        # host tensor
+
+
+def _bwd(lib, **kw):
+    args = dict(q=FAKE, kn=FAKE * 2, kr=FAKE * 3, v=FAKE * 4, mask=None, out=FAKE * 5, dout=FAKE * 6,
+                lse=FAKE * 7, dq=FAKE * 8, dkn=FAKE * 9, dkr=FAKE * 10, dv=FAKE * 11, B=1, H=2, Lq=32, Lk=96,
+                Dn=128, Dr=64, Dv=128, scale=192 ** -0.5, dt=1, mdt=0, ws=FAKE * 256, wsb=1 << 24, flags=0)
+    args.update(kw)
+    k = ["q", "kn", "kr", "v", "mask", "out", "dout", "lse", "dq", "dkn", "dkr", "dv", "B", "H", "Lq", "Lk",
+         "Dn", "Dr", "Dv", "scale", "dt", "mdt", "ws", "wsb", "flags"]
+    return lib.dflash_mla_attn_bwd(*[args[n] for n in k], None)
+
+
+def test_bwd_workspace_bytes(lib):
+    assert lib.dflash_mla_attn_bwd_workspace_bytes(1, 2, 0, 96) == 0
+    assert lib.dflash_mla_attn_bwd_workspace_bytes(1, 0, 32, 96) == 0
+    n = lib.dflash_mla_attn_bwd_workspace_bytes(1, 64, 1024, 9216)
+    # tile map + lse2/D + q^T + dout^T (padded queries) + k_nope^T + k_rope^T + per-head rope parts
+    assert n >= lib.dflash_mla_attn_workspace_bytes(1, 1024, 9216) + 64 * 1024 * (8 + 2 * 320) \
+        + 64 * 9216 * 2 * 128 + 9216 * 2 * 64 + 64 * 9216 * 64 * 4
+
+
+# every case fails validation, so nothing is launched
+@pytest.mark.parametrize("kw,status", [
+    (dict(dout=None), 1),
+    (dict(lse=FAKE * 7 + 2), 1),              # lse misaligned
+    (dict(dq=FAKE * 8 + 8), 1),
+    (dict(Lq=0), 1),
+    (dict(scale=-1.0), 1),
+    (dict(flags=0x2), 1),                     # only REUSE_TILE_MAP is accepted
+    (dict(dt=0), 2),                          # f32 backward is not built
+    (dict(Dr=32), 2),
+    (dict(B=300, H=300), 2),                  # B * H beyond one grid dimension
+    (dict(ws=None, wsb=0), 3),
+    (dict(wsb=64), 3),
+    (dict(ws=FAKE * 256 + 16), 3),
+    (dict(dq=FAKE), 1),                       # dq aliases q
+    (dict(dv=FAKE * 10), 1),                  # dv aliases dk_rope
+    (dict(ws=FAKE * 2), 1),                   # workspace overlaps k_nope
+])
+def test_attn_bwd_validation(lib, kw, status):
+    assert _bwd(lib, **kw) == status
+    assert lib.dflash_last_error() != b""
+
+
+def test_attn_lse_validation(lib):
+    f = lib.dflash_mla_attn_lse
+    base = [FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None, FAKE * 5]
+    tail = [1, 2, 32, 96, 128, 64, 128, 192 ** -0.5, 1, 0, None, 0, 0, None]
+    assert f(*base, None, *tail) == 1                       # lse NULL
+    assert f(*base, FAKE * 5, *tail) == 1                   # lse overlaps out
+    assert f(*base, FAKE * 6 + 1, *tail) == 1               # misaligned
