@@ -35,6 +35,14 @@ What it computes, and the passages it follows:
   The draft is trained (DFlash page, KimiK3DFlashDraftModel class text: the
   DFlash trainer; DSpark page, module text: speculative-decoding training).
 
+* ``projection.context_project`` / ``q_project`` / ``kv_project`` / ``rms_norm``
+  -- the Linear + RMSNorm chains around the attention: fc and hidden_norm on the
+  target context, Q-LoRA (q_a_proj, q_a_layernorm, q_b_proj), and the keys and
+  values over [context | noise] (kv_a_proj_with_mqa, kv_a_layernorm on the
+  latent part, kv_b_proj).  DFlash page module text (Q-LoRA, compressed KV
+  latent, fp32-variance RMSNorm); DSpark page KimiK3DSparkAttention attributes
+  and forward, KimiK3DSparkModel._forward_backbone.
+
 Readings where the pages are silent (also listed in the design notes):
 a row whose every score is -inf returns 0; a mask entry is "masked" only if it
 is exactly -inf, any finite value (including large negatives) is added as is.
@@ -44,5 +52,6 @@ a library routine) -- nothing here is "parity unpinned".
 """
 from .attention import mla_attention, softmax_weights  # noqa: F401
 from .backward import logsumexp_rows, mla_attention_backward  # noqa: F401
+from .projection import context_project, kv_project, linear, q_project, rms_norm  # noqa: F401
 from .expand import latent_expand  # noqa: F401
 from .occupancy import tile_bits, tile_classes, tile_lists  # noqa: F401

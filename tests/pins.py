@@ -423,7 +423,95 @@ def pin_logsumexp_normalises_the_forward():
                 np.testing.assert_allclose(np.dot(p, v[b, h]), out[b, h, i], atol=1e-12)
 
 
+# ---------------------------------------------------------------- projections
+
+def _brute_rms(row, gamma, eps):
+    ms = sum(float(x) * float(x) for x in row) / len(row)
+    return [float(x) / math.sqrt(ms + eps) * float(g) for x, g in zip(row, gamma)]
+
+
+def pin_rms_norm():
+    """Constant rows, a pure-Python loop, and torch's rms_norm (fp64, CPU)."""
+    import torch
+    rng = np.random.default_rng(70)
+    g = rng.standard_normal(5)
+    for c in (2.0, -0.5):
+        out = oracle.rms_norm(np.full((1, 5), c), g, 0.25)
+        np.testing.assert_allclose(out, c / math.sqrt(c * c + 0.25) * g[None], atol=1e-14)
+    x = rng.standard_normal((3, 4, 7))
+    gam = rng.standard_normal(7)
+    out = oracle.rms_norm(x, gam, 0.3)
+    for i in range(3):
+        for j in range(4):
+            np.testing.assert_allclose(out[i, j], _brute_rms(x[i, j], gam, 0.3), atol=1e-13)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (7,), weight=torch.from_numpy(gam), eps=0.3)
+    np.testing.assert_allclose(out, ref.numpy(), atol=1e-13)
+
+
+def pin_context_project_brute_force():
+    rng = np.random.default_rng(71)
+    B, ctx, K, Hd = 2, 3, 5, 4
+    th = rng.standard_normal((B, ctx, K))
+    w = rng.standard_normal((Hd, K))
+    g = rng.standard_normal(Hd)
+    out = oracle.context_project(th, w, g, 0.2)
+    for b in range(B):
+        for t in range(ctx):
+            y = [sum(th[b, t, k] * w[n, k] for k in range(K)) for n in range(Hd)]
+            np.testing.assert_allclose(out[b, t], _brute_rms(y, g, 0.2), atol=1e-12)
+
+
+def pin_q_project_brute_force():
+    """Head-major output: q[b,h,t,d] uses row h*Dqk + d of q_b_proj."""
+    rng = np.random.default_rng(72)
+    B, L, Hd, Rq, H, Dqk = 2, 3, 5, 6, 2, 3
+    x = rng.standard_normal((B, L, Hd))
+    wa = rng.standard_normal((Rq, Hd))
+    ga = rng.standard_normal(Rq)
+    wb = rng.standard_normal((H * Dqk, Rq))
+    q = oracle.q_project(x, wa, ga, 0.1, wb, H)
+    assert q.shape == (B, H, L, Dqk)
+    for b in range(B):
+        for t in range(L):
+            qa = _brute_rms([sum(x[b, t, k] * wa[r, k] for k in range(Hd)) for r in range(Rq)], ga, 0.1)
+            for h in range(H):
+                for d in range(Dqk):
+                    want = sum(qa[r] * wb[h * Dqk + d, r] for r in range(Rq))
+                    assert abs(q[b, h, t, d] - want) < 1e-11, (b, h, t, d)
+
+
+def pin_kv_project_brute_force():
+    """Context rows first, then noise; latent = the first R outputs (normed),
+    k_rope = the last Dr (not normed); per head [k_nope | v] rows of kv_b_proj."""
+    rng = np.random.default_rng(73)
+    B, ctx, L, Hd, R, Dr, H, Dn, Dv = 2, 2, 3, 5, 4, 2, 2, 2, 3
+    ch = rng.standard_normal((B, ctx, Hd))
+    nh = rng.standard_normal((B, L, Hd))
+    wa = rng.standard_normal((R + Dr, Hd))
+    g = rng.standard_normal(R)
+    wb = rng.standard_normal((H * (Dn + Dv), R))
+    kn, kr, v = oracle.kv_project(ch, nh, wa, g, 0.15, wb, H, R, Dn, Dv)
+    assert kn.shape == (B, H, ctx + L, Dn) and kr.shape == (B, ctx + L, Dr) and v.shape == (B, H, ctx + L, Dv)
+    for b in range(B):
+        for t in range(ctx + L):
+            hrow = ch[b, t] if t < ctx else nh[b, t - ctx]
+            c = [sum(hrow[k] * wa[n, k] for k in range(Hd)) for n in range(R + Dr)]
+            np.testing.assert_allclose(kr[b, t], c[R:], atol=1e-12)
+            lat = _brute_rms(c[:R], g, 0.15)
+            for h in range(H):
+                for d in range(Dn):
+                    assert abs(kn[b, h, t, d] - sum(lat[r] * wb[h * (Dn + Dv) + d, r] for r in range(R))) < 1e-11
+                for d in range(Dv):
+                    assert abs(v[b, h, t, d] - sum(lat[r] * wb[h * (Dn + Dv) + Dn + d, r] for r in range(R))) < 1e-11
+    kn0, kr0, v0 = oracle.kv_project(None, nh, wa, g, 0.15, wb, H, R, Dn, Dv)
+    np.testing.assert_allclose(kn0, kn[:, :, ctx:], atol=1e-12)
+    np.testing.assert_allclose(kr0, kr[:, ctx:], atol=1e-12)
+
+
+PROJECTION_PINS = [pin_rms_norm, pin_context_project_brute_force, pin_q_project_brute_force,
+                   pin_kv_project_brute_force]
+
 BACKWARD_PINS = [pin_backward_finite_differences, pin_backward_matches_torch_autograd,
                  pin_backward_invariants, pin_logsumexp_normalises_the_forward]
 
-ALL_PINS = ATTENTION_PINS + EXPAND_PINS + OCCUPANCY_PINS + BACKWARD_PINS
+ALL_PINS = ATTENTION_PINS + EXPAND_PINS + OCCUPANCY_PINS + BACKWARD_PINS + PROJECTION_PINS

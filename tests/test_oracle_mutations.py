@@ -158,6 +158,56 @@ def _lse_log2(q, k_nope, k_rope, mask, scale):
     return _orig_lse(q, k_nope, k_rope, mask, scale) / math.log(2.0)
 
 
+from oracle import projection as oproj
+
+
+def _rms_no_eps(x, gamma, eps):
+    return _orig_rms(x, gamma, 0.0)
+
+
+def _rms_no_gamma(x, gamma, eps):
+    return _orig_rms(x, np.ones_like(f64(gamma)), eps)
+
+
+def _rms_mean_abs(x, gamma, eps):
+    x = f64(x)
+    return x / (np.abs(x).mean(axis=-1, keepdims=True) + eps) * f64(gamma)
+
+
+def _q_heads_inner(x, w_q_a, gamma_q, eps, w_q_b, H):
+    q = oproj.linear(oproj.rms_norm(oproj.linear(x, w_q_a), gamma_q, eps), w_q_b)
+    B, L, N = q.shape
+    return q.reshape(B, L, N // H, H).transpose(0, 3, 1, 2)
+
+
+def _kv_noise_first(ctx_hidden, noise_hidden, w_kv_a, gamma_kv, eps, w_kv_b, H, R, Dn=128, Dv=128):
+    if ctx_hidden is None:
+        return _orig_kv(None, noise_hidden, w_kv_a, gamma_kv, eps, w_kv_b, H, R, Dn, Dv)
+    h = np.concatenate([f64(noise_hidden), f64(ctx_hidden)], axis=1)
+    c = oproj.linear(h, w_kv_a)
+    kn, v = oracle.latent_expand(oproj.rms_norm(c[..., :R], gamma_kv, eps), w_kv_b, H, Dn, Dv)
+    return kn, c[..., R:], v
+
+
+def _kv_rope_first(ctx_hidden, noise_hidden, w_kv_a, gamma_kv, eps, w_kv_b, H, R, Dn=128, Dv=128):
+    h = f64(noise_hidden) if ctx_hidden is None else np.concatenate([f64(ctx_hidden), f64(noise_hidden)], axis=1)
+    c = oproj.linear(h, w_kv_a)
+    Dr = c.shape[-1] - R
+    kn, v = oracle.latent_expand(oproj.rms_norm(c[..., Dr:], gamma_kv, eps), w_kv_b, H, Dn, Dv)
+    return kn, c[..., :Dr], v
+
+
+def _kv_norm_whole(ctx_hidden, noise_hidden, w_kv_a, gamma_kv, eps, w_kv_b, H, R, Dn=128, Dv=128):
+    h = f64(noise_hidden) if ctx_hidden is None else np.concatenate([f64(ctx_hidden), f64(noise_hidden)], axis=1)
+    c = oproj.linear(h, w_kv_a)
+    Dr = c.shape[-1] - R
+    cn = oproj.rms_norm(c, np.concatenate([f64(gamma_kv), np.ones(Dr)]), eps)
+    kn, v = oracle.latent_expand(cn[..., :R], w_kv_b, H, Dn, Dv)
+    return kn, cn[..., R:], v
+
+
+_orig_rms = oproj.rms_norm
+_orig_kv = oracle.kv_project
 _orig_lse = oracle.logsumexp_rows
 _orig_attn = oracle.mla_attention
 _orig_classes = oracle.tile_classes
@@ -187,6 +237,13 @@ MUTANTS = {
     "backward_dk_unscaled": [(oracle, "mla_attention_backward", _bwd_variant("dk_unscaled"))],
     "backward_rope_last_head": [(oracle, "mla_attention_backward", _bwd_variant("rope_last_head"))],
     "lse_in_log2": [(oracle, "logsumexp_rows", _lse_log2)],
+    "rms_no_eps": [(oproj, "rms_norm", _rms_no_eps), (oracle, "rms_norm", _rms_no_eps)],
+    "rms_no_gamma": [(oproj, "rms_norm", _rms_no_gamma), (oracle, "rms_norm", _rms_no_gamma)],
+    "rms_mean_abs": [(oproj, "rms_norm", _rms_mean_abs), (oracle, "rms_norm", _rms_mean_abs)],
+    "q_heads_inner": [(oracle, "q_project", _q_heads_inner)],
+    "kv_noise_first": [(oracle, "kv_project", _kv_noise_first)],
+    "kv_rope_first": [(oracle, "kv_project", _kv_rope_first)],
+    "kv_norm_whole_row": [(oracle, "kv_project", _kv_norm_whole)],
 }
 
 
