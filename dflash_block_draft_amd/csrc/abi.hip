@@ -240,7 +240,7 @@ dflash_status dflash_mla_latent_expand(const void* latent, const void* w_kv_b, v
   const Range rv = range_of(v, static_cast<size_t>(M) * H * 128 * es);
   if (overlaps(rk, rv) || overlaps(rk, rl) || overlaps(rk, rw) || overlaps(rv, rl) || overlaps(rv, rw))
     return fail(DFLASH_ERR_INVALID_ARG, "outputs overlap each other or an input");
-  dflash::ExpandArgs a;
+  dflash::ExpandArgs a = {};
   a.latent = latent;
   a.w = w_kv_b;
   a.kn = k_nope;
@@ -522,6 +522,216 @@ dflash_status dflash_mla_attn_bwd(const void* q, const void* k_nope, const void*
   a.Lkp = static_cast<int>(L.Lkp);
   a.scale = scale;
   return hip_status(dflash::launch_attn_bwd_bf16(a, s), "attention backward launch");
+}
+
+// ---------------------------------------------------------------- projections
+
+size_t dflash_mla_projection_workspace_bytes(int64_t rows, int64_t width) {
+  int64_t e, st;
+  if (rows <= 0 || width <= 0 || !mul_ok(rows, width, &e) || !mul_ok(rows, (width + 127) / 128, &st)) return 0;
+  return align_up(static_cast<size_t>(e) * 2, 256) + align_up(static_cast<size_t>(st) * 4, 256);
+}
+
+}  // extern "C"
+
+namespace {
+
+dflash_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (!ws) return fail(DFLASH_ERR_WORKSPACE, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(DFLASH_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (ws_bytes < need) return fail(DFLASH_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  return ok();
+}
+
+bool any_overlap(const Range* r, int n) {
+  for (int i = 0; i < n; ++i)
+    for (int j = i + 1; j < n; ++j)
+      if (overlaps(r[i], r[j])) return true;
+  return false;
+}
+
+dflash::LinearArgs linear_args() {
+  dflash::LinearArgs l = {};
+  l.mode = dflash::kLinearPlain;
+  return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+dflash_status dflash_mla_context_project(const void* target_hidden, const void* w_fc, const void* gamma, float eps,
+                                         void* out, int64_t B, int64_t ctx, int64_t K_in, int64_t hidden,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!target_hidden || !w_fc || !gamma || !out) return fail(DFLASH_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!aligned16(target_hidden) || !aligned16(w_fc) || !aligned16(gamma) || !aligned16(out))
+    return fail(DFLASH_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (B <= 0 || ctx <= 0 || K_in <= 0 || hidden <= 0) return fail(DFLASH_ERR_INVALID_ARG, "sizes must be positive");
+  if (!std::isfinite(eps) || eps < 0.f) return fail(DFLASH_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (K_in % 32 != 0 || hidden % 128 != 0)
+    return fail(DFLASH_ERR_UNSUPPORTED, "K_in must be a multiple of 32 and hidden of 128");
+  int64_t M, tmp;
+  if (!mul_ok(B, ctx, &M) || M > INT32_MAX || K_in > INT32_MAX || hidden > INT32_MAX || !mul_ok(M, K_in, &tmp) ||
+      !mul_ok(hidden, K_in, &tmp) || (M + 127) / 128 > INT32_MAX)
+    return fail(DFLASH_ERR_UNSUPPORTED, "sizes too large");
+  const size_t need = dflash_mla_projection_workspace_bytes(M, hidden);
+  dflash_status st = check_ws(workspace, workspace_bytes, need);
+  if (st != DFLASH_OK) return st;
+  const Range r[4] = {range_of(out, static_cast<size_t>(M) * hidden * 2), range_of(target_hidden, static_cast<size_t>(M) * K_in * 2),
+                      range_of(w_fc, static_cast<size_t>(hidden) * K_in * 2), range_of(workspace, need)};
+  const Range g = range_of(gamma, static_cast<size_t>(hidden) * 2);
+  if (any_overlap(r, 4) || overlaps(r[0], g) || overlaps(r[3], g))
+    return fail(DFLASH_ERR_INVALID_ARG, "out / workspace overlap an input or each other");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* stats = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(static_cast<size_t>(M) * hidden * 2, 256));
+  dflash::LinearArgs l = linear_args();
+  l.a1 = static_cast<const uint16_t*>(target_hidden);
+  l.B = static_cast<int>(B);
+  l.T1 = static_cast<int>(ctx);
+  l.K = static_cast<int>(K_in);
+  l.w = static_cast<const uint16_t*>(w_fc);
+  l.N = static_cast<int>(hidden);
+  l.y1 = static_cast<uint16_t*>(out);
+  l.stats_out = stats;
+  l.Nstat = static_cast<int>(hidden);
+  st = hip_status(dflash::launch_linear_bf16(l, s), "fc launch");
+  if (st != DFLASH_OK) return st;
+  dflash::RmsApplyArgs n = {};
+  n.x = static_cast<const uint16_t*>(out);
+  n.y = static_cast<uint16_t*>(out);
+  n.M = M;
+  n.N = static_cast<int>(hidden);
+  n.stats = stats;
+  n.parts = static_cast<int>(hidden / 128);
+  n.gamma = static_cast<const uint16_t*>(gamma);
+  n.eps = eps;
+  return hip_status(dflash::launch_rms_apply_bf16(n, s), "hidden_norm launch");
+}
+
+dflash_status dflash_mla_q_project(const void* x, const void* w_q_a, const void* gamma_q, float eps, const void* w_q_b,
+                                   void* q, int64_t B, int64_t Lq, int64_t hidden, int64_t q_lora_rank, int64_t H,
+                                   int64_t Dqk, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !w_q_a || !gamma_q || !w_q_b || !q) return fail(DFLASH_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!aligned16(x) || !aligned16(w_q_a) || !aligned16(gamma_q) || !aligned16(w_q_b) || !aligned16(q))
+    return fail(DFLASH_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (B <= 0 || Lq <= 0 || hidden <= 0 || q_lora_rank <= 0 || H <= 0 || Dqk <= 0)
+    return fail(DFLASH_ERR_INVALID_ARG, "sizes must be positive");
+  if (!std::isfinite(eps) || eps < 0.f) return fail(DFLASH_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (hidden % 32 != 0 || q_lora_rank % 128 != 0 || Dqk % 4 != 0)
+    return fail(DFLASH_ERR_UNSUPPORTED, "hidden must be a multiple of 32, q_lora_rank of 128, Dqk of 4");
+  int64_t M, N, tmp;
+  if (!mul_ok(B, Lq, &M) || M > INT32_MAX || !mul_ok(H, Dqk, &N) || N > INT32_MAX || hidden > INT32_MAX ||
+      q_lora_rank > INT32_MAX || !mul_ok(M, hidden, &tmp) || !mul_ok(N, q_lora_rank, &tmp) || !mul_ok(M, N, &tmp) ||
+      !mul_ok(q_lora_rank, hidden, &tmp))
+    return fail(DFLASH_ERR_UNSUPPORTED, "sizes too large");
+  const size_t need = dflash_mla_projection_workspace_bytes(M, q_lora_rank);
+  dflash_status st = check_ws(workspace, workspace_bytes, need);
+  if (st != DFLASH_OK) return st;
+  const Range r[6] = {range_of(q, static_cast<size_t>(M) * N * 2), range_of(workspace, need),
+                      range_of(x, static_cast<size_t>(M) * hidden * 2), range_of(w_q_a, static_cast<size_t>(q_lora_rank) * hidden * 2),
+                      range_of(w_q_b, static_cast<size_t>(N) * q_lora_rank * 2), range_of(gamma_q, static_cast<size_t>(q_lora_rank) * 2)};
+  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 6; ++j)
+      if (i != j && overlaps(r[i], r[j])) return fail(DFLASH_ERR_INVALID_ARG, "q / workspace overlap another buffer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* qa = static_cast<uint16_t*>(workspace);
+  float* stats = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(static_cast<size_t>(M) * q_lora_rank * 2, 256));
+  dflash::LinearArgs l = linear_args();
+  l.a1 = static_cast<const uint16_t*>(x);
+  l.B = static_cast<int>(B);
+  l.T1 = static_cast<int>(Lq);
+  l.K = static_cast<int>(hidden);
+  l.w = static_cast<const uint16_t*>(w_q_a);
+  l.N = static_cast<int>(q_lora_rank);
+  l.y1 = qa;
+  l.stats_out = stats;
+  l.Nstat = static_cast<int>(q_lora_rank);
+  st = hip_status(dflash::launch_linear_bf16(l, s), "q_a_proj launch");
+  if (st != DFLASH_OK) return st;
+  dflash::LinearArgs l2 = linear_args();
+  l2.a1 = qa;
+  l2.B = static_cast<int>(B);
+  l2.T1 = static_cast<int>(Lq);
+  l2.K = static_cast<int>(q_lora_rank);
+  l2.w = static_cast<const uint16_t*>(w_q_b);
+  l2.N = static_cast<int>(N);
+  l2.stats_in = stats;
+  l2.stats_parts = static_cast<int>(q_lora_rank / 128);
+  l2.gamma = static_cast<const uint16_t*>(gamma_q);
+  l2.eps = eps;
+  l2.mode = dflash::kLinearHeads;
+  l2.y1 = static_cast<uint16_t*>(q);
+  l2.D = static_cast<int>(Dqk);
+  return hip_status(dflash::launch_linear_bf16(l2, s), "q_b_proj launch");
+}
+
+dflash_status dflash_mla_kv_project(const void* ctx_hidden, const void* noise_hidden, const void* w_kv_a,
+                                    const void* gamma_kv, float eps, const void* w_kv_b, void* k_nope,
+                                    void* k_rope_shared, void* v, int64_t B, int64_t ctx, int64_t Lq, int64_t hidden,
+                                    int64_t R, int64_t Dr, int64_t H, int64_t Dn, int64_t Dv, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if ((ctx > 0 && !ctx_hidden) || !noise_hidden || !w_kv_a || !gamma_kv || !w_kv_b || !k_nope || !k_rope_shared || !v)
+    return fail(DFLASH_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if ((ctx > 0 && !aligned16(ctx_hidden)) || !aligned16(noise_hidden) || !aligned16(w_kv_a) || !aligned16(gamma_kv) ||
+      !aligned16(w_kv_b) || !aligned16(k_nope) || !aligned16(k_rope_shared) || !aligned16(v))
+    return fail(DFLASH_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (B <= 0 || ctx < 0 || Lq <= 0 || hidden <= 0 || R <= 0 || Dr <= 0 || H <= 0 || Dn <= 0 || Dv <= 0)
+    return fail(DFLASH_ERR_INVALID_ARG, "sizes must be positive (ctx >= 0)");
+  if (!std::isfinite(eps) || eps < 0.f) return fail(DFLASH_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (Dn != dflash::kDn || Dv != dflash::kDv) return fail(DFLASH_ERR_UNSUPPORTED, "only Dn = Dv = 128 are built");
+  if (hidden % 32 != 0 || R % 128 != 0 || Dr % 4 != 0)
+    return fail(DFLASH_ERR_UNSUPPORTED, "hidden must be a multiple of 32, R of 128, Dr of 4");
+  int64_t M, tmp;
+  const int64_t Lk = ctx + Lq;
+  if (!mul_ok(B, Lk, &M) || M > INT32_MAX || hidden > INT32_MAX || R + Dr > INT32_MAX || H > 16384 ||
+      !mul_ok(M, hidden, &tmp) || !mul_ok(M, R + Dr, &tmp) || !mul_ok(M * H, 256, &tmp) || !mul_ok(R + Dr, hidden, &tmp))
+    return fail(DFLASH_ERR_UNSUPPORTED, "sizes too large");
+  const size_t need = dflash_mla_projection_workspace_bytes(M, R);
+  dflash_status st = check_ws(workspace, workspace_bytes, need);
+  if (st != DFLASH_OK) return st;
+  const Range r[10] = {range_of(k_nope, static_cast<size_t>(M) * H * Dn * 2), range_of(v, static_cast<size_t>(M) * H * Dv * 2),
+                       range_of(k_rope_shared, static_cast<size_t>(M) * Dr * 2), range_of(workspace, need),
+                       ctx > 0 ? range_of(ctx_hidden, static_cast<size_t>(B) * ctx * hidden * 2) : Range{0, 0},
+                       range_of(noise_hidden, static_cast<size_t>(B) * Lq * hidden * 2),
+                       range_of(w_kv_a, static_cast<size_t>(R + Dr) * hidden * 2), range_of(gamma_kv, static_cast<size_t>(R) * 2),
+                       range_of(w_kv_b, static_cast<size_t>(H) * (Dn + Dv) * R * 2), Range{0, 0}};
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 10; ++j)
+      if (i != j && overlaps(r[i], r[j])) return fail(DFLASH_ERR_INVALID_ARG, "an output or the workspace overlaps another buffer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* latent = static_cast<uint16_t*>(workspace);
+  float* stats = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(static_cast<size_t>(M) * R * 2, 256));
+  dflash::LinearArgs l = linear_args();
+  l.a1 = static_cast<const uint16_t*>(ctx_hidden);
+  l.a2 = static_cast<const uint16_t*>(noise_hidden);
+  l.B = static_cast<int>(B);
+  l.T1 = static_cast<int>(ctx);
+  l.T2 = static_cast<int>(Lq);
+  l.K = static_cast<int>(hidden);
+  l.w = static_cast<const uint16_t*>(w_kv_a);
+  l.N = static_cast<int>(R + Dr);
+  l.mode = dflash::kLinearSplit;
+  l.y1 = latent;
+  l.y2 = static_cast<uint16_t*>(k_rope_shared);
+  l.N1 = static_cast<int>(R);
+  l.stats_out = stats;
+  l.Nstat = static_cast<int>(R);
+  st = hip_status(dflash::launch_linear_bf16(l, s), "kv_a_proj_with_mqa launch");
+  if (st != DFLASH_OK) return st;
+  dflash::ExpandArgs e = {};
+  e.latent = latent;
+  e.w = w_kv_b;
+  e.kn = k_nope;
+  e.v = v;
+  e.B = static_cast<int>(B);
+  e.Lk = static_cast<int>(Lk);
+  e.R = static_cast<int>(R);
+  e.H = static_cast<int>(H);
+  e.stats = stats;
+  e.stats_parts = static_cast<int>(R / 128);
+  e.gamma = static_cast<const uint16_t*>(gamma_kv);
+  e.eps = eps;
+  return hip_status(dflash::launch_expand_bf16(e, s), "kv_b_proj launch");
 }
 
 dflash_status dflash_mla_block_occupancy(const int32_t* anchors, const int32_t* ctx_valid, int64_t B, int64_t A,

@@ -14,6 +14,7 @@
 // free.
 #include "common.h"
 #include "launch.h"
+#include "rmsnorm.h"
 
 namespace dflash {
 namespace {
@@ -36,6 +37,15 @@ __global__ void __launch_bounds__(256) expand_bf16(ExpandArgs a) {
   const uint16_t* W = static_cast<const uint16_t*>(a.w) + (static_cast<size_t>(h) * 256 + part * 128) * a.R;
   const uint16_t* L = static_cast<const uint16_t*>(a.latent);
 
+  // optional RMSNorm of the latent rows (kv_a_layernorm) applied as they are staged
+  float rsc[2] = {1.f, 1.f};
+  if (a.stats) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int64_t m = m0 + ((t + 256 * i) >> 2);
+      if (m < M) rsc[i] = rms_row_scale(a.stats, a.stats_parts, m, a.R, a.eps);
+    }
+  }
   u32x4_t sw[2], sl[2];
   auto load = [&](int k0) {
 #pragma unroll
@@ -45,6 +55,7 @@ __global__ void __launch_bounds__(256) expand_bf16(ExpandArgs a) {
       const int64_t m = m0 + row;
       const u32x4_t z = {0u, 0u, 0u, 0u};
       sl[i] = m < M ? ldg16(L + static_cast<size_t>(m) * a.R + k0 + c * 8) : z;
+      if (a.stats && m < M) sl[i] = rms_norm_chunk(sl[i], rsc[i], ldg16(a.gamma + k0 + c * 8));
     }
   };
   auto store = [&](uint16_t* buf) {

@@ -74,8 +74,38 @@ struct ExpandArgs {
   const void* latent; const void* w;  // [B,Lk,R], [H*256,R]
   void* kn; void* v;                  // [B,H,Lk,128] each
   int B, Lk, R, H;
+  // optional RMSNorm of the latent rows on load (bf16 only): partial sums of
+  // squares [B*Lk, stats_parts] from the producing projection, weight [R]
+  const float* stats; int stats_parts; const uint16_t* gamma; float eps;
 };
 
+// Linear layer y = a W^T (bf16, fp32 accumulation) for the projections around
+// the attention.  Rows m = b * (T1 + T2) + t come from a1[b, t] (t < T1) or
+// a2[b, t - T1]; both [.., K] row-major.  Optional RMSNorm of the rows on load
+// (stats_in: per-row partial sums of squares of the producer's bf16 outputs,
+// stats_parts per row, over K entries; gamma [K]).  Optional statistics out:
+// per-row partial sums of squares of the bf16 outputs over each 128-column tile
+// of columns [0, Nstat), stats_out [M, Nstat / 128].
+constexpr int kLinearPlain = 0;   // y1 [M, N]
+constexpr int kLinearSplit = 1;   // y1 [M, N1] (columns < N1), y2 [M, N - N1]
+constexpr int kLinearHeads = 2;   // y1 [B, N / D, T1 + T2, D]
+struct LinearArgs {
+  const uint16_t* a1; const uint16_t* a2;
+  int B, T1, T2, K;
+  const uint16_t* w; int N;
+  const float* stats_in; int stats_parts; const uint16_t* gamma; float eps;
+  int mode; uint16_t* y1; uint16_t* y2; int N1; int D;
+  float* stats_out; int Nstat;
+};
+
+// y = RMSNorm(x) with statistics from the producer: y[m] = bf16(bf16(x[m] * r_m) * gamma).
+struct RmsApplyArgs {
+  const uint16_t* x; uint16_t* y; int64_t M; int N;
+  const float* stats; int parts; const uint16_t* gamma; float eps;
+};
+
+hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t s);
+hipError_t launch_rms_apply_bf16(const RmsApplyArgs& a, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnBf16Args& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnF32Args& a, hipStream_t s);
 hipError_t launch_occupancy(const OccupancyArgs& a, hipStream_t s);

@@ -31,7 +31,8 @@ EXPORTED = (
     "dflash_mla_attn_workspace_bytes", "dflash_mla_tile_map_layout",
     "dflash_mla_mask_occupancy", "dflash_mla_attn", "dflash_mla_block_occupancy",
     "dflash_mla_attn_blocks", "dflash_mla_attn_lse", "dflash_mla_attn_bwd_workspace_bytes",
-    "dflash_mla_attn_bwd",
+    "dflash_mla_attn_bwd", "dflash_mla_projection_workspace_bytes", "dflash_mla_context_project",
+    "dflash_mla_q_project", "dflash_mla_kv_project",
 )
 
 
@@ -82,6 +83,15 @@ def load_library() -> ctypes.CDLL:
     lib.dflash_mla_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                         i64, i64, i64, f32, i32, i32, vp, sz, u32, vp]
     lib.dflash_mla_attn_bwd.restype = i32
+    lib.dflash_mla_projection_workspace_bytes.argtypes = [i64, i64]
+    lib.dflash_mla_projection_workspace_bytes.restype = sz
+    lib.dflash_mla_context_project.argtypes = [vp, vp, vp, f32, vp, i64, i64, i64, i64, vp, sz, vp]
+    lib.dflash_mla_context_project.restype = i32
+    lib.dflash_mla_q_project.argtypes = [vp, vp, vp, f32, vp, vp, i64, i64, i64, i64, i64, i64, vp, sz, vp]
+    lib.dflash_mla_q_project.restype = i32
+    lib.dflash_mla_kv_project.argtypes = [vp, vp, vp, vp, f32, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
+                                          i64, i64, vp, sz, vp]
+    lib.dflash_mla_kv_project.restype = i32
     lib.dflash_mla_block_occupancy.argtypes = [vp, vp, i64, i64, i64, i64, vp, sz, vp]
     lib.dflash_mla_block_occupancy.restype = i32
     lib.dflash_mla_attn_blocks.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64,
@@ -356,3 +366,88 @@ def mla_attn_blocks(q: torch.Tensor, k_nope: torch.Tensor, k_rope: torch.Tensor,
                                       _BF16, _ptr(workspace), workspace.numel(),
                                       FLAG_REUSE_TILE_MAP if reuse_tile_map else 0, _stream(q)))
     return out
+
+
+def _proj_ws(rows: int, width: int, device, workspace):
+    n = int(load_library().dflash_mla_projection_workspace_bytes(rows, width))
+    if n == 0:
+        raise ValueError("invalid projection sizes")
+    if workspace is None:
+        workspace = torch.empty(n, dtype=torch.uint8, device=device)
+    _dev(workspace, "workspace", dtype=torch.uint8)
+    return workspace
+
+
+def context_project(target_hidden: torch.Tensor, w_fc: torch.Tensor, gamma: torch.Tensor, eps: float, *,
+                    out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """rmsnorm(target_hidden @ w_fc^T) * gamma: [B, ctx, K_in] -> [B, ctx, hidden] (bf16)."""
+    lib = load_library()
+    _dev(target_hidden, "target_hidden", dtype=torch.bfloat16, ndim=3)
+    _dev(w_fc, "w_fc", dtype=torch.bfloat16, ndim=2)
+    _dev(gamma, "gamma", dtype=torch.bfloat16, ndim=1)
+    B, ctx, K_in = target_hidden.shape
+    hidden = w_fc.shape[0]
+    if w_fc.shape[1] != K_in or gamma.shape[0] != hidden:
+        raise ValueError("w_fc must be [hidden, K_in] and gamma [hidden]")
+    if out is None:
+        out = torch.empty((B, ctx, hidden), dtype=torch.bfloat16, device=target_hidden.device)
+    _dev(out, "out", dtype=torch.bfloat16, ndim=3)
+    workspace = _proj_ws(B * ctx, hidden, target_hidden.device, workspace)
+    _check(lib.dflash_mla_context_project(_ptr(target_hidden), _ptr(w_fc), _ptr(gamma), float(eps), _ptr(out),
+                                          B, ctx, K_in, hidden, _ptr(workspace), workspace.numel(),
+                                          _stream(target_hidden)))
+    return out
+
+
+def q_project(x: torch.Tensor, w_q_a: torch.Tensor, gamma_q: torch.Tensor, eps: float, w_q_b: torch.Tensor,
+              H: int, *, out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Q-LoRA: (rmsnorm(x @ w_q_a^T) * gamma_q) @ w_q_b^T, as [B, H, Lq, Dqk] (bf16)."""
+    lib = load_library()
+    _dev(x, "x", dtype=torch.bfloat16, ndim=3)
+    for t, n in ((w_q_a, "w_q_a"), (w_q_b, "w_q_b")):
+        _dev(t, n, dtype=torch.bfloat16, ndim=2)
+    _dev(gamma_q, "gamma_q", dtype=torch.bfloat16, ndim=1)
+    B, Lq, hidden = x.shape
+    Rq = w_q_a.shape[0]
+    if w_q_a.shape[1] != hidden or gamma_q.shape[0] != Rq or w_q_b.shape[1] != Rq or w_q_b.shape[0] % H:
+        raise ValueError("inconsistent Q-LoRA shapes")
+    Dqk = w_q_b.shape[0] // H
+    if out is None:
+        out = torch.empty((B, H, Lq, Dqk), dtype=torch.bfloat16, device=x.device)
+    _dev(out, "out", dtype=torch.bfloat16, ndim=4)
+    workspace = _proj_ws(B * Lq, Rq, x.device, workspace)
+    _check(lib.dflash_mla_q_project(_ptr(x), _ptr(w_q_a), _ptr(gamma_q), float(eps), _ptr(w_q_b), _ptr(out),
+                                    B, Lq, hidden, Rq, H, Dqk, _ptr(workspace), workspace.numel(), _stream(x)))
+    return out
+
+
+def kv_project(ctx_hidden: Optional[torch.Tensor], noise_hidden: torch.Tensor, w_kv_a: torch.Tensor,
+               gamma_kv: torch.Tensor, eps: float, w_kv_b: torch.Tensor, H: int, R: int, *,
+               workspace: Optional[torch.Tensor] = None):
+    """Keys and values over [context | noise]: returns (k_nope [B,H,Lk,128],
+    k_rope_shared [B,Lk,Dr], v [B,H,Lk,128]) with Lk = ctx + Lq (bf16)."""
+    lib = load_library()
+    _dev(noise_hidden, "noise_hidden", dtype=torch.bfloat16, ndim=3)
+    B, Lq, hidden = noise_hidden.shape
+    ctx = 0
+    if ctx_hidden is not None:
+        _dev(ctx_hidden, "ctx_hidden", dtype=torch.bfloat16, ndim=3)
+        if ctx_hidden.shape[0] != B or ctx_hidden.shape[2] != hidden:
+            raise ValueError("ctx_hidden must be [B, ctx, hidden]")
+        ctx = ctx_hidden.shape[1]
+    for t, n in ((w_kv_a, "w_kv_a"), (w_kv_b, "w_kv_b")):
+        _dev(t, n, dtype=torch.bfloat16, ndim=2)
+    _dev(gamma_kv, "gamma_kv", dtype=torch.bfloat16, ndim=1)
+    Dr = w_kv_a.shape[0] - R
+    if w_kv_a.shape[1] != hidden or Dr <= 0 or gamma_kv.shape[0] != R or tuple(w_kv_b.shape) != (H * 256, R):
+        raise ValueError("inconsistent kv projection shapes")
+    Lk = ctx + Lq
+    dev = noise_hidden.device
+    kn = torch.empty((B, H, Lk, 128), dtype=torch.bfloat16, device=dev)
+    v = torch.empty((B, H, Lk, 128), dtype=torch.bfloat16, device=dev)
+    kr = torch.empty((B, Lk, Dr), dtype=torch.bfloat16, device=dev)
+    workspace = _proj_ws(B * Lk, R, dev, workspace)
+    _check(lib.dflash_mla_kv_project(_ptr(ctx_hidden), _ptr(noise_hidden), _ptr(w_kv_a), _ptr(gamma_kv), float(eps),
+                                     _ptr(w_kv_b), _ptr(kn), _ptr(kr), _ptr(v), B, ctx, Lq, hidden, R, Dr, H, 128, 128,
+                                     _ptr(workspace), workspace.numel(), _stream(noise_hidden)))
+    return kn, kr, v

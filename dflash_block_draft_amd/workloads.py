@@ -206,3 +206,40 @@ def visible_flops(mask: Optional[torch.Tensor], B: int, H: int, Lq: int, Lk: int
     """Visible FLOPs: finite-mask (query, key) pairs x heads x (2*Dqk + 2*Dv)."""
     pairs = B * Lq * Lk if mask is None else visible_pairs(mask)
     return pairs * H * (2 * Dqk + 2 * Dv)
+
+
+# --------------------------------------------------------------------------
+# projections around the attention (fc + hidden_norm, Q-LoRA, kv_a + kv_b)
+# --------------------------------------------------------------------------
+
+# Sizes for the full-size projection workload.  The pages give kv_lora_rank 512
+# (the expand workload), qk_rope 64, qk_nope 128, v 128; the hidden size, the
+# Q-LoRA rank and the number of target layers feeding fc are not stated, so
+# they take the values of the Kimi/DeepSeek-V3 MLA family the draft inherits
+# (hidden 7168, q_lora_rank 1536) and four target layers.
+PROJ_HIDDEN = 7168
+PROJ_Q_LORA = 1536
+PROJ_TARGET_LAYERS = 4
+RMS_EPS = 1e-6
+
+
+def projection_inputs(seed: int, B: int, ctx: int, Lq: int, H: int, hidden: int = PROJ_HIDDEN,
+                      q_lora_rank: int = PROJ_Q_LORA, R: int = R_LATENT, Dr: int = DR,
+                      n_target_layers: int = PROJ_TARGET_LAYERS) -> dict:
+    """Hidden states N(0,1); Linear weights N(0, 0.02^2); RMSNorm weights 1 + N(0, 0.1^2); all bf16."""
+    rng = np.random.default_rng(seed)
+    return {
+        "target_hidden": normal(rng, (B, ctx, n_target_layers * hidden), 1.0, "bf16"),
+        "w_fc": normal(rng, (hidden, n_target_layers * hidden), 0.02, "bf16"),
+        "g_hidden": (1.0 + normal(rng, (hidden,), 0.1, "f32")).to(torch.bfloat16),
+        "ctx_hidden": normal(rng, (B, ctx, hidden), 1.0, "bf16"),
+        "noise_hidden": normal(rng, (B, Lq, hidden), 1.0, "bf16"),
+        "w_q_a": normal(rng, (q_lora_rank, hidden), 0.02, "bf16"),
+        "g_q": (1.0 + normal(rng, (q_lora_rank,), 0.1, "f32")).to(torch.bfloat16),
+        "w_q_b": normal(rng, (H * (DN + DR), q_lora_rank), 0.02, "bf16"),
+        "w_kv_a": normal(rng, (R + Dr, hidden), 0.02, "bf16"),
+        "g_kv": (1.0 + normal(rng, (R,), 0.1, "f32")).to(torch.bfloat16),
+        "w_kv_b": normal(rng, (H * (DN + DV), R), 0.02, "bf16"),
+        "B": B, "ctx": ctx, "Lq": Lq, "H": H, "hidden": hidden, "q_lora_rank": q_lora_rank, "R": R, "Dr": Dr,
+        "eps": RMS_EPS,
+    }

@@ -257,6 +257,64 @@ dflash_status dflash_mla_attn_bwd(const void* q, const void* k_nope, const void*
                                   size_t workspace_bytes, uint32_t flags, void* stream);
 
 /*
+ * ---- Projections on either side of the attention (bf16 only) ----
+ *
+ * The draft's MLA uses Q-LoRA and a compressed KV latent with fp32-variance
+ * RMSNorms (DFlash page, module text; DSpark page, KimiK3DSparkAttention
+ * attributes q_a_proj, q_a_layernorm, q_b_proj, kv_a_proj_with_mqa,
+ * kv_a_layernorm, kv_b_proj), and the target context is projected by fc and
+ * normed once per step (DSpark page, KimiK3DSparkModel._forward_backbone).
+ * Linear weights are [out, in] row-major (PyTorch Linear).  RMSNorm:
+ *   rmsnorm(x)[k] = bf16( bf16(x[k] * rsqrt(mean_j(x[j]^2) + eps)) * gamma[k] ),
+ * with the mean over the row in fp32 of the bf16 values.  Matrix products run as
+ * bf16 MFMA with fp32 accumulation and round their outputs to bf16.  The norms
+ * are fused: the producing product writes per-row partial sums of squares, and
+ * the consuming product normalises its operand rows as it loads them.
+ * All tensors are contiguous device memory, 16-byte aligned; outputs and the
+ * workspace must not overlap any other buffer.  Errors: INVALID_ARG (NULL or
+ * misaligned pointers, sizes <= 0, eps < 0 or not finite, overlaps),
+ * UNSUPPORTED (divisibility below, sizes beyond int32), WORKSPACE, HIP.
+ */
+
+/* Workspace for one projection chain: an intermediate of [rows, width] bf16 plus
+ * its row statistics.  context_project: (B*ctx, hidden); q_project:
+ * (B*Lq, q_lora_rank); kv_project: (B*(ctx+Lq), R).  0 for invalid sizes. */
+size_t dflash_mla_projection_workspace_bytes(int64_t rows, int64_t width);
+
+/* out[b,t,:] = rmsnorm(target_hidden[b,t,:] . w_fc^T) with weight gamma [hidden]:
+ * target_hidden [B, ctx, K_in], w_fc [hidden, K_in], out [B, ctx, hidden].
+ * K_in a multiple of 32, hidden a multiple of 128. */
+dflash_status dflash_mla_context_project(const void* target_hidden, const void* w_fc, const void* gamma,
+                                         float eps, void* out, int64_t B, int64_t ctx, int64_t K_in,
+                                         int64_t hidden, void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
+/* q[b,h,t,:] = (rmsnorm(x[b,t,:] . w_q_a^T) . w_q_b^T)[h*Dqk : (h+1)*Dqk]:
+ * x [B, Lq, hidden], w_q_a [q_lora_rank, hidden], gamma_q [q_lora_rank],
+ * w_q_b [H*Dqk, q_lora_rank], q [B, H, Lq, Dqk] (the layout dflash_mla_attn
+ * takes; within a head, q_nope then q_rope).  hidden a multiple of 32,
+ * q_lora_rank of 128, Dqk of 4. */
+dflash_status dflash_mla_q_project(const void* x, const void* w_q_a, const void* gamma_q, float eps,
+                                   const void* w_q_b, void* q, int64_t B, int64_t Lq, int64_t hidden,
+                                   int64_t q_lora_rank, int64_t H, int64_t Dqk, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* Keys and values of the draft attention over [context | noise]:
+ *   h = [ctx_hidden[b] ; noise_hidden[b]]         ([ctx + Lq, hidden] per batch row)
+ *   c = h . w_kv_a^T                               ([.., R + Dr])
+ *   k_rope_shared[b,t,:] = c[t, R:]                ([B, ctx+Lq, Dr], head-shared)
+ *   latent = rmsnorm(c[t, :R]) with gamma_kv [R]
+ *   k_nope, v = kv_b_proj(latent) as dflash_mla_latent_expand ([B, H, ctx+Lq, 128] each)
+ * ctx_hidden [B, ctx, hidden] (NULL allowed when ctx == 0), noise_hidden
+ * [B, Lq, hidden], w_kv_a [R + Dr, hidden], w_kv_b [H*(Dn+Dv), R].
+ * hidden a multiple of 32, R of 128, Dr of 4, Dn = Dv = 128. */
+dflash_status dflash_mla_kv_project(const void* ctx_hidden, const void* noise_hidden, const void* w_kv_a,
+                                    const void* gamma_kv, float eps, const void* w_kv_b, void* k_nope,
+                                    void* k_rope_shared, void* v, int64_t B, int64_t ctx, int64_t Lq,
+                                    int64_t hidden, int64_t R, int64_t Dr, int64_t H, int64_t Dn, int64_t Dv,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The tile map of the DFlash block mask computed from the block structure itself
  * instead of a dense mask: no mask bytes are read.  Row b, query i belongs to
  * block j = i / block_size and sees context key k (k < ctx) iff
