@@ -43,10 +43,10 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="2", help="headline workload: 0,1,2,3a,3b,4")
-    p.add_argument("--secondary", default="4,1,3a,3b,2s,4s,2b,4b",
+    p.add_argument("--secondary", default="4,1,3a,3b,2s,4s,2b,4b,2p",
                    help="comma list, or 'none'; a trailing 's' takes the mask from the block "
                         "structure (anchors) instead of the dense tensor, a trailing 'b' times "
-                        "the backward")
+                        "the backward, a trailing 'p' the projections around the attention")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -60,7 +60,7 @@ def parse():
 
 def make_workload(key: str):
     from dflash_block_draft_amd import workloads as W
-    key = key.rstrip("sb")
+    key = key.rstrip("sbp")
     if key == "3a":
         return W.config(3, block_size=8)
     if key == "3b":
@@ -223,6 +223,64 @@ def measure_bwd(wl, steps: int, warmup: int) -> dict:
     return res
 
 
+def measure_proj(wl, steps: int, warmup: int) -> dict:
+    """The projections around the attention at the workload's B, ctx, Lq and H
+    with hidden 7168, q_lora_rank 1536, R 512 and four target layers into fc:
+    context_project (fc + hidden_norm), q_project (Q-LoRA), kv_project
+    (kv_a_proj + kv_a_layernorm + kv_b_proj).  Each is timed on its own."""
+    import torch
+    from dflash_block_draft_amd import mla
+    from dflash_block_draft_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    p = W.projection_inputs(2000 + wl.seed, wl.B, wl.ctx, wl.Lq, wl.H)
+    t = {k: (v.to(dev) if hasattr(v, "to") else v) for k, v in p.items()}
+    B, ctx, Lq, H, hid, rq, R, Dr = wl.B, wl.ctx, wl.Lq, wl.H, p["hidden"], p["q_lora_rank"], p["R"], p["Dr"]
+    Kin = t["target_hidden"].shape[2]
+    Lk = ctx + Lq
+    ctx_out = torch.empty((B, ctx, hid), dtype=torch.bfloat16, device=dev)
+    q_out = torch.empty((B, H, Lq, 192), dtype=torch.bfloat16, device=dev)
+    ws_c = torch.empty(mla.load_library().dflash_mla_projection_workspace_bytes(B * ctx, hid), dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(mla.load_library().dflash_mla_projection_workspace_bytes(B * Lq, rq), dtype=torch.uint8, device=dev)
+    ws_kv = torch.empty(mla.load_library().dflash_mla_projection_workspace_bytes(B * Lk, R), dtype=torch.uint8, device=dev)
+    calls = {
+        "context_project": (lambda: mla.context_project(t["target_hidden"], t["w_fc"], t["g_hidden"], p["eps"],
+                                                        out=ctx_out, workspace=ws_c),
+                            2.0 * B * ctx * Kin * hid),
+        "q_project": (lambda: mla.q_project(t["noise_hidden"], t["w_q_a"], t["g_q"], p["eps"], t["w_q_b"], H,
+                                            out=q_out, workspace=ws_q),
+                      2.0 * B * Lq * (hid * rq + rq * H * 192)),
+        "kv_project": (lambda: mla.kv_project(t["ctx_hidden"], t["noise_hidden"], t["w_kv_a"], t["g_kv"], p["eps"],
+                                              t["w_kv_b"], H, R, workspace=ws_kv),
+                       2.0 * B * Lk * (hid * (R + Dr) + R * H * 256)),
+    }
+    res = {"workload": wl.name, "pass": "projections (hidden 7168, q_lora_rank 1536, R 512, fc from 4 layers)",
+           "parts": {}}
+    tot_ms = tot_f = 0.0
+    for name, (fn, flops) in calls.items():
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        tot_ms += ms
+        tot_f += flops
+        res["parts"][name] = {"ms": round(ms, 4), "gflop": round(flops / 1e9, 2),
+                              "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                              "pct_bf16_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    res.update({"ms_per_step": round(tot_ms, 4), "visible_gflop": round(tot_f / 1e9, 2),
+                "tflops": round(tot_f / (tot_ms * 1e-3) / 1e12, 2),
+                "pct_bf16_peak": round(100 * tot_f / (tot_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)})
+    del t, ctx_out, q_out, ws_c, ws_q, ws_kv
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(wl, budget_s: float) -> dict:
     """The fp64 oracle as it stands, timed on the host on a bounded sample:
     batch row 0, heads 0, 1, ... (all query rows each) until the budget is used."""
@@ -355,6 +413,8 @@ def main():
             log(describe(w2))
             if key.endswith("b"):
                 r = measure_bwd(w2, max(3, args.steps // 2), max(1, args.warmup // 2))
+            elif key.endswith("p"):
+                r = measure_proj(w2, max(3, args.steps // 2), max(1, args.warmup // 2))
             else:
                 r = measure(w2, max(3, args.steps // 2), max(1, args.warmup // 2), structured=key.endswith("s"))
             log(f"{key}: {r['ms_per_step']} ms/step, {r['tflops']} TFLOP/s ({r['pct_bf16_peak']}%)")

@@ -218,6 +218,31 @@ dflash_status dflash_mla_mask_occupancy(const void* additive_mask, dflash_dtype 
   return hip_status(dflash::launch_occupancy(o, static_cast<hipStream_t>(stream)), "mask occupancy launch");
 }
 
+}  // extern "C"
+
+namespace {
+
+// kv_b_proj as a linear layer: rows (b, token), outputs n = h * 256 + e scattered to
+// k_nope (e < 128) and v (e >= 128) in [B, H, Lk, 128].
+dflash::LinearArgs expand_linear(const void* latent, const void* w, void* kn, void* v, int64_t B, int64_t Lk,
+                                 int64_t R, int64_t H) {
+  dflash::LinearArgs l = {};
+  l.a1 = static_cast<const uint16_t*>(latent);
+  l.B = static_cast<int>(B);
+  l.T1 = static_cast<int>(Lk);
+  l.K = static_cast<int>(R);
+  l.w = static_cast<const uint16_t*>(w);
+  l.N = static_cast<int>(H * 256);
+  l.mode = dflash::kLinearKV;
+  l.y1 = static_cast<uint16_t*>(kn);
+  l.y2 = static_cast<uint16_t*>(v);
+  return l;
+}
+
+}  // namespace
+
+extern "C" {
+
 dflash_status dflash_mla_latent_expand(const void* latent, const void* w_kv_b, void* k_nope, void* v,
                                        int64_t B, int64_t Lk, int64_t R, int64_t H, int64_t Dn,
                                        int64_t Dv, dflash_dtype dt, void* stream) {
@@ -250,8 +275,11 @@ dflash_status dflash_mla_latent_expand(const void* latent, const void* w_kv_b, v
   a.R = static_cast<int>(R);
   a.H = static_cast<int>(H);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(dt == DFLASH_BF16 ? dflash::launch_expand_bf16(a, s) : dflash::launch_expand_f32(a, s),
-                    "latent expand launch");
+  if (dt == DFLASH_BF16) {
+    const dflash::LinearArgs l = expand_linear(latent, w_kv_b, k_nope, v, B, Lk, R, H);
+    return hip_status(dflash::launch_linear_bf16(l, s), "latent expand launch");
+  }
+  return hip_status(dflash::launch_expand_f32(a, s), "latent expand launch");
 }
 
 }  // extern "C"
@@ -718,20 +746,12 @@ dflash_status dflash_mla_kv_project(const void* ctx_hidden, const void* noise_hi
   l.Nstat = static_cast<int>(R);
   st = hip_status(dflash::launch_linear_bf16(l, s), "kv_a_proj_with_mqa launch");
   if (st != DFLASH_OK) return st;
-  dflash::ExpandArgs e = {};
-  e.latent = latent;
-  e.w = w_kv_b;
-  e.kn = k_nope;
-  e.v = v;
-  e.B = static_cast<int>(B);
-  e.Lk = static_cast<int>(Lk);
-  e.R = static_cast<int>(R);
-  e.H = static_cast<int>(H);
-  e.stats = stats;
+  dflash::LinearArgs e = expand_linear(latent, w_kv_b, k_nope, v, B, Lk, R, H);
+  e.stats_in = stats;
   e.stats_parts = static_cast<int>(R / 128);
   e.gamma = static_cast<const uint16_t*>(gamma_kv);
   e.eps = eps;
-  return hip_status(dflash::launch_expand_bf16(e, s), "kv_b_proj launch");
+  return hip_status(dflash::launch_linear_bf16(e, s), "kv_b_proj launch");
 }
 
 dflash_status dflash_mla_block_occupancy(const int32_t* anchors, const int32_t* ctx_valid, int64_t B, int64_t A,

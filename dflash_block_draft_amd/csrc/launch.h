@@ -70,13 +70,10 @@ struct AttnBwdArgs {
   float scale;
 };
 
-struct ExpandArgs {
+struct ExpandArgs {                   // fp32 expand
   const void* latent; const void* w;  // [B,Lk,R], [H*256,R]
   void* kn; void* v;                  // [B,H,Lk,128] each
   int B, Lk, R, H;
-  // optional RMSNorm of the latent rows on load (bf16 only): partial sums of
-  // squares [B*Lk, stats_parts] from the producing projection, weight [R]
-  const float* stats; int stats_parts; const uint16_t* gamma; float eps;
 };
 
 // Linear layer y = a W^T (bf16, fp32 accumulation) for the projections around
@@ -85,10 +82,11 @@ struct ExpandArgs {
 // (stats_in: per-row partial sums of squares of the producer's bf16 outputs,
 // stats_parts per row, over K entries; gamma [K]).  Optional statistics out:
 // per-row partial sums of squares of the bf16 outputs over each 128-column tile
-// of columns [0, Nstat), stats_out [M, Nstat / 128].
+// of columns [0, Nstat), stats_out [M, Nstat / 128] (Nstat a multiple of 128).
 constexpr int kLinearPlain = 0;   // y1 [M, N]
 constexpr int kLinearSplit = 1;   // y1 [M, N1] (columns < N1), y2 [M, N - N1]
 constexpr int kLinearHeads = 2;   // y1 [B, N / D, T1 + T2, D]
+constexpr int kLinearKV = 3;      // per head h = n / 256: y1 = k_nope [B, N/256, T, 128] (n % 256 < 128), y2 = v
 struct LinearArgs {
   const uint16_t* a1; const uint16_t* a2;
   int B, T1, T2, K;
@@ -114,7 +112,6 @@ hipError_t launch_block_occupancy(const OccupancyArgs& a, hipStream_t s);
 // Rewrite the lists so every k-tile is visited (empty tiles as class 3); debug/verification mode.
 hipError_t launch_lists_all_tiles(const OccupancyArgs& a, hipStream_t s);
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s);
-hipError_t launch_expand_bf16(const ExpandArgs& a, hipStream_t s);
 hipError_t launch_expand_f32(const ExpandArgs& a, hipStream_t s);
 
 }  // namespace dflash

@@ -28,31 +28,44 @@
 namespace dflash {
 namespace {
 
-constexpr int kNT = 128;            // outputs per tile
-constexpr int kMT = 128;            // rows per tile
-constexpr int kKS = 32;             // k per LDS stage
-constexpr int kRowStride = kKS + 8; // bf16 per LDS row
-constexpr int kStage = (kNT + kMT) * kRowStride;
+// Tile shapes: NT outputs x MT rows per workgroup, K staged KS at a time, WN x WM
+// waves each covering (NT / WN) x (MT / WM) as 32 x 32 MFMA blocks.
+template <int NT, int MT, int KS, int WN, int WM>
+struct Tile {
+  static constexpr int kThreads = 64 * WN * WM;
+  static constexpr int kFN = NT / WN / 32, kFM = MT / WM / 32;
+  static constexpr int kRow = KS + 8;                       // bf16 per LDS row: 16 * odd bytes
+  static constexpr int kStage = (NT + MT) * kRow;
+  static constexpr int kChunks = KS / 8;                    // 16-byte chunks per row and stage
+  static constexpr int kCW = NT * kChunks / kThreads, kCA = MT * kChunks / kThreads;
+  static_assert(kFN >= 1 && kFM >= 1 && kCW >= 1 && kCA >= 1, "tile shape");
+  static_assert(NT * kChunks % kThreads == 0 && MT * kChunks % kThreads == 0, "tile shape");
+  static_assert(NT / WN == 64 && NT % 128 == 0, "two waves per 128-column statistics group");
+};
+using BigTile = Tile<256, 256, 64, 4, 2>;     // 8 waves, 64 x 128 each
+using SmallTile = Tile<128, 128, 32, 2, 2>;   // 4 waves, 64 x 64 each
 
-__global__ void __launch_bounds__(256) linear_bf16(LinearArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStage];
-  __shared__ float s_part[2][kMT];
+template <int NT, int MT, int KS, int WN, int WM>
+__global__ void __launch_bounds__(64 * WN * WM) linear_bf16(LinearArgs a) {
+  using TL = Tile<NT, MT, KS, WN, WM>;
+  constexpr int FN = TL::kFN, FM = TL::kFM, ROW = TL::kRow, CH = TL::kChunks, NTH = TL::kThreads;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * TL::kStage];
+  __shared__ float s_part[WN][MT];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave % WN, wm = wave / WN;
   const int li = lane & 31, hi = lane >> 5;
   const int T = a.T1 + a.T2;
   const int64_t M = static_cast<int64_t>(a.B) * T;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * kMT;
-  const int n0 = blockIdx.y * kNT;
-  const uint16_t* W = a.w;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * MT;
+  const int n0 = blockIdx.y * NT;
 
-  // this thread's two staging rows (A side) and their sources
-  const uint16_t* arow[2];
-  bool aok[2], wok[2];
-  float rsc[2] = {1.f, 1.f};
+  // this thread's staging rows (A side: rows m, with their sources and norm scales)
+  const uint16_t* arow[TL::kCA];
+  bool aok[TL::kCA];
+  float rsc[TL::kCA];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int ci = t + 256 * i, row = ci >> 2;
+  for (int i = 0; i < TL::kCA; ++i) {
+    const int row = (t + NTH * i) / CH;
     const int64_t m = m0 + row;
     aok[i] = m < M;
     const int64_t mm = aok[i] ? m : 0;
@@ -60,70 +73,78 @@ __global__ void __launch_bounds__(256) linear_bf16(LinearArgs a) {
     const int tt = static_cast<int>(mm % T);
     arow[i] = tt < a.T1 ? a.a1 + (static_cast<size_t>(b) * a.T1 + tt) * a.K
                         : a.a2 + (static_cast<size_t>(b) * a.T2 + (tt - a.T1)) * a.K;
-    wok[i] = n0 + row < a.N;
-    if (a.stats_in && aok[i]) rsc[i] = rms_row_scale(a.stats_in, a.stats_parts, m, a.K, a.eps);
+    rsc[i] = (a.stats_in && aok[i]) ? rms_row_scale(a.stats_in, a.stats_parts, m, a.K, a.eps) : 1.f;
   }
 
-  u32x4_t sw[2], sl[2];
+  u32x4_t sw[TL::kCW], sl[TL::kCA];
   auto load = [&](int k0) {
+    const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ci = t + 256 * i, row = ci >> 2, c = ci & 3;
-      const u32x4_t z = {0u, 0u, 0u, 0u};
-      sw[i] = wok[i] ? ldg16(W + static_cast<size_t>(n0 + row) * a.K + k0 + c * 8) : z;
+    for (int i = 0; i < TL::kCW; ++i) {
+      const int ci = t + NTH * i, row = ci / CH, c = ci % CH;
+      sw[i] = n0 + row < a.N ? ldg16(a.w + static_cast<size_t>(n0 + row) * a.K + k0 + c * 8) : z;
+    }
+#pragma unroll
+    for (int i = 0; i < TL::kCA; ++i) {
+      const int c = (t + NTH * i) % CH;
       sl[i] = aok[i] ? ldg16(arow[i] + k0 + c * 8) : z;
       if (a.stats_in && aok[i]) sl[i] = rms_norm_chunk(sl[i], rsc[i], ldg16(a.gamma + k0 + c * 8));
     }
   };
   auto store = [&](uint16_t* buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ci = t + 256 * i, row = ci >> 2, c = ci & 3;
-      stg16(buf + row * kRowStride + c * 8, sw[i]);
-      stg16(buf + (kNT + row) * kRowStride + c * 8, sl[i]);
+    for (int i = 0; i < TL::kCW; ++i) {
+      const int ci = t + NTH * i;
+      stg16(buf + (ci / CH) * ROW + (ci % CH) * 8, sw[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < TL::kCA; ++i) {
+      const int ci = t + NTH * i;
+      stg16(buf + (NT + ci / CH) * ROW + (ci % CH) * 8, sl[i]);
     }
   };
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[FN][FM];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FN; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < FM; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = a.K / kKS;
+  const int nk = a.K / KS;
   load(0);
   store(smem);
   __syncthreads();
   for (int it = 0; it < nk; ++it) {
     const bool more = it + 1 < nk;
-    if (more) load((it + 1) * kKS);
-    const uint16_t* Ws = smem + (it & 1) * kStage;
-    const uint16_t* Ls = Ws + kNT * kRowStride;
+    if (more) load((it + 1) * KS);
+    const uint16_t* Ws = smem + (it & 1) * TL::kStage;
+    const uint16_t* Ls = Ws + NT * ROW;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t af[2], bf[2];
+    for (int ks = 0; ks < KS / 16; ++ks) {
+      bf16x8_t af[FN], bf[FM];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        af[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(Ws + (64 * wn + 32 * i + li) * kRowStride + 16 * ks + 8 * hi));
-        bf[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(Ls + (64 * wm + 32 * i + li) * kRowStride + 16 * ks + 8 * hi));
-      }
+      for (int i = 0; i < FN; ++i)
+        af[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(Ws + ((NT / WN) * wn + 32 * i + li) * ROW + 16 * ks + 8 * hi));
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < FM; ++j)
+        bf[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(Ls + ((MT / WM) * wm + 32 * j + li) * ROW + 16 * ks + 8 * hi));
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
     }
-    if (more) store(smem + ((it + 1) & 1) * kStage);
+    if (more) store(smem + ((it + 1) & 1) * TL::kStage);
     __syncthreads();
   }
 
   // epilogue: lane owns row m (column li of sub-tile j) and outputs
-  // n = n0 + 64*wn + 32*i + 8*g + 4*hi + 0..3 (register 4g + 0..3 of acc[i][j])
+  // n = n0 + (NT/WN)*wn + 32*i + 8*g + 4*hi + 0..3 (registers 4g + 0..3 of acc[i][j])
   const bool stats = a.stats_out && n0 < a.Nstat;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int rl = 64 * wm + 32 * j + li;
+  for (int j = 0; j < FM; ++j) {
+    const int rl = (MT / WM) * wm + 32 * j + li;
     const int64_t m = m0 + rl;
     const bool mok = m < M;
     const int64_t mm = mok ? m : 0;
@@ -131,10 +152,10 @@ __global__ void __launch_bounds__(256) linear_bf16(LinearArgs a) {
     const int tt = static_cast<int>(mm % T);
     float ssq = 0.f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FN; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + 64 * wn + 32 * i + 8 * g + 4 * hi;
+        const int n = n0 + (NT / WN) * wn + 32 * i + 8 * g + 4 * hi;
         const uint32_t p0 = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
         const uint32_t p1 = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
         if (n < a.N) {
@@ -148,9 +169,12 @@ __global__ void __launch_bounds__(256) linear_bf16(LinearArgs a) {
             } else if (a.mode == kLinearSplit) {
               dst = n < a.N1 ? a.y1 + static_cast<size_t>(m) * a.N1 + n
                              : a.y2 + static_cast<size_t>(m) * (a.N - a.N1) + (n - a.N1);
-            } else {                                   // heads: [B, N / D, T, D]
+            } else if (a.mode == kLinearHeads) {       // [B, N / D, T, D]
               const int h = n / a.D, d = n % a.D;
               dst = a.y1 + ((static_cast<size_t>(b) * (a.N / a.D) + h) * T + tt) * a.D + d;
+            } else {                                   // kv: per head [k_nope (128) | v (128)]
+              const int h = n >> 8, e = n & 255;
+              dst = (e < kDn ? a.y1 : a.y2) + ((static_cast<size_t>(b) * (a.N >> 8) + h) * T + tt) * kDn + (e & 127);
             }
             *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{p0, p1};
           }
@@ -161,40 +185,62 @@ __global__ void __launch_bounds__(256) linear_bf16(LinearArgs a) {
       if (hi == 0) s_part[wn][rl] = ssq;
     }
   }
-  if (stats) {
+  if (stats) {                                        // one partial per 128-column group
     __syncthreads();
-    if (t < kMT) {
-      const int64_t m = m0 + t;
-      if (m < M) a.stats_out[m * (a.Nstat / kNT) + blockIdx.y] = s_part[0][t] + s_part[1][t];
+    constexpr int G = NT / 128;
+    const int parts = a.Nstat / 128;
+    for (int idx = t; idx < MT * G; idx += NTH) {
+      const int r = idx % MT, gi = idx / MT;
+      const int part = n0 / 128 + gi;
+      const int64_t m = m0 + r;
+      if (m < M && part < parts) a.stats_out[m * parts + part] = s_part[2 * gi][r] + s_part[2 * gi + 1][r];
     }
   }
 }
 
 // RMSNorm from producer statistics: y = bf16(bf16(x * r) * gamma), r = rsqrt(mean(x^2) + eps).
-// One thread per 8 consecutive entries.
+// One workgroup per row: thread 0 sums the row's partials once, every thread then
+// normalises 8-entry chunks of the row.
 __global__ void __launch_bounds__(256) rms_apply_bf16(RmsApplyArgs a) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int per_row = a.N / 8;
-  if (i >= a.M * per_row) return;
-  const int64_t m = i / per_row;
-  const int c = static_cast<int>(i % per_row);
-  const float r = rms_row_scale(a.stats, a.parts, m, a.N, a.eps);
-  const u32x4_t x = ldg16(a.x + static_cast<size_t>(m) * a.N + 8 * c);
-  stg16(a.y + static_cast<size_t>(m) * a.N + 8 * c, rms_norm_chunk(x, r, ldg16(a.gamma + 8 * c)));
+  __shared__ float s_r;
+  const int64_t m = blockIdx.x;
+  if (threadIdx.x == 0) s_r = rms_row_scale(a.stats, a.parts, m, a.N, a.eps);
+  __syncthreads();
+  const float r = s_r;
+  const uint16_t* xr = a.x + static_cast<size_t>(m) * a.N;
+  uint16_t* yr = a.y + static_cast<size_t>(m) * a.N;
+  for (int c = threadIdx.x; c < a.N / 8; c += 256)
+    stg16(yr + 8 * c, rms_norm_chunk(ldg16(xr + 8 * c), r, ldg16(a.gamma + 8 * c)));
 }
 
 }  // namespace
 
+// The 256 x 256 tile moves half the operand bytes per flop of the 128 x 128 one,
+// but one workgroup fills a CU, so it is taken only when its tiles fill the
+// 256 CUs in whole rounds (at least 85% of the last round busy, or many rounds)
+// and the long K loop amortises the prologue and epilogue.
+static bool linear_big_tile(const LinearArgs& a) {
+  const int64_t M = static_cast<int64_t>(a.B) * (a.T1 + a.T2);
+  const int64_t tiles = ((M + 255) / 256) * ((a.N + 255) / 256);
+  if (a.K % 64 != 0 || a.K < 1024 || tiles < 240) return false;
+  const int64_t rounds = (tiles + 255) / 256;
+  return rounds >= 4 || tiles * 100 >= rounds * 256 * 85;
+}
+
 hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t s) {
   const int64_t M = static_cast<int64_t>(a.B) * (a.T1 + a.T2);
-  const dim3 grid(static_cast<unsigned>((M + kMT - 1) / kMT), static_cast<unsigned>((a.N + kNT - 1) / kNT));
-  hipLaunchKernelGGL(linear_bf16, grid, dim3(256), 0, s, a);
+  if (linear_big_tile(a)) {
+    const dim3 grid(static_cast<unsigned>((M + 255) / 256), static_cast<unsigned>((a.N + 255) / 256));
+    hipLaunchKernelGGL((linear_bf16<256, 256, 64, 4, 2>), grid, dim3(BigTile::kThreads), 0, s, a);
+  } else {
+    const dim3 grid(static_cast<unsigned>((M + 127) / 128), static_cast<unsigned>((a.N + 127) / 128));
+    hipLaunchKernelGGL((linear_bf16<128, 128, 32, 2, 2>), grid, dim3(SmallTile::kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_rms_apply_bf16(const RmsApplyArgs& a, hipStream_t s) {
-  const int64_t n = a.M * (a.N / 8);
-  hipLaunchKernelGGL(rms_apply_bf16, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(rms_apply_bf16, dim3(static_cast<unsigned>(a.M)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

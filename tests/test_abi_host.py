@@ -242,3 +242,36 @@ def test_attn_lse_validation(lib):
     assert f(*base, None, *tail) == 1                       # lse NULL
     assert f(*base, FAKE * 5, *tail) == 1                   # lse overlaps out
     assert f(*base, FAKE * 6 + 1, *tail) == 1               # misaligned
+
+
+def test_projection_workspace_bytes(lib):
+    assert lib.dflash_mla_projection_workspace_bytes(0, 128) == 0
+    assert lib.dflash_mla_projection_workspace_bytes(1000, 512) >= 1000 * 512 * 2 + 1000 * 4 * 4
+
+
+def test_projection_validation(lib):
+    cp, qp, kvp = lib.dflash_mla_context_project, lib.dflash_mla_q_project, lib.dflash_mla_kv_project
+    ws, wsb = FAKE * 256, 1 << 26
+    # context: (th, w_fc, gamma, eps, out, B, ctx, K_in, hidden, ws, wsb, stream)
+    assert cp(None, FAKE * 2, FAKE * 3, 1e-6, FAKE * 4, 1, 64, 256, 128, ws, wsb, None) == 1
+    assert cp(FAKE, FAKE * 2, FAKE * 3, -1.0, FAKE * 4, 1, 64, 256, 128, ws, wsb, None) == 1   # eps < 0
+    assert cp(FAKE, FAKE * 2, FAKE * 3, 1e-6, FAKE * 4, 1, 64, 250, 128, ws, wsb, None) == 2   # K_in % 32
+    assert cp(FAKE, FAKE * 2, FAKE * 3, 1e-6, FAKE * 4, 1, 64, 256, 100, ws, wsb, None) == 2   # hidden % 128
+    assert cp(FAKE, FAKE * 2, FAKE * 3, 1e-6, FAKE * 4, 1, 64, 256, 128, None, 0, None) == 3
+    assert cp(FAKE, FAKE * 2, FAKE * 3, 1e-6, FAKE, 1, 64, 256, 128, ws, wsb, None) == 1       # out aliases input
+    # q: (x, wqa, gq, eps, wqb, q, B, Lq, hidden, Rq, H, Dqk, ws, wsb, stream)
+    assert qp(FAKE, FAKE * 2, FAKE * 3, 1e-6, FAKE * 4, FAKE * 5, 1, 32, 256, 100, 2, 192, ws, wsb, None) == 2  # Rq % 128
+    assert qp(FAKE, FAKE * 2, FAKE * 3, 1e-6, FAKE * 4, FAKE * 5, 1, 32, 256, 128, 2, 190, ws, wsb, None) == 2  # Dqk % 4
+    assert qp(FAKE, FAKE * 2, FAKE * 3, 1e-6, FAKE * 4, FAKE * 5, 1, 0, 256, 128, 2, 192, ws, wsb, None) == 1
+    assert qp(FAKE, FAKE * 2, FAKE * 3, 1e-6, FAKE * 4, FAKE * 5, 1, 32, 256, 128, 2, 192, ws, 64, None) == 3
+    # kv: (ctx_h, noise_h, wkva, gkv, eps, wkvb, kn, kr, v, B, ctx, Lq, hidden, R, Dr, H, Dn, Dv, ws, wsb, stream)
+    args = [FAKE, FAKE * 2, FAKE * 3, FAKE * 4, 1e-6, FAKE * 5, FAKE * 6, FAKE * 7, FAKE * 8,
+            1, 64, 32, 256, 512, 64, 2, 128, 128, ws, wsb, None]
+    bad = list(args); bad[0] = None
+    assert kvp(*bad) == 1                                   # ctx > 0 needs ctx_hidden
+    bad = list(args); bad[13] = 500
+    assert kvp(*bad) == 2                                   # R % 128
+    bad = list(args); bad[16] = 64
+    assert kvp(*bad) == 2                                   # Dn
+    bad = list(args); bad[6] = FAKE * 8
+    assert kvp(*bad) == 1                                   # k_nope overlaps v
