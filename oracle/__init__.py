@@ -43,6 +43,12 @@ What it computes, and the passages it follows:
   latent, fp32-variance RMSNorm); DSpark page KimiK3DSparkAttention attributes
   and forward, KimiK3DSparkModel._forward_backbone.
 
+* ``gqa.materialize`` / ``forward_block`` / ``gqa_attention`` / ``rope`` /
+  ``yarn_inv_freq`` -- the MHA/GQA DFlash draft of the Modular MAX page
+  (pipelines.architectures.dflash_kimi_k25): qk-normed, yarn-RoPE keys and the
+  values of the context written into a cache once (materialize), then each
+  block attends non-causally to that cache plus itself (forward_block).
+
 Readings where the pages are silent (also listed in the design notes):
 a row whose every score is -inf returns 0; a mask entry is "masked" only if it
 is exactly -inf, any finite value (including large negatives) is added as is.
@@ -53,5 +59,6 @@ a library routine) -- nothing here is "parity unpinned".
 from .attention import mla_attention, softmax_weights  # noqa: F401
 from .backward import logsumexp_rows, mla_attention_backward  # noqa: F401
 from .projection import context_project, kv_project, linear, q_project, rms_norm  # noqa: F401
+from .gqa import forward_block, gqa_attention, materialize, rope, yarn_inv_freq, yarn_mscale  # noqa: F401
 from .expand import latent_expand  # noqa: F401
 from .occupancy import tile_bits, tile_classes, tile_lists  # noqa: F401

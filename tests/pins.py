@@ -511,7 +511,126 @@ def pin_kv_project_brute_force():
 PROJECTION_PINS = [pin_rms_norm, pin_context_project_brute_force, pin_q_project_brute_force,
                    pin_kv_project_brute_force]
 
+# ---------------------------------------------------------------- GQA draft (yarn RoPE, qk-norm)
+
+def pin_yarn_limits():
+    """factor 1 is plain RoPE; otherwise the first pairs keep 1/theta^(2i/d), the last
+    are divided by the factor, and the ratio in between never decreases."""
+    d, base = 64, 10000.0
+    plain = 1.0 / base ** (np.arange(0, d, 2) / d)
+    np.testing.assert_allclose(oracle.yarn_inv_freq(d, base, 1.0, 4096, 32, 1), plain, rtol=1e-15)
+    inv = oracle.yarn_inv_freq(d, base, 8.0, 4096, 32, 1)
+    ratio = plain / inv
+    assert abs(ratio[0] - 1.0) < 1e-15 and abs(ratio[-1] - 8.0) < 1e-12
+    assert np.all(np.diff(ratio) >= -1e-12) and (ratio == 1.0).sum() >= 2 and (abs(ratio - 8.0) < 1e-12).sum() >= 2
+    assert abs(oracle.yarn_mscale(1.0, 0.7) - 1.0) < 1e-15
+    assert abs(oracle.yarn_mscale(math.e, 1.0) - 1.1) < 1e-15
+
+
+def pin_rope_properties():
+    """Dimension i pairs with i + d/2; rotation keeps the norm; the product of a
+    rotated query and key depends only on their position difference."""
+    rng = np.random.default_rng(74)
+    d = 16
+    inv = oracle.yarn_inv_freq(d, 500.0, 4.0, 64, 8, 1)
+    for i in (0, 3, d // 2 - 1):
+        e = np.zeros(d)
+        e[i] = 1.0
+        out = oracle.rope(e[None], [37], inv)[0]
+        want = np.zeros(d)
+        want[i] = math.cos(37 * inv[i])
+        want[i + d // 2] = math.sin(37 * inv[i])
+        np.testing.assert_allclose(out, want, atol=1e-14)
+    x = rng.standard_normal((5, d))
+    np.testing.assert_allclose(np.linalg.norm(oracle.rope(x, np.arange(5) * 101, inv), axis=-1),
+                               np.linalg.norm(x, axis=-1), rtol=1e-13)
+    q, k = rng.standard_normal(d), rng.standard_normal(d)
+    for m, n, sh in ((5, 2, 40), (0, 17, 1000)):
+        a = oracle.rope(q[None], [m], inv)[0] @ oracle.rope(k[None], [n], inv)[0]
+        b = oracle.rope(q[None], [m + sh], inv)[0] @ oracle.rope(k[None], [n + sh], inv)[0]
+        assert abs(a - b) < 1e-11
+    np.testing.assert_allclose(oracle.rope(x, [0] * 5, inv, 1.5), 1.5 * x, atol=1e-14)
+
+
+def pin_gqa_matches_torch_sdpa():
+    """PyTorch's attention (fp64, CPU) with the KV heads repeated over their query
+    group and a key-length mask per batch row."""
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(75)
+    B, Hq, Hkv, Lq, Lk, d = 2, 6, 2, 5, 11, 8
+    q = rng.standard_normal((B, Hq, Lq, d))
+    k = rng.standard_normal((B, Hkv, Lk, d))
+    v = rng.standard_normal((B, Hkv, Lk, d))
+    lens = [11, 7]
+    mask = np.zeros((B, 1, Lq, Lk))
+    mask[1, :, :, 7:] = -np.inf
+    kr = torch.from_numpy(k).repeat_interleave(3, dim=1)
+    vr = torch.from_numpy(v).repeat_interleave(3, dim=1)
+    ref = F.scaled_dot_product_attention(torch.from_numpy(q), kr, vr, attn_mask=torch.from_numpy(mask),
+                                         scale=0.3).numpy()
+    np.testing.assert_allclose(oracle.gqa_attention(q, k, v, lens, 0.3), ref, atol=1e-12)
+
+
+def _gqa_case(seed, B=2, Lc=7, bs=3, hidden=8, Hq=4, Hkv=2, d=8):
+    rng = np.random.default_rng(seed)
+    return dict(ctx=rng.standard_normal((B, Lc, hidden)), blk=rng.standard_normal((B, bs, hidden)),
+                wq=rng.standard_normal((Hq * d, hidden)) * 0.3, wk=rng.standard_normal((Hkv * d, hidden)) * 0.3,
+                wv=rng.standard_normal((Hkv * d, hidden)) * 0.3, gq=1 + 0.1 * rng.standard_normal(d),
+                gk=1 + 0.1 * rng.standard_normal(d), inv=oracle.yarn_inv_freq(d, 100.0, 2.0, 16, 4, 1),
+                Hq=Hq, Hkv=Hkv, d=d, B=B, Lc=Lc, bs=bs)
+
+
+def pin_forward_block_equals_whole_sequence():
+    """With ctx_len = Lc, a block over the materialised context equals attention
+    over the K/V materialised from the whole [context | block] sequence (positions
+    continue across the boundary, context first); cached keys past ctx_len[b]
+    are never read; the block's queries come from the q chain at those positions."""
+    c = _gqa_case(76)
+    kc, vc = oracle.materialize(c["ctx"], c["wk"], c["wv"], c["gk"], 0.1, c["Hkv"], c["inv"], 1.2)
+    out = oracle.forward_block(c["blk"], c["wq"], c["wk"], c["wv"], c["gq"], c["gk"], 0.1, c["Hq"], c["Hkv"],
+                               kc, vc, [c["Lc"]] * c["B"], c["inv"], 1.2)
+    whole = np.concatenate([c["ctx"], c["blk"]], axis=1)
+    kw, vw = oracle.materialize(whole, c["wk"], c["wv"], c["gk"], 0.1, c["Hkv"], c["inv"], 1.2)
+    L = c["Lc"] + c["bs"]
+    qw, _ = oracle.materialize(whole, c["wq"], c["wq"], c["gq"], 0.1, c["Hq"], c["inv"], 1.2)
+    want = oracle.gqa_attention(qw[:, :, c["Lc"]:], kw, vw, [L] * c["B"], c["d"] ** -0.5)
+    np.testing.assert_allclose(out, want, atol=1e-12)
+    # a shorter context in row 1: garbage past ctx_len is ignored, positions restart at ctx_len
+    kg, vg = kc.copy(), vc.copy()
+    kg[1, :, 4:] = 1e3
+    vg[1, :, 4:] = -1e3
+    out2 = oracle.forward_block(c["blk"], c["wq"], c["wk"], c["wv"], c["gq"], c["gk"], 0.1, c["Hq"], c["Hkv"],
+                                kg, vg, [c["Lc"], 4], c["inv"], 1.2)
+    whole1 = np.concatenate([c["ctx"][1:2, :4], c["blk"][1:2]], axis=1)
+    kw1, vw1 = oracle.materialize(whole1, c["wk"], c["wv"], c["gk"], 0.1, c["Hkv"], c["inv"], 1.2)
+    qw1, _ = oracle.materialize(whole1, c["wq"], c["wq"], c["gq"], 0.1, c["Hq"], c["inv"], 1.2)
+    want1 = oracle.gqa_attention(qw1[:, :, 4:], kw1, vw1, [4 + c["bs"]], c["d"] ** -0.5)
+    np.testing.assert_allclose(out2[1:2], want1, atol=1e-12)
+    np.testing.assert_allclose(out2[0], out[0], atol=0)
+
+
+def pin_materialize_brute_force():
+    """k = RoPE(RMSNorm(x W_k^T per head)), v = x W_v^T, written out with loops."""
+    c = _gqa_case(77, B=1, Lc=4, hidden=5, Hkv=2, d=4)
+    k, v = oracle.materialize(c["ctx"], c["wk"], c["wv"], c["gk"], 0.2, 2, c["inv"], 1.0)
+    d = 4
+    for t in range(4):
+        x = c["ctx"][0, t]
+        for h in range(2):
+            raw = [sum(x[j] * c["wk"][h * d + e, j] for j in range(5)) for e in range(d)]
+            nk = _brute_rms(raw, c["gk"], 0.2)
+            for e in range(d):
+                ang = t * c["inv"][e % (d // 2)]
+                partner = -nk[e + d // 2] if e < d // 2 else nk[e - d // 2]
+                assert abs(k[0, h, t, e] - (nk[e] * math.cos(ang) + partner * math.sin(ang))) < 1e-12
+                assert abs(v[0, h, t, e] - sum(x[j] * c["wv"][h * d + e, j] for j in range(5))) < 1e-12
+
+
+GQA_PINS = [pin_yarn_limits, pin_rope_properties, pin_gqa_matches_torch_sdpa,
+            pin_forward_block_equals_whole_sequence, pin_materialize_brute_force]
+
 BACKWARD_PINS = [pin_backward_finite_differences, pin_backward_matches_torch_autograd,
                  pin_backward_invariants, pin_logsumexp_normalises_the_forward]
 
-ALL_PINS = ATTENTION_PINS + EXPAND_PINS + OCCUPANCY_PINS + BACKWARD_PINS + PROJECTION_PINS
+ALL_PINS = ATTENTION_PINS + EXPAND_PINS + OCCUPANCY_PINS + BACKWARD_PINS + PROJECTION_PINS + GQA_PINS

@@ -206,6 +206,66 @@ def _kv_norm_whole(ctx_hidden, noise_hidden, w_kv_a, gamma_kv, eps, w_kv_b, H, R
     return kn, cn[..., R:], v
 
 
+from oracle import gqa as ogqa
+
+
+def _rope_interleaved(x, positions, inv_freq, mscale=1.0):
+    x = f64(x)
+    ang = np.asarray(positions, dtype=np.float64)[..., None] * f64(inv_freq)
+    c, sn = np.cos(ang) * mscale, np.sin(ang) * mscale
+    out = x.copy()
+    out[..., 0::2] = x[..., 0::2] * c - x[..., 1::2] * sn
+    out[..., 1::2] = x[..., 1::2] * c + x[..., 0::2] * sn
+    return out
+
+
+def _rope_sign(x, positions, inv_freq, mscale=1.0):
+    return _orig_rope(x, -np.asarray(positions, dtype=np.float64), inv_freq, mscale)
+
+
+def _gqa_head_modulo(q, k, v, lens, scale):
+    q, k, v = f64(q), f64(k), f64(v)
+    Hkv = k.shape[1]
+    out = np.zeros(q.shape[:3] + (v.shape[-1],))
+    for b in range(q.shape[0]):
+        n = int(lens[b])
+        for h in range(q.shape[1]):
+            s_ = scale * (q[b, h] @ k[b, h % Hkv, :n].T)
+            p_ = np.exp(s_ - s_.max(axis=-1, keepdims=True))
+            out[b, h] = (p_ / p_.sum(axis=-1, keepdims=True)) @ v[b, h % Hkv, :n]
+    return out
+
+
+def _yarn_betas_swapped(dim, base, factor, orig, beta_fast, beta_slow):
+    return _orig_yarn(dim, base, factor, orig, beta_slow, beta_fast)
+
+
+def _fb_zero(blk_hidden, w_q, w_k, w_v, gamma_q, gamma_k, eps, Hq, Hkv, k_ctx, v_ctx, ctx_len, inv_freq, mscale):
+    x = f64(blk_hidden)
+    B, bs, _ = x.shape
+    pos = np.arange(bs)[None, None, :]
+    q = ogqa.rope(oproj.rms_norm(ogqa._heads(oproj.linear(x, w_q), Hq), gamma_q, eps), pos, inv_freq, mscale)
+    kb = ogqa.rope(oproj.rms_norm(ogqa._heads(oproj.linear(x, w_k), Hkv), gamma_k, eps), pos, inv_freq, mscale)
+    vb = ogqa._heads(oproj.linear(x, w_v), Hkv)
+    out = np.zeros((B, Hq, bs, q.shape[-1]))
+    for b in range(B):
+        n = int(ctx_len[b])
+        k = np.concatenate([f64(k_ctx[b:b + 1, :, :n]), kb[b:b + 1]], axis=2)
+        v = np.concatenate([f64(v_ctx[b:b + 1, :, :n]), vb[b:b + 1]], axis=2)
+        out[b] = ogqa.gqa_attention(q[b:b + 1], k, v, [n + bs], q.shape[-1] ** -0.5)[0]
+    return out
+
+
+def _materialize_norm_after_rope(ctx_hidden, w_k, w_v, gamma_k, eps, Hkv, inv_freq, mscale=1.0):
+    x = f64(ctx_hidden)
+    k = oproj.rms_norm(ogqa.rope(ogqa._heads(oproj.linear(x, w_k), Hkv), np.arange(x.shape[1]), inv_freq, mscale),
+                       gamma_k, eps)
+    return k, ogqa._heads(oproj.linear(x, w_v), Hkv)
+
+
+_orig_rope = ogqa.rope
+_orig_yarn = ogqa.yarn_inv_freq
+_orig_fb = ogqa.forward_block
 _orig_rms = oproj.rms_norm
 _orig_kv = oracle.kv_project
 _orig_lse = oracle.logsumexp_rows
@@ -244,6 +304,12 @@ MUTANTS = {
     "kv_noise_first": [(oracle, "kv_project", _kv_noise_first)],
     "kv_rope_first": [(oracle, "kv_project", _kv_rope_first)],
     "kv_norm_whole_row": [(oracle, "kv_project", _kv_norm_whole)],
+    "rope_interleaved_pairs": [(ogqa, "rope", _rope_interleaved), (oracle, "rope", _rope_interleaved)],
+    "rope_sign": [(ogqa, "rope", _rope_sign), (oracle, "rope", _rope_sign)],
+    "gqa_head_modulo": [(ogqa, "gqa_attention", _gqa_head_modulo), (oracle, "gqa_attention", _gqa_head_modulo)],
+    "yarn_betas_swapped": [(ogqa, "yarn_inv_freq", _yarn_betas_swapped), (oracle, "yarn_inv_freq", _yarn_betas_swapped)],
+    "block_positions_from_zero": [(oracle, "forward_block", _fb_zero)],
+    "qk_norm_after_rope": [(oracle, "materialize", _materialize_norm_after_rope)],
 }
 
 
