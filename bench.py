@@ -43,10 +43,11 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="2", help="headline workload: 0,1,2,3a,3b,4")
-    p.add_argument("--secondary", default="4,1,3a,3b,2s,4s,2b,4b,2p",
+    p.add_argument("--secondary", default="4,1,3a,3b,2s,4s,2b,4b,2p,gqa",
                    help="comma list, or 'none'; a trailing 's' takes the mask from the block "
                         "structure (anchors) instead of the dense tensor, a trailing 'b' times "
-                        "the backward, a trailing 'p' the projections around the attention")
+                        "the backward, a trailing 'p' the projections around the attention; 'gqa' "
+                        "the MHA/GQA draft of the MAX page")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -60,6 +61,8 @@ def parse():
 
 def make_workload(key: str):
     from dflash_block_draft_amd import workloads as W
+    if key == "gqa":
+        return None
     key = key.rstrip("sbp")
     if key == "3a":
         return W.config(3, block_size=8)
@@ -281,6 +284,65 @@ def measure_proj(wl, steps: int, warmup: int) -> dict:
     return res
 
 
+def measure_gqa(steps: int, warmup: int) -> dict:
+    """The MHA/GQA draft: 8 requests with contexts of 8K-32K tokens (hidden 7168,
+    32 query heads over 8 KV heads of 128, block 16).  Times the context
+    materialisation (a GEMM into the cache) and forward_block; the block's
+    attention reads every cached key and value once per KV head, so it is
+    reported in HBM bytes per second against 8 TB/s."""
+    import numpy as np
+    import torch
+    from dflash_block_draft_amd import mla
+    from dflash_block_draft_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    B, Lc, bs, hidden, Hq, Hkv = 8, 32768, 16, 7168, 32, 8
+    ctx = np.random.default_rng(3000).integers(8192, Lc + 1, size=B)
+    # weights and the block from the seeded host recipe; the 8 x 32768 x 7168 context
+    # hidden states N(0,1) from a seeded device generator (the host one would take minutes)
+    p = W.gqa_inputs(3001, B, 16, bs, hidden, Hq, Hkv, ctx_len=ctx, Lmax=-(-(Lc + bs) // 8) * 8)
+    t = {k: (v.to(dev) if hasattr(v, "to") else v) for k, v in p.items()}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3002)
+    t["ctx_hidden"] = torch.randn((B, Lc, hidden), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    kc, vc = mla.gqa_new_cache(B, Hkv, p["Lmax"], dev)
+    ws = torch.empty(mla.load_library().dflash_gqa_workspace_bytes(B, bs, Hq, Hkv, p["Lmax"]), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((B, Hq, bs, 128), dtype=torch.bfloat16, device=dev)
+
+    def mat():
+        mla.gqa_materialize(t["ctx_hidden"], t["w_k"], t["w_v"], t["g_k"], p["eps"], p["rope"], kc, vc)
+
+    def blk():
+        mla.gqa_forward_block(t["blk_hidden"], t["w_q"], t["w_k"], t["w_v"], t["g_q"], t["g_k"], p["eps"], p["rope"],
+                              kc, vc, t["ctx_len"], Hq, out=out, workspace=ws)
+
+    res = {"workload": "gqa_draft_b8_ctx8k-32k_h32kv8_bs16", "pass": "MAX-page GQA draft (materialize, forward_block)"}
+    for name, fn, n in (("materialize", mat, max(2, steps // 4)), ("forward_block", blk, steps)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        res[name + "_ms"] = round(a.elapsed_time(b) / n, 4)
+    mat_flops = 2.0 * B * Lc * hidden * 2 * Hkv * 128
+    kv_bytes = float(sum(int(c) + bs for c in ctx)) * Hkv * 128 * 2 * 2
+    res["materialize_tflops"] = round(mat_flops / (res["materialize_ms"] * 1e-3) / 1e12, 2)
+    res["forward_block_kv_bytes"] = int(kv_bytes)
+    res["forward_block_GBs"] = round(kv_bytes / (res["forward_block_ms"] * 1e-3) / 1e9, 1)
+    res["forward_block_pct_hbm_peak"] = round(100 * kv_bytes / (res["forward_block_ms"] * 1e-3) / 8e12, 2)
+    res["ms_per_step"] = res["forward_block_ms"]
+    res["tflops"] = None
+    res["pct_bf16_peak"] = None
+    del t, kc, vc, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(wl, budget_s: float) -> dict:
     """The fp64 oracle as it stands, timed on the host on a bounded sample:
     batch row 0, heads 0, 1, ... (all query rows each) until the budget is used."""
@@ -407,6 +469,13 @@ def main():
     if args.secondary.strip().lower() != "none":
         for key in [k.strip() for k in args.secondary.split(",") if k.strip()]:
             if key == args.workload:
+                continue
+            if key == "gqa":
+                log("GQA draft: materialize + forward_block")
+                r = measure_gqa(max(3, args.steps // 2), max(1, args.warmup // 2))
+                log(f"gqa: forward_block {r['forward_block_ms']} ms ({r['forward_block_GBs']} GB/s), "
+                    f"materialize {r['materialize_ms']} ms ({r['materialize_tflops']} TFLOP/s)")
+                secondary.append(r)
                 continue
             log(f"building workload {key}")
             w2 = make_workload(key)

@@ -2,6 +2,7 @@
 // workspace layout and kernel dispatch.  Nothing here allocates device memory
 // or keeps state; every launch goes on the caller's stream.
 #include <cmath>
+#include <algorithm>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -752,6 +753,234 @@ dflash_status dflash_mla_kv_project(const void* ctx_hidden, const void* noise_hi
   e.gamma = static_cast<const uint16_t*>(gamma_kv);
   e.eps = eps;
   return hip_status(dflash::launch_linear_bf16(e, s), "kv_b_proj launch");
+}
+
+// ---------------------------------------------------------------- GQA draft (MAX variant)
+
+}  // extern "C"
+
+namespace {
+
+struct GqaSplit {
+  int splits, tiles_per_split;
+};
+
+GqaSplit gqa_split(int64_t B, int64_t Hkv, int64_t Lmax) {
+  const int64_t ntiles = (Lmax + 63) / 64;
+  int64_t want = (1024 + B * Hkv - 1) / (B * Hkv);
+  want = std::max<int64_t>(1, std::min(want, ntiles));
+  const int64_t tps = (ntiles + want - 1) / want;
+  return {static_cast<int>((ntiles + tps - 1) / tps), static_cast<int>(tps)};
+}
+
+bool gqa_layout(int64_t B, int64_t bs, int64_t Hq, int64_t Hkv, int64_t Lmax, size_t* q_off, size_t* o_off,
+                size_t* ml_off, size_t* total) {
+  if (B <= 0 || bs <= 0 || Hq <= 0 || Hkv <= 0 || Lmax <= 0 || B > 65535 || Hq > 4096 || Lmax > INT32_MAX) return false;
+  const GqaSplit sp = gqa_split(B, Hkv, Lmax);
+  const size_t rows = static_cast<size_t>(B) * Hkv * sp.splits * 64;
+  *q_off = 0;
+  *o_off = align_up(static_cast<size_t>(B) * Hq * bs * 128 * 2, 256);
+  *ml_off = *o_off + align_up(rows * 128 * 4, 256);
+  *total = *ml_off + align_up(rows * 2 * 4, 256);
+  return true;
+}
+
+dflash::NormRopeArgs norm_rope_args(const float* rope, const void* gamma, float eps) {
+  dflash::NormRopeArgs n = {};
+  n.gamma = static_cast<const uint16_t*>(gamma);
+  n.eps = eps;
+  n.theta = rope[0];
+  n.factor = rope[1];
+  n.orig_max_pos = rope[2];
+  n.beta_fast = rope[3];
+  n.beta_slow = rope[4];
+  n.mscale = rope[5];
+  n.mscale_all_dim = rope[6];
+  return n;
+}
+
+dflash_status check_rope(const float* rope) {
+  if (!rope) return fail(DFLASH_ERR_INVALID_ARG, "rope parameters are NULL");
+  for (int i = 0; i < 7; ++i)
+    if (!std::isfinite(rope[i])) return fail(DFLASH_ERR_INVALID_ARG, "rope parameter %d is not finite", i);
+  if (!(rope[0] > 1.f) || !(rope[1] > 0.f) || !(rope[2] > 0.f) || !(rope[3] > 0.f) || !(rope[4] > 0.f))
+    return fail(DFLASH_ERR_INVALID_ARG, "rope: theta > 1 and factor, original length, beta_fast, beta_slow > 0");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dflash_gqa_workspace_bytes(int64_t B, int64_t bs, int64_t Hq, int64_t Hkv, int64_t Lmax) {
+  size_t q, o, ml, total;
+  return gqa_layout(B, bs, Hq, Hkv, Lmax, &q, &o, &ml, &total) ? total : 0;
+}
+
+dflash_status dflash_gqa_materialize(const void* ctx_hidden, const void* w_k, const void* w_v, const void* gamma_k,
+                                     float eps, const float* rope, void* k_cache, void* v_cache_t, int64_t B,
+                                     int64_t Lc, int64_t Lmax, int64_t hidden, int64_t Hkv, int64_t head_dim,
+                                     void* stream) {
+  if (!ctx_hidden || !w_k || !w_v || !gamma_k || !k_cache || !v_cache_t)
+    return fail(DFLASH_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!aligned16(ctx_hidden) || !aligned16(w_k) || !aligned16(w_v) || !aligned16(gamma_k) || !aligned16(k_cache) ||
+      !aligned16(v_cache_t))
+    return fail(DFLASH_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  dflash_status st = check_rope(rope);
+  if (st != DFLASH_OK) return st;
+  if (B <= 0 || Lc <= 0 || Lmax <= 0 || hidden <= 0 || Hkv <= 0 || head_dim <= 0)
+    return fail(DFLASH_ERR_INVALID_ARG, "sizes must be positive");
+  if (!std::isfinite(eps) || eps < 0.f) return fail(DFLASH_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (Lc > Lmax) return fail(DFLASH_ERR_INVALID_ARG, "Lc exceeds the cache length");
+  if (head_dim != 128 || hidden % 32 != 0 || Lmax % 8 != 0)
+    return fail(DFLASH_ERR_UNSUPPORTED, "head_dim must be 128, hidden a multiple of 32, Lmax of 8");
+  int64_t M, tmp;
+  if (!mul_ok(B, Lc, &M) || M > INT32_MAX || B > 65535 || Lmax > INT32_MAX || hidden > INT32_MAX ||
+      !mul_ok(B * Hkv, Lmax * 128, &tmp) || Hkv * 128 > INT32_MAX || !mul_ok(M, hidden, &tmp))
+    return fail(DFLASH_ERR_UNSUPPORTED, "sizes too large");
+  const size_t cache = static_cast<size_t>(B) * Hkv * Lmax * 128 * 2;
+  const Range r[6] = {range_of(k_cache, cache), range_of(v_cache_t, cache),
+                      range_of(ctx_hidden, static_cast<size_t>(M) * hidden * 2),
+                      range_of(w_k, static_cast<size_t>(Hkv) * 128 * hidden * 2),
+                      range_of(w_v, static_cast<size_t>(Hkv) * 128 * hidden * 2), range_of(gamma_k, 256)};
+  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 6; ++j)
+      if (i != j && overlaps(r[i], r[j])) return fail(DFLASH_ERR_INVALID_ARG, "a cache overlaps another buffer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  dflash::LinearArgs l = linear_args();
+  l.a1 = static_cast<const uint16_t*>(ctx_hidden);
+  l.B = static_cast<int>(B);
+  l.T1 = static_cast<int>(Lc);
+  l.K = static_cast<int>(hidden);
+  l.w = static_cast<const uint16_t*>(w_k);
+  l.N = static_cast<int>(Hkv * 128);
+  l.mode = dflash::kLinearHeads;
+  l.D = 128;
+  l.Lt = static_cast<int>(Lmax);
+  l.y1 = static_cast<uint16_t*>(k_cache);
+  st = hip_status(dflash::launch_linear_bf16(l, s), "k projection launch");
+  if (st != DFLASH_OK) return st;
+  dflash::NormRopeArgs n = norm_rope_args(rope, gamma_k, eps);
+  n.x = static_cast<uint16_t*>(k_cache);
+  n.B = static_cast<int>(B);
+  n.H = static_cast<int>(Hkv);
+  n.Lt = static_cast<int>(Lmax);
+  n.T = static_cast<int>(Lc);
+  st = hip_status(dflash::launch_norm_rope_bf16(n, s), "k norm / rope launch");
+  if (st != DFLASH_OK) return st;
+  l.w = static_cast<const uint16_t*>(w_v);
+  l.mode = dflash::kLinearHeadsT;
+  l.y1 = static_cast<uint16_t*>(v_cache_t);
+  return hip_status(dflash::launch_linear_bf16(l, s), "v projection launch");
+}
+
+dflash_status dflash_gqa_forward_block(const void* blk_hidden, const void* w_q, const void* w_k, const void* w_v,
+                                       const void* gamma_q, const void* gamma_k, float eps, const float* rope,
+                                       void* k_cache, void* v_cache_t, const int32_t* ctx_len, void* out, int64_t B,
+                                       int64_t bs, int64_t Lmax, int64_t hidden, int64_t Hq, int64_t Hkv,
+                                       int64_t head_dim, float scale, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  if (!blk_hidden || !w_q || !w_k || !w_v || !gamma_q || !gamma_k || !k_cache || !v_cache_t || !ctx_len || !out)
+    return fail(DFLASH_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!aligned16(blk_hidden) || !aligned16(w_q) || !aligned16(w_k) || !aligned16(w_v) || !aligned16(gamma_q) ||
+      !aligned16(gamma_k) || !aligned16(k_cache) || !aligned16(v_cache_t) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(ctx_len) & 3u) != 0)
+    return fail(DFLASH_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned (ctx_len 4-byte)");
+  dflash_status st = check_rope(rope);
+  if (st != DFLASH_OK) return st;
+  if (B <= 0 || bs <= 0 || Lmax <= 0 || hidden <= 0 || Hq <= 0 || Hkv <= 0 || head_dim <= 0)
+    return fail(DFLASH_ERR_INVALID_ARG, "sizes must be positive");
+  if (!std::isfinite(eps) || eps < 0.f || !std::isfinite(scale) || !(scale > 0.f))
+    return fail(DFLASH_ERR_INVALID_ARG, "eps must be >= 0 and scale > 0, both finite");
+  if (bs > Lmax) return fail(DFLASH_ERR_INVALID_ARG, "the block is longer than the cache");
+  if (head_dim != 128 || hidden % 32 != 0 || Lmax % 8 != 0 || Hq % Hkv != 0 || (Hq / Hkv) * bs > 64)
+    return fail(DFLASH_ERR_UNSUPPORTED, "head_dim 128, hidden % 32, Lmax % 8, Hq % Hkv and (Hq / Hkv) * bs <= 64 required");
+  size_t qo, oo, mlo, need;
+  if (!gqa_layout(B, bs, Hq, Hkv, Lmax, &qo, &oo, &mlo, &need) || hidden > INT32_MAX)
+    return fail(DFLASH_ERR_UNSUPPORTED, "sizes too large");
+  st = check_ws(workspace, workspace_bytes, need);
+  if (st != DFLASH_OK) return st;
+  const size_t cache = static_cast<size_t>(B) * Hkv * Lmax * 128 * 2;
+  const Range r[10] = {range_of(k_cache, cache), range_of(v_cache_t, cache),
+                       range_of(out, static_cast<size_t>(B) * Hq * bs * 128 * 2), range_of(workspace, need),
+                       range_of(blk_hidden, static_cast<size_t>(B) * bs * hidden * 2),
+                       range_of(w_q, static_cast<size_t>(Hq) * 128 * hidden * 2),
+                       range_of(w_k, static_cast<size_t>(Hkv) * 128 * hidden * 2),
+                       range_of(w_v, static_cast<size_t>(Hkv) * 128 * hidden * 2), range_of(gamma_q, 256),
+                       range_of(ctx_len, static_cast<size_t>(B) * 4)};
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 10; ++j)
+      if (i != j && overlaps(r[i], r[j])) return fail(DFLASH_ERR_INVALID_ARG, "an output or the workspace overlaps another buffer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* qbuf = reinterpret_cast<uint16_t*>(ws + qo);
+  const int off_max = static_cast<int>(Lmax - bs);
+  // q: projection, then qk-norm + RoPE at positions ctx_len + t
+  dflash::LinearArgs l = linear_args();
+  l.a1 = static_cast<const uint16_t*>(blk_hidden);
+  l.B = static_cast<int>(B);
+  l.T1 = static_cast<int>(bs);
+  l.K = static_cast<int>(hidden);
+  l.w = static_cast<const uint16_t*>(w_q);
+  l.N = static_cast<int>(Hq * 128);
+  l.mode = dflash::kLinearHeads;
+  l.D = 128;
+  l.y1 = qbuf;
+  st = hip_status(dflash::launch_linear_bf16(l, s), "q projection launch");
+  if (st != DFLASH_OK) return st;
+  dflash::NormRopeArgs n = norm_rope_args(rope, gamma_q, eps);
+  n.x = qbuf;
+  n.B = static_cast<int>(B);
+  n.H = static_cast<int>(Hq);
+  n.Lt = static_cast<int>(bs);
+  n.T = static_cast<int>(bs);
+  n.row_off = ctx_len;
+  n.off_max = off_max;
+  n.rows_local = 1;
+  st = hip_status(dflash::launch_norm_rope_bf16(n, s), "q norm / rope launch");
+  if (st != DFLASH_OK) return st;
+  // the block's k and v appended to the caches at ctx_len
+  l.w = static_cast<const uint16_t*>(w_k);
+  l.N = static_cast<int>(Hkv * 128);
+  l.y1 = static_cast<uint16_t*>(k_cache);
+  l.Lt = static_cast<int>(Lmax);
+  l.row_off = ctx_len;
+  l.off_max = off_max;
+  st = hip_status(dflash::launch_linear_bf16(l, s), "k projection launch");
+  if (st != DFLASH_OK) return st;
+  dflash::NormRopeArgs nk = norm_rope_args(rope, gamma_k, eps);
+  nk.x = static_cast<uint16_t*>(k_cache);
+  nk.B = static_cast<int>(B);
+  nk.H = static_cast<int>(Hkv);
+  nk.Lt = static_cast<int>(Lmax);
+  nk.T = static_cast<int>(bs);
+  nk.row_off = ctx_len;
+  nk.off_max = off_max;
+  st = hip_status(dflash::launch_norm_rope_bf16(nk, s), "k norm / rope launch");
+  if (st != DFLASH_OK) return st;
+  l.w = static_cast<const uint16_t*>(w_v);
+  l.mode = dflash::kLinearHeadsT;
+  l.y1 = static_cast<uint16_t*>(v_cache_t);
+  st = hip_status(dflash::launch_linear_bf16(l, s), "v projection launch");
+  if (st != DFLASH_OK) return st;
+  const GqaSplit sp = gqa_split(B, Hkv, Lmax);
+  dflash::GqaAttnArgs g = {};
+  g.q = qbuf;
+  g.k = static_cast<const uint16_t*>(k_cache);
+  g.vt = static_cast<const uint16_t*>(v_cache_t);
+  g.out = static_cast<uint16_t*>(out);
+  g.ctx_len = ctx_len;
+  g.B = static_cast<int>(B);
+  g.Hq = static_cast<int>(Hq);
+  g.Hkv = static_cast<int>(Hkv);
+  g.bs = static_cast<int>(bs);
+  g.Lmax = static_cast<int>(Lmax);
+  g.splits = sp.splits;
+  g.tiles_per_split = sp.tiles_per_split;
+  g.scale = scale;
+  g.part_o = reinterpret_cast<float*>(ws + oo);
+  g.part_ml = reinterpret_cast<float*>(ws + mlo);
+  return hip_status(dflash::launch_gqa_attn_bf16(g, s), "block attention launch");
 }
 
 dflash_status dflash_mla_block_occupancy(const int32_t* anchors, const int32_t* ctx_valid, int64_t B, int64_t A,

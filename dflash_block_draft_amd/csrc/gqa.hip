@@ -1,0 +1,315 @@
+// The MHA/GQA DFlash draft's attention path (Modular MAX page,
+// pipelines.architectures.dflash_kimi_k25): qk-norm + yarn RoPE applied in
+// place to head-major rows, and block attention of the draft's queries over the
+// bf16 KV cache that holds the materialised context plus the block itself.
+//
+// norm_rope: one workgroup per (token, batch row), one wave per head row of 128:
+// lane l holds entries l and l + 64, which are exactly a rotate-half pair, so the
+// RMSNorm reduction is one wave sum and the rotation needs no data movement.  The
+// 64 angles of the token are formed once per workgroup in fp64 (yarn frequency,
+// position times frequency reduced modulo 2 pi) and shared through LDS.
+//
+// gqa_attn: the cache is read once per KV head for its whole query group (g heads
+// x bs block tokens <= 64 query rows), so each key byte feeds 64 rows: the
+// kernel streams K and V at HBM rate and is bound by HBM, not by the matrix
+// cores.  Keys are split across workgroups (split-K, flash-decoding style) so
+// B * Hkv * splits workgroups cover the chip; each keeps fp32 (O, m, l) partials
+// and a combine kernel merges the splits in order.  Inside a workgroup, four
+// waves = 2 query blocks of 32 x 2 key halves of each 64-key tile; scores are
+// computed transposed (S^T = K Q^T, one query per lane) so P^T feeds
+// O^T += V^T P^T straight from the accumulator, with V^T read from the cache's
+// transposed V (keys contiguous per dimension) -- no transposing LDS reads.
+#include "common.h"
+#include "launch.h"
+
+#include <math.h>
+
+namespace dflash {
+namespace {
+
+constexpr int kD = 128;                       // head_dim this file is built for
+constexpr int kKT = 64;                       // keys per tile
+constexpr int kSK = kD * 2 + 16;              // K tile row stride (bytes): 272
+constexpr int kSV = kKT * 2 + 16;             // V^T tile row stride (bytes): 144
+constexpr int kStageK = kKT * kSK;
+constexpr int kStage = kStageK + kD * kSV;    // 35840 bytes
+
+__device__ __forceinline__ float bf16r(float x) { return bf16_bits_to_f32(pack_bf16x2(x, 0.f) & 0xFFFFu); }
+
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// yarn inverse frequency of rotary pair i (DeepSeek-V3 yarn), fp64
+__device__ double yarn_inv_freq(int i, const NormRopeArgs& a) {
+  const double d = kD;
+  const double extra = 1.0 / pow(a.theta, 2.0 * i / d);
+  const double inter = extra / a.factor;
+  const double two_pi = 6.283185307179586;
+  const double lb = 2.0 * log(a.theta);
+  double low = floor(d * log(a.orig_max_pos / (a.beta_fast * two_pi)) / lb);
+  double high = ceil(d * log(a.orig_max_pos / (a.beta_slow * two_pi)) / lb);
+  low = fmax(low, 0.0);
+  high = fmin(high, d - 1.0);
+  if (low == high) high += 0.001;
+  const double ramp = fmin(fmax((i - low) / (high - low), 0.0), 1.0);
+  return inter * ramp + extra * (1.0 - ramp);
+}
+
+__device__ double yarn_mscale(double scale, double m) { return scale <= 1.0 ? 1.0 : 0.1 * m * log(scale) + 1.0; }
+
+__global__ void __launch_bounds__(256) norm_rope_bf16(NormRopeArgs a) {
+  __shared__ float s_cos[kD / 2], s_sin[kD / 2];
+  const int t = blockIdx.x, b = blockIdx.y;
+  const int t0 = a.row_off ? min(max(a.row_off[b], 0), a.off_max) : 0;
+  const int ti = t0 + t;
+  if (threadIdx.x < kD / 2) {
+    const double ms = yarn_mscale(a.factor, a.mscale) / yarn_mscale(a.factor, a.mscale_all_dim);
+    const double ang = fmod(static_cast<double>(ti) * yarn_inv_freq(threadIdx.x, a), 6.283185307179586);
+    s_cos[threadIdx.x] = static_cast<float>(cos(ang) * ms);
+    s_sin[threadIdx.x] = static_cast<float>(sin(ang) * ms);
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float g0 = bf16_bits_to_f32(a.gamma[lane]), g1 = bf16_bits_to_f32(a.gamma[lane + 64]);
+  const float c = s_cos[lane], sn = s_sin[lane];
+  for (int h = wave; h < a.H; h += 4) {
+    uint16_t* row = a.x + ((static_cast<size_t>(b) * a.H + h) * a.Lt + (a.rows_local ? t : ti)) * kD;
+    const float x0 = bf16_bits_to_f32(row[lane]), x1 = bf16_bits_to_f32(row[lane + 64]);
+    float ss = x0 * x0 + x1 * x1;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+    const float r = rsqrtf(ss / kD + a.eps);
+    const float n0 = bf16r(bf16r(x0 * r) * g0), n1 = bf16r(bf16r(x1 * r) * g1);
+    const uint32_t w = pack_bf16x2(n0 * c - n1 * sn, n1 * c + n0 * sn);
+    row[lane] = static_cast<uint16_t>(w & 0xFFFFu);
+    row[lane + 64] = static_cast<uint16_t>(w >> 16);
+  }
+}
+
+__global__ void __launch_bounds__(256) gqa_attn_bf16(GqaAttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int li = lane & 31, hi = lane >> 5;
+  const int qb = w & 1, kh = w >> 1;
+  const int sp = blockIdx.x, bk = blockIdx.y;
+  const int b = bk / a.Hkv, hk = bk % a.Hkv;
+  const int g = a.Hq / a.Hkv, Qg = g * a.bs;
+  const int L = min(max(a.ctx_len[b], 0), a.Lmax - a.bs) + a.bs;
+  const int ntiles = (L + kKT - 1) / kKT;
+  const int tile0 = sp * a.tiles_per_split, tile1 = min(tile0 + a.tiles_per_split, ntiles);
+
+  // this lane's query row of the group
+  const int r = 32 * qb + li;
+  const bool r_ok = r < Qg;
+  const int h = hk * g + (r_ok ? r / a.bs : 0), i = r_ok ? r % a.bs : 0;
+  bf16x8_t qreg[kD / 16];
+#pragma unroll
+  for (int s = 0; s < kD / 16; ++s) {
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    qreg[s] = as_bf16x8(r_ok ? ldg16(a.q + ((static_cast<size_t>(b) * a.Hq + h) * a.bs + i) * kD + 16 * s + 8 * hi) : z);
+  }
+  const uint16_t* kbase = a.k + static_cast<size_t>(bk) * a.Lmax * kD;
+  const uint16_t* vbase = a.vt + static_cast<size_t>(bk) * kD * a.Lmax;
+
+  f32x16_t o[kD / 32];
+#pragma unroll
+  for (int j = 0; j < kD / 32; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[j][e] = 0.f;
+  float m = -INFINITY, l = 0.f;                       // log2 units
+
+  u32x4_t pre[8];
+  auto prefetch = [&](int tile) {
+    const int k0 = tile * kKT;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {                     // K: 64 rows x 16 chunks
+      const int ci = t + 256 * c, row = ci >> 4, ch = ci & 15, key = k0 + row;
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+      pre[c] = key < L ? ldg16(kbase + static_cast<size_t>(key) * kD + 8 * ch) : z;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {                     // V^T: 128 rows x 8 chunks of 8 keys
+      const int ci = t + 256 * c, row = ci >> 3, ch = ci & 7, key = k0 + 8 * ch;
+      u32x4_t x = {0u, 0u, 0u, 0u};
+      if (key < L) {
+        x = ldg16(vbase + static_cast<size_t>(row) * a.Lmax + key);
+        if (key + 8 > L) {                            // zero the keys past the end (the cache there is unset)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int k2 = key + 2 * e;
+            const uint32_t keep = (k2 < L ? 0x0000FFFFu : 0u) | (k2 + 1 < L ? 0xFFFF0000u : 0u);
+            x[e] &= keep;
+          }
+        }
+      }
+      pre[4 + c] = x;
+    }
+  };
+  auto commit = [&](char* st) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int ci = t + 256 * c;
+      *reinterpret_cast<u32x4_t*>(st + (ci >> 4) * kSK + (ci & 15) * 16) = pre[c];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int ci = t + 256 * c;
+      *reinterpret_cast<u32x4_t*>(st + kStageK + (ci >> 3) * kSV + (ci & 7) * 16) = pre[4 + c];
+    }
+  };
+
+  const float c2 = a.scale * kLog2e;
+  auto compute = [&](const char* st, int tile) {
+    f32x16_t s = {};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] = 0.f;
+#pragma unroll
+    for (int k = 0; k < kD / 16; ++k)
+      s = mfma32(as_bf16x8(*reinterpret_cast<const u32x4_t*>(st + (32 * kh + li) * kSK + (16 * k + 8 * hi) * 2)),
+                 qreg[k], s);
+    float x[16], tmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = tile * kKT + 32 * kh + 8 * (e >> 2) + 4 * hi + (e & 3);
+      x[e] = key < L ? s[e] * c2 : -INFINITY;
+      tmax = fmaxf(tmax, x[e]);
+    }
+    // a key half can lie wholly past L (the tail tile): m_new stays -inf there, and a
+    // finite stabiliser keeps exp2(-inf - m) = 0 instead of exp2(-inf + inf) = NaN
+    const float m_new = fmaxf(m, halves_max(tmax));
+    const float m_sub = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
+    float p[16], sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p[e] = bf16r(__builtin_amdgcn_exp2f(x[e] - m_sub));
+      sum += p[e];
+    }
+    l = l * alpha + halves_sum(sum);
+    m = m_new;
+#pragma unroll
+    for (int j = 0; j < kD / 32; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[j][e] *= alpha;
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const u32x4_t wv = {pack_bf16x2(p[8 * kk], p[8 * kk + 1]), pack_bf16x2(p[8 * kk + 2], p[8 * kk + 3]),
+                          pack_bf16x2(p[8 * kk + 4], p[8 * kk + 5]), pack_bf16x2(p[8 * kk + 6], p[8 * kk + 7])};
+      pb[kk] = as_bf16x8(wv);
+    }
+#pragma unroll
+    for (int j = 0; j < kD / 32; ++j) {
+      const char* rowp = st + kStageK + (32 * j + li) * kSV;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        // keys 32kh + 16kk + {4hi .. 4hi+3} and {8 + 4hi .. 8 + 4hi + 3}: the accumulator's row order
+        const int kb = 32 * kh + 16 * kk + 4 * hi;
+        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(rowp + kb * 2);
+        const u32x2_t up = *reinterpret_cast<const u32x2_t*>(rowp + (kb + 8) * 2);
+        const u32x4_t av = {lo[0], lo[1], up[0], up[1]};
+        o[j] = mfma32(as_bf16x8(av), pb[kk], o[j]);
+      }
+    }
+  };
+
+  if (tile0 < tile1) {
+    prefetch(tile0);
+    commit(smem);
+    __syncthreads();
+    for (int tile = tile0; tile < tile1; ++tile) {
+      const bool more = tile + 1 < tile1;
+      if (more) prefetch(tile + 1);
+      compute(smem + ((tile - tile0) & 1) * kStage, tile);
+      if (!more) break;
+      commit(smem + ((tile + 1 - tile0) & 1) * kStage);
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+
+  // merge the two key halves of each query block, write the split's partial
+  float* red = reinterpret_cast<float*>(smem) + qb * (64 * (16 * kD / 32 + 2));
+  if (kh == 1) {
+#pragma unroll
+    for (int j = 0; j < kD / 32; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[(j * 16 + e) * 64 + lane] = o[j][e];
+    red[(kD / 2) * 64 + lane] = m;
+    red[(kD / 2 + 1) * 64 + lane] = l;
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const float m1 = red[(kD / 2) * 64 + lane], l1 = red[(kD / 2 + 1) * 64 + lane];
+    const float mm = fmaxf(m, m1);
+    const float a0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mm);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+    const size_t prow = (static_cast<size_t>(bk) * a.splits + sp) * 64 + r;
+    if (r_ok) {
+      float* po = a.part_o + prow * kD;
+      // o[j][e] holds dim 32 j + 8 (e / 4) + 4 hi + e % 4
+#pragma unroll
+      for (int j = 0; j < kD / 32; ++j)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          f32x4_t v;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int e = 4 * gq + c;
+            v[c] = o[j][e] * a0 + red[(j * 16 + e) * 64 + lane] * a1;
+          }
+          *reinterpret_cast<f32x4_t*>(po + 32 * j + 8 * gq + 4 * hi) = v;
+        }
+      if (hi == 0) {
+        a.part_ml[prow * 2] = mm;
+        a.part_ml[prow * 2 + 1] = l * a0 + l1 * a1;
+      }
+    }
+  }
+}
+
+// out[b, h, i, :] = sum over splits of the partials, merged in split order.
+__global__ void __launch_bounds__(kD) gqa_combine_bf16(GqaAttnArgs a) {
+  const int r = blockIdx.x, bk = blockIdx.y;
+  const int b = bk / a.Hkv, hk = bk % a.Hkv, g = a.Hq / a.Hkv;
+  const int d = threadIdx.x;
+  const size_t base = static_cast<size_t>(bk) * a.splits * 64 + r;
+  float mm = -INFINITY;
+  for (int s = 0; s < a.splits; ++s) mm = fmaxf(mm, a.part_ml[(base + static_cast<size_t>(s) * 64) * 2]);
+  float lsum = 0.f, acc = 0.f;
+  for (int s = 0; s < a.splits; ++s) {
+    const size_t row = base + static_cast<size_t>(s) * 64;
+    const float ms = a.part_ml[row * 2];
+    if (ms == -INFINITY) continue;
+    const float wgt = __builtin_amdgcn_exp2f(ms - mm);
+    lsum += wgt * a.part_ml[row * 2 + 1];
+    acc += wgt * a.part_o[row * kD + d];
+  }
+  const int h = hk * g + r / a.bs, i = r % a.bs;
+  const float v = lsum > 0.f ? acc / lsum : 0.f;
+  a.out[((static_cast<size_t>(b) * a.Hq + h) * a.bs + i) * kD + d] = static_cast<uint16_t>(pack_bf16x2(v, 0.f) & 0xFFFFu);
+}
+
+}  // namespace
+
+hipError_t launch_norm_rope_bf16(const NormRopeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(norm_rope_bf16, dim3(a.T, a.B), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gqa_attn_bf16(const GqaAttnArgs& a, hipStream_t s) {
+  const unsigned bk = static_cast<unsigned>(a.B) * a.Hkv;
+  hipLaunchKernelGGL(gqa_attn_bf16, dim3(a.splits, bk), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gqa_combine_bf16, dim3((a.Hq / a.Hkv) * a.bs, bk), dim3(kD), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace dflash

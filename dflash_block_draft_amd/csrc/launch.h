@@ -87,6 +87,7 @@ constexpr int kLinearPlain = 0;   // y1 [M, N]
 constexpr int kLinearSplit = 1;   // y1 [M, N1] (columns < N1), y2 [M, N - N1]
 constexpr int kLinearHeads = 2;   // y1 [B, N / D, T1 + T2, D]
 constexpr int kLinearKV = 3;      // per head h = n / 256: y1 = k_nope [B, N/256, T, 128] (n % 256 < 128), y2 = v
+constexpr int kLinearHeadsT = 4;  // y1 [B, N / D, D, Lt] (time innermost), time index as for kLinearHeads
 struct LinearArgs {
   const uint16_t* a1; const uint16_t* a2;
   int B, T1, T2, K;
@@ -94,6 +95,30 @@ struct LinearArgs {
   const float* stats_in; int stats_parts; const uint16_t* gamma; float eps;
   int mode; uint16_t* y1; uint16_t* y2; int N1; int D;
   float* stats_out; int Nstat;
+  // head-major modes: time index of row t of batch row b is off(b) + t in a time
+  // axis of Lt entries (Lt = 0: T1 + T2 and no offset); off(b) = clamp(row_off[b], 0, off_max)
+  const int32_t* row_off; int off_max; int Lt;
+};
+
+// In-place qk-norm + yarn RoPE of rows of a head-major tensor x [B, H, Lt, d]:
+// rows t0(b) .. t0(b) + T - 1 with t0(b) = clamp(row_off[b], 0, off_max) (0 without
+// row_off); position of row t0(b) + t is t0(b) + t.  d = 128.
+struct NormRopeArgs {
+  uint16_t* x; int B, H, Lt, T;
+  const int32_t* row_off; int off_max;
+  int rows_local;                         // 1: rows 0 .. T-1 (positions still t0(b) + t)
+  const uint16_t* gamma; float eps;
+  double theta, factor, orig_max_pos, beta_fast, beta_slow, mscale, mscale_all_dim;
+};
+
+// Block attention of the GQA draft: q [B, Hq, bs, d]; k cache [B, Hkv, Lmax, d];
+// v cache transposed [B, Hkv, d, Lmax]; row b sees keys < clamp(ctx_len[b], 0, Lmax - bs) + bs.
+struct GqaAttnArgs {
+  const uint16_t* q; const uint16_t* k; const uint16_t* vt; uint16_t* out;
+  const int32_t* ctx_len;
+  int B, Hq, Hkv, bs, Lmax, splits, tiles_per_split;
+  float scale;
+  float* part_o; float* part_ml;        // [B*Hkv, splits, 64, 128], [B*Hkv, splits, 64, 2]
 };
 
 // y = RMSNorm(x) with statistics from the producer: y[m] = bf16(bf16(x[m] * r_m) * gamma).
@@ -103,6 +128,8 @@ struct RmsApplyArgs {
 };
 
 hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t s);
+hipError_t launch_norm_rope_bf16(const NormRopeArgs& a, hipStream_t s);
+hipError_t launch_gqa_attn_bf16(const GqaAttnArgs& a, hipStream_t s);
 hipError_t launch_rms_apply_bf16(const RmsApplyArgs& a, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnBf16Args& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnF32Args& a, hipStream_t s);

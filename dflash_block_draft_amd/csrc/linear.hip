@@ -169,9 +169,21 @@ __global__ void __launch_bounds__(64 * WN * WM) linear_bf16(LinearArgs a) {
             } else if (a.mode == kLinearSplit) {
               dst = n < a.N1 ? a.y1 + static_cast<size_t>(m) * a.N1 + n
                              : a.y2 + static_cast<size_t>(m) * (a.N - a.N1) + (n - a.N1);
-            } else if (a.mode == kLinearHeads) {       // [B, N / D, T, D]
+            } else if (a.mode == kLinearHeads || a.mode == kLinearHeadsT) {
               const int h = n / a.D, d = n % a.D;
-              dst = a.y1 + ((static_cast<size_t>(b) * (a.N / a.D) + h) * T + tt) * a.D + d;
+              const int Lt = a.Lt ? a.Lt : T;
+              const int ti = (a.row_off ? min(max(a.row_off[b], 0), a.off_max) : 0) + tt;
+              const size_t bh = static_cast<size_t>(b) * (a.N / a.D) + h;
+              if (a.mode == kLinearHeads) {            // [B, N / D, Lt, D]
+                dst = a.y1 + (bh * Lt + ti) * a.D + d;
+              } else {                                 // [B, N / D, D, Lt]
+                uint16_t* col = a.y1 + (bh * a.D + d) * Lt + ti;
+                col[0] = static_cast<uint16_t>(p0 & 0xFFFFu);
+                col[Lt] = static_cast<uint16_t>(p0 >> 16);
+                col[2 * static_cast<size_t>(Lt)] = static_cast<uint16_t>(p1 & 0xFFFFu);
+                col[3 * static_cast<size_t>(Lt)] = static_cast<uint16_t>(p1 >> 16);
+                continue;
+              }
             } else {                                   // kv: per head [k_nope (128) | v (128)]
               const int h = n >> 8, e = n & 255;
               dst = (e < kDn ? a.y1 : a.y2) + ((static_cast<size_t>(b) * (a.N >> 8) + h) * T + tt) * kDn + (e & 127);

@@ -32,7 +32,8 @@ EXPORTED = (
     "dflash_mla_mask_occupancy", "dflash_mla_attn", "dflash_mla_block_occupancy",
     "dflash_mla_attn_blocks", "dflash_mla_attn_lse", "dflash_mla_attn_bwd_workspace_bytes",
     "dflash_mla_attn_bwd", "dflash_mla_projection_workspace_bytes", "dflash_mla_context_project",
-    "dflash_mla_q_project", "dflash_mla_kv_project",
+    "dflash_mla_q_project", "dflash_mla_kv_project", "dflash_gqa_materialize", "dflash_gqa_workspace_bytes",
+    "dflash_gqa_forward_block",
 )
 
 
@@ -92,6 +93,13 @@ def load_library() -> ctypes.CDLL:
     lib.dflash_mla_kv_project.argtypes = [vp, vp, vp, vp, f32, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
                                           i64, i64, vp, sz, vp]
     lib.dflash_mla_kv_project.restype = i32
+    lib.dflash_gqa_materialize.argtypes = [vp, vp, vp, vp, f32, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
+    lib.dflash_gqa_materialize.restype = i32
+    lib.dflash_gqa_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+    lib.dflash_gqa_workspace_bytes.restype = sz
+    lib.dflash_gqa_forward_block.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                             i64, i64, i64, f32, vp, sz, vp]
+    lib.dflash_gqa_forward_block.restype = i32
     lib.dflash_mla_block_occupancy.argtypes = [vp, vp, i64, i64, i64, i64, vp, sz, vp]
     lib.dflash_mla_block_occupancy.restype = i32
     lib.dflash_mla_attn_blocks.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64,
@@ -451,3 +459,65 @@ def kv_project(ctx_hidden: Optional[torch.Tensor], noise_hidden: torch.Tensor, w
                                      _ptr(w_kv_b), _ptr(kn), _ptr(kr), _ptr(v), B, ctx, Lq, hidden, R, Dr, H, 128, 128,
                                      _ptr(workspace), workspace.numel(), _stream(noise_hidden)))
     return kn, kr, v
+
+
+def _rope_array(rope):
+    """(theta, factor, original_max_position, beta_fast, beta_slow, mscale, mscale_all_dim)."""
+    vals = [float(x) for x in rope]
+    if len(vals) != 7:
+        raise ValueError("rope takes 7 values")
+    return (ctypes.c_float * 7)(*vals)
+
+
+def gqa_new_cache(B: int, Hkv: int, Lmax: int, device):
+    """(k_cache [B, Hkv, Lmax, 128], v_cache_t [B, Hkv, 128, Lmax]) bf16, uninitialised."""
+    return (torch.empty((B, Hkv, Lmax, 128), dtype=torch.bfloat16, device=device),
+            torch.empty((B, Hkv, 128, Lmax), dtype=torch.bfloat16, device=device))
+
+
+def gqa_materialize(ctx_hidden: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor, gamma_k: torch.Tensor,
+                    eps: float, rope, k_cache: torch.Tensor, v_cache_t: torch.Tensor) -> None:
+    """Write the context's qk-normed, yarn-RoPE'd keys and its values into the caches."""
+    lib = load_library()
+    _dev(ctx_hidden, "ctx_hidden", dtype=torch.bfloat16, ndim=3)
+    for t, n in ((w_k, "w_k"), (w_v, "w_v")):
+        _dev(t, n, dtype=torch.bfloat16, ndim=2)
+    _dev(gamma_k, "gamma_k", dtype=torch.bfloat16, ndim=1)
+    _dev(k_cache, "k_cache", dtype=torch.bfloat16, ndim=4)
+    _dev(v_cache_t, "v_cache_t", dtype=torch.bfloat16, ndim=4)
+    B, Lc, hidden = ctx_hidden.shape
+    _, Hkv, Lmax, hd = k_cache.shape
+    if tuple(v_cache_t.shape) != (B, Hkv, hd, Lmax) or tuple(w_k.shape) != (Hkv * hd, hidden) or w_v.shape != w_k.shape:
+        raise ValueError("inconsistent cache / weight shapes")
+    _check(lib.dflash_gqa_materialize(_ptr(ctx_hidden), _ptr(w_k), _ptr(w_v), _ptr(gamma_k), float(eps),
+                                      ctypes.cast(_rope_array(rope), ctypes.c_void_p), _ptr(k_cache), _ptr(v_cache_t),
+                                      B, Lc, Lmax, hidden, Hkv, hd, _stream(ctx_hidden)))
+
+
+def gqa_forward_block(blk_hidden: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor,
+                      gamma_q: torch.Tensor, gamma_k: torch.Tensor, eps: float, rope, k_cache: torch.Tensor,
+                      v_cache_t: torch.Tensor, ctx_len: torch.Tensor, Hq: int, scale: Optional[float] = None, *,
+                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """A block over [cached context | itself]: appends the block's k / v to the caches
+    at ctx_len (int32 [B], device) and returns the attention output [B, Hq, bs, 128]."""
+    lib = load_library()
+    _dev(blk_hidden, "blk_hidden", dtype=torch.bfloat16, ndim=3)
+    _dev(ctx_len, "ctx_len", dtype=torch.int32, ndim=1)
+    B, bs, hidden = blk_hidden.shape
+    _, Hkv, Lmax, hd = k_cache.shape
+    if scale is None:
+        scale = hd ** -0.5
+    if out is None:
+        out = torch.empty((B, Hq, bs, hd), dtype=torch.bfloat16, device=blk_hidden.device)
+    _dev(out, "out", dtype=torch.bfloat16, ndim=4)
+    if workspace is None:
+        n = int(lib.dflash_gqa_workspace_bytes(B, bs, Hq, Hkv, Lmax))
+        if n == 0:
+            raise ValueError("invalid sizes for the block attention")
+        workspace = torch.empty(n, dtype=torch.uint8, device=blk_hidden.device)
+    _dev(workspace, "workspace", dtype=torch.uint8)
+    _check(lib.dflash_gqa_forward_block(_ptr(blk_hidden), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(gamma_q), _ptr(gamma_k),
+                                        float(eps), ctypes.cast(_rope_array(rope), ctypes.c_void_p), _ptr(k_cache),
+                                        _ptr(v_cache_t), _ptr(ctx_len), _ptr(out), B, bs, Lmax, hidden, Hq, Hkv, hd,
+                                        float(scale), _ptr(workspace), workspace.numel(), _stream(blk_hidden)))
+    return out

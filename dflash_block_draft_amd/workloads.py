@@ -243,3 +243,38 @@ def projection_inputs(seed: int, B: int, ctx: int, Lq: int, H: int, hidden: int 
         "B": B, "ctx": ctx, "Lq": Lq, "H": H, "hidden": hidden, "q_lora_rank": q_lora_rank, "R": R, "Dr": Dr,
         "eps": RMS_EPS,
     }
+
+
+# --------------------------------------------------------------------------
+# the MHA/GQA draft (Modular MAX page) -- materialised context + block attention
+# --------------------------------------------------------------------------
+
+# The page gives the config fields, not their values.  Readings: the target's
+# hidden 7168; 32 query heads over 8 KV heads of 128; block size 16; yarn RoPE
+# with theta 50000, factor 32 over an original 4096 positions, beta_fast 32,
+# beta_slow 1, mscale = mscale_all_dim = 1 (the Kimi K2 family's values).
+GQA_ROPE = (50000.0, 32.0, 4096.0, 32.0, 1.0, 1.0, 1.0)
+
+
+def gqa_inputs(seed: int, B: int, Lc: int, bs: int, hidden: int, Hq: int, Hkv: int, ctx_len=None,
+               Lmax: Optional[int] = None, d: int = 128) -> dict:
+    """Hidden states N(0,1), projections N(0, 0.02^2), qk-norm weights 1 + N(0, 0.1^2),
+    all bf16; ctx_len[b] (default: uniform in [Lc/2, Lc]) int32."""
+    rng = np.random.default_rng(seed)
+    if ctx_len is None:
+        ctx_len = rng.integers(Lc // 2, Lc + 1, size=B)
+    ctx_len = np.asarray(ctx_len, dtype=np.int32)
+    if Lmax is None:
+        Lmax = -(-(Lc + bs) // 8) * 8
+    return {
+        "ctx_hidden": normal(rng, (B, Lc, hidden), 1.0, "bf16"),
+        "blk_hidden": normal(rng, (B, bs, hidden), 1.0, "bf16"),
+        "w_q": normal(rng, (Hq * d, hidden), 0.02, "bf16"),
+        "w_k": normal(rng, (Hkv * d, hidden), 0.02, "bf16"),
+        "w_v": normal(rng, (Hkv * d, hidden), 0.02, "bf16"),
+        "g_q": (1.0 + normal(rng, (d,), 0.1, "f32")).to(torch.bfloat16),
+        "g_k": (1.0 + normal(rng, (d,), 0.1, "f32")).to(torch.bfloat16),
+        "ctx_len": torch.from_numpy(ctx_len),
+        "B": B, "Lc": Lc, "bs": bs, "hidden": hidden, "Hq": Hq, "Hkv": Hkv, "Lmax": Lmax, "d": d,
+        "eps": RMS_EPS, "rope": GQA_ROPE,
+    }

@@ -315,6 +315,58 @@ dflash_status dflash_mla_kv_project(const void* ctx_hidden, const void* noise_hi
                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ---- The MHA/GQA DFlash draft (Modular MAX page, pipelines.architectures.dflash_kimi_k25) ----
+ *
+ * A DFlash draft for a Kimi K2.5 target whose own attention is MHA/GQA with
+ * DeepSeek-yarn RoPE and qk-norm; the context's keys and values are written once
+ * into a bf16 cache (DFlashKimiK25.materialize) and each block then attends
+ * non-causally to that cache plus itself (DFlashKimiK25.forward_block).
+ *
+ * Cache layout (caller-owned, bf16): k_cache [B, Hkv, Lmax, 128]; v_cache_t
+ * [B, Hkv, 128, Lmax] (V transposed: keys contiguous per dimension, so the
+ * attention reads V^T operands without transposing).  Lmax a multiple of 8.
+ * rope: host array of 7 floats {theta, factor, original_max_position,
+ * beta_fast, beta_slow, mscale, mscale_all_dim}; yarn inverse frequencies
+ * blend 1/theta^(2i/128) and that divided by factor with a linear ramp between
+ * the correction dimensions of beta_fast and beta_slow rotations, and cos/sin
+ * are scaled by m(factor, mscale) / m(factor, mscale_all_dim), m(s, x) =
+ * 0.1 x ln s + 1 (1 for s <= 1).  RoPE pairs dimension i with i + 64
+ * (rotate-half).  qk-norm: RMSNorm over the 128 dims of every head
+ * (fp32 variance; weight [128]) before RoPE.  Projections are bf16 MFMA with
+ * fp32 accumulation (weights [out, in]); the attention uses scale `scale`.
+ * head_dim must be 128.  Errors as for the projections.
+ */
+
+/* k_cache[b, :, t] = RoPE(qk-norm(ctx_hidden[b, t] . w_k^T)) at position t, and
+ * v_cache_t[b, :, :, t] = ctx_hidden[b, t] . w_v^T, for t < Lc (<= Lmax).
+ * ctx_hidden [B, Lc, hidden], w_k / w_v [Hkv * 128, hidden], gamma_k [128]. */
+dflash_status dflash_gqa_materialize(const void* ctx_hidden, const void* w_k, const void* w_v,
+                                     const void* gamma_k, float eps, const float* rope, void* k_cache,
+                                     void* v_cache_t, int64_t B, int64_t Lc, int64_t Lmax, int64_t hidden,
+                                     int64_t Hkv, int64_t head_dim, void* stream);
+
+/* Workspace bytes of dflash_gqa_forward_block (the block's q and the split-K
+ * partials); 0 for invalid sizes. */
+size_t dflash_gqa_workspace_bytes(int64_t B, int64_t bs, int64_t Hq, int64_t Hkv, int64_t Lmax);
+
+/* One draft block per batch row: with c = clamp(ctx_len[b], 0, Lmax - bs)
+ * (ctx_len: int32 [B], device) and positions c + i for block token i:
+ *   q = RoPE(qk-norm(blk_hidden . w_q^T)) per head            ([B, Hq, bs, 128])
+ *   the block's k, v (as dflash_gqa_materialize) are written into the caches at
+ *   times c .. c + bs - 1
+ *   out[b, h, i] = softmax_j(scale * q . k_cache[b, h / (Hq/Hkv), j]) v_j over the
+ *   keys j < c + bs (the context and the whole block: non-causal)
+ * blk_hidden [B, bs, hidden], w_q [Hq * 128, hidden], gamma_q / gamma_k [128],
+ * out [B, Hq, bs, 128] bf16.  Hq a multiple of Hkv and (Hq / Hkv) * bs <= 64.
+ * The caches are modified (the block's rows); calls on overlapping caches race. */
+dflash_status dflash_gqa_forward_block(const void* blk_hidden, const void* w_q, const void* w_k,
+                                       const void* w_v, const void* gamma_q, const void* gamma_k, float eps,
+                                       const float* rope, void* k_cache, void* v_cache_t,
+                                       const int32_t* ctx_len, void* out, int64_t B, int64_t bs, int64_t Lmax,
+                                       int64_t hidden, int64_t Hq, int64_t Hkv, int64_t head_dim, float scale,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The tile map of the DFlash block mask computed from the block structure itself
  * instead of a dense mask: no mask bytes are read.  Row b, query i belongs to
  * block j = i / block_size and sees context key k (k < ctx) iff
