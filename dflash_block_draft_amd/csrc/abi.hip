@@ -555,10 +555,21 @@ dflash_status dflash_mla_attn_bwd(const void* q, const void* k_nope, const void*
 
 // ---------------------------------------------------------------- projections
 
+// intermediate [rows, width] bf16, its row statistics, and split-K scratch for the
+// product that makes the intermediate (capped at 64 MiB: larger products fill
+// the chip without splitting)
+static size_t proj_split_bytes(int64_t rows, int64_t width) {
+  const size_t full = static_cast<size_t>(dflash::kLinearMaxSplits) * rows * width * 4;
+  return std::min<size_t>(full, size_t(64) << 20);
+}
+
 size_t dflash_mla_projection_workspace_bytes(int64_t rows, int64_t width) {
   int64_t e, st;
-  if (rows <= 0 || width <= 0 || !mul_ok(rows, width, &e) || !mul_ok(rows, (width + 127) / 128, &st)) return 0;
-  return align_up(static_cast<size_t>(e) * 2, 256) + align_up(static_cast<size_t>(st) * 4, 256);
+  if (rows <= 0 || width <= 0 || !mul_ok(rows, width, &e) || !mul_ok(rows, (width + 127) / 128, &st) ||
+      !mul_ok(e, 64, &st))
+    return 0;
+  return align_up(static_cast<size_t>(e) * 2, 256) + align_up(static_cast<size_t>(rows) * ((width + 127) / 128) * 4, 256) +
+         align_up(proj_split_bytes(rows, width), 256);
 }
 
 }  // extern "C"
@@ -675,7 +686,9 @@ dflash_status dflash_mla_q_project(const void* x, const void* w_q_a, const void*
   l.y1 = qa;
   l.stats_out = stats;
   l.Nstat = static_cast<int>(q_lora_rank);
-  st = hip_status(dflash::launch_linear_bf16(l, s), "q_a_proj launch");
+  float* split = reinterpret_cast<float*>(reinterpret_cast<char*>(stats) +
+                                          align_up(static_cast<size_t>(M) * (q_lora_rank / 128) * 4, 256));
+  st = hip_status(dflash::launch_linear_bf16(l, s, split, proj_split_bytes(M, q_lora_rank)), "q_a_proj launch");
   if (st != DFLASH_OK) return st;
   dflash::LinearArgs l2 = linear_args();
   l2.a1 = qa;
@@ -781,7 +794,9 @@ bool gqa_layout(int64_t B, int64_t bs, int64_t Hq, int64_t Hkv, int64_t Lmax, si
   *q_off = 0;
   *o_off = align_up(static_cast<size_t>(B) * Hq * bs * 128 * 2, 256);
   *ml_off = *o_off + align_up(rows * 128 * 4, 256);
-  *total = *ml_off + align_up(rows * 2 * 4, 256);
+  // split-K scratch for the block's projections (the widest is q: B*bs rows x Hq*128)
+  *total = *ml_off + align_up(rows * 2 * 4, 256) +
+           align_up(static_cast<size_t>(dflash::kLinearMaxSplits) * B * bs * Hq * 128 * 4, 256);
   return true;
 }
 
@@ -914,6 +929,9 @@ dflash_status dflash_gqa_forward_block(const void* blk_hidden, const void* w_q, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   uint16_t* qbuf = reinterpret_cast<uint16_t*>(ws + qo);
+  const size_t split_off = mlo + align_up(static_cast<size_t>(B) * Hkv * gqa_split(B, Hkv, Lmax).splits * 64 * 2 * 4, 256);
+  float* split = reinterpret_cast<float*>(ws + split_off);
+  const size_t split_bytes = need - split_off;
   const int off_max = static_cast<int>(Lmax - bs);
   // q: projection, then qk-norm + RoPE at positions ctx_len + t
   dflash::LinearArgs l = linear_args();
@@ -926,7 +944,7 @@ dflash_status dflash_gqa_forward_block(const void* blk_hidden, const void* w_q, 
   l.mode = dflash::kLinearHeads;
   l.D = 128;
   l.y1 = qbuf;
-  st = hip_status(dflash::launch_linear_bf16(l, s), "q projection launch");
+  st = hip_status(dflash::launch_linear_bf16(l, s, split, split_bytes), "q projection launch");
   if (st != DFLASH_OK) return st;
   dflash::NormRopeArgs n = norm_rope_args(rope, gamma_q, eps);
   n.x = qbuf;
@@ -946,7 +964,7 @@ dflash_status dflash_gqa_forward_block(const void* blk_hidden, const void* w_q, 
   l.Lt = static_cast<int>(Lmax);
   l.row_off = ctx_len;
   l.off_max = off_max;
-  st = hip_status(dflash::launch_linear_bf16(l, s), "k projection launch");
+  st = hip_status(dflash::launch_linear_bf16(l, s, split, split_bytes), "k projection launch");
   if (st != DFLASH_OK) return st;
   dflash::NormRopeArgs nk = norm_rope_args(rope, gamma_k, eps);
   nk.x = static_cast<uint16_t*>(k_cache);
@@ -961,7 +979,7 @@ dflash_status dflash_gqa_forward_block(const void* blk_hidden, const void* w_q, 
   l.w = static_cast<const uint16_t*>(w_v);
   l.mode = dflash::kLinearHeadsT;
   l.y1 = static_cast<uint16_t*>(v_cache_t);
-  st = hip_status(dflash::launch_linear_bf16(l, s), "v projection launch");
+  st = hip_status(dflash::launch_linear_bf16(l, s, split, split_bytes), "v projection launch");
   if (st != DFLASH_OK) return st;
   const GqaSplit sp = gqa_split(B, Hkv, Lmax);
   dflash::GqaAttnArgs g = {};

@@ -3,11 +3,12 @@
 // place to head-major rows, and block attention of the draft's queries over the
 // bf16 KV cache that holds the materialised context plus the block itself.
 //
-// norm_rope: one workgroup per (token, batch row), one wave per head row of 128:
-// lane l holds entries l and l + 64, which are exactly a rotate-half pair, so the
-// RMSNorm reduction is one wave sum and the rotation needs no data movement.  The
-// 64 angles of the token are formed once per workgroup in fp64 (yarn frequency,
-// position times frequency reduced modulo 2 pi) and shared through LDS.
+// norm_rope: one workgroup per 4 tokens of a batch row, one wave per head row of
+// 128: lane l holds entries l and l + 64, which are exactly a rotate-half pair, so
+// the RMSNorm reduction is one wave sum and the rotation needs no data movement.
+// The yarn frequencies are formed once per workgroup in fp64, each angle
+// (position times frequency) is reduced modulo 2 pi in fp64 and only then taken
+// through fp32 sin / cos, so large positions lose no accuracy.
 //
 // gqa_attn: the cache is read once per KV head for its whole query group (g heads
 // x bs block tokens <= 64 query rows), so each key byte feeds 64 rows: the
@@ -63,29 +64,43 @@ __device__ double yarn_inv_freq(int i, const NormRopeArgs& a) {
 
 __device__ double yarn_mscale(double scale, double m) { return scale <= 1.0 ? 1.0 : 0.1 * m * log(scale) + 1.0; }
 
+constexpr int kRopeTok = 4;                    // tokens per norm/rope workgroup
+
 __global__ void __launch_bounds__(256) norm_rope_bf16(NormRopeArgs a) {
-  __shared__ float s_cos[kD / 2], s_sin[kD / 2];
-  const int t = blockIdx.x, b = blockIdx.y;
+  __shared__ double s_inv[kD / 2];
+  __shared__ float s_cos[kRopeTok][kD / 2], s_sin[kRopeTok][kD / 2];
+  const int b = blockIdx.y;
+  const int tbase = blockIdx.x * kRopeTok;
   const int t0 = a.row_off ? min(max(a.row_off[b], 0), a.off_max) : 0;
-  const int ti = t0 + t;
-  if (threadIdx.x < kD / 2) {
-    const double ms = yarn_mscale(a.factor, a.mscale) / yarn_mscale(a.factor, a.mscale_all_dim);
-    const double ang = fmod(static_cast<double>(ti) * yarn_inv_freq(threadIdx.x, a), 6.283185307179586);
-    s_cos[threadIdx.x] = static_cast<float>(cos(ang) * ms);
-    s_sin[threadIdx.x] = static_cast<float>(sin(ang) * ms);
+  if (threadIdx.x < kD / 2) s_inv[threadIdx.x] = yarn_inv_freq(threadIdx.x, a);
+  __syncthreads();
+  {  // one angle per thread: the product and its reduction modulo 2 pi in fp64, sin / cos in fp32
+    const int tk = threadIdx.x / (kD / 2), i = threadIdx.x % (kD / 2);
+    const double two_pi = 6.283185307179586;
+    const double ang = static_cast<double>(t0 + tbase + tk) * s_inv[i];
+    const float red = static_cast<float>(ang - floor(ang / two_pi) * two_pi);
+    const float ms = static_cast<float>(yarn_mscale(a.factor, a.mscale) / yarn_mscale(a.factor, a.mscale_all_dim));
+    float sn, cs;
+    sincosf(red, &sn, &cs);
+    s_cos[tk][i] = cs * ms;
+    s_sin[tk][i] = sn * ms;
   }
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float g0 = bf16_bits_to_f32(a.gamma[lane]), g1 = bf16_bits_to_f32(a.gamma[lane + 64]);
-  const float c = s_cos[lane], sn = s_sin[lane];
-  for (int h = wave; h < a.H; h += 4) {
-    uint16_t* row = a.x + ((static_cast<size_t>(b) * a.H + h) * a.Lt + (a.rows_local ? t : ti)) * kD;
+  for (int job = wave; job < kRopeTok * a.H; job += 4) {
+    const int tk = job / a.H, h = job % a.H;
+    const int t = tbase + tk;
+    if (t >= a.T) break;                              // jobs are token-major: the rest are past T too
+    const int row_t = a.rows_local ? t : t0 + t;
+    uint16_t* row = a.x + ((static_cast<size_t>(b) * a.H + h) * a.Lt + row_t) * kD;
     const float x0 = bf16_bits_to_f32(row[lane]), x1 = bf16_bits_to_f32(row[lane + 64]);
     float ss = x0 * x0 + x1 * x1;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
     const float r = rsqrtf(ss / kD + a.eps);
     const float n0 = bf16r(bf16r(x0 * r) * g0), n1 = bf16r(bf16r(x1 * r) * g1);
+    const float c = s_cos[tk][lane], sn = s_sin[tk][lane];
     const uint32_t w = pack_bf16x2(n0 * c - n1 * sn, n1 * c + n0 * sn);
     row[lane] = static_cast<uint16_t>(w & 0xFFFFu);
     row[lane + 64] = static_cast<uint16_t>(w >> 16);
@@ -299,7 +314,7 @@ __global__ void __launch_bounds__(kD) gqa_combine_bf16(GqaAttnArgs a) {
 }  // namespace
 
 hipError_t launch_norm_rope_bf16(const NormRopeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(norm_rope_bf16, dim3(a.T, a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(norm_rope_bf16, dim3((a.T + kRopeTok - 1) / kRopeTok, a.B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -98,6 +98,7 @@ struct LinearArgs {
   // head-major modes: time index of row t of batch row b is off(b) + t in a time
   // axis of Lt entries (Lt = 0: T1 + T2 and no offset); off(b) = clamp(row_off[b], 0, off_max)
   const int32_t* row_off; int off_max; int Lt;
+  float* split_part;                 // set by the launcher for split-K runs: [splits, M, N] fp32
 };
 
 // In-place qk-norm + yarn RoPE of rows of a head-major tensor x [B, H, Lt, d]:
@@ -127,7 +128,12 @@ struct RmsApplyArgs {
   const float* stats; int parts; const uint16_t* gamma; float eps;
 };
 
-hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t s);
+// scratch (may be null): fp32 space for split-K partials; the launcher splits K
+// across workgroups (then reduces the partials in order) when the output tiles
+// alone cannot fill the chip and the scratch holds linear_split_bytes(a) bytes.
+hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t s, float* scratch = nullptr, size_t scratch_bytes = 0);
+size_t linear_split_bytes(const LinearArgs& a);
+constexpr int kLinearMaxSplits = 16;
 hipError_t launch_norm_rope_bf16(const NormRopeArgs& a, hipStream_t s);
 hipError_t launch_gqa_attn_bf16(const GqaAttnArgs& a, hipStream_t s);
 hipError_t launch_rms_apply_bf16(const RmsApplyArgs& a, hipStream_t s);

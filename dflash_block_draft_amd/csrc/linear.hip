@@ -45,6 +45,37 @@ struct Tile {
 using BigTile = Tile<256, 256, 64, 4, 2>;     // 8 waves, 64 x 128 each
 using SmallTile = Tile<128, 128, 32, 2, 2>;   // 4 waves, 64 x 64 each
 
+// Store four consecutive bf16 outputs n .. n + 3 of row m (batch row b, time tt)
+// in the layout of the output mode.
+__device__ __forceinline__ void emit4(const LinearArgs& a, int64_t m, int64_t b, int tt, int T, int n, uint32_t p0,
+                                      uint32_t p1) {
+  uint16_t* dst;
+  if (a.mode == kLinearPlain) {
+    dst = a.y1 + static_cast<size_t>(m) * a.N + n;
+  } else if (a.mode == kLinearSplit) {
+    dst = n < a.N1 ? a.y1 + static_cast<size_t>(m) * a.N1 + n
+                   : a.y2 + static_cast<size_t>(m) * (a.N - a.N1) + (n - a.N1);
+  } else if (a.mode == kLinearHeads || a.mode == kLinearHeadsT) {
+    const int h = n / a.D, d = n % a.D;
+    const int Lt = a.Lt ? a.Lt : T;
+    const int ti = (a.row_off ? min(max(a.row_off[b], 0), a.off_max) : 0) + tt;
+    const size_t bh = static_cast<size_t>(b) * (a.N / a.D) + h;
+    if (a.mode == kLinearHeadsT) {                  // [B, N / D, D, Lt]
+      uint16_t* col = a.y1 + (bh * a.D + d) * Lt + ti;
+      col[0] = static_cast<uint16_t>(p0 & 0xFFFFu);
+      col[Lt] = static_cast<uint16_t>(p0 >> 16);
+      col[2 * static_cast<size_t>(Lt)] = static_cast<uint16_t>(p1 & 0xFFFFu);
+      col[3 * static_cast<size_t>(Lt)] = static_cast<uint16_t>(p1 >> 16);
+      return;
+    }
+    dst = a.y1 + (bh * Lt + ti) * a.D + d;          // [B, N / D, Lt, D]
+  } else {                                          // kv: per head [k_nope (128) | v (128)]
+    const int h = n >> 8, e = n & 255;
+    dst = (e < kDn ? a.y1 : a.y2) + ((static_cast<size_t>(b) * (a.N >> 8) + h) * T + tt) * kDn + (e & 127);
+  }
+  *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{p0, p1};
+}
+
 template <int NT, int MT, int KS, int WN, int WM>
 __global__ void __launch_bounds__(64 * WN * WM) linear_bf16(LinearArgs a) {
   using TL = Tile<NT, MT, KS, WN, WM>;
@@ -112,13 +143,15 @@ __global__ void __launch_bounds__(64 * WN * WM) linear_bf16(LinearArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = a.K / KS;
-  load(0);
+  const int kc = a.split_part ? a.K / gridDim.z : a.K;   // this workgroup's share of K
+  const int kbeg = blockIdx.z * kc;
+  const int nk = kc / KS;
+  load(kbeg);
   store(smem);
   __syncthreads();
   for (int it = 0; it < nk; ++it) {
     const bool more = it + 1 < nk;
-    if (more) load((it + 1) * KS);
+    if (more) load(kbeg + (it + 1) * KS);
     const uint16_t* Ws = smem + (it & 1) * TL::kStage;
     const uint16_t* Ls = Ws + NT * ROW;
 #pragma unroll
@@ -141,6 +174,24 @@ __global__ void __launch_bounds__(64 * WN * WM) linear_bf16(LinearArgs a) {
 
   // epilogue: lane owns row m (column li of sub-tile j) and outputs
   // n = n0 + (NT/WN)*wn + 32*i + 8*g + 4*hi + 0..3 (registers 4g + 0..3 of acc[i][j])
+  if (a.split_part) {                                 // split K: fp32 partials, reduced in order later
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int64_t m = m0 + (MT / WM) * wm + 32 * j + li;
+      if (m >= M) continue;
+      float* prow = a.split_part + (static_cast<size_t>(blockIdx.z) * M + m) * a.N;
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + (NT / WN) * wn + 32 * i + 8 * g + 4 * hi;
+          if (n < a.N)
+            *reinterpret_cast<f32x4_t*>(prow + n) =
+                f32x4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        }
+    }
+    return;
+  }
   const bool stats = a.stats_out && n0 < a.Nstat;
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
@@ -162,34 +213,7 @@ __global__ void __launch_bounds__(64 * WN * WM) linear_bf16(LinearArgs a) {
           const float x0 = bf16_bits_to_f32(p0 & 0xFFFFu), x1 = bf16_bits_to_f32(p0 >> 16);
           const float x2 = bf16_bits_to_f32(p1 & 0xFFFFu), x3 = bf16_bits_to_f32(p1 >> 16);
           ssq += x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
-          if (mok) {
-            uint16_t* dst;
-            if (a.mode == kLinearPlain) {
-              dst = a.y1 + static_cast<size_t>(m) * a.N + n;
-            } else if (a.mode == kLinearSplit) {
-              dst = n < a.N1 ? a.y1 + static_cast<size_t>(m) * a.N1 + n
-                             : a.y2 + static_cast<size_t>(m) * (a.N - a.N1) + (n - a.N1);
-            } else if (a.mode == kLinearHeads || a.mode == kLinearHeadsT) {
-              const int h = n / a.D, d = n % a.D;
-              const int Lt = a.Lt ? a.Lt : T;
-              const int ti = (a.row_off ? min(max(a.row_off[b], 0), a.off_max) : 0) + tt;
-              const size_t bh = static_cast<size_t>(b) * (a.N / a.D) + h;
-              if (a.mode == kLinearHeads) {            // [B, N / D, Lt, D]
-                dst = a.y1 + (bh * Lt + ti) * a.D + d;
-              } else {                                 // [B, N / D, D, Lt]
-                uint16_t* col = a.y1 + (bh * a.D + d) * Lt + ti;
-                col[0] = static_cast<uint16_t>(p0 & 0xFFFFu);
-                col[Lt] = static_cast<uint16_t>(p0 >> 16);
-                col[2 * static_cast<size_t>(Lt)] = static_cast<uint16_t>(p1 & 0xFFFFu);
-                col[3 * static_cast<size_t>(Lt)] = static_cast<uint16_t>(p1 >> 16);
-                continue;
-              }
-            } else {                                   // kv: per head [k_nope (128) | v (128)]
-              const int h = n >> 8, e = n & 255;
-              dst = (e < kDn ? a.y1 : a.y2) + ((static_cast<size_t>(b) * (a.N >> 8) + h) * T + tt) * kDn + (e & 127);
-            }
-            *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{p0, p1};
-          }
+          if (mok) emit4(a, m, b, tt, T, n, p0, p1);
         }
       }
     if (stats) {
@@ -207,6 +231,38 @@ __global__ void __launch_bounds__(64 * WN * WM) linear_bf16(LinearArgs a) {
       const int64_t m = m0 + r;
       if (m < M && part < parts) a.stats_out[m * parts + part] = s_part[2 * gi][r] + s_part[2 * gi + 1][r];
     }
+  }
+}
+
+// Split-K reduction: the partials of each output are summed in split order and
+// the result goes through the same epilogue (rounding, layout, statistics).  One
+// thread per row and 4 columns; 32 threads cover one 128-column group.
+__global__ void __launch_bounds__(256) linear_split_reduce(LinearArgs a, int splits) {
+  const int T = a.T1 + a.T2;
+  const int64_t M = static_cast<int64_t>(a.B) * T;
+  const int groups = (a.N + 127) / 128;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
+  if (gid >= M * groups) return;                    // whole 32-thread groups leave together
+  const int l32 = threadIdx.x & 31;
+  const int64_t m = gid / groups;
+  const int grp = static_cast<int>(gid % groups);
+  const int n = grp * 128 + 4 * l32;
+  const int64_t b = m / T;
+  const int tt = static_cast<int>(m % T);
+  float ssq = 0.f;
+  if (n < a.N) {
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+    for (int z = 0; z < splits; ++z) v += *reinterpret_cast<const f32x4_t*>(a.split_part + (static_cast<size_t>(z) * M + m) * a.N + n);
+    const uint32_t p0 = pack_bf16x2(v[0], v[1]), p1 = pack_bf16x2(v[2], v[3]);
+    const float x0 = bf16_bits_to_f32(p0 & 0xFFFFu), x1 = bf16_bits_to_f32(p0 >> 16);
+    const float x2 = bf16_bits_to_f32(p1 & 0xFFFFu), x3 = bf16_bits_to_f32(p1 >> 16);
+    ssq = x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
+    emit4(a, m, b, tt, T, n, p0, p1);
+  }
+  if (a.stats_out && grp * 128 < a.Nstat) {
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) ssq += __shfl_xor(ssq, o);
+    if (l32 == 0) a.stats_out[m * (a.Nstat / 128) + grp] = ssq;
   }
 }
 
@@ -239,8 +295,39 @@ static bool linear_big_tile(const LinearArgs& a) {
   return rounds >= 4 || tiles * 100 >= rounds * 256 * 85;
 }
 
-hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t s) {
+// Splits of K when the 128 x 128 output tiles cannot fill the chip on their own:
+// double while the workgroups stay under ~2 per CU and every split keeps >= 256
+// of K in whole 32-wide stages.
+static int linear_splits(const LinearArgs& a) {
+  if (linear_big_tile(a)) return 1;
   const int64_t M = static_cast<int64_t>(a.B) * (a.T1 + a.T2);
+  const int64_t tiles = ((M + 127) / 128) * ((a.N + 127) / 128);
+  int sp = 1;
+  while (sp * 2 <= kLinearMaxSplits && tiles * sp * 2 <= 512 && a.K % (32 * sp * 2) == 0 && a.K / (sp * 2) >= 256)
+    sp *= 2;
+  return sp;
+}
+
+size_t linear_split_bytes(const LinearArgs& a) {
+  const int sp = linear_splits(a);
+  const int64_t M = static_cast<int64_t>(a.B) * (a.T1 + a.T2);
+  return sp > 1 ? static_cast<size_t>(sp) * M * a.N * 4 : 0;
+}
+
+hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t s, float* scratch, size_t scratch_bytes) {
+  const int64_t M = static_cast<int64_t>(a.B) * (a.T1 + a.T2);
+  const int sp = linear_splits(a);
+  if (sp > 1 && scratch && scratch_bytes >= linear_split_bytes(a)) {
+    LinearArgs b = a;
+    b.split_part = scratch;
+    const dim3 grid(static_cast<unsigned>((M + 127) / 128), static_cast<unsigned>((a.N + 127) / 128), sp);
+    hipLaunchKernelGGL((linear_bf16<128, 128, 32, 2, 2>), grid, dim3(SmallTile::kThreads), 0, s, b);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t items = M * ((a.N + 127) / 128);
+    hipLaunchKernelGGL(linear_split_reduce, dim3(static_cast<unsigned>((items + 7) / 8)), dim3(256), 0, s, b, sp);
+    return hipGetLastError();
+  }
   if (linear_big_tile(a)) {
     const dim3 grid(static_cast<unsigned>((M + 255) / 256), static_cast<unsigned>((a.N + 255) / 256));
     hipLaunchKernelGGL((linear_bf16<256, 256, 64, 4, 2>), grid, dim3(BigTile::kThreads), 0, s, a);

@@ -74,6 +74,7 @@ CASES = [
     ("gqa4_bs16_no_ctx", 2, 64, 16, 192, 8, 2, [0, 64], 0),
     ("gqa8_bs8_clamped", 2, 200, 8, 160, 16, 2, [200, 5000], 0),
     ("long", 1, 4100, 16, 256, 8, 2, [4100], 0),
+    ("split_k_projections", 2, 300, 16, 2048, 8, 2, [300, 111], 0),   # hidden 2048: K split across workgroups
 ]
 
 

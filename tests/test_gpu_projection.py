@@ -59,7 +59,8 @@ def test_context_project(dev, shape):
     _check("context", out, oracle.context_project(p["target_hidden"], p["w_fc"], p["g_hidden"], p["eps"]))
 
 
-@pytest.mark.parametrize("shape", [(2, 100, 70, 3, 160, 256), (1, 64, 129, 2, 256, 384)])
+@pytest.mark.parametrize("shape", [(2, 100, 70, 3, 160, 256), (1, 64, 129, 2, 256, 384),
+                                   (2, 16, 70, 2, 2048, 256)])   # few output tiles, long K: split-K
 def test_q_project(dev, shape):
     B, ctx, Lq, H, hidden, rq = shape
     p = _small(81, B, ctx, Lq, H, hidden, rq)
