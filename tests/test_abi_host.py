@@ -275,3 +275,29 @@ def test_projection_validation(lib):
     assert kvp(*bad) == 2                                   # Dn
     bad = list(args); bad[6] = FAKE * 8
     assert kvp(*bad) == 1                                   # k_nope overlaps v
+
+
+def test_gqa_validation(lib):
+    import ctypes as C
+    rope = (C.c_float * 7)(50000.0, 32.0, 4096.0, 32.0, 1.0, 1.0, 1.0)
+    bad_rope = (C.c_float * 7)(0.5, 32.0, 4096.0, 32.0, 1.0, 1.0, 1.0)
+    mat = lib.dflash_gqa_materialize
+    # (ctx, wk, wv, gk, eps, rope, kc, vc, B, Lc, Lmax, hidden, Hkv, hd, stream)
+    good = [FAKE, FAKE * 2, FAKE * 3, FAKE * 4, 1e-6, C.cast(rope, C.c_void_p), FAKE * 64, FAKE * 128,
+            1, 64, 128, 256, 2, 128, None]
+    for idx, val, status in ((0, None, 1), (5, None, 1), (5, C.cast(bad_rope, C.c_void_p), 1), (9, 200, 1),
+                             (13, 64, 2), (10, 130, 2), (11, 250, 2), (7, FAKE * 64, 1)):
+        args = list(good)
+        args[idx] = val
+        assert mat(*args) == status, (idx, val)
+    fb = lib.dflash_gqa_forward_block
+    # (blk, wq, wk, wv, gq, gk, eps, rope, kc, vc, ctx_len, out, B, bs, Lmax, hidden, Hq, Hkv, hd, scale, ws, wsb, stream)
+    good = [FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, FAKE * 6, 1e-6, C.cast(rope, C.c_void_p), FAKE * 64,
+            FAKE * 128, FAKE * 7, FAKE * 8, 1, 16, 128, 256, 8, 2, 128, 0.088, FAKE * 256, 1 << 26, None]
+    for idx, val, status in ((10, None, 1), (10, FAKE * 7 + 2, 1), (16, 7, 2), (13, 32, 2), (13, 200, 1),
+                             (19, 0.0, 1), (20, None, 3), (21, 64, 3), (11, FAKE * 64, 1)):
+        args = list(good)
+        args[idx] = val
+        assert fb(*args) == status, (idx, val)
+    assert lib.dflash_gqa_workspace_bytes(1, 16, 8, 2, 128) > 0
+    assert lib.dflash_gqa_workspace_bytes(0, 16, 8, 2, 128) == 0
