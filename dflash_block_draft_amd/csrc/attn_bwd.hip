@@ -71,6 +71,16 @@ __device__ __forceinline__ int relabel16(int k) { return (k & 3) | ((k & 4) << 1
 
 __device__ __forceinline__ u32x4_t zero4() { return u32x4_t{0u, 0u, 0u, 0u}; }
 
+// Buffer resource over `bytes` bytes at p: loads at offsets >= bytes return zeros,
+// which is how rows past the end of a tensor read as zero without a compare.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), 0x00020000);
+}
+// 16 bytes at voffset (per lane) + soffset (uniform)
+__device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), 0));
+}
+
 __device__ __forceinline__ bf16x8_t lds_frag(const char* p) { return as_bf16x8(*reinterpret_cast<const u32x4_t*>(p)); }
 
 // 8 floats -> one bf16x8 operand (round to nearest even)
@@ -252,28 +262,38 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv(AttnBwdArgs a) {
     }
   };
 
+  // staging: per-lane byte offsets are fixed, the chunk moves the uniform offset;
+  // rows past Lq read as zeros through the resources' ranges
+  const __amdgpu_buffer_rsrc_t r_q = rsrc(a.q + bh * a.Lq * kDqk, static_cast<size_t>(a.Lq) * kDqk * 2);
+  const __amdgpu_buffer_rsrc_t r_o = rsrc(a.dout + bh * a.Lq * kDv, static_cast<size_t>(a.Lq) * kDv * 2);
+  const __amdgpu_buffer_rsrc_t r_qt = rsrc(a.qT + bh * kDqk * a.Lqp, static_cast<size_t>(kDqk) * a.Lqp * 2);
+  const __amdgpu_buffer_rsrc_t r_ot = rsrc(a.doT + bh * kDv * a.Lqp, static_cast<size_t>(kDv) * a.Lqp * 2);
+  uint32_t voff_q[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int ci = t + kThreads * i;
+    voff_q[i] = (ci / 24) * (kDqk * 2) + (ci % 24) * 16;
+  }
   u32x4_t pre[11];
   auto prefetch = [&](int qt, int c, int cls0, int cls1) {
     const int q0 = qt * kTileM + c * kQC;
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {                     // q rows: 32 x 24 chunks
-      const int ci = t + kThreads * i, r = ci / 24, ch = ci % 24, qi = q0 + r;
-      pre[i] = qi < a.Lq ? ldg16(a.q + (bh * a.Lq + qi) * kDqk + ch * 8) : zero4();
-    }
+    for (int i = 0; i < 3; ++i)                       // q rows: 32 x 24 chunks
+      pre[i] = bload16(r_q, voff_q[i], static_cast<uint32_t>(q0) * (kDqk * 2));
 #pragma unroll
     for (int i = 0; i < 2; ++i) {                     // dout rows: 32 x 16 chunks
-      const int ci = t + kThreads * i, r = ci >> 4, ch = ci & 15, qi = q0 + r;
-      pre[3 + i] = qi < a.Lq ? ldg16(a.dout + (bh * a.Lq + qi) * kDv + ch * 8) : zero4();
+      const int ci = t + kThreads * i;
+      pre[3 + i] = bload16(r_o, (ci >> 4) * (kDv * 2) + (ci & 15) * 16, static_cast<uint32_t>(q0) * (kDv * 2));
     }
 #pragma unroll
     for (int i = 0; i < 3; ++i) {                     // q^T: 192 rows x 4 chunks
-      const int ci = t + kThreads * i, d = ci >> 2, ch = ci & 3;
-      pre[5 + i] = ldg16(a.qT + (bh * kDqk + d) * a.Lqp + q0 + ch * 8);
+      const int ci = t + kThreads * i;
+      pre[5 + i] = bload16(r_qt, (ci >> 2) * (a.Lqp * 2) + (ci & 3) * 16, static_cast<uint32_t>(q0) * 2);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {                     // dout^T: 128 rows x 4 chunks
-      const int ci = t + kThreads * i, d = ci >> 2, ch = ci & 3;
-      pre[8 + i] = ldg16(a.doT + (bh * kDv + d) * a.Lqp + q0 + ch * 8);
+      const int ci = t + kThreads * i;
+      pre[8 + i] = bload16(r_ot, (ci >> 2) * (a.Lqp * 2) + (ci & 3) * 16, static_cast<uint32_t>(q0) * 2);
     }
     pre[10] = zero4();
     if (t < 16) {                                     // lse2 (t < 8), D (8 <= t < 16)
@@ -293,7 +313,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv(AttnBwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
       const int ci = t + kThreads * i;
-      *reinterpret_cast<u32x4_t*>(st + kA_Q + (ci / 24) * kSQ + (ci % 24) * 16) = pre[i];
+      *reinterpret_cast<u32x4_t*>(st + kA_Q + (ci / 24) * kSQ + (ci % 24) * 16) = pre[i];   // (constant per thread)
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -449,36 +469,53 @@ __global__ void __launch_bounds__(kThreads) bwd_dq(AttnBwdArgs a) {
   const int32_t* list = a.lists ? a.lists + static_cast<size_t>(row) * a.nkt : nullptr;
   auto entry = [&](int e) -> int { return list ? list[e] : (e | (1 << 24)); };
 
+  // staging: per-lane byte offsets are fixed, the tile moves the uniform offset
+  const __amdgpu_buffer_rsrc_t r_kn = rsrc(a.kn + bh * a.Lk * kDn, static_cast<size_t>(a.Lk) * kDn * 2);
+  const __amdgpu_buffer_rsrc_t r_kr = rsrc(a.kr + static_cast<size_t>(b) * a.Lk * kDr, static_cast<size_t>(a.Lk) * kDr * 2);
+  const __amdgpu_buffer_rsrc_t r_v = rsrc(a.v + bh * a.Lk * kDv, static_cast<size_t>(a.Lk) * kDv * 2);
+  const __amdgpu_buffer_rsrc_t r_knt = rsrc(a.knT + bh * kDn * a.Lkp, static_cast<size_t>(kDn) * a.Lkp * 2);
+  const __amdgpu_buffer_rsrc_t r_krt = rsrc(a.krT + static_cast<size_t>(b) * kDr * a.Lkp, static_cast<size_t>(kDr) * a.Lkp * 2);
+  // chunk c of this thread's i-th load: K nope rows 64 x 16 (i < 4), K rope rows 64 x 8 (2),
+  // V rows 64 x 16 (4), K^T nope rows 128 x 8 (4), K^T rope rows 64 x 8 (2)
   u32x4_t pre[16];
   auto prefetch = [&](int kt) {
-    const int k0 = kt * kTileN;
+    const uint32_t k0 = static_cast<uint32_t>(kt) * kTileN;
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {                     // K rows: 64 x (16 nope + 8 rope) chunks
-      const int ci = t + kThreads * i, r = ci / 24, ch = ci % 24, kj = k0 + r;
-      u32x4_t x = zero4();
-      if (kj < a.Lk)
-        x = ch < 16 ? ldg16(a.kn + (bh * a.Lk + kj) * kDn + ch * 8)
-                    : ldg16(a.kr + (static_cast<size_t>(b) * a.Lk + kj) * kDr + (ch - 16) * 8);
-      pre[i] = x;
+    for (int i = 0; i < 4; ++i) {
+      const int ci = t + kThreads * i;
+      pre[i] = bload16(r_kn, (ci >> 4) * (kDn * 2) + (ci & 15) * 16, k0 * (kDn * 2));
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {                     // V rows: 64 x 16 chunks
-      const int ci = t + kThreads * i, r = ci >> 4, ch = ci & 15, kj = k0 + r;
-      pre[6 + i] = kj < a.Lk ? ldg16(a.v + (bh * a.Lk + kj) * kDv + ch * 8) : zero4();
+    for (int i = 0; i < 2; ++i) {
+      const int ci = t + kThreads * i;
+      pre[4 + i] = bload16(r_kr, (ci >> 3) * (kDr * 2) + (ci & 7) * 16, k0 * (kDr * 2));
     }
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {                     // K^T: 192 rows x 8 chunks
-      const int ci = t + kThreads * i, d = ci >> 3, ch = ci & 7;
-      const uint16_t* src = d < kDn ? a.knT + (bh * kDn + d) * a.Lkp
-                                    : a.krT + (static_cast<size_t>(b) * kDr + d - kDn) * a.Lkp;
-      pre[10 + i] = ldg16(src + k0 + ch * 8);
+    for (int i = 0; i < 4; ++i) {
+      const int ci = t + kThreads * i;
+      pre[6 + i] = bload16(r_v, (ci >> 4) * (kDv * 2) + (ci & 15) * 16, k0 * (kDv * 2));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ci = t + kThreads * i;
+      pre[10 + i] = bload16(r_knt, (ci >> 3) * (a.Lkp * 2) + (ci & 7) * 16, k0 * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ci = t + kThreads * i;
+      pre[14 + i] = bload16(r_krt, (ci >> 3) * (a.Lkp * 2) + (ci & 7) * 16, k0 * 2);
     }
   };
   auto commit = [&](char* st) {
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const int ci = t + kThreads * i;
-      *reinterpret_cast<u32x4_t*>(st + kB_K + (ci / 24) * kSQ + (ci % 24) * 16) = pre[i];
+      *reinterpret_cast<u32x4_t*>(st + kB_K + (ci >> 4) * kSQ + (ci & 15) * 16) = pre[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ci = t + kThreads * i;
+      *reinterpret_cast<u32x4_t*>(st + kB_K + (ci >> 3) * kSQ + kDn * 2 + (ci & 7) * 16) = pre[4 + i];
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -486,9 +523,14 @@ __global__ void __launch_bounds__(kThreads) bwd_dq(AttnBwdArgs a) {
       *reinterpret_cast<u32x4_t*>(st + kB_V + (ci >> 4) * kSO + (ci & 15) * 16) = pre[6 + i];
     }
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const int ci = t + kThreads * i;
       *reinterpret_cast<u32x4_t*>(st + kB_KT + (ci >> 3) * kSKT + (ci & 7) * 16) = pre[10 + i];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ci = t + kThreads * i;
+      *reinterpret_cast<u32x4_t*>(st + kB_KT + (kDn + (ci >> 3)) * kSKT + (ci & 7) * 16) = pre[14 + i];
     }
   };
 

@@ -237,7 +237,9 @@ size_t dflash_mla_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Lq, int
  * key) pass no gradient; hidden entries (mask -inf) have p = 0.  The mask gets
  * no gradient.
  * Supported: dt = BF16 (F32 returns UNSUPPORTED), mask_dt F32 or BF16, Dn 128,
- *   Dr 64, Dv 128, B * H <= 65535, at most 2^24 - 1 key tiles.  bf16 MFMA with
+ *   Dr 64, Dv 128, B * H <= 65535, at most 2^24 - 1 key tiles, and Lq and Lk
+ *   (rounded up to 128 / 64) at most 2^31 / 384 (one (batch, head) slice of an
+ *   operand within 2 GiB).  bf16 MFMA with
  *   fp32 accumulation; p and ds are rounded to bf16 as MFMA operands; outputs
  *   rounded to nearest even.  Deterministic: no atomics, dk_rope summed over
  *   heads in head order.
