@@ -59,11 +59,17 @@ def parse():
     return p.parse_args()
 
 
+def split_key(key: str):
+    """'3b' -> ('3b', ''), '4s' -> ('4', 's'), '3bb' -> ('3b', 'b'): workload, then mode suffix."""
+    base = key[:2] if key.startswith("3") else key[:1]
+    return base, key[len(base):]
+
+
 def make_workload(key: str):
     from dflash_block_draft_amd import workloads as W
     if key == "gqa":
         return None
-    key = key.rstrip("sbp")
+    key = split_key(key)[0]
     if key == "3a":
         return W.config(3, block_size=8)
     if key == "3b":
@@ -480,12 +486,13 @@ def main():
             log(f"building workload {key}")
             w2 = make_workload(key)
             log(describe(w2))
-            if key.endswith("b"):
+            mode = split_key(key)[1]
+            if mode == "b":
                 r = measure_bwd(w2, max(3, args.steps // 2), max(1, args.warmup // 2))
-            elif key.endswith("p"):
+            elif mode == "p":
                 r = measure_proj(w2, max(3, args.steps // 2), max(1, args.warmup // 2))
             else:
-                r = measure(w2, max(3, args.steps // 2), max(1, args.warmup // 2), structured=key.endswith("s"))
+                r = measure(w2, max(3, args.steps // 2), max(1, args.warmup // 2), structured=mode == "s")
             log(f"{key}: {r['ms_per_step']} ms/step, {r['tflops']} TFLOP/s ({r['pct_bf16_peak']}%)")
             secondary.append(r)
             del w2

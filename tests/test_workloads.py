@@ -63,3 +63,12 @@ def test_visible_flops_definition():
     wl = W.config(0)
     pairs = int(np.isfinite(wl.mask.float().numpy()).sum())
     assert W.visible_flops(wl.mask, wl.B, wl.H, wl.Lq, wl.Lk) == pairs * 4 * 640
+
+
+def test_bench_keys():
+    import bench
+    assert bench.split_key("3b") == ("3b", "")
+    assert bench.split_key("3a") == ("3a", "")
+    assert bench.split_key("4b") == ("4", "b")
+    assert bench.split_key("2s") == ("2", "s")
+    assert bench.split_key("3bs") == ("3b", "s")
