@@ -22,6 +22,7 @@
 // consecutive outputs (8-byte stores), K staged 32 at a time through a double
 // buffer with 80-byte LDS rows (conflict-free 16-byte operand reads).
 #include "common.h"
+#include "dma.h"
 #include "launch.h"
 #include "rmsnorm.h"
 
@@ -234,6 +235,134 @@ __global__ void __launch_bounds__(64 * WN * WM) linear_bf16(LinearArgs a) {
   }
 }
 
+// The 256 x 256 tile with its operands copied global -> LDS by the buffer unit
+// (no staging registers) three stages deep, K = 32 per stage.  A stage holds 256
+// W rows then 256 rows of a, 80 bytes each (64 of data + 16 of padding, which
+// keeps the 16-byte operand reads conflict-free): 2560 16-byte chunks = 40 copy
+// instructions of 64 lanes, five per wave; waves 0-3 copy W, waves 4-7 copy a.
+// Lane l of copy j of wave w fills chunk c = (5w + j) * 64 + l, i.e. row c / 5,
+// column c % 5; the padding column re-reads column 0 (any valid address).  Rows
+// past N or M read zeros through the descriptors' ranges.  For single-source a
+// without norm-on-load.
+constexpr int kKS_DMA = 32;
+constexpr int kDmaStages = 3;
+constexpr int kDmaRow = 80;                                      // bytes per LDS row
+constexpr int kDmaStage = 512 * kDmaRow;                         // 40960 bytes
+
+__global__ void __launch_bounds__(512) linear_bf16_dma(LinearArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[kDmaStages * kDmaStage];
+  __shared__ float s_part[4][256];
+  typedef __attribute__((address_space(3))) char lds_char_t;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wn = wave & 3, wm = wave >> 2;
+  const int li = lane & 31, hi = lane >> 5;
+  const int T = a.T1 + a.T2;
+  const int64_t M = static_cast<int64_t>(a.B) * T;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * 256;
+  const int n0 = blockIdx.y * 256;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.K) * 2;
+
+  // copy plan of this wave: one descriptor (W or a), five chunk offsets
+  const bool is_w = wave < 4;
+  const int64_t nrows = is_w ? min(256, a.N - n0) : static_cast<int64_t>(min<int64_t>(256, M - m0));
+  const u32x4_t rs = buffer_desc(is_w ? static_cast<const void*>(a.w + static_cast<size_t>(n0) * a.K)
+                                      : static_cast<const void*>(a.a1 + static_cast<size_t>(m0) * a.K),
+                                 static_cast<uint32_t>(nrows * row_bytes));
+  uint32_t voff[5];
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    const int c = (5 * wave + j) * 64 + lane;
+    const int row = c / 5 - (is_w ? 0 : 256), col = c % 5;
+    voff[j] = static_cast<uint32_t>(row) * row_bytes + (col == 4 ? 0 : col) * 16;
+  }
+  const uint32_t lds_copy = lds0 + 5 * wave * 1024;
+  auto issue = [&](int it) __attribute__((always_inline)) {
+    const uint32_t base = lds_copy + (it % kDmaStages) * kDmaStage;
+    const uint32_t soff = static_cast<uint32_t>(it) * (kKS_DMA * 2);
+    dma16<0>(rs, base, voff[0], soff);
+    dma16<1024>(rs, base, voff[1], soff);
+    dma16<2048>(rs, base, voff[2], soff);
+    dma16<3072>(rs, base, voff[3], soff);
+    dma16<4096>(rs, base, voff[4], soff);
+  };
+
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = a.K / kKS_DMA;
+  issue(0);
+  if (nk > 1) issue(1);
+  for (int it = 0; it < nk; ++it) {
+    if (it + 1 < nk) wait_vmem<5>(); else wait_vmem<0>();   // this wave's copies of stage it
+    __syncthreads();                                        // everyone's; stage it-1 fully read
+    if (it + 2 < nk) issue(it + 2);
+    const char* Ws = smem + (it % kDmaStages) * kDmaStage;
+    const char* Ls = Ws + 256 * kDmaRow;
+#pragma unroll
+    for (int ks = 0; ks < kKS_DMA / 16; ++ks) {
+      bf16x8_t af[2], bf[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(Ws + (64 * wn + 32 * i + li) * kDmaRow + (16 * ks + 8 * hi) * 2));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bf[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(Ls + (128 * wm + 32 * j + li) * kDmaRow + (16 * ks + 8 * hi) * 2));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+    }
+  }
+
+  // epilogue: as linear_bf16 (lane owns row m; outputs n0 + 64 wn + 32 i + 8 g + 4 hi + 0..3)
+  const bool stats = a.stats_out && n0 < a.Nstat;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int rl = 128 * wm + 32 * j + li;
+    const int64_t m = m0 + rl;
+    const bool mok = m < M;
+    const int64_t mm = mok ? m : 0;
+    const int64_t b = mm / T;
+    const int tt = static_cast<int>(mm % T);
+    float ssq = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + 64 * wn + 32 * i + 8 * g + 4 * hi;
+        const uint32_t p0 = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+        const uint32_t p1 = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+        if (n < a.N) {
+          const float x0 = bf16_bits_to_f32(p0 & 0xFFFFu), x1 = bf16_bits_to_f32(p0 >> 16);
+          const float x2 = bf16_bits_to_f32(p1 & 0xFFFFu), x3 = bf16_bits_to_f32(p1 >> 16);
+          ssq += x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
+          if (mok) emit4(a, m, b, tt, T, n, p0, p1);
+        }
+      }
+    if (stats) {
+      ssq += __shfl_xor(ssq, 32);
+      if (hi == 0) s_part[wn][rl] = ssq;
+    }
+  }
+  if (stats) {
+    __syncthreads();
+    const int parts = a.Nstat / 128;
+    for (int idx = t; idx < 2 * 256; idx += 512) {
+      const int r = idx % 256, gi = idx / 256;
+      const int part = n0 / 128 + gi;
+      const int64_t m = m0 + r;
+      if (m < M && part < parts) a.stats_out[m * parts + part] = s_part[2 * gi][r] + s_part[2 * gi + 1][r];
+    }
+  }
+}
+
 // Split-K reduction: the partials of each output are summed in split order and
 // the result goes through the same epilogue (rounding, layout, statistics).  One
 // thread per row and 4 columns; 32 threads cover one 128-column group.
@@ -330,7 +459,9 @@ hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t s, float* scratch
   }
   if (linear_big_tile(a)) {
     const dim3 grid(static_cast<unsigned>((M + 255) / 256), static_cast<unsigned>((a.N + 255) / 256));
-    hipLaunchKernelGGL((linear_bf16<256, 256, 64, 4, 2>), grid, dim3(BigTile::kThreads), 0, s, a);
+    const bool dma = !a.stats_in && (a.T2 == 0 || !a.a2) && static_cast<int64_t>(a.K) * 2 * 256 <= INT32_MAX;
+    if (dma) hipLaunchKernelGGL(linear_bf16_dma, grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((linear_bf16<256, 256, 64, 4, 2>), grid, dim3(BigTile::kThreads), 0, s, a);
   } else {
     const dim3 grid(static_cast<unsigned>((M + 127) / 128), static_cast<unsigned>((a.N + 127) / 128));
     hipLaunchKernelGGL((linear_bf16<128, 128, 32, 2, 2>), grid, dim3(SmallTile::kThreads), 0, s, a);

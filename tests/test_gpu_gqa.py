@@ -75,6 +75,7 @@ CASES = [
     ("gqa8_bs8_clamped", 2, 200, 8, 160, 16, 2, [200, 5000], 0),
     ("long", 1, 4100, 16, 256, 8, 2, [4100], 0),
     ("split_k_projections", 2, 300, 16, 2048, 8, 2, [300, 111], 0),   # hidden 2048: K split across workgroups
+    ("large_tile_materialize", 1, 16384, 16, 1024, 32, 8, [16384], 0),  # 16384 x 1024 cache projection: 256-wide tiles
 ]
 
 

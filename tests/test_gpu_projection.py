@@ -120,3 +120,13 @@ def test_projections_full_size_then_attention(dev):
     d = (out.float() - ref.float()).abs()
     say(f"  attention on projected vs oracle-projected inputs: max={d.max().item():.3e} mean={d.mean().item():.3e}")
     assert d.mean().item() <= 1e-2
+
+
+def test_context_project_large_tile(dev):
+    """Enough output tiles for the 256 x 256 tile with its three-stage copy pipeline
+    (4096 rows x 4096 outputs, K 4096)."""
+    p = W.projection_inputs(84, 1, 4096, 16, 2, hidden=4096, q_lora_rank=128, n_target_layers=1)
+    say("context_project 4096 x 4096, K 4096 (large tile)")
+    out = mla.context_project(p["target_hidden"].to(dev), p["w_fc"].to(dev), p["g_hidden"].to(dev), p["eps"])
+    torch.cuda.synchronize()
+    _check("context (large tile)", out, oracle.context_project(p["target_hidden"], p["w_fc"], p["g_hidden"], p["eps"]))
