@@ -94,10 +94,8 @@ def test_config1_expand_then_attention(dev):
     say("config1 attention on the expanded k/v")
     out = mla.mla_attn(q, kn, kr, v, m, wl.scale)
     torch.cuda.synchronize()
-    wl.k_nope, wl.v = kn.cpu(), v.cpu()
-    ref = oracle.mla_attention(wl.q, wl.k_nope, wl.k_rope, wl.v, wl.mask, wl.scale)
-    _check(out, ref, "bf16", "config1 attention")
-    # end to end against the fp64 expansion as well
+    # end to end: the oracle's attention on the oracle's own fp64 expansion (the GPU
+    # path rounded its k/v to bf16 first, which the bf16 tolerance covers)
     ref_e2e = oracle.mla_attention(wl.q, ref_kn, wl.k_rope, ref_v, wl.mask, wl.scale)
     _check(out, ref_e2e, "bf16", "config1 end-to-end (fp64 expand)")
 
