@@ -123,12 +123,16 @@ dflash_status dflash_mla_tile_map_layout(int64_t B, int64_t Lq, int64_t Lk, int6
   return ok();
 }
 
+// need_mask = false: only the tile map in the workspace is used (a map computed
+// earlier, e.g. from the block structure), no mask is read.
 static dflash_status check_occupancy_args(const void* mask, int mask_dt, int64_t B, int64_t Lq,
                                           int64_t Lk, const void* ws, size_t ws_bytes,
-                                          TileLayout* t) {
-  if (!mask) return fail(DFLASH_ERR_INVALID_ARG, "additive_mask is NULL");
-  if (!valid_dtype(mask_dt)) return fail(DFLASH_ERR_INVALID_ARG, "mask_dt %d is not a dflash_dtype", mask_dt);
-  if (!aligned16(mask)) return fail(DFLASH_ERR_INVALID_ARG, "additive_mask is not 16-byte aligned");
+                                          TileLayout* t, bool need_mask = true) {
+  if (need_mask) {
+    if (!mask) return fail(DFLASH_ERR_INVALID_ARG, "additive_mask is NULL");
+    if (!valid_dtype(mask_dt)) return fail(DFLASH_ERR_INVALID_ARG, "mask_dt %d is not a dflash_dtype", mask_dt);
+    if (!aligned16(mask)) return fail(DFLASH_ERR_INVALID_ARG, "additive_mask is not 16-byte aligned");
+  }
   if (B <= 0 || Lq <= 0 || Lk <= 0)
     return fail(DFLASH_ERR_INVALID_ARG, "B, Lq, Lk must be positive (got %lld, %lld, %lld)", (long long)B, (long long)Lq, (long long)Lk);
   if (B > INT32_MAX || Lq > INT32_MAX || Lk > INT32_MAX)
@@ -334,6 +338,10 @@ dflash_status attn_impl(const void* q, const void* k_nope, const void* k_rope_sh
   if (dt == DFLASH_BF16 && (Lk + DFLASH_TILE_N - 1) / DFLASH_TILE_N > dflash::kMaxKeyTiles)
     return fail(DFLASH_ERR_UNSUPPORTED, "a bf16 call supports at most %d key tiles, got Lk = %lld",
                 dflash::kMaxKeyTiles, (long long)Lk);
+  const bool map_only = !additive_mask && (flags & DFLASH_ATTN_REUSE_TILE_MAP);   // the workspace's map alone
+  if (map_only && dt == DFLASH_F32) return fail(DFLASH_ERR_INVALID_ARG, "the f32 path keeps no tile map to reuse");
+  if (map_only && (flags & DFLASH_ATTN_NO_TILE_SKIP))
+    return fail(DFLASH_ERR_INVALID_ARG, "NO_TILE_SKIP needs the mask (a reused map alone has no values for empty tiles)");
   if (flags & DFLASH_ATTN_CHECK_ONLY) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
 
@@ -375,9 +383,10 @@ dflash_status attn_impl(const void* q, const void* k_nope, const void* k_rope_sh
   if (a.nkt > dflash::kMaxKeyTiles)
     return fail(DFLASH_ERR_UNSUPPORTED, "a bf16 call supports at most %d key tiles, got Lk = %lld",
                 dflash::kMaxKeyTiles, (long long)Lk);
-  if (additive_mask) {
+  if (additive_mask || map_only) {
     TileLayout t;
-    dflash_status st = check_occupancy_args(additive_mask, mask_dt, B, Lq, Lk, workspace, workspace_bytes, &t);
+    dflash_status st = check_occupancy_args(additive_mask, mask_dt, B, Lq, Lk, workspace, workspace_bytes, &t,
+                                            !map_only);
     if (st != DFLASH_OK) return st;
     const Range rw = range_of(workspace, t.total);
     if (overlaps(ro, rw) || overlaps(rl, rw)) return fail(DFLASH_ERR_INVALID_ARG, "out / lse overlap the workspace");
@@ -510,8 +519,10 @@ dflash_status dflash_mla_attn_bwd(const void* q, const void* k_nope, const void*
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   dflash::AttnBwdArgs a = {};
-  if (additive_mask) {
-    dflash_status st = check_occupancy_args(additive_mask, mask_dt, B, Lq, Lk, workspace, workspace_bytes, &L.t);
+  const bool map_only = !additive_mask && (flags & DFLASH_ATTN_REUSE_TILE_MAP);   // the workspace's map alone
+  if (additive_mask || map_only) {
+    dflash_status st = check_occupancy_args(additive_mask, mask_dt, B, Lq, Lk, workspace, workspace_bytes, &L.t,
+                                            !map_only);
     if (st != DFLASH_OK) return st;
     const dflash::OccupancyArgs o = occupancy_args(additive_mask, mask_dt, B, Lq, Lk, workspace, L.t);
     if (!(flags & DFLASH_ATTN_REUSE_TILE_MAP)) {

@@ -328,7 +328,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
       // accumulator r <-> key k0 + kh*32 + 8*(r>>2) + 4*hi + (r&3)
       const int kbase = k0 + kh * 32 + 4 * hi;
       float x[16];
-      if (cls == 3) {
+      if (cls == 3 && a.mask) {   // (a reused map without its mask: no values to add)
         // general mask values: x = scale*qk + mask
         float mv[16];
 #pragma unroll

@@ -351,7 +351,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv(AttnBwdArgs a) {
     float madd[16];                                   // log2(e) * mask values (general tiles only)
 #pragma unroll
     for (int r = 0; r < 16; ++r) madd[r] = 0.f;
-    if (cls == 3) {
+    if (cls == 3 && a.mask) {
       for (int r = 0; r < 16; ++r) {
         const int qr = 8 * (r >> 2) + 4 * hi + (r & 3);
         if (key_ok && q0 + qr < a.Lq)
@@ -552,7 +552,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dq(AttnBwdArgs a) {
       float madd[16];                                 // log2(e) * mask values (general tiles only)
 #pragma unroll
       for (int r = 0; r < 16; ++r) madd[r] = 0.f;
-      if (cls == 3) {
+      if (cls == 3 && a.mask) {
         for (int r = 0; r < 16; ++r) {
           const int kj = kt * kTileN + 32 * half + 8 * (r >> 2) + 4 * hi + (r & 3);
           if (kj < a.Lk && q_ok)

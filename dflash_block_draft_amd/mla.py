@@ -242,6 +242,8 @@ def mla_attn(q: torch.Tensor, k_nope: torch.Tensor, k_rope: torch.Tensor, v: tor
             if reuse_tile_map:
                 raise ValueError("reuse_tile_map needs the workspace that holds the map")
             workspace = new_workspace(B, Lq, Lk, q.device)
+    elif reuse_tile_map and workspace is None:
+        raise ValueError("reuse_tile_map without a mask needs the workspace that holds the map")
     if out is None:
         out = torch.empty((B, H, Lq, Dv), dtype=dt, device=q.device)
     _dev(out, "out", dtype=dt, ndim=4)

@@ -184,6 +184,13 @@ dflash_status dflash_mla_mask_occupancy(const void* additive_mask, dflash_dtype 
  * Workspace (BF16 with a mask): at least dflash_mla_attn_workspace_bytes(B, Lq, Lk)
  *   bytes, 256-byte aligned; unused (may be NULL/0) when the mask is NULL or dt is F32.
  * flags: any of DFLASH_ATTN_REUSE_TILE_MAP, DFLASH_ATTN_NO_TILE_SKIP, DFLASH_ATTN_CHECK_ONLY.
+ * additive_mask NULL with DFLASH_ATTN_REUSE_TILE_MAP (BF16 only): the tile map
+ *   already in the workspace alone decides which keys each query sees -- e.g. a
+ *   map from dflash_mla_block_occupancy, which makes this the block-structure
+ *   attention with any of the entry points (with lse, backward).  Such a map
+ *   must come from a 0 / -inf visibility (classes empty / zero / binary); tiles of
+ *   general values, which need the mask, are then read as all visible.
+ *   NO_TILE_SKIP is rejected there (INVALID_ARG), as is F32.
  */
 dflash_status dflash_mla_attn(const void* q, const void* k_nope, const void* k_rope_shared,
                               const void* v, const void* additive_mask, void* out,
@@ -246,7 +253,9 @@ size_t dflash_mla_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Lq, int
  * Workspace: at least dflash_mla_attn_bwd_workspace_bytes(B, H, Lq, Lk) bytes,
  *   256-byte aligned, not overlapping any tensor.  flags: 0, or
  *   DFLASH_ATTN_REUSE_TILE_MAP when the workspace already holds the tile map of
- *   this mask (a forward call on the same workspace).
+ *   this mask (a forward call on the same workspace); with additive_mask NULL and
+ *   REUSE_TILE_MAP the map alone decides visibility, as for dflash_mla_attn
+ *   (the block-structure path: dflash_mla_block_occupancy on this workspace first).
  * Errors: INVALID_ARG (NULL or misaligned pointers, sizes <= 0, bad scale, unknown
  *   flags, overlapping buffers), UNSUPPORTED, WORKSPACE, HIP.
  */

@@ -301,3 +301,10 @@ def test_gqa_validation(lib):
         assert fb(*args) == status, (idx, val)
     assert lib.dflash_gqa_workspace_bytes(1, 16, 8, 2, 128) > 0
     assert lib.dflash_gqa_workspace_bytes(0, 16, 8, 2, 128) == 0
+
+
+def test_map_only_reuse_validation(lib):
+    # mask NULL + REUSE_TILE_MAP: bf16 needs the workspace; f32 and NO_TILE_SKIP are rejected
+    assert _attn(lib, flags=0x1) == 3
+    assert _attn(lib, flags=0x1, dt=0) == 1
+    assert _attn(lib, flags=0x3, ws=FAKE * 256, wsb=1 << 20) == 1

@@ -143,3 +143,29 @@ def test_block_reuse_tile_map(dev):
     torch.cuda.synchronize()
     assert torch.equal(b, c)
     assert torch.equal(a, a2)
+
+
+def test_block_structure_training_step(dev):
+    """The block-structure map on a backward workspace drives the forward with lse
+    and the backward through the map alone (no mask): bitwise equal to the same
+    calls with the dense 0 / -inf mask."""
+    rng = np.random.default_rng(44)
+    B, A, bs, ctx, H = 2, 9, 16, 500, 3
+    anchors = W.draw_anchors(rng, B, A, ctx)
+    Lq, Lk = A * bs, ctx + A * bs
+    q, kn, kr, v = (t.to(dev) for t in W.random_attention_inputs(45, B, H, Lq, Lk, dtype="bf16"))
+    dout = W.normal(rng, (B, H, Lq, 128), 1.0, "bf16").to(dev)
+    mask = _dense_mask(anchors, ctx, None, bs).to(dev)
+    ws = mla.new_bwd_workspace(B, H, Lq, Lk, dev)
+    mla.block_occupancy(_i32(anchors, dev), bs, ctx, workspace=ws)
+    lse = torch.empty((B, H, Lq), dtype=torch.float32, device=dev)
+    out = mla.mla_attn(q, kn, kr, v, None, lse=lse, workspace=ws, reuse_tile_map=True)
+    g = mla.mla_attn_bwd(q, kn, kr, v, None, out, dout, lse, workspace=ws, reuse_tile_map=True)
+    lse_d = torch.empty_like(lse)
+    out_d = mla.mla_attn(q, kn, kr, v, mask, lse=lse_d)
+    g_d = mla.mla_attn_bwd(q, kn, kr, v, mask, out_d, dout, lse_d)
+    blk = mla.mla_attn_blocks(q, kn, kr, v, _i32(anchors, dev), bs, ctx)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_d) and torch.equal(out, blk) and torch.equal(lse, lse_d)
+    for x, y in zip(g, g_d):
+        assert torch.equal(x, y)
