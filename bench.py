@@ -102,7 +102,9 @@ def measure(wl, steps: int, warmup: int, structured: bool = False) -> dict:
         v = torch.empty((wl.B, wl.H, wl.Lk, wl.Dv), dtype=q.dtype, device=dev)
     else:
         kn, v = wl.k_nope.to(dev), wl.v.to(dev)
-    ws = mla.new_workspace(wl.B, wl.Lq, wl.Lk, dev)
+    ws = mla.new_workspace(wl.B, wl.Lq, wl.Lk, dev, H=wl.H)   # room for key-split partials on small grids
+    extra = mla.attn_split_workspace_bytes(wl.B, wl.H, wl.Lq, wl.Lk) - mla.attn_workspace_bytes(wl.B, wl.Lq, wl.Lk)
+    key_runs = 1 if wl.dtype != "bf16" or extra <= 0 else round(extra / (wl.B * wl.H * wl.Lq * (wl.Dv * 4 + 4)))
     anchors = torch.as_tensor(wl.anchors.astype("int32")).to(dev)
     ctx_valid = torch.full((wl.B,), wl.ctx_valid, dtype=torch.int32, device=dev)
     out = torch.empty((wl.B, wl.H, wl.Lq, wl.Dv), dtype=q.dtype, device=dev)
@@ -169,6 +171,7 @@ def measure(wl, steps: int, warmup: int, structured: bool = False) -> dict:
         "attn_kernel_tflops": round(vis_flops / (att * 1e-3) / 1e12, 2),
         "occupancy_ms": round(occ, 4),
         "occupancy_mask_GBs": None if structured else round(mask_bytes / (occ * 1e-3) / 1e9, 1),
+        "key_runs": key_runs,
         "tile_fractions_128x64": frac,
         "attn_algorithmic_bytes": attn_bytes,
         "mask_bytes": mask_bytes,

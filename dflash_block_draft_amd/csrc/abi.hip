@@ -84,6 +84,44 @@ bool tile_layout(int64_t B, int64_t Lq, int64_t Lk, TileLayout* t) {
   return true;
 }
 
+// Key-range splits of a bf16 forward: when the (batch, q-tile, head) grid alone
+// would leave compute units idle (fewer than 256 items, one workgroup per CU),
+// each item's tile list is cut into 2, 4 or 8 runs, each run keeping >= 8 of the
+// k-tiles.  (At 256 items and more the partial-result traffic and the merge cost
+// more than the balance gains: measured on the 4 x 32-head, 256-query workload.)
+int attn_splits(int64_t B, int64_t H, int64_t Lq, int64_t Lk) {
+  const int64_t items = B * ((Lq + DFLASH_TILE_M - 1) / DFLASH_TILE_M) * H;
+  const int64_t nkt = (Lk + DFLASH_TILE_N - 1) / DFLASH_TILE_N;
+  int sp = 1;
+  while (sp < 8 && items * sp < 256 && nkt / (2 * sp) >= 8) sp *= 2;
+  return sp;
+}
+
+// Workspace of a split forward: the tile map, then part_o [S,B,H,Lq,Dv] f32 and
+// part_lse [S,B,H,Lq] f32.  Returns false on overflow / invalid sizes.
+struct SplitLayout {
+  int nsplit;
+  size_t part_o, part_lse, total;
+};
+bool split_layout(int64_t B, int64_t H, int64_t Lq, int64_t Lk, SplitLayout* L) {
+  TileLayout t;
+  if (H <= 0 || !tile_layout(B, Lq, Lk, &t)) return false;
+  L->nsplit = attn_splits(B, H, Lq, Lk);
+  int64_t rows, n;
+  if (!mul_ok(B, H, &rows) || !mul_ok(rows, Lq, &rows) || !mul_ok(rows, L->nsplit, &n) ||
+      !mul_ok(n, static_cast<int64_t>(dflash::kDv) * 4, &n))
+    return false;
+  if (L->nsplit == 1) {
+    L->part_o = L->part_lse = L->total = t.total;
+    return true;
+  }
+  L->part_o = align_up(t.total, 256);
+  L->part_lse = align_up(L->part_o + static_cast<size_t>(n), 256);
+  L->total = align_up(L->part_lse + static_cast<size_t>(rows) * L->nsplit * 4, 256);
+  return true;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -105,6 +143,12 @@ size_t dflash_mla_attn_workspace_bytes(int64_t B, int64_t Lq, int64_t Lk) {
   TileLayout t;
   if (!tile_layout(B, Lq, Lk, &t)) return 0;
   return t.total;
+}
+
+size_t dflash_mla_attn_split_workspace_bytes(int64_t B, int64_t H, int64_t Lq, int64_t Lk) {
+  SplitLayout L;
+  if (!split_layout(B, H, Lq, Lk, &L)) return 0;
+  return L.total;
 }
 
 dflash_status dflash_mla_tile_map_layout(int64_t B, int64_t Lq, int64_t Lk, int64_t* n_q_tiles,
@@ -305,7 +349,8 @@ dflash_status attn_impl(const void* q, const void* k_nope, const void* k_rope_sh
     return fail(DFLASH_ERR_INVALID_ARG, "sizes must be positive (B=%lld H=%lld Lq=%lld Lk=%lld)", (long long)B, (long long)H, (long long)Lq, (long long)Lk);
   if (!std::isfinite(scale) || !(scale > 0.f)) return fail(DFLASH_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (!valid_dtype(dt) || !valid_dtype(mask_dt)) return fail(DFLASH_ERR_INVALID_ARG, "dtype is not a dflash_dtype");
-  if (flags & ~(DFLASH_ATTN_REUSE_TILE_MAP | DFLASH_ATTN_NO_TILE_SKIP | DFLASH_ATTN_CHECK_ONLY))
+  if (flags & ~(DFLASH_ATTN_REUSE_TILE_MAP | DFLASH_ATTN_NO_TILE_SKIP | DFLASH_ATTN_CHECK_ONLY |
+                DFLASH_ATTN_SPLIT_KEYS))
     return fail(DFLASH_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   if (Dn != dflash::kDn || Dr != dflash::kDr || Dv != dflash::kDv)
     return fail(DFLASH_ERR_UNSUPPORTED, "only Dn=128, Dr=64, Dv=128 are built (got %lld, %lld, %lld)", (long long)Dn, (long long)Dr, (long long)Dv);
@@ -342,10 +387,26 @@ dflash_status attn_impl(const void* q, const void* k_nope, const void* k_rope_sh
   if (map_only && dt == DFLASH_F32) return fail(DFLASH_ERR_INVALID_ARG, "the f32 path keeps no tile map to reuse");
   if (map_only && (flags & DFLASH_ATTN_NO_TILE_SKIP))
     return fail(DFLASH_ERR_INVALID_ARG, "NO_TILE_SKIP needs the mask (a reused map alone has no values for empty tiles)");
-  if (flags & DFLASH_ATTN_CHECK_ONLY) return ok();
+  SplitLayout sl = {1, 0, 0, 0};
+  if (dt == DFLASH_BF16 && (flags & DFLASH_ATTN_SPLIT_KEYS) && !(flags & DFLASH_ATTN_NO_TILE_SKIP)) {
+    if (!split_layout(B, H, Lq, Lk, &sl)) return fail(DFLASH_ERR_UNSUPPORTED, "sizes too large");
+    if (sl.nsplit > 1) {
+      if (!workspace) return fail(DFLASH_ERR_WORKSPACE, "SPLIT_KEYS needs a workspace");
+      if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(DFLASH_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+      if (workspace_bytes < sl.total)
+        return fail(DFLASH_ERR_WORKSPACE, "workspace has %zu bytes, a split call of this shape needs %zu",
+                    workspace_bytes, sl.total);
+      const Range rw = range_of(workspace, sl.total);
+      if (overlaps(ro, rw) || overlaps(rl, rw)) return fail(DFLASH_ERR_INVALID_ARG, "out / lse overlap the workspace");
+      for (const Range& r : ins)
+        if (overlaps(rw, r)) return fail(DFLASH_ERR_INVALID_ARG, "the workspace overlaps an input");
+    }
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   if (dt == DFLASH_F32) {
+    if (flags & DFLASH_ATTN_CHECK_ONLY) return ok();
     if (static_cast<int64_t>(B) > 65535 || H > 65535) return fail(DFLASH_ERR_UNSUPPORTED, "B and H must be <= 65535 for f32");
     dflash::AttnF32Args a;
     a.q = static_cast<const float*>(q);
@@ -392,6 +453,7 @@ dflash_status attn_impl(const void* q, const void* k_nope, const void* k_rope_sh
     if (overlaps(ro, rw) || overlaps(rl, rw)) return fail(DFLASH_ERR_INVALID_ARG, "out / lse overlap the workspace");
     for (const Range& r : ins)
       if (overlaps(rw, r)) return fail(DFLASH_ERR_INVALID_ARG, "the workspace overlaps an input");
+    if (flags & DFLASH_ATTN_CHECK_ONLY) return ok();
     const dflash::OccupancyArgs o = occupancy_args(additive_mask, mask_dt, B, Lq, Lk, workspace, t);
     if (!(flags & DFLASH_ATTN_REUSE_TILE_MAP)) {
       st = hip_status(dflash::launch_occupancy(o, s), "mask occupancy launch");
@@ -407,7 +469,24 @@ dflash_status attn_impl(const void* q, const void* k_nope, const void* k_rope_sh
     a.order = o.order;
     a.bits = o.bits;
   }
-  return hip_status(dflash::launch_attn_bf16(a, s), "bf16 attention launch");
+  if (flags & DFLASH_ATTN_CHECK_ONLY) return ok();
+  a.nsplit = sl.nsplit;
+  if (sl.nsplit > 1) {
+    char* ws = static_cast<char*>(workspace);
+    a.part_o = reinterpret_cast<float*>(ws + sl.part_o);
+    a.part_lse = reinterpret_cast<float*>(ws + sl.part_lse);
+    a.lse = nullptr;
+  }
+  dflash_status st = hip_status(dflash::launch_attn_bf16(a, s), "bf16 attention launch");
+  if (st != DFLASH_OK || sl.nsplit == 1) return st;
+  dflash::AttnCombineArgs c;
+  c.part_o = a.part_o;
+  c.part_lse = a.part_lse;
+  c.out = a.out;
+  c.lse = lse;
+  c.rows = B * H * Lq;
+  c.nsplit = sl.nsplit;
+  return hip_status(dflash::launch_attn_combine(c, s), "split combine launch");
 }
 
 // Backward workspace: the forward's tile map, then the backward's own arrays.
@@ -1031,54 +1110,29 @@ dflash_status dflash_mla_attn_blocks(const void* q, const void* k_nope, const vo
                                      int64_t H, int64_t A, int64_t block_size, int64_t ctx, int64_t Dn, int64_t Dr,
                                      int64_t Dv, float scale, dflash_dtype dt, void* workspace,
                                      size_t workspace_bytes, uint32_t flags, void* stream) {
-  if (flags & ~DFLASH_ATTN_REUSE_TILE_MAP) return fail(DFLASH_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  if (flags & ~(DFLASH_ATTN_REUSE_TILE_MAP | DFLASH_ATTN_SPLIT_KEYS))
+    return fail(DFLASH_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   if (valid_dtype(dt) && dt != DFLASH_BF16) return fail(DFLASH_ERR_UNSUPPORTED, "the block-structure path is BF16 only");
   TileLayout t;
   int64_t Lq, Lk;
   dflash_status st = check_block_args(anchors, ctx_valid, B, A, block_size, ctx, workspace, workspace_bytes, &t, &Lq, &Lk);
   if (st != DFLASH_OK) return st;
-  // the shape / pointer checks of the dense-mask call (no mask, no workspace there)
-  st = dflash_mla_attn(q, k_nope, k_rope_shared, v, nullptr, out, B, H, Lq, Lk, Dn, Dr, Dv, scale, dt,
-                       DFLASH_F32, nullptr, 0, DFLASH_ATTN_CHECK_ONLY, stream);
+  // the attention on the workspace's map alone: its shape, pointer and workspace checks
+  const uint32_t attn_flags = (flags & DFLASH_ATTN_SPLIT_KEYS) | DFLASH_ATTN_REUSE_TILE_MAP;
+  st = attn_impl(q, k_nope, k_rope_shared, v, nullptr, out, nullptr, B, H, Lq, Lk, Dn, Dr, Dv, scale, dt,
+                 DFLASH_F32, workspace, workspace_bytes, attn_flags | DFLASH_ATTN_CHECK_ONLY, stream);
   if (st != DFLASH_OK) return st;
-  const Range rw = range_of(workspace, t.total);
-  const int64_t bh = B * H;
-  const Range io[5] = {
-      range_of(out, static_cast<size_t>(bh) * Lq * Dv * 2), range_of(q, static_cast<size_t>(bh) * Lq * (Dn + Dr) * 2),
-      range_of(k_nope, static_cast<size_t>(bh) * Lk * Dn * 2), range_of(k_rope_shared, static_cast<size_t>(B) * Lk * Dr * 2),
-      range_of(v, static_cast<size_t>(bh) * Lk * Dv * 2)};
-  for (const Range& r : io)
-    if (overlaps(rw, r)) return fail(DFLASH_ERR_INVALID_ARG, "the workspace overlaps a tensor");
-  if (overlaps(io[0], range_of(anchors, static_cast<size_t>(B) * A * 4)) ||
-      (ctx_valid && overlaps(io[0], range_of(ctx_valid, static_cast<size_t>(B) * 4))))
+  const Range ro = range_of(out, static_cast<size_t>(B) * H * Lq * Dv * 2);
+  if (overlaps(ro, range_of(anchors, static_cast<size_t>(B) * A * 4)) ||
+      (ctx_valid && overlaps(ro, range_of(ctx_valid, static_cast<size_t>(B) * 4))))
     return fail(DFLASH_ERR_INVALID_ARG, "out overlaps anchors / ctx_valid");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const dflash::OccupancyArgs o = block_args(anchors, ctx_valid, B, A, block_size, ctx, Lq, Lk, workspace, t);
   if (!(flags & DFLASH_ATTN_REUSE_TILE_MAP)) {
-    st = hip_status(dflash::launch_block_occupancy(o, s), "block occupancy launch");
+    const dflash::OccupancyArgs o = block_args(anchors, ctx_valid, B, A, block_size, ctx, Lq, Lk, workspace, t);
+    st = hip_status(dflash::launch_block_occupancy(o, static_cast<hipStream_t>(stream)), "block occupancy launch");
     if (st != DFLASH_OK) return st;
   }
-  dflash::AttnBf16Args a = {};
-  a.q = static_cast<const uint16_t*>(q);
-  a.kn = static_cast<const uint16_t*>(k_nope);
-  a.kr = static_cast<const uint16_t*>(k_rope_shared);
-  a.v = static_cast<const uint16_t*>(v);
-  a.mask = nullptr;                 // a block-structure map has no class-3 tiles
-  a.out = static_cast<uint16_t*>(out);
-  a.B = static_cast<int>(B);
-  a.H = static_cast<int>(H);
-  a.Lq = static_cast<int>(Lq);
-  a.Lk = static_cast<int>(Lk);
-  a.nqt = static_cast<int>(t.nqt);
-  a.nkt = static_cast<int>(t.nkt);
-  a.scale = scale;
-  a.mask_bf16 = 0;
-  a.classes = o.classes;
-  a.counts = o.counts;
-  a.lists = o.lists;
-  a.order = o.order;
-  a.bits = o.bits;
-  return hip_status(dflash::launch_attn_bf16(a, s), "bf16 attention launch");
+  return attn_impl(q, k_nope, k_rope_shared, v, nullptr, out, nullptr, B, H, Lq, Lk, Dn, Dr, Dv, scale, dt,
+                   DFLASH_F32, workspace, workspace_bytes, attn_flags, stream);
 }
 
 }  // extern "C"

@@ -130,13 +130,18 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
   const int li = lane & 31;
   const int hi = lane >> 5;
 
-  // ---- work item: heads of one (batch, q-tile) are adjacent in launch order
+  // ---- work item: heads of one (batch, q-tile, split) are adjacent in launch
+  // order; split sp takes the sp-th of nsplit contiguous runs of the tile list
   const int h = blockIdx.x % a.H;
-  const int rank = blockIdx.x / a.H;
+  const int item = blockIdx.x / a.H;
+  const int sp = item % a.nsplit;
+  const int rank = item / a.nsplit;
   const int bq = a.order ? a.order[rank] : rank;
   const int b = bq / a.nqt;
   const int qt = bq % a.nqt;
-  const int ntiles = a.counts ? a.counts[bq] : a.nkt;
+  const int n_all = a.counts ? a.counts[bq] : a.nkt;
+  const int t_begin = static_cast<int>(static_cast<int64_t>(n_all) * sp / a.nsplit);
+  const int ntiles = static_cast<int>(static_cast<int64_t>(n_all) * (sp + 1) / a.nsplit) - t_begin;
 
   const size_t bh = static_cast<size_t>(b) * a.H + h;
   const int q_local = qg * 32 + li;               // this lane's query within the tile
@@ -147,11 +152,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
   // ---- tile list of this q-tile (entry: k-tile | class << 24), read with scalar
   // loads; past the end an entry is 0 (no tile); without a mask every k-tile is class 1
   typedef __attribute__((address_space(4))) const int32_t const_i32;
-  const int32_t* list = a.counts ? a.lists + tile_row0 : nullptr;
+  const int32_t* list = a.counts ? a.lists + tile_row0 + t_begin : nullptr;
   const const_i32* clist = (const const_i32*)(uintptr_t)(list);
   auto entry = [&](int i) __attribute__((always_inline)) -> int {
     if (i >= ntiles) return 0;
-    if (!list) return i | (1 << 24);
+    if (!list) return (t_begin + i) | (1 << 24);
     return clist[i];
   };
 
@@ -475,7 +480,28 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
     const float a1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * kLog2e);
     const float l = l_run * a0 + l1 * a1;
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    if (a.lse && q_ok && hi == 0) a.lse[bh * a.Lq + q_row] = l > 0.f ? m + __logf(l) : -INFINITY;
+    const float lse_row = l > 0.f ? m + __logf(l) : -INFINITY;
+    if (a.part_o) {            // one run of a split row: fp32 partials for the combine
+      const size_t prow = (static_cast<size_t>(sp) * a.B * a.H + bh) * a.Lq + q_row;
+      if (q_ok && hi == 0) a.part_lse[prow] = lse_row;
+      if (q_ok) {
+        float* pp = a.part_o + prow * kDv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            f32x4_t x;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const int r = 4 * g + c;
+              x[c] = (o[j][r] * a0 + red[(r * 4 + j) * 64 + lane] * a1) * inv;
+            }
+            *reinterpret_cast<f32x4_t*>(pp + 32 * j + 8 * g + 4 * hi) = x;
+          }
+      }
+      return;
+    }
+    if (a.lse && q_ok && hi == 0) a.lse[bh * a.Lq + q_row] = lse_row;
     if (q_ok) {
       uint16_t* op = a.out + (bh * a.Lq + q_row) * kDv;
       // o[j][r] holds dv = 32*j + 8*(r>>2) + 4*hi + (r&3)
@@ -496,10 +522,45 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
   }
 }
 
+// Merge of the split runs of every row: with w_s = exp(lse_s - max lse),
+// out = sum_s w_s o_s / sum_s w_s and lse = max + log(sum_s w_s), summed in split
+// order (deterministic).  A row whose runs are all empty gives 0 and -inf.
+// One thread per 4 output columns, 32 threads per row.
+__global__ void __launch_bounds__(256) attn_combine(AttnCombineArgs a) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
+  if (row >= a.rows) return;
+  const int d = (threadIdx.x & 31) * 4;
+  float mx = -INFINITY;
+  for (int sp = 0; sp < a.nsplit; ++sp) mx = fmaxf(mx, a.part_lse[sp * a.rows + row]);
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (mx != -INFINITY) {
+    for (int sp = 0; sp < a.nsplit; ++sp) {
+      const float ls = a.part_lse[sp * a.rows + row];
+      if (ls == -INFINITY) continue;
+      const float w = __builtin_amdgcn_exp2f((ls - mx) * kLog2e);
+      const f32x4_t o = *reinterpret_cast<const f32x4_t*>(a.part_o + (sp * a.rows + row) * kDv + d);
+      wsum += w;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] = __builtin_fmaf(w, o[c], acc[c]);
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const u32x2_t w2 = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  *reinterpret_cast<u32x2_t*>(a.out + row * kDv + d) = w2;
+  if (a.lse && d == 0) a.lse[row] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
+}
+
 }  // namespace
 
+hipError_t launch_attn_combine(const AttnCombineArgs& a, hipStream_t s) {
+  const unsigned grid = static_cast<unsigned>((a.rows + 7) / 8);
+  hipLaunchKernelGGL(attn_combine, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_bf16(const AttnBf16Args& a, hipStream_t s) {
-  const unsigned grid = static_cast<unsigned>(a.B) * a.nqt * a.H;
+  const unsigned grid = static_cast<unsigned>(a.B) * a.nqt * a.H * a.nsplit;
   if (a.mask && a.mask_bf16)
     hipLaunchKernelGGL(attn_fwd_bf16<true>, dim3(grid), dim3(kThreads), 0, s, a);
   else

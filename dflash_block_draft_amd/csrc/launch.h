@@ -24,6 +24,21 @@ struct AttnBf16Args {
   float scale;            // softmax scale (natural units)
   int mask_bf16;          // 1: mask is bf16, 0: f32
   float* lse;             // [B,H,Lq] f32 natural-log row normaliser (-inf: dead row), or null
+  // key-range split: work item (b, q-tile, h) is cut into nsplit contiguous runs of
+  // its tile list; with nsplit > 1 each run writes its normalised fp32 output and
+  // its row normaliser to part_o [nsplit,B,H,Lq,128] / part_lse [nsplit,B,H,Lq]
+  // instead of out / lse, and launch_attn_combine merges them
+  int nsplit;
+  float* part_o;
+  float* part_lse;
+};
+
+// out / lse of a split forward from its partial results (fixed order over the splits)
+struct AttnCombineArgs {
+  const float* part_o; const float* part_lse;
+  uint16_t* out; float* lse;   // lse may be null
+  int64_t rows;                // B*H*Lq
+  int nsplit;
 };
 
 struct AttnF32Args {
@@ -138,6 +153,7 @@ hipError_t launch_norm_rope_bf16(const NormRopeArgs& a, hipStream_t s);
 hipError_t launch_gqa_attn_bf16(const GqaAttnArgs& a, hipStream_t s);
 hipError_t launch_rms_apply_bf16(const RmsApplyArgs& a, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnBf16Args& a, hipStream_t s);
+hipError_t launch_attn_combine(const AttnCombineArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnF32Args& a, hipStream_t s);
 hipError_t launch_occupancy(const OccupancyArgs& a, hipStream_t s);
 // The same tile map from the block structure (anchors, ctx_valid, bs) instead of a dense mask.

@@ -25,6 +25,7 @@ _DT = {torch.float32: _F32, torch.bfloat16: _BF16}
 FLAG_REUSE_TILE_MAP = 0x1
 FLAG_NO_TILE_SKIP = 0x2
 FLAG_CHECK_ONLY = 0x4
+FLAG_SPLIT_KEYS = 0x8
 
 EXPORTED = (
     "dflash_status_string", "dflash_last_error", "dflash_mla_latent_expand",
@@ -33,7 +34,7 @@ EXPORTED = (
     "dflash_mla_attn_blocks", "dflash_mla_attn_lse", "dflash_mla_attn_bwd_workspace_bytes",
     "dflash_mla_attn_bwd", "dflash_mla_projection_workspace_bytes", "dflash_mla_context_project",
     "dflash_mla_q_project", "dflash_mla_kv_project", "dflash_gqa_materialize", "dflash_gqa_workspace_bytes",
-    "dflash_gqa_forward_block",
+    "dflash_gqa_forward_block", "dflash_mla_attn_split_workspace_bytes",
 )
 
 
@@ -68,6 +69,8 @@ def load_library() -> ctypes.CDLL:
     lib.dflash_mla_latent_expand.restype = i32
     lib.dflash_mla_attn_workspace_bytes.argtypes = [i64, i64, i64]
     lib.dflash_mla_attn_workspace_bytes.restype = sz
+    lib.dflash_mla_attn_split_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.dflash_mla_attn_split_workspace_bytes.restype = sz
     p64, psz = ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_size_t)
     lib.dflash_mla_tile_map_layout.argtypes = [i64, i64, i64, p64, p64, psz, psz, psz, psz, psz]
     lib.dflash_mla_tile_map_layout.restype = i32
@@ -169,9 +172,24 @@ def attn_workspace_bytes(B: int, Lq: int, Lk: int) -> int:
     return int(load_library().dflash_mla_attn_workspace_bytes(B, Lq, Lk))
 
 
-def new_workspace(B: int, Lq: int, Lk: int, device) -> torch.Tensor:
+def attn_split_workspace_bytes(B: int, H: int, Lq: int, Lk: int) -> int:
+    return int(load_library().dflash_mla_attn_split_workspace_bytes(B, H, Lq, Lk))
+
+
+def new_workspace(B: int, Lq: int, Lk: int, device, H: Optional[int] = None) -> torch.Tensor:
+    """Attention workspace: the tile map; with H also room for the key-split partials."""
     n = attn_workspace_bytes(B, Lq, Lk)
+    if H is not None:
+        n = max(n, attn_split_workspace_bytes(B, H, Lq, Lk))
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _split_flag(B: int, H: int, Lq: int, Lk: int, workspace: Optional[torch.Tensor]) -> int:
+    """FLAG_SPLIT_KEYS when this shape splits and the workspace holds the partials."""
+    sb = attn_split_workspace_bytes(B, H, Lq, Lk)
+    if workspace is None or sb <= attn_workspace_bytes(B, Lq, Lk) or workspace.numel() < sb:
+        return 0
+    return FLAG_SPLIT_KEYS
 
 
 def mask_occupancy(mask: torch.Tensor, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -212,11 +230,14 @@ def tile_map_view(workspace: torch.Tensor, B: int, Lq: int, Lk: int) -> dict:
 def mla_attn(q: torch.Tensor, k_nope: torch.Tensor, k_rope: torch.Tensor, v: torch.Tensor,
              mask: Optional[torch.Tensor] = None, scale: Optional[float] = None, *,
              out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-             reuse_tile_map: bool = False, tile_skip: bool = True, lse: Optional[torch.Tensor] = None):
+             reuse_tile_map: bool = False, tile_skip: bool = True, lse: Optional[torch.Tensor] = None,
+             split_keys: bool = True):
     """Draft MLA attention: q [B,H,Lq,Dn+Dr], k_nope [B,H,Lk,Dn], k_rope [B,Lk,Dr] (head-shared),
     v [B,H,Lk,Dv], mask [B,1,Lq,Lk] or None -> out [B,H,Lq,Dv].  scale defaults to
     q_head_dim ** -0.5.  With `lse` (a float32 [B,H,Lq] device tensor) the row
-    log-normalisers are written there too (dflash_mla_attn_lse)."""
+    log-normalisers are written there too (dflash_mla_attn_lse).  bf16 with
+    `split_keys`: a small grid is split over key ranges when the workspace (allocated
+    here when not given) holds the partials."""
     lib = load_library()
     _dev(q, "q", ndim=4)
     dt = q.dtype
@@ -238,18 +259,24 @@ def mla_attn(q: torch.Tensor, k_nope: torch.Tensor, k_rope: torch.Tensor, v: tor
         if tuple(mask.shape) != (B, 1, Lq, Lk):
             raise ValueError(f"mask must be [{B}, 1, {Lq}, {Lk}], got {tuple(mask.shape)}")
         mask_dt = _DT[mask.dtype]
+    split = split_keys and dt == torch.bfloat16 and tile_skip
+    if mask is not None:
         if workspace is None:
             if reuse_tile_map:
                 raise ValueError("reuse_tile_map needs the workspace that holds the map")
-            workspace = new_workspace(B, Lq, Lk, q.device)
+            workspace = new_workspace(B, Lq, Lk, q.device, H=H if split else None)
     elif reuse_tile_map and workspace is None:
         raise ValueError("reuse_tile_map without a mask needs the workspace that holds the map")
+    elif workspace is None and split and attn_split_workspace_bytes(B, H, Lq, Lk) > attn_workspace_bytes(B, Lq, Lk):
+        workspace = new_workspace(B, Lq, Lk, q.device, H=H)
     if out is None:
         out = torch.empty((B, H, Lq, Dv), dtype=dt, device=q.device)
     _dev(out, "out", dtype=dt, ndim=4)
     if workspace is not None:
         _dev(workspace, "workspace", dtype=torch.uint8)
     flags = (FLAG_REUSE_TILE_MAP if reuse_tile_map else 0) | (0 if tile_skip else FLAG_NO_TILE_SKIP)
+    if split:
+        flags |= _split_flag(B, H, Lq, Lk, workspace)
     wsb = 0 if workspace is None else workspace.numel()
     if lse is None:
         _check(lib.dflash_mla_attn(_ptr(q), _ptr(k_nope), _ptr(k_rope), _ptr(v), _ptr(mask), _ptr(out),
@@ -345,9 +372,11 @@ def block_occupancy(anchors: torch.Tensor, block_size: int, ctx: int, ctx_valid:
 def mla_attn_blocks(q: torch.Tensor, k_nope: torch.Tensor, k_rope: torch.Tensor, v: torch.Tensor,
                     anchors: torch.Tensor, block_size: int, ctx: int, ctx_valid: Optional[torch.Tensor] = None,
                     scale: Optional[float] = None, *, out: Optional[torch.Tensor] = None,
-                    workspace: Optional[torch.Tensor] = None, reuse_tile_map: bool = False) -> torch.Tensor:
+                    workspace: Optional[torch.Tensor] = None, reuse_tile_map: bool = False,
+                    split_keys: bool = True) -> torch.Tensor:
     """mla_attn with the DFlash block mask given by anchors [B, A] (int32), block_size,
-    ctx and ctx_valid [B] (int32, or None = ctx) instead of a dense mask."""
+    ctx and ctx_valid [B] (int32, or None = ctx) instead of a dense mask (key split
+    as for mla_attn)."""
     lib = load_library()
     _dev(q, "q", dtype=torch.bfloat16, ndim=4)
     _dev(k_nope, "k_nope", dtype=torch.bfloat16, ndim=4)
@@ -366,15 +395,15 @@ def mla_attn_blocks(q: torch.Tensor, k_nope: torch.Tensor, k_rope: torch.Tensor,
     if workspace is None:
         if reuse_tile_map:
             raise ValueError("reuse_tile_map needs the workspace that holds the map")
-        workspace = new_workspace(B, Lq, Lk, q.device)
+        workspace = new_workspace(B, Lq, Lk, q.device, H=H if split_keys else None)
     _dev(workspace, "workspace", dtype=torch.uint8)
     if out is None:
         out = torch.empty((B, H, Lq, Dv), dtype=q.dtype, device=q.device)
     _dev(out, "out", dtype=q.dtype, ndim=4)
+    flags = (FLAG_REUSE_TILE_MAP if reuse_tile_map else 0) | (_split_flag(B, H, Lq, Lk, workspace) if split_keys else 0)
     _check(lib.dflash_mla_attn_blocks(_ptr(q), _ptr(k_nope), _ptr(k_rope), _ptr(v), _ptr(anchors), _ptr(ctx_valid),
                                       _ptr(out), B, H, A, int(block_size), int(ctx), Dn, Dr, Dv, float(scale),
-                                      _BF16, _ptr(workspace), workspace.numel(),
-                                      FLAG_REUSE_TILE_MAP if reuse_tile_map else 0, _stream(q)))
+                                      _BF16, _ptr(workspace), workspace.numel(), flags, _stream(q)))
     return out
 
 

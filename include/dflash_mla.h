@@ -74,6 +74,14 @@ typedef enum dflash_dtype {
                                             workspace lists are left covering every tile, so a later
                                             REUSE_TILE_MAP call on it also visits every tile */
 #define DFLASH_ATTN_CHECK_ONLY 0x4u      /* validate the arguments and return; launch nothing */
+#define DFLASH_ATTN_SPLIT_KEYS 0x8u      /* BF16: when the (batch, q-tile, head) grid is small, cut
+                                            each q-tile's key tiles into 2, 4 or 8 runs processed
+                                            in parallel and merged in a fixed order (the pages'
+                                            softmax, regrouped: results equal the unsplit call's up
+                                            to fp32 rounding; still deterministic run to run).  The
+                                            workspace must then hold
+                                            dflash_mla_attn_split_workspace_bytes(B, H, Lq, Lk).
+                                            Ignored together with NO_TILE_SKIP. */
 
 /* Human-readable name of a status. Never NULL. */
 const char* dflash_status_string(dflash_status status);
@@ -112,6 +120,16 @@ dflash_status dflash_mla_latent_expand(const void* latent, const void* w_kv_b,
  * non-empty k-tiles and the schedule).  0 if any size is not positive.
  */
 size_t dflash_mla_attn_workspace_bytes(int64_t B, int64_t Lq, int64_t Lk);
+
+/*
+ * Bytes of workspace a BF16 dflash_mla_attn / dflash_mla_attn_lse /
+ * dflash_mla_attn_blocks call with DFLASH_ATTN_SPLIT_KEYS needs: the tile map
+ * (same layout and offsets as dflash_mla_attn_workspace_bytes) followed by the
+ * fp32 partial outputs of the key-range runs, [S, B, H, Lq, Dv] and [S, B, H, Lq],
+ * S in {1, 2, 4, 8} chosen from the shape (S = 1: the map size alone, no split).
+ * 0 if any size is not positive or the sizes overflow.
+ */
+size_t dflash_mla_attn_split_workspace_bytes(int64_t B, int64_t H, int64_t Lq, int64_t Lk);
 
 /*
  * Where the occupancy results sit inside the workspace, so a caller can read
@@ -183,7 +201,10 @@ dflash_status dflash_mla_mask_occupancy(const void* additive_mask, dflash_dtype 
  *   definition does.
  * Workspace (BF16 with a mask): at least dflash_mla_attn_workspace_bytes(B, Lq, Lk)
  *   bytes, 256-byte aligned; unused (may be NULL/0) when the mask is NULL or dt is F32.
- * flags: any of DFLASH_ATTN_REUSE_TILE_MAP, DFLASH_ATTN_NO_TILE_SKIP, DFLASH_ATTN_CHECK_ONLY.
+ * flags: any of DFLASH_ATTN_REUSE_TILE_MAP, DFLASH_ATTN_NO_TILE_SKIP, DFLASH_ATTN_CHECK_ONLY,
+ *   DFLASH_ATTN_SPLIT_KEYS (BF16; ignored by F32).  With SPLIT_KEYS on a shape that
+ *   splits, the workspace is required (also without a mask): NULL or smaller than
+ *   dflash_mla_attn_split_workspace_bytes returns WORKSPACE.
  * additive_mask NULL with DFLASH_ATTN_REUSE_TILE_MAP (BF16 only): the tile map
  *   already in the workspace alone decides which keys each query sees -- e.g. a
  *   map from dflash_mla_block_occupancy, which makes this the block-structure
@@ -405,8 +426,11 @@ dflash_status dflash_mla_block_occupancy(const int32_t* anchors, const int32_t* 
  * dflash_mla_block_occupancy): out equals dflash_mla_attn with the dense 0 / -inf
  * additive mask of that structure, bitwise.  Lq = A * block_size, Lk = ctx + Lq;
  * tensors as for dflash_mla_attn.  BF16 only (F32 returns UNSUPPORTED).  The
- * workspace is required.  flags: 0 or DFLASH_ATTN_REUSE_TILE_MAP (the workspace
- * holds the map of this same structure, e.g. for the next draft layer).
+ * workspace is required.  flags: 0 or any of DFLASH_ATTN_REUSE_TILE_MAP (the
+ * workspace holds the map of this same structure, e.g. for the next draft layer)
+ * and DFLASH_ATTN_SPLIT_KEYS (as for dflash_mla_attn: then the result equals the
+ * dense-mask call with SPLIT_KEYS bitwise, and the workspace must hold
+ * dflash_mla_attn_split_workspace_bytes).
  */
 dflash_status dflash_mla_attn_blocks(const void* q, const void* k_nope, const void* k_rope_shared,
                                      const void* v, const int32_t* anchors, const int32_t* ctx_valid,

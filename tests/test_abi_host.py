@@ -308,3 +308,31 @@ def test_map_only_reuse_validation(lib):
     assert _attn(lib, flags=0x1) == 3
     assert _attn(lib, flags=0x1, dt=0) == 1
     assert _attn(lib, flags=0x3, ws=FAKE * 256, wsb=1 << 20) == 1
+
+
+def test_split_keys_workspace_bytes(lib):
+    mb, sb = lib.dflash_mla_attn_workspace_bytes, lib.dflash_mla_attn_split_workspace_bytes
+    assert sb(1, 64, 1024, 9216) == mb(1, 1024, 9216)      # 512 items already: no split, the map alone
+    assert sb(1, 2, 32, 96) == mb(1, 32, 96)               # 2 k-tiles: too short to split
+    # 2 batches x 2 q-tiles x 16 heads = 64 items over 36 k-tiles: 4 runs
+    rows, m = 2 * 16 * 256, mb(2, 256, 2304)
+    n = sb(2, 16, 256, 2304)
+    assert m + 4 * rows * (128 * 4 + 4) <= n <= m + 4 * rows * (128 * 4 + 4) + 3 * 256
+    # 1 x 1 q-tile x 8 heads over 129 k-tiles: 8 runs (the cap)
+    n8 = sb(1, 8, 16, 8208)
+    assert n8 >= mb(1, 16, 8208) + 8 * 8 * 16 * (128 * 4 + 4)
+    assert sb(0, 1, 32, 96) == 0 and sb(1, 0, 32, 96) == 0 and sb(1, 1, 0, 96) == 0
+
+
+def test_split_keys_validation(lib):
+    big = dict(q=1 << 40, kn=2 << 40, kr=3 << 40, v=4 << 40, out=5 << 40, B=2, H=16, Lq=256, Lk=2304)
+    need = lib.dflash_mla_attn_split_workspace_bytes(2, 16, 256, 2304)
+    ws = 6 << 40
+    assert _attn(lib, flags=0x8, **big) == 3                               # a split shape needs the workspace
+    assert _attn(lib, flags=0x8, ws=ws, wsb=need - 256, **big) == 3        # too small for the partials
+    assert _attn(lib, flags=0x8, ws=ws + 16, wsb=need, **big) == 1         # misaligned
+    assert _attn(lib, flags=0x8, ws=(4 << 40) + 256, wsb=need, **big) == 1  # overlaps v
+    assert _attn(lib, flags=0xC, ws=ws, wsb=need, **big) == 0              # valid (check only)
+    assert _attn(lib, flags=0xC, dt=0, **big) == 0                         # f32 ignores the split
+    assert _attn(lib, flags=0xE, **big) == 0                               # ignored with NO_TILE_SKIP (no mask)
+    assert _attn(lib, flags=0xC, ws=None, wsb=0) == 0                      # a shape that does not split

@@ -289,7 +289,7 @@ def test_tile_map_many_rows_order(dev):
 def test_skip_on_equals_skip_off_bitwise(dev):
     wl = W.custom(seed=19, B=2, H=4, ctx=900, A=12, bs=16, dtype="bf16", mask_dtype="bf16")
     q, kn, kr, v, m = _to(dev, wl.q, wl.k_nope, wl.k_rope, wl.v, wl.mask)
-    a = mla.mla_attn(q, kn, kr, v, m, tile_skip=True)
+    a = mla.mla_attn(q, kn, kr, v, m, tile_skip=True, split_keys=False)   # (visiting every tile is unsplit)
     b = mla.mla_attn(q, kn, kr, v, m, tile_skip=False)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
@@ -298,7 +298,8 @@ def test_skip_on_equals_skip_off_bitwise(dev):
 def test_deterministic_and_reuse_tile_map(dev):
     wl = W.custom(seed=20, B=1, H=8, ctx=1500, A=24, bs=16, dtype="bf16", mask_dtype="f32")
     q, kn, kr, v, m = _to(dev, wl.q, wl.k_nope, wl.k_rope, wl.v, wl.mask)
-    ws = mla.new_workspace(wl.B, wl.Lq, wl.Lk, dev)
+    ws = mla.new_workspace(wl.B, wl.Lq, wl.Lk, dev, H=wl.H)   # 24 work items: split over keys
+    assert ws.numel() > mla.attn_workspace_bytes(wl.B, wl.Lq, wl.Lk)
     a = mla.mla_attn(q, kn, kr, v, m, workspace=ws)
     b = mla.mla_attn(q, kn, kr, v, m, workspace=ws)
     q2 = torch.flip(q, dims=[1]).contiguous()               # "next layer": new q, same mask
