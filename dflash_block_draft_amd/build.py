@@ -30,8 +30,12 @@ COMMON_FLAGS = [
 # (dK, dV or dQ) plus register-resident operands; letting the MFMAs write their
 # score tiles to ordinary VGPRs (which the softmax reads anyway) instead of
 # accumulator registers avoids spilling.
+#
+# The GQA block attention rescales its output accumulators on the vector unit;
+# in VGPR form they need no copies out of and back into accumulator registers.
 FILE_FLAGS = {
     "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "gqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -893,17 +893,32 @@ bool gqa_layout(int64_t B, int64_t bs, int64_t Hq, int64_t Hkv, int64_t Lmax, si
   return true;
 }
 
+double yarn_mscale(double scale, double m) { return scale <= 1.0 ? 1.0 : 0.1 * m * std::log(scale) + 1.0; }
+
+// yarn RoPE as DeepSeek-V3 defines it (fp64): per rotary pair i of the 128-wide
+// head, the extrapolated frequency theta^(-2i/d) and the interpolated one (divided
+// by factor) blended by a linear ramp between the correction dimensions of
+// beta_fast and beta_slow rotations at the original context length; cos / sin
+// are scaled by mscale(factor, mscale) / mscale(factor, mscale_all_dim).
+// rope = {theta, factor, original length, beta_fast, beta_slow, mscale, mscale_all_dim}.
 dflash::NormRopeArgs norm_rope_args(const float* rope, const void* gamma, float eps) {
   dflash::NormRopeArgs n = {};
   n.gamma = static_cast<const uint16_t*>(gamma);
   n.eps = eps;
-  n.theta = rope[0];
-  n.factor = rope[1];
-  n.orig_max_pos = rope[2];
-  n.beta_fast = rope[3];
-  n.beta_slow = rope[4];
-  n.mscale = rope[5];
-  n.mscale_all_dim = rope[6];
+  const double theta = rope[0], factor = rope[1], omp = rope[2], beta_fast = rope[3], beta_slow = rope[4];
+  const double d = 128.0, two_pi = 6.283185307179586, lb = 2.0 * std::log(theta);
+  double low = std::floor(d * std::log(omp / (beta_fast * two_pi)) / lb);
+  double high = std::ceil(d * std::log(omp / (beta_slow * two_pi)) / lb);
+  low = std::fmax(low, 0.0);
+  high = std::fmin(high, d - 1.0);
+  if (low == high) high += 0.001;
+  for (int i = 0; i < 64; ++i) {
+    const double extra = 1.0 / std::pow(theta, 2.0 * i / d);
+    const double inter = extra / factor;
+    const double ramp = std::fmin(std::fmax((i - low) / (high - low), 0.0), 1.0);
+    n.inv_freq[i] = inter * ramp + extra * (1.0 - ramp);
+  }
+  n.mscale = static_cast<float>(yarn_mscale(factor, rope[5]) / yarn_mscale(factor, rope[6]));
   return n;
 }
 
@@ -1003,6 +1018,8 @@ dflash_status dflash_gqa_forward_block(const void* blk_hidden, const void* w_q, 
   if (bs > Lmax) return fail(DFLASH_ERR_INVALID_ARG, "the block is longer than the cache");
   if (head_dim != 128 || hidden % 32 != 0 || Lmax % 8 != 0 || Hq % Hkv != 0 || (Hq / Hkv) * bs > 64)
     return fail(DFLASH_ERR_UNSUPPORTED, "head_dim 128, hidden % 32, Lmax % 8, Hq % Hkv and (Hq / Hkv) * bs <= 64 required");
+  if (Lmax * 128 * 2 > INT32_MAX)   // one (batch row, KV head) slice of the cache is read through a 32-bit buffer range
+    return fail(DFLASH_ERR_UNSUPPORTED, "Lmax must be below 2^23 keys");
   size_t qo, oo, mlo, need;
   if (!gqa_layout(B, bs, Hq, Hkv, Lmax, &qo, &oo, &mlo, &need) || hidden > INT32_MAX)
     return fail(DFLASH_ERR_UNSUPPORTED, "sizes too large");

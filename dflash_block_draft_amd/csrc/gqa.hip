@@ -25,6 +25,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace dflash {
 namespace {
 
@@ -34,6 +36,7 @@ constexpr int kSK = kD * 2 + 16;              // K tile row stride (bytes): 272
 constexpr int kSV = kKT * 2 + 16;             // V^T tile row stride (bytes): 144
 constexpr int kStageK = kKT * kSK;
 constexpr int kStage = kStageK + kD * kSV;    // 35840 bytes
+constexpr int kDepth = 3;                      // tiles in flight: register sets = LDS stages
 
 __device__ __forceinline__ float bf16r(float x) { return bf16_bits_to_f32(pack_bf16x2(x, 0.f) & 0xFFFFu); }
 
@@ -46,69 +49,67 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// yarn inverse frequency of rotary pair i (DeepSeek-V3 yarn), fp64
-__device__ double yarn_inv_freq(int i, const NormRopeArgs& a) {
-  const double d = kD;
-  const double extra = 1.0 / pow(a.theta, 2.0 * i / d);
-  const double inter = extra / a.factor;
-  const double two_pi = 6.283185307179586;
-  const double lb = 2.0 * log(a.theta);
-  double low = floor(d * log(a.orig_max_pos / (a.beta_fast * two_pi)) / lb);
-  double high = ceil(d * log(a.orig_max_pos / (a.beta_slow * two_pi)) / lb);
-  low = fmax(low, 0.0);
-  high = fmin(high, d - 1.0);
-  if (low == high) high += 0.001;
-  const double ramp = fmin(fmax((i - low) / (high - low), 0.0), 1.0);
-  return inter * ramp + extra * (1.0 - ramp);
-}
-
-__device__ double yarn_mscale(double scale, double m) { return scale <= 1.0 ? 1.0 : 0.1 * m * log(scale) + 1.0; }
-
 constexpr int kRopeTok = 4;                    // tokens per norm/rope workgroup
 
+constexpr int kRopeBatch = 8;                  // (token, head) rows a wave loads before it computes
+
 __global__ void __launch_bounds__(256) norm_rope_bf16(NormRopeArgs a) {
-  __shared__ double s_inv[kD / 2];
   __shared__ float s_cos[kRopeTok][kD / 2], s_sin[kRopeTok][kD / 2];
   const int b = blockIdx.y;
   const int tbase = blockIdx.x * kRopeTok;
   const int t0 = a.row_off ? min(max(a.row_off[b], 0), a.off_max) : 0;
-  if (threadIdx.x < kD / 2) s_inv[threadIdx.x] = yarn_inv_freq(threadIdx.x, a);
-  __syncthreads();
   {  // one angle per thread: the product and its reduction modulo 2 pi in fp64, sin / cos in fp32
     const int tk = threadIdx.x / (kD / 2), i = threadIdx.x % (kD / 2);
     const double two_pi = 6.283185307179586;
-    const double ang = static_cast<double>(t0 + tbase + tk) * s_inv[i];
+    const double ang = static_cast<double>(t0 + tbase + tk) * a.inv_freq[i];
     const float red = static_cast<float>(ang - floor(ang / two_pi) * two_pi);
-    const float ms = static_cast<float>(yarn_mscale(a.factor, a.mscale) / yarn_mscale(a.factor, a.mscale_all_dim));
     float sn, cs;
     sincosf(red, &sn, &cs);
-    s_cos[tk][i] = cs * ms;
-    s_sin[tk][i] = sn * ms;
+    s_cos[tk][i] = cs * a.mscale;
+    s_sin[tk][i] = sn * a.mscale;
   }
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float g0 = bf16_bits_to_f32(a.gamma[lane]), g1 = bf16_bits_to_f32(a.gamma[lane + 64]);
-  for (int job = wave; job < kRopeTok * a.H; job += 4) {
-    const int tk = job / a.H, h = job % a.H;
-    const int t = tbase + tk;
-    if (t >= a.T) break;                              // jobs are token-major: the rest are past T too
-    const int row_t = a.rows_local ? t : t0 + t;
-    uint16_t* row = a.x + ((static_cast<size_t>(b) * a.H + h) * a.Lt + row_t) * kD;
-    const float x0 = bf16_bits_to_f32(row[lane]), x1 = bf16_bits_to_f32(row[lane + 64]);
-    float ss = x0 * x0 + x1 * x1;
+  const int njobs = min(kRopeTok, a.T - tbase) * a.H;   // token-major (token, head) rows of this workgroup
+  // each wave takes jobs wave, wave + 4, ...; the rows of a batch are all loaded
+  // before any is normalised, so their latencies overlap
+  for (int base = wave; base < njobs; base += 4 * kRopeBatch) {
+    float x0[kRopeBatch], x1[kRopeBatch];
+    uint16_t* rows[kRopeBatch];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-    const float r = rsqrtf(ss / kD + a.eps);
-    const float n0 = bf16r(bf16r(x0 * r) * g0), n1 = bf16r(bf16r(x1 * r) * g1);
-    const float c = s_cos[tk][lane], sn = s_sin[tk][lane];
-    const uint32_t w = pack_bf16x2(n0 * c - n1 * sn, n1 * c + n0 * sn);
-    row[lane] = static_cast<uint16_t>(w & 0xFFFFu);
-    row[lane + 64] = static_cast<uint16_t>(w >> 16);
+    for (int u = 0; u < kRopeBatch; ++u) {
+      const int job = min(base + 4 * u, njobs - 1);      // past the end: a repeat of the last row, not stored
+      const int tk = job / a.H, h = job % a.H;
+      const int t = tbase + tk;
+      const int row_t = a.rows_local ? t : t0 + t;
+      rows[u] = a.x + ((static_cast<size_t>(b) * a.H + h) * a.Lt + row_t) * kD;
+      x0[u] = bf16_bits_to_f32(rows[u][lane]);
+      x1[u] = bf16_bits_to_f32(rows[u][lane + 64]);
+    }
+#pragma unroll
+    for (int u = 0; u < kRopeBatch; ++u) {
+      const int job = base + 4 * u;
+      float ss = x0[u] * x0[u] + x1[u] * x1[u];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+      if (job >= njobs) continue;
+      const int tk = job / a.H;
+      const float r = rsqrtf(ss / kD + a.eps);
+      const float n0 = bf16r(bf16r(x0[u] * r) * g0), n1 = bf16r(bf16r(x1[u] * r) * g1);
+      const float c = s_cos[tk][lane], sn = s_sin[tk][lane];
+      const uint32_t w = pack_bf16x2(n0 * c - n1 * sn, n1 * c + n0 * sn);
+      rows[u][lane] = static_cast<uint16_t>(w & 0xFFFFu);
+      rows[u][lane + 64] = static_cast<uint16_t>(w >> 16);
+    }
   }
 }
 
+template <int N>
+using IC = std::integral_constant<int, N>;
+
 __global__ void __launch_bounds__(256) gqa_attn_bf16(GqaAttnArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+  __shared__ __attribute__((aligned(16))) char smem[kDepth * kStage];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int li = lane & 31, hi = lane >> 5;
   const int qb = w & 1, kh = w >> 1;
@@ -139,48 +140,69 @@ __global__ void __launch_bounds__(256) gqa_attn_bf16(GqaAttnArgs a) {
     for (int e = 0; e < 16; ++e) o[j][e] = 0.f;
   float m = -INFINITY, l = 0.f;                       // log2 units
 
-  u32x4_t pre[8];
-  auto prefetch = [&](int tile) {
-    const int k0 = tile * kKT;
+  // Tile i of the split goes global -> registers set i % kDepth (issued kDepth - 1
+  // tiles ahead) -> LDS stage i % kDepth: while tile i is computed, the loads of
+  // tiles i+1 .. i+kDepth are in flight (the register sets come from the file this
+  // one-wave-per-SIMD kernel has to spare).  The loads go through buffer resources
+  // and are issued unconditionally, so the compiler can count them (a wait for one
+  // set leaves the younger sets in flight): K rows past L read as zeros (the
+  // resource ends at row L), a tile past the split uses an offset beyond both
+  // resources (zeros, no traffic), and V^T keys past L are zeroed when the tail
+  // tile is committed (they are inside the resource: the cache there is unset).
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kbase), 0, L * kD * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vbase), 0, kD * a.Lmax * 2, 0x00020000);
+  constexpr uint32_t kPastEnd = 0x80000000u;   // > every resource size (the host bounds a slice by 2^31 bytes)
+  uint32_t kvo[4], vvo[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {                     // K: 64 rows x 16 chunks
-      const int ci = t + 256 * c, row = ci >> 4, ch = ci & 15, key = k0 + row;
-      const u32x4_t z = {0u, 0u, 0u, 0u};
-      pre[c] = key < L ? ldg16(kbase + static_cast<size_t>(key) * kD + 8 * ch) : z;
+  for (int c = 0; c < 4; ++c) {
+    const int ci = t + 256 * c;
+    kvo[c] = static_cast<uint32_t>((ci >> 4) * kD * 2 + (ci & 15) * 16);        // K: 64 rows x 16 chunks
+    vvo[c] = static_cast<uint32_t>((ci >> 3) * a.Lmax * 2 + (ci & 7) * 16);     // V^T: 128 rows x 8 chunks of 8 keys
+  }
+  u32x4_t pre[kDepth][8];
+  auto prefetch = [&](auto S, int tile) __attribute__((always_inline)) {
+    constexpr int set = decltype(S)::value;
+    const bool real = tile < tile1;
+    const uint32_t ks = real ? static_cast<uint32_t>(tile) * kKT * kD * 2 : kPastEnd;
+    const uint32_t vs = real ? static_cast<uint32_t>(tile) * kKT * 2 : kPastEnd;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      pre[set][c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, kvo[c], ks, 0));
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      pre[set][4 + c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, vvo[c], vs, 0));
+  };
+  auto commit = [&](auto S, int tile) __attribute__((always_inline)) {
+    constexpr int set = decltype(S)::value;
+    char* st = smem + set * kStage;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int ci = t + 256 * c;
+      *reinterpret_cast<u32x4_t*>(st + (ci >> 4) * kSK + (ci & 15) * 16) = pre[set][c];
     }
+    if ((tile + 1) * kKT > L) {                     // the tail tile: zero V^T keys >= L
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {                     // V^T: 128 rows x 8 chunks of 8 keys
-      const int ci = t + 256 * c, row = ci >> 3, ch = ci & 7, key = k0 + 8 * ch;
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (key < L) {
-        x = ldg16(vbase + static_cast<size_t>(row) * a.Lmax + key);
-        if (key + 8 > L) {                            // zero the keys past the end (the cache there is unset)
+      for (int c = 0; c < 4; ++c) {
+        const int key = tile * kKT + 8 * ((t + 256 * c) & 7);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int k2 = key + 2 * e;
-            const uint32_t keep = (k2 < L ? 0x0000FFFFu : 0u) | (k2 + 1 < L ? 0xFFFF0000u : 0u);
-            x[e] &= keep;
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int k2 = key + 2 * e;
+          const uint32_t keep = (k2 < L ? 0x0000FFFFu : 0u) | (k2 + 1 < L ? 0xFFFF0000u : 0u);
+          pre[set][4 + c][e] &= keep;
         }
       }
-      pre[4 + c] = x;
-    }
-  };
-  auto commit = [&](char* st) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int ci = t + 256 * c;
-      *reinterpret_cast<u32x4_t*>(st + (ci >> 4) * kSK + (ci & 15) * 16) = pre[c];
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int ci = t + 256 * c;
-      *reinterpret_cast<u32x4_t*>(st + kStageK + (ci >> 3) * kSV + (ci & 7) * 16) = pre[4 + c];
+      *reinterpret_cast<u32x4_t*>(st + kStageK + (ci >> 3) * kSV + (ci & 7) * 16) = pre[set][4 + c];
     }
   };
 
   const float c2 = a.scale * kLog2e;
-  auto compute = [&](const char* st, int tile) {
+  auto compute = [&](const char* st, int tile) __attribute__((always_inline)) {
     f32x16_t s = {};
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.f;
@@ -199,19 +221,22 @@ __global__ void __launch_bounds__(256) gqa_attn_bf16(GqaAttnArgs a) {
     // finite stabiliser keeps exp2(-inf - m) = 0 instead of exp2(-inf + inf) = NaN
     const float m_new = fmaxf(m, halves_max(tmax));
     const float m_sub = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
+    if (__any(m_new != m)) {          // rescale only when some row's maximum rose (alpha = 1 elsewhere)
+      const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int j = 0; j < kD / 32; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[j][e] *= alpha;
+      m = m_new;
+    }
     float p[16], sum = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       p[e] = bf16r(__builtin_amdgcn_exp2f(x[e] - m_sub));
       sum += p[e];
     }
-    l = l * alpha + halves_sum(sum);
-    m = m_new;
-#pragma unroll
-    for (int j = 0; j < kD / 32; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[j][e] *= alpha;
+    l += halves_sum(sum);
     bf16x8_t pb[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -234,17 +259,32 @@ __global__ void __launch_bounds__(256) gqa_attn_bf16(GqaAttnArgs a) {
     }
   };
 
-  if (tile0 < tile1) {
-    prefetch(tile0);
-    commit(smem);
+  // One step on tile `tile` (set / stage S = its index % kDepth): start the loads of
+  // tile + kDepth - 1 (past the split: a no-traffic zero read) into the set tile - 1
+  // used (committed one step ago), compute,
+  // then commit tile + 1 into its stage (last read by the step before this one,
+  // which every wave has left: the barrier that ended it).  Returns false after the
+  // split's last tile.
+  auto step = [&](auto S, int tile) __attribute__((always_inline)) -> bool {
+    constexpr int set = decltype(S)::value;
+    constexpr int prev = (set + kDepth - 1) % kDepth, next = (set + 1) % kDepth;
+    prefetch(IC<prev>{}, tile + kDepth - 1);
+    compute(smem + set * kStage, tile);
+    if (tile + 1 >= tile1) return false;
+    commit(IC<next>{}, tile + 1);
     __syncthreads();
-    for (int tile = tile0; tile < tile1; ++tile) {
-      const bool more = tile + 1 < tile1;
-      if (more) prefetch(tile + 1);
-      compute(smem + ((tile - tile0) & 1) * kStage, tile);
-      if (!more) break;
-      commit(smem + ((tile + 1 - tile0) & 1) * kStage);
-      __syncthreads();
+    return true;
+  };
+  if (tile0 < tile1) {
+    static_assert(kDepth == 3, "the prologue and the unrolled loop below are written for three sets");
+    prefetch(IC<0>{}, tile0);
+    prefetch(IC<1>{}, tile0 + 1);
+    commit(IC<0>{}, tile0);
+    __syncthreads();
+    for (int tile = tile0;; tile += kDepth) {
+      if (!step(IC<0>{}, tile)) break;
+      if (!step(IC<1>{}, tile + 1)) break;
+      if (!step(IC<2>{}, tile + 2)) break;
     }
   }
   __syncthreads();

@@ -124,7 +124,8 @@ struct NormRopeArgs {
   const int32_t* row_off; int off_max;
   int rows_local;                         // 1: rows 0 .. T-1 (positions still t0(b) + t)
   const uint16_t* gamma; float eps;
-  double theta, factor, orig_max_pos, beta_fast, beta_slow, mscale, mscale_all_dim;
+  double inv_freq[64];                    // yarn inverse frequency of each rotary pair (fp64, from the host)
+  float mscale;                           // cos / sin scale of yarn
 };
 
 // Block attention of the GQA draft: q [B, Hq, bs, d]; k cache [B, Hkv, Lmax, d];

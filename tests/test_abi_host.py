@@ -295,7 +295,8 @@ def test_gqa_validation(lib):
     good = [FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, FAKE * 6, 1e-6, C.cast(rope, C.c_void_p), FAKE * 64,
             FAKE * 128, FAKE * 7, FAKE * 8, 1, 16, 128, 256, 8, 2, 128, 0.088, FAKE * 256, 1 << 26, None]
     for idx, val, status in ((10, None, 1), (10, FAKE * 7 + 2, 1), (16, 7, 2), (13, 32, 2), (13, 200, 1),
-                             (19, 0.0, 1), (20, None, 3), (21, 64, 3), (11, FAKE * 64, 1)):
+                             (19, 0.0, 1), (20, None, 3), (21, 64, 3), (11, FAKE * 64, 1),
+                             (14, 1 << 23, 2)):                 # a cache slice beyond a 32-bit buffer range
         args = list(good)
         args[idx] = val
         assert fb(*args) == status, (idx, val)
