@@ -871,9 +871,15 @@ struct GqaSplit {
   int splits, tiles_per_split;
 };
 
+// Key splits of the GQA block attention: about one workgroup per compute unit in
+// total (256), so every split starts at once and none waits for a second round.
+// Measured on 8 rows x 8 KV heads with 8K-32K contexts: 4 splits (256 workgroups)
+// beat 6, 8, 16 and 32, and beat splitting each row in proportion to its length
+// from the device-side context lengths (the rounding up of every row's share
+// pushed some workgroups into a second round).
 GqaSplit gqa_split(int64_t B, int64_t Hkv, int64_t Lmax) {
   const int64_t ntiles = (Lmax + 63) / 64;
-  int64_t want = (1024 + B * Hkv - 1) / (B * Hkv);
+  int64_t want = (256 + B * Hkv - 1) / (B * Hkv);
   want = std::max<int64_t>(1, std::min(want, ntiles));
   const int64_t tps = (ntiles + want - 1) / want;
   return {static_cast<int>((ntiles + tps - 1) / tps), static_cast<int>(tps)};
