@@ -575,8 +575,9 @@ dflash_status dflash_mla_attn_bwd(const void* q, const void* k_nope, const void*
   if (L.t.nkt > dflash::kMaxKeyTiles || bh * L.t.nqt > INT32_MAX || L.Lqp > INT32_MAX || L.Lkp > INT32_MAX)
     return fail(DFLASH_ERR_UNSUPPORTED, "sizes too large for the backward launches");
   // the staging loads address one (b, h) slice of each operand through a 32-bit range
-  if (L.Lkp * 2 * 192 > INT32_MAX || L.Lqp * 2 * 192 > INT32_MAX)
-    return fail(DFLASH_ERR_UNSUPPORTED, "the backward takes at most 2^31 bytes per (batch, head) operand slice");
+  if (L.Lkp * 2 * 192 > INT32_MAX || L.Lqp * 2 * 192 > INT32_MAX || B * L.t.nqt * L.t.nkt * 1024 > INT32_MAX)
+    return fail(DFLASH_ERR_UNSUPPORTED, "the backward takes at most 2^31 bytes per (batch, head) operand slice "
+                "and per tile-map visibility array");
   if (!workspace) return fail(DFLASH_ERR_WORKSPACE, "workspace is NULL");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(DFLASH_ERR_WORKSPACE, "workspace is not 256-byte aligned");
   if (workspace_bytes < L.total)

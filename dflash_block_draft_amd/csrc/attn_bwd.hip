@@ -27,17 +27,27 @@
 //     B operand of dQ^T += K^T dS^T, with K^T from the transposed copy.
 //  5. rope_reduce: dk_rope = sum over heads of the per-head parts, in head order.
 //
-// Operand staging is plain: 16-byte global loads into registers one chunk /
-// tile ahead, then 16-byte LDS stores into the other half of a double buffer,
-// with LDS rows padded by 16 bytes so the 16-byte column reads of 16 lanes hit
-// distinct banks.  Masks: class-0 tiles are skipped, class-1 tiles need no
+// Operand staging: dK/dV copies each 32-query chunk global -> LDS through the
+// buffer unit (no staging registers) into a three-stage ring, two chunks ahead;
+// dQ loads each 64-key tile into registers one tile ahead and stores it into the
+// other half of a double buffer.  LDS rows are padded by 16 bytes so the 16-byte
+// column reads of 16 lanes hit distinct banks.  Every staging load is issued
+// unconditionally (past the end: an offset beyond the resource, zeros, no
+// traffic) and the loads the compiler must wait for are issued before them, so
+// no wait in the loops drains the copies in flight.  Masks: class-0 tiles are skipped, class-1 tiles need no
 // mask work, class-2 tiles zero p for keys whose visibility bit is clear,
 // class-3 tiles add the mask values; keys past Lk get p = 0.
 #include "common.h"
+#include "dma.h"
 #include "launch.h"
+
+#include <type_traits>
 
 namespace dflash {
 namespace {
+
+template <int N>
+using IC = std::integral_constant<int, N>;
 
 constexpr int kThreads = 256;
 constexpr int kQC = 32;                         // queries per dK/dV chunk
@@ -48,16 +58,23 @@ constexpr int kSO = kDv * 2 + 16;               // 272: dout / v rows
 constexpr int kSQT = kQC * 2 + 16;              // 80:  transposed q / dout rows (32 queries)
 constexpr int kSKT = kTileN * 2 + 16;           // 144: transposed k rows (64 keys)
 
-// dK/dV stage: Q, dO, Q^T, dO^T, lse2, D, visibility words (32 rows x 2 k-tiles)
-constexpr int kA_Q = 0;
-constexpr int kA_O = kA_Q + kQC * kSQ;
-constexpr int kA_QT = kA_O + kQC * kSO;
-constexpr int kA_OT = kA_QT + kDqk * kSQT;
-constexpr int kA_L = kA_OT + kDv * kSQT;
-constexpr int kA_D = kA_L + kQC * 4;
-constexpr int kA_B = kA_D + kQC * 4;
-constexpr int kA_Stage = kA_B + kQC * 2 * 8;
-static_assert(kA_Stage % 16 == 0, "stage alignment");
+// dK/dV stage: Q, dO, Q^T, dO^T, lse2, D, visibility words (2 k-tiles x 32 rows),
+// each region rounded up to whole 1 KiB blocks: one block is one buffer -> LDS copy
+// instruction (64 lanes x 16 bytes), and no instruction spans two sources.
+constexpr int kA_Q = 0;                          // 32 rows x 400 B in 13 blocks
+constexpr int kA_O = kA_Q + 13 * 1024;           // 32 rows x 272 B in 9 blocks
+constexpr int kA_QT = kA_O + 9 * 1024;           // 192 rows x 80 B = 15 blocks
+constexpr int kA_OT = kA_QT + 15 * 1024;         // 128 rows x 80 B = 10 blocks
+constexpr int kA_L = kA_OT + 10 * 1024;          // 32 floats
+constexpr int kA_D = kA_L + 1024;                // 32 floats
+constexpr int kA_B = kA_D + 1024;                // [2 k-tiles][32 rows] uint64
+constexpr int kA_Stage = kA_B + 1024;            // 50 blocks
+constexpr int kA_Blocks = kA_Stage / 1024;
+constexpr int kA_Stages = 3;                     // chunks in flight: the next two while one is computed
+constexpr int kA_PerWave = (kA_Blocks + 3) / 4;  // copy instructions per wave and stage: 13 (the last wave 11)
+static_assert(kQC * kSQ <= 13 * 1024 && kQC * kSO <= 9 * 1024 && kDqk * kSQT == 15 * 1024 && kDv * kSQT == 10 * 1024,
+              "dK/dV stage regions");
+static_assert(kA_Stages * kA_Stage <= 160 * 1024, "LDS budget");
 
 // dQ stage: K, V, K^T
 constexpr int kB_K = 0;
@@ -212,10 +229,40 @@ __global__ void __launch_bounds__(kThreads) bwd_prep_k(AttnBwdArgs a) {
 }
 
 // ---------------------------------------------------------------- 3. dK / dV
+// Copy plan of the dK/dV stage: block `blk` (0..49) of a stage, lane l: the source
+// region, the lane's byte offset inside it (fixed for the kernel; the chunk moves
+// the uniform offset) -- padding chunks of a row and lanes past a region's rows
+// re-read a valid chunk of the same row / region, landing in LDS padding.
+enum : int { kRegQ, kRegO, kRegQT, kRegOT, kRegL, kRegD, kRegB };
+__device__ __forceinline__ int a_region(int blk) {
+  return blk < 13 ? kRegQ : blk < 22 ? kRegO : blk < 37 ? kRegQT : blk < 47 ? kRegOT : blk - 47 + kRegL;
+}
+__device__ __forceinline__ uint32_t a_voff(int blk, int lane, int Lqp) {
+  switch (a_region(blk)) {
+    case kRegQ: {
+      const int j = blk * 64 + lane, row = j / 25, col = j % 25;
+      return row >= kQC ? 0u : static_cast<uint32_t>(row * (kDqk * 2) + (col < 24 ? col : 0) * 16);
+    }
+    case kRegO: {
+      const int j = (blk - 13) * 64 + lane, row = j / 17, col = j % 17;
+      return row >= kQC ? 0u : static_cast<uint32_t>(row * (kDv * 2) + (col < 16 ? col : 0) * 16);
+    }
+    case kRegQT: case kRegOT: {
+      const int j = (blk - (blk < 37 ? 22 : 37)) * 64 + lane, row = j / 5, col = j % 5;
+      return static_cast<uint32_t>(row) * Lqp * 2 + (col < 4 ? col : 0) * 16;
+    }
+    case kRegL: case kRegD: return lane < 8 ? lane * 16u : 0u;
+    default:  // visibility words: lanes 0..15 the first k-tile's 32 rows, 16..31 the second's
+      return lane < 16 ? lane * 16u : lane < 32 ? 1024u + (lane - 16) * 16u : 0u;
+  }
+}
+
 template <bool MASK_BF16>
 __global__ void __launch_bounds__(kThreads) bwd_dkdv(AttnBwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kA_Stage];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  __shared__ __attribute__((aligned(1024))) char smem[kA_Stages * kA_Stage];
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int li = lane & 31, hi = lane >> 5;
   const int kb = blockIdx.x;
   const size_t bh = blockIdx.y;
@@ -237,6 +284,10 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv(AttnBwdArgs a) {
 #pragma unroll
   for (int s = 0; s < 8; ++s)
     vreg[s] = as_bf16x8(key_ok ? ldg16(a.v + (bh * a.Lk + key) * kDv + 16 * s + 8 * hi) : zero4());
+  // K and V in registers before any stage copy: the compiler cannot count the copies
+  // (inline asm), so a wait of its own for these loads inside the loop would be a
+  // full vmcnt(0) -- draining the copies in flight at every chunk
+  wait_vmem<0>();
 
   f32x16_t dk[6], dv[4];
 #pragma unroll
@@ -244,17 +295,23 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv(AttnBwdArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) dv[i] = zero16();
 
-  // chunk iterator over (q-tile, 32-query chunk) with a non-empty tile in kt0 / kt0+1
-  auto tile_cls = [&](int qt, int kt) -> int {
+  // tile classes through scalar loads (the aligned dword holding the byte), so no
+  // vector-memory wait of the compiler's lands between the stage copies
+  typedef __attribute__((address_space(4))) const uint32_t const_u32;
+  auto tile_cls = [&](int qt, int kt) __attribute__((always_inline)) -> int {
     if (!a.classes) return 1;
-    return a.classes[(static_cast<size_t>(b) * a.nqt + qt) * a.nkt + kt];
+    const size_t idx = (static_cast<size_t>(b) * a.nqt + qt) * a.nkt + kt;
+    const const_u32* p = (const const_u32*)(uintptr_t)(a.classes + (idx & ~static_cast<size_t>(3)));
+    return static_cast<int>((p[0] >> (8 * (idx & 3))) & 0xFFu);
   };
+  // chunk iterator over (q-tile, 32-query chunk) with a non-empty tile in kt0 / kt0+1
   auto next_qt = [&](int qt) -> int {
     for (++qt; qt < a.nqt; ++qt)
       if (tile_cls(qt, kt0) != 0 || (has_kt1 && tile_cls(qt, kt0 + 1) != 0)) break;
     return qt;
   };
   auto advance = [&](int& qt, int& c) {
+    if (qt >= a.nqt) return;
     ++c;
     if (c == kTileM / kQC || qt * kTileM + c * kQC >= a.Lq) {
       c = 0;
@@ -262,84 +319,62 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv(AttnBwdArgs a) {
     }
   };
 
-  // staging: per-lane byte offsets are fixed, the chunk moves the uniform offset;
-  // rows past Lq read as zeros through the resources' ranges
-  const __amdgpu_buffer_rsrc_t r_q = rsrc(a.q + bh * a.Lq * kDqk, static_cast<size_t>(a.Lq) * kDqk * 2);
-  const __amdgpu_buffer_rsrc_t r_o = rsrc(a.dout + bh * a.Lq * kDv, static_cast<size_t>(a.Lq) * kDv * 2);
-  const __amdgpu_buffer_rsrc_t r_qt = rsrc(a.qT + bh * kDqk * a.Lqp, static_cast<size_t>(kDqk) * a.Lqp * 2);
-  const __amdgpu_buffer_rsrc_t r_ot = rsrc(a.doT + bh * kDv * a.Lqp, static_cast<size_t>(kDv) * a.Lqp * 2);
-  uint32_t voff_q[3];
+  // ---- stage copies: global -> LDS through the buffer unit (no staging registers).
+  // Wave w copies blocks 13w .. 13w + 12 of each stage; its per-lane offsets are
+  // fixed, the chunk sets the uniform offsets.  A chunk past the end copies with an
+  // offset beyond every resource (zeros, no traffic), so every wave issues the same
+  // number of copies each step and the wait counts are constants.  Rows past Lq
+  // read as zeros through the resources' ranges.
+  const u32x4_t d_q = buffer_desc(a.q + bh * a.Lq * kDqk, static_cast<uint32_t>(a.Lq) * kDqk * 2);
+  const u32x4_t d_o = buffer_desc(a.dout + bh * a.Lq * kDv, static_cast<uint32_t>(a.Lq) * kDv * 2);
+  const u32x4_t d_qt = buffer_desc(a.qT + bh * kDqk * a.Lqp, static_cast<uint32_t>(kDqk) * a.Lqp * 2);
+  const u32x4_t d_ot = buffer_desc(a.doT + bh * kDv * a.Lqp, static_cast<uint32_t>(kDv) * a.Lqp * 2);
+  const u32x4_t d_l = buffer_desc(a.lse2 + bh * a.Lqp, static_cast<uint32_t>(a.Lqp) * 4);
+  const u32x4_t d_d = buffer_desc(a.dd + bh * a.Lqp, static_cast<uint32_t>(a.Lqp) * 4);
+  const u32x4_t d_b = buffer_desc(a.bits, a.bits ? static_cast<uint32_t>(
+                                              static_cast<size_t>(a.B) * a.nqt * a.nkt * kTileM * 8) : 0u);
+  uint32_t voff[kA_PerWave];
 #pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    const int ci = t + kThreads * i;
-    voff_q[i] = (ci / 24) * (kDqk * 2) + (ci % 24) * 16;
+  for (int j = 0; j < kA_PerWave; ++j) {
+    const int blk = kA_PerWave * w + j;
+    voff[j] = blk < kA_Blocks ? a_voff(blk, lane, a.Lqp) : 0u;
   }
-  u32x4_t pre[11];
-  auto prefetch = [&](int qt, int c, int cls0, int cls1) {
-    const int q0 = qt * kTileM + c * kQC;
-#pragma unroll
-    for (int i = 0; i < 3; ++i)                       // q rows: 32 x 24 chunks
-      pre[i] = bload16(r_q, voff_q[i], static_cast<uint32_t>(q0) * (kDqk * 2));
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {                     // dout rows: 32 x 16 chunks
-      const int ci = t + kThreads * i;
-      pre[3 + i] = bload16(r_o, (ci >> 4) * (kDv * 2) + (ci & 15) * 16, static_cast<uint32_t>(q0) * (kDv * 2));
-    }
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {                     // q^T: 192 rows x 4 chunks
-      const int ci = t + kThreads * i;
-      pre[5 + i] = bload16(r_qt, (ci >> 2) * (a.Lqp * 2) + (ci & 3) * 16, static_cast<uint32_t>(q0) * 2);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {                     // dout^T: 128 rows x 4 chunks
-      const int ci = t + kThreads * i;
-      pre[8 + i] = bload16(r_ot, (ci >> 2) * (a.Lqp * 2) + (ci & 3) * 16, static_cast<uint32_t>(q0) * 2);
-    }
-    pre[10] = zero4();
-    if (t < 16) {                                     // lse2 (t < 8), D (8 <= t < 16)
-      const float* src = t < 8 ? a.lse2 : a.dd;
-      pre[10] = *reinterpret_cast<const u32x4_t*>(src + bh * a.Lqp + q0 + 4 * (t & 7));
-    } else if (t < 16 + 2 * kQC) {                    // visibility words of class-2 tiles
-      const int j = t - 16, r = j >> 1, th = j & 1;
-      const int cls = th ? cls1 : cls0;
-      if (cls == 2 && q0 + r < a.Lq) {
-        const size_t tile = (static_cast<size_t>(b) * a.nqt + qt) * a.nkt + kt0 + th;
-        const uint64_t word = a.bits[tile * kTileM + c * kQC + r];
-        pre[10] = u32x4_t{static_cast<uint32_t>(word), static_cast<uint32_t>(word >> 32), 0u, 0u};
+  constexpr uint32_t kPastEnd = 0x80000000u;           // beyond every resource (the host bounds them by 2^31 bytes)
+  auto issue = [&](auto W, uint32_t stage_off, int qt, int c) __attribute__((always_inline)) {
+    constexpr int wv = decltype(W)::value;
+    const bool live = qt < a.nqt;
+    const uint32_t q0 = static_cast<uint32_t>(qt * kTileM + c * kQC);
+    const uint32_t tile = static_cast<uint32_t>(((static_cast<size_t>(b) * a.nqt + qt) * a.nkt + kt0) * kTileM * 8);
+    const uint32_t base = lds0 + stage_off + kA_PerWave * wv * 1024;
+    auto one = [&](auto J) __attribute__((always_inline)) {
+      constexpr int j = decltype(J)::value, blk = kA_PerWave * wv + j;
+      if constexpr (blk < kA_Blocks) {
+        constexpr int reg = blk < 13 ? kRegQ : blk < 22 ? kRegO : blk < 37 ? kRegQT : blk < 47 ? kRegOT : blk - 47 + kRegL;
+        const u32x4_t d = reg == kRegQ ? d_q : reg == kRegO ? d_o : reg == kRegQT ? d_qt : reg == kRegOT ? d_ot
+                        : reg == kRegL ? d_l : reg == kRegD ? d_d : d_b;
+        const uint32_t so = !live ? kPastEnd
+                          : reg == kRegQ ? q0 * (kDqk * 2) : reg == kRegO ? q0 * (kDv * 2)
+                          : reg == kRegQT || reg == kRegOT ? q0 * 2 : reg == kRegB ? tile + c * (kQC * 8) : q0 * 4;
+        dma16<j * 1024>(d, base, voff[j], so);
       }
-    }
+    };
+    one(IC<0>{}); one(IC<1>{}); one(IC<2>{}); one(IC<3>{}); one(IC<4>{}); one(IC<5>{}); one(IC<6>{});
+    one(IC<7>{}); one(IC<8>{}); one(IC<9>{}); one(IC<10>{}); one(IC<11>{}); one(IC<12>{});
+    static_assert(kA_PerWave == 13, "the unrolled copy list above");
   };
-  auto commit = [&](char* st) {
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int ci = t + kThreads * i;
-      *reinterpret_cast<u32x4_t*>(st + kA_Q + (ci / 24) * kSQ + (ci % 24) * 16) = pre[i];   // (constant per thread)
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ci = t + kThreads * i;
-      *reinterpret_cast<u32x4_t*>(st + kA_O + (ci >> 4) * kSO + (ci & 15) * 16) = pre[3 + i];
-    }
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int ci = t + kThreads * i;
-      *reinterpret_cast<u32x4_t*>(st + kA_QT + (ci >> 2) * kSQT + (ci & 3) * 16) = pre[5 + i];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ci = t + kThreads * i;
-      *reinterpret_cast<u32x4_t*>(st + kA_OT + (ci >> 2) * kSQT + (ci & 3) * 16) = pre[8 + i];
-    }
-    if (t < 16) {
-      *reinterpret_cast<u32x4_t*>(st + (t < 8 ? kA_L : kA_D) + 16 * (t & 7)) = pre[10];
-    } else if (t < 16 + 2 * kQC) {
-      const int j = t - 16;
-      *reinterpret_cast<u32x2_t*>(st + kA_B + 8 * j) = u32x2_t{pre[10][0], pre[10][1]};
-    }
+  auto issue_stage = [&](uint32_t stage_off, int qt, int c) __attribute__((always_inline)) {
+    if (w == 0) issue(IC<0>{}, stage_off, qt, c);
+    else if (w == 1) issue(IC<1>{}, stage_off, qt, c);
+    else if (w == 2) issue(IC<2>{}, stage_off, qt, c);
+    else issue(IC<3>{}, stage_off, qt, c);
+  };
+  // this wave's copies of the older stage done, those of the newest one still in flight
+  auto wait_older = [&]() __attribute__((always_inline)) {
+    if (w == 3) wait_vmem<kA_Blocks - 3 * kA_PerWave>(); else wait_vmem<kA_PerWave>();
   };
 
   const float scale_log2 = a.scale * kLog2e;
-  auto compute = [&](const char* st, int qt, int c, int cls) {
+  auto compute = [&](const char* st, int qt, int c, int cls) __attribute__((always_inline)) {
     if (cls == 0) return;
     f32x16_t S = zero16(), dP = zero16();
 #pragma unroll
@@ -368,7 +403,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv(AttnBwdArgs a) {
         const int r = 4 * g + e, qr = 8 * g + 4 * hi + e;   // accumulator row r <-> chunk query qr
         bool vis = key_ok;
         if (cls == 2) {
-          const uint64_t word = *reinterpret_cast<const uint64_t*>(st + kA_B + (2 * qr + (w >> 1)) * 8);
+          const uint64_t word = *reinterpret_cast<const uint64_t*>(st + kA_B + ((w >> 1) * kQC + qr) * 8);
           vis = vis && ((word >> bit) & 1ull);
         }
         const float pr = vis ? __builtin_amdgcn_exp2f(S[r] * scale_log2 - l4[e] + madd[r]) : 0.f;
@@ -394,31 +429,31 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv(AttnBwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  int qt = next_qt(-1), c = 0;
-  if (qt < a.nqt) {
-    int cls0 = tile_cls(qt, kt0), cls1 = has_kt1 ? tile_cls(qt, kt0 + 1) : 0;
-    prefetch(qt, c, cls0, cls1);
-    commit(smem);
+  // chunks it, it+1, it+2 (qt >= nqt: past the end)
+  int qa = next_qt(-1), ca = 0;
+  if (qa < a.nqt) {
+    int qb_ = qa, cb = ca;
+    advance(qb_, cb);
+    int qc = qb_, cc = cb;
+    advance(qc, cc);
+    issue_stage(0, qa, ca);
+    issue_stage(kA_Stage, qb_, cb);
+    wait_older();
     __syncthreads();
-    for (int it = 0;; ++it) {
-      int nqt_ = qt, nc = c;
-      advance(nqt_, nc);
-      const bool more = nqt_ < a.nqt;
-      int ncls0 = 0, ncls1 = 0;
-      if (more) {
-        ncls0 = tile_cls(nqt_, kt0);
-        ncls1 = has_kt1 ? tile_cls(nqt_, kt0 + 1) : 0;
-        prefetch(nqt_, nc, ncls0, ncls1);
-      }
-      compute(smem + (it & 1) * kA_Stage, qt, c, (w >> 1) ? cls1 : cls0);
-      if (!more) break;
-      commit(smem + ((it + 1) & 1) * kA_Stage);
+    int s0 = 0;                                          // stage of chunk it
+    for (;;) {
+      const int s2 = s0 == 0 ? 2 : s0 - 1;               // stage of chunk it+2 (that of chunk it-1)
+      issue_stage(s2 * kA_Stage, qc, cc);
+      compute(smem + s0 * kA_Stage, qa, ca, (w >> 1) ? (has_kt1 ? tile_cls(qa, kt0 + 1) : 0) : tile_cls(qa, kt0));
+      if (qb_ >= a.nqt) break;
+      wait_older();
       __syncthreads();
-      qt = nqt_;
-      c = nc;
-      cls0 = ncls0;
-      cls1 = ncls1;
+      qa = qb_; ca = cb;
+      qb_ = qc; cb = cc;
+      advance(qc, cc);
+      s0 = s0 == 2 ? 0 : s0 + 1;
     }
+    wait_vmem<0>();
   }
 
   // accumulator row r <-> key 8*(r/4) + 4*hi + r%4 of the wave's 32, column <-> dim
@@ -478,32 +513,37 @@ __global__ void __launch_bounds__(kThreads) bwd_dq(AttnBwdArgs a) {
   // chunk c of this thread's i-th load: K nope rows 64 x 16 (i < 4), K rope rows 64 x 8 (2),
   // V rows 64 x 16 (4), K^T nope rows 128 x 8 (4), K^T rope rows 64 x 8 (2)
   u32x4_t pre[16];
-  auto prefetch = [&](int kt) {
+  // issued every step (past the last tile: an offset beyond every resource, zeros
+  // and no traffic), so the compiler's wait counts for the loads around it are exact
+  constexpr uint32_t kPastEnd = 0x80000000u;
+  auto prefetch = [&](int kt, bool live) {
     const uint32_t k0 = static_cast<uint32_t>(kt) * kTileN;
+    const uint32_t so_kn = live ? k0 * (kDn * 2) : kPastEnd, so_kr = live ? k0 * (kDr * 2) : kPastEnd;
+    const uint32_t so_v = live ? k0 * (kDv * 2) : kPastEnd, so_t = live ? k0 * 2 : kPastEnd;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ci = t + kThreads * i;
-      pre[i] = bload16(r_kn, (ci >> 4) * (kDn * 2) + (ci & 15) * 16, k0 * (kDn * 2));
+      pre[i] = bload16(r_kn, (ci >> 4) * (kDn * 2) + (ci & 15) * 16, so_kn);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int ci = t + kThreads * i;
-      pre[4 + i] = bload16(r_kr, (ci >> 3) * (kDr * 2) + (ci & 7) * 16, k0 * (kDr * 2));
+      pre[4 + i] = bload16(r_kr, (ci >> 3) * (kDr * 2) + (ci & 7) * 16, so_kr);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ci = t + kThreads * i;
-      pre[6 + i] = bload16(r_v, (ci >> 4) * (kDv * 2) + (ci & 15) * 16, k0 * (kDv * 2));
+      pre[6 + i] = bload16(r_v, (ci >> 4) * (kDv * 2) + (ci & 15) * 16, so_v);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ci = t + kThreads * i;
-      pre[10 + i] = bload16(r_knt, (ci >> 3) * (a.Lkp * 2) + (ci & 7) * 16, k0 * 2);
+      pre[10 + i] = bload16(r_knt, (ci >> 3) * (a.Lkp * 2) + (ci & 7) * 16, so_t);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int ci = t + kThreads * i;
-      pre[14 + i] = bload16(r_krt, (ci >> 3) * (a.Lkp * 2) + (ci & 7) * 16, k0 * 2);
+      pre[14 + i] = bload16(r_krt, (ci >> 3) * (a.Lkp * 2) + (ci & 7) * 16, so_t);
     }
   };
   auto commit = [&](char* st) {
@@ -535,9 +575,18 @@ __global__ void __launch_bounds__(kThreads) bwd_dq(AttnBwdArgs a) {
   };
 
   const float scale_log2 = a.scale * kLog2e;
-  auto compute = [&](const char* st, int kt, int cls) {
-    uint64_t word = 0;
-    if (cls == 2 && q_ok) word = a.bits[((static_cast<size_t>(row) * a.nkt + kt) * kTileM) + 32 * w + li];
+  // visibility word of this lane's query in a class-2 tile (zero elsewhere): loaded
+  // unconditionally through a resource, before the next tile's staging loads are
+  // issued, so the wait for it is a count that leaves those in flight
+  const __amdgpu_buffer_rsrc_t r_bits =
+      rsrc(a.bits, a.bits ? static_cast<size_t>(a.B) * a.nqt * a.nkt * kTileM * 8 : 0);
+  const uint32_t vo_bits = q_ok ? static_cast<uint32_t>(32 * w + li) * 8 : kPastEnd;
+  auto vis_word = [&](int kt, int cls) -> uint64_t {
+    const uint32_t so = cls == 2 ? static_cast<uint32_t>((static_cast<size_t>(row) * a.nkt + kt) * kTileM * 8) : kPastEnd;
+    const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(r_bits, vo_bits, so, 0);
+    return __builtin_bit_cast(uint64_t, v2);
+  };
+  auto compute = [&](const char* st, int kt, int cls, uint64_t word) {
     bf16x8_t bS[4];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -583,17 +632,15 @@ __global__ void __launch_bounds__(kThreads) bwd_dq(AttnBwdArgs a) {
 
   if (n > 0) {
     int e0 = entry(0);
-    prefetch(e0 & 0xFFFFFF);
+    prefetch(e0 & 0xFFFFFF, true);
     commit(smem);
     __syncthreads();
     for (int e = 0; e < n; ++e) {
       const bool more = e + 1 < n;
-      int e1 = 0;
-      if (more) {
-        e1 = entry(e + 1);
-        prefetch(e1 & 0xFFFFFF);
-      }
-      compute(smem + (e & 1) * kB_Stage, e0 & 0xFFFFFF, e0 >> 24);
+      const uint64_t word = vis_word(e0 & 0xFFFFFF, e0 >> 24);
+      const int e1 = more ? entry(e + 1) : 0;
+      prefetch(e1 & 0xFFFFFF, more);
+      compute(smem + (e & 1) * kB_Stage, e0 & 0xFFFFFF, e0 >> 24, word);
       if (!more) break;
       commit(smem + ((e + 1) & 1) * kB_Stage);
       __syncthreads();
