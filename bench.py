@@ -146,6 +146,20 @@ def measure(wl, steps: int, warmup: int, structured: bool = False) -> dict:
     att_min = min(mk[2].elapsed_time(mk[3]) for mk in marks)
     exp_ms = sum(mk[0].elapsed_time(mk[1]) for mk in marks) / steps if expand else None
 
+    # Cold caches: a 512 MB write (more than the 256 MB Infinity Cache and the L2s)
+    # before every call, outside the events; reported next to the warm figures.
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    n_cold = max(3, steps // 4)
+    cmarks = [[ev() for _ in range(4)] for _ in range(n_cold)]
+    for k in range(n_cold):
+        flush.zero_()
+        step(cmarks[k])
+    torch.cuda.synchronize()
+    first = 0 if expand else 1
+    cold_ms = sum(mk[first].elapsed_time(mk[3]) for mk in cmarks) / n_cold
+    cold_att = sum(mk[2].elapsed_time(mk[3]) for mk in cmarks) / n_cold
+    del flush
+
     # tile statistics from the occupancy map of this mask
     tm = mla.tile_map_view(ws, wl.B, wl.Lq, wl.Lk)
     cls = tm["classes"].cpu()
@@ -169,6 +183,9 @@ def measure(wl, steps: int, warmup: int, structured: bool = False) -> dict:
         "attn_kernel_ms": round(att, 4),
         "attn_kernel_ms_min": round(att_min, 4),
         "attn_kernel_tflops": round(vis_flops / (att * 1e-3) / 1e12, 2),
+        "cold_ms_per_step": round(cold_ms, 4),
+        "cold_attn_kernel_ms": round(cold_att, 4),
+        "cold_tflops": round(vis_flops / (cold_ms * 1e-3) / 1e12, 2),
         "occupancy_ms": round(occ, 4),
         "occupancy_mask_GBs": None if structured else round(mask_bytes / (occ * 1e-3) / 1e9, 1),
         "key_runs": key_runs,
