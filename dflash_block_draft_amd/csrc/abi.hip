@@ -383,6 +383,11 @@ dflash_status attn_impl(const void* q, const void* k_nope, const void* k_rope_sh
   if (dt == DFLASH_BF16 && (Lk + DFLASH_TILE_N - 1) / DFLASH_TILE_N > dflash::kMaxKeyTiles)
     return fail(DFLASH_ERR_UNSUPPORTED, "a bf16 call supports at most %d key tiles, got Lk = %lld",
                 dflash::kMaxKeyTiles, (long long)Lk);
+  // the bf16 kernel copies K / V tiles through buffer resources whose range and
+  // offsets are 32-bit: one (batch, head) slice of k_nope or v must fit in 2^31 bytes
+  if (dt == DFLASH_BF16 && Lk * (Dn * 2) > INT32_MAX)
+    return fail(DFLASH_ERR_UNSUPPORTED, "a bf16 call takes at most %lld keys (one (batch, head) k_nope / v slice "
+                "within 2^31 bytes), got Lk = %lld", (long long)(INT32_MAX / (Dn * 2)), (long long)Lk);
   const bool map_only = !additive_mask && (flags & DFLASH_ATTN_REUSE_TILE_MAP);   // the workspace's map alone
   if (map_only && dt == DFLASH_F32) return fail(DFLASH_ERR_INVALID_ARG, "the f32 path keeps no tile map to reuse");
   if (map_only && (flags & DFLASH_ATTN_NO_TILE_SKIP))

@@ -191,7 +191,9 @@ dflash_status dflash_mla_mask_occupancy(const void* additive_mask, dflash_dtype 
  *
  * Supported: Dn == 128, Dr == 64, Dv == 128;
  *   (dt, mask_dt) in {(F32, F32), (BF16, F32), (BF16, BF16)};
- *   a BF16 call takes at most 2^24 - 1 key tiles of 64 keys, else UNSUPPORTED.
+ *   a BF16 call takes at most 2^23 - 1 keys (one (b, h) slice of k_nope or v
+ *   within 2^31 bytes: the kernel addresses it through a 32-bit buffer range),
+ *   else UNSUPPORTED.
  * BF16: QK^T and PV run as bf16 MFMA with fp32 accumulation and an online
  *   softmax in fp32; the probabilities are rounded to bf16 for PV; out is
  *   rounded to nearest even.  F32: fp32 arithmetic throughout.

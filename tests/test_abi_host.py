@@ -105,10 +105,17 @@ def _attn(lib, **kw):
     (dict(q=1 << 44, kn=2 << 44, kr=3 << 44, v=4 << 44, out=5 << 44, mask=6 << 44, Lk=1 << 30,
           ws=7 << 44, wsb=1 << 40), 2),     # masked bf16 call with 2^24 key tiles
     (dict(q=1 << 44, kn=2 << 44, kr=3 << 44, v=4 << 44, out=5 << 44, Lk=1 << 30), 2),   # unmasked, same limit
+    (dict(q=1 << 44, kn=2 << 44, kr=3 << 44, v=4 << 44, out=5 << 44, Lk=1 << 23), 2),   # k_nope slice of 2^31 bytes
 ])
 def test_attn_validation(lib, kw, status):
     assert _attn(lib, **kw) == status
     assert lib.dflash_last_error() != b""
+
+
+def test_attn_largest_bf16_key_count_passes_validation(lib):
+    # 2^23 - 1 keys: the (batch, head) slice of k_nope is just under 2^31 bytes (CHECK_ONLY launches nothing)
+    kw = dict(q=1 << 44, kn=2 << 44, kr=3 << 44, v=4 << 44, out=5 << 44, Lk=(1 << 23) - 1, flags=0x4)
+    assert _attn(lib, **kw) == 0
 
 
 def test_expand_validation(lib):
