@@ -312,22 +312,33 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
     return l0 + l1;
   };
   // Vector phase: softmax of the raw scores in s (tile entry e) -> pk, m_run, l_run, o.
-  // Fast path (zero-mask tile, no ragged end): probabilities with the current
-  // stabiliser.  Exact path (binary or general mask, ragged end, no stabiliser
-  // yet, or a probability that may exceed 2^8): masked natural-unit scores, tile
-  // max, rescale of O and l when the stabiliser rises, probabilities.
+  // Fast path (zero or binary tile, no ragged end): probabilities with the
+  // current stabiliser, hidden keys set to -inf first.  Exact path (general mask,
+  // ragged end, no stabiliser yet, or a probability that may exceed 2^8): masked
+  // natural-unit scores, tile max, rescale of O and l when the stabiliser rises,
+  // probabilities.
   auto softmax = [&](int e) __attribute__((always_inline)) {
     const int cls = e >> 24;
     const int k0 = (e & 0xFFFFFF) * kTileN;
     const bool ragged = k0 + kTileN > a.Lk;
     float lsum = 0.f;
     bool exact = true;
-    if (cls == 1 && !ragged) {
+    // (a lane with no stabiliser yet takes the exact path: skip the fast attempt)
+    if ((cls == 1 || cls == 2) && !ragged && !__any(m_run == -INFINITY)) {
+      // hidden keys of a binary tile become -inf, whose probability is exactly 0
       float x[16];
+      if (cls == 2) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = s[r];
+        for (int r = 0; r < 16; ++r) {
+          const int h1 = __builtin_amdgcn_sbfe(static_cast<int>(hid), 8 * (r >> 2) + (r & 3), 1);   // -1: hidden
+          x[r] = __int_as_float((h1 & static_cast<int>(kNegInfBits)) | (~h1 & __float_as_int(s[r])));
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = s[r];
+      }
       lsum = probs(x, scale_log2, -(m_run == -INFINITY ? 0.f : m_run) * kLog2e);
-      exact = __any(!(lsum <= kSumLimit) || (m_run == -INFINITY));   // NaN sums too
+      exact = __any(!(lsum <= kSumLimit));   // NaN sums too
     }
     if (__builtin_expect(exact, 0)) {
       // accumulator r <-> key k0 + kh*32 + 8*(r>>2) + 4*hi + (r&3)
