@@ -198,6 +198,27 @@ def test_fully_masked_rows_and_huge_negatives(dev):
     _check(out, ref, "bf16", "dead rows / finfo.min rows")
 
 
+def test_huge_negative_tile_then_binary_tiles(dev):
+    """A first key tile of huge finite negatives (a general tile: the stabiliser
+    becomes about -3.4e38), then binary 0 / -inf tiles.  There the fast path's
+    exponent offset overflows, and the tile must be redone on the exact path; rows
+    whose binary tiles hide every key keep the softmax over the huge negatives,
+    which in fp32 and fp64 alike is the plain mean of their values."""
+    B, H, Lq, Lk = 1, 2, 128, 384
+    q, kn, kr, v = W.random_attention_inputs(19, B, H, Lq, Lk, dtype="bf16")
+    rng = np.random.default_rng(19)
+    m = np.where(rng.random((B, 1, Lq, Lk)) < 0.5, 0.0, -np.inf).astype(np.float32)
+    m[..., :64] = float(torch.finfo(torch.bfloat16).min)   # representable in both mask dtypes
+    m[0, 0, 10:20, 64:] = -np.inf
+    for mdt in (torch.float32, torch.bfloat16):
+        mask = torch.from_numpy(m).to(mdt)
+        qd, knd, krd, vd, md = _to(dev, q, kn, kr, v, mask)
+        out = mla.mla_attn(qd, knd, krd, vd, md)
+        torch.cuda.synchronize()
+        ref = oracle.mla_attention(q, kn, kr, v, mask, 192 ** -0.5)
+        _check(out, ref, "bf16", f"huge-negative tile then binary tiles, {mdt}")
+
+
 def test_single_visible_key_returns_its_value(dev):
     B, H, Lq, Lk = 2, 3, 64, 130
     q, kn, kr, v = W.random_attention_inputs(17, B, H, Lq, Lk, dtype="bf16")
