@@ -219,6 +219,38 @@ def test_huge_negative_tile_then_binary_tiles(dev):
         _check(out, ref, "bf16", f"huge-negative tile then binary tiles, {mdt}")
 
 
+def test_largest_key_count(dev):
+    """The largest bf16 key count, 2^23 - 1: one (batch, head) slice of k_nope / v
+    is just under 2^31 bytes, the limit of the kernel's 32-bit buffer ranges, and
+    the last (ragged, binary) key tile sits at byte offsets just below it.  One DFlash
+    block of 16 queries whose anchor is 1000 sees 1001 context keys and its own 16
+    noise keys at the very end.  K / V are drawn on the device (seeded); the oracle
+    gets the visible keys only -- exact, since every other key has weight 0."""
+    Lk, bs, anchor = (1 << 23) - 1, 16, 1000
+    ctx = Lk - bs
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(23)
+    say(f"largest key count: Lk={Lk}")
+    q = torch.randn((1, 1, bs, 192), generator=gen, device=dev).to(torch.bfloat16)
+    kn = torch.randn((1, 1, Lk, 128), generator=gen, device=dev).to(torch.bfloat16)
+    kr = torch.randn((1, Lk, 64), generator=gen, device=dev).to(torch.bfloat16)
+    v = torch.randn((1, 1, Lk, 128), generator=gen, device=dev).to(torch.bfloat16)
+    mask = torch.full((1, 1, bs, Lk), float("-inf"), dtype=torch.bfloat16, device=dev)
+    mask[..., :anchor + 1] = 0
+    mask[..., ctx:] = 0
+    out = mla.mla_attn(q, kn, kr, v, mask)
+    anchors = torch.tensor([[anchor]], dtype=torch.int32, device=dev)
+    out_blocks = mla.mla_attn_blocks(q, kn, kr, v, anchors, bs, ctx)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_blocks)
+    cols = torch.cat([torch.arange(anchor + 1), torch.arange(ctx, Lk)]).to(dev)
+    ref = oracle.mla_attention(q.cpu(), kn[:, :, cols].cpu(), kr[:, cols].cpu(), v[:, :, cols].cpu(),
+                               mask[..., cols].cpu(), 192 ** -0.5)
+    _check(out, ref, "bf16", "largest key count")
+    del q, kn, kr, v, mask, out, out_blocks
+    torch.cuda.empty_cache()
+
+
 def test_single_visible_key_returns_its_value(dev):
     B, H, Lq, Lk = 2, 3, 64, 130
     q, kn, kr, v = W.random_attention_inputs(17, B, H, Lq, Lk, dtype="bf16")
