@@ -170,3 +170,40 @@ def test_backward_config4_properties(dev):
     sv = dv.double().sum(dim=2)
     want = dout.double().sum(dim=2)
     assert ((sv - want).abs() <= 2e-2 * dout.double().abs().sum(dim=2) + 1e-3).all()
+
+
+def test_backward_largest_key_count(dev):
+    """The largest key count the backward takes, 5592383 (the padded k^T copy of
+    one (batch, head) just under 2^31 bytes), one block of 16 queries whose
+    anchor is 1000: 1001 context keys and the last 16 keys are visible, the last
+    key tile is ragged.  Keys nobody sees get exactly zero gradients; the visible
+    keys' gradients and dq match the oracle run on the visible keys alone (the
+    other keys' probabilities are exactly 0)."""
+    Lk, bs, anchor = 5592383, 16, 1000
+    ctx = Lk - bs
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(61)
+    say(f"backward, largest key count: Lk={Lk}")
+    q = torch.randn((1, 1, bs, 192), generator=gen, device=dev).to(torch.bfloat16)
+    kn = torch.randn((1, 1, Lk, 128), generator=gen, device=dev).to(torch.bfloat16)
+    kr = torch.randn((1, Lk, 64), generator=gen, device=dev).to(torch.bfloat16)
+    v = torch.randn((1, 1, Lk, 128), generator=gen, device=dev).to(torch.bfloat16)
+    dout = torch.randn((1, 1, bs, 128), generator=gen, device=dev).to(torch.bfloat16)
+    mask = torch.full((1, 1, bs, Lk), float("-inf"), dtype=torch.bfloat16, device=dev)
+    mask[..., :anchor + 1] = 0
+    mask[..., ctx:] = 0
+    scale = 192 ** -0.5
+    out, lse = _forward_lse(dev, q, kn, kr, v, mask, scale)
+    dq, dkn, dkr, dv = mla.mla_attn_bwd(q, kn, kr, v, mask, out, dout, lse, scale)
+    torch.cuda.synchronize()
+    hidden = slice(anchor + 1, ctx)
+    for t, nm in ((dkn[:, :, hidden], "dk_nope"), (dkr[:, hidden], "dk_rope"), (dv[:, :, hidden], "dv")):
+        assert torch.count_nonzero(t).item() == 0, nm
+    cols = torch.cat([torch.arange(anchor + 1), torch.arange(ctx, Lk)]).to(dev)
+    ref = oracle.mla_attention_backward(q.cpu(), kn[:, :, cols].cpu(), kr[:, cols].cpu(), v[:, :, cols].cpu(),
+                                        mask[..., cols].cpu(), dout.cpu(), scale)
+    got = (dq, dkn[:, :, cols], dkr[:, cols], dv[:, :, cols])
+    for nm, g, r in zip(("dq", "dk_nope", "dk_rope", "dv"), got, ref):
+        _grad_check(nm, g, r)
+    del q, kn, kr, v, dout, mask, out, lse, dq, dkn, dkr, dv, got
+    torch.cuda.empty_cache()
