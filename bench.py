@@ -460,7 +460,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the draft attention "
-              "shards over heads/batch rows with no exchange, but no multi-GPU run is part of this build.",
+              "shards over heads/batch rows with no exchange, but only the one-GPU path is implemented.",
               file=sys.stderr, flush=True)
         sys.exit(2)
     import torch

@@ -43,7 +43,7 @@ extern "C" {
 typedef enum dflash_status {
   DFLASH_OK = 0,
   DFLASH_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, non-positive size, bad scale, aliasing, bad flags */
-  DFLASH_ERR_UNSUPPORTED = 2,  /* head dims or dtype combination this build does not implement */
+  DFLASH_ERR_UNSUPPORTED = 2,  /* head dims or dtype combination the library does not implement */
   DFLASH_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
   DFLASH_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
 } dflash_status;

@@ -94,7 +94,7 @@ def _attn(lib, **kw):
     (dict(scale=float("inf")), 1),
     (dict(dt=7), 1),
     (dict(flags=0x80), 1),
-    (dict(Dn=64), 2),                       # head dims this build does not implement
+    (dict(Dn=64), 2),                       # head dims the library does not implement
     (dict(Dr=32), 2),
     (dict(Dv=64), 2),
     (dict(dt=0, mdt=1, mask=FAKE * 8), 2),  # f32 attention with a bf16 mask
