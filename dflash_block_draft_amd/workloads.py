@@ -156,7 +156,7 @@ def _make(name, seed, B, H, ctx, A, bs, dtype, mask_dtype, pad=0, std=1.0,
 
 
 def config(idx: int, block_size: Optional[int] = None) -> Workload:
-    """Workload `idx` (0..4) with seed = idx.  Config 3 takes block_size 8 or 32."""
+    """Workload `idx` (0..4) with seed = idx; the block-size sweep (3) takes block_size 8 or 32."""
     if idx == 0:
         return _make("tiny_f32_ctx64_h4", 0, B=1, H=4, ctx=64, A=2, bs=16,
                      dtype="f32", mask_dtype="f32")
