@@ -1,4 +1,5 @@
-// Fused non-causal draft MLA attention forward, bf16 MFMA on gfx950.
+// Fused non-causal draft MLA attention forward, bf16 MFMA on gfx950: one wave
+// per SIMD holding 64 queries.
 //
 // What it computes (NeMo AutoModel DFlash page, KimiK3DFlashAttention.forward;
 // DSpark page, KimiK3DSparkAttention): for every (batch, head, noise query)
@@ -6,64 +7,81 @@
 //   out = softmax_j(s) @ v[h]
 // over the keys [context | noise block], with no materialised score matrix.
 //
-// Decomposition (one workgroup = one (batch, head, 128-query tile)):
-//  * 8 waves, two per SIMD: wave w owns queries 32*(w&3) .. +31 of the tile
-//    and keys 32*(w>>2) .. +31 of every 64-key tile; the two key-half waves of
-//    a query group keep separate (m, l, O) and merge them once at the end.
-//  * Ping-pong: each wave alternates a matrix phase (score MFMAs of the next
-//    tile + PV MFMAs of the current one) and a vector phase (softmax of the
-//    next tile), with a workgroup barrier after every phase.  The key-half-1
-//    waves run one phase behind the key-half-0 waves, so on every SIMD (waves
-//    w and w+4) one wave feeds the matrix core while the other does its
-//    exponentials.
-//  * Scores are computed transposed, S^T = K Q^T with v_mfma_f32_32x32x16_bf16:
-//    a lane holds one query and 16 of its keys, so row sums are in-lane, and
-//    the packed bf16 P^T values are directly the B operand of O^T = V^T P^T
-//    (the key order of the contraction is free, so keys are relabelled to
-//    match the accumulator layout).  V^T operands come from the V tile with
-//    the gfx950 transposing LDS read (ds_read_b64_tr_b16).
+// Decomposition (one workgroup = one (batch, head, 128-query tile), two waves,
+// two workgroups per CU so every SIMD holds exactly one wave):
+//  * Wave w owns queries 64w .. 64w+63 of the tile as two streams of 32
+//    (stream i: queries 64w + 32i + lane%32).  Each V operand read from LDS
+//    feeds one PV MFMA of each stream.
+//  * The key loop walks the tile list in steps of 32 keys (half a 64-key tile),
+//    each in two phases of 20 MFMAs with one workgroup barrier per step:
+//      phase A: score MFMAs of stream 0 for the next step, PV of stream 0
+//               || softmax of stream 1 for the current step
+//      phase B: score MFMAs of stream 1 for the next step, PV of stream 1
+//               || softmax of stream 0 for the next step
+//    The matrix and vector work of a phase belong to different streams, so the
+//    wave keeps the matrix core busy while its VALU does exponentials (the
+//    ping-pong of FlashAttention-3's warp-group scheduling, inside one wave).
+//    Each phase is hand-scheduled into 20 slots (one MFMA, its operand reads
+//    and one unit of softmax work per slot, with scheduling barriers between
+//    slots).
+//  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
+//    a lane holds one query and 16 of its 32 keys, so row sums are in-lane (one
+//    permlane32 swap joins the halves), and the packed bf16 P^T is directly the
+//    B operand of O^T = V^T P^T (keys are relabelled to the accumulator order).
+//    V^T operands come from the V tile with the transposing LDS read.
+//  * Keys hidden by a binary (0 / -inf) tile are removed by the first score
+//    MFMA itself: its C operand is a bias block of 0 / -inf built from the
+//    tile's per-query visibility words.  Tiles with other mask values, ragged
+//    key tails and the first visible step take an exact path that reads them.
 //  * K = [k_nope | head-shared k_rope], V and the visibility words go global ->
-//    LDS with buffer_load ... lds (no VGPR staging; out-of-range reads give
-//    zeros) into three-slot rings; every copy has two phases of slack before
-//    the barrier that publishes it.  The key loop is unrolled by the ring
-//    length so every LDS address and copy destination is a constant.  LDS
-//    tiles are 16-row x 64 B blocks with XOR-swizzled K chunks: conflict-free
-//    operand reads, 64-byte coalesced loads.
-//  * Q (32 x 192 bf16 per wave) stays in registers for the whole key loop; the
-//    K operands of the next score tile are read into registers at the end of
-//    the vector phase, so the matrix phase starts on data already there.
-//  * Binary-mask tiles (only 0 / -inf) initialise the score accumulator to
-//    0 / -inf from a 64-bit visibility word per query, so the MFMA applies the
-//    mask; general masks add their values to the scaled scores.
-//  * Online softmax in fp32 with the hardware exp2 and a stabiliser m that is
-//    only raised when needed: the probabilities of a tile are first formed
-//    with the current m; if some lane's tile sum exceeds 2^8 (or m is still
-//    -inf) the wave takes the exact path (tile max, rescale of O and l by
-//    exp(m_old - m_new), recompute).  Any stabiliser gives the same result in
-//    exact arithmetic because it scales O and l alike.
+//    LDS with buffer_load ... lds (no VGPR staging; out-of-range rows read
+//    zeros, so ragged and phantom steps need no branches) into rings of 4 (K),
+//    3 (V) and 3 (words) slots; the copies of a step are spread over the MFMA
+//    slots of its two phases.  LDS tiles are 16-row x 64 B blocks with
+//    XOR-swizzled K chunks: conflict-free 16-byte operand reads.
+//  * Q (2 x 32 x 192 bf16) stays in registers for the whole loop; K operands
+//    are read two MFMAs ahead of their use.
+//  * Online softmax in fp32 with the hardware exp2 and a stabiliser m fixed at
+//    the first visible step of each row: later steps form exp(s - m) without
+//    rescaling O.  Any stabiliser gives the same result in exact arithmetic
+//    because it scales O and l alike; it only has to keep every exp(s - m)
+//    within fp32 range and the bf16 P operand accurate, so a step whose scores
+//    exceed m by more than 20 ln 2 (p > 2^20) marks the workgroup, and a
+//    marked workgroup runs again in two passes: the exact row maxima first,
+//    then the accumulation with those maxima as stabilisers.
 #include "common.h"
 #include "dma.h"
 #include "launch.h"
 
 #include <type_traits>
+#include <utility>
 
 namespace dflash {
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 2;
 constexpr int kThreads = kWaves * 64;
-constexpr int kKBytes = kTileN * kDqk * 2;          // 24 KiB: 4 row blocks x 6 chunk quads x 1 KiB
-constexpr int kVBytes = kTileN * kDv * 2;           // 16 KiB: 4 row blocks x 4 chunk quads x 1 KiB
-constexpr int kBitsBytes = kTileM * 8;              // 1 KiB: one visibility word per query
-constexpr int kKRingN = 4;                           // K and visibility-word rings: copies lead by 2.5 tiles
-constexpr int kVRingN = 3;                           // V ring: copies lead by 2 tiles
+constexpr int kKSlot = 32 * kDqk * 2;               // 12 KiB: 2 row blocks x 6 chunk quads x 1 KiB
+constexpr int kVSlot = 32 * kDv * 2;                // 8 KiB: 2 row blocks x 4 chunk quads x 1 KiB
+constexpr int kBitsSlot = kTileM * 8;               // 1 KiB: one visibility word per query of a 64-key tile
+constexpr int kNK = 4;                              // K ring slots (32-key steps)
+constexpr int kNV = 3;                              // V ring slots (32-key steps)
+constexpr int kNB = 3;                              // visibility-word ring slots (64-key tiles)
 constexpr int kKRing = 0;
-constexpr int kVRing = kKRing + kKRingN * kKBytes;
-constexpr int kBitsRing = kVRing + kVRingN * kVBytes;
-constexpr int kRingBytes = kBitsRing + kKRingN * kBitsBytes;
-static_assert(kRingBytes <= 160 * 1024, "LDS budget");
-constexpr int kPrefetchK = 8;                        // K operand chunks read before the matrix phase
-constexpr float kSumLimit = 256.0f;                  // fast path keeps every probability <= 2^8
+constexpr int kVRing = kKRing + kNK * kKSlot;
+constexpr int kBitsRing = kVRing + kNV * kVSlot;
+constexpr int kLdsBytes = kBitsRing + kNB * kBitsSlot;
+constexpr int kPK = 2;                               // K chunks of a phase read before its first MFMA
+// MFMA order of a phase: score chunks c (0-11, one dependent chain) and PV
+// operations 100 + v (v = 4*st + j: four independent accumulators), placed so
+// that only three score MFMAs directly follow their predecessor in the chain and
+// the chain ends in the last slot
+constexpr int kSlotOp[20] = {0, 100, 1, 101, 2, 102, 3, 103, 4, 104, 5, 105, 6, 106, 7, 8, 107, 9, 10, 11};
+static_assert(kLdsBytes <= 80 * 1024, "two workgroups per CU");
+constexpr float kSumLimit = 1048576.0f;              // fast path keeps every probability <= 2^20
+constexpr float kHeadroom = 13.8629436f;             // 20 ln 2: scores may exceed the stabiliser by this much
+constexpr int kPassNormal = 0;                       // accumulate O and l
+constexpr int kPassMax = 1;                          // row maxima only (second pass of a rare item)
 constexpr uint32_t kNegInfBits = 0xFF800000u;
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -72,6 +90,9 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 typedef __attribute__((address_space(3))) uint64_t lds_u64_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
+
+template <int N>
+using IC = std::integral_constant<int, N>;
 
 // max / sum of x over lanes l and l ^ 32
 __device__ __forceinline__ float halves_max(float x) {
@@ -89,22 +110,18 @@ __device__ __forceinline__ s16x4_t ds_read_tr(const lds_char_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
 }
 
-// LDS tile layout (K and V): row block rb (16 rows) x chunk quad cq (4 x 16 B
-// chunks) -> 1 KiB block (rb * nq + cq); inside it row r%16 takes 64 B and the
-// 16-byte chunk c%4 of that row sits at slot (c%4) ^ swz(r), swz(r) = (r>>2)&3
-// for K and 0 for V.  Wave w copies, of each tile, row block w/2 of K: the
-// k_nope quads 2(w%2), 2(w%2)+1 (adjacent blocks) and the k_rope quad 4 + w%2,
-// and V blocks 2w, 2w+1; lane l of a block covers row rb*16 + l/4, slot l%4.
-struct TileCopy {
-  u32x4_t kn, kr, v, bits;     // descriptors: this (b, h)'s k_nope, the shared k_rope, v, visibility words
-  uint32_t voff[4];            // per-lane byte offset inside the source rows (tile start excluded)
-  uint32_t kn_lds, kr_lds, v_lds;   // LDS address of this wave's k_nope pair / k_rope / V pair in slot 0
-};
-
-__device__ __forceinline__ u32x4_t uniform4(u32x4_t d) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) d[i] = __builtin_amdgcn_readfirstlane(d[i]);
-  return d;
+// 16 bytes per lane from a buffer straight into LDS at lds_base + 16*lane, from
+// byte voff + SOFF of the buffer.  SOFF selects a 64-byte chunk quad inside a
+// row and goes in the scalar offset (the instruction's immediate offset would
+// move the LDS destination too); the row offset is in voff, so a row is in or
+// out of the buffer's range as a whole and out-of-range rows read zeros.
+// Inline asm for the same reason as dma16: the compiler must not make unrelated
+// LDS reads wait for this write; completion is awaited with wait_vmem before
+// the barrier that publishes the slot.
+template <int SOFF>
+__device__ __forceinline__ void dma16i(u32x4_t rsrc, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base)), "s"(SOFF));
 }
 
 template <bool MASK_BF16>
@@ -113,20 +130,50 @@ __device__ __forceinline__ float load_mask(const void* mask, size_t idx) {
   return static_cast<const float*>(mask)[idx];
 }
 
-template <int N>
-using IC = std::integral_constant<int, N>;
+// f(IC<0>{}), ..., f(IC<N-1>{}) in order
+template <int... Is, class F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, Is...>, F&& f) {
+  (f(IC<Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(std::make_integer_sequence<int, N>{}, f);
+}
+
+// One chunk of S^T = K Q^T with the accumulator in vector registers, where the
+// softmax reads it with plain VALU instructions (the accumulators of O stay in
+// accumulator registers, written by the compiler's own MFMAs).  QA: the B
+// operand sits in an accumulator register.  The first chunk adds the bias block
+// that hides the masked keys of a binary tile (0 elsewhere).  Written as asm,
+// the compiler does not know the result arrives one MFMA latency later: every
+// reader of acc is placed at least two MFMA issues later, or behind
+// s_nop_after_mfma.
+template <bool FIRST, bool QA>
+__device__ __forceinline__ void mfma_s(f32x16_t& acc, bf16x8_t k, bf16x8_t q, const f32x16_t& bias) {
+  const u32x4_t kk = __builtin_bit_cast(u32x4_t, k);
+  const u32x4_t qq = __builtin_bit_cast(u32x4_t, q);
+  if (FIRST) {   // the chain starts from the hidden-key bias (0 or -inf per key)
+    if (QA) asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(acc) : "v"(kk), "a"(qq), "v"(bias));
+    else asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(acc) : "v"(kk), "v"(qq), "v"(bias));
+  } else {
+    if (QA) asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(kk), "a"(qq));
+    else asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(kk), "v"(qq));
+  }
+}
+// the MFMA result in acc is readable by the VALU after this (16 wait states)
+__device__ __forceinline__ void s_nop_after_mfma(f32x16_t& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(acc));
+}
 
 template <bool MASK_BF16>
-__global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
-  __shared__ __attribute__((aligned(1024))) char smem[kRingBytes];
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+attn_fwd_bf16(AttnBf16Args a) {
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   lds_char_t* const lds = (lds_char_t*)smem;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
 
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: keeps descriptors scalar
-  const int qg = wave & 3;      // query group: 32 queries
-  const int kh = wave >> 2;     // key half of each 64-key tile; also the ping-pong group
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 31;
   const int hi = lane >> 5;
 
@@ -142,15 +189,21 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
   const int n_all = a.counts ? a.counts[bq] : a.nkt;
   const int t_begin = static_cast<int>(static_cast<int64_t>(n_all) * sp / a.nsplit);
   const int ntiles = static_cast<int>(static_cast<int64_t>(n_all) * (sp + 1) / a.nsplit) - t_begin;
+  const int nsteps = 2 * ntiles;
 
   const size_t bh = static_cast<size_t>(b) * a.H + h;
-  const int q_local = qg * 32 + li;               // this lane's query within the tile
-  const int q_row = qt * kTileM + q_local;
-  const bool q_ok = q_row < a.Lq;
   const size_t tile_row0 = static_cast<size_t>(bq) * a.nkt;
+  int q_local[2], q_row[2];
+  bool q_ok[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    q_local[i] = 64 * wave + 32 * i + li;
+    q_row[i] = qt * kTileM + q_local[i];
+    q_ok[i] = q_row[i] < a.Lq;
+  }
 
-  // ---- tile list of this q-tile (entry: k-tile | class << 24), read with scalar
-  // loads; past the end an entry is 0 (no tile); without a mask every k-tile is class 1
+  // ---- tile list (entry: k-tile | class << 24), scalar loads; past the end an
+  // entry is 0 (no tile); without a mask every k-tile is class 1
   typedef __attribute__((address_space(4))) const int32_t const_i32;
   const int32_t* list = a.counts ? a.lists + tile_row0 + t_begin : nullptr;
   const const_i32* clist = (const const_i32*)(uintptr_t)(list);
@@ -160,144 +213,163 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
     return clist[i];
   };
 
-  // ---- global -> LDS copy plan of this wave
-  TileCopy tc;
-  tc.kn = buffer_desc(a.kn + bh * a.Lk * kDn, a.Lk * kDn * 2);
-  tc.kr = buffer_desc(a.kr + static_cast<size_t>(b) * a.Lk * kDr, a.Lk * kDr * 2);
-  tc.v = buffer_desc(a.v + bh * a.Lk * kDv, a.Lk * kDv * 2);
-  tc.bits = buffer_desc(a.bits ? a.bits + tile_row0 * kTileM : nullptr, a.bits ? a.nkt * kBitsBytes : 0);
-  {
-    const int r16 = lane >> 2, s4 = lane & 3;
-    const int krb = wave >> 1;                                   // K row block of this wave
-    const int krow = krb * 16 + r16;
-    const int kslot = s4 ^ ((r16 >> 2) & 3);                     // swizzled 16-byte chunk in the quad
-#pragma unroll
-    for (int i = 0; i < 2; ++i)                                  // k_nope quads 2(w%2) + i: dims 64(w%2) + 32i ..
-      tc.voff[i] = krow * (kDn * 2) + ((2 * (wave & 1) + i) * 4 + kslot) * 16;
-    tc.voff[2] = krow * (kDr * 2) + ((wave & 1) * 4 + kslot) * 16;   // k_rope quad 4 + w%2
-    tc.kn_lds = lds0 + kKRing + (krb * 6 + 2 * (wave & 1)) * 1024;
-    tc.kr_lds = lds0 + kKRing + (krb * 6 + 4 + (wave & 1)) * 1024;
-    // V blocks 2w, 2w+1 of 16 (4 row blocks x 4 quads): row block w/2, quads 2(w%2) + i
-    const int vrow0 = (wave >> 1) * 16 + r16;
-    tc.voff[3] = vrow0 * (kDv * 2) + (2 * (wave & 1) * 4 + s4) * 16;   // second block is +64 B in the row
-    tc.v_lds = lds0 + kVRing + 2 * wave * 1024;
-  }
-  // Tiles past the end use k0 = Lk: every lane's read is out of range (zeros, no
-  // traffic), so every wave always issues the same number of copies and the
-  // wait counts are constants.
-  auto k0_of = [&](int e) __attribute__((always_inline)) -> int { return (e >> 24) ? (e & 0xFFFFFF) * kTileN : a.Lk; };
-  auto bits_kt = [&](int e) __attribute__((always_inline)) -> int { return (e >> 24) == 2 ? (e & 0xFFFFFF) : a.nkt; };
-  auto issue_k = [&](uint32_t slot_off, int k0) __attribute__((always_inline)) {
-    dma16<0>(tc.kn, tc.kn_lds + slot_off, tc.voff[0], k0 * (kDn * 2));
-    dma16<1024>(tc.kn, tc.kn_lds + slot_off, tc.voff[1], k0 * (kDn * 2));
-    dma16<0>(tc.kr, tc.kr_lds + slot_off, tc.voff[2], k0 * (kDr * 2));
+  // ---- global -> LDS copy plan: wave w copies row block w (keys 16w .. 16w+15
+  // of the step) of K (k_nope quads 0-3, k_rope quads 4-5) and of V (quads 0-3);
+  // lane l covers row 16w + l/4, LDS slot l%4 of each quad, K chunks swizzled
+  const u32x4_t d_kn = buffer_desc(a.kn + bh * a.Lk * kDn, a.Lk * kDn * 2);
+  const u32x4_t d_kr = buffer_desc(a.kr + static_cast<size_t>(b) * a.Lk * kDr, a.Lk * kDr * 2);
+  const u32x4_t d_v = buffer_desc(a.v + bh * a.Lk * kDv, a.Lk * kDv * 2);
+  const u32x4_t d_bits = buffer_desc(a.bits ? a.bits + tile_row0 * kTileM : nullptr, a.bits ? a.nkt * kBitsSlot : 0);
+  const int r16 = lane >> 2, s4 = lane & 3;
+  const int crow = wave * 16 + r16;                       // key row of the step this lane copies
+  const int kslot = s4 ^ ((r16 >> 2) & 3);
+  const uint32_t vo_kn = crow * (kDn * 2) + kslot * 16;
+  const uint32_t vo_kr = crow * (kDr * 2) + kslot * 16;
+  const uint32_t vo_v = crow * (kDv * 2) + s4 * 16;
+  const uint32_t lds_k = lds0 + kKRing + wave * 6 * 1024;
+  const uint32_t lds_v = lds0 + kVRing + wave * 4 * 1024;
+  // first key of the step at (entry, half); a phantom step past the end reads at Lk: all out of range
+  auto key0_of = [&](int e, int half) __attribute__((always_inline)) -> int {
+    return (e >> 24) ? (e & 0xFFFFFF) * kTileN + 32 * half : a.Lk;
   };
-  auto issue_v = [&](uint32_t slot_off, int k0) __attribute__((always_inline)) {
-    dma16<0>(tc.v, tc.v_lds + slot_off, tc.voff[3], k0 * (kDv * 2));
-    dma16<1024>(tc.v, tc.v_lds + slot_off, tc.voff[3] + 64, k0 * (kDv * 2));
+  auto issue_k = [&](int slot, int key0) __attribute__((always_inline)) {
+    const uint32_t lk = lds_k + slot * kKSlot;
+    const uint32_t on = vo_kn + static_cast<uint32_t>(key0) * (kDn * 2);
+    const uint32_t orp = vo_kr + static_cast<uint32_t>(key0) * (kDr * 2);
+    dma16i<0>(d_kn, lk, on);
+    dma16i<64>(d_kn, lk + 1024, on);
+    dma16i<128>(d_kn, lk + 2048, on);
+    dma16i<192>(d_kn, lk + 3072, on);
+    dma16i<0>(d_kr, lk + 4096, orp);
+    dma16i<64>(d_kr, lk + 5120, orp);
   };
-  // visibility words of a class-2 tile (1 KiB, copied by wave 0); kt = nkt reads zeros
-  auto issue_bits = [&](uint32_t slot_off, int kt) __attribute__((always_inline)) {
-    if (wave == 0) dma16<kBitsRing>(tc.bits, lds0 + slot_off, lane * 16, kt * kBitsBytes);
+  auto issue_v = [&](int slot, int key0) __attribute__((always_inline)) {
+    const uint32_t lv = lds_v + slot * kVSlot;
+    const uint32_t ov = vo_v + static_cast<uint32_t>(key0) * (kDv * 2);
+    dma16i<0>(d_v, lv, ov);
+    dma16i<64>(d_v, lv + 1024, ov);
+    dma16i<128>(d_v, lv + 2048, ov);
+    dma16i<192>(d_v, lv + 3072, ov);
+  };
+  // piece P of issue_k / issue_v (k_nope quads 0-3, k_rope quads 4-5; V quads 0-3),
+  // for spreading a step's copies over its MFMA slots
+  auto issue_k_piece = [&](auto P, int slot, int key0) __attribute__((always_inline)) {
+    constexpr int pc = decltype(P)::value;
+    const uint32_t lk = lds_k + slot * kKSlot + pc * 1024;
+    if constexpr (pc < 4) dma16i<pc * 64>(d_kn, lk, vo_kn + static_cast<uint32_t>(key0) * (kDn * 2));
+    else dma16i<(pc - 4) * 64>(d_kr, lk, vo_kr + static_cast<uint32_t>(key0) * (kDr * 2));
+  };
+  auto issue_v_piece = [&](auto P, int slot, int key0) __attribute__((always_inline)) {
+    constexpr int pc = decltype(P)::value;
+    dma16i<pc * 64>(d_v, lds_v + slot * kVSlot + pc * 1024, vo_v + static_cast<uint32_t>(key0) * (kDv * 2));
+  };
+  // visibility words of a class-2 tile (1 KiB, copied by wave 0); other tiles read zeros
+  auto issue_bits = [&](int slot, int e) __attribute__((always_inline)) {
+    const int kt = (e >> 24) == 2 ? (e & 0xFFFFFF) : a.nkt;
+    if (wave == 0) dma16i<0>(d_bits, lds0 + kBitsRing + slot * kBitsSlot, lane * 16 + static_cast<uint32_t>(kt) * kBitsSlot);
   };
 
-  // ---- per-lane LDS read offsets (bytes inside a slot)
-  // K operand of chunk c (dims 16c .. 16c+15): 16-byte chunk 2c+hi of row kh*32+li
-  // -> block (rb*6 + c/2), slot (2*(c&1) + hi) ^ swz(row).
-  const int krow = kh * 32 + li;
+  // ---- per-lane LDS read offsets inside a slot
+  // K operand of chunk c (dims 16c .. 16c+15): 16-byte chunk 2c+hi of key row li
+  // -> block (li/16)*6 + c/2, slot (2(c&1) + hi) ^ swz(row)
   const int kq = (li >> 2) & 3;
-  const int k_even = ((krow >> 4) * 6) * 1024 + (krow & 15) * 64 + (hi ^ kq) * 16;
-  const int k_odd = ((krow >> 4) * 6) * 1024 + (krow & 15) * 64 + ((2 + hi) ^ kq) * 16;
+  const int k_even = ((li >> 4) * 6) * 1024 + (li & 15) * 64 + (hi ^ kq) * 16;
+  const int k_odd = ((li >> 4) * 6) * 1024 + (li & 15) * 64 + ((2 + hi) ^ kq) * 16;
   // V^T operand (transposing read): lane i of 16-lane group G addresses row
-  // kh*32 + 16*step + 4*hi + i/4 (+8), dims 32*j + 16*(G&1) + 4*(i&3).
+  // 16*st + 4*hi + i/4 (+8), dims 32*j + 16*(G&1) + 4*(i&3)
   const int g16 = lane >> 4, i16 = lane & 15;
-  const int vrow = kh * 32 + 4 * hi + (i16 >> 2);
-  const int v_base = ((vrow >> 4) * 4) * 1024 + (vrow & 15) * 64 + (2 * (g16 & 1) + ((i16 & 3) >> 1)) * 16 + (i16 & 1) * 8;
+  const int vrow = 4 * hi + (i16 >> 2);
+  const int v_base = vrow * 64 + (2 * (g16 & 1) + ((i16 & 3) >> 1)) * 16 + (i16 & 1) * 8;
   const lds_char_t* const ke_ptr = lds + kKRing + k_even;
   const lds_char_t* const ko_ptr = lds + kKRing + k_odd;
   const lds_char_t* const v_ptr = lds + kVRing + v_base;
-  const lds_u64_t* const bits_ptr = reinterpret_cast<const lds_u64_t*>(lds + kBitsRing + q_local * 8);
 
-  // ---- Q fragments (B operand of S^T = K Q^T): 12 chunks of 16 dims
-  bf16x8_t qf[kDqk / 16];
-  {
-    const uint16_t* qp = a.q + (bh * a.Lq + (q_ok ? q_row : 0)) * kDqk + 8 * hi;
+  // ---- Q fragments (B operand of S^T = K Q^T), stream i, 12 chunks of 16 dims.
+  // The q_rope chunks 8-11 are loaded straight into accumulator registers (the
+  // MFMA reads its B operand from either file; each asm load waits for itself):
+  // the vector registers stay free for the operand windows and the softmax.
+  // Rows past Lq read row 0 (their results are never stored).
+  bf16x8_t qf[2][kDqk / 16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint16_t* qp = a.q + (bh * a.Lq + (q_ok[i] ? q_row[i] : 0)) * kDqk + 8 * hi;
 #pragma unroll
     for (int c = 0; c < kDqk / 16; ++c) {
-      const u32x4_t z = {0u, 0u, 0u, 0u};
-      qf[c] = as_bf16x8(q_ok ? ldg16(qp + 16 * c) : z);
+      if (c < 8) {
+        qf[i][c] = as_bf16x8(ldg16(qp + 16 * c));
+      } else {
+        u32x4_t x;
+        asm volatile("global_load_dwordx4 %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=a"(x) : "v"(qp + 16 * c) : "memory");
+        qf[i][c] = as_bf16x8(x);
+      }
     }
   }
 
-  f32x16_t o[4];
+  f32x16_t o[2][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[j][r] = 0.f;
-  float m_run = -INFINITY;   // stabiliser (natural units), same in both lane halves
-  float l_run = 0.f;         // this lane's partial row sum
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[i][j][r] = 0.f;
+  float m_run[2] = {-INFINITY, -INFINITY};   // stabiliser (natural units), same in both lane halves
+  float l_run[2] = {0.f, 0.f};               // this lane's partial row sums
+  // per stream: the C operand of the first score MFMA of a step, -inf at the keys
+  // a binary tile hides and 0 elsewhere (all zero outside binary tiles; bias_nz
+  // tells whether it needs clearing)
+  f32x16_t bias[2];
+  bool bias_nz[2] = {false, false};
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) bias[i][r] = 0.f;
+  bool over = false;                         // a score rose more than kHeadroom above its stabiliser
+  f32x16_t s[2];                             // raw scores of each stream's pending softmax step
+  uint32_t pk[2][8];                         // P^T of each stream's step awaiting PV, bf16 pairs
+  bf16x8_t kf[kPK];                          // first K operands of the next phase, read ahead
+  s16x8_t vf[8];                             // V^T operands of the step awaiting PV (op = 4*st + j)
 
   const float scale = a.scale;
   const float scale_log2 = a.scale * kLog2e;
-  const size_t mask_row = (static_cast<size_t>(b) * a.Lq + (q_ok ? q_row : 0)) * a.Lk;
-
-  f32x16_t s;                    // scores of the tile between its matrix and vector phases
-  bf16x8_t kf[kDqk / 16];        // K operands of the next score tile
-  uint32_t pk[8];                // P^T of the tile awaiting PV, bf16 pairs
-
-  // K operand chunks [C0, C1) of ring slot SL into registers
-  auto read_k = [&](uint32_t slot_off, auto C0, auto C1) __attribute__((always_inline)) {
+  size_t mask_row[2];
 #pragma unroll
-    for (int c = decltype(C0)::value; c < decltype(C1)::value; ++c) {
-      const lds_char_t* kp = ((c & 1) ? ko_ptr : ke_ptr) + slot_off + (c >> 1) * 1024;
-      kf[c] = as_bf16x8(*reinterpret_cast<const lds_u32x4_t*>(kp));
-    }
+  for (int i = 0; i < 2; ++i) mask_row[i] = (static_cast<size_t>(b) * a.Lq + (q_ok[i] ? q_row[i] : 0)) * a.Lk;
+
+  auto read_k = [&](int slot, int c) __attribute__((always_inline)) -> bf16x8_t {
+    const lds_char_t* kp = ((c & 1) ? ko_ptr : ke_ptr) + slot * kKSlot + (c >> 1) * 1024;
+    return as_bf16x8(*reinterpret_cast<const lds_u32x4_t*>(kp));
   };
-  // First K operands of ring slot SL (the rest are read in the matrix phase, behind
-  // the first MFMAs); for a binary tile also its hidden-key word, applied to the
-  // scores in the vector phase.
-  uint32_t hid_next = 0, hid = 0;   // bit 8g+c <-> key kh*32+8g+4hi+c of the tile is hidden
-  auto load_k = [&](int slot, int e) __attribute__((always_inline)) {
-    read_k(slot * kKBytes, IC<0>{}, IC<kPrefetchK>{});
+  auto read_v = [&](int slot, int op) __attribute__((always_inline)) -> s16x8_t {
+    const lds_char_t* vp = v_ptr + slot * kVSlot + (op >> 2) * 4096 + (op & 3) * 1024;
+    const s16x4_t lo = ds_read_tr(vp);
+    const s16x4_t hi4 = ds_read_tr(vp + 512);
+    return s16x8_t{lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+  };
+  // bias of stream i for step s of tile entry e: from the query's visibility
+  // word, bit 8g+c <-> key 8g+4hi+c of the step (accumulator r = 4g+c), when
+  // the tile is binary.  The bit-field width comes from an opaque register (it
+  // is 1) so each entry compiles to a bit-field extract and an and.
+  int one;
+  asm("s_mov_b32 %0, 1" : "=s"(one));
+  auto set_bias = [&](auto I, int s, int e) __attribute__((always_inline)) {
+    constexpr int i = decltype(I)::value;
     if ((e >> 24) == 2) {
-      const uint64_t w64 = bits_ptr[slot * (kBitsBytes / 8)];
-      hid_next = ~static_cast<uint32_t>(w64 >> (kh * 32 + 4 * hi));
+      const int bslot = (s >> 1) % kNB;
+      const uint64_t w64 = *reinterpret_cast<const lds_u64_t*>(lds + kBitsRing + bslot * kBitsSlot + q_local[i] * 8);
+      const int hv = static_cast<int>(~static_cast<uint32_t>(w64 >> (32 * (s & 1) + 4 * hi)));
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        bias[i][r] = __int_as_float(__builtin_amdgcn_sbfe(hv, 8 * (r >> 2) + (r & 3), one) & static_cast<int>(kNegInfBits));
+      bias_nz[i] = true;
+    } else if (bias_nz[i]) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) bias[i][r] = 0.f;
+      bias_nz[i] = false;
     }
   };
-  auto score_mfma = [&]() __attribute__((always_inline)) {
-    const f32x16_t z = {};
-    s = mfma32(kf[0], qf[0], z);
-#pragma unroll
-    for (int c = 1; c < kDqk / 16; ++c) s = mfma32(kf[c], qf[c], s);
-  };
-  // O^T += V^T P^T over this wave's 32 keys (two 16-key MFMA steps).  B operand
-  // element e of lane (li, hi) is key 8*(e>>2) + 4*hi + (e&3) of the step; the
-  // transposing reads deliver V[that key][32*j + li] as A operand.
-  s16x8_t av[2][4];              // V^T operands of the tile awaiting PV
-  auto read_v = [&](uint32_t slot_off) __attribute__((always_inline)) {
-#pragma unroll
-    for (int step = 0; step < 2; ++step)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const lds_char_t* vp = v_ptr + slot_off + step * 4096 + j * 1024;
-        const s16x4_t lo = ds_read_tr(vp);
-        const s16x4_t hi4 = ds_read_tr(vp + 512);
-        av[step][j] = s16x8_t{lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-      }
-  };
-  auto pv_mfma = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int step = 0; step < 2; ++step) {
-      const u32x4_t pb = {pk[4 * step + 0], pk[4 * step + 1], pk[4 * step + 2], pk[4 * step + 3]};
-      const bf16x8_t bfr = as_bf16x8(pb);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] = mfma32(__builtin_bit_cast(bf16x8_t, av[step][j]), bfr, o[j]);
-    }
-  };
-  // p = exp2(fma(x, ca, cb)) -> pk (bf16 pairs); returns the lane's sum of p.  The sum
-  // uses plain fp32 adds: v_dot2 would wait for the matrix core, which the other
-  // wave of the SIMD keeps busy during this phase.
-  auto probs = [&](const float* x, float ca, float cb) __attribute__((always_inline)) -> float {
+
+  // p = exp2(fma(x, ca, cb)) -> pk (bf16 pairs); returns the lane's sum of p
+  auto probs = [&](uint32_t* pk, const float* x, float ca, float cb) __attribute__((always_inline)) -> float {
     float p[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], ca, cb));
@@ -311,191 +383,304 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
     }
     return l0 + l1;
   };
-  // Vector phase: softmax of the raw scores in s (tile entry e) -> pk, m_run, l_run, o.
-  // Fast path (zero or binary tile, no ragged end): probabilities with the
-  // current stabiliser, hidden keys set to -inf first.  Exact path (general mask,
-  // ragged end, no stabiliser yet, or a probability that may exceed 2^8): masked
-  // natural-unit scores, tile max, rescale of O and l when the stabiliser rises,
-  // probabilities.
-  auto softmax = [&](int e) __attribute__((always_inline)) {
+  // scaled scores of stream i on the step at (entry e, half), natural units:
+  // general mask values added and keys past Lk at -inf (the hidden keys of a
+  // binary tile are -inf already: the score MFMAs started from their bias)
+  auto masked_scores = [&](auto I, int e, int half, const f32x16_t& s, float* x) __attribute__((always_inline)) {
+    constexpr int i = decltype(I)::value;
     const int cls = e >> 24;
-    const int k0 = (e & 0xFFFFFF) * kTileN;
-    const bool ragged = k0 + kTileN > a.Lk;
-    float lsum = 0.f;
-    bool exact = true;
-    // (a lane with no stabiliser yet takes the exact path: skip the fast attempt)
-    if ((cls == 1 || cls == 2) && !ragged && !__any(m_run == -INFINITY)) {
-      // hidden keys of a binary tile become -inf, whose probability is exactly 0
-      float x[16];
-      if (cls == 2) {
+    // accumulator r <-> key kbase + 8*(r>>2) + (r&3)
+    const int kbase = (e & 0xFFFFFF) * kTileN + 32 * half + 4 * hi;
+    if (cls == 3 && a.mask) {   // (a reused map without its mask: no values to add)
+      float mv[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int h1 = __builtin_amdgcn_sbfe(static_cast<int>(hid), 8 * (r >> 2) + (r & 3), 1);   // -1: hidden
-          x[r] = __int_as_float((h1 & static_cast<int>(kNegInfBits)) | (~h1 & __float_as_int(s[r])));
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = s[r];
+      for (int r = 0; r < 16; ++r) {   // all 16 loads in flight together (clamped index, fixed below)
+        const int kk = kbase + 8 * (r >> 2) + (r & 3);
+        mv[r] = load_mask<MASK_BF16>(a.mask, mask_row[i] + min(kk, a.Lk - 1));
       }
-      lsum = probs(x, scale_log2, -(m_run == -INFINITY ? 0.f : m_run) * kLog2e);
-      exact = __any(!(lsum <= kSumLimit));   // NaN sums too
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = __builtin_fmaf(s[r], scale, q_ok[i] ? mv[r] : 0.f);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = s[r] * scale;
     }
-    if (__builtin_expect(exact, 0)) {
-      // accumulator r <-> key k0 + kh*32 + 8*(r>>2) + 4*hi + (r&3)
-      const int kbase = k0 + kh * 32 + 4 * hi;
-      float x[16];
-      if (cls == 3 && a.mask) {   // (a reused map without its mask: no values to add)
-        // general mask values: x = scale*qk + mask
-        float mv[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {   // all 16 loads in flight together (clamped index, fixed below)
-          const int kk = kbase + 8 * (r >> 2) + (r & 3);
-          mv[r] = load_mask<MASK_BF16>(a.mask, mask_row + min(kk, a.Lk - 1));
-        }
+    for (int r = 0; r < 16; ++r)
+      if (kbase + 8 * (r >> 2) + (r & 3) >= a.Lk) x[r] = -INFINITY;
+  };
+  // maximum of the lane's query over the step (both lane halves)
+  auto step_max = [&](const float* x) __attribute__((always_inline)) -> float {
+    float tmax = x[0];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = __builtin_fmaf(s[r], scale, q_ok ? mv[r] : 0.f);
+    for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, x[r]);
+    return halves_max(tmax);
+  };
+  // exact path of stream i.  The stabiliser is never raised once set, so O is
+  // never rescaled: a lane without one takes the step's maximum (its O and l are
+  // still zero), and a lane whose scores rise more than kHeadroom above its
+  // stabiliser marks the work item for the second pass.
+  auto soft_exact = [&](auto I, int e, int half, const f32x16_t& s, uint32_t* pk) __attribute__((always_inline)) {
+    constexpr int i = decltype(I)::value;
+    float x[16];
+    masked_scores(I, e, half, s, x);
+    const float tmax = step_max(x);
+    if (m_run[i] == -INFINITY) m_run[i] = tmax;
+    else if (!(tmax <= m_run[i] + kHeadroom)) over = true;
+    // subtract before scaling: m * log2e can overflow where x - m does not (mask values near -FLT_MAX)
+    const float m_use = m_run[i] == -INFINITY ? 0.f : m_run[i];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] -= m_use;
+    l_run[i] += probs(pk, x, kLog2e, 0.f);
+  };
+  // ---- one phase of the accumulation pass, scheduled by hand: 20 slots
+  // separated by scheduling barriers.  Slot k issues the k-th MFMA of stream
+  // MS's matrix work (scores of the next step into s[MS] from K slot ks, the
+  // first kPK chunks already in kf, chunk c+2 read in the slot of chunk c; PV of
+  // the current step into o[MS] with the V operands vf and P^T pk[MS], each V
+  // register refilled from slot vsl after its MFMA with RELOAD) and, from slot 2
+  // on, one unit of the fast softmax of stream VS = 1 - MS on s[VS],
+  // software-pipelined over its 16 scores (exponential of score u, sum and bf16
+  // pair of score u-1).  Starting the softmax two MFMA
+  // issues into the phase keeps the other stream's last score MFMA of the
+  // previous phase at a safe distance from its readers.  Returns the lane's sum.
+  auto phase_fast = [&](auto MSc, auto RELOAD, auto EXTRA, int ks, int vsl) __attribute__((always_inline)) -> float {
+    constexpr int ms = decltype(MSc)::value;
+    constexpr int vs = 1 - ms;
+    constexpr bool reload = decltype(RELOAD)::value;
+    const float cb = -m_run[vs] * kLog2e;
+    bf16x8_t kw[kDqk / 16];
+#pragma unroll
+    for (int c = 0; c < kPK; ++c) kw[c] = kf[c];
+    f32x16_t acc;
+    float p[16];
+    float l0 = 0.f, l1 = 0.f;
+    static_for<20>([&](auto K) __attribute__((always_inline)) {
+      constexpr int k = decltype(K)::value;
+      constexpr int op = kSlotOp[k];
+      if constexpr (op < 100) {
+        constexpr int c = op;
+        if constexpr (c + kPK < kDqk / 16) kw[c + kPK] = read_k(ks, c + kPK);
+        mfma_s<c == 0, (c >= 8)>(acc, kw[c], qf[ms][c], bias[ms]);
       } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = s[r] * scale;
-        if (cls == 2) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int h1 = __builtin_amdgcn_sbfe(static_cast<int>(hid), 8 * (r >> 2) + (r & 3), 1);   // -1: hidden
-            x[r] = __int_as_float((h1 & static_cast<int>(kNegInfBits)) | (~h1 & __float_as_int(x[r])));
-          }
+        constexpr int v = op - 100, st = v >> 2, j = v & 3;
+        const u32x4_t pb = {pk[ms][4 * st + 0], pk[ms][4 * st + 1], pk[ms][4 * st + 2], pk[ms][4 * st + 3]};
+        o[ms][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[v]), as_bf16x8(pb),
+                                                           o[ms][j], 0, 0, 0);
+        if constexpr (reload) vf[v] = read_v(vsl, v);
+      }
+      EXTRA(K);
+      constexpr int u = k - 2;
+      if constexpr (u >= 0 && u < 16) {
+        p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[vs][u], scale_log2, cb));
+      }
+      if constexpr (u >= 1 && u <= 16) {
+        constexpr int w = u - 1;
+        if constexpr (w & 1) {
+          l1 += p[w];
+          pk[vs][w >> 1] = pack_bf16x2(p[w - 1], p[w]);
+        } else {
+          l0 += p[w];
         }
       }
-      if (ragged) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kbase + 8 * (r >> 2) + (r & 3) >= a.Lk) x[r] = -INFINITY;
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    s[ms] = acc;
+    return l0 + l1;
+  };
+  // ---- one phase of the max-only pass: scores of the next step for stream MS,
+  // the maximum of stream VS's step
+  auto phase_max = [&](auto MSc, auto EXTRA, int ks, int e, int half, bool live) __attribute__((always_inline)) {
+    constexpr int ms = decltype(MSc)::value;
+    constexpr int vs = 1 - ms;
+    static_for<20>([&](auto K) __attribute__((always_inline)) { EXTRA(K); });
+    f32x16_t acc;
+    static_for<kDqk / 16>([&](auto C) __attribute__((always_inline)) {
+      constexpr int c = decltype(C)::value;
+      bf16x8_t kop;
+      if constexpr (c < kPK) kop = kf[c]; else kop = read_k(ks, c);
+      mfma_s<c == 0, (c >= 8)>(acc, kop, qf[ms][c], bias[ms]);
+    });
+    s_nop_after_mfma(acc);
+    s[ms] = acc;
+    if (live) {
+      float x[16];
+      masked_scores(IC<vs>{}, e, half, s[vs], x);
+      m_run[vs] = fmaxf(m_run[vs], step_max(x));
+    }
+  };
+  // ---- one phase: matrix work of stream MS and softmax of stream VS = 1 - MS
+  // for the step at (entry e, half); the exact path follows when the step is
+  // general or ragged, a lane has no stabiliser yet, or a probability may exceed
+  // the headroom
+  auto phase = [&](auto MSc, auto MODE, auto RELOAD, auto EXTRA, int ks, int vsl, int e, int half, bool live)
+      __attribute__((always_inline)) {
+    constexpr int vs = 1 - decltype(MSc)::value;
+    if constexpr (decltype(MODE)::value == kPassMax) {
+      phase_max(MSc, EXTRA, ks, e, half, live);
+    } else {
+      const int cls = e >> 24;
+      const bool slow = cls == 3 || (e & 0xFFFFFF) * kTileN + 32 * half + 32 > a.Lk || __any(m_run[vs] == -INFINITY);
+      const float lsum = phase_fast(MSc, RELOAD, EXTRA, ks, vsl);
+      // the fast path's results are used on every path, so the compiler keeps it
+      // in the scheduled block instead of moving it behind the test below
+      asm volatile("" :: "v"(lsum), "v"(pk[vs][0]), "v"(pk[vs][1]), "v"(pk[vs][2]), "v"(pk[vs][3]), "v"(pk[vs][4]),
+                   "v"(pk[vs][5]), "v"(pk[vs][6]), "v"(pk[vs][7]));
+      if (live) {
+        if (__builtin_expect(slow || __any(!(lsum <= kSumLimit)), 0))   // NaN sums too
+          soft_exact(IC<vs>{}, e, half, s[vs], pk[vs]);
+        else
+          l_run[vs] += lsum;
       }
-      float tmax = x[0];
+    }
+  };
+
+  // ---- one pass over the tile list (MODE: kPassNormal accumulates O and l,
+  // kPassMax only the row maxima)
+  auto run = [&](auto MODE) __attribute__((always_inline)) {
+    // prologue: K(0..3), V(0..2), words of tiles 0, 1 land; scores of step 0 for
+    // both streams and stream 0's softmax of step 0; V(0) and the first K(1)
+    // chunks into registers
+    int e0 = entry(0), e1 = entry(1), e2 = entry(2), e3 = entry(3);   // tiles T .. T+3 (T = t/2)
+    issue_k(0, key0_of(e0, 0));
+    issue_k(1, key0_of(e0, 1));
+    issue_k(2, key0_of(e1, 0));
+    issue_k(3, key0_of(e1, 1));
+    issue_v(0, key0_of(e0, 0));
+    issue_v(1, key0_of(e0, 1));
+    issue_v(2, key0_of(e1, 0));
+    issue_bits(0, e0);
+    issue_bits(1, e1);
+    wait_vmem<0>();
+    __syncthreads();
+    set_bias(IC<0>{}, 0, e0);
+    set_bias(IC<1>{}, 0, e0);
+    {
+      f32x16_t a0, a1;
+      static_for<kDqk / 16>([&](auto C) __attribute__((always_inline)) {
+        constexpr int c = decltype(C)::value;
+        const bf16x8_t kop = read_k(0, c);
+        mfma_s<c == 0, (c >= 8)>(a0, kop, qf[0][c], bias[0]);
+        mfma_s<c == 0, (c >= 8)>(a1, kop, qf[1][c], bias[1]);
+      });
+      s_nop_after_mfma(a0);
+      s_nop_after_mfma(a1);
+      s[0] = a0;
+      s[1] = a1;
+    }
+    if (nsteps > 0) {
+      if (decltype(MODE)::value == kPassMax) {
+        float x[16];
+        masked_scores(IC<0>{}, e0, 0, s[0], x);
+        m_run[0] = fmaxf(m_run[0], step_max(x));
+      } else {
+        soft_exact(IC<0>{}, e0, 0, s[0], pk[0]);
+      }
+    }
+    set_bias(IC<0>{}, 1, e0);
 #pragma unroll
-      for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, x[r]);
-      const float m_new = fmaxf(m_run, halves_max(tmax));
-      if (__any(m_new != m_run)) {
-        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e);
-        l_run *= alpha;
+    for (int op = 0; op < 8; ++op) vf[op] = read_v(0, op);
+#pragma unroll
+    for (int c = 0; c < kPK; ++c) kf[c] = read_k(1, c);
+    __syncthreads();
+
+    // Step t (tile T = t/2 in e0, T+1 in e1, T+2 in e2; half t&1).  K(s) lives in
+    // K slot s%4, V(s) in V slot s%3, the words of tile T in slot T%3.  Registers
+    // on entry: vf = V(t), kf = first chunks of K(t+1), s[1] = stream 1's raw
+    // scores of step t, pk[0] = stream 0's P^T of step t.
+    //   copies: K(t+4) into K(t)'s slot (read in step t-1), V(t+3) into V(t)'s
+    //           slot (read into registers in step t-1) and, at even t, the words
+    //           of tile T+2
+    //   phase A: matrix of stream 0 (scores t+1 from K(t+1), PV t)
+    //            || softmax of stream 1, step t
+    //   phase B: matrix of stream 1 (scores t+1 from K(t+1), PV t; V(t+1)
+    //            replaces vf register by register) || softmax of stream 0, step
+    //            t+1; then the first chunks of K(t+2)
+    //   then each wave waits for its copies of step t-1 and the workgroup
+    //   synchronises: K(t+3), V(t+2) and their words are published, the slots
+    //   read in step t are free.
+    for (int t = 0; t < nsteps; ++t) {
+      const int half = t & 1;
+      const int k4 = t & 3;
+      const int k41 = (t + 1) & 3;
+      const int k42 = (t + 2) & 3;
+      const int v3 = t % 3;
+      const int v31 = v3 == 2 ? 0 : v3 + 1;          // (t+1) % 3
+      // copies of the step, one per MFMA slot: K(t+4) and (even t) the words of
+      // tile T+2 in phase A, V(t+3) in phase B
+      const int kkey = key0_of(e2, half);                              // K(t+4)
+      const int vkey = half ? key0_of(e2, 0) : key0_of(e1, 1);         // V(t+3)
+      const int bslot = ((t >> 1) + 2) % kNB;
+      auto copies_a = [&](auto K) __attribute__((always_inline)) {
+        constexpr int k = decltype(K)::value;
+        if constexpr (k % 3 == 1 && k / 3 < 6) issue_k_piece(IC<k / 3>{}, k4, kkey);
+        if constexpr (k == 18) {
+          if (!half) issue_bits(bslot, e2);
+        }
+      };
+      auto copies_b = [&](auto K) __attribute__((always_inline)) {
+        constexpr int k = decltype(K)::value;
+        if constexpr (k % 4 == 1 && k / 4 < 4) issue_v_piece(IC<k / 4>{}, v3, vkey);
+      };
+      // ---- phase A
+      phase(IC<0>{}, MODE, std::false_type{}, copies_a, k41, 0, e0, half, true);
+#pragma unroll
+      for (int c = 0; c < kPK; ++c) kf[c] = read_k(k41, c);
+      set_bias(IC<1>{}, t + 1, half ? e1 : e0);                       // scores of stream 1, step t+1
+      // ---- phase B
+      phase(IC<1>{}, MODE, std::true_type{}, copies_b, k41, v31, half ? e1 : e0, half ^ 1, t + 1 < nsteps);
+#pragma unroll
+      for (int c = 0; c < kPK; ++c) kf[c] = read_k(k42, c);
+      set_bias(IC<0>{}, t + 2, e1);                                     // scores of stream 0, step t+2
+      // copies of step t-1 complete (those of step t, 10 per wave and wave 0's
+      // word copy at even t, may still be in flight)
+      if (wave == 0 && !half) wait_vmem<11>(); else wait_vmem<10>();
+      __syncthreads();
+      if (half) {
+        e0 = e1; e1 = e2; e2 = e3;
+        e3 = entry((t >> 1) + 4);
+      }
+    }
+    wait_vmem<0>();
+  };
+
+  run(IC<kPassNormal>{});
+  // Some row of the item rose more than the headroom above its stabiliser: both
+  // waves take the second pass (row maxima, then the accumulation again with the
+  // exact maxima as stabilisers, which no probability can exceed).
+  {
+    __syncthreads();
+    int* const flag = reinterpret_cast<int*>(smem);
+    if (threadIdx.x == 0) *flag = 0;
+    __syncthreads();
+    if (lane == 0 && __any(over)) *flag = 1;
+    __syncthreads();
+    const bool redo = *flag != 0;
+    __syncthreads();
+    if (__builtin_expect(redo, 0)) {
+      m_run[0] = m_run[1] = -INFINITY;
+      run(IC<kPassMax>{});
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        l_run[i] = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[j][r] *= alpha;
-        m_run = m_new;
+          for (int r = 0; r < 16; ++r) o[i][j][r] = 0.f;
       }
-      // subtract before scaling: m * log2e can overflow where x - m does not (mask values near -FLT_MAX)
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] -= m_use;
-      lsum = probs(x, kLog2e, 0.f);
+      run(IC<kPassNormal>{});
     }
-    l_run += lsum;
-  };
-
-  // ---- prologue: K(0..3), bits(0..3), V(0..1) land before anyone reads
-  int e0 = entry(0), e1 = entry(1), e2 = entry(2), e3 = entry(3), e4 = entry(4);   // tiles t .. t+4
-  int e5 = entry(5);
-  issue_k(0 * kKBytes, k0_of(e0));
-  issue_k(1 * kKBytes, k0_of(e1));
-  issue_k(2 * kKBytes, k0_of(e2));
-  issue_k(3 * kKBytes, k0_of(e3));
-  issue_v(0 * kVBytes, k0_of(e0));
-  issue_v(1 * kVBytes, k0_of(e1));
-  issue_bits(0 * kBitsBytes, bits_kt(e0));
-  issue_bits(1 * kBitsBytes, bits_kt(e1));
-  issue_bits(2 * kBitsBytes, bits_kt(e2));
-  issue_bits(3 * kBitsBytes, bits_kt(e3));
-  wait_vmem<0>();
-  __syncthreads();
-
-  // Phase schedule (every phase ends with a workgroup barrier):
-  //   key half 0:  S(0) | V(0) | M(0) | V(1) | M(1) | ... | M(T-1) | idle
-  //   key half 1:  idle | S(0) | V(0) | M(0) | V(1) | ... | V(T-1) | M(T-1)
-  // M(t) = scores of tile t+1 and PV of tile t; V(t) = softmax of tile t.
-  // Tile u lives in K / bits slot u%4 and V slot u%3.  Copies of K(t+4),
-  // bits(t+4) and V(t+2) are issued at the start of the phase both halves run
-  // in slot 2t+2 (half 0: M(t), half 1: V(t)): the slots they overwrite were
-  // last read in slot 2t+1.  Each wave waits for its own copies before the
-  // barrier that precedes their first read: K(t+2), bits(t+2) at the end of
-  // slot 2t+2 (first read in slot 2t+3), V(t+1) at the end of slot 2t+3.
-  if (kh == 1) __syncthreads();
-  load_k(0, e0);
-  read_k(0, IC<kPrefetchK>{}, IC<kDqk / 16>{});
-  score_mfma();
-  hid = hid_next;
-  __syncthreads();
-
-  int v3 = 0;                                      // t % 3
-  for (int it = 0; it < ntiles; ++it) {
-    const int k4 = it & 3;                         // K / bits slot of tile it (and it+4)
-    const int k4n = (it + 1) & 3;                  // K / bits slot of tile it+1
-    const int v3n2 = v3 == 0 ? 2 : v3 - 1;         // V slot of tile it+2
-    const int e_next = e5;
-    e5 = entry(it + 6);
-    auto issue_copies = [&]() __attribute__((always_inline)) {
-      issue_k(k4 * kKBytes, k0_of(e4));
-      issue_bits(k4 * kBitsBytes, bits_kt(e4));
-      issue_v(v3n2 * kVBytes, k0_of(e2));
-    };
-    // ---- vector phase: K operands of tile it+1, softmax of tile it
-    if (it + 1 < ntiles) load_k(k4n, e1);
-    if (kh == 1) issue_copies();
-    softmax(e0);
-    if (kh == 0) {            // V(it): issued three phases ago, five (six) copies since
-      if (wave == 0) wait_vmem<6>(); else wait_vmem<5>();
-    } else {                  // K(it+2): twelve copies since
-      wait_vmem<12>();
-    }
-    __syncthreads();
-    // ---- matrix phase: scores of tile it+1 (after the last tile they score stale
-    // data and are never used), PV of tile it.  The remaining K operands and all V
-    // operands are requested before the first MFMA; the first eight score MFMAs run
-    // on operands already in registers while they arrive.
-    if (kh == 0) issue_copies();
-    read_k(k4n * kKBytes, IC<kPrefetchK>{}, IC<kDqk / 16>{});
-    read_v(v3 * kVBytes);
-    __builtin_amdgcn_sched_barrier(0);
-    score_mfma();
-    pv_mfma();
-    if (kh == 0) {            // K(it+2), bits(it+2): twelve (fourteen) copies since
-      if (wave == 0) wait_vmem<14>(); else wait_vmem<12>();
-    } else {                  // V(it+1): five copies since
-      wait_vmem<5>();
-    }
-    __syncthreads();
-    e0 = e1; e1 = e2; e2 = e3; e3 = e4; e4 = e_next;
-    hid = hid_next;
-    v3 = v3 == 2 ? 0 : v3 + 1;
   }
-  if (kh == 0) __syncthreads();
-  wait_vmem<0>();
 
-  // ---- merge the two key halves of each query group, normalise, store
-  l_run = halves_sum(l_run);
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(smem) + qg * (64 * 66);   // O[16][4][64] + m[64] + l[64]
-  if (kh == 1) {
+  // ---- normalise and store
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) red[(r * 4 + j) * 64 + lane] = o[j][r];
-    red[64 * 64 + lane] = m_run;
-    red[65 * 64 + lane] = l_run;
-  }
-  __syncthreads();
-  if (kh == 0) {
-    const float m1 = red[64 * 64 + lane];
-    const float l1 = red[65 * 64 + lane];
-    const float m = fmaxf(m_run, m1);
-    const float a0 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m) * kLog2e);
-    const float a1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * kLog2e);
-    const float l = l_run * a0 + l1 * a1;
+  for (int i = 0; i < 2; ++i) {
+    const float l = halves_sum(l_run[i]);
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    const float lse_row = l > 0.f ? m + __logf(l) : -INFINITY;
+    const float lse_row = l > 0.f ? m_run[i] + __logf(l) : -INFINITY;
     if (a.part_o) {            // one run of a split row: fp32 partials for the combine
-      const size_t prow = (static_cast<size_t>(sp) * a.B * a.H + bh) * a.Lq + q_row;
-      if (q_ok && hi == 0) a.part_lse[prow] = lse_row;
-      if (q_ok) {
+      const size_t prow = (static_cast<size_t>(sp) * a.B * a.H + bh) * a.Lq + q_row[i];
+      if (q_ok[i] && hi == 0) a.part_lse[prow] = lse_row;
+      if (q_ok[i]) {
         float* pp = a.part_o + prow * kDv;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -503,30 +688,22 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_bf16(AttnBf16Args a) {
           for (int g = 0; g < 4; ++g) {
             f32x4_t x;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const int r = 4 * g + c;
-              x[c] = (o[j][r] * a0 + red[(r * 4 + j) * 64 + lane] * a1) * inv;
-            }
+            for (int c = 0; c < 4; ++c) x[c] = o[i][j][4 * g + c] * inv;
             *reinterpret_cast<f32x4_t*>(pp + 32 * j + 8 * g + 4 * hi) = x;
           }
       }
-      return;
+      continue;
     }
-    if (a.lse && q_ok && hi == 0) a.lse[bh * a.Lq + q_row] = lse_row;
-    if (q_ok) {
-      uint16_t* op = a.out + (bh * a.Lq + q_row) * kDv;
-      // o[j][r] holds dv = 32*j + 8*(r>>2) + 4*hi + (r&3)
+    if (a.lse && q_ok[i] && hi == 0) a.lse[bh * a.Lq + q_row[i]] = lse_row;
+    if (q_ok[i]) {
+      uint16_t* op = a.out + (bh * a.Lq + q_row[i]) * kDv;
+      // o[i][j][r] holds dv = 32*j + 8*(r>>2) + 4*hi + (r&3)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          float x[4];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int r = 4 * g + c;
-            x[c] = (o[j][r] * a0 + red[(r * 4 + j) * 64 + lane] * a1) * inv;
-          }
-          const u32x2_t w2 = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+          const u32x2_t w2 = {pack_bf16x2(o[i][j][4 * g] * inv, o[i][j][4 * g + 1] * inv),
+                              pack_bf16x2(o[i][j][4 * g + 2] * inv, o[i][j][4 * g + 3] * inv)};
           *reinterpret_cast<u32x2_t*>(op + 32 * j + 8 * g + 4 * hi) = w2;
         }
     }

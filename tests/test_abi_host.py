@@ -320,7 +320,10 @@ def test_map_only_reuse_validation(lib):
 
 def test_split_keys_workspace_bytes(lib):
     mb, sb = lib.dflash_mla_attn_workspace_bytes, lib.dflash_mla_attn_split_workspace_bytes
-    assert sb(1, 64, 1024, 9216) == mb(1, 1024, 9216)      # 512 items already: no split, the map alone
+    # 512 items fit one round of two workgroups per CU: 2 runs each
+    rows2, m2 = 64 * 1024, mb(1, 1024, 9216)
+    assert m2 + 2 * rows2 * (128 * 4 + 4) <= sb(1, 64, 1024, 9216) <= m2 + 2 * rows2 * (128 * 4 + 4) + 3 * 256
+    assert sb(1, 32, 4096, 36864) == mb(1, 4096, 36864)    # 1024 items: no split, the map alone
     assert sb(1, 2, 32, 96) == mb(1, 32, 96)               # 2 k-tiles: too short to split
     # 2 batches x 2 q-tiles x 16 heads = 64 items over 36 k-tiles: 4 runs
     rows, m = 2 * 16 * 256, mb(2, 256, 2304)
