@@ -15,7 +15,8 @@ What it computes, and the passages it follows:
   weighted sum of v.  NeMo AutoModel pages: "dflash.draft_kimi_k3" --
   KimiK3DFlashAttention (class text and forward: one K/V per query head, no GQA
   repeat; the mask is passed through unchanged) and the module text on NoPE
-  (the rope slice is a plain head-shared extension of the key); "dspark.draft_kimi_k3"
+  (no rotary embedding: the 64 rope channels are one more part of the key, the
+  same for every head); "dspark.draft_kimi_k3"
   -- KimiK3DSparkAttention attributes (q_head_dim, scaling) and forward
   (context concatenated before the noise block).
 * ``expand.latent_expand`` -- kv_b_proj as a plain Linear: per head a slice of

@@ -1,16 +1,17 @@
 """fp64 GQA draft attention with yarn RoPE and qk-norm -- the plain definitions (test infrastructure only).
 
-Modular MAX page, pipelines.architectures.dflash_kimi_k25: a DFlash draft for
-a Kimi K2.5 (DeepSeek-V3 MLA) target whose own attention is standard MHA/GQA
-with DeepSeek-yarn RoPE, so its KV cache is decoupled from the target's MLA
-layout; the context K/V are written into the draft's cache once
-(DFlashKimiK25.materialize) and every block then attends to that cache plus
-itself (DFlashKimiK25.forward_block; same architecture as the llama3 DFlash
-draft: a non-causal block transformer with external-KV materialisation).  The
-cache is bfloat16 whatever the target caches in and as wide as the block it
-writes (construct_kv_params); the config has num_attention_heads,
-num_key_value_heads, head_dim, rms_norm_eps, rope_theta, rope_scaling and
-use_qk_norm (DFlashKimiK25DraftConfig).
+Modular MAX page, pipelines.architectures.dflash_kimi_k25 (module text): a
+DFlash draft for a Kimi K2.5 (DeepSeek-V3 MLA) target.  The draft's own
+attention is ordinary MHA/GQA with DeepSeek-yarn RoPE, so its KV cache has its
+own layout, independent of the target's MLA cache.  The context K/V go into
+the draft's cache once (DFlashKimiK25.materialize); each block then attends to
+that cache plus its own keys (DFlashKimiK25.forward_block), as in the page's
+llama3 DFlash draft.  construct_kv_params: the draft's cache is always bf16,
+independent of the target's cache dtype, and is sized by the draft block it
+stores.  The
+config fields are num_attention_heads, num_key_value_heads, head_dim,
+rms_norm_eps, rope_theta, rope_scaling and use_qk_norm
+(DFlashKimiK25DraftConfig).
 
 Readings (the page prints no arithmetic):
   * yarn RoPE as DeepSeek-V3 defines it: per frequency pair i of the rotary

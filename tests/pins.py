@@ -527,6 +527,70 @@ def pin_yarn_limits():
     assert abs(oracle.yarn_mscale(math.e, 1.0) - 1.1) < 1e-15
 
 
+def _rotations(j, d, theta, orig):
+    """Turns pair j makes over orig positions at its unscaled frequency theta^(-2j/d)."""
+    return orig * theta ** (-2.0 * j / d) / (2.0 * math.pi)
+
+
+def pin_yarn_ntk_by_parts():
+    """yarn's frequency split, from its defining rule (YaRN paper, section 3.2,
+    "NTK-by-parts"; the MAX page's DFlashKimiK25DraftConfig names the Deepseek-yarn
+    variant through rope_scaling): a pair that turns at least beta_fast times over
+    the original context keeps theta^(-2j/d); a pair that turns at most beta_slow
+    times is divided by factor; pairs in between are blended with a weight linear
+    in the pair index between the first and last pair of the two kinds.
+
+    Hand-derived case (the GQA draft's rope settings: d 128, theta 5e4, factor 32,
+    original context 4096, beta_fast 32, beta_slow 1).  Pair j turns
+    r_j = 4096 * 5e4^(-j/64) / (2 pi) times, so r_j = beta at
+    j = 128 ln(4096 / (2 pi beta)) / (2 ln 5e4):
+      beta 32: ln(20.37183) = 3.014153 -> j = 128 * 3.014153 / 21.639557 = 17.829
+      beta 1:  ln(651.8986) = 6.479889 -> j = 128 * 6.479889 / 21.639557 = 38.329
+    Pair 17 turns 36.81 times (kept), pair 18 31.09 (on the ramp), pair 38 1.057
+    (on the ramp), pair 39 0.893 (divided).  The ramp runs from pair 17 (weight 0)
+    to pair 39 (weight 1) in steps of 1/22, so pair 20 is e (1 - 3/22) + e/32 * 3/22
+    = e * 611/704 and pair 30 is e (1 - 13/22) + e/32 * 13/22 = e * 301/704,
+    e = 5e4^(-j/64)."""
+    d, th, fac, orig = 128, 50000.0, 32.0, 4096
+    inv = oracle.yarn_inv_freq(d, th, fac, orig, 32, 1)
+    e = lambda j: th ** (-j / 64.0)   # noqa: E731
+    assert abs(inv[17] / e(17) - 1.0) < 1e-14 and abs(inv[39] * 32.0 / e(39) - 1.0) < 1e-14
+    assert inv[18] < e(18) * (1.0 - 1e-3) and inv[38] > e(38) / 32.0 * (1.0 + 1e-3)
+    assert abs(inv[18] / (e(18) * (21.0 / 22.0 + 1.0 / 704.0)) - 1.0) < 1e-14
+    assert abs(inv[20] / (e(20) * 611.0 / 704.0) - 1.0) < 1e-14
+    assert abs(inv[30] / (e(30) * 301.0 / 704.0) - 1.0) < 1e-14
+    # the rule itself, over several settings whose boundaries fall between pairs
+    for d, th, fac, orig, bf, bs in ((128, 50000.0, 32.0, 4096, 32, 1), (64, 10000.0, 8.0, 4096, 32, 1),
+                                     (128, 10000.0, 40.0, 4096, 32, 1), (96, 1e6, 4.0, 8192, 16, 2),
+                                     (32, 500.0, 4.0, 256, 8, 1)):
+        inv = oracle.yarn_inv_freq(d, th, fac, orig, bf, bs)
+        ext = th ** (-np.arange(0, d, 2, dtype=np.float64) / d)
+        w = (ext - inv) / (ext - ext / fac)            # blend weight of the divided frequency
+        r = np.array([_rotations(j, d, th, orig) for j in range(d // 2)])
+        assert np.all((np.abs(w) < 1e-12) == (r >= bf)), (d, th, fac, orig)
+        assert np.all((np.abs(w - 1.0) < 1e-12) == (r <= bs)), (d, th, fac, orig)
+        mid = np.nonzero((r < bf) & (r > bs))[0]
+        lo, hi = mid[0] - 1, mid[-1] + 1               # last kept pair, first divided pair
+        np.testing.assert_allclose(w[mid], (mid - lo) / (hi - lo), rtol=1e-12, atol=1e-13)
+    # an independent implementation: transformers' yarn initialiser (fp32)
+    try:
+        import torch
+        from transformers import PretrainedConfig
+        from transformers.modeling_rope_utils import ROPE_INIT_FUNCTIONS
+    except ImportError:
+        return
+    for d, th, fac, orig, bf, bs in ((128, 50000.0, 32.0, 4096, 32, 1), (64, 10000.0, 8.0, 4096, 32, 1),
+                                     (16, 500.0, 4.0, 64, 8, 1)):
+        rp = {"rope_type": "yarn", "rope_theta": th, "factor": fac, "original_max_position_embeddings": orig,
+              "beta_fast": bf, "beta_slow": bs, "mscale": 0.707, "mscale_all_dim": 1.0}
+        cfg = PretrainedConfig(head_dim=d, hidden_size=4 * d, num_attention_heads=4,
+                               max_position_embeddings=int(orig * fac), rope_parameters=rp, rope_theta=th)
+        hf_inv, hf_att = ROPE_INIT_FUNCTIONS["yarn"](cfg, torch.device("cpu"))
+        np.testing.assert_allclose(oracle.yarn_inv_freq(d, th, fac, orig, bf, bs), hf_inv.double().numpy(),
+                                   rtol=1e-6)
+        assert abs(oracle.yarn_mscale(fac, 0.707) / oracle.yarn_mscale(fac, 1.0) - hf_att) < 1e-12
+
+
 def pin_rope_properties():
     """Dimension i pairs with i + d/2; rotation keeps the norm; the product of a
     rotated query and key depends only on their position difference."""
@@ -627,7 +691,7 @@ def pin_materialize_brute_force():
                 assert abs(v[0, h, t, e] - sum(x[j] * c["wv"][h * d + e, j] for j in range(5))) < 1e-12
 
 
-GQA_PINS = [pin_yarn_limits, pin_rope_properties, pin_gqa_matches_torch_sdpa,
+GQA_PINS = [pin_yarn_limits, pin_yarn_ntk_by_parts, pin_rope_properties, pin_gqa_matches_torch_sdpa,
             pin_forward_block_equals_whole_sequence, pin_materialize_brute_force]
 
 BACKWARD_PINS = [pin_backward_finite_differences, pin_backward_matches_torch_autograd,

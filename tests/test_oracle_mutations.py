@@ -240,6 +240,21 @@ def _yarn_betas_swapped(dim, base, factor, orig, beta_fast, beta_slow):
     return _orig_yarn(dim, base, factor, orig, beta_slow, beta_fast)
 
 
+def _correction_dim_no_two_pi(rotations, dim, base, max_pos):
+    return dim * math.log(max_pos / rotations) / (2.0 * math.log(base))
+
+
+def _yarn_floor_ceil_swapped(dim, base, factor, orig, beta_fast, beta_slow):
+    i = np.arange(0, dim, 2, dtype=np.float64)
+    extra = 1.0 / base ** (i / dim)
+    low = max(math.ceil(ogqa._correction_dim(beta_fast, dim, base, orig)), 0)
+    high = min(math.floor(ogqa._correction_dim(beta_slow, dim, base, orig)), dim - 1)
+    if low == high:
+        high += 0.001
+    w = np.clip((np.arange(dim // 2, dtype=np.float64) - low) / (high - low), 0.0, 1.0)
+    return extra * (1.0 - w) + extra / factor * w
+
+
 def _fb_zero(blk_hidden, w_q, w_k, w_v, gamma_q, gamma_k, eps, Hq, Hkv, k_ctx, v_ctx, ctx_len, inv_freq, mscale):
     x = f64(blk_hidden)
     B, bs, _ = x.shape
@@ -308,6 +323,9 @@ MUTANTS = {
     "rope_sign": [(ogqa, "rope", _rope_sign), (oracle, "rope", _rope_sign)],
     "gqa_head_modulo": [(ogqa, "gqa_attention", _gqa_head_modulo), (oracle, "gqa_attention", _gqa_head_modulo)],
     "yarn_betas_swapped": [(ogqa, "yarn_inv_freq", _yarn_betas_swapped), (oracle, "yarn_inv_freq", _yarn_betas_swapped)],
+    "yarn_no_two_pi": [(ogqa, "_correction_dim", _correction_dim_no_two_pi)],
+    "yarn_floor_ceil_swapped": [(ogqa, "yarn_inv_freq", _yarn_floor_ceil_swapped),
+                                (oracle, "yarn_inv_freq", _yarn_floor_ceil_swapped)],
     "block_positions_from_zero": [(oracle, "forward_block", _fb_zero)],
     "qk_norm_after_rope": [(oracle, "materialize", _materialize_norm_after_rope)],
 }
