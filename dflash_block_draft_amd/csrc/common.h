@@ -4,18 +4,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "dims.h"
+
 namespace dflash {
 
-// Head dimensions the kernels are specialised for (Kimi K3 MLA: qk_nope 128,
-// head-shared qk_rope 64, v 128; DSpark page, KimiK3DSparkAttention attributes).
-constexpr int kDn = 128;
-constexpr int kDr = 64;
-constexpr int kDqk = kDn + kDr;
-constexpr int kDv = 128;
-
-// Attention tile (queries x keys).  Must match DFLASH_TILE_M / DFLASH_TILE_N.
-constexpr int kTileM = 128;
-constexpr int kTileN = 64;
 
 constexpr float kLog2e = 1.4426950408889634f;
 

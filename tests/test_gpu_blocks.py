@@ -106,9 +106,8 @@ def test_block_attention_small(dev, case):
 
 @pytest.mark.parametrize("idx,bs", [(2, None), (3, 8), (3, 32), (4, None)])
 def test_block_attention_workloads(dev, idx, bs):
-    """The bf16 workloads at full size: bitwise equal to the dense-mask call; the
-    oracle checks sampled rows of the mid-size ones (the dense path's own
-    parity covers the rest)."""
+    """The bf16 workloads at full size: bitwise equal to the dense-mask call,
+    whose whole output the parity tests compare with the oracle."""
     wl = W.config(idx, bs)
     say(f"{wl.name}: block structure vs dense mask")
     q, kn, kr, v, m = (t.to(dev) for t in (wl.q, wl.k_nope, wl.k_rope, wl.v, wl.mask))
@@ -118,13 +117,6 @@ def test_block_attention_workloads(dev, idx, bs):
     dense = mla.mla_attn(q, kn, kr, v, m, wl.scale)
     torch.cuda.synchronize()
     assert torch.equal(out, dense)
-    if idx == 3:
-        rows = np.array(sorted({0, 127, 128, wl.Lq // 2 + 3, wl.Lq - 1}))
-        ref = oracle.mla_attention(wl.q, wl.k_nope, wl.k_rope, wl.v, wl.mask, wl.scale, q_rows=rows)
-        got = out[:, :, torch.as_tensor(rows, device=dev)]
-        d = np.abs(got.to("cpu", torch.float64).numpy() - ref)
-        say(f"  sampled max|err|={d.max():.3e} mean|err|={d.mean():.3e}")
-        assert d.max() <= TOL_BF16_MAX and d.mean() <= TOL_BF16_MEAN
 
 
 def test_block_reuse_tile_map(dev):

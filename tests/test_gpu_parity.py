@@ -2,9 +2,9 @@
 
 Tolerances (absolute, on the output): fp32 inputs max|err| <= 1e-5; bf16
 inputs max|err| <= 1.5e-2 and mean|err| <= 1e-3.  The oracle always runs on
-exactly the values the GPU consumed (bf16/f32 upcast to fp64).  Full-size
-workloads are checked on sampled query rows (every q-tile's first and last
-row plus random rows, all heads), which the oracle computes one by one.
+exactly the values the GPU consumed (bf16/f32 upcast to fp64).  Every
+workload is compared over its whole output (all of B*H*Lq*Dv); the longest
+one in four groups of heads, so each oracle call takes seconds.
 """
 import sys
 
@@ -52,15 +52,6 @@ def _check(out_gpu, ref, dtype, what):
         assert mx <= TOL_BF16_MAX and mean <= TOL_BF16_MEAN, what
 
 
-def _sample_rows(Lq, seed, extra=24):
-    rng = np.random.default_rng(seed)
-    rows = set([0, Lq - 1])
-    for qt in range(0, Lq, mla.TILE_M):
-        rows.update([qt, min(qt + mla.TILE_M - 1, Lq - 1)])
-    rows.update(rng.integers(0, Lq, size=extra).tolist())
-    return np.array(sorted(rows))
-
-
 def _attn_case(dev, wl, rows=None, **kw):
     say(f"{wl.name}: B={wl.B} H={wl.H} Lq={wl.Lq} Lk={wl.Lk} dtype={wl.dtype} mask={wl.mask_dtype}")
     q, kn, kr, v, m = _to(dev, wl.q, wl.k_nope, wl.k_rope, wl.v, wl.mask)
@@ -100,20 +91,33 @@ def test_config1_expand_then_attention(dev):
     _check(out, ref_e2e, "bf16", "config1 end-to-end (fp64 expand)")
 
 
-def test_config2_sampled(dev):
-    wl = W.config(2)
-    _attn_case(dev, wl, rows=_sample_rows(wl.Lq, 2))
+def test_config2_whole(dev):
+    _attn_case(dev, W.config(2))
 
 
 @pytest.mark.parametrize("bs", [8, 32])
-def test_config3_sampled(dev, bs):
-    wl = W.config(3, block_size=bs)
-    _attn_case(dev, wl, rows=_sample_rows(wl.Lq, 3))
+def test_config3_whole(dev, bs):
+    _attn_case(dev, W.config(3, block_size=bs))
 
 
-def test_config4_sampled(dev):
+@pytest.fixture(scope="module")
+def config4_out(dev):
     wl = W.config(4)
-    _attn_case(dev, wl, rows=_sample_rows(wl.Lq, 4, extra=16))
+    say(f"{wl.name}: B={wl.B} H={wl.H} Lq={wl.Lq} Lk={wl.Lk}")
+    q, kn, kr, v, m = _to(dev, wl.q, wl.k_nope, wl.k_rope, wl.v, wl.mask)
+    out = mla.mla_attn(q, kn, kr, v, m, wl.scale)
+    torch.cuda.synchronize()
+    return wl, out.cpu()
+
+
+@pytest.mark.parametrize("group", range(4))
+def test_config4_whole(config4_out, group):
+    """All rows of heads 8g .. 8g+7; the four groups together are the whole output
+    (each group's mean bound implies the bound on the mean of all four)."""
+    wl, out = config4_out
+    hs = slice(8 * group, 8 * group + 8)
+    ref = oracle.mla_attention(wl.q[:, hs], wl.k_nope[:, hs], wl.k_rope, wl.v[:, hs], wl.mask, wl.scale)
+    _check(out[:, hs], ref, wl.dtype, f"{wl.name} heads {hs.start}-{hs.stop - 1}")
 
 
 # ------------------------------------------------------------- ragged and edge cases
@@ -151,15 +155,9 @@ def test_no_mask_equals_zero_mask_and_oracle(dev):
 
 
 def test_general_additive_mask(dev):
-    """Finite non-zero mask values (class-2 tiles everywhere) plus -inf holes.
-
+    """Finite non-zero mask values (general tiles everywhere) plus -inf holes.
     Mask values ~ N(0, 3^2) make the softmax far peakier than the DFlash
-    workloads, so the fixed 1.5e-2 bound is replaced by one derived from the
-    arithmetic: rounding each probability to bf16 perturbs a weight by at most
-    2^-9 of itself, moving the output by at most 2^-9 * sum_j p_j |v_j - out|
-    <= 2^-9 * 2 max|v|, and the bf16 output adds 2^-9 |out|.  Bound: 2^-9 *
-    (max|out| + 2 max|v|) * 1.25 (the factor covers fp32 accumulation); the mean
-    bound stays 1e-3."""
+    workloads; the bf16 bounds still hold."""
     B, H, Lq, Lk = 2, 2, 160, 300
     q, kn, kr, v = W.random_attention_inputs(15, B, H, Lq, Lk, dtype="bf16")
     rng = np.random.default_rng(15)
@@ -172,11 +170,7 @@ def test_general_additive_mask(dev):
         out = mla.mla_attn(qd, knd, krd, vd, md)
         torch.cuda.synchronize()
         ref = oracle.mla_attention(q, kn, kr, v, mask, 192 ** -0.5)
-        mx, mean = _err(out, ref)
-        vmax = float(v.float().abs().max())
-        bound = 2.0 ** -9 * (float(np.abs(ref).max()) + 2.0 * vmax) * 1.25
-        say(f"general mask {mdt}: max|err|={mx:.3e} (derived bound {bound:.3e}) mean|err|={mean:.3e}")
-        assert mx <= bound and mean <= TOL_BF16_MEAN
+        _check(out, ref, "bf16", f"general mask {mdt}")
 
 
 def test_fully_masked_rows_and_huge_negatives(dev):

@@ -3,9 +3,9 @@
 A split run is the pages' softmax regrouped: each run normalises its own keys
 and the runs are merged with weights exp(lse_run - lse) in a fixed order.  The
 tolerances are those of the unsplit bf16 path (max 1.5e-2, mean 1e-3 on out;
-4e-3 on lse, from the bf16 rounding of the probabilities); split and unsplit
-outputs are also compared with each other (they round the probabilities relative
-to different stabilisers).
+5e-4 on lse, which sums fp32 probabilities); split and unsplit outputs are also
+compared with each other (they round the probabilities relative to different
+stabilisers).
 """
 import sys
 
@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 TOL_BF16_MAX = 1.5e-2
 TOL_BF16_MEAN = 1e-3
-LSE_TOL = 4e-3
+LSE_TOL = 5e-4
 
 
 def say(msg):
