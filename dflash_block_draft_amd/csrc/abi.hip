@@ -1032,7 +1032,7 @@ dflash_status dflash_gqa_forward_block(const void* blk_hidden, const void* w_q, 
     return fail(DFLASH_ERR_INVALID_ARG, "eps must be >= 0 and scale > 0, both finite");
   if (bs > Lmax) return fail(DFLASH_ERR_INVALID_ARG, "the block is longer than the cache");
   if (head_dim != 128 || hidden % 32 != 0 || Lmax % 8 != 0 || Hq % Hkv != 0 || (Hq / Hkv) * bs > 64)
-    return fail(DFLASH_ERR_UNSUPPORTED, "head_dim 128, hidden % 32, Lmax % 8, Hq % Hkv and (Hq / Hkv) * bs <= 64 required");
+    return fail(DFLASH_ERR_UNSUPPORTED, "head_dim 128, hidden %% 32 == 0, Lmax %% 8 == 0, Hq %% Hkv == 0 and (Hq / Hkv) * bs <= 64 required");
   if (Lmax * 128 * 2 > INT32_MAX)   // one (batch row, KV head) slice of the cache is read through a 32-bit buffer range
     return fail(DFLASH_ERR_UNSUPPORTED, "Lmax must be below 2^23 keys");
   size_t qo, oo, mlo, need;

@@ -48,7 +48,11 @@
 //    within fp32 range and the bf16 P operand accurate, so a step whose scores
 //    exceed m by more than 20 ln 2 (p > 2^20) marks the workgroup, and a
 //    marked workgroup runs again in two passes: the exact row maxima first,
-//    then the accumulation with those maxima as stabilisers.
+//    then the accumulation with those maxima as stabilisers.  The row sum l adds
+//    the bf16-rounded probabilities PV applies, so out = sum p v / sum p with the
+//    same weights on both sides: the stabiliser is no row maximum, so no weight
+//    is exactly 1, and a rounding of the dominant weight would otherwise show in
+//    full in a peaked row.
 #include "common.h"
 #include "dma.h"
 #include "launch.h"
@@ -128,6 +132,13 @@ template <bool MASK_BF16>
 __device__ __forceinline__ float load_mask(const void* mask, size_t idx) {
   if (MASK_BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(mask)[idx]);
   return static_cast<const float*>(mask)[idx];
+}
+
+// acc + the two bf16 values of a packed pair (a dot product with (1, 1))
+__device__ __forceinline__ float sum_bf16x2(uint32_t pair, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair), __builtin_bit_cast(bf16x2_t, 0x3F803F80u),
+                                         acc, false);
 }
 
 // f(IC<0>{}), ..., f(IC<N-1>{}) in order
@@ -368,7 +379,8 @@ attn_fwd_bf16(AttnBf16Args a) {
     }
   };
 
-  // p = exp2(fma(x, ca, cb)) -> pk (bf16 pairs); returns the lane's sum of p
+  // p = exp2(fma(x, ca, cb)) -> pk (bf16 pairs); returns the lane's sum of the
+  // bf16-rounded p, the weights PV applies
   auto probs = [&](uint32_t* pk, const float* x, float ca, float cb) __attribute__((always_inline)) -> float {
     float p[16];
 #pragma unroll
@@ -377,9 +389,9 @@ attn_fwd_bf16(AttnBf16Args a) {
     for (int u = 0; u < 8; ++u) pk[u] = pack_bf16x2(p[2 * u], p[2 * u + 1]);
     float l0 = 0.f, l1 = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      l0 += p[r];
-      l1 += p[r + 1];
+    for (int u = 0; u < 8; u += 2) {
+      l0 = sum_bf16x2(pk[u], l0);
+      l1 = sum_bf16x2(pk[u + 1], l1);
     }
     return l0 + l1;
   };
@@ -439,8 +451,9 @@ attn_fwd_bf16(AttnBf16Args a) {
   // the current step into o[MS] with the V operands vf and P^T pk[MS], each V
   // register refilled from slot vsl after its MFMA with RELOAD) and, from slot 2
   // on, one unit of the fast softmax of stream VS = 1 - MS on s[VS],
-  // software-pipelined over its 16 scores (exponential of score u, sum and bf16
-  // pair of score u-1).  Starting the softmax two MFMA
+  // software-pipelined over its 16 scores (exponential of score u, the bf16
+  // pair of scores u-2 and u-1, the sum of the pair packed before it: the row
+  // sum adds the rounded values PV applies).  Starting the softmax two MFMA
   // issues into the phase keeps the other stream's last score MFMA of the
   // previous phase at a safe distance from its readers.  Returns the lane's sum.
   auto phase_fast = [&](auto MSc, auto RELOAD, auto EXTRA, int ks, int vsl) __attribute__((always_inline)) -> float {
@@ -476,12 +489,13 @@ attn_fwd_bf16(AttnBf16Args a) {
       if constexpr (u >= 1 && u <= 16) {
         constexpr int w = u - 1;
         if constexpr (w & 1) {
-          l1 += p[w];
           pk[vs][w >> 1] = pack_bf16x2(p[w - 1], p[w]);
-        } else {
-          l0 += p[w];
+        } else if constexpr (w >= 2) {
+          if constexpr (w & 2) l1 = sum_bf16x2(pk[vs][(w >> 1) - 1], l1);
+          else l0 = sum_bf16x2(pk[vs][(w >> 1) - 1], l0);
         }
       }
+      if constexpr (k == 19) l1 = sum_bf16x2(pk[vs][7], l1);
       __builtin_amdgcn_sched_barrier(0);
     });
     s[ms] = acc;

@@ -3,9 +3,9 @@
 A split run is the pages' softmax regrouped: each run normalises its own keys
 and the runs are merged with weights exp(lse_run - lse) in a fixed order.  The
 tolerances are those of the unsplit bf16 path (max 1.5e-2, mean 1e-3 on out;
-5e-4 on lse, which sums fp32 probabilities); split and unsplit outputs are also
-compared with each other (they round the probabilities relative to different
-stabilisers).
+4e-3 on lse, from the bf16 rounding of the probabilities it sums); split and
+unsplit outputs are also compared with each other (they round the
+probabilities relative to different stabilisers).
 """
 import sys
 
@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 TOL_BF16_MAX = 1.5e-2
 TOL_BF16_MEAN = 1e-3
-LSE_TOL = 5e-4
+LSE_TOL = 4e-3
 
 
 def say(msg):
@@ -90,7 +90,12 @@ def test_split_forward_and_lse(dev, case):
     torch.cuda.synchronize()
     assert torch.equal(out, blk)                 # the block-structure map splits the same way
     _split_vs_unsplit(out, out1)
-    assert torch.allclose(lse, lse1, rtol=1e-5, atol=1e-5)
+    # each lse sums probabilities rounded to bf16 (relative error <= 2^-9 each, all
+    # terms positive: the sum and so exp(lse) within 2^-9), relative to different
+    # stabilisers in the two calls: they differ by at most about 2 * 2^-9
+    dl = (lse - lse1).abs().max().item()
+    say(f"  lse split vs unsplit: max|diff|={dl:.2e}")
+    assert dl <= 4e-3
     _check_out(out, oracle.mla_attention(q, kn, kr, v, mask, 192 ** -0.5), "split out vs oracle")
     want = oracle.logsumexp_rows(q, kn, kr, mask, 192 ** -0.5)
     lerr = np.abs(lse.cpu().double().numpy() - want).max()
