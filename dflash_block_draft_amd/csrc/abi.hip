@@ -1,12 +1,14 @@
 // C ABI of the library (declared in include/dflash_mla.h): argument checks,
-// workspace layout and kernel dispatch.  Nothing here allocates device memory
-// or keeps state; every launch goes on the caller's stream.
+// workspace layout and kernel dispatch.  Nothing here allocates device memory;
+// every launch goes on the caller's stream.  The only state is the static
+// scratch array of dflash_mla_attn_no_alloc and its per-device addresses.
 #include <cmath>
 #include <algorithm>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/dflash_mla.h"
@@ -546,6 +548,79 @@ dflash_status dflash_mla_attn_lse(const void* q, const void* k_nope, const void*
   if (!lse) return fail(DFLASH_ERR_INVALID_ARG, "lse is NULL");
   return attn_impl(q, k_nope, k_rope_shared, v, additive_mask, out, lse, B, H, Lq, Lk, Dn, Dr, Dv, scale, dt,
                    mask_dt, workspace, workspace_bytes, flags, stream);
+}
+
+}  // extern "C"
+
+// Scratch of dflash_mla_attn_no_alloc: the tile map of a masked bf16 call lives
+// here instead of in a caller's workspace.  Every GPU the library runs on holds
+// its own copy until the process ends; calls on one GPU share it.  In host code
+// `scratch` is only a stand-in for the device array: its address on each device
+// comes from hipGetSymbolAddress (once per device, with that device current), and
+// only that address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[DFLASH_NO_ALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxScratchDevices] = {};
+
+// the current device's address of `scratch`
+dflash_status scratch_address(void** addr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(DFLASH_ERR_UNSUPPORTED, "device %d: the no-alloc scratch serves devices 0..%d", dev,
+                kMaxScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress of the no-alloc scratch");
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255u) != 0)
+      return fail(DFLASH_ERR_HIP, "the no-alloc scratch has no 256-byte aligned device address");
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dflash_status dflash_mla_attn_no_alloc(const void* q, const void* k_nope, const void* k_rope_shared,
+                                       const void* v, const void* additive_mask, void* out, int64_t B,
+                                       int64_t H, int64_t Lq, int64_t Lk, int64_t Dn, int64_t Dr,
+                                       int64_t Dv, float scale, dflash_dtype dt, dflash_dtype mask_dt,
+                                       uint32_t flags, void* stream) {
+  if (flags & ~(DFLASH_ATTN_NO_TILE_SKIP | DFLASH_ATTN_CHECK_ONLY))
+    return fail(DFLASH_ERR_INVALID_ARG, "dflash_mla_attn_no_alloc takes only NO_TILE_SKIP and CHECK_ONLY "
+                "(got flags 0x%x): its scratch holds no map to reuse and no room for split partials", flags);
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (dt == DFLASH_BF16 && additive_mask) {
+    const size_t need = dflash_mla_attn_workspace_bytes(B, Lq, Lk);
+    if (need == 0)
+      return fail(DFLASH_ERR_INVALID_ARG, "B, Lq, Lk must be positive (got %lld, %lld, %lld)", (long long)B,
+                  (long long)Lq, (long long)Lk);
+    if (need > DFLASH_NO_ALLOC_SCRATCH_BYTES)
+      return fail(DFLASH_ERR_UNSUPPORTED, "the tile map of B=%lld, Lq=%lld, Lk=%lld needs %zu bytes; the no-alloc "
+                  "scratch holds %zu (use dflash_mla_attn with a workspace)", (long long)B, (long long)Lq,
+                  (long long)Lk, need, static_cast<size_t>(DFLASH_NO_ALLOC_SCRATCH_BYTES));
+    ws_bytes = DFLASH_NO_ALLOC_SCRATCH_BYTES;
+    if (flags & DFLASH_ATTN_CHECK_ONLY) {
+      // validation only, nothing launched: a stand-in address above every allocation
+      ws = reinterpret_cast<void*>(uintptr_t(1) << 62);
+    } else {
+      const dflash_status st = scratch_address(&ws);
+      if (st != DFLASH_OK) return st;
+    }
+  }
+  return attn_impl(q, k_nope, k_rope_shared, v, additive_mask, out, nullptr, B, H, Lq, Lk, Dn, Dr, Dv, scale, dt,
+                   mask_dt, ws, ws_bytes, flags, stream);
 }
 
 size_t dflash_mla_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Lq, int64_t Lk) {

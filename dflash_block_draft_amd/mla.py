@@ -34,7 +34,7 @@ EXPORTED = (
     "dflash_mla_attn_blocks", "dflash_mla_attn_lse", "dflash_mla_attn_bwd_workspace_bytes",
     "dflash_mla_attn_bwd", "dflash_mla_projection_workspace_bytes", "dflash_mla_context_project",
     "dflash_mla_q_project", "dflash_mla_kv_project", "dflash_gqa_materialize", "dflash_gqa_workspace_bytes",
-    "dflash_gqa_forward_block", "dflash_mla_attn_split_workspace_bytes",
+    "dflash_gqa_forward_block", "dflash_mla_attn_split_workspace_bytes", "dflash_mla_attn_no_alloc",
 )
 
 
@@ -82,6 +82,9 @@ def load_library() -> ctypes.CDLL:
     lib.dflash_mla_attn_lse.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32,
                                         i32, i32, vp, sz, u32, vp]
     lib.dflash_mla_attn_lse.restype = i32
+    lib.dflash_mla_attn_no_alloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f32,
+                                             i32, i32, u32, vp]
+    lib.dflash_mla_attn_no_alloc.restype = i32
     lib.dflash_mla_attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
     lib.dflash_mla_attn_bwd_workspace_bytes.restype = sz
     lib.dflash_mla_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
@@ -289,6 +292,35 @@ def mla_attn(q: torch.Tensor, k_nope: torch.Tensor, k_rope: torch.Tensor, v: tor
         _check(lib.dflash_mla_attn_lse(_ptr(q), _ptr(k_nope), _ptr(k_rope), _ptr(v), _ptr(mask), _ptr(out),
                                        _ptr(lse), B, H, Lq, Lk, Dn, Dr, Dv, float(scale), _DT[dt], mask_dt,
                                        _ptr(workspace), wsb, flags, _stream(q)))
+    return out
+
+
+def mla_attn_no_alloc(q: torch.Tensor, k_nope: torch.Tensor, k_rope: torch.Tensor, v: torch.Tensor,
+                      mask: Optional[torch.Tensor] = None, scale: Optional[float] = None, *,
+                      out: torch.Tensor, tile_skip: bool = True) -> torch.Tensor:
+    """dflash_mla_attn_no_alloc: mla_attn without a workspace (the tile map goes to the
+    library's static per-GPU scratch).  `out` must be given: nothing is allocated here
+    either."""
+    lib = load_library()
+    _dev(q, "q", ndim=4)
+    dt = q.dtype
+    _dev(k_nope, "k_nope", dtype=dt, ndim=4)
+    _dev(k_rope, "k_rope", dtype=dt, ndim=3)
+    _dev(v, "v", dtype=dt, ndim=4)
+    _dev(out, "out", dtype=dt, ndim=4)
+    B, H, Lq, _ = q.shape
+    Lk, Dn = k_nope.shape[2], k_nope.shape[3]
+    Dr, Dv = k_rope.shape[2], v.shape[3]
+    if scale is None:
+        scale = float(Dn + Dr) ** -0.5
+    mask_dt = _F32
+    if mask is not None:
+        _dev(mask, "mask", ndim=4)
+        mask_dt = _DT[mask.dtype]
+    flags = 0 if tile_skip else FLAG_NO_TILE_SKIP
+    _check(lib.dflash_mla_attn_no_alloc(_ptr(q), _ptr(k_nope), _ptr(k_rope), _ptr(v), _ptr(mask), _ptr(out),
+                                        B, H, Lq, Lk, Dn, Dr, Dv, float(scale), _DT[dt], mask_dt, flags,
+                                        _stream(q)))
     return out
 
 

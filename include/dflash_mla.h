@@ -242,6 +242,30 @@ dflash_status dflash_mla_attn_lse(const void* q, const void* k_nope, const void*
                                   void* stream);
 
 /*
+ * dflash_mla_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation with no workspace argument.  The tile map of a masked
+ * BF16 call goes to a static device array of DFLASH_NO_ALLOC_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on until the process ends; the
+ * call allocates nothing.  Shapes whose map needs more
+ * (dflash_mla_attn_workspace_bytes(B, Lq, Lk) > DFLASH_NO_ALLOC_SCRATCH_BYTES,
+ * e.g. B * ceil(Lq/128) * ceil(Lk/64) beyond about 31,000 tiles) return
+ * UNSUPPORTED.  flags: only DFLASH_ATTN_NO_TILE_SKIP and DFLASH_ATTN_CHECK_ONLY
+ * (REUSE_TILE_MAP and SPLIT_KEYS return INVALID_ARG).  The current device must be
+ * the stream's.  Every call on one GPU uses the same scratch and leaves its map
+ * there: calls that overlap on one GPU (different streams, or threads) race and
+ * must be serialised by the caller; calls in order on one stream are safe.
+ * Other arguments, limits and errors as dflash_mla_attn.
+ */
+#define DFLASH_NO_ALLOC_SCRATCH_BYTES (32u << 20)
+dflash_status dflash_mla_attn_no_alloc(const void* q, const void* k_nope, const void* k_rope_shared,
+                                       const void* v, const void* additive_mask, void* out,
+                                       int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                                       int64_t Dn, int64_t Dr, int64_t Dv, float scale,
+                                       dflash_dtype dt, dflash_dtype mask_dt,
+                                       uint32_t flags, void* stream);
+
+/*
  * Bytes of device workspace dflash_mla_attn_bwd needs (0 for invalid sizes).  It
  * begins with the forward's tile map in the dflash_mla_tile_map_layout layout,
  * so one workspace of this size serves the forward (dflash_mla_attn_lse) and then

@@ -347,3 +347,23 @@ def test_split_keys_validation(lib):
     assert _attn(lib, flags=0xC, dt=0, **big) == 0                         # f32 ignores the split
     assert _attn(lib, flags=0xE, **big) == 0                               # ignored with NO_TILE_SKIP (no mask)
     assert _attn(lib, flags=0xC, ws=None, wsb=0) == 0                      # a shape that does not split
+
+
+def test_no_alloc_validation(lib):
+    f = lib.dflash_mla_attn_no_alloc
+    base = (FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 100, FAKE * 5, 1, 2, 32, 96, 128, 64, 128, 192 ** -0.5, 1, 1)
+    assert f(*base, 0x4, None) == 0                         # valid (check only: nothing launched)
+    assert f(*base, 0x1, None) == 1                         # REUSE_TILE_MAP: the scratch holds no map to reuse
+    assert f(*base, 0x8, None) == 1                         # SPLIT_KEYS: no room for partials
+    assert f(*base[:6], 0, 2, 32, 96, *base[10:], 0x4, None) == 1     # B = 0
+    big = (1 << 44, 2 << 44, 3 << 44, 4 << 44, 5 << 44, 6 << 44)
+    # a tile map past the static scratch: UNSUPPORTED
+    assert mla_ws(lib, 1, 128 * 64, 64 * 600) > 32 << 20
+    assert f(*big, 1, 1, 128 * 64, 64 * 600, 128, 64, 128, 0.07, 1, 1, 0x4, None) == 2
+    assert b"scratch" in lib.dflash_last_error()
+    # the largest map that fits is accepted
+    assert f(*big, 1, 1, 128 * 32, 64 * 576, 128, 64, 128, 0.07, 1, 1, 0x4, None) == 0
+
+
+def mla_ws(lib, B, Lq, Lk):
+    return lib.dflash_mla_attn_workspace_bytes(B, Lq, Lk)
