@@ -50,8 +50,8 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(hipcc: str, src: str, extra) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(hipcc: str, src: str, extra, build_dir: str = BUILD) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     cmd = [hipcc, *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature"
@@ -78,6 +78,46 @@ def build(verbose: bool = True, extra_flags=()) -> str:
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources")
     return LIB
+
+
+# Host-side sanitizer build of the C ABI layer (argument checks, layouts,
+# dispatch): abi.hip's host code is compiled with AddressSanitizer and
+# UndefinedBehaviorSanitizer (device code untouched: each -fsanitize applies to
+# the host pass only), the other objects come from the regular build.  Loading
+# it needs the ASan runtime preloaded (san_runtime()).
+SAN_BUILD = os.path.join(HERE, "_build_san")
+SAN_LIB = os.path.join(SAN_BUILD, "libdflash_mla_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-g"]
+
+
+def san_runtime() -> str:
+    """The clang AddressSanitizer runtime matching hipcc's compiler."""
+    root = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(_hipcc()))), "llvm", "lib", "clang")
+    for ver in sorted(os.listdir(root), reverse=True):
+        p = os.path.join(root, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(p):
+            return p
+    raise RuntimeError("the clang ASan runtime is not installed")
+
+
+def build_sanitized(verbose: bool = True) -> str:
+    hipcc = _hipcc()
+    if not os.path.exists(LIB):
+        build(verbose=verbose)
+    os.makedirs(SAN_BUILD, exist_ok=True)
+    abi = os.path.join(CSRC, "abi.hip")
+    san_obj = _compile(hipcc, abi, SAN_FLAGS, SAN_BUILD)
+    objs = [san_obj] + [os.path.join(BUILD, os.path.basename(s) + ".o") for s in sources() if s != abi]
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-shared-libasan",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", *objs, "-o", SAN_LIB]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {SAN_LIB} (host ASan + UBSan on abi.hip)")
+    return SAN_LIB
 
 
 if __name__ == "__main__":

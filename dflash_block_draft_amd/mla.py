@@ -14,7 +14,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdflash_mla.so")
+# the in-tree build; DFLASH_MLA_LIB selects another build of the same library
+# (e.g. the host-sanitized one the ABI tests run under)
+LIB_PATH = os.environ.get("DFLASH_MLA_LIB") or os.path.join(_HERE, "libdflash_mla.so")
 
 TILE_M = 128
 TILE_N = 64

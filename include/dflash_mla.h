@@ -40,7 +40,16 @@
 extern "C" {
 #endif
 
-typedef enum dflash_status {
+/* The enums are int-sized in C and C++ alike.  C++ code sees them with a fixed
+ * underlying type int, so any int a C caller passes (e.g. an unknown dtype the
+ * library must reject) is a valid value there too, not undefined behaviour. */
+#ifdef __cplusplus
+#define DFLASH_ENUM_BASE : int
+#else
+#define DFLASH_ENUM_BASE
+#endif
+
+typedef enum dflash_status DFLASH_ENUM_BASE {
   DFLASH_OK = 0,
   DFLASH_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, non-positive size, bad scale, aliasing, bad flags */
   DFLASH_ERR_UNSUPPORTED = 2,  /* head dims or dtype combination the library does not implement */
@@ -48,7 +57,7 @@ typedef enum dflash_status {
   DFLASH_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
 } dflash_status;
 
-typedef enum dflash_dtype {
+typedef enum dflash_dtype DFLASH_ENUM_BASE {
   DFLASH_F32 = 0,
   DFLASH_BF16 = 1
 } dflash_dtype;
