@@ -10,8 +10,8 @@
 // Decomposition (one workgroup = one (batch, head, 128-query tile), two waves,
 // two workgroups per CU so every SIMD holds exactly one wave):
 //  * Wave w owns queries 64w .. 64w+63 of the tile as two streams of 32
-//    (stream i: queries 64w + 32i + lane%32).  Each V operand read from LDS
-//    feeds one PV MFMA of each stream.
+//    (stream i: queries 64w + 32i + lane%32).  Each K and V operand read from
+//    LDS feeds one MFMA of each stream.
 //  * The key loop walks the tile list in steps of 32 keys (half a 64-key tile),
 //    each in two phases of 20 MFMAs with one workgroup barrier per step:
 //      phase A: score MFMAs of stream 0 for the next step, PV of stream 0
@@ -39,8 +39,10 @@
 //    3 (V) and 3 (words) slots; the copies of a step are spread over the MFMA
 //    slots of its two phases.  LDS tiles are 16-row x 64 B blocks with
 //    XOR-swizzled K chunks: conflict-free 16-byte operand reads.
-//  * Q (2 x 32 x 192 bf16) stays in registers for the whole loop; K operands
-//    are read two MFMAs ahead of their use.
+//  * Q (2 x 32 x 192 bf16) stays in accumulator registers for the whole loop.
+//    The K operands of a step (32 keys x 192) sit in vector registers: read
+//    once from LDS, a whole phase before their first use, they serve the score
+//    MFMAs of both streams.
 //  * Online softmax in fp32 with the hardware exp2 and a stabiliser m fixed at
 //    the first visible step of each row: later steps form exp(s - m) without
 //    rescaling O.  Any stabiliser gives the same result in exact arithmetic
@@ -48,11 +50,13 @@
 //    within fp32 range and the bf16 P operand accurate, so a step whose scores
 //    exceed m by more than 20 ln 2 (p > 2^20) marks the workgroup, and a
 //    marked workgroup runs again in two passes: the exact row maxima first,
-//    then the accumulation with those maxima as stabilisers.  The row sum l adds
-//    the bf16-rounded probabilities PV applies, so out = sum p v / sum p with the
-//    same weights on both sides: the stabiliser is no row maximum, so no weight
-//    is exactly 1, and a rounding of the dominant weight would otherwise show in
-//    full in a peaked row.
+//    then the accumulation with those maxima as stabilisers.  The row sum l
+//    adds the fp32 probabilities on the fast path and, on the exact path
+//    (general mask values, where peaked rows come from), the bf16-rounded
+//    values PV applies: the stabiliser is no row maximum, so no weight is
+//    exactly 1, and there the rounding of a dominant weight would otherwise
+//    show in full.  (Summing rounded values costs a dot2 per pair, which waits
+//    on the matrix core: 5% of the loop on the fast path.)
 #include "common.h"
 #include "dma.h"
 #include "launch.h"
@@ -75,7 +79,6 @@ constexpr int kKRing = 0;
 constexpr int kVRing = kKRing + kNK * kKSlot;
 constexpr int kBitsRing = kVRing + kNV * kVSlot;
 constexpr int kLdsBytes = kBitsRing + kNB * kBitsSlot;
-constexpr int kPK = 2;                               // K chunks of a phase read before its first MFMA
 // MFMA order of a phase: score chunks c (0-11, one dependent chain) and PV
 // operations 100 + v (v = 4*st + j: four independent accumulators), placed so
 // that only three score MFMAs directly follow their predecessor in the chain and
@@ -141,6 +144,13 @@ __device__ __forceinline__ float sum_bf16x2(uint32_t pair, float acc) {
                                          acc, false);
 }
 
+// Workgroup barrier of the key loop.  It publishes the LDS copies each wave has
+// already waited for (wait_vmem); the operand reads a wave has in flight need no
+// wait here (__syncthreads would add one): the slots they read are rewritten
+// only after a later barrier, and their registers are waited for where they are
+// used.  The memory clobber keeps the compiler from moving LDS accesses across.
+__device__ __forceinline__ void step_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // f(IC<0>{}), ..., f(IC<N-1>{}) in order
 template <int... Is, class F>
 __device__ __forceinline__ void static_for_impl(std::integer_sequence<int, Is...>, F&& f) {
@@ -153,23 +163,19 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // One chunk of S^T = K Q^T with the accumulator in vector registers, where the
 // softmax reads it with plain VALU instructions (the accumulators of O stay in
-// accumulator registers, written by the compiler's own MFMAs).  QA: the B
-// operand sits in an accumulator register.  The first chunk adds the bias block
+// accumulator registers, written by the compiler's own MFMAs); the B operand
+// (Q) sits in accumulator registers.  The first chunk adds the bias block
 // that hides the masked keys of a binary tile (0 elsewhere).  Written as asm,
 // the compiler does not know the result arrives one MFMA latency later: every
 // reader of acc is placed at least two MFMA issues later, or behind
 // s_nop_after_mfma.
-template <bool FIRST, bool QA>
-__device__ __forceinline__ void mfma_s(f32x16_t& acc, bf16x8_t k, bf16x8_t q, const f32x16_t& bias) {
+template <bool FIRST>
+__device__ __forceinline__ void mfma_s(f32x16_t& acc, bf16x8_t k, const u32x4_t& q, const f32x16_t& bias) {
   const u32x4_t kk = __builtin_bit_cast(u32x4_t, k);
-  const u32x4_t qq = __builtin_bit_cast(u32x4_t, q);
-  if (FIRST) {   // the chain starts from the hidden-key bias (0 or -inf per key)
-    if (QA) asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(acc) : "v"(kk), "a"(qq), "v"(bias));
-    else asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(acc) : "v"(kk), "v"(qq), "v"(bias));
-  } else {
-    if (QA) asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(kk), "a"(qq));
-    else asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(kk), "v"(qq));
-  }
+  if (FIRST)     // the chain starts from the hidden-key bias (0 or -inf per key)
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(acc) : "v"(kk), "a"(q), "v"(bias));
+  else
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(kk), "a"(q));
 }
 // the MFMA result in acc is readable by the VALU after this (16 wait states)
 __device__ __forceinline__ void s_nop_after_mfma(f32x16_t& acc) {
@@ -274,10 +280,12 @@ attn_fwd_bf16(AttnBf16Args a) {
     constexpr int pc = decltype(P)::value;
     dma16i<pc * 64>(d_v, lds_v + slot * kVSlot + pc * 1024, vo_v + static_cast<uint32_t>(key0) * (kDv * 2));
   };
-  // visibility words of a class-2 tile (1 KiB, copied by wave 0); other tiles read zeros
+  // visibility words of a class-2 tile (1 KiB); other tiles read zeros.  Both
+  // waves copy the same bytes (no branch inside a scheduled phase), and the
+  // copy is repeated in the tile's second step (its slot is not read then).
   auto issue_bits = [&](int slot, int e) __attribute__((always_inline)) {
     const int kt = (e >> 24) == 2 ? (e & 0xFFFFFF) : a.nkt;
-    if (wave == 0) dma16i<0>(d_bits, lds0 + kBitsRing + slot * kBitsSlot, lane * 16 + static_cast<uint32_t>(kt) * kBitsSlot);
+    dma16i<0>(d_bits, lds0 + kBitsRing + slot * kBitsSlot, lane * 16 + static_cast<uint32_t>(kt) * kBitsSlot);
   };
 
   // ---- per-lane LDS read offsets inside a slot
@@ -295,25 +303,26 @@ attn_fwd_bf16(AttnBf16Args a) {
   const lds_char_t* const ko_ptr = lds + kKRing + k_odd;
   const lds_char_t* const v_ptr = lds + kVRing + v_base;
 
-  // ---- Q fragments (B operand of S^T = K Q^T), stream i, 12 chunks of 16 dims.
-  // The q_rope chunks 8-11 are loaded straight into accumulator registers (the
-  // MFMA reads its B operand from either file; each asm load waits for itself):
-  // the vector registers stay free for the operand windows and the softmax.
-  // Rows past Lq read row 0 (their results are never stored).
-  bf16x8_t qf[2][kDqk / 16];
+  // ---- Q fragments (B operand of S^T = K Q^T), stream i, 12 chunks of 16 dims,
+  // kept in accumulator registers for the whole loop (the MFMA reads its B
+  // operand from either file): the vector registers hold the K operands of a
+  // whole step, the V operands and the softmax.  All 24 loads are in flight
+  // together; each chunk then moves to accumulator registers (a tied asm
+  // operand: the compiler emits the moves).  Rows past Lq read row 0 (their
+  // results are never stored).
+  u32x4_t qf[2][kDqk / 16];
+  {
+    u32x4_t qv[2][kDqk / 16];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint16_t* qp = a.q + (bh * a.Lq + (q_ok[i] ? q_row[i] : 0)) * kDqk + 8 * hi;
+    for (int i = 0; i < 2; ++i) {
+      const uint16_t* qp = a.q + (bh * a.Lq + (q_ok[i] ? q_row[i] : 0)) * kDqk + 8 * hi;
 #pragma unroll
-    for (int c = 0; c < kDqk / 16; ++c) {
-      if (c < 8) {
-        qf[i][c] = as_bf16x8(ldg16(qp + 16 * c));
-      } else {
-        u32x4_t x;
-        asm volatile("global_load_dwordx4 %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=a"(x) : "v"(qp + 16 * c) : "memory");
-        qf[i][c] = as_bf16x8(x);
-      }
+      for (int c = 0; c < kDqk / 16; ++c) qv[i][c] = ldg16(qp + 16 * c);
     }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int c = 0; c < kDqk / 16; ++c) asm volatile("" : "=a"(qf[i][c]) : "0"(qv[i][c]));
   }
 
   f32x16_t o[2][4];
@@ -329,7 +338,6 @@ attn_fwd_bf16(AttnBf16Args a) {
   // a binary tile hides and 0 elsewhere (all zero outside binary tiles; bias_nz
   // tells whether it needs clearing)
   f32x16_t bias[2];
-  bool bias_nz[2] = {false, false};
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -337,7 +345,7 @@ attn_fwd_bf16(AttnBf16Args a) {
   bool over = false;                         // a score rose more than kHeadroom above its stabiliser
   f32x16_t s[2];                             // raw scores of each stream's pending softmax step
   uint32_t pk[2][8];                         // P^T of each stream's step awaiting PV, bf16 pairs
-  bf16x8_t kf[kPK];                          // first K operands of the next phase, read ahead
+  bf16x8_t kreg[kDqk / 16];                  // K operands of the next step's scores (both streams)
   s16x8_t vf[8];                             // V^T operands of the step awaiting PV (op = 4*st + j)
 
   const float scale = a.scale;
@@ -362,20 +370,39 @@ attn_fwd_bf16(AttnBf16Args a) {
   // is 1) so each entry compiles to a bit-field extract and an and.
   int one;
   asm("s_mov_b32 %0, 1" : "=s"(one));
-  auto set_bias = [&](auto I, int s, int e) __attribute__((always_inline)) {
+  // The bias of a step is built in pieces so that a phase can spread it over
+  // its MFMA slots: the visibility word (the ring slot of a tile that is not
+  // binary holds zeros and is not used), the hidden-key bits of this lane's 16
+  // keys (none outside binary tiles), then the entries.
+  auto bias_word = [&](auto I, int s) __attribute__((always_inline)) -> uint64_t {
     constexpr int i = decltype(I)::value;
-    if ((e >> 24) == 2) {
-      const int bslot = (s >> 1) % kNB;
-      const uint64_t w64 = *reinterpret_cast<const lds_u64_t*>(lds + kBitsRing + bslot * kBitsSlot + q_local[i] * 8);
-      const int hv = static_cast<int>(~static_cast<uint32_t>(w64 >> (32 * (s & 1) + 4 * hi)));
+    return *reinterpret_cast<const lds_u64_t*>(lds + kBitsRing + ((s >> 1) % kNB) * kBitsSlot + q_local[i] * 8);
+  };
+  auto bias_hidden = [&](int s, int e, uint64_t w64) __attribute__((always_inline)) -> int {
+    const int hv = static_cast<int>(~static_cast<uint32_t>(w64 >> (32 * (s & 1) + 4 * hi)));
+    return (e >> 24) == 2 ? hv : 0;
+  };
+  auto bias_entry = [&](auto I, int r, int hv) __attribute__((always_inline)) -> float {
+    constexpr int i = decltype(I)::value;
+    const float b = __int_as_float(__builtin_amdgcn_sbfe(hv, 8 * (r >> 2) + (r & 3), one) & static_cast<int>(kNegInfBits));
+    bias[i][r] = b;
+    return b;
+  };
+  auto set_bias = [&](auto I, int s, int e) __attribute__((always_inline)) {
+    const int hv = bias_hidden(s, e, bias_word(I, s));
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        bias[i][r] = __int_as_float(__builtin_amdgcn_sbfe(hv, 8 * (r >> 2) + (r & 3), one) & static_cast<int>(kNegInfBits));
-      bias_nz[i] = true;
-    } else if (bias_nz[i]) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) bias[i][r] = 0.f;
-      bias_nz[i] = false;
+    for (int r = 0; r < 16; ++r) bias_entry(I, r, hv);
+  };
+  // a phase's vector side work, slot by slot: the bias of stream I for step s
+  // of entry e (word read in slot 0, one entry formed per slot in slots 4-19)
+  struct BiasJob { uint64_t w; int hv; };
+  auto bias_slot = [&](auto I, auto K, int s, int e, BiasJob& job) __attribute__((always_inline)) {
+    constexpr int k = decltype(K)::value;
+    if constexpr (k == 0) job.w = bias_word(I, s);
+    if constexpr (k == 4) job.hv = bias_hidden(s, e, job.w);
+    if constexpr (k >= 4 && k < 20) {
+      const float b = bias_entry(I, k - 4, job.hv);
+      asm volatile("" :: "v"(b));   // formed here, not sunk to its MFMA
     }
   };
 
@@ -446,24 +473,23 @@ attn_fwd_bf16(AttnBf16Args a) {
   };
   // ---- one phase of the accumulation pass, scheduled by hand: 20 slots
   // separated by scheduling barriers.  Slot k issues the k-th MFMA of stream
-  // MS's matrix work (scores of the next step into s[MS] from K slot ks, the
-  // first kPK chunks already in kf, chunk c+2 read in the slot of chunk c; PV of
-  // the current step into o[MS] with the V operands vf and P^T pk[MS], each V
-  // register refilled from slot vsl after its MFMA with RELOAD) and, from slot 2
+  // MS's matrix work (scores of the next step into s[MS] from the K operands in
+  // kreg; PV of the current step into o[MS] with the V operands vf and P^T
+  // pk[MS]; with RELOAD, the second phase of a step, each K and V register is
+  // refilled right after its MFMA, K from slot ks (the step after next) and V
+  // from slot vsl (the next step): the reads have a whole phase to land, and
+  // each K operand is read once per step for both streams) and, from slot 2
   // on, one unit of the fast softmax of stream VS = 1 - MS on s[VS],
-  // software-pipelined over its 16 scores (exponential of score u, the bf16
-  // pair of scores u-2 and u-1, the sum of the pair packed before it: the row
-  // sum adds the rounded values PV applies).  Starting the softmax two MFMA
+  // software-pipelined over its 16 scores (exponential of score u; the bf16
+  // pair of scores u-2 and u-1 and the fp32 sum of score u-1).  Starting the softmax two MFMA
   // issues into the phase keeps the other stream's last score MFMA of the
   // previous phase at a safe distance from its readers.  Returns the lane's sum.
-  auto phase_fast = [&](auto MSc, auto RELOAD, auto EXTRA, int ks, int vsl) __attribute__((always_inline)) -> float {
+  auto phase_fast = [&](auto MSc, auto RELOAD, auto EXTRA, auto VEXTRA, int ks, int vsl)
+      __attribute__((always_inline)) -> float {
     constexpr int ms = decltype(MSc)::value;
     constexpr int vs = 1 - ms;
     constexpr bool reload = decltype(RELOAD)::value;
     const float cb = -m_run[vs] * kLog2e;
-    bf16x8_t kw[kDqk / 16];
-#pragma unroll
-    for (int c = 0; c < kPK; ++c) kw[c] = kf[c];
     f32x16_t acc;
     float p[16];
     float l0 = 0.f, l1 = 0.f;
@@ -472,8 +498,8 @@ attn_fwd_bf16(AttnBf16Args a) {
       constexpr int op = kSlotOp[k];
       if constexpr (op < 100) {
         constexpr int c = op;
-        if constexpr (c + kPK < kDqk / 16) kw[c + kPK] = read_k(ks, c + kPK);
-        mfma_s<c == 0, (c >= 8)>(acc, kw[c], qf[ms][c], bias[ms]);
+        mfma_s<c == 0>(acc, kreg[c], qf[ms][c], bias[ms]);
+        if constexpr (reload) kreg[c] = read_k(ks, c);
       } else {
         constexpr int v = op - 100, st = v >> 2, j = v & 3;
         const u32x4_t pb = {pk[ms][4 * st + 0], pk[ms][4 * st + 1], pk[ms][4 * st + 2], pk[ms][4 * st + 3]};
@@ -482,38 +508,49 @@ attn_fwd_bf16(AttnBf16Args a) {
         if constexpr (reload) vf[v] = read_v(vsl, v);
       }
       EXTRA(K);
+      VEXTRA(K);
       constexpr int u = k - 2;
+      // (each value is pinned to its slot by an empty asm that uses it: the
+      // compiler would otherwise sink the softmax towards its consumers)
       if constexpr (u >= 0 && u < 16) {
         p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[vs][u], scale_log2, cb));
+        asm volatile("" :: "v"(p[u]));
       }
       if constexpr (u >= 1 && u <= 16) {
         constexpr int w = u - 1;
         if constexpr (w & 1) {
           pk[vs][w >> 1] = pack_bf16x2(p[w - 1], p[w]);
-        } else if constexpr (w >= 2) {
-          if constexpr (w & 2) l1 = sum_bf16x2(pk[vs][(w >> 1) - 1], l1);
-          else l0 = sum_bf16x2(pk[vs][(w >> 1) - 1], l0);
+          asm volatile("" :: "v"(pk[vs][w >> 1]));
+          l1 += p[w];
+        } else {
+          l0 += p[w];
         }
+        asm volatile("" :: "v"(l0), "v"(l1));
       }
-      if constexpr (k == 19) l1 = sum_bf16x2(pk[vs][7], l1);
       __builtin_amdgcn_sched_barrier(0);
     });
+    // The first score MFMA reads bias[MS] as its C operand over its whole
+    // execution; an asm MFMA is opaque to the compiler's hazard checks, so keep
+    // those registers out of reuse (e.g. by the other stream's bias formed in
+    // this phase) until the phase is over.
+    asm volatile("" :: "v"(bias[ms]));
     s[ms] = acc;
     return l0 + l1;
   };
   // ---- one phase of the max-only pass: scores of the next step for stream MS,
   // the maximum of stream VS's step
-  auto phase_max = [&](auto MSc, auto EXTRA, int ks, int e, int half, bool live) __attribute__((always_inline)) {
+  auto phase_max = [&](auto MSc, auto RELOAD, auto EXTRA, auto VEXTRA, int ks, int e, int half, bool live)
+      __attribute__((always_inline)) {
     constexpr int ms = decltype(MSc)::value;
     constexpr int vs = 1 - ms;
     static_for<20>([&](auto K) __attribute__((always_inline)) { EXTRA(K); });
     f32x16_t acc;
     static_for<kDqk / 16>([&](auto C) __attribute__((always_inline)) {
       constexpr int c = decltype(C)::value;
-      bf16x8_t kop;
-      if constexpr (c < kPK) kop = kf[c]; else kop = read_k(ks, c);
-      mfma_s<c == 0, (c >= 8)>(acc, kop, qf[ms][c], bias[ms]);
+      mfma_s<c == 0>(acc, kreg[c], qf[ms][c], bias[ms]);
+      if constexpr (decltype(RELOAD)::value) kreg[c] = read_k(ks, c);
     });
+    static_for<20>([&](auto K) __attribute__((always_inline)) { VEXTRA(K); });
     s_nop_after_mfma(acc);
     s[ms] = acc;
     if (live) {
@@ -526,15 +563,16 @@ attn_fwd_bf16(AttnBf16Args a) {
   // for the step at (entry e, half); the exact path follows when the step is
   // general or ragged, a lane has no stabiliser yet, or a probability may exceed
   // the headroom
-  auto phase = [&](auto MSc, auto MODE, auto RELOAD, auto EXTRA, int ks, int vsl, int e, int half, bool live)
+  auto phase = [&](auto MSc, auto MODE, auto RELOAD, auto EXTRA, auto VEXTRA, int ks, int vsl, int e, int half,
+                   bool live)
       __attribute__((always_inline)) {
     constexpr int vs = 1 - decltype(MSc)::value;
     if constexpr (decltype(MODE)::value == kPassMax) {
-      phase_max(MSc, EXTRA, ks, e, half, live);
+      phase_max(MSc, RELOAD, EXTRA, VEXTRA, ks, e, half, live);
     } else {
       const int cls = e >> 24;
       const bool slow = cls == 3 || (e & 0xFFFFFF) * kTileN + 32 * half + 32 > a.Lk || __any(m_run[vs] == -INFINITY);
-      const float lsum = phase_fast(MSc, RELOAD, EXTRA, ks, vsl);
+      const float lsum = phase_fast(MSc, RELOAD, EXTRA, VEXTRA, ks, vsl);
       // the fast path's results are used on every path, so the compiler keeps it
       // in the scheduled block instead of moving it behind the test below
       asm volatile("" :: "v"(lsum), "v"(pk[vs][0]), "v"(pk[vs][1]), "v"(pk[vs][2]), "v"(pk[vs][3]), "v"(pk[vs][4]),
@@ -573,8 +611,8 @@ attn_fwd_bf16(AttnBf16Args a) {
       static_for<kDqk / 16>([&](auto C) __attribute__((always_inline)) {
         constexpr int c = decltype(C)::value;
         const bf16x8_t kop = read_k(0, c);
-        mfma_s<c == 0, (c >= 8)>(a0, kop, qf[0][c], bias[0]);
-        mfma_s<c == 0, (c >= 8)>(a1, kop, qf[1][c], bias[1]);
+        mfma_s<c == 0>(a0, kop, qf[0][c], bias[0]);
+        mfma_s<c == 0>(a1, kop, qf[1][c], bias[1]);
       });
       s_nop_after_mfma(a0);
       s_nop_after_mfma(a1);
@@ -594,28 +632,27 @@ attn_fwd_bf16(AttnBf16Args a) {
 #pragma unroll
     for (int op = 0; op < 8; ++op) vf[op] = read_v(0, op);
 #pragma unroll
-    for (int c = 0; c < kPK; ++c) kf[c] = read_k(1, c);
+    for (int c = 0; c < kDqk / 16; ++c) kreg[c] = read_k(1, c);
     __syncthreads();
 
     // Step t (tile T = t/2 in e0, T+1 in e1, T+2 in e2; half t&1).  K(s) lives in
     // K slot s%4, V(s) in V slot s%3, the words of tile T in slot T%3.  Registers
-    // on entry: vf = V(t), kf = first chunks of K(t+1), s[1] = stream 1's raw
-    // scores of step t, pk[0] = stream 0's P^T of step t.
+    // on entry: vf = V(t), kreg = K(t+1), s[1] = stream 1's raw scores of step
+    // t, pk[0] = stream 0's P^T of step t.
     //   copies: K(t+4) into K(t)'s slot (read in step t-1), V(t+3) into V(t)'s
     //           slot (read into registers in step t-1) and, at even t, the words
     //           of tile T+2
     //   phase A: matrix of stream 0 (scores t+1 from K(t+1), PV t)
     //            || softmax of stream 1, step t
-    //   phase B: matrix of stream 1 (scores t+1 from K(t+1), PV t; V(t+1)
-    //            replaces vf register by register) || softmax of stream 0, step
-    //            t+1; then the first chunks of K(t+2)
+    //   phase B: matrix of stream 1 (scores t+1 from K(t+1), PV t; K(t+2)
+    //            replaces kreg and V(t+1) replaces vf, register by register)
+    //            || softmax of stream 0, step t+1
     //   then each wave waits for its copies of step t-1 and the workgroup
     //   synchronises: K(t+3), V(t+2) and their words are published, the slots
     //   read in step t are free.
     for (int t = 0; t < nsteps; ++t) {
       const int half = t & 1;
       const int k4 = t & 3;
-      const int k41 = (t + 1) & 3;
       const int k42 = (t + 2) & 3;
       const int v3 = t % 3;
       const int v31 = v3 == 2 ? 0 : v3 + 1;          // (t+1) % 3
@@ -627,28 +664,26 @@ attn_fwd_bf16(AttnBf16Args a) {
       auto copies_a = [&](auto K) __attribute__((always_inline)) {
         constexpr int k = decltype(K)::value;
         if constexpr (k % 3 == 1 && k / 3 < 6) issue_k_piece(IC<k / 3>{}, k4, kkey);
-        if constexpr (k == 18) {
-          if (!half) issue_bits(bslot, e2);
-        }
+        if constexpr (k == 18) issue_bits(bslot, e2);
       };
       auto copies_b = [&](auto K) __attribute__((always_inline)) {
         constexpr int k = decltype(K)::value;
         if constexpr (k % 4 == 1 && k / 4 < 4) issue_v_piece(IC<k / 4>{}, v3, vkey);
       };
+      // biases built during the phases: stream 1's for step t+1 (phase B's
+      // scores) in phase A, stream 0's for step t+2 (the next phase A) in phase B
+      const int es1 = half ? e1 : e0;
+      BiasJob job1, job0;
+      auto bias_a = [&](auto K) __attribute__((always_inline)) { bias_slot(IC<1>{}, K, t + 1, es1, job1); };
+      auto bias_b = [&](auto K) __attribute__((always_inline)) { bias_slot(IC<0>{}, K, t + 2, e1, job0); };
       // ---- phase A
-      phase(IC<0>{}, MODE, std::false_type{}, copies_a, k41, 0, e0, half, true);
-#pragma unroll
-      for (int c = 0; c < kPK; ++c) kf[c] = read_k(k41, c);
-      set_bias(IC<1>{}, t + 1, half ? e1 : e0);                       // scores of stream 1, step t+1
+      phase(IC<0>{}, MODE, std::false_type{}, copies_a, bias_a, k42, 0, e0, half, true);
       // ---- phase B
-      phase(IC<1>{}, MODE, std::true_type{}, copies_b, k41, v31, half ? e1 : e0, half ^ 1, t + 1 < nsteps);
-#pragma unroll
-      for (int c = 0; c < kPK; ++c) kf[c] = read_k(k42, c);
-      set_bias(IC<0>{}, t + 2, e1);                                     // scores of stream 0, step t+2
-      // copies of step t-1 complete (those of step t, 10 per wave and wave 0's
-      // word copy at even t, may still be in flight)
-      if (wave == 0 && !half) wait_vmem<11>(); else wait_vmem<10>();
-      __syncthreads();
+      phase(IC<1>{}, MODE, std::true_type{}, copies_b, bias_b, k42, v31, es1, half ^ 1, t + 1 < nsteps);
+      // copies of step t-1 complete (those of step t, 11 per wave, may still be
+      // in flight)
+      wait_vmem<11>();
+      step_barrier();
       if (half) {
         e0 = e1; e1 = e2; e2 = e3;
         e3 = entry((t >> 1) + 4);

@@ -236,10 +236,13 @@ dflash_status dflash_mla_attn(const void* q, const void* k_nope, const void* k_r
  * dflash_mla_attn that also writes, for every (b, h, i), the natural-log row
  * normaliser lse[b,h,i] = log(sum_j exp(s_j)) (f32, [B, H, Lq]; -inf for a row
  * with no finite score), which the backward takes instead of recomputing the
- * softmax statistics.  In the BF16 path the sum adds the bf16-rounded
- * probabilities the kernel applies in PV, so exp(s_j - lse) are, to fp32
- * accuracy, the normalised weights that produced out (each within a relative
- * 2^-9 of the exact softmax weight).  lse must be 4-byte aligned and overlap nothing else; other
+ * softmax statistics.  In the BF16 path the sum adds the fp32 probabilities,
+ * except on key steps of the exact path (a tile with general mask values, a
+ * ragged key tail, a row's first visible step), where it adds the bf16-rounded
+ * probabilities the kernel applies in PV.  Each probability is within a
+ * relative 2^-9 of its rounding, so exp(s_j - lse) are within about 2^-9 of
+ * both the exact softmax weights and the normalised weights that produced out.
+ * lse must be 4-byte aligned and overlap nothing else; other
  * arguments, limits and errors as dflash_mla_attn.
  */
 dflash_status dflash_mla_attn_lse(const void* q, const void* k_nope, const void* k_rope_shared,

@@ -1,9 +1,10 @@
 """The attention backward and the forward's row log-normaliser on the GPU,
 against the fp64 oracle (oracle.mla_attention_backward / logsumexp_rows).
 
-Tolerances, from the arithmetic.  The lse of the bf16 forward sums the bf16-
-rounded probabilities (relative error <= 2^-9 each, all positive, so the sum
-too), so |lse - exact| <= ~2^-9: bound 4e-3.  The backward rounds p and ds to
+Tolerances, from the arithmetic.  The lse of the bf16 forward sums fp32
+probabilities, or on its exact-path steps their bf16 roundings (relative error
+<= 2^-9 each, all positive, so the sum too), so |lse - exact| <= ~2^-9: bound
+4e-3.  The backward rounds p and ds to
 bf16 as MFMA operands and every output to bf16 (each a relative 2^-9
 perturbation of a term or a result), recomputes p from that lse (another
 relative 2^-9) and takes D from the bf16
