@@ -40,8 +40,10 @@ def log(msg: str) -> None:
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warm-seconds", type=float, default=0.5,
+                   help="untimed busy time before each timed region, after the warmup steps (0 under a profiler)")
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="2", help="headline workload: 0,1,2,3a,3b,4")
     p.add_argument("--secondary", default="4,1,3a,3b,2s,4s,2b,4b,2p,gqa",
                    help="comma list, or 'none'; a trailing 's' takes the mask from the block "
@@ -88,6 +90,92 @@ def kernel_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+class SclkSampler:
+    """Samples the shader clock the driver reports (amdsmi's GFX clock, else the
+    sysfs pp_dpm_sclk level marked '*') from a thread while the timed region
+    runs; None where neither is readable."""
+
+    def __init__(self, period_s: float = 0.005):
+        import glob
+        import threading
+        self.files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.smi = None
+        try:                                   # the ROCm SMI library, when present
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.smi = amdsmi.amdsmi_get_processor_handles()[0]
+            self.source = "amdsmi GFX clock during the timed steps"
+        except Exception:
+            self.source = "sysfs pp_dpm_sclk during the timed steps"
+        self.period = period_s
+        self.samples = []
+        self.stop = threading.Event()
+        self.thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        if self.smi is not None:
+            try:
+                import amdsmi
+                info = amdsmi.amdsmi_get_clock_info(self.smi, amdsmi.AmdSmiClkType.GFX)
+                return float(info["clk"])
+            except Exception:
+                self.smi = None
+        for path in self.files:
+            try:
+                for line in open(path):
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().rstrip("*").strip().lower().replace("mhz", ""))
+            except (OSError, ValueError, IndexError):
+                continue
+        return None
+
+    def _run(self):
+        while not self.stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self.stop.wait(self.period)
+
+    def __enter__(self):
+        if self.files or self.smi is not None:
+            self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        if self.thread.is_alive():
+            self.thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        s = self.samples
+        return {"mean_MHz": round(sum(s) / len(s)), "min_MHz": round(min(s)), "max_MHz": round(max(s)),
+                "samples": len(s), "source": self.source}
+
+
+WARM = {"seconds": 0.5}     # set from --warm-seconds
+
+
+def host_info() -> dict:
+    try:
+        aff = sorted(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        aff = []
+    runs, start = [], None
+    for c in aff:                      # compress the affinity set into ranges
+        if start is None:
+            start = prev = c
+        elif c == prev + 1:
+            prev = c
+        else:
+            runs.append(f"{start}-{prev}" if prev > start else f"{start}")
+            start = prev = c
+    if start is not None:
+        runs.append(f"{start}-{prev}" if prev > start else f"{start}")
+    return {"os_cpu_count": os.cpu_count(), "affinity_cpus": len(aff), "affinity": ",".join(runs)}
+
+
 def measure(wl, steps: int, warmup: int, structured: bool = False) -> dict:
     import torch
     from dflash_block_draft_amd import mla
@@ -131,15 +219,23 @@ def measure(wl, steps: int, warmup: int, structured: bool = False) -> dict:
     for _ in range(warmup):
         step(scratch)
     torch.cuda.synchronize()
+    # then keep the GPU busy for at least --warm-seconds so its clocks settle at
+    # their sustained level before the timed steps (untimed)
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < WARM["seconds"]:
+        for _ in range(8):
+            step(scratch)
+        torch.cuda.synchronize()
     marks = [[ev() for _ in range(4)] for _ in range(steps)]
     start, end = ev(), ev()
-    t0 = time.perf_counter()
-    start.record()
-    for k in range(steps):
-        step(marks[k])
-    end.record()
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    with SclkSampler() as sclk:
+        t0 = time.perf_counter()
+        start.record()
+        for k in range(steps):
+            step(marks[k])
+        end.record()
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     ms = start.elapsed_time(end) / steps
     occ = sum(mk[1].elapsed_time(mk[2]) for mk in marks) / steps
     att = sum(mk[2].elapsed_time(mk[3]) for mk in marks) / steps
@@ -191,7 +287,10 @@ def measure(wl, steps: int, warmup: int, structured: bool = False) -> dict:
         "key_runs": key_runs,
         "tile_fractions_128x64": frac,
         "attn_algorithmic_bytes": attn_bytes,
+        "attn_GBs": round(attn_bytes / (att * 1e-3) / 1e9, 1),
+        "attn_pct_hbm_peak": round(100.0 * attn_bytes / (att * 1e-3) / 8e12, 2),
         "mask_bytes": mask_bytes,
+        "sclk": sclk.summary(),
     }
     if expand:
         xf = 2 * wl.B * wl.Lk * 512 * wl.H * (wl.Dn + wl.Dv)
@@ -455,6 +554,7 @@ def traffic_from(args) -> None:
 
 def main():
     args = parse()
+    WARM["seconds"] = max(0.0, args.warm_seconds)
     if args.traffic_from:
         traffic_from(args)
         return
@@ -543,6 +643,8 @@ def main():
                      "traffic": traffic_for(wl.name),
                      "basis": "visible FLOPs (finite-mask pairs x heads x 640) / mean attention-kernel time (HIP events on its stream)"},
         "cpu_baseline": cpu,
+        "host": host_info(),
+        "sclk": head.get("sclk"),
         "headline": head,
         "secondary": secondary,
         "attn_kernel_sha": kernel_sha(),
