@@ -503,17 +503,17 @@ dflash_status attn_impl(const void* q, const void* k_nope, const void* k_rope_sh
 struct BwdLayout {
   TileLayout t;
   int64_t Lqp, Lkp;
-  size_t lse2, dd, qT, doT, knT, krT, rope, total;
+  size_t lse2, dd, qT, doT, knT, krT, rope, ld, bitsT, total;
 };
 
 bool bwd_layout(int64_t B, int64_t H, int64_t Lq, int64_t Lk, BwdLayout* L) {
   if (H <= 0 || !tile_layout(B, Lq, Lk, &L->t)) return false;
   L->Lqp = L->t.nqt * DFLASH_TILE_M;
   L->Lkp = L->t.nkt * DFLASH_TILE_N;
-  int64_t bh, a, c, d, e, f, g;
+  int64_t bh, a, c, d, e, f, g, bt;
   if (!mul_ok(B, H, &bh) || !mul_ok(bh, L->Lqp, &a) || !mul_ok(a, 4, &c) || !mul_ok(a, 2 * 192, &d) ||
       !mul_ok(bh, L->Lkp, &e) || !mul_ok(e, 2 * 128, &e) || !mul_ok(B, L->Lkp * 2 * 64, &f) ||
-      !mul_ok(bh, Lk, &g) || !mul_ok(g, 64 * 4, &g))
+      !mul_ok(bh, Lk, &g) || !mul_ok(g, 64 * 4, &g) || !mul_ok(B * L->t.nqt, L->t.nkt, &bt) || !mul_ok(bt, 1024, &bt))
     return false;
   L->lse2 = align_up(L->t.total, 256);
   L->dd = L->lse2 + align_up(static_cast<size_t>(c), 256);
@@ -522,7 +522,9 @@ bool bwd_layout(int64_t B, int64_t H, int64_t Lq, int64_t Lk, BwdLayout* L) {
   L->knT = L->doT + align_up(static_cast<size_t>(a) * 2 * 128, 256);
   L->krT = L->knT + align_up(static_cast<size_t>(e), 256);
   L->rope = L->krT + align_up(static_cast<size_t>(f), 256);
-  L->total = L->rope + align_up(static_cast<size_t>(g), 256);
+  L->ld = L->rope + align_up(static_cast<size_t>(g), 256);
+  L->bitsT = L->ld + align_up(static_cast<size_t>(c) * 2, 256);
+  L->total = L->bitsT + align_up(static_cast<size_t>(bt), 256);
   return true;
 }
 
@@ -718,6 +720,8 @@ dflash_status dflash_mla_attn_bwd(const void* q, const void* k_nope, const void*
   a.knT = reinterpret_cast<uint16_t*>(ws + L.knT);
   a.krT = reinterpret_cast<uint16_t*>(ws + L.krT);
   a.rope_part = reinterpret_cast<float*>(ws + L.rope);
+  a.ld = reinterpret_cast<float*>(ws + L.ld);
+  a.bitsT = reinterpret_cast<uint32_t*>(ws + L.bitsT);
   a.B = static_cast<int>(B);
   a.H = static_cast<int>(H);
   a.Lq = static_cast<int>(Lq);

@@ -40,7 +40,6 @@
 #include "common.h"
 #include "dma.h"
 #include "launch.h"
-#include "bwd_plan.h"
 
 #include <type_traits>
 
@@ -51,6 +50,11 @@ template <int N>
 using IC = std::integral_constant<int, N>;
 
 constexpr int kThreads = 256;
+constexpr int kQC = 32;                         // queries per prep_q workgroup
+// LDS row strides (bytes): row + 16, so 16-lane column reads hit distinct banks
+constexpr int kSQ = kDqk * 2 + 16;              // 400: q / k rows
+constexpr int kSO = kDv * 2 + 16;               // 272: dout / v rows
+constexpr int kSKT = kTileN * 2 + 16;           // 144: transposed k rows (64 keys)
 // dQ stage: K, V, K^T
 constexpr int kB_K = 0;
 constexpr int kB_V = kB_K + kTileN * kSQ;
@@ -136,6 +140,10 @@ __global__ void __launch_bounds__(kThreads) bwd_prep_q(AttnBwdArgs a) {
       a.dd[bh * a.Lqp + qi] = acc;
       const float l = qi < a.Lq ? a.lse[bh * a.Lq + qi] : -INFINITY;
       a.lse2[bh * a.Lqp + qi] = l == -INFINITY ? INFINITY : l * kLog2e;
+      // per 32-query chunk: the exponent offsets, then -D
+      float* ld = a.ld + (bh * (a.Lqp / kQC) + blockIdx.x) * 64;
+      ld[r] = l == -INFINITY ? -INFINITY : -l * kLog2e;
+      ld[kQC + r] = -acc;
     }
   }
   __syncthreads();
@@ -203,220 +211,7 @@ __global__ void __launch_bounds__(kThreads) bwd_prep_k(AttnBwdArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- 3. dK / dV
-template <bool MASK_BF16>
-__global__ void __launch_bounds__(kThreads) bwd_dkdv(AttnBwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[kA_Stages * kA_Stage];
-  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
-  const int t = threadIdx.x, lane = t & 63;
-  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int li = lane & 31, hi = lane >> 5;
-  const int kb = blockIdx.x;
-  const size_t bh = blockIdx.y;
-  const int b = static_cast<int>(bh / a.H);
-  const int kt0 = 2 * kb;                              // this workgroup's k-tiles: kt0, kt0 + 1
-  const bool has_kt1 = kt0 + 1 < a.nkt;
-  const int key = kb * kKB + 32 * w + li;              // this lane's key (operands, p column)
-  const bool key_ok = key < a.Lk;
-  const int bit = (w & 1) * 32 + li;                   // its bit in the k-tile's visibility words
-
-  bf16x8_t kreg[12], vreg[8];
-#pragma unroll
-  for (int s = 0; s < 12; ++s) {
-    u32x4_t x = zero4();
-    if (key_ok) x = s < 8 ? ldg16(a.kn + (bh * a.Lk + key) * kDn + 16 * s + 8 * hi)
-                          : ldg16(a.kr + (static_cast<size_t>(b) * a.Lk + key) * kDr + 16 * (s - 8) + 8 * hi);
-    kreg[s] = as_bf16x8(x);
-  }
-#pragma unroll
-  for (int s = 0; s < 8; ++s)
-    vreg[s] = as_bf16x8(key_ok ? ldg16(a.v + (bh * a.Lk + key) * kDv + 16 * s + 8 * hi) : zero4());
-  // K and V in registers before any stage copy: the compiler cannot count the copies
-  // (inline asm), so a wait of its own for these loads inside the loop would be a
-  // full vmcnt(0) -- draining the copies in flight at every chunk
-  wait_vmem<0>();
-
-  f32x16_t dk[6], dv[4];
-#pragma unroll
-  for (int i = 0; i < 6; ++i) dk[i] = zero16();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dv[i] = zero16();
-
-  // tile classes through scalar loads (the aligned dword holding the byte), so no
-  // vector-memory wait of the compiler's lands between the stage copies
-  typedef __attribute__((address_space(4))) const uint32_t const_u32;
-  auto tile_cls = [&](int qt, int kt) __attribute__((always_inline)) -> int {
-    if (!a.classes) return 1;
-    const size_t idx = (static_cast<size_t>(b) * a.nqt + qt) * a.nkt + kt;
-    const const_u32* p = (const const_u32*)(uintptr_t)(a.classes + (idx & ~static_cast<size_t>(3)));
-    return static_cast<int>((p[0] >> (8 * (idx & 3))) & 0xFFu);
-  };
-  // chunk iterator over (q-tile, 32-query chunk) with a non-empty tile in kt0 / kt0+1
-  auto next_qt = [&](int qt) -> int {
-    for (++qt; qt < a.nqt; ++qt)
-      if (tile_cls(qt, kt0) != 0 || (has_kt1 && tile_cls(qt, kt0 + 1) != 0)) break;
-    return qt;
-  };
-  auto advance = [&](int& qt, int& c) {
-    if (qt >= a.nqt) return;
-    ++c;
-    if (c == kTileM / kQC || qt * kTileM + c * kQC >= a.Lq) {
-      c = 0;
-      qt = next_qt(qt);
-    }
-  };
-
-  // ---- stage copies: global -> LDS through the buffer unit (no staging registers).
-  // Wave w copies blocks 13w .. 13w + 12 of each stage; its per-lane offsets are
-  // fixed, the chunk sets the uniform offsets.  A chunk past the end copies with an
-  // offset beyond every resource (zeros, no traffic), so every wave issues the same
-  // number of copies each step and the wait counts are constants.  Rows past Lq
-  // read as zeros through the resources' ranges.
-  const u32x4_t d_q = buffer_desc(a.q + bh * a.Lq * kDqk, static_cast<uint32_t>(a.Lq) * kDqk * 2);
-  const u32x4_t d_o = buffer_desc(a.dout + bh * a.Lq * kDv, static_cast<uint32_t>(a.Lq) * kDv * 2);
-  const u32x4_t d_qt = buffer_desc(a.qT + bh * kDqk * a.Lqp, static_cast<uint32_t>(kDqk) * a.Lqp * 2);
-  const u32x4_t d_ot = buffer_desc(a.doT + bh * kDv * a.Lqp, static_cast<uint32_t>(kDv) * a.Lqp * 2);
-  const u32x4_t d_l = buffer_desc(a.lse2 + bh * a.Lqp, static_cast<uint32_t>(a.Lqp) * 4);
-  const u32x4_t d_d = buffer_desc(a.dd + bh * a.Lqp, static_cast<uint32_t>(a.Lqp) * 4);
-  const u32x4_t d_b = buffer_desc(a.bits, a.bits ? static_cast<uint32_t>(
-                                              static_cast<size_t>(a.B) * a.nqt * a.nkt * kTileM * 8) : 0u);
-  uint32_t voff[kA_PerWave];
-#pragma unroll
-  for (int j = 0; j < kA_PerWave; ++j) {
-    const int blk = kA_PerWave * w + j;
-    voff[j] = blk < kA_Blocks ? a_voff(blk, lane, a.Lqp) : 0u;
-  }
-  constexpr uint32_t kPastEnd = 0x80000000u;           // beyond every resource (the host bounds them by 2^31 bytes)
-  auto issue = [&](auto W, uint32_t stage_off, int qt, int c) __attribute__((always_inline)) {
-    constexpr int wv = decltype(W)::value;
-    const bool live = qt < a.nqt;
-    const uint32_t q0 = static_cast<uint32_t>(qt * kTileM + c * kQC);
-    const uint32_t tile = static_cast<uint32_t>(((static_cast<size_t>(b) * a.nqt + qt) * a.nkt + kt0) * kTileM * 8);
-    const uint32_t base = lds0 + stage_off + kA_PerWave * wv * 1024;
-    auto one = [&](auto J) __attribute__((always_inline)) {
-      constexpr int j = decltype(J)::value, blk = kA_PerWave * wv + j;
-      if constexpr (blk < kA_Blocks) {
-        constexpr int reg = blk < 13 ? kRegQ : blk < 22 ? kRegO : blk < 37 ? kRegQT : blk < 47 ? kRegOT : blk - 47 + kRegL;
-        const u32x4_t d = reg == kRegQ ? d_q : reg == kRegO ? d_o : reg == kRegQT ? d_qt : reg == kRegOT ? d_ot
-                        : reg == kRegL ? d_l : reg == kRegD ? d_d : d_b;
-        const uint32_t so = !live ? kPastEnd : a_soff(reg, q0, tile, c);
-        dma16<j * 1024>(d, base, voff[j], so);
-      }
-    };
-    one(IC<0>{}); one(IC<1>{}); one(IC<2>{}); one(IC<3>{}); one(IC<4>{}); one(IC<5>{}); one(IC<6>{});
-    one(IC<7>{}); one(IC<8>{}); one(IC<9>{}); one(IC<10>{}); one(IC<11>{}); one(IC<12>{});
-    static_assert(kA_PerWave == 13, "the unrolled copy list above");
-  };
-  auto issue_stage = [&](uint32_t stage_off, int qt, int c) __attribute__((always_inline)) {
-    if (w == 0) issue(IC<0>{}, stage_off, qt, c);
-    else if (w == 1) issue(IC<1>{}, stage_off, qt, c);
-    else if (w == 2) issue(IC<2>{}, stage_off, qt, c);
-    else issue(IC<3>{}, stage_off, qt, c);
-  };
-  // this wave's copies of the older stage done, those of the newest one still in flight
-  auto wait_older = [&]() __attribute__((always_inline)) {
-    if (w == 3) wait_vmem<kA_Blocks - 3 * kA_PerWave>(); else wait_vmem<kA_PerWave>();
-  };
-
-  const float scale_log2 = a.scale * kLog2e;
-  auto compute = [&](const char* st, int qt, int c, int cls) __attribute__((always_inline)) {
-    if (cls == 0) return;
-    f32x16_t S = zero16(), dP = zero16();
-#pragma unroll
-    for (int s = 0; s < 12; ++s) S = mfma32(lds_frag(st + kA_Q + li * kSQ + (16 * s + 8 * hi) * 2), kreg[s], S);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) dP = mfma32(lds_frag(st + kA_O + li * kSO + (16 * s + 8 * hi) * 2), vreg[s], dP);
-    __builtin_amdgcn_sched_barrier(0);
-    const int q0 = qt * kTileM + c * kQC;
-    float madd[16];                                   // log2(e) * mask values (general tiles only)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) madd[r] = 0.f;
-    if (cls == 3 && a.mask) {
-      for (int r = 0; r < 16; ++r) {
-        const int qr = 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (key_ok && q0 + qr < a.Lq)
-          madd[r] = mask_value<MASK_BF16>(a.mask, (static_cast<size_t>(b) * a.Lq + q0 + qr) * a.Lk + key) * kLog2e;
-      }
-    }
-    float p[16], ds[16];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(st + kA_L + (8 * g + 4 * hi) * 4);
-      const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(st + kA_D + (8 * g + 4 * hi) * 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * g + e, qr = 8 * g + 4 * hi + e;   // accumulator row r <-> chunk query qr
-        bool vis = key_ok;
-        if (cls == 2) {
-          const uint64_t word = *reinterpret_cast<const uint64_t*>(st + kA_B + ((w >> 1) * kQC + qr) * 8);
-          vis = vis && ((word >> bit) & 1ull);
-        }
-        const float pr = vis ? __builtin_amdgcn_exp2f(S[r] * scale_log2 - l4[e] + madd[r]) : 0.f;
-        p[r] = pr;
-        ds[r] = pr * (dP[r] - d4[e]);
-      }
-    }
-    const bf16x8_t aP0 = pack8(p), aP1 = pack8(p + 8);
-    const bf16x8_t aS0 = pack8(ds), aS1 = pack8(ds + 8);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const char* rowp = st + kA_OT + (32 * nt + li) * kSQT + 16 * hi;
-      dv[nt] = mfma32(aP0, lds_frag(rowp), dv[nt]);
-      dv[nt] = mfma32(aP1, lds_frag(rowp + 32), dv[nt]);
-    }
-#pragma unroll
-    for (int nt = 0; nt < 6; ++nt) {
-      const char* rowp = st + kA_QT + (32 * nt + li) * kSQT + 16 * hi;
-      dk[nt] = mfma32(aS0, lds_frag(rowp), dk[nt]);
-      dk[nt] = mfma32(aS1, lds_frag(rowp + 32), dk[nt]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  // chunks it, it+1, it+2 (qt >= nqt: past the end)
-  int qa = next_qt(-1), ca = 0;
-  if (qa < a.nqt) {
-    int qb_ = qa, cb = ca;
-    advance(qb_, cb);
-    int qc = qb_, cc = cb;
-    advance(qc, cc);
-    issue_stage(0, qa, ca);
-    issue_stage(kA_Stage, qb_, cb);
-    wait_older();
-    __syncthreads();
-    int s0 = 0;                                          // stage of chunk it
-    for (;;) {
-      const int s2 = s0 == 0 ? 2 : s0 - 1;               // stage of chunk it+2 (that of chunk it-1)
-      issue_stage(s2 * kA_Stage, qc, cc);
-      compute(smem + s0 * kA_Stage, qa, ca, (w >> 1) ? (has_kt1 ? tile_cls(qa, kt0 + 1) : 0) : tile_cls(qa, kt0));
-      if (qb_ >= a.nqt) break;
-      wait_older();
-      __syncthreads();
-      qa = qb_; ca = cb;
-      qb_ = qc; cb = cc;
-      advance(qc, cc);
-      s0 = s0 == 2 ? 0 : s0 + 1;
-    }
-    wait_vmem<0>();
-  }
-
-  // accumulator row r <-> key 8*(r/4) + 4*hi + r%4 of the wave's 32, column <-> dim
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int kj = kb * kKB + 32 * w + 8 * (r >> 2) + 4 * hi + (r & 3);
-    if (kj >= a.Lk) continue;
-    const size_t row = bh * a.Lk + kj;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const uint32_t kv = pack_bf16x2(dk[nt][r] * a.scale, dv[nt][r]);
-      a.dkn[row * kDn + 32 * nt + li] = static_cast<uint16_t>(kv & 0xFFFFu);
-      a.dv[row * kDv + 32 * nt + li] = static_cast<uint16_t>(kv >> 16);
-    }
-#pragma unroll
-    for (int nt = 4; nt < 6; ++nt) a.rope_part[row * kDr + 32 * (nt - 4) + li] = dk[nt][r] * a.scale;
-  }
-}
+// ---------------------------------------------------------------- 3. dK / dV: bwd_dkdv.hip
 
 // ---------------------------------------------------------------- 4. dQ
 template <bool MASK_BF16>
@@ -634,10 +429,7 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_prep_k, dim3(a.Lkp / kTileN, bh), dim3(kThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const dim3 gkv((a.Lk + kKB - 1) / kKB, bh);
-  if (a.mask && a.mask_bf16) hipLaunchKernelGGL(bwd_dkdv<true>, gkv, dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL(bwd_dkdv<false>, gkv, dim3(kThreads), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_bwd_dkdv(a, s)) != hipSuccess) return e;
   const dim3 gq(static_cast<unsigned>(a.B) * a.nqt * a.H);
   if (a.mask && a.mask_bf16) hipLaunchKernelGGL(bwd_dq<true>, gq, dim3(kThreads), 0, s, a);
   else hipLaunchKernelGGL(bwd_dq<false>, gq, dim3(kThreads), 0, s, a);

@@ -1,6 +1,18 @@
-// Stage layout and global -> LDS copy plan of the backward's dK/dV kernel, as
-// plain constexpr integer code (no device code), so that a host-side check can
-// walk the plan and confirm every byte the kernel reads lands from its source.
+// Staging layout of the backward's dK/dV kernel, as plain constexpr integer code
+// (no device code), so that a host-side check can replay every global -> LDS
+// copy and confirm that each operand read of the compute finds its bytes.
+//
+// The kernel walks 32-query chunks.  Chunk j's data is split in two parts: the
+// F part (q and dout rows, the rows' exponent offsets and -D, the transposed
+// visibility words) feeds the scores of chunk j in step j - 1; the T part (the
+// transposed q and dout) feeds dV of chunk j, whose operands are read from the
+// end of step j - 1 on, and dK of chunk j in step j.  Both parts of chunk j are
+// copied in step j - 3: the F ring has three slots, the T ring four.
+//
+// Every row region is stored as 1 KiB blocks of 16 rows x 64 bytes with the four
+// 16-byte pieces of a row permuted by the row (piece p at position p ^ swz(row)),
+// so the 16-byte operand reads of 16 lanes hit distinct banks without padding,
+// and every region is a whole number of blocks that the four waves split evenly.
 #pragma once
 
 #include <stdint.h>
@@ -9,65 +21,105 @@
 
 namespace dflash {
 
-constexpr int kQC = 32;                         // queries per dK/dV chunk
-constexpr int kKB = 128;                        // keys per dK/dV workgroup
-// LDS row strides (bytes): row + 16
-constexpr int kSQ = kDqk * 2 + 16;              // 400: q / k rows
-constexpr int kSO = kDv * 2 + 16;               // 272: dout / v rows
-constexpr int kSQT = kQC * 2 + 16;              // 80:  transposed q / dout rows (32 queries)
-constexpr int kSKT = kTileN * 2 + 16;           // 144: transposed k rows (64 keys)
+constexpr int kQC = 32;                          // queries per chunk
+constexpr int kKB = 128;                         // keys per workgroup (two k-tiles)
+constexpr int kKvWaves = 4;
 
-// dK/dV stage: Q, dO, Q^T, dO^T, lse2, D, visibility words (2 k-tiles x 32 rows),
-// each region rounded up to whole 1 KiB blocks: one block is one buffer -> LDS copy
-// instruction (64 lanes x 16 bytes), and no instruction spans two sources.
-constexpr int kA_Q = 0;                          // 32 rows x 400 B in 13 blocks
-constexpr int kA_O = kA_Q + 13 * 1024;           // 32 rows x 272 B in 9 blocks
-constexpr int kA_QT = kA_O + 9 * 1024;           // 192 rows x 80 B = 15 blocks
-constexpr int kA_OT = kA_QT + 15 * 1024;         // 128 rows x 80 B = 10 blocks
-constexpr int kA_L = kA_OT + 10 * 1024;          // 32 floats
-constexpr int kA_D = kA_L + 1024;                // 32 floats
-constexpr int kA_B = kA_D + 1024;                // [2 k-tiles][32 rows] uint64
-constexpr int kA_Stage = kA_B + 1024;            // 50 blocks
-constexpr int kA_Blocks = kA_Stage / 1024;
-constexpr int kA_Stages = 3;                     // chunks in flight: the next two while one is computed
-constexpr int kA_PerWave = (kA_Blocks + 3) / 4;  // copy instructions per wave and stage: 13 (the last wave 11)
-static_assert(kQC * kSQ <= 13 * 1024 && kQC * kSO <= 9 * 1024 && kDqk * kSQT == 15 * 1024 && kDv * kSQT == 10 * 1024,
-              "dK/dV stage regions");
-static_assert(kA_Stages * kA_Stage <= 160 * 1024, "LDS budget");
+// F slot: q rows (32 x 384 B), dout rows (32 x 256 B), then two 1 KiB blocks:
+// LD (the chunk's 32 exponent offsets -lse*log2(e), then its 32 values -D) and
+// the visibility words of the two k-tiles (64 keys x 32 query bits each)
+constexpr int kF_Q = 0;
+constexpr int kF_O = kF_Q + kQC * kDqk * 2;      // 12288
+constexpr int kF_LD = kF_O + kQC * kDv * 2;      // 20480
+constexpr int kF_B = kF_LD + 1024;               // 21504
+constexpr int kF_Slot = kF_B + 1024;             // 22528
+// T slot: transposed q (192 rows x 64 B), transposed dout (128 rows x 64 B)
+constexpr int kT_QT = 0;
+constexpr int kT_OT = kT_QT + kDqk * kQC * 2;    // 12288
+constexpr int kT_Slot = kT_OT + kDv * kQC * 2;   // 20480
+constexpr int kFSlots = 3;
+constexpr int kTSlots = 4;
 
-// Copy plan of the dK/dV stage: block `blk` (0..49) of a stage, lane l: the source
-// region, the lane's byte offset inside it (fixed for the kernel; the chunk moves
-// the uniform offset) -- padding chunks of a row and lanes past a region's rows
-// re-read a valid chunk of the same row / region, landing in LDS padding.
-enum : int { kRegQ, kRegO, kRegQT, kRegOT, kRegL, kRegD, kRegB };
-constexpr int a_region(int blk) {
-  return blk < 13 ? kRegQ : blk < 22 ? kRegO : blk < 37 ? kRegQT : blk < 47 ? kRegOT : blk - 47 + kRegL;
+// copy instructions per wave and step: 3 q, 2 dout, LD, words (F); 3 q^T, 2 dout^T (T)
+constexpr int kCopiesPerStep = 12;
+
+// position of 16-byte piece p of row r inside its 64-byte block row
+constexpr int swz(int r) { return (r >> 2) & 3; }
+
+// LDS byte of (row, byte x) of a row region whose rows are `width` bytes wide
+constexpr int region_byte(int row, int x, int width) {
+  return ((row >> 4) * (width / 64) + x / 64) * 1024 + (row & 15) * 64 + ((((x & 63) >> 4) ^ swz(row)) << 4) +
+         (x & 15);
 }
-constexpr uint32_t a_voff(int blk, int lane, int Lqp) {
-  switch (a_region(blk)) {
-    case kRegQ: {
-      const int j = blk * 64 + lane, row = j / 25, col = j % 25;
-      return row >= kQC ? 0u : static_cast<uint32_t>(row * (kDqk * 2) + (col < 24 ? col : 0) * 16);
+
+// ---- copy plan: instruction j (0..11) of wave w.  Lane l writes 16 bytes at
+// LDS byte dst_base(w, j) + 16 l of its slot; the source is region src_region(j)
+// at byte voff(w, j, l) + the step's uniform offset (q0 the chunk's first query):
+//   q: q0 * 384; dout: q0 * 256; LD: q0 * 8 (64 floats per chunk); words: q0 * 8
+//   (256 bytes per chunk and k-tile, k-tiles nqt * 1024 bytes apart); q^T and
+//   dout^T: q0 * 2 (rows Lqp * 2 bytes apart).
+// A lane with nothing to copy reads past the end of every resource (zeros, no
+// traffic) into an unused part of the block.
+enum : int { kSrcQ, kSrcO, kSrcLD, kSrcB, kSrcQT, kSrcOT };
+constexpr uint32_t kPastEnd = 0x80000000u;       // beyond every resource (the host bounds them by 2^31 bytes)
+
+constexpr int src_region(int j) {
+  return j < 3 ? kSrcQ : j < 5 ? kSrcO : j == 5 ? kSrcLD : j == 6 ? kSrcB : j < 10 ? kSrcQT : kSrcOT;
+}
+constexpr bool f_part(int j) { return j < 7; }
+// LDS destination of instruction j of wave w, relative to its slot (F or T)
+constexpr int dst_base(int w, int j) {
+  return j < 3 ? kF_Q + (3 * w + j) * 1024
+       : j < 5 ? kF_O + (2 * w + j - 3) * 1024
+       : j == 5 ? kF_LD
+       : j == 6 ? kF_B
+       : j < 10 ? kT_QT + (3 * w + j - 7) * 1024
+       : kT_OT + (2 * w + j - 10) * 1024;
+}
+// block blk of a region of `width`-byte rows, lane l: (row, byte of the row)
+constexpr int blk_row(int blk, int l, int width) { return 16 * (blk / (width / 64)) + (l >> 2); }
+constexpr int blk_x(int blk, int l, int width) {
+  return (blk % (width / 64)) * 64 + (((l & 3) ^ swz(blk_row(blk, l, width))) << 4);
+}
+constexpr uint32_t voff(int w, int j, int l, int Lqp, int nqt) {
+  switch (src_region(j)) {
+    case kSrcQ: {
+      const int blk = 3 * w + j;
+      return static_cast<uint32_t>(blk_row(blk, l, 384) * 384 + blk_x(blk, l, 384));
     }
-    case kRegO: {
-      const int j = (blk - 13) * 64 + lane, row = j / 17, col = j % 17;
-      return row >= kQC ? 0u : static_cast<uint32_t>(row * (kDv * 2) + (col < 16 ? col : 0) * 16);
+    case kSrcO: {
+      const int blk = 2 * w + j - 3;
+      return static_cast<uint32_t>(blk_row(blk, l, 256) * 256 + blk_x(blk, l, 256));
     }
-    case kRegQT: case kRegOT: {
-      const int j = (blk - (blk < 37 ? 22 : 37)) * 64 + lane, row = j / 5, col = j % 5;
-      return static_cast<uint32_t>(row) * Lqp * 2 + (col < 4 ? col : 0) * 16;
+    case kSrcLD: return l < 16 ? static_cast<uint32_t>(l) * 16u : kPastEnd;
+    case kSrcB:
+      return l < 16 ? static_cast<uint32_t>(l) * 16u
+           : l < 32 ? static_cast<uint32_t>(nqt) * 1024u + static_cast<uint32_t>(l - 16) * 16u : kPastEnd;
+    case kSrcQT: {
+      const int blk = 3 * w + j - 7;
+      return static_cast<uint32_t>(blk_row(blk, l, 64)) * static_cast<uint32_t>(Lqp) * 2u +
+             static_cast<uint32_t>(blk_x(blk, l, 64));
     }
-    case kRegL: case kRegD: return lane < 8 ? lane * 16u : 0u;
-    default:  // visibility words: lanes 0..15 the first k-tile's 32 rows, 16..31 the second's
-      return lane < 16 ? lane * 16u : lane < 32 ? 1024u + (lane - 16) * 16u : 0u;
+    default: {
+      const int blk = 2 * w + j - 10;
+      return static_cast<uint32_t>(blk_row(blk, l, 64)) * static_cast<uint32_t>(Lqp) * 2u +
+             static_cast<uint32_t>(blk_x(blk, l, 64));
+    }
   }
 }
-// the chunk's uniform offset into region reg: q0 its first query, tile the byte
-// offset of the visibility words of (its q-tile, the workgroup's first k-tile),
-// c the chunk's index in its q-tile
-constexpr uint32_t a_soff(int reg, uint32_t q0, uint32_t tile, int c) {
-  return reg == kRegQ ? q0 * (kDqk * 2) : reg == kRegO ? q0 * (kDv * 2)
-       : reg == kRegQT || reg == kRegOT ? q0 * 2 : reg == kRegB ? tile + static_cast<uint32_t>(c) * (kQC * 8) : q0 * 4;
-}
+
+// ---- reads of the compute (lane l: li = l % 32, hi = l / 32), LDS byte in the slot
+// S = Q K^T, operand chunk s (dims 16s .. 16s+15): row li, bytes 32s + 16hi .. +16
+constexpr int rd_q(int s, int li, int hi) { return kF_Q + region_byte(li, 32 * s + 16 * hi, 384); }
+// dP = dO V^T, operand chunk s (dims 16s ..)
+constexpr int rd_o(int s, int li, int hi) { return kF_O + region_byte(li, 32 * s + 16 * hi, 256); }
+// dK += dS^T Q: Q^T row 32nt + li, positions 16kk + 8hi .. +8 of the chunk's 32 (relabelled) queries
+constexpr int rd_qt(int nt, int kk, int li, int hi) { return kT_QT + region_byte(32 * nt + li, 32 * kk + 16 * hi, 64); }
+constexpr int rd_ot(int nt, int kk, int li, int hi) { return kT_OT + region_byte(32 * nt + li, 32 * kk + 16 * hi, 64); }
+// four consecutive floats: queries 8g + 4hi .. +3 (accumulator rows 4g .. 4g+3)
+constexpr int rd_nl(int g, int hi) { return kF_LD + (8 * g + 4 * hi) * 4; }
+constexpr int rd_nd(int g, int hi) { return kF_LD + 128 + (8 * g + 4 * hi) * 4; }
+// the visibility word (32 query bits) of key kl (0..63) of k-tile t of the workgroup
+constexpr int rd_word(int t, int kl) { return kF_B + t * 256 + kl * 4; }
 
 }  // namespace dflash

@@ -81,6 +81,10 @@ struct AttnBwdArgs {
   uint16_t* knT;                          // [B*H, 128, Lkp]
   uint16_t* krT;                          // [B, 64, Lkp]
   float* rope_part;                       // [B*H, Lk, 64] per-head k_rope gradients
+  float* ld;                              // [B*H, Lqp/32, 64]: per 32-query chunk, -lse*log2(e) (-inf for
+                                          //   dead or padded rows), then -D
+  uint32_t* bitsT;                        // [B, nkt, nqt, 4, 64] visibility of class-2 tiles by key: word
+                                          //   (c, k) bit i = query 32c + i of the q-tile sees key k
   int B, H, Lq, Lk, nqt, nkt, Lqp, Lkp;
   float scale;
 };
@@ -162,6 +166,8 @@ hipError_t launch_block_occupancy(const OccupancyArgs& a, hipStream_t s);
 // Rewrite the lists so every k-tile is visited (empty tiles as class 3); debug/verification mode.
 hipError_t launch_lists_all_tiles(const OccupancyArgs& a, hipStream_t s);
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s);
+// dK, dV and the per-head k_rope parts (with the transposed visibility words they read)
+hipError_t launch_bwd_dkdv(const AttnBwdArgs& a, hipStream_t s);
 hipError_t launch_expand_f32(const ExpandArgs& a, hipStream_t s);
 
 }  // namespace dflash

@@ -1,13 +1,18 @@
 """The global -> LDS copy plan of the backward's dK/dV kernel, walked on the CPU.
 
-The kernel stages each 32-query chunk (q, dout, their transposes, the row
-normalisers, D and the visibility words) with 50 copy instructions of 64 lanes x
-16 bytes whose per-lane source offsets are fixed for the kernel (the header
-csrc/bwd_plan.h, compiled here with the host compiler).  This test replays every
-copy of a stage and checks that each byte the kernel's compute step reads holds
-the byte of the source it expects, and that no LDS byte receives two different
-source bytes.  The expected layout is written out below from the compute step's
-reads, not from the plan.
+The kernel stages each 32-query chunk in two parts (q and dout rows, exponent
+offsets, -D and visibility words; the transposed q and dout) with 12 copy
+instructions per wave of 64 lanes x 16 bytes, whose per-lane source offsets are
+fixed for the kernel (the header csrc/bwd_plan.h, compiled here with the host
+compiler).  This test replays the copies of all four waves and checks that
+
+  * no LDS byte of a slot receives two different source bytes, and lanes with
+    nothing to copy read past the end of every resource;
+  * every 16-byte operand read of the compute (the header's read addresses, the
+    ones the kernel uses) finds the bytes of the operand the MFMA needs there,
+    with the operand written out below from the MFMA's lane layout, not from the
+    plan: lane l of a 32x32x16 MFMA supplies row/column l % 32 and the 8
+    reduction indices 8 (l / 32) .. +8 of a 16-wide chunk.
 """
 import os
 import subprocess
@@ -24,21 +29,32 @@ DUMP = r"""
 #include "bwd_plan.h"
 using namespace dflash;
 int main(int argc, char** argv) {
-  const int Lqp = atoi(argv[1]);
-  const unsigned q0 = strtoul(argv[2], 0, 10), tile = strtoul(argv[3], 0, 10);
-  const int c = atoi(argv[4]);
-  printf("%d %d %d %d %d %d %d %d %d %d %d %d %d\n", kA_Q, kA_O, kA_QT, kA_OT, kA_L, kA_D, kA_B, kA_Stage,
-         kA_Blocks, kSQ, kSO, kSQT, kQC);
-  for (int blk = 0; blk < kA_Blocks; ++blk) {
-    const int reg = a_region(blk);
-    for (int lane = 0; lane < 64; ++lane)
-      printf("%d %d %d %u\n", blk, lane, reg, a_voff(blk, lane, Lqp) + a_soff(reg, q0, tile, c));
+  const int Lqp = atoi(argv[1]), nqt = atoi(argv[2]);
+  printf("%d %d %d %d %d %d %d %d %d %u\n", kF_Q, kF_O, kF_LD, kF_B, kF_Slot, kT_QT, kT_OT, kT_Slot,
+         kCopiesPerStep, kPastEnd);
+  for (int w = 0; w < kKvWaves; ++w)
+    for (int j = 0; j < kCopiesPerStep; ++j)
+      for (int l = 0; l < 64; ++l)
+        printf("C %d %d %d %d %d %d %u\n", w, j, l, f_part(j) ? 1 : 0, src_region(j), dst_base(w, j) + 16 * l,
+               voff(w, j, l, Lqp, nqt));
+  for (int l = 0; l < 64; ++l) {
+    const int li = l % 32, hi = l / 32;
+    for (int s = 0; s < 12; ++s) printf("R q %d %d %d\n", l, s, rd_q(s, li, hi));
+    for (int s = 0; s < 8; ++s) printf("R o %d %d %d\n", l, s, rd_o(s, li, hi));
+    for (int nt = 0; nt < 6; ++nt)
+      for (int kk = 0; kk < 2; ++kk) printf("R qt %d %d %d\n", l, 2 * nt + kk, rd_qt(nt, kk, li, hi));
+    for (int nt = 0; nt < 4; ++nt)
+      for (int kk = 0; kk < 2; ++kk) printf("R ot %d %d %d\n", l, 2 * nt + kk, rd_ot(nt, kk, li, hi));
+    for (int g = 0; g < 4; ++g) printf("R nl %d %d %d\n", l, g, rd_nl(g, hi));
+    for (int g = 0; g < 4; ++g) printf("R nd %d %d %d\n", l, g, rd_nd(g, hi));
   }
+  for (int t = 0; t < 2; ++t)
+    for (int k = 0; k < 64; ++k) printf("R w %d %d %d\n", t, k, rd_word(t, k));
   return 0;
 }
 """
 
-REG_Q, REG_O, REG_QT, REG_OT, REG_L, REG_D, REG_B = range(7)
+SRC_Q, SRC_O, SRC_LD, SRC_B, SRC_QT, SRC_OT = range(6)
 
 
 @pytest.fixture(scope="module")
@@ -50,46 +66,84 @@ def dump_exe(tmp_path_factory):
     return str(exe)
 
 
-def _plan(exe, Lqp, q0, tile, c):
-    out = subprocess.run([exe, str(Lqp), str(q0), str(tile), str(c)], check=True, capture_output=True,
-                         text=True).stdout.split("\n")
-    consts = [int(x) for x in out[0].split()]
-    rows = np.array([[int(x) for x in l.split()] for l in out[1:] if l.strip()], dtype=np.int64)
-    return consts, rows
+def _plan(exe, Lqp, nqt):
+    out = subprocess.run([exe, str(Lqp), str(nqt)], check=True, capture_output=True, text=True).stdout
+    lines = out.split("\n")
+    consts = [int(x) for x in lines[0].split()]
+    copies, reads = [], {}
+    for l in lines[1:]:
+        f = l.split()
+        if not f:
+            continue
+        if f[0] == "C":
+            copies.append(tuple(int(x) for x in f[1:]))
+        else:
+            reads[(f[1], int(f[2]), int(f[3]))] = int(f[4])
+    return consts, copies, reads
 
 
-def _expected(consts, Lqp, q0, tile, c):
-    """(LDS byte, region, source byte) of every byte the compute step reads."""
-    A_Q, A_O, A_QT, A_OT, A_L, A_D, A_B, _, _, SQ, SO, SQT, QC = consts
-    exp = []
-    for r in range(QC):                                   # q rows: 192 bf16 = 384 bytes
-        exp += [(A_Q + r * SQ + x, REG_Q, (q0 + r) * 384 + x) for x in range(384)]
-        exp += [(A_O + r * SO + x, REG_O, (q0 + r) * 256 + x) for x in range(256)]
-    for d in range(192):                                  # q^T rows: this chunk's 32 queries
-        exp += [(A_QT + d * SQT + x, REG_QT, d * Lqp * 2 + q0 * 2 + x) for x in range(64)]
-    for d in range(128):
-        exp += [(A_OT + d * SQT + x, REG_OT, d * Lqp * 2 + q0 * 2 + x) for x in range(64)]
-    exp += [(A_L + x, REG_L, q0 * 4 + x) for x in range(4 * QC)]
-    exp += [(A_D + x, REG_D, q0 * 4 + x) for x in range(4 * QC)]
-    for t in range(2):                                    # the workgroup's two k-tiles
-        for r in range(QC):
-            exp += [(A_B + (t * QC + r) * 8 + x, REG_B, tile + t * 128 * 8 + c * QC * 8 + r * 8 + x)
-                    for x in range(8)]
-    return exp
-
-
-@pytest.mark.parametrize("Lqp,qt,c,tile", [(128, 0, 0, 0), (384, 1, 3, 7 * 1024), (4096, 17, 2, 123 * 1024)])
-def test_dkdv_copy_plan_delivers_every_read_byte(dump_exe, Lqp, qt, c, tile):
-    q0 = qt * 128 + c * 32
-    consts, rows = _plan(dump_exe, Lqp, q0, tile, c)
-    stage = consts[7]
-    assert consts[8] * 1024 == stage and rows.shape[0] == consts[8] * 64
-    written = {}
-    for blk, lane, reg, off in rows:
+def _slots(consts, copies):
+    """LDS byte -> (source region, source byte) per part, from replaying every copy."""
+    past_end = consts[9]
+    parts = {0: {}, 1: {}}
+    for w, j, l, fpart, reg, dst, vo in copies:
+        if vo >= past_end:
+            continue                                   # reads zeros: nothing lands that a read may use
+        slot = parts[1 if fpart else 0]
         for x in range(16):
-            dst = blk * 1024 + lane * 16 + x
-            assert 0 <= dst < stage
-            src = (reg, off + x)
-            assert written.setdefault(dst, src) == src, f"LDS byte {dst} gets two sources"
-    for dst, reg, off in _expected(consts, Lqp, q0, tile, c):
-        assert written.get(dst) == (reg, off), f"LDS byte {dst}: want {(reg, off)}, plan gives {written.get(dst)}"
+            src = (reg, vo + x)
+            assert slot.setdefault(dst + x, src) == src, f"LDS byte {dst + x} gets two sources"
+    return parts[1], parts[0]
+
+
+@pytest.mark.parametrize("Lqp,nqt", [(128, 1), (384, 3), (4096, 32)])
+def test_dkdv_copy_plan_delivers_every_operand(dump_exe, Lqp, nqt):
+    consts, copies, reads = _plan(dump_exe, Lqp, nqt)
+    F_Q, F_O, F_LD, F_B, F_SLOT, T_QT, T_OT, T_SLOT, NCOPY, PAST_END = consts
+    assert len(copies) == 4 * NCOPY * 64
+    F, T = _slots(consts, copies)
+    assert all(0 <= b < F_SLOT for b in F) and all(0 <= b < T_SLOT for b in T)
+
+    def check(slot, lds, region, src0, what):
+        for x in range(16):
+            got = slot.get(lds + x)
+            assert got == (region, src0 + x), f"{what}: LDS byte {lds + x} holds {got}, want {(region, src0 + x)}"
+
+    for l in range(64):
+        li, hi = l % 32, l // 32
+        # S = Q K^T: A operand = q row li, dims 16s + 8hi .. +8 (bf16); chunk offset q0 * 384
+        for s in range(12):
+            check(F, reads[("q", l, s)], SRC_Q, li * 384 + (16 * s + 8 * hi) * 2, f"q lane {l} chunk {s}")
+        for s in range(8):
+            check(F, reads[("o", l, s)], SRC_O, li * 256 + (16 * s + 8 * hi) * 2, f"dout lane {l} chunk {s}")
+        # dK += dS^T Q: B operand = Q^T row d = 32nt + li, chunk positions 16kk + 8hi .. +8
+        for nt in range(6):
+            for kk in range(2):
+                d = 32 * nt + li
+                check(T, reads[("qt", l, 2 * nt + kk)], SRC_QT, d * Lqp * 2 + (16 * kk + 8 * hi) * 2,
+                      f"q^T lane {l} tile {nt} half {kk}")
+        for nt in range(4):
+            for kk in range(2):
+                d = 32 * nt + li
+                check(T, reads[("ot", l, 2 * nt + kk)], SRC_OT, d * Lqp * 2 + (16 * kk + 8 * hi) * 2,
+                      f"dout^T lane {l} tile {nt} half {kk}")
+        # accumulator rows 4g .. 4g+3 <-> queries 8g + 4hi .. +3: their offsets, then their -D
+        for g in range(4):
+            check(F, reads[("nl", l, g)], SRC_LD, (8 * g + 4 * hi) * 4, f"offsets lane {l} group {g}")
+            check(F, reads[("nd", l, g)], SRC_LD, 128 + (8 * g + 4 * hi) * 4, f"-D lane {l} group {g}")
+    # the word of key k of k-tile t: k-tiles nqt * 1024 bytes apart, 4 bytes per key
+    for t in range(2):
+        for k in range(64):
+            lds = reads[("w", t, k)]
+            for x in range(4):
+                assert F.get(lds + x) == (SRC_B, t * nqt * 1024 + k * 4 + x), f"word of tile {t} key {k}"
+
+
+def test_dkdv_plan_is_the_same_for_every_wave(dump_exe):
+    """Each wave issues the same 12 copy instructions (the same regions, in the
+    same order), so the kernel's wait counts are one constant for all waves."""
+    _, copies, _ = _plan(dump_exe, 256, 2)
+    regs = {}
+    for w, j, l, fpart, reg, dst, vo in copies:
+        regs.setdefault(w, {})[j] = (fpart, reg)
+    assert all(regs[w] == regs[0] for w in range(4))
