@@ -54,50 +54,11 @@ constexpr int kQC = 32;                         // queries per prep_q workgroup
 // LDS row strides (bytes): row + 16, so 16-lane column reads hit distinct banks
 constexpr int kSQ = kDqk * 2 + 16;              // 400: q / k rows
 constexpr int kSO = kDv * 2 + 16;               // 272: dout / v rows
-constexpr int kSKT = kTileN * 2 + 16;           // 144: transposed k rows (64 keys)
-// dQ stage: K, V, K^T
-constexpr int kB_K = 0;
-constexpr int kB_V = kB_K + kTileN * kSQ;
-constexpr int kB_KT = kB_V + kTileN * kSO;
-constexpr int kB_Stage = kB_KT + kDqk * kSKT;
-static_assert(2 * kB_Stage <= 160 * 1024, "LDS budget");
 
 // Position k of a 16-entry group holds entry relabel16(k): bits 2 and 3 swapped.
 __device__ __forceinline__ int relabel16(int k) { return (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
 __device__ __forceinline__ u32x4_t zero4() { return u32x4_t{0u, 0u, 0u, 0u}; }
-
-// Buffer resource over `bytes` bytes at p: loads at offsets >= bytes return zeros,
-// which is how rows past the end of a tensor read as zero without a compare.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, size_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), 0x00020000);
-}
-// 16 bytes at voffset (per lane) + soffset (uniform)
-__device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), 0));
-}
-
-__device__ __forceinline__ bf16x8_t lds_frag(const char* p) { return as_bf16x8(*reinterpret_cast<const u32x4_t*>(p)); }
-
-// 8 floats -> one bf16x8 operand (round to nearest even)
-__device__ __forceinline__ bf16x8_t pack8(const float* x) {
-  const u32x4_t w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                     pack_bf16x2(x[6], x[7])};
-  return as_bf16x8(w);
-}
-
-__device__ __forceinline__ f32x16_t zero16() {
-  f32x16_t z;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) z[r] = 0.f;
-  return z;
-}
-
-template <bool MASK_BF16>
-__device__ __forceinline__ float mask_value(const void* mask, size_t idx) {
-  if (MASK_BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(mask)[idx]);
-  return static_cast<const float*>(mask)[idx];
-}
 
 // ---------------------------------------------------------------- 1. prep_q
 // grid (Lqp / 32, B*H): D, lse2 and the transposed q / dout of 32 queries.
@@ -213,194 +174,7 @@ __global__ void __launch_bounds__(kThreads) bwd_prep_k(AttnBwdArgs a) {
 
 // ---------------------------------------------------------------- 3. dK / dV: bwd_dkdv.hip
 
-// ---------------------------------------------------------------- 4. dQ
-template <bool MASK_BF16>
-__global__ void __launch_bounds__(kThreads) bwd_dq(AttnBwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kB_Stage];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int li = lane & 31, hi = lane >> 5;
-  const int rank = blockIdx.x / a.H, h = blockIdx.x % a.H;
-  const int row = a.order ? a.order[rank] : rank;      // b * nqt + qt
-  const int b = row / a.nqt, qt = row % a.nqt;
-  const size_t bh = static_cast<size_t>(b) * a.H + h;
-  const int qi = qt * kTileM + 32 * w + li;            // this lane's query
-  const bool q_ok = qi < a.Lq;
-
-  bf16x8_t qreg[12], oreg[8];
-#pragma unroll
-  for (int s = 0; s < 12; ++s)
-    qreg[s] = as_bf16x8(q_ok ? ldg16(a.q + (bh * a.Lq + qi) * kDqk + 16 * s + 8 * hi) : zero4());
-#pragma unroll
-  for (int s = 0; s < 8; ++s)
-    oreg[s] = as_bf16x8(q_ok ? ldg16(a.dout + (bh * a.Lq + qi) * kDv + 16 * s + 8 * hi) : zero4());
-  const float lse2 = a.lse2[bh * a.Lqp + qi];
-  const float dd = a.dd[bh * a.Lqp + qi];
-
-  f32x16_t dq[6];
-#pragma unroll
-  for (int i = 0; i < 6; ++i) dq[i] = zero16();
-
-  const int n = a.lists ? a.counts[row] : a.nkt;
-  const int32_t* list = a.lists ? a.lists + static_cast<size_t>(row) * a.nkt : nullptr;
-  auto entry = [&](int e) -> int { return list ? list[e] : (e | (1 << 24)); };
-
-  // staging: per-lane byte offsets are fixed, the tile moves the uniform offset
-  const __amdgpu_buffer_rsrc_t r_kn = rsrc(a.kn + bh * a.Lk * kDn, static_cast<size_t>(a.Lk) * kDn * 2);
-  const __amdgpu_buffer_rsrc_t r_kr = rsrc(a.kr + static_cast<size_t>(b) * a.Lk * kDr, static_cast<size_t>(a.Lk) * kDr * 2);
-  const __amdgpu_buffer_rsrc_t r_v = rsrc(a.v + bh * a.Lk * kDv, static_cast<size_t>(a.Lk) * kDv * 2);
-  const __amdgpu_buffer_rsrc_t r_knt = rsrc(a.knT + bh * kDn * a.Lkp, static_cast<size_t>(kDn) * a.Lkp * 2);
-  const __amdgpu_buffer_rsrc_t r_krt = rsrc(a.krT + static_cast<size_t>(b) * kDr * a.Lkp, static_cast<size_t>(kDr) * a.Lkp * 2);
-  // chunk c of this thread's i-th load: K nope rows 64 x 16 (i < 4), K rope rows 64 x 8 (2),
-  // V rows 64 x 16 (4), K^T nope rows 128 x 8 (4), K^T rope rows 64 x 8 (2)
-  u32x4_t pre[16];
-  // issued every step (past the last tile: an offset beyond every resource, zeros
-  // and no traffic), so the compiler's wait counts for the loads around it are exact
-  constexpr uint32_t kPastEnd = 0x80000000u;
-  auto prefetch = [&](int kt, bool live) {
-    const uint32_t k0 = static_cast<uint32_t>(kt) * kTileN;
-    const uint32_t so_kn = live ? k0 * (kDn * 2) : kPastEnd, so_kr = live ? k0 * (kDr * 2) : kPastEnd;
-    const uint32_t so_v = live ? k0 * (kDv * 2) : kPastEnd, so_t = live ? k0 * 2 : kPastEnd;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ci = t + kThreads * i;
-      pre[i] = bload16(r_kn, (ci >> 4) * (kDn * 2) + (ci & 15) * 16, so_kn);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ci = t + kThreads * i;
-      pre[4 + i] = bload16(r_kr, (ci >> 3) * (kDr * 2) + (ci & 7) * 16, so_kr);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ci = t + kThreads * i;
-      pre[6 + i] = bload16(r_v, (ci >> 4) * (kDv * 2) + (ci & 15) * 16, so_v);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ci = t + kThreads * i;
-      pre[10 + i] = bload16(r_knt, (ci >> 3) * (a.Lkp * 2) + (ci & 7) * 16, so_t);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ci = t + kThreads * i;
-      pre[14 + i] = bload16(r_krt, (ci >> 3) * (a.Lkp * 2) + (ci & 7) * 16, so_t);
-    }
-  };
-  auto commit = [&](char* st) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ci = t + kThreads * i;
-      *reinterpret_cast<u32x4_t*>(st + kB_K + (ci >> 4) * kSQ + (ci & 15) * 16) = pre[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ci = t + kThreads * i;
-      *reinterpret_cast<u32x4_t*>(st + kB_K + (ci >> 3) * kSQ + kDn * 2 + (ci & 7) * 16) = pre[4 + i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ci = t + kThreads * i;
-      *reinterpret_cast<u32x4_t*>(st + kB_V + (ci >> 4) * kSO + (ci & 15) * 16) = pre[6 + i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ci = t + kThreads * i;
-      *reinterpret_cast<u32x4_t*>(st + kB_KT + (ci >> 3) * kSKT + (ci & 7) * 16) = pre[10 + i];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ci = t + kThreads * i;
-      *reinterpret_cast<u32x4_t*>(st + kB_KT + (kDn + (ci >> 3)) * kSKT + (ci & 7) * 16) = pre[14 + i];
-    }
-  };
-
-  const float scale_log2 = a.scale * kLog2e;
-  // visibility word of this lane's query in a class-2 tile (zero elsewhere): loaded
-  // unconditionally through a resource, before the next tile's staging loads are
-  // issued, so the wait for it is a count that leaves those in flight
-  const __amdgpu_buffer_rsrc_t r_bits =
-      rsrc(a.bits, a.bits ? static_cast<size_t>(a.B) * a.nqt * a.nkt * kTileM * 8 : 0);
-  const uint32_t vo_bits = q_ok ? static_cast<uint32_t>(32 * w + li) * 8 : kPastEnd;
-  auto vis_word = [&](int kt, int cls) -> uint64_t {
-    const uint32_t so = cls == 2 ? static_cast<uint32_t>((static_cast<size_t>(row) * a.nkt + kt) * kTileM * 8) : kPastEnd;
-    const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(r_bits, vo_bits, so, 0);
-    return __builtin_bit_cast(uint64_t, v2);
-  };
-  auto compute = [&](const char* st, int kt, int cls, uint64_t word) {
-    bf16x8_t bS[4];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      f32x16_t S = zero16(), dP = zero16();
-#pragma unroll
-      for (int s = 0; s < 12; ++s)
-        S = mfma32(lds_frag(st + kB_K + (32 * half + li) * kSQ + (16 * s + 8 * hi) * 2), qreg[s], S);
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        dP = mfma32(lds_frag(st + kB_V + (32 * half + li) * kSO + (16 * s + 8 * hi) * 2), oreg[s], dP);
-      __builtin_amdgcn_sched_barrier(0);
-      float madd[16];                                 // log2(e) * mask values (general tiles only)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) madd[r] = 0.f;
-      if (cls == 3 && a.mask) {
-        for (int r = 0; r < 16; ++r) {
-          const int kj = kt * kTileN + 32 * half + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (kj < a.Lk && q_ok)
-            madd[r] = mask_value<MASK_BF16>(a.mask, (static_cast<size_t>(b) * a.Lq + qi) * a.Lk + kj) * kLog2e;
-        }
-      }
-      float ds[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kl = 32 * half + 8 * (r >> 2) + 4 * hi + (r & 3);   // key within the tile
-        bool vis = kt * kTileN + kl < a.Lk;
-        if (cls == 2) vis = vis && ((word >> kl) & 1ull);
-        const float pr = vis ? __builtin_amdgcn_exp2f(S[r] * scale_log2 - lse2 + madd[r]) : 0.f;
-        ds[r] = pr * (dP[r] - dd);
-      }
-      bS[2 * half] = pack8(ds);
-      bS[2 * half + 1] = pack8(ds + 8);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int mt = 0; mt < 6; ++mt) {
-      const char* rowp = st + kB_KT + (32 * mt + li) * kSKT + 16 * hi;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) dq[mt] = mfma32(lds_frag(rowp + 32 * kk), bS[kk], dq[mt]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  if (n > 0) {
-    int e0 = entry(0);
-    prefetch(e0 & 0xFFFFFF, true);
-    commit(smem);
-    __syncthreads();
-    for (int e = 0; e < n; ++e) {
-      const bool more = e + 1 < n;
-      const uint64_t word = vis_word(e0 & 0xFFFFFF, e0 >> 24);
-      const int e1 = more ? entry(e + 1) : 0;
-      prefetch(e1 & 0xFFFFFF, more);
-      compute(smem + (e & 1) * kB_Stage, e0 & 0xFFFFFF, e0 >> 24, word);
-      if (!more) break;
-      commit(smem + ((e + 1) & 1) * kB_Stage);
-      __syncthreads();
-      e0 = e1;
-    }
-  }
-
-  // accumulator row r <-> dim 32*mt + 8*(r/4) + 4*hi + r%4, column <-> this lane's query
-  if (q_ok) {
-    uint16_t* op = a.dq + (bh * a.Lq + qi) * kDqk;
-#pragma unroll
-    for (int mt = 0; mt < 6; ++mt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2_t w2 = {pack_bf16x2(dq[mt][4 * g] * a.scale, dq[mt][4 * g + 1] * a.scale),
-                            pack_bf16x2(dq[mt][4 * g + 2] * a.scale, dq[mt][4 * g + 3] * a.scale)};
-        *reinterpret_cast<u32x2_t*>(op + 32 * mt + 8 * g + 4 * hi) = w2;
-      }
-  }
-}
+// ---------------------------------------------------------------- 4. dQ: bwd_dq.hip
 
 // ---------------------------------------------------------------- 5. dk_rope
 // One thread per 4 consecutive dims of one (b, key): sum over heads in order.
@@ -430,10 +204,7 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(bwd_prep_k, dim3(a.Lkp / kTileN, bh), dim3(kThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = launch_bwd_dkdv(a, s)) != hipSuccess) return e;
-  const dim3 gq(static_cast<unsigned>(a.B) * a.nqt * a.H);
-  if (a.mask && a.mask_bf16) hipLaunchKernelGGL(bwd_dq<true>, gq, dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL(bwd_dq<false>, gq, dim3(kThreads), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_bwd_dq(a, s)) != hipSuccess) return e;
   const int64_t n4 = static_cast<int64_t>(a.B) * a.Lk * (kDr / 4);
   hipLaunchKernelGGL(bwd_rope_reduce, dim3(static_cast<unsigned>((n4 + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, a);
   return hipGetLastError();

@@ -124,23 +124,19 @@ bwd_dkdv(AttnBwdArgs a) {
 
   // ---- the wave's K and V operands (B operands of S = Q K^T and dP = dO V^T:
   // key li, dims 16s + 8hi .. +8), moved to accumulator registers
+  // (loaded here, moved once the first chunk list is built: the loads and the
+  // tile classes of the list travel together)
   u32x4_t kq[kDqk / 16], vq[kDv / 16];
-  {
-    u32x4_t kv[kDqk / 16], vv[kDv / 16];
+  u32x4_t kv[kDqk / 16], vv[kDv / 16];
 #pragma unroll
-    for (int s = 0; s < kDqk / 16; ++s) {
-      kv[s] = zero4();
-      if (key_ok) kv[s] = s < kDn / 16 ? ldg16(a.kn + (bh * a.Lk + key) * kDn + 16 * s + 8 * hi)
-                                        : ldg16(a.kr + (static_cast<size_t>(b) * a.Lk + key) * kDr +
-                                                16 * (s - kDn / 16) + 8 * hi);
-    }
-#pragma unroll
-    for (int s = 0; s < kDv / 16; ++s) vv[s] = key_ok ? ldg16(a.v + (bh * a.Lk + key) * kDv + 16 * s + 8 * hi) : zero4();
-#pragma unroll
-    for (int s = 0; s < kDqk / 16; ++s) asm volatile("" : "=a"(kq[s]) : "0"(kv[s]));
-#pragma unroll
-    for (int s = 0; s < kDv / 16; ++s) asm volatile("" : "=a"(vq[s]) : "0"(vv[s]));
+  for (int s = 0; s < kDqk / 16; ++s) {
+    kv[s] = zero4();
+    if (key_ok) kv[s] = s < kDn / 16 ? ldg16(a.kn + (bh * a.Lk + key) * kDn + 16 * s + 8 * hi)
+                                      : ldg16(a.kr + (static_cast<size_t>(b) * a.Lk + key) * kDr +
+                                              16 * (s - kDn / 16) + 8 * hi);
   }
+#pragma unroll
+  for (int s = 0; s < kDv / 16; ++s) vv[s] = key_ok ? ldg16(a.v + (bh * a.Lk + key) * kDv + 16 * s + 8 * hi) : zero4();
 
   f32x16_t dk[kDqk / 32], dv[kDv / 32];
 #pragma unroll
@@ -188,10 +184,10 @@ bwd_dkdv(AttnBwdArgs a) {
   lds_int_t* const list = (lds_int_t*)(lds + kList);
   lds_int_t* const cnt = (lds_int_t*)(lds + kCnt);
 
-  for (int qb = 0; qb < a.nqt; qb += kListMax) {
+  // ---- chunk list of the window of q-tiles from qb: the q-tiles with a non-empty
+  // tile among the two k-tiles, entry = q-tile | class(kt0) << 24 | class(kt0 + 1) << 28
+  auto build_list = [&](int qb) -> int {
     const int qe = min(a.nqt, qb + kListMax);
-    // ---- chunk list of the window: q-tiles with a non-empty tile among the two
-    // k-tiles, entry = q-tile | class(kt0) << 24 | class(kt0 + 1) << 28
     int n = 0;
     for (int base = qb; base < qe; base += kThreads) {
       const int qt = base + t;
@@ -217,6 +213,15 @@ bwd_dkdv(AttnBwdArgs a) {
       n += tot;
       __syncthreads();
     }
+    return n;
+  };
+  int n = build_list(0);
+#pragma unroll
+  for (int s = 0; s < kDqk / 16; ++s) asm volatile("" : "=a"(kq[s]) : "0"(kv[s]));
+#pragma unroll
+  for (int s = 0; s < kDv / 16; ++s) asm volatile("" : "=a"(vq[s]) : "0"(vv[s]));
+
+  for (int qb = 0; qb < a.nqt; qb += kListMax, n = qb < a.nqt ? build_list(qb) : 0) {
     const int nch = 4 * n;                              // every q-tile in four chunks
     if (nch == 0) continue;
     // entry of chunk j (0 past the end: no copy, class 0)

@@ -122,4 +122,79 @@ constexpr int rd_nd(int g, int hi) { return kF_LD + 128 + (8 * g + 4 * hi) * 4; 
 // the visibility word (32 query bits) of key kl (0..63) of k-tile t of the workgroup
 constexpr int rd_word(int t, int kl) { return kF_B + t * 256 + kl * 4; }
 
+// ======================================================================== dQ
+// The dQ kernel walks the 32-key steps of its q-tile's tile list (two per
+// 64-key tile).  Step m's data is split in two parts: the F part (k_nope and
+// k_rope rows, v rows, and the tile's visibility words: 128 queries x 64 bits)
+// feeds S^T and dP^T of step m, computed in step m - 1, whose first K operands
+// are read at the end of step m - 2; the T part (the transposed k_nope and
+// k_rope of the step's 32 keys) feeds dQ of step m in step m.  F(m) is copied in
+// step m - 4 (ring of four slots), T(m) in step m - 2 (ring of three).
+constexpr int kQ_KN = 0;                         // 32 rows x 256 B
+constexpr int kQ_KR = kQ_KN + 32 * kDn * 2;      // 32 rows x 128 B   (8192)
+constexpr int kQ_V = kQ_KR + 32 * kDr * 2;       // 32 rows x 256 B   (12288)
+constexpr int kQ_B = kQ_V + 32 * kDv * 2;        // 128 x 8 B          (20480)
+constexpr int kQF_Slot = kQ_B + 1024;            // 21504
+constexpr int kQ_KTN = 0;                        // 128 rows x 64 B
+constexpr int kQ_KTR = kQ_KTN + kDn * 64;        // 64 rows x 64 B     (8192)
+constexpr int kQT_Slot = kQ_KTR + kDr * 64;      // 12288
+constexpr int kQFSlots = 4;
+constexpr int kQTSlots = 3;
+// copy instructions per wave and step: 2 k_nope, 1 k_rope, 2 v, words (F); 2 k_nope^T, 1 k_rope^T (T)
+constexpr int kQCopiesPerStep = 9;
+
+// copy plan: instruction j (0..8) of wave w; the step's uniform offsets (key0 its
+// first key): k_nope and v: key0 * 256; k_rope: key0 * 128; words: the tile's
+// 1 KiB; transposed rows: key0 * 2 (rows Lkp * 2 bytes apart)
+enum : int { kSrcKN, kSrcKR, kSrcV, kSrcBits, kSrcKTN, kSrcKTR };
+constexpr int q_src_region(int j) {
+  return j < 2 ? kSrcKN : j == 2 ? kSrcKR : j < 5 ? kSrcV : j == 5 ? kSrcBits : j < 8 ? kSrcKTN : kSrcKTR;
+}
+constexpr bool q_f_part(int j) { return j < 6; }
+constexpr int q_dst_base(int w, int j) {
+  return j < 2 ? kQ_KN + (2 * w + j) * 1024
+       : j == 2 ? kQ_KR + w * 1024
+       : j < 5 ? kQ_V + (2 * w + j - 3) * 1024
+       : j == 5 ? kQ_B
+       : j < 8 ? kQ_KTN + (2 * w + j - 6) * 1024
+       : kQ_KTR + w * 1024;
+}
+constexpr uint32_t q_voff(int w, int j, int l, int Lkp) {
+  switch (q_src_region(j)) {
+    case kSrcKN: {
+      const int blk = 2 * w + j;
+      return static_cast<uint32_t>(blk_row(blk, l, 256) * 256 + blk_x(blk, l, 256));
+    }
+    case kSrcKR: return static_cast<uint32_t>(blk_row(w, l, 128) * 128 + blk_x(w, l, 128));
+    case kSrcV: {
+      const int blk = 2 * w + j - 3;
+      return static_cast<uint32_t>(blk_row(blk, l, 256) * 256 + blk_x(blk, l, 256));
+    }
+    case kSrcBits: return static_cast<uint32_t>(l) * 16u;
+    case kSrcKTN: {
+      const int blk = 2 * w + j - 6;
+      return static_cast<uint32_t>(blk_row(blk, l, 64)) * static_cast<uint32_t>(Lkp) * 2u +
+             static_cast<uint32_t>(blk_x(blk, l, 64));
+    }
+    default:
+      return static_cast<uint32_t>(blk_row(w, l, 64)) * static_cast<uint32_t>(Lkp) * 2u +
+             static_cast<uint32_t>(blk_x(w, l, 64));
+  }
+}
+// reads (lane l: li = l % 32, hi = l / 32)
+// S^T = K Q^T, A operand chunk s (dims 16s ..): key row li
+constexpr int rd_k(int s, int li, int hi) {
+  return s < kDn / 16 ? kQ_KN + region_byte(li, 32 * s + 16 * hi, kDn * 2)
+                      : kQ_KR + region_byte(li, 32 * (s - kDn / 16) + 16 * hi, kDr * 2);
+}
+// dP^T = V dO^T, A operand chunk s
+constexpr int rd_v(int s, int li, int hi) { return kQ_V + region_byte(li, 32 * s + 16 * hi, kDv * 2); }
+// dQ^T += K^T dS^T: K^T row d = 32mt + li, positions 16kk + 8hi .. +8 of the step's 32 (relabelled) keys
+constexpr int rd_kt(int mt, int kk, int li, int hi) {
+  return 32 * mt + li < kDn ? kQ_KTN + region_byte(32 * mt + li, 32 * kk + 16 * hi, 64)
+                            : kQ_KTR + region_byte(32 * mt + li - kDn, 32 * kk + 16 * hi, 64);
+}
+// the visibility word (64 key bits) of query row ql (0..127) of the tile
+constexpr int rd_qword(int ql) { return kQ_B + ql * 8; }
+
 }  // namespace dflash

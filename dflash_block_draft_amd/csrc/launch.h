@@ -168,6 +168,8 @@ hipError_t launch_lists_all_tiles(const OccupancyArgs& a, hipStream_t s);
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s);
 // dK, dV and the per-head k_rope parts (with the transposed visibility words they read)
 hipError_t launch_bwd_dkdv(const AttnBwdArgs& a, hipStream_t s);
+// dQ
+hipError_t launch_bwd_dq(const AttnBwdArgs& a, hipStream_t s);
 hipError_t launch_expand_f32(const ExpandArgs& a, hipStream_t s);
 
 }  // namespace dflash

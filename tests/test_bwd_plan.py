@@ -147,3 +147,94 @@ def test_dkdv_plan_is_the_same_for_every_wave(dump_exe):
     for w, j, l, fpart, reg, dst, vo in copies:
         regs.setdefault(w, {})[j] = (fpart, reg)
     assert all(regs[w] == regs[0] for w in range(4))
+
+
+DUMP_Q = r"""
+#include <cstdio>
+#include <cstdlib>
+#include "bwd_plan.h"
+using namespace dflash;
+int main(int argc, char** argv) {
+  const int Lkp = atoi(argv[1]);
+  printf("%d %d %d\n", kQF_Slot, kQT_Slot, kQCopiesPerStep);
+  for (int w = 0; w < 4; ++w)
+    for (int j = 0; j < kQCopiesPerStep; ++j)
+      for (int l = 0; l < 64; ++l)
+        printf("C %d %d %d %d %d %d %u\n", w, j, l, q_f_part(j) ? 1 : 0, q_src_region(j), q_dst_base(w, j) + 16 * l,
+               q_voff(w, j, l, Lkp));
+  for (int l = 0; l < 64; ++l) {
+    const int li = l % 32, hi = l / 32;
+    for (int s = 0; s < 12; ++s) printf("R k %d %d %d\n", l, s, rd_k(s, li, hi));
+    for (int s = 0; s < 8; ++s) printf("R v %d %d %d\n", l, s, rd_v(s, li, hi));
+    for (int mt = 0; mt < 6; ++mt)
+      for (int kk = 0; kk < 2; ++kk) printf("R kt %d %d %d\n", l, 2 * mt + kk, rd_kt(mt, kk, li, hi));
+  }
+  for (int q = 0; q < 128; ++q) printf("R w %d 0 %d\n", q, rd_qword(q));
+  return 0;
+}
+"""
+
+SRC_KN, SRC_KR, SRC_V, SRC_BITS, SRC_KTN, SRC_KTR = range(6)
+
+
+@pytest.fixture(scope="module")
+def dump_q_exe(tmp_path_factory):
+    d = tmp_path_factory.mktemp("bwd_plan_q")
+    src, exe = d / "dump.cpp", d / "dump"
+    src.write_text(DUMP_Q)
+    subprocess.run(["g++", "-std=c++17", "-O1", "-I", CSRC, str(src), "-o", str(exe)], check=True)
+    return str(exe)
+
+
+@pytest.mark.parametrize("Lkp", [64, 320, 9216])
+def test_dq_copy_plan_delivers_every_operand(dump_q_exe, Lkp):
+    """The dQ kernel's staging of a 32-key step: k_nope, k_rope and v rows, the
+    tile's 128 visibility words (F part), the transposed k rows (T part)."""
+    out = subprocess.run([dump_q_exe, str(Lkp)], check=True, capture_output=True, text=True).stdout.split("\n")
+    F_SLOT, T_SLOT, NCOPY = (int(x) for x in out[0].split())
+    copies, reads = [], {}
+    for l in out[1:]:
+        f = l.split()
+        if not f:
+            continue
+        if f[0] == "C":
+            copies.append(tuple(int(x) for x in f[1:]))
+        else:
+            reads[(f[1], int(f[2]), int(f[3]))] = int(f[4])
+    assert len(copies) == 4 * NCOPY * 64
+    parts = {0: {}, 1: {}}
+    regs = {}
+    for w, j, l, fpart, reg, dst, vo in copies:
+        regs.setdefault(w, {})[j] = (fpart, reg)
+        slot = parts[fpart]
+        for x in range(16):
+            src = (reg, vo + x)
+            assert slot.setdefault(dst + x, src) == src, f"LDS byte {dst + x} gets two sources"
+    assert all(regs[w] == regs[0] for w in range(4)), "every wave issues the same copy sequence"
+    F, T = parts[1], parts[0]
+    assert all(0 <= b < F_SLOT for b in F) and all(0 <= b < T_SLOT for b in T)
+
+    def check(slot, lds, region, src0, n, what):
+        for x in range(n):
+            got = slot.get(lds + x)
+            assert got == (region, src0 + x), f"{what}: LDS byte {lds + x} holds {got}, want {(region, src0 + x)}"
+
+    for l in range(64):
+        li, hi = l % 32, l // 32
+        # S^T = K Q^T: A operand = key row li, dims 16s + 8hi .. +8 (k_nope dims < 128, then k_rope)
+        for s in range(12):
+            if s < 8:
+                check(F, reads[("k", l, s)], SRC_KN, li * 256 + (16 * s + 8 * hi) * 2, 16, f"k_nope lane {l} chunk {s}")
+            else:
+                check(F, reads[("k", l, s)], SRC_KR, li * 128 + (16 * (s - 8) + 8 * hi) * 2, 16, f"k_rope lane {l} chunk {s}")
+        for s in range(8):
+            check(F, reads[("v", l, s)], SRC_V, li * 256 + (16 * s + 8 * hi) * 2, 16, f"v lane {l} chunk {s}")
+        # dQ^T += K^T dS^T: A operand = K^T row d = 32mt + li, positions 16kk + 8hi .. +8 of the step's keys
+        for mt in range(6):
+            for kk in range(2):
+                d = 32 * mt + li
+                reg, row = (SRC_KTN, d) if d < 128 else (SRC_KTR, d - 128)
+                check(T, reads[("kt", l, 2 * mt + kk)], reg, row * Lkp * 2 + (16 * kk + 8 * hi) * 2, 16,
+                      f"k^T lane {l} tile {mt} half {kk}")
+    for q in range(128):                                  # query row q's 64-bit visibility word
+        check(F, reads[("w", q, 0)], SRC_BITS, q * 8, 8, f"word of query {q}")
