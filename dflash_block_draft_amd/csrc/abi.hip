@@ -503,7 +503,7 @@ dflash_status attn_impl(const void* q, const void* k_nope, const void* k_rope_sh
 struct BwdLayout {
   TileLayout t;
   int64_t Lqp, Lkp;
-  size_t lse2, dd, qT, doT, knT, krT, rope, ld, bitsT, total;
+  size_t qT, doT, knT, krT, rope, ld, bitsT, total;
 };
 
 bool bwd_layout(int64_t B, int64_t H, int64_t Lq, int64_t Lk, BwdLayout* L) {
@@ -515,9 +515,7 @@ bool bwd_layout(int64_t B, int64_t H, int64_t Lq, int64_t Lk, BwdLayout* L) {
       !mul_ok(bh, L->Lkp, &e) || !mul_ok(e, 2 * 128, &e) || !mul_ok(B, L->Lkp * 2 * 64, &f) ||
       !mul_ok(bh, Lk, &g) || !mul_ok(g, 64 * 4, &g) || !mul_ok(B * L->t.nqt, L->t.nkt, &bt) || !mul_ok(bt, 1024, &bt))
     return false;
-  L->lse2 = align_up(L->t.total, 256);
-  L->dd = L->lse2 + align_up(static_cast<size_t>(c), 256);
-  L->qT = L->dd + align_up(static_cast<size_t>(c), 256);
+  L->qT = align_up(L->t.total, 256);
   L->doT = L->qT + align_up(static_cast<size_t>(d), 256);
   L->knT = L->doT + align_up(static_cast<size_t>(a) * 2 * 128, 256);
   L->krT = L->knT + align_up(static_cast<size_t>(e), 256);
@@ -713,8 +711,6 @@ dflash_status dflash_mla_attn_bwd(const void* q, const void* k_nope, const void*
   a.dkn = static_cast<uint16_t*>(dk_nope);
   a.dkr = static_cast<uint16_t*>(dk_rope_shared);
   a.dv = static_cast<uint16_t*>(dv);
-  a.lse2 = reinterpret_cast<float*>(ws + L.lse2);
-  a.dd = reinterpret_cast<float*>(ws + L.dd);
   a.qT = reinterpret_cast<uint16_t*>(ws + L.qT);
   a.doT = reinterpret_cast<uint16_t*>(ws + L.doT);
   a.knT = reinterpret_cast<uint16_t*>(ws + L.knT);

@@ -9,34 +9,21 @@
 //   dq_i = scale * sum_j ds_ij k_j    dk_rope_j = sum over heads of dk_j[Dn:]
 // and the score matrix is never stored: both passes recompute their tile of p.
 //
-// Four launches (one ordered stream, no atomics, bitwise deterministic):
-//  1. prep_q: D, lse in log2 units (+inf for dead or padded rows, so their p is
-//     exactly 0), and transposed copies of q and dout.
+// The launches, on one ordered stream (no atomics: bitwise deterministic):
+//  1. prep_q: per 32-query chunk the exponent offsets -lse log2(e) (-inf for
+//     dead or padded rows, so their p is exactly 0) and -D, and transposed
+//     copies of q and dout.
 //  2. prep_k: transposed copies of k_nope (per head) and k_rope (per row).
-//  3. dkdv: one workgroup per (b, h, 128 keys); wave w owns 32 keys, keeps their
-//     K and V operands in registers and dK (32 x 192) and dV (32 x 128) in
-//     accumulators, and walks the 32-query chunks of every q-tile whose tiles
-//     with these keys are not empty.  S = Q K^T and dP = dO V^T put one key per
-//     lane, which is the A-operand layout of dV += P^T dO and dK += dS^T Q, so
-//     P and dS go from accumulator to operand without moving; the other
-//     operands (q and dout, reduction over queries) come from the transposed
-//     copies with 16-byte LDS reads.  dk_rope is written per head (fp32).
-//  4. dq: one workgroup per (b, q-tile, h) in the forward's ranked order; wave w
-//     owns 32 queries, keeps Q and dO in registers and walks the tile list:
-//     S^T = K Q^T and dP^T = V dO^T put one query per lane, and dS^T is the
-//     B operand of dQ^T += K^T dS^T, with K^T from the transposed copy.
-//  5. rope_reduce: dk_rope = sum over heads of the per-head parts, in head order.
-//
-// Operand staging: dK/dV copies each 32-query chunk global -> LDS through the
-// buffer unit (no staging registers) into a three-stage ring, two chunks ahead;
-// dQ loads each 64-key tile into registers one tile ahead and stores it into the
-// other half of a double buffer.  LDS rows are padded by 16 bytes so the 16-byte
-// column reads of 16 lanes hit distinct banks.  Every staging load is issued
-// unconditionally (past the end: an offset beyond the resource, zeros, no
-// traffic) and the loads the compiler must wait for are issued before them, so
-// no wait in the loops drains the copies in flight.  Masks: class-0 tiles are skipped, class-1 tiles need no
-// mask work, class-2 tiles zero p for keys whose visibility bit is clear,
-// class-3 tiles add the mask values; keys past Lk get p = 0.
+//  3. prep_bits (bwd_dkdv.hip): the visibility words of the masked (class-2)
+//     tiles transposed to one word per key.
+//  4. dkdv (bwd_dkdv.hip): dK, dV and the per-head k_rope parts, one workgroup
+//     per (b, h, 128 keys).
+//  5. dq (bwd_dq.hip): one workgroup per (b, q-tile, h) in the forward's ranked
+//     order.
+//  6. rope_reduce: dk_rope = sum over heads of the per-head parts, in head order.
+// The transposed copies hold, per 16-entry group, entry 16g + k at position
+// 16g + k with bits 2 and 3 of k swapped: the order in which the rows of an
+// MFMA accumulator become the reduction index of the next product.
 #include "common.h"
 #include "dma.h"
 #include "launch.h"
@@ -61,7 +48,7 @@ __device__ __forceinline__ int relabel16(int k) { return (k & 3) | ((k & 4) << 1
 __device__ __forceinline__ u32x4_t zero4() { return u32x4_t{0u, 0u, 0u, 0u}; }
 
 // ---------------------------------------------------------------- 1. prep_q
-// grid (Lqp / 32, B*H): D, lse2 and the transposed q / dout of 32 queries.
+// grid (Lqp / 32, B*H): the exponent offsets and -D of 32 queries, and their transposed q / dout.
 __global__ void __launch_bounds__(kThreads) bwd_prep_q(AttnBwdArgs a) {
   __shared__ __attribute__((aligned(16))) char sq[kQC * kSQ];
   __shared__ __attribute__((aligned(16))) char so[kQC * kSO];
@@ -98,9 +85,7 @@ __global__ void __launch_bounds__(kThreads) bwd_prep_q(AttnBwdArgs a) {
     acc += __shfl_xor(acc, 2);
     acc += __shfl_xor(acc, 4);
     if (part == 0) {
-      a.dd[bh * a.Lqp + qi] = acc;
       const float l = qi < a.Lq ? a.lse[bh * a.Lq + qi] : -INFINITY;
-      a.lse2[bh * a.Lqp + qi] = l == -INFINITY ? INFINITY : l * kLog2e;
       // per 32-query chunk: the exponent offsets, then -D
       float* ld = a.ld + (bh * (a.Lqp / kQC) + blockIdx.x) * 64;
       ld[r] = l == -INFINITY ? -INFINITY : -l * kLog2e;

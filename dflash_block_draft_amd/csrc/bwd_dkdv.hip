@@ -277,12 +277,12 @@ bwd_dkdv(AttnBwdArgs a) {
     // ---- prologue: F(0), F(1), F(2), T(0), T(1), T(2) copied; chunk 0's S, dP, P
     int e0 = ent(0), e1 = ent(1), e2 = ent(2), e3 = ent(3);
     copy_f(0, e0);
-    copy_f(1, e1);
-    copy_f(2, e2);
     copy_t(0, e0);
+    copy_f(1, e1);
     copy_t(1, e1);
+    copy_f(2, e2);
     copy_t(2, e2);
-    wait_vmem<0>();
+    wait_vmem<2 * kCopiesPerStep>();                    // chunk 0's parts landed, chunks 1 and 2 in flight
     __syncthreads();
 
     f32x16_t acc;                                       // S of the next chunk
@@ -328,6 +328,7 @@ bwd_dkdv(AttnBwdArgs a) {
 #pragma unroll
       for (int v = 0; v < 8; ++v) fo[v] = *(const lds_u32x4_t*)(ts + ((v & 1) ? t_lane1 : t_lane0) + (v >> 1) * 2048);
     }
+    wait_vmem<kCopiesPerStep>();                        // chunk 1's parts landed (read in step 0)
     __syncthreads();                                    // F(0)'s slot is rewritten in step 0
 
     // Step i.  Entering: sp, pkP = P(i); dpp = dP(i) - D(i); fo = dO^T(i) operands.
@@ -417,22 +418,40 @@ bwd_dkdv(AttnBwdArgs a) {
     __syncthreads();
   }
 
-  // ---- store: accumulator row r <-> key 8(r/4) + 4hi + r%4 of the wave's 32, column <-> dim
+  // ---- store: accumulator row r <-> key 8(r/4) + 4hi + r%4 of the wave's 32, column <-> dim.
+  // Rows r and r+1 are adjacent keys: lanes 2c and 2c+1 swap one value each, so
+  // that the even lane stores dims (2c, 2c+1) of row r and the odd lane those of
+  // row r+1, two elements per store.
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(dk[0]), "+a"(dk[1]), "+a"(dk[2]), "+a"(dk[3]), "+a"(dk[4]),
                "+a"(dk[5]), "+a"(dv[0]), "+a"(dv[1]), "+a"(dv[2]), "+a"(dv[3]));
+  const bool odd = (li & 1) != 0;
+  auto swap_pair = [](float x) __attribute__((always_inline)) -> float {   // value of lane l ^ 1
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+  };
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int kj = kb * kKB + 32 * w + 8 * (r >> 2) + 4 * hi + (r & 3);
-    if (kj >= a.Lk) continue;
+  for (int r = 0; r < 16; r += 2) {
+    const int kj = kb * kKB + 32 * w + 8 * (r >> 2) + 4 * hi + (r & 3) + (odd ? 1 : 0);
     const size_t row = bh * a.Lk + kj;
+    const int col = li & ~1;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      const uint32_t kv = pack_bf16x2(dk[nt][r] * a.scale, dv[nt][r]);
-      a.dkn[row * kDn + 32 * nt + li] = static_cast<uint16_t>(kv & 0xFFFFu);
-      a.dv[row * kDv + 32 * nt + li] = static_cast<uint16_t>(kv >> 16);
+      const float k0 = dk[nt][r] * a.scale, k1 = dk[nt][r + 1] * a.scale, v0 = dv[nt][r], v1 = dv[nt][r + 1];
+      const float kx = swap_pair(odd ? k0 : k1), vx = swap_pair(odd ? v0 : v1);
+      const uint32_t kp = odd ? pack_bf16x2(kx, k1) : pack_bf16x2(k0, kx);
+      const uint32_t vp = odd ? pack_bf16x2(vx, v1) : pack_bf16x2(v0, vx);
+      if (kj < a.Lk) {
+        *reinterpret_cast<uint32_t*>(a.dkn + row * kDn + 32 * nt + col) = kp;
+        *reinterpret_cast<uint32_t*>(a.dv + row * kDv + 32 * nt + col) = vp;
+      }
     }
 #pragma unroll
-    for (int nt = 4; nt < 6; ++nt) a.rope_part[row * kDr + 32 * (nt - 4) + li] = dk[nt][r] * a.scale;
+    for (int nt = 4; nt < 6; ++nt) {
+      const float k0 = dk[nt][r] * a.scale, k1 = dk[nt][r + 1] * a.scale;
+      const float kx = swap_pair(odd ? k0 : k1);
+      const u32x2_t pr = odd ? u32x2_t{__float_as_uint(kx), __float_as_uint(k1)}
+                             : u32x2_t{__float_as_uint(k0), __float_as_uint(kx)};
+      if (kj < a.Lk) *reinterpret_cast<u32x2_t*>(a.rope_part + row * kDr + 32 * (nt - 4) + col) = pr;
+    }
   }
 }
 

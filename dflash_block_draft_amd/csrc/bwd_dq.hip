@@ -191,6 +191,9 @@ bwd_dq(AttnBwdArgs a) {
   for (int s = 0; s < kDqk / 16; ++s) asm volatile("" : "=a"(qf[s]) : "0"(qv[s]));
 #pragma unroll
   for (int s = 0; s < kDv / 16; ++s) asm volatile("" : "=a"(of[s]) : "0"(ov[s]));
+  // the row values have landed before any copy is issued: the compiler cannot
+  // count the copies, so a wait of its own for them later would drain those too
+  asm volatile("" :: "v"(nlse), "v"(ndd), "v"(lse_nat));
 
   for (int tb = 0; tb < n_all; tb += kListMax, nent = tb < n_all ? load_list(tb) : 0) {
     const int nsteps = 2 * nent;
@@ -247,12 +250,12 @@ bwd_dq(AttnBwdArgs a) {
       const int e0 = ent(0);
       copy_f(0, e0);
       copy_f(1, e1);
-      copy_f(2, e2);
-      copy_f(3, e3);
       copy_t(0, e0);
+      copy_f(2, e2);
       copy_t(1, e1);
+      copy_f(3, e3);
     }
-    wait_vmem<0>();
+    wait_vmem<2 * kQCopiesPerStep>();                  // F(0), F(1) landed; T(0), F(2), T(1), F(3) in flight
     __syncthreads();
 
     f32x16_t acc;                                      // S^T of the next step
@@ -287,6 +290,7 @@ bwd_dq(AttnBwdArgs a) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) fk[s] = *(const lds_u32x4_t*)(f1 + k_off(s));
     }
+    wait_vmem<kQCopiesPerStep>();                      // T(0), F(2) landed (read in step 0)
     __syncthreads();                                   // F(0)'s slot is rewritten in step 0
 
     // Step j.  Entering: p = P(j), dpp = dP(j) - D, fk[0..7] = K operands 0-7 of

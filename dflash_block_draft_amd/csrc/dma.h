@@ -6,11 +6,12 @@
 
 namespace dflash {
 
-// s_waitcnt vmcnt(N) with expcnt/lgkmcnt left at their no-wait maxima (gfx9 encoding).
+// s_waitcnt vmcnt(N) with expcnt/lgkmcnt left at their no-wait maxima (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14).
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // 16 bytes per lane from a buffer straight into LDS at lds_base + OFF + 16*lane; reads past

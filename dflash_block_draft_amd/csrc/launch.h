@@ -74,8 +74,6 @@ struct AttnBwdArgs {
   uint16_t* dq; uint16_t* dkn; uint16_t* dkr; uint16_t* dv;
   const uint8_t* classes; const int32_t* counts; const int32_t* lists; const int32_t* order;
   const uint64_t* bits;                   // tile map (null classes: every tile visible, no lists)
-  float* lse2;                            // [B*H, Lqp] lse * log2(e); +inf for dead / padded rows
-  float* dd;                              // [B*H, Lqp] rowsum(dout * out)
   uint16_t* qT;                           // [B*H, 192, Lqp]
   uint16_t* doT;                          // [B*H, 128, Lqp]
   uint16_t* knT;                          // [B*H, 128, Lkp]
