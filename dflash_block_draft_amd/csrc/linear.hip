@@ -48,10 +48,14 @@ using SmallTile = Tile<128, 128, 32, 2, 2>;   // 4 waves, 64 x 64 each
 
 // Store four consecutive bf16 outputs n .. n + 3 of row m (batch row b, time tt)
 // in the layout of the output mode.
+template <int MODE = -1>
 __device__ __forceinline__ void emit4(const LinearArgs& a, int64_t m, int64_t b, int tt, int T, int n, uint32_t p0,
                                       uint32_t p1) {
   uint16_t* dst;
-  if (a.mode == kLinearPlain) {
+  if (MODE == kLinearKV || (MODE < 0 && a.mode == kLinearKV)) {   // per head [k_nope (128) | v (128)]
+    const int h = n >> 8, e = n & 255;
+    dst = (e < kDn ? a.y1 : a.y2) + ((static_cast<size_t>(b) * (a.N >> 8) + h) * T + tt) * kDn + (e & 127);
+  } else if (a.mode == kLinearPlain) {
     dst = a.y1 + static_cast<size_t>(m) * a.N + n;
   } else if (a.mode == kLinearSplit) {
     dst = n < a.N1 ? a.y1 + static_cast<size_t>(m) * a.N1 + n
@@ -70,9 +74,8 @@ __device__ __forceinline__ void emit4(const LinearArgs& a, int64_t m, int64_t b,
       return;
     }
     dst = a.y1 + (bh * Lt + ti) * a.D + d;          // [B, N / D, Lt, D]
-  } else {                                          // kv: per head [k_nope (128) | v (128)]
-    const int h = n >> 8, e = n & 255;
-    dst = (e < kDn ? a.y1 : a.y2) + ((static_cast<size_t>(b) * (a.N >> 8) + h) * T + tt) * kDn + (e & 127);
+  } else {
+    return;
   }
   *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{p0, p1};
 }
@@ -363,6 +366,162 @@ __global__ void __launch_bounds__(512) linear_bf16_dma(LinearArgs a) {
   }
 }
 
+// A deeper copy pipeline for GEMMs whose K is short next to the latency of a
+// global load: S stages of K = 32, S - 1 of them in flight, copied global -> LDS
+// by the buffer unit.  A stage holds NT W rows then MT rows of a, 64 bytes each,
+// as 1 KiB blocks of 16 rows in which the four 16-byte pieces of a row are
+// permuted by the row (piece p at position p ^ ((row >> 2) & 3)): the 16-byte
+// operand reads of 16 lanes hit distinct banks without padding.  Each wave
+// copies the same number of blocks per stage and a stage past the end copies
+// with an offset beyond the resources (zeros), so the wait counts are constants.
+// For single-source a without norm-on-load.
+template <int NT, int MT, int WN, int WM, int S>
+struct DmaTile {
+  static constexpr int kWaves = WN * WM, kThreads = 64 * kWaves;
+  static constexpr int kFN = NT / WN / 32, kFM = MT / WM / 32;
+  static constexpr int kWBlocks = NT / 16, kBlocks = (NT + MT) / 16;
+  // copy blocks per wave; the last blocks of a stage may be spare (past the end, zeros)
+  static constexpr int kPerWave = (kBlocks + kWaves - 1) / kWaves;
+  static constexpr int kStage = kPerWave * kWaves * 1024;
+  static_assert(kFN >= 1 && kFM >= 1 && NT % 16 == 0 && MT % 32 == 0, "tile shape");
+  static_assert(NT / WN == 64 && NT % 128 == 0, "two waves per 128-column statistics group");
+  static_assert(kPerWave * (S - 1) < 64 && S * kStage + WN * MT * 4 <= 160 * 1024, "pipeline depth");
+};
+
+template <int NT, int MT, int WN, int WM, int S, int MODE>
+__global__ void __launch_bounds__(64 * WN * WM) linear_dma(LinearArgs a) {
+  using TL = DmaTile<NT, MT, WN, WM, S>;
+  constexpr int FN = TL::kFN, FM = TL::kFM, PW = TL::kPerWave;
+  __shared__ __attribute__((aligned(1024))) char smem[S * TL::kStage];
+  __shared__ float s_part[WN][MT];
+  typedef __attribute__((address_space(3))) char lds_char_t;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wn = wave % WN, wm = wave / WN;
+  const int li = lane & 31, hi = lane >> 5;
+  const int T = a.T1 + a.T2;
+  const int64_t M = static_cast<int64_t>(a.B) * T;
+  // tile of this workgroup: workgroups go to the 8 XCDs in turn, so XCD x gets
+  // M quarter x / 2 and N half x % 2 of the tiles (its operands share its L2)
+  int bx = blockIdx.x, by = blockIdx.y;
+  if (gridDim.x % 4 == 0 && gridDim.y % 2 == 0) {
+    const int id = blockIdx.y * gridDim.x + blockIdx.x, x = id % 8, j = id / 8;
+    const int mq = gridDim.x / 4;
+    bx = mq * (x / 2) + j % mq;
+    by = (gridDim.y / 2) * (x % 2) + j / mq;
+  }
+  const int64_t m0 = static_cast<int64_t>(bx) * MT;
+  const int n0 = by * NT;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.K) * 2;
+
+  // copy plan: block blk = PW * wave + j of a stage; lane l fills row 16 (blk mod
+  // its operand) + l / 4, position l & 3 with piece (l & 3) ^ swz
+  constexpr uint32_t kPastEnd = 0x80000000u;           // beyond every resource (the host bounds them by 2^31 bytes)
+  const u32x4_t dw = buffer_desc(a.w + static_cast<size_t>(n0) * a.K,
+                                 static_cast<uint32_t>(min(NT, a.N - n0)) * row_bytes);
+  const u32x4_t da = buffer_desc(a.a1 + static_cast<size_t>(m0) * a.K,
+                                 static_cast<uint32_t>(min<int64_t>(MT, M - m0)) * row_bytes);
+  uint32_t voff[PW];
+  bool isw[PW];
+  {
+    const int r16 = lane >> 2, pos = lane & 3;
+#pragma unroll
+    for (int j = 0; j < PW; ++j) {
+      const int blk = PW * wave + j;
+      isw[j] = blk < TL::kWBlocks;
+      const int row = 16 * (isw[j] ? blk : blk - TL::kWBlocks) + r16;
+      voff[j] = blk >= TL::kBlocks ? kPastEnd
+              : static_cast<uint32_t>(row) * row_bytes + static_cast<uint32_t>((pos ^ ((r16 >> 2) & 3)) * 16);
+    }
+  }
+  const int nk = a.K / 32;
+  auto issue = [&](int it) __attribute__((always_inline)) {
+    const uint32_t base = lds0 + (it % S) * TL::kStage + PW * wave * 1024;
+    const uint32_t soff = it < nk ? static_cast<uint32_t>(it) * 64u : kPastEnd;
+#pragma unroll
+    for (int j = 0; j < PW; ++j) dma16<0>(isw[j] ? dw : da, base + j * 1024, voff[j], soff);
+  };
+  // operand reads: row r of the stage, 16-byte piece p
+  const int rsw = (li >> 2) & 3;
+  auto rd = [&](const char* st, int row, int p) __attribute__((always_inline)) -> bf16x8_t {
+    return as_bf16x8(*reinterpret_cast<const u32x4_t*>(st + (row >> 4) * 1024 + (row & 15) * 64 + ((p ^ rsw) << 4)));
+  };
+
+  f32x16_t acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) issue(s);
+  for (int it = 0; it < nk; ++it) {
+    wait_vmem<PW * (S - 2)>();                          // this wave's copies of stage it
+    __syncthreads();                                    // everyone's; stage it - 1 fully read
+    issue(it + S - 1);
+    const char* st = smem + (it % S) * TL::kStage;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8_t af[FN], bf[FM];
+#pragma unroll
+      for (int i = 0; i < FN; ++i) af[i] = rd(st, (NT / WN) * wn + 32 * i + li, 2 * ks + hi);
+#pragma unroll
+      for (int j = 0; j < FM; ++j) bf[j] = rd(st, NT + (MT / WM) * wm + 32 * j + li, 2 * ks + hi);
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+    }
+  }
+  wait_vmem<0>();
+
+  // epilogue: as linear_bf16 (lane owns row m; outputs n0 + 64 wn + 32 i + 8 g + 4 hi + 0..3);
+  // MODE >= 0 fixes the output mode at compile time (no statistics)
+  const bool stats = MODE < 0 && a.stats_out && n0 < a.Nstat;
+#pragma unroll
+  for (int j = 0; j < FM; ++j) {
+    const int rl = (MT / WM) * wm + 32 * j + li;
+    const int64_t m = m0 + rl;
+    const bool mok = m < M;
+    const int64_t mm = mok ? m : 0;
+    const int64_t b = mm / T;
+    const int tt = static_cast<int>(mm % T);
+    float ssq = 0.f;
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + 64 * wn + 32 * i + 8 * g + 4 * hi;
+        const uint32_t p0 = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+        const uint32_t p1 = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+        if (n < a.N) {
+          const float x0 = bf16_bits_to_f32(p0 & 0xFFFFu), x1 = bf16_bits_to_f32(p0 >> 16);
+          const float x2 = bf16_bits_to_f32(p1 & 0xFFFFu), x3 = bf16_bits_to_f32(p1 >> 16);
+          ssq += x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
+          if (mok) emit4<MODE>(a, m, b, tt, T, n, p0, p1);
+        }
+      }
+    if (stats) {
+      ssq += __shfl_xor(ssq, 32);
+      if (hi == 0) s_part[wn][rl] = ssq;
+    }
+  }
+  if (stats) {
+    __syncthreads();
+    constexpr int G = NT / 128;
+    const int parts = a.Nstat / 128;
+    for (int idx = t; idx < MT * G; idx += TL::kThreads) {
+      const int r = idx % MT, gi = idx / MT;
+      const int part = n0 / 128 + gi;
+      const int64_t m = m0 + r;
+      if (m < M && part < parts) a.stats_out[m * parts + part] = s_part[2 * gi][r] + s_part[2 * gi + 1][r];
+    }
+  }
+}
+
 // Split-K reduction: the partials of each output are summed in split order and
 // the result goes through the same epilogue (rounding, layout, statistics).  One
 // thread per row and 4 columns; 32 threads cover one 128-column group.
@@ -443,8 +602,26 @@ size_t linear_split_bytes(const LinearArgs& a) {
   return sp > 1 ? static_cast<size_t>(sp) * M * a.N * 4 : 0;
 }
 
+// The deep-pipeline tile (288 rows x 256 outputs, 12 waves, four stages) for the
+// latent expand: its K (the latent rank) is short next to the copy latency, and
+// its output is large.  Taken when the tiles fill the chip's 256 CUs in one
+// round of at least 7/8 (a second, partly filled round would cost a whole tile).
+constexpr int kDeepMT = 288, kDeepNT = 256;
+static bool linear_deep(const LinearArgs& a) {
+  const int64_t M = static_cast<int64_t>(a.B) * (a.T1 + a.T2);
+  if (a.mode != kLinearKV || a.stats_in || a.stats_out || a.split_part || (a.T2 != 0 && a.a2)) return false;
+  if (a.K % 32 != 0 || a.K > 1024) return false;
+  const int64_t tiles = ((M + kDeepMT - 1) / kDeepMT) * ((a.N + kDeepNT - 1) / kDeepNT);
+  return tiles >= 224 && tiles <= 256;
+}
+
 hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t s, float* scratch, size_t scratch_bytes) {
   const int64_t M = static_cast<int64_t>(a.B) * (a.T1 + a.T2);
+  if (linear_deep(a)) {
+    const dim3 grid(static_cast<unsigned>((M + kDeepMT - 1) / kDeepMT), static_cast<unsigned>((a.N + kDeepNT - 1) / kDeepNT));
+    hipLaunchKernelGGL((linear_dma<kDeepNT, kDeepMT, 4, 3, 4, kLinearKV>), grid, dim3(768), 0, s, a);
+    return hipGetLastError();
+  }
   const int sp = linear_splits(a);
   if (sp > 1 && scratch && scratch_bytes >= linear_split_bytes(a)) {
     LinearArgs b = a;

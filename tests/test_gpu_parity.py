@@ -371,6 +371,24 @@ def test_non_default_stream(dev):
 
 
 # ------------------------------------------------------------- expand
+@pytest.mark.gpu
+def test_expand_deep_tile_ragged(dev):
+    """The expand's one-round tile path (288 rows x 256 outputs per workgroup,
+    chosen when those tiles fill the chip once): 4600 rows (a ragged last row
+    tile), R = 512, 16 heads, bf16, against the fp64 definition."""
+    rng = np.random.default_rng(23)
+    B, Lk, R, H = 2, 2300, 512, 16
+    lat = W.normal(rng, (B, Lk, R), 1.0, "bf16")
+    w = W.normal(rng, (H * 256, R), R ** -0.5, "bf16")
+    ld, wd = _to(dev, lat, w)
+    say(f"expand deep tile: B={B} Lk={Lk} R={R} H={H}")
+    kn, v = mla.latent_expand(ld, wd, H)
+    torch.cuda.synchronize()
+    ref_kn, ref_v = oracle.latent_expand(lat, w, H, 128, 128)
+    for got, ref in ((kn, ref_kn), (v, ref_v)):
+        g = got.to("cpu", torch.float64).numpy()
+        assert np.all(np.abs(g - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6)
+
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_expand_ragged(dev, dtype):
