@@ -96,12 +96,13 @@ __global__ void __launch_bounds__(kClassifyThreads) classify_tiles_vec(Occupancy
   constexpr int NIT = kTileM / RPB;
   __shared__ uint8_t s_vis[kTileM][CH];
   __shared__ int s_flags[kClassifyWaves];
-  const int64_t tile = blockIdx.x;
-  const int kt = static_cast<int>(tile % a.nkt);
-  const int64_t rest = tile / a.nkt;
-  const int qt = static_cast<int>(rest % a.nqt);
-  const int b = static_cast<int>(rest / a.nqt);
-  const int r0 = qt * kTileM, c0 = kt * kTileN;
+  // (the tile count is far below 2^31: 32-bit index arithmetic)
+  const uint32_t tile = blockIdx.x;
+  const uint32_t kt = tile % static_cast<uint32_t>(a.nkt);
+  const uint32_t rest = tile / static_cast<uint32_t>(a.nkt);
+  const uint32_t qt = rest % static_cast<uint32_t>(a.nqt);
+  const uint32_t b = rest / static_cast<uint32_t>(a.nqt);
+  const int r0 = static_cast<int>(qt) * kTileM, c0 = static_cast<int>(kt) * kTileN;
   const int rows = min(kTileM, a.Lq - r0);
   const int cols = min(kTileN, a.Lk - c0);          // a multiple of EPL here
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -109,34 +110,58 @@ __global__ void __launch_bounds__(kClassifyThreads) classify_tiles_vec(Occupancy
   if (tile == 0 && t == 0) *a.sync = 0u;              // the list pass that follows counts its workgroups
   const bool col_ok = c * EPL < cols;
   const size_t esz = BF16 ? 2 : 4;
-  const char* base = static_cast<const char*>(a.mask) + ((static_cast<size_t>(b) * a.Lq + r0) * a.Lk + c0 + c * EPL) * esz;
+  // chunks outside the mask read a valid chunk of the tile instead (row 0 or chunk 0,
+  // always inside) and are left out of the flags and visibility bits below
+  const char* base = static_cast<const char*>(a.mask) +
+                     ((static_cast<size_t>(b) * a.Lq + r0) * a.Lk + c0 + (col_ok ? c * EPL : 0)) * esz;
 
   u32x4_t w[NIT];
 #pragma unroll
-  for (int i = 0; i < NIT; ++i) {                   // all loads in flight together
+  for (int i = 0; i < NIT; ++i) {                   // all loads in flight together, no branches
     const int r = rr + RPB * i;
-    const u32x4_t ninf = BF16 ? u32x4_t{0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u}
-                              : u32x4_t{0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u};
-    w[i] = (r < rows && col_ok) ? ldg16(base + static_cast<size_t>(r) * a.Lk * esz) : ninf;
+    w[i] = ldg16(base + static_cast<size_t>(r < rows ? r : 0) * a.Lk * esz);
   }
   bool any_vis = false, any_nonzero = false, any_other = false;
 #pragma unroll
   for (int i = 0; i < NIT; ++i) {
     const int r = rr + RPB * i;
-    uint32_t vis = 0;
+    uint32_t vis = 0, nz_acc = 0, nn_acc = 0, ot_acc = 0;
+    if constexpr (BF16) {
+      // two entries per word: with a = |x| per half (< 0x8000), a + 0x7FFF has bit 15
+      // of the half set exactly when that half is nonzero (no carry between halves);
+      // x ^ -inf is zero exactly at -inf, and its own bit 15 covers halves >= 0x8000
+      uint32_t zsh = 0;                             // zero flags of entry 2q at bit 2q, of 2q+1 at 16 + 2q
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const uint32_t x = BF16 ? ((w[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu) : w[i][e];
-      const bool zero = BF16 ? (x & 0x7FFFu) == 0u : (x & 0x7FFFFFFFu) == 0u;
-      const bool ninf = BF16 ? x == 0xFF80u : x == 0xFF800000u;
-      vis |= static_cast<uint32_t>(zero) << e;
-      if (r < rows && col_ok) {                     // entries outside the mask do not count
-        any_vis |= !ninf;
-        any_nonzero |= !zero;
-        any_other |= !zero && !ninf;
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t x = w[i][q];
+        const uint32_t nz = ((x & 0x7FFF7FFFu) + 0x7FFF7FFFu) & 0x80008000u;        // not +-0
+        const uint32_t n = x ^ 0xFF80FF80u;
+        const uint32_t nn = (((n & 0x7FFF7FFFu) + 0x7FFF7FFFu) | n) & 0x80008000u;   // not -inf
+        nz_acc |= nz;
+        nn_acc |= nn;
+        ot_acc |= nz & nn;
+        zsh |= (~nz & 0x80008000u) >> (15 - 2 * q);
+      }
+      vis = (zsh & 0x55u) | ((zsh >> 15) & 0xAAu);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const uint32_t x = w[i][e];
+        const uint32_t nz = (x & 0x7FFFFFFFu) != 0u ? 1u : 0u;
+        const uint32_t nn = x != 0xFF800000u ? 1u : 0u;
+        vis |= (nz ^ 1u) << e;
+        nz_acc |= nz;
+        nn_acc |= nn;
+        ot_acc |= nz & nn;
       }
     }
-    s_vis[r][c] = static_cast<uint8_t>(vis);        // outside the mask: loaded as -inf, bits 0
+    const bool in_mask = r < rows && col_ok;       // entries outside the mask do not count
+    if (in_mask) {
+      any_vis |= nn_acc != 0u;
+      any_nonzero |= nz_acc != 0u;
+      any_other |= ot_acc != 0u;
+    }
+    s_vis[r][c] = static_cast<uint8_t>(in_mask ? vis : 0u);
   }
   int flags = (__ballot(any_vis) ? 1 : 0) | (__ballot(any_nonzero) ? 2 : 0) | (__ballot(any_other) ? 4 : 0);
   if (lane == 0) s_flags[wave] = flags;
