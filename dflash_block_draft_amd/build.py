@@ -34,6 +34,9 @@ COMMON_FLAGS = [
 # The GQA block attention rescales its output accumulators on the vector unit;
 # in VGPR form they need no copies out of and back into accumulator registers.
 FILE_FLAGS = {
+    # The forward key loop's exact path is rare; placing those blocks after the
+    # loop keeps the common path free of jumps over them.
+    "attn_bf16.hip": ["-mllvm", "-force-loop-cold-block"],
     "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "gqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }

@@ -61,6 +61,7 @@
 #include "dma.h"
 #include "launch.h"
 
+#include <cfloat>
 #include <type_traits>
 #include <utility>
 
@@ -118,17 +119,18 @@ __device__ __forceinline__ s16x4_t ds_read_tr(const lds_char_t* p) {
 }
 
 // 16 bytes per lane from a buffer straight into LDS at lds_base + 16*lane, from
-// byte voff + SOFF of the buffer.  SOFF selects a 64-byte chunk quad inside a
+// byte voff + SOFF of the buffer, lds_base a uniform LDS address and LOFF a
+// constant added to it (one scalar add into m0).  SOFF selects a 64-byte chunk quad inside a
 // row and goes in the scalar offset (the instruction's immediate offset would
 // move the LDS destination too); the row offset is in voff, so a row is in or
 // out of the buffer's range as a whole and out-of-range rows read zeros.
 // Inline asm for the same reason as dma16: the compiler must not make unrelated
 // LDS reads wait for this write; completion is awaited with wait_vmem before
 // the barrier that publishes the slot.
-template <int SOFF>
+template <int SOFF, int LOFF>
 __device__ __forceinline__ void dma16i(u32x4_t rsrc, uint32_t lds_base, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base)), "s"(SOFF));
+  asm volatile("s_add_u32 m0, %2, %3\n\tbuffer_load_dwordx4 %0, %1, %4 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(lds_base), "i"(LOFF), "s"(SOFF) : "scc");
 }
 
 template <bool MASK_BF16>
@@ -169,20 +171,36 @@ __device__ __forceinline__ void static_for(F&& f) {
 // the compiler does not know the result arrives one MFMA latency later: every
 // reader of acc is placed at least two MFMA issues later, or behind
 // s_nop_after_mfma.
-template <bool FIRST>
+template <int KIND>   // 0: continue the chain; 1: start it from bias; 2: start it from zero
 __device__ __forceinline__ void mfma_s(f32x16_t& acc, bf16x8_t k, const u32x4_t& q, const f32x16_t& bias) {
   const u32x4_t kk = __builtin_bit_cast(u32x4_t, k);
-  if (FIRST)     // the chain starts from the hidden-key bias (0 or -inf per key)
+  if constexpr (KIND == 1)   // the chain starts from the hidden-key bias (0 or -inf per key)
     asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(acc) : "v"(kk), "a"(q), "v"(bias));
+  else if constexpr (KIND == 2)
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(kk), "a"(q));
   else
     asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(kk), "a"(q));
+}
+// first chunk of a chain: from the bias block when the step's tile is binary
+// (bin != 0), else from zero; the choice is one scalar branch around the MFMA
+__device__ __forceinline__ void mfma_s_first(int bin, f32x16_t& acc, bf16x8_t k, const u32x4_t& q,
+                                             const f32x16_t& bias) {
+  const u32x4_t kk = __builtin_bit_cast(u32x4_t, k);
+  asm("s_cmp_eq_u32 %4, 0\n\t"
+      "s_cbranch_scc1 1f\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3\n\t"
+      "s_branch 2f\n"
+      "1:\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0\n"
+      "2:"
+      : "=&v"(acc) : "v"(kk), "a"(q), "v"(bias), "s"(bin) : "scc");
 }
 // the MFMA result in acc is readable by the VALU after this (16 wait states)
 __device__ __forceinline__ void s_nop_after_mfma(f32x16_t& acc) {
   asm volatile("s_nop 7\n\ts_nop 7" : "+v"(acc));
 }
 
-template <bool MASK_BF16>
+template <bool MASK_BF16, bool LIST>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_fwd_bf16(AttnBf16Args a) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
@@ -203,7 +221,7 @@ attn_fwd_bf16(AttnBf16Args a) {
   const int bq = a.order ? a.order[rank] : rank;
   const int b = bq / a.nqt;
   const int qt = bq % a.nqt;
-  const int n_all = a.counts ? a.counts[bq] : a.nkt;
+  const int n_all = LIST ? a.counts[bq] : a.nkt;
   const int t_begin = static_cast<int>(static_cast<int64_t>(n_all) * sp / a.nsplit);
   const int ntiles = static_cast<int>(static_cast<int64_t>(n_all) * (sp + 1) / a.nsplit) - t_begin;
   const int nsteps = 2 * ntiles;
@@ -219,20 +237,42 @@ attn_fwd_bf16(AttnBf16Args a) {
     q_ok[i] = q_row[i] < a.Lq;
   }
 
-  // ---- tile list (entry: k-tile | class << 24), scalar loads; past the end an
-  // entry is 0 (no tile); without a mask every k-tile is class 1
-  typedef __attribute__((address_space(4))) const int32_t const_i32;
-  const int32_t* list = a.counts ? a.lists + tile_row0 + t_begin : nullptr;
-  const const_i32* clist = (const const_i32*)(uintptr_t)(list);
+  // ---- tile list (entry: k-tile | class << 24).  Entries past the end repeat
+  // the last one: the steps they feed are never used (their scores are dropped,
+  // their copies land in slots no used step reads), so they only need addresses
+  // the copies may read, which any entry gives (the copies are range checked).
+  // Without a list every k-tile of the run is class 1.  The list is read through
+  // a window of 64 entries held one per lane of a vector register (readlane per
+  // entry, a refill every 64 tiles): no scalar loads in the key loop, whose
+  // completion, out of order with LDS reads, would make every LDS wait drain.
+  const int32_t* list = LIST ? a.lists + tile_row0 + t_begin : nullptr;
+  const int last = max(ntiles - 1, 0);
+  int wbase = 0;                               // entries wbase .. wbase+63 are in lwin
+  int32_t lwin = LIST ? list[min(lane, last)] : 0;
   auto entry = [&](int i) __attribute__((always_inline)) -> int {
-    if (i >= ntiles) return 0;
-    if (!list) return (t_begin + i) | (1 << 24);
-    return clist[i];
+    const int j = min(i, last);
+    if constexpr (LIST) {
+      if (j - wbase >= 64) {                   // entries are read in increasing order
+        wbase = j;
+        lwin = list[min(j + lane, last)];
+        asm volatile("" :: "v"(lwin));       // waited for here, not where the paths join
+      }
+      return __builtin_amdgcn_readlane(lwin, j - wbase);
+    } else {
+      return (t_begin + j) | (1 << 24);
+    }
+  };
+  auto ktile = [](int e) __attribute__((always_inline)) -> int { return e & 0xFFFFFF; };
+  auto key0_of = [&](int e, int half) __attribute__((always_inline)) -> int { return ktile(e) * kTileN + 32 * half; };
+  // steps of tile e go to the exact path: general mask values, or keys past Lk
+  auto slow_tile = [&](int e) __attribute__((always_inline)) -> bool {
+    return (e >> 24) == 3 || ktile(e) * kTileN + kTileN > a.Lk;
   };
 
   // ---- global -> LDS copy plan: wave w copies row block w (keys 16w .. 16w+15
   // of the step) of K (k_nope quads 0-3, k_rope quads 4-5) and of V (quads 0-3);
-  // lane l covers row 16w + l/4, LDS slot l%4 of each quad, K chunks swizzled
+  // lane l covers row 16w + l/4, LDS slot l%4 of each quad, K chunks swizzled.
+  // LDS slot addresses are uniform values plus constants.
   const u32x4_t d_kn = buffer_desc(a.kn + bh * a.Lk * kDn, a.Lk * kDn * 2);
   const u32x4_t d_kr = buffer_desc(a.kr + static_cast<size_t>(b) * a.Lk * kDr, a.Lk * kDr * 2);
   const u32x4_t d_v = buffer_desc(a.v + bh * a.Lk * kDv, a.Lk * kDv * 2);
@@ -243,49 +283,31 @@ attn_fwd_bf16(AttnBf16Args a) {
   const uint32_t vo_kn = crow * (kDn * 2) + kslot * 16;
   const uint32_t vo_kr = crow * (kDr * 2) + kslot * 16;
   const uint32_t vo_v = crow * (kDv * 2) + s4 * 16;
-  const uint32_t lds_k = lds0 + kKRing + wave * 6 * 1024;
-  const uint32_t lds_v = lds0 + kVRing + wave * 4 * 1024;
-  // first key of the step at (entry, half); a phantom step past the end reads at Lk: all out of range
-  auto key0_of = [&](int e, int half) __attribute__((always_inline)) -> int {
-    return (e >> 24) ? (e & 0xFFFFFF) * kTileN + 32 * half : a.Lk;
-  };
-  auto issue_k = [&](int slot, int key0) __attribute__((always_inline)) {
-    const uint32_t lk = lds_k + slot * kKSlot;
-    const uint32_t on = vo_kn + static_cast<uint32_t>(key0) * (kDn * 2);
-    const uint32_t orp = vo_kr + static_cast<uint32_t>(key0) * (kDr * 2);
-    dma16i<0>(d_kn, lk, on);
-    dma16i<64>(d_kn, lk + 1024, on);
-    dma16i<128>(d_kn, lk + 2048, on);
-    dma16i<192>(d_kn, lk + 3072, on);
-    dma16i<0>(d_kr, lk + 4096, orp);
-    dma16i<64>(d_kr, lk + 5120, orp);
-  };
-  auto issue_v = [&](int slot, int key0) __attribute__((always_inline)) {
-    const uint32_t lv = lds_v + slot * kVSlot;
-    const uint32_t ov = vo_v + static_cast<uint32_t>(key0) * (kDv * 2);
-    dma16i<0>(d_v, lv, ov);
-    dma16i<64>(d_v, lv + 1024, ov);
-    dma16i<128>(d_v, lv + 2048, ov);
-    dma16i<192>(d_v, lv + 3072, ov);
-  };
-  // piece P of issue_k / issue_v (k_nope quads 0-3, k_rope quads 4-5; V quads 0-3),
-  // for spreading a step's copies over its MFMA slots
-  auto issue_k_piece = [&](auto P, int slot, int key0) __attribute__((always_inline)) {
+  const uint32_t lds_k = __builtin_amdgcn_readfirstlane(lds0 + kKRing + wave * 6 * 1024);
+  const uint32_t lds_v = __builtin_amdgcn_readfirstlane(lds0 + kVRing + wave * 4 * 1024);
+  const uint32_t lds_b = __builtin_amdgcn_readfirstlane(lds0 + kBitsRing);
+  // piece P of a step's K copy (k_nope quads 0-3, k_rope quads 4-5) or V copy
+  // (quads 0-3) into the slot at LDS address base, for keys key0 .. key0+31
+  auto issue_k_piece = [&](auto P, uint32_t base, int key0) __attribute__((always_inline)) {
     constexpr int pc = decltype(P)::value;
-    const uint32_t lk = lds_k + slot * kKSlot + pc * 1024;
-    if constexpr (pc < 4) dma16i<pc * 64>(d_kn, lk, vo_kn + static_cast<uint32_t>(key0) * (kDn * 2));
-    else dma16i<(pc - 4) * 64>(d_kr, lk, vo_kr + static_cast<uint32_t>(key0) * (kDr * 2));
+    if constexpr (pc < 4) dma16i<pc * 64, pc * 1024>(d_kn, base, vo_kn + static_cast<uint32_t>(key0) * (kDn * 2));
+    else dma16i<(pc - 4) * 64, pc * 1024>(d_kr, base, vo_kr + static_cast<uint32_t>(key0) * (kDr * 2));
   };
-  auto issue_v_piece = [&](auto P, int slot, int key0) __attribute__((always_inline)) {
+  auto issue_v_piece = [&](auto P, uint32_t base, int key0) __attribute__((always_inline)) {
     constexpr int pc = decltype(P)::value;
-    dma16i<pc * 64>(d_v, lds_v + slot * kVSlot + pc * 1024, vo_v + static_cast<uint32_t>(key0) * (kDv * 2));
+    dma16i<pc * 64, pc * 1024>(d_v, base, vo_v + static_cast<uint32_t>(key0) * (kDv * 2));
   };
-  // visibility words of a class-2 tile (1 KiB); other tiles read zeros.  Both
-  // waves copy the same bytes (no branch inside a scheduled phase), and the
-  // copy is repeated in the tile's second step (its slot is not read then).
-  auto issue_bits = [&](int slot, int e) __attribute__((always_inline)) {
-    const int kt = (e >> 24) == 2 ? (e & 0xFFFFFF) : a.nkt;
-    dma16i<0>(d_bits, lds0 + kBitsRing + slot * kBitsSlot, lane * 16 + static_cast<uint32_t>(kt) * kBitsSlot);
+  auto issue_k = [&](uint32_t base, int key0) __attribute__((always_inline)) {
+    static_for<6>([&](auto P) __attribute__((always_inline)) { issue_k_piece(P, base, key0); });
+  };
+  auto issue_v = [&](uint32_t base, int key0) __attribute__((always_inline)) {
+    static_for<4>([&](auto P) __attribute__((always_inline)) { issue_v_piece(P, base, key0); });
+  };
+  // visibility words of tile e (1 KiB) into the word slot at byte offset boff;
+  // both waves copy the same bytes.  Only binary tiles have words; the slot of
+  // any other tile is never read.
+  auto issue_bits = [&](uint32_t boff, int e) __attribute__((always_inline)) {
+    dma16i<0, 0>(d_bits, lds_b + boff, lane * 16 + static_cast<uint32_t>(ktile(e)) * kBitsSlot);
   };
 
   // ---- per-lane LDS read offsets inside a slot
@@ -334,15 +356,24 @@ attn_fwd_bf16(AttnBf16Args a) {
       for (int r = 0; r < 16; ++r) o[i][j][r] = 0.f;
   float m_run[2] = {-INFINITY, -INFINITY};   // stabiliser (natural units), same in both lane halves
   float l_run[2] = {0.f, 0.f};               // this lane's partial row sums
-  // per stream: the C operand of the first score MFMA of a step, -inf at the keys
-  // a binary tile hides and 0 elsewhere (all zero outside binary tiles; bias_nz
-  // tells whether it needs clearing)
-  f32x16_t bias[2];
+  float l_max[2] = {0.f, 0.f};               // largest fast-path step sum (checked once, after the pass)
+  // the C operand of the next phase's first score MFMA when its step's tile is
+  // binary: -inf at the keys the tile hides from the phase's stream, 0 elsewhere
+  // (one block serves both streams: each phase's block is built just before it)
+  f32x16_t biasb;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) bias[i][r] = 0.f;
+  for (int r = 0; r < 16; ++r) biasb[r] = 0.f;
   bool over = false;                         // a score rose more than kHeadroom above its stabiliser
+  bool first[2];                             // some lane of the stream has no stabiliser yet
+  // -m * log2e of each stream's stabiliser, the fast path's exponent offset,
+  // held within +-FLT_MAX (NaN kept): with m near -FLT_MAX the product
+  // overflows, and a hidden key's -inf plus an infinite offset would be NaN where
+  // the finite bound gives exp2(-inf) = 0.  Updated wherever m changes.
+  float cbs[2];
+  auto stab_off = [](float m) __attribute__((always_inline)) -> float {
+    const float c = -m * kLog2e;
+    return c > FLT_MAX ? FLT_MAX : (c < -FLT_MAX ? -FLT_MAX : c);
+  };
   f32x16_t s[2];                             // raw scores of each stream's pending softmax step
   uint32_t pk[2][8];                         // P^T of each stream's step awaiting PV, bf16 pairs
   bf16x8_t kreg[kDqk / 16];                  // K operands of the next step's scores (both streams)
@@ -354,56 +385,45 @@ attn_fwd_bf16(AttnBf16Args a) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) mask_row[i] = (static_cast<size_t>(b) * a.Lq + (q_ok[i] ? q_row[i] : 0)) * a.Lk;
 
-  auto read_k = [&](int slot, int c) __attribute__((always_inline)) -> bf16x8_t {
-    const lds_char_t* kp = ((c & 1) ? ko_ptr : ke_ptr) + slot * kKSlot + (c >> 1) * 1024;
+  // operand reads from the ring slot at byte offset off
+  auto read_k = [&](uint32_t off, int c) __attribute__((always_inline)) -> bf16x8_t {
+    const lds_char_t* kp = ((c & 1) ? ko_ptr : ke_ptr) + off + (c >> 1) * 1024;
     return as_bf16x8(*reinterpret_cast<const lds_u32x4_t*>(kp));
   };
-  auto read_v = [&](int slot, int op) __attribute__((always_inline)) -> s16x8_t {
-    const lds_char_t* vp = v_ptr + slot * kVSlot + (op >> 2) * 4096 + (op & 3) * 1024;
+  auto read_v = [&](uint32_t off, int op) __attribute__((always_inline)) -> s16x8_t {
+    const lds_char_t* vp = v_ptr + off + (op >> 2) * 4096 + (op & 3) * 1024;
     const s16x4_t lo = ds_read_tr(vp);
     const s16x4_t hi4 = ds_read_tr(vp + 512);
     return s16x8_t{lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
   };
-  // bias of stream i for step s of tile entry e: from the query's visibility
-  // word, bit 8g+c <-> key 8g+4hi+c of the step (accumulator r = 4g+c), when
-  // the tile is binary.  The bit-field width comes from an opaque register (it
-  // is 1) so each entry compiles to a bit-field extract and an and.
+  // bias of stream i for half `half` of a binary tile: from the query's
+  // visibility word, bit 8g+c <-> key 8g+4hi+c of the step (accumulator r =
+  // 4g+c).  The bit-field width comes from an opaque register (it is 1) so each
+  // entry compiles to a bit-field extract and an and.
   int one;
   asm("s_mov_b32 %0, 1" : "=s"(one));
-  // The bias of a step is built in pieces so that a phase can spread it over
-  // its MFMA slots: the visibility word (the ring slot of a tile that is not
-  // binary holds zeros and is not used), the hidden-key bits of this lane's 16
-  // keys (none outside binary tiles), then the entries.
-  auto bias_word = [&](auto I, int s) __attribute__((always_inline)) -> uint64_t {
+  // the visibility word of stream i's query in the word slot at byte offset boff
+  auto bias_word = [&](auto I, uint32_t boff) __attribute__((always_inline)) -> uint64_t {
     constexpr int i = decltype(I)::value;
-    return *reinterpret_cast<const lds_u64_t*>(lds + kBitsRing + ((s >> 1) % kNB) * kBitsSlot + q_local[i] * 8);
+    return *reinterpret_cast<const lds_u64_t*>(lds + kBitsRing + boff + q_local[i] * 8);
   };
-  auto bias_hidden = [&](int s, int e, uint64_t w64) __attribute__((always_inline)) -> int {
-    const int hv = static_cast<int>(~static_cast<uint32_t>(w64 >> (32 * (s & 1) + 4 * hi)));
-    return (e >> 24) == 2 ? hv : 0;
-  };
-  auto bias_entry = [&](auto I, int r, int hv) __attribute__((always_inline)) -> float {
-    constexpr int i = decltype(I)::value;
-    const float b = __int_as_float(__builtin_amdgcn_sbfe(hv, 8 * (r >> 2) + (r & 3), one) & static_cast<int>(kNegInfBits));
-    bias[i][r] = b;
-    return b;
-  };
-  auto set_bias = [&](auto I, int s, int e) __attribute__((always_inline)) {
-    const int hv = bias_hidden(s, e, bias_word(I, s));
+  auto bias_build = [&](int half, uint64_t w64) __attribute__((always_inline)) -> f32x16_t {
+    const int hv = static_cast<int>(~static_cast<uint32_t>(w64 >> (32 * half + 4 * hi)));   // hidden keys
+    f32x16_t bb;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) bias_entry(I, r, hv);
+    for (int r = 0; r < 16; ++r)
+      bb[r] = __int_as_float(__builtin_amdgcn_sbfe(hv, 8 * (r >> 2) + (r & 3), one) & static_cast<int>(kNegInfBits));
+    return bb;
   };
-  // a phase's vector side work, slot by slot: the bias of stream I for step s
-  // of entry e (word read in slot 0, one entry formed per slot in slots 4-19)
-  struct BiasJob { uint64_t w; int hv; };
-  auto bias_slot = [&](auto I, auto K, int s, int e, BiasJob& job) __attribute__((always_inline)) {
-    constexpr int k = decltype(K)::value;
-    if constexpr (k == 0) job.w = bias_word(I, s);
-    if constexpr (k == 4) job.hv = bias_hidden(s, e, job.w);
-    if constexpr (k >= 4 && k < 20) {
-      const float b = bias_entry(I, k - 4, job.hv);
-      asm volatile("" :: "v"(b));   // formed here, not sunk to its MFMA
-    }
+  // A phase prefetches the visibility word its stream's next scores need (slot
+  // 0); after the phase the block is built from it only when that step's tile is
+  // binary (a uniform branch), and the next phase's first score MFMA reads it
+  // only then.  Steps of the other tiles, most of them, build nothing.
+  auto bias_slot = [&](auto I, auto K, uint32_t boff, uint64_t& w) __attribute__((always_inline)) {
+    if constexpr (decltype(K)::value == 0) w = bias_word(I, boff);
+  };
+  auto bias_fix = [&](int half, int e, uint64_t w) __attribute__((always_inline)) {
+    if ((e >> 24) == 2) biasb = bias_build(half, w);
   };
 
   // p = exp2(fma(x, ca, cb)) -> pk (bf16 pairs); returns the lane's sum of the
@@ -470,6 +490,8 @@ attn_fwd_bf16(AttnBf16Args a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[r] -= m_use;
     l_run[i] += probs(pk, x, kLog2e, 0.f);
+    first[i] = __any(m_run[i] == -INFINITY);
+    cbs[i] = stab_off(m_run[i]);
   };
   // ---- one phase of the accumulation pass, scheduled by hand: 20 slots
   // separated by scheduling barriers.  Slot k issues the k-th MFMA of stream
@@ -484,12 +506,12 @@ attn_fwd_bf16(AttnBf16Args a) {
   // pair of scores u-2 and u-1 and the fp32 sum of score u-1).  Starting the softmax two MFMA
   // issues into the phase keeps the other stream's last score MFMA of the
   // previous phase at a safe distance from its readers.  Returns the lane's sum.
-  auto phase_fast = [&](auto MSc, auto RELOAD, auto EXTRA, auto VEXTRA, int ks, int vsl)
+  auto phase_fast = [&](auto MSc, auto RELOAD, auto EXTRA, auto VEXTRA, uint32_t ks, uint32_t vsl, int bin)
       __attribute__((always_inline)) -> float {
     constexpr int ms = decltype(MSc)::value;
     constexpr int vs = 1 - ms;
     constexpr bool reload = decltype(RELOAD)::value;
-    const float cb = -m_run[vs] * kLog2e;
+    const float cb = cbs[vs];
     f32x16_t acc;
     float p[16];
     float l0 = 0.f, l1 = 0.f;
@@ -498,7 +520,8 @@ attn_fwd_bf16(AttnBf16Args a) {
       constexpr int op = kSlotOp[k];
       if constexpr (op < 100) {
         constexpr int c = op;
-        mfma_s<c == 0>(acc, kreg[c], qf[ms][c], bias[ms]);
+        if constexpr (c == 0) mfma_s_first(bin, acc, kreg[c], qf[ms][c], biasb);
+        else mfma_s<0>(acc, kreg[c], qf[ms][c], biasb);
         if constexpr (reload) kreg[c] = read_k(ks, c);
       } else {
         constexpr int v = op - 100, st = v >> 2, j = v & 3;
@@ -529,17 +552,18 @@ attn_fwd_bf16(AttnBf16Args a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     });
-    // The first score MFMA reads bias[MS] as its C operand over its whole
+    // The first score MFMA reads the bias block as its C operand over its whole
     // execution; an asm MFMA is opaque to the compiler's hazard checks, so keep
     // those registers out of reuse (e.g. by the other stream's bias formed in
     // this phase) until the phase is over.
-    asm volatile("" :: "v"(bias[ms]));
+    asm volatile("" :: "v"(biasb));
     s[ms] = acc;
     return l0 + l1;
   };
   // ---- one phase of the max-only pass: scores of the next step for stream MS,
   // the maximum of stream VS's step
-  auto phase_max = [&](auto MSc, auto RELOAD, auto EXTRA, auto VEXTRA, int ks, int e, int half, bool live)
+  auto phase_max = [&](auto MSc, auto RELOAD, auto EXTRA, auto VEXTRA, uint32_t ks, int e, int half, bool live,
+                       int bin)
       __attribute__((always_inline)) {
     constexpr int ms = decltype(MSc)::value;
     constexpr int vs = 1 - ms;
@@ -547,7 +571,8 @@ attn_fwd_bf16(AttnBf16Args a) {
     f32x16_t acc;
     static_for<kDqk / 16>([&](auto C) __attribute__((always_inline)) {
       constexpr int c = decltype(C)::value;
-      mfma_s<c == 0>(acc, kreg[c], qf[ms][c], bias[ms]);
+      if constexpr (c == 0) mfma_s_first(bin, acc, kreg[c], qf[ms][c], biasb);
+      else mfma_s<0>(acc, kreg[c], qf[ms][c], biasb);
       if constexpr (decltype(RELOAD)::value) kreg[c] = read_k(ks, c);
     });
     static_for<20>([&](auto K) __attribute__((always_inline)) { VEXTRA(K); });
@@ -560,29 +585,34 @@ attn_fwd_bf16(AttnBf16Args a) {
     }
   };
   // ---- one phase: matrix work of stream MS and softmax of stream VS = 1 - MS
-  // for the step at (entry e, half); the exact path follows when the step is
-  // general or ragged, a lane has no stabiliser yet, or a probability may exceed
-  // the headroom
-  auto phase = [&](auto MSc, auto MODE, auto RELOAD, auto EXTRA, auto VEXTRA, int ks, int vsl, int e, int half,
-                   bool live)
+  // for the step at (entry e, half); the exact path follows when the step's tile
+  // is slow (slow_tile), a lane has no stabiliser yet, or a probability may
+  // exceed the headroom
+  auto phase = [&](auto MSc, auto MODE, auto RELOAD, auto EXTRA, auto VEXTRA, uint32_t ks, uint32_t vsl, int e,
+                   int half, bool live, int bin, bool slow_e)
       __attribute__((always_inline)) {
     constexpr int vs = 1 - decltype(MSc)::value;
     if constexpr (decltype(MODE)::value == kPassMax) {
-      phase_max(MSc, RELOAD, EXTRA, VEXTRA, ks, e, half, live);
+      phase_max(MSc, RELOAD, EXTRA, VEXTRA, ks, e, half, live, bin);
     } else {
-      const int cls = e >> 24;
-      const bool slow = cls == 3 || (e & 0xFFFFFF) * kTileN + 32 * half + 32 > a.Lk || __any(m_run[vs] == -INFINITY);
-      const float lsum = phase_fast(MSc, RELOAD, EXTRA, VEXTRA, ks, vsl);
+      const bool slow = slow_e || first[vs];
+      const float lsum = phase_fast(MSc, RELOAD, EXTRA, VEXTRA, ks, vsl, bin);
       // the fast path's results are used on every path, so the compiler keeps it
       // in the scheduled block instead of moving it behind the test below
       asm volatile("" :: "v"(lsum), "v"(pk[vs][0]), "v"(pk[vs][1]), "v"(pk[vs][2]), "v"(pk[vs][3]), "v"(pk[vs][4]),
                    "v"(pk[vs][5]), "v"(pk[vs][6]), "v"(pk[vs][7]));
-      if (live) {
-        if (__builtin_expect(slow || __any(!(lsum <= kSumLimit)), 0))   // NaN sums too
-          soft_exact(IC<vs>{}, e, half, s[vs], pk[vs]);
-        else
-          l_run[vs] += lsum;
-      }
+      // A fast step whose probabilities exceed the headroom (or are not
+      // finite) is not redone here: l_max and l_run record it, and the pass's
+      // end sends the item to the two-pass rerun, which recomputes every step
+      // (the test costs one max per phase instead of a branch on fresh sums).
+      // The fast step's sums are added without a branch (nothing for a step
+      // past the end or one the exact path redoes); the exact path is the only
+      // branch, rarely taken.
+      const bool exact = live && slow;
+      const float la = live && !slow ? lsum : 0.f;
+      l_run[vs] += la;
+      l_max[vs] = fmaxf(l_max[vs], la);
+      if (__builtin_expect(exact, 0)) soft_exact(IC<vs>{}, e, half, s[vs], pk[vs]);
     }
   };
 
@@ -592,27 +622,33 @@ attn_fwd_bf16(AttnBf16Args a) {
     // prologue: K(0..3), V(0..2), words of tiles 0, 1 land; scores of step 0 for
     // both streams and stream 0's softmax of step 0; V(0) and the first K(1)
     // chunks into registers
-    int e0 = entry(0), e1 = entry(1), e2 = entry(2), e3 = entry(3);   // tiles T .. T+3 (T = t/2)
-    issue_k(0, key0_of(e0, 0));
-    issue_k(1, key0_of(e0, 1));
-    issue_k(2, key0_of(e1, 0));
-    issue_k(3, key0_of(e1, 1));
-    issue_v(0, key0_of(e0, 0));
-    issue_v(1, key0_of(e0, 1));
-    issue_v(2, key0_of(e1, 0));
+    int e0 = entry(0), e1 = entry(1), e2 = entry(2), e3 = entry(3);   // tiles T .. T+3
+    issue_k(lds_k + 0 * kKSlot, key0_of(e0, 0));
+    issue_k(lds_k + 1 * kKSlot, key0_of(e0, 1));
+    issue_k(lds_k + 2 * kKSlot, key0_of(e1, 0));
+    issue_k(lds_k + 3 * kKSlot, key0_of(e1, 1));
+    issue_v(lds_v + 0 * kVSlot, key0_of(e0, 0));
+    issue_v(lds_v + 1 * kVSlot, key0_of(e0, 1));
+    issue_v(lds_v + 2 * kVSlot, key0_of(e1, 0));
     issue_bits(0, e0);
-    issue_bits(1, e1);
+    issue_bits(kBitsSlot, e1);
     wait_vmem<0>();
     __syncthreads();
-    set_bias(IC<0>{}, 0, e0);
-    set_bias(IC<1>{}, 0, e0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      first[i] = __any(m_run[i] == -INFINITY);
+      cbs[i] = stab_off(m_run[i]);
+    }
     {
+      const bool bin0 = (e0 >> 24) == 2;
+      const f32x16_t b0 = bin0 ? bias_build(0, bias_word(IC<0>{}, 0)) : f32x16_t{};
+      const f32x16_t b1 = bin0 ? bias_build(0, bias_word(IC<1>{}, 0)) : f32x16_t{};
       f32x16_t a0, a1;
       static_for<kDqk / 16>([&](auto C) __attribute__((always_inline)) {
         constexpr int c = decltype(C)::value;
         const bf16x8_t kop = read_k(0, c);
-        mfma_s<c == 0>(a0, kop, qf[0][c], bias[0]);
-        mfma_s<c == 0>(a1, kop, qf[1][c], bias[1]);
+        mfma_s<c == 0 ? 1 : 0>(a0, kop, qf[0][c], b0);
+        mfma_s<c == 0 ? 1 : 0>(a1, kop, qf[1][c], b1);
       });
       s_nop_after_mfma(a0);
       s_nop_after_mfma(a1);
@@ -628,20 +664,22 @@ attn_fwd_bf16(AttnBf16Args a) {
         soft_exact(IC<0>{}, e0, 0, s[0], pk[0]);
       }
     }
-    set_bias(IC<0>{}, 1, e0);
+    bias_fix(1, e0, bias_word(IC<0>{}, 0));            // stream 0, step 1 (the first phase A)
 #pragma unroll
     for (int op = 0; op < 8; ++op) vf[op] = read_v(0, op);
 #pragma unroll
-    for (int c = 0; c < kDqk / 16; ++c) kreg[c] = read_k(1, c);
+    for (int c = 0; c < kDqk / 16; ++c) kreg[c] = read_k(kKSlot, c);
     __syncthreads();
 
-    // Step t (tile T = t/2 in e0, T+1 in e1, T+2 in e2; half t&1).  K(s) lives in
-    // K slot s%4, V(s) in V slot s%3, the words of tile T in slot T%3.  Registers
-    // on entry: vf = V(t), kreg = K(t+1), s[1] = stream 1's raw scores of step
-    // t, pk[0] = stream 0's P^T of step t.
+    // Tile T (entries e0 .. e3 = tiles T .. T+3), steps t = 2T + H (H = 0, 1).
+    // K(s) lives in K slot s%4, V(s) in V slot s%3, the words of tile T in word
+    // slot T%3; the slots are tracked as byte offsets (kpar = 2*kKSlot*(T&1),
+    // vs0..vs2 = V slots of steps t, t+1, t+2, bs0..bs2 = word slots of tiles
+    // T, T+1, T+2).  Registers on entry to step t: vf = V(t), kreg = K(t+1),
+    // s[1] = stream 1's raw scores of step t, pk[0] = stream 0's P^T of step t.
     //   copies: K(t+4) into K(t)'s slot (read in step t-1), V(t+3) into V(t)'s
-    //           slot (read into registers in step t-1) and, at even t, the words
-    //           of tile T+2
+    //           slot (read into registers in step t-1) and, at H = 0, the
+    //           words of tile T+2
     //   phase A: matrix of stream 0 (scores t+1 from K(t+1), PV t)
     //            || softmax of stream 1, step t
     //   phase B: matrix of stream 1 (scores t+1 from K(t+1), PV t; K(t+2)
@@ -650,49 +688,67 @@ attn_fwd_bf16(AttnBf16Args a) {
     //   then each wave waits for its copies of step t-1 and the workgroup
     //   synchronises: K(t+3), V(t+2) and their words are published, the slots
     //   read in step t are free.
-    for (int t = 0; t < nsteps; ++t) {
-      const int half = t & 1;
-      const int k4 = t & 3;
-      const int k42 = (t + 2) & 3;
-      const int v3 = t % 3;
-      const int v31 = v3 == 2 ? 0 : v3 + 1;          // (t+1) % 3
-      // copies of the step, one per MFMA slot: K(t+4) and (even t) the words of
-      // tile T+2 in phase A, V(t+3) in phase B
-      const int kkey = key0_of(e2, half);                              // K(t+4)
-      const int vkey = half ? key0_of(e2, 0) : key0_of(e1, 1);         // V(t+3)
-      const int bslot = ((t >> 1) + 2) % kNB;
-      auto copies_a = [&](auto K) __attribute__((always_inline)) {
-        constexpr int k = decltype(K)::value;
-        if constexpr (k % 3 == 1 && k / 3 < 6) issue_k_piece(IC<k / 3>{}, k4, kkey);
-        if constexpr (k == 18) issue_bits(bslot, e2);
+    uint32_t kpar = 0;
+    uint32_t vs0 = 0, vs1 = kVSlot, vs2 = 2 * kVSlot;
+    uint32_t bs0 = 0, bs1 = kBitsSlot, bs2 = 2 * kBitsSlot;
+    for (int T = 0; T < ntiles; ++T) {
+      const bool slow0 = slow_tile(e0), slow1 = slow_tile(e1);
+      auto step = [&](auto HC) __attribute__((always_inline)) {
+        constexpr int H = decltype(HC)::value;
+        const uint32_t kcopy = lds_k + kpar + H * kKSlot;               // K slot of steps t and t+4
+        const uint32_t kread = (kpar ^ (2 * kKSlot)) + H * kKSlot;      // K slot of step t+2
+        const int kkey = key0_of(e2, H);                                 // K(t+4)
+        const int vkey = H ? key0_of(e2, 0) : key0_of(e1, 1);            // V(t+3)
+        const int es1 = H ? e1 : e0;                                     // tile of step t+1
+        const uint32_t vcopy = lds_v + vs0, vread = vs1;
+        const uint32_t bcopy = bs2, bnext = H ? bs1 : bs0, bafter = bs1;  // word slots: T+2, tile of t+1, of t+2
+        // copies of the step, one per MFMA slot: K(t+4) and (H = 0) the words of
+        // tile T+2 in phase A, V(t+3) in phase B
+        auto copies_a = [&](auto K) __attribute__((always_inline)) {
+          constexpr int k = decltype(K)::value;
+          if constexpr (k % 3 == 1 && k / 3 < 6) issue_k_piece(IC<k / 3>{}, kcopy, kkey);
+          if constexpr (H == 0 && k == 18) issue_bits(bcopy, e2);
+        };
+        auto copies_b = [&](auto K) __attribute__((always_inline)) {
+          constexpr int k = decltype(K)::value;
+          if constexpr (k % 4 == 1 && k / 4 < 4) issue_v_piece(IC<k / 4>{}, vcopy, vkey);
+        };
+        // visibility words prefetched in the phases: stream 1's for step t+1
+        // (phase B's scores) in phase A, stream 0's for step t+2 (the next phase
+        // A) in phase B
+        uint64_t w1, w0;
+        auto bias_a = [&](auto K) __attribute__((always_inline)) { bias_slot(IC<1>{}, K, bnext, w1); };
+        auto bias_b = [&](auto K) __attribute__((always_inline)) { bias_slot(IC<0>{}, K, bafter, w0); };
+        const int bin = (es1 >> 25) & ~(es1 >> 24) & 1;   // class 2: both phases score step t+1
+        // ---- phase A
+        phase(IC<0>{}, MODE, std::false_type{}, copies_a, bias_a, kread, 0u, e0, H, true, bin, slow0);
+        bias_fix(H ^ 1, es1, w1);
+        // ---- phase B
+        phase(IC<1>{}, MODE, std::true_type{}, copies_b, bias_b, kread, vread, es1, H ^ 1, H == 0 || T + 1 < ntiles,
+              bin, H ? slow1 : slow0);
+        bias_fix(H, e1, w0);
+        // copies of step t-1 complete (those of step t may still be in flight)
+        wait_vmem<H == 0 ? 11 : 10>();
+        step_barrier();
+        const uint32_t tv = vs0;
+        vs0 = vs1; vs1 = vs2; vs2 = tv;
       };
-      auto copies_b = [&](auto K) __attribute__((always_inline)) {
-        constexpr int k = decltype(K)::value;
-        if constexpr (k % 4 == 1 && k / 4 < 4) issue_v_piece(IC<k / 4>{}, v3, vkey);
-      };
-      // biases built during the phases: stream 1's for step t+1 (phase B's
-      // scores) in phase A, stream 0's for step t+2 (the next phase A) in phase B
-      const int es1 = half ? e1 : e0;
-      BiasJob job1, job0;
-      auto bias_a = [&](auto K) __attribute__((always_inline)) { bias_slot(IC<1>{}, K, t + 1, es1, job1); };
-      auto bias_b = [&](auto K) __attribute__((always_inline)) { bias_slot(IC<0>{}, K, t + 2, e1, job0); };
-      // ---- phase A
-      phase(IC<0>{}, MODE, std::false_type{}, copies_a, bias_a, k42, 0, e0, half, true);
-      // ---- phase B
-      phase(IC<1>{}, MODE, std::true_type{}, copies_b, bias_b, k42, v31, es1, half ^ 1, t + 1 < nsteps);
-      // copies of step t-1 complete (those of step t, 11 per wave, may still be
-      // in flight)
-      wait_vmem<11>();
-      step_barrier();
-      if (half) {
-        e0 = e1; e1 = e2; e2 = e3;
-        e3 = entry((t >> 1) + 4);
-      }
+      step(IC<0>{});
+      step(IC<1>{});
+      const uint32_t tb = bs0;
+      bs0 = bs1; bs1 = bs2; bs2 = tb;
+      kpar ^= 2 * kKSlot;
+      e0 = e1; e1 = e2; e2 = e3;
+      e3 = entry(T + 4);
     }
     wait_vmem<0>();
   };
 
   run(IC<kPassNormal>{});
+  // fast steps beyond the headroom, or non-finite sums (NaN and inf fail both tests)
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    if (!(l_max[i] <= kSumLimit) || !(l_run[i] <= 3.0e38f)) over = true;
   // Some row of the item rose more than the headroom above its stabiliser: both
   // waves take the second pass (row maxima, then the accumulation again with the
   // exact maxima as stabilisers, which no probability can exceed).
@@ -798,10 +854,12 @@ hipError_t launch_attn_combine(const AttnCombineArgs& a, hipStream_t s) {
 
 hipError_t launch_attn_bf16(const AttnBf16Args& a, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(a.B) * a.nqt * a.H * a.nsplit;
-  if (a.mask && a.mask_bf16)
-    hipLaunchKernelGGL(attn_fwd_bf16<true>, dim3(grid), dim3(kThreads), 0, s, a);
+  if (!a.counts)
+    hipLaunchKernelGGL((attn_fwd_bf16<false, false>), dim3(grid), dim3(kThreads), 0, s, a);
+  else if (a.mask && a.mask_bf16)
+    hipLaunchKernelGGL((attn_fwd_bf16<true, true>), dim3(grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(attn_fwd_bf16<false>, dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_bf16<false, true>), dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
