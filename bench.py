@@ -91,9 +91,11 @@ def kernel_sha() -> str:
 
 
 class SclkSampler:
-    """Samples the shader clock the driver reports (amdsmi's GFX clock, else the
-    sysfs pp_dpm_sclk level marked '*') from a thread while the timed region
-    runs; None where neither is readable."""
+    """Samples the shader clock the driver reports from a thread while the GPU
+    runs the warm-up and the timed steps: amdsmi's GPU metrics (the SMU's average
+    GFX clock, else the mean of the current per-XCC clocks), else sysfs
+    pp_dpm_sclk.  Readings below 500 MHz are idle or deep-sleep values, not the
+    clock of a busy GPU, and are dropped; None where nothing usable is read."""
 
     def __init__(self, period_s: float = 0.005):
         import glob
@@ -116,6 +118,18 @@ class SclkSampler:
         if self.smi is not None:
             try:
                 import amdsmi
+                m = amdsmi.amdsmi_get_gpu_metrics_info(self.smi)
+                v = m.get("average_gfxclk_frequency")
+                if not isinstance(v, (int, float)) or v <= 0 or v >= 0xFFFF:
+                    cur = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 0xFFFF]
+                    v = sum(cur) / len(cur) if cur else None
+                if v is not None:
+                    self.source = "amdsmi GPU metrics GFX clock during warm-up and timed steps"
+                    return float(v)
+            except Exception:
+                pass
+            try:
+                import amdsmi
                 info = amdsmi.amdsmi_get_clock_info(self.smi, amdsmi.AmdSmiClkType.GFX)
                 return float(info["clk"])
             except Exception:
@@ -132,7 +146,7 @@ class SclkSampler:
     def _run(self):
         while not self.stop.is_set():
             v = self._read()
-            if v is not None:
+            if v is not None and v >= 500:
                 self.samples.append(v)
             self.stop.wait(self.period)
 
@@ -221,14 +235,14 @@ def measure(wl, steps: int, warmup: int, structured: bool = False) -> dict:
     torch.cuda.synchronize()
     # then keep the GPU busy for at least --warm-seconds so its clocks settle at
     # their sustained level before the timed steps (untimed)
-    t_warm = time.perf_counter()
-    while time.perf_counter() - t_warm < WARM["seconds"]:
-        for _ in range(8):
-            step(scratch)
-        torch.cuda.synchronize()
     marks = [[ev() for _ in range(4)] for _ in range(steps)]
     start, end = ev(), ev()
     with SclkSampler() as sclk:
+        t_warm = time.perf_counter()
+        while time.perf_counter() - t_warm < WARM["seconds"]:
+            for _ in range(8):
+                step(scratch)
+            torch.cuda.synchronize()
         t0 = time.perf_counter()
         start.record()
         for k in range(steps):
