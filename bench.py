@@ -206,7 +206,7 @@ def measure(wl, steps: int, warmup: int, structured: bool = False) -> dict:
         kn, v = wl.k_nope.to(dev), wl.v.to(dev)
     ws = mla.new_workspace(wl.B, wl.Lq, wl.Lk, dev, H=wl.H)   # room for key-split partials on small grids
     extra = mla.attn_split_workspace_bytes(wl.B, wl.H, wl.Lq, wl.Lk) - mla.attn_workspace_bytes(wl.B, wl.Lq, wl.Lk)
-    key_runs = 1 if wl.dtype != "bf16" or extra <= 0 else round(extra / (wl.B * wl.H * wl.Lq * (wl.Dv * 4 + 4)))
+    key_runs = 1 if wl.dtype != "bf16" or extra <= 0 else round(extra / (wl.B * wl.H * wl.Lq * (wl.Dv * 2 + 4)))
     anchors = torch.as_tensor(wl.anchors.astype("int32")).to(dev)
     ctx_valid = torch.full((wl.B,), wl.ctx_valid, dtype=torch.int32, device=dev)
     out = torch.empty((wl.B, wl.H, wl.Lq, wl.Dv), dtype=q.dtype, device=dev)

@@ -102,7 +102,7 @@ int attn_splits(int64_t B, int64_t H, int64_t Lq, int64_t Lk) {
   return sp;
 }
 
-// Workspace of a split forward: the tile map, then part_o [S,B,H,Lq,Dv] f32 and
+// Workspace of a split forward: the tile map, then part_o [S,B,H,Lq,Dv] bf16 and
 // part_lse [S,B,H,Lq] f32.  Returns false on overflow / invalid sizes.
 struct SplitLayout {
   int nsplit;
@@ -114,7 +114,7 @@ bool split_layout(int64_t B, int64_t H, int64_t Lq, int64_t Lk, SplitLayout* L) 
   L->nsplit = attn_splits(B, H, Lq, Lk);
   int64_t rows, n;
   if (!mul_ok(B, H, &rows) || !mul_ok(rows, Lq, &rows) || !mul_ok(rows, L->nsplit, &n) ||
-      !mul_ok(n, static_cast<int64_t>(dflash::kDv) * 4, &n))
+      !mul_ok(n, static_cast<int64_t>(dflash::kDv) * 2, &n))
     return false;
   if (L->nsplit == 1) {
     L->part_o = L->part_lse = L->total = t.total;
@@ -483,7 +483,7 @@ dflash_status attn_impl(const void* q, const void* k_nope, const void* k_rope_sh
   a.nsplit = sl.nsplit;
   if (sl.nsplit > 1) {
     char* ws = static_cast<char*>(workspace);
-    a.part_o = reinterpret_cast<float*>(ws + sl.part_o);
+    a.part_o = reinterpret_cast<uint16_t*>(ws + sl.part_o);
     a.part_lse = reinterpret_cast<float*>(ws + sl.part_lse);
     a.lse = nullptr;
   }

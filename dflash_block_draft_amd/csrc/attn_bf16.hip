@@ -782,19 +782,18 @@ attn_fwd_bf16(AttnBf16Args a) {
     const float l = halves_sum(l_run[i]);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const float lse_row = l > 0.f ? m_run[i] + __logf(l) : -INFINITY;
-    if (a.part_o) {            // one run of a split row: fp32 partials for the combine
+    if (a.part_o) {            // one run of a split row: bf16 partials for the combine
       const size_t prow = (static_cast<size_t>(sp) * a.B * a.H + bh) * a.Lq + q_row[i];
       if (q_ok[i] && hi == 0) a.part_lse[prow] = lse_row;
       if (q_ok[i]) {
-        float* pp = a.part_o + prow * kDv;
+        uint16_t* pp = a.part_o + prow * kDv;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            f32x4_t x;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) x[c] = o[i][j][4 * g + c] * inv;
-            *reinterpret_cast<f32x4_t*>(pp + 32 * j + 8 * g + 4 * hi) = x;
+            const u32x2_t w2 = {pack_bf16x2(o[i][j][4 * g] * inv, o[i][j][4 * g + 1] * inv),
+                                pack_bf16x2(o[i][j][4 * g + 2] * inv, o[i][j][4 * g + 3] * inv)};
+            *reinterpret_cast<u32x2_t*>(pp + 32 * j + 8 * g + 4 * hi) = w2;
           }
       }
       continue;
@@ -832,7 +831,9 @@ __global__ void __launch_bounds__(256) attn_combine(AttnCombineArgs a) {
       const float ls = a.part_lse[sp * a.rows + row];
       if (ls == -INFINITY) continue;
       const float w = __builtin_amdgcn_exp2f((ls - mx) * kLog2e);
-      const f32x4_t o = *reinterpret_cast<const f32x4_t*>(a.part_o + (sp * a.rows + row) * kDv + d);
+      const u32x2_t ob = *reinterpret_cast<const u32x2_t*>(a.part_o + (sp * a.rows + row) * kDv + d);
+      const f32x4_t o = {__uint_as_float(ob[0] << 16), __uint_as_float(ob[0] & 0xFFFF0000u),
+                         __uint_as_float(ob[1] << 16), __uint_as_float(ob[1] & 0xFFFF0000u)};
       wsum += w;
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc[c] = __builtin_fmaf(w, o[c], acc[c]);

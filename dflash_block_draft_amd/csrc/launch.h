@@ -25,17 +25,17 @@ struct AttnBf16Args {
   int mask_bf16;          // 1: mask is bf16, 0: f32
   float* lse;             // [B,H,Lq] f32 natural-log row normaliser (-inf: dead row), or null
   // key-range split: work item (b, q-tile, h) is cut into nsplit contiguous runs of
-  // its tile list; with nsplit > 1 each run writes its normalised fp32 output and
-  // its row normaliser to part_o [nsplit,B,H,Lq,128] / part_lse [nsplit,B,H,Lq]
-  // instead of out / lse, and launch_attn_combine merges them
+  // its tile list; with nsplit > 1 each run writes its normalised output (bf16,
+  // RNE) and its row normaliser (f32) to part_o [nsplit,B,H,Lq,128] / part_lse
+  // [nsplit,B,H,Lq] instead of out / lse, and launch_attn_combine merges them
   int nsplit;
-  float* part_o;
+  uint16_t* part_o;
   float* part_lse;
 };
 
 // out / lse of a split forward from its partial results (fixed order over the splits)
 struct AttnCombineArgs {
-  const float* part_o; const float* part_lse;
+  const uint16_t* part_o; const float* part_lse;
   uint16_t* out; float* lse;   // lse may be null
   int64_t rows;                // B*H*Lq
   int nsplit;

@@ -87,7 +87,8 @@ typedef enum dflash_dtype DFLASH_ENUM_BASE {
                                             each q-tile's key tiles into 2, 4 or 8 runs processed
                                             in parallel and merged in a fixed order (the pages'
                                             softmax, regrouped: results equal the unsplit call's up
-                                            to fp32 rounding; still deterministic run to run).  The
+                                            to bf16 rounding of each run's weights and output;
+                                            still deterministic run to run).  The
                                             workspace must then hold
                                             dflash_mla_attn_split_workspace_bytes(B, H, Lq, Lk).
                                             Ignored together with NO_TILE_SKIP. */

@@ -40,7 +40,7 @@ def _runs(B, H, Lq, Lk):
     extra = mla.attn_split_workspace_bytes(B, H, Lq, Lk) - mla.attn_workspace_bytes(B, Lq, Lk)
     if extra <= 0:
         return 1
-    per_run = B * H * Lq * (128 * 4 + 4)
+    per_run = B * H * Lq * (128 * 2 + 4)   # bf16 output + f32 normaliser per row and run
     return int(round(extra / per_run))
 
 
