@@ -586,8 +586,7 @@ attn_fwd_bf16(AttnBf16Args a) {
   };
   // ---- one phase: matrix work of stream MS and softmax of stream VS = 1 - MS
   // for the step at (entry e, half); the exact path follows when the step's tile
-  // is slow (slow_tile), a lane has no stabiliser yet, or a probability may
-  // exceed the headroom
+  // is slow (slow_tile) or a lane without a stabiliser sees a key in the step
   auto phase = [&](auto MSc, auto MODE, auto RELOAD, auto EXTRA, auto VEXTRA, uint32_t ks, uint32_t vsl, int e,
                    int half, bool live, int bin, bool slow_e)
       __attribute__((always_inline)) {
@@ -595,12 +594,19 @@ attn_fwd_bf16(AttnBf16Args a) {
     if constexpr (decltype(MODE)::value == kPassMax) {
       phase_max(MSc, RELOAD, EXTRA, VEXTRA, ks, e, half, live, bin);
     } else {
-      const bool slow = slow_e || first[vs];
       const float lsum = phase_fast(MSc, RELOAD, EXTRA, VEXTRA, ks, vsl, bin);
       // the fast path's results are used on every path, so the compiler keeps it
       // in the scheduled block instead of moving it behind the test below
       asm volatile("" :: "v"(lsum), "v"(pk[vs][0]), "v"(pk[vs][1]), "v"(pk[vs][2]), "v"(pk[vs][3]), "v"(pk[vs][4]),
                    "v"(pk[vs][5]), "v"(pk[vs][6]), "v"(pk[vs][7]));
+      // A lane without a stabiliser has the offset +FLT_MAX: its hidden keys
+      // (score -inf) get probability 0 and a visible key an infinite one.  While
+      // such a lane sees nothing (a key run that starts past its row's context),
+      // the fast step is exact for it (zeros); the first step in which it sees a
+      // key (sum not 0) goes to the exact path, which sets its stabiliser.
+      bool fresh = first[vs];
+      if (__builtin_expect(fresh, 0)) fresh = __any(m_run[vs] == -INFINITY && !(lsum == 0.f));
+      const bool slow = slow_e || fresh;
       // A fast step whose probabilities exceed the headroom (or are not
       // finite) is not redone here: l_max and l_run record it, and the pass's
       // end sends the item to the two-pass rerun, which recomputes every step
