@@ -655,7 +655,7 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_for(wl.name),
-                     "basis": "visible FLOPs (finite-mask pairs x heads x 640) / mean attention-kernel time (HIP events on its stream)"},
+                     "basis": "visible FLOPs (finite-mask pairs x heads x 640) / mean time of the attention call (HIP events on its stream: the attention kernel plus, where the key list is split into runs, the merge of the runs)"},
         "cpu_baseline": cpu,
         "host": host_info(),
         "sclk": head.get("sclk"),
