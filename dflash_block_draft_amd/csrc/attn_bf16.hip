@@ -182,18 +182,18 @@ __device__ __forceinline__ void mfma_s(f32x16_t& acc, bf16x8_t k, const u32x4_t&
     asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(kk), "a"(q));
 }
 // first chunk of a chain: from the bias block when the step's tile is binary
-// (bin != 0), else from zero; the choice is one scalar branch around the MFMA
-__device__ __forceinline__ void mfma_s_first(int bin, f32x16_t& acc, bf16x8_t k, const u32x4_t& q,
+// (class 2), else from zero; the choice is one scalar branch around the MFMA
+__device__ __forceinline__ void mfma_s_first(int cls, f32x16_t& acc, bf16x8_t k, const u32x4_t& q,
                                              const f32x16_t& bias) {
   const u32x4_t kk = __builtin_bit_cast(u32x4_t, k);
-  asm("s_cmp_eq_u32 %4, 0\n\t"
+  asm("s_cmp_lg_u32 %4, 2\n\t"
       "s_cbranch_scc1 1f\n\t"
       "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3\n\t"
       "s_branch 2f\n"
       "1:\n\t"
       "v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0\n"
       "2:"
-      : "=&v"(acc) : "v"(kk), "a"(q), "v"(bias), "s"(bin) : "scc");
+      : "=&v"(acc) : "v"(kk), "a"(q), "v"(bias), "s"(cls) : "scc");
 }
 // the MFMA result in acc is readable by the VALU after this (16 wait states)
 __device__ __forceinline__ void s_nop_after_mfma(f32x16_t& acc) {
@@ -248,26 +248,31 @@ attn_fwd_bf16(AttnBf16Args a) {
   const int32_t* list = LIST ? a.lists + tile_row0 + t_begin : nullptr;
   const int last = max(ntiles - 1, 0);
   int wbase = 0;                               // entries wbase .. wbase+63 are in lwin
-  int32_t lwin = LIST ? list[min(lane, last)] : 0;
+  // In the kernel an entry also carries bit 26, set for a slow tile (general
+  // mask values, or keys past Lk: its steps go to the exact path), added when
+  // the window is filled so the loop tests one bit.
+  auto tag_slow = [&](int32_t x) __attribute__((always_inline)) -> int32_t {
+    const bool slow = (x >> 24) == 3 || (x & 0xFFFFFF) * kTileN + kTileN > a.Lk;
+    return x | (slow ? 1 << 26 : 0);
+  };
+  int32_t lwin = LIST ? tag_slow(list[min(lane, last)]) : 0;
   auto entry = [&](int i) __attribute__((always_inline)) -> int {
     const int j = min(i, last);
     if constexpr (LIST) {
       if (j - wbase >= 64) {                   // entries are read in increasing order
         wbase = j;
-        lwin = list[min(j + lane, last)];
+        lwin = tag_slow(list[min(j + lane, last)]);
         asm volatile("" :: "v"(lwin));       // waited for here, not where the paths join
       }
       return __builtin_amdgcn_readlane(lwin, j - wbase);
     } else {
-      return (t_begin + j) | (1 << 24);
+      return tag_slow((t_begin + j) | (1 << 24));
     }
   };
   auto ktile = [](int e) __attribute__((always_inline)) -> int { return e & 0xFFFFFF; };
+  auto eclass = [](int e) __attribute__((always_inline)) -> int { return (e >> 24) & 3; };
   auto key0_of = [&](int e, int half) __attribute__((always_inline)) -> int { return ktile(e) * kTileN + 32 * half; };
-  // steps of tile e go to the exact path: general mask values, or keys past Lk
-  auto slow_tile = [&](int e) __attribute__((always_inline)) -> bool {
-    return (e >> 24) == 3 || ktile(e) * kTileN + kTileN > a.Lk;
-  };
+  auto slow_tile = [](int e) __attribute__((always_inline)) -> bool { return (e >> 26) & 1; };
 
   // ---- global -> LDS copy plan: wave w copies row block w (keys 16w .. 16w+15
   // of the step) of K (k_nope quads 0-3, k_rope quads 4-5) and of V (quads 0-3);
@@ -423,7 +428,7 @@ attn_fwd_bf16(AttnBf16Args a) {
     if constexpr (decltype(K)::value == 0) w = bias_word(I, boff);
   };
   auto bias_fix = [&](int half, int e, uint64_t w) __attribute__((always_inline)) {
-    if ((e >> 24) == 2) biasb = bias_build(half, w);
+    if (eclass(e) == 2) biasb = bias_build(half, w);
   };
 
   // p = exp2(fma(x, ca, cb)) -> pk (bf16 pairs); returns the lane's sum of the
@@ -447,7 +452,7 @@ attn_fwd_bf16(AttnBf16Args a) {
   // binary tile are -inf already: the score MFMAs started from their bias)
   auto masked_scores = [&](auto I, int e, int half, const f32x16_t& s, float* x) __attribute__((always_inline)) {
     constexpr int i = decltype(I)::value;
-    const int cls = e >> 24;
+    const int cls = eclass(e);
     // accumulator r <-> key kbase + 8*(r>>2) + (r&3)
     const int kbase = (e & 0xFFFFFF) * kTileN + 32 * half + 4 * hi;
     if (cls == 3 && a.mask) {   // (a reused map without its mask: no values to add)
@@ -506,7 +511,7 @@ attn_fwd_bf16(AttnBf16Args a) {
   // pair of scores u-2 and u-1 and the fp32 sum of score u-1).  Starting the softmax two MFMA
   // issues into the phase keeps the other stream's last score MFMA of the
   // previous phase at a safe distance from its readers.  Returns the lane's sum.
-  auto phase_fast = [&](auto MSc, auto RELOAD, auto EXTRA, auto VEXTRA, uint32_t ks, uint32_t vsl, int bin)
+  auto phase_fast = [&](auto MSc, auto RELOAD, auto EXTRA, auto VEXTRA, uint32_t ks, uint32_t vsl, int cls)
       __attribute__((always_inline)) -> float {
     constexpr int ms = decltype(MSc)::value;
     constexpr int vs = 1 - ms;
@@ -520,7 +525,7 @@ attn_fwd_bf16(AttnBf16Args a) {
       constexpr int op = kSlotOp[k];
       if constexpr (op < 100) {
         constexpr int c = op;
-        if constexpr (c == 0) mfma_s_first(bin, acc, kreg[c], qf[ms][c], biasb);
+        if constexpr (c == 0) mfma_s_first(cls, acc, kreg[c], qf[ms][c], biasb);
         else mfma_s<0>(acc, kreg[c], qf[ms][c], biasb);
         if constexpr (reload) kreg[c] = read_k(ks, c);
       } else {
@@ -563,7 +568,7 @@ attn_fwd_bf16(AttnBf16Args a) {
   // ---- one phase of the max-only pass: scores of the next step for stream MS,
   // the maximum of stream VS's step
   auto phase_max = [&](auto MSc, auto RELOAD, auto EXTRA, auto VEXTRA, uint32_t ks, int e, int half, bool live,
-                       int bin)
+                       int cls)
       __attribute__((always_inline)) {
     constexpr int ms = decltype(MSc)::value;
     constexpr int vs = 1 - ms;
@@ -571,7 +576,7 @@ attn_fwd_bf16(AttnBf16Args a) {
     f32x16_t acc;
     static_for<kDqk / 16>([&](auto C) __attribute__((always_inline)) {
       constexpr int c = decltype(C)::value;
-      if constexpr (c == 0) mfma_s_first(bin, acc, kreg[c], qf[ms][c], biasb);
+      if constexpr (c == 0) mfma_s_first(cls, acc, kreg[c], qf[ms][c], biasb);
       else mfma_s<0>(acc, kreg[c], qf[ms][c], biasb);
       if constexpr (decltype(RELOAD)::value) kreg[c] = read_k(ks, c);
     });
@@ -588,37 +593,43 @@ attn_fwd_bf16(AttnBf16Args a) {
   // for the step at (entry e, half); the exact path follows when the step's tile
   // is slow (slow_tile) or a lane without a stabiliser sees a key in the step
   auto phase = [&](auto MSc, auto MODE, auto RELOAD, auto EXTRA, auto VEXTRA, uint32_t ks, uint32_t vsl, int e,
-                   int half, bool live, int bin, bool slow_e)
+                   int half, bool live, int cls, bool slow_e)
       __attribute__((always_inline)) {
     constexpr int vs = 1 - decltype(MSc)::value;
     if constexpr (decltype(MODE)::value == kPassMax) {
-      phase_max(MSc, RELOAD, EXTRA, VEXTRA, ks, e, half, live, bin);
+      phase_max(MSc, RELOAD, EXTRA, VEXTRA, ks, e, half, live, cls);
     } else {
-      const float lsum = phase_fast(MSc, RELOAD, EXTRA, VEXTRA, ks, vsl, bin);
+      const float lsum = phase_fast(MSc, RELOAD, EXTRA, VEXTRA, ks, vsl, cls);
       // the fast path's results are used on every path, so the compiler keeps it
       // in the scheduled block instead of moving it behind the test below
       asm volatile("" :: "v"(lsum), "v"(pk[vs][0]), "v"(pk[vs][1]), "v"(pk[vs][2]), "v"(pk[vs][3]), "v"(pk[vs][4]),
                    "v"(pk[vs][5]), "v"(pk[vs][6]), "v"(pk[vs][7]));
-      // A lane without a stabiliser has the offset +FLT_MAX: its hidden keys
-      // (score -inf) get probability 0 and a visible key an infinite one.  While
-      // such a lane sees nothing (a key run that starts past its row's context),
-      // the fast step is exact for it (zeros); the first step in which it sees a
-      // key (sum not 0) goes to the exact path, which sets its stabiliser.
-      bool fresh = first[vs];
-      if (__builtin_expect(fresh, 0)) fresh = __any(m_run[vs] == -INFINITY && !(lsum == 0.f));
-      const bool slow = slow_e || fresh;
       // A fast step whose probabilities exceed the headroom (or are not
       // finite) is not redone here: l_max and l_run record it, and the pass's
       // end sends the item to the two-pass rerun, which recomputes every step
       // (the test costs one max per phase instead of a branch on fresh sums).
       // The fast step's sums are added without a branch (nothing for a step
-      // past the end or one the exact path redoes); the exact path is the only
-      // branch, rarely taken.
+      // past the end or one the exact path may redo); the exact path is the
+      // only branch, rarely taken.
+      const bool slow = slow_e || first[vs];
       const bool exact = live && slow;
       const float la = live && !slow ? lsum : 0.f;
       l_run[vs] += la;
       l_max[vs] = fmaxf(l_max[vs], la);
-      if (__builtin_expect(exact, 0)) soft_exact(IC<vs>{}, e, half, s[vs], pk[vs]);
+      if (__builtin_expect(exact, 0)) {
+        // A lane without a stabiliser has the offset +FLT_MAX: its hidden keys
+        // (score -inf) get probability 0 and a visible key an infinite one.
+        // While such a lane sees nothing (a key run that starts past its row's
+        // context) the fast step is exact for it (zeros), so a step of a fast
+        // tile needs the exact path only where one of them sees a key (sum not
+        // 0); that step sets its stabiliser.
+        if (!slow_e && !__any(m_run[vs] == -INFINITY && !(lsum == 0.f))) {
+          l_run[vs] += lsum;
+          l_max[vs] = fmaxf(l_max[vs], lsum);
+        } else {
+          soft_exact(IC<vs>{}, e, half, s[vs], pk[vs]);
+        }
+      }
     }
   };
 
@@ -646,7 +657,7 @@ attn_fwd_bf16(AttnBf16Args a) {
       cbs[i] = stab_off(m_run[i]);
     }
     {
-      const bool bin0 = (e0 >> 24) == 2;
+      const bool bin0 = eclass(e0) == 2;
       const f32x16_t b0 = bin0 ? bias_build(0, bias_word(IC<0>{}, 0)) : f32x16_t{};
       const f32x16_t b1 = bin0 ? bias_build(0, bias_word(IC<1>{}, 0)) : f32x16_t{};
       f32x16_t a0, a1;
@@ -725,17 +736,21 @@ attn_fwd_bf16(AttnBf16Args a) {
         uint64_t w1, w0;
         auto bias_a = [&](auto K) __attribute__((always_inline)) { bias_slot(IC<1>{}, K, bnext, w1); };
         auto bias_b = [&](auto K) __attribute__((always_inline)) { bias_slot(IC<0>{}, K, bafter, w0); };
-        const int bin = (es1 >> 25) & ~(es1 >> 24) & 1;   // class 2: both phases score step t+1
+        const int cls = eclass(es1);   // class of the tile of step t+1, which both phases score
         // ---- phase A
-        phase(IC<0>{}, MODE, std::false_type{}, copies_a, bias_a, kread, 0u, e0, H, true, bin, slow0);
+        phase(IC<0>{}, MODE, std::false_type{}, copies_a, bias_a, kread, 0u, e0, H, true, cls, slow0);
         bias_fix(H ^ 1, es1, w1);
         // ---- phase B
         phase(IC<1>{}, MODE, std::true_type{}, copies_b, bias_b, kread, vread, es1, H ^ 1, H == 0 || T + 1 < ntiles,
-              bin, H ? slow1 : slow0);
+              cls, H ? slow1 : slow0);
         bias_fix(H, e1, w0);
         // copies of step t-1 complete (those of step t may still be in flight)
         wait_vmem<H == 0 ? 11 : 10>();
         step_barrier();
+        // phase B's operand reads (the next step's K and V) have landed by now;
+        // one wait here replaces the compiler's countdown of a dozen waits in
+        // front of phase A's MFMAs
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt / expcnt not waited
         const uint32_t tv = vs0;
         vs0 = vs1; vs1 = vs2; vs2 = tv;
       };
