@@ -414,43 +414,58 @@ bwd_dkdv(AttnBwdArgs a) {
       e2 = e3;
       e3 = __builtin_amdgcn_readfirstlane(i + 4 < nch ? e4v : 0);
     }
+    // The last dK / dV MFMAs (inline asm, invisible to the hazard checks) must
+    // finish before the vector unit reads their accumulators: 24 wait states
+    // here, ahead of the barrier that every read below follows.  (An asm naming
+    // the accumulators as operands would make the allocator copy them into
+    // fresh register tuples.)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
     wait_vmem<0>();
     __syncthreads();
   }
 
   // ---- store: accumulator row r <-> key 8(r/4) + 4hi + r%4 of the wave's 32, column <-> dim.
-  // Rows r and r+1 are adjacent keys: lanes 2c and 2c+1 swap one value each, so
-  // that the even lane stores dims (2c, 2c+1) of row r and the odd lane those of
-  // row r+1, two elements per store.
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(dk[0]), "+a"(dk[1]), "+a"(dk[2]), "+a"(dk[3]), "+a"(dk[4]),
-               "+a"(dk[5]), "+a"(dv[0]), "+a"(dv[1]), "+a"(dv[2]), "+a"(dv[3]));
+  // Rows r and r+1 are adjacent keys: the even lane of a lane pair stores dims
+  // (2c, 2c+1) of row r and the odd lane those of row r+1, two elements per
+  // store.  For bf16 each lane packs its own (row r, row r+1) values of its dim,
+  // takes its partner's pack and picks one half of each (a byte permute).  The
+  // stores go through buffer resources spanning the (b, h) slice, whose range
+  // check drops the rows past Lk: no per-row tests.
   const bool odd = (li & 1) != 0;
-  auto swap_pair = [](float x) __attribute__((always_inline)) -> float {   // value of lane l ^ 1
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+  auto swap_pair = [](uint32_t x) __attribute__((always_inline)) -> uint32_t {   // value of lane l ^ 1
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), 0xB1, 0xF, 0xF, false));
   };
+  // byte selector over {partner (bytes 4-7), own (bytes 0-3)}: even lane (own.lo,
+  // partner.lo), odd lane (partner.hi, own.hi)
+  const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+  const uint32_t slice = static_cast<uint32_t>(a.Lk);
+  const __amdgpu_buffer_rsrc_t r_dk = __builtin_amdgcn_make_buffer_rsrc(a.dkn + bh * a.Lk * kDn, 0,
+                                                                       static_cast<int>(slice * (kDn * 2)), 0x00020000);
+  const __amdgpu_buffer_rsrc_t r_dv = __builtin_amdgcn_make_buffer_rsrc(a.dv + bh * a.Lk * kDv, 0,
+                                                                       static_cast<int>(slice * (kDv * 2)), 0x00020000);
+  const __amdgpu_buffer_rsrc_t r_rp = __builtin_amdgcn_make_buffer_rsrc(a.rope_part + bh * a.Lk * kDr, 0,
+                                                                       static_cast<int>(slice * (kDr * 4)), 0x00020000);
+  const int col = li & ~1;
+  const uint32_t row0 = static_cast<uint32_t>(kb * kKB + 32 * w + 4 * hi + (odd ? 1 : 0));
 #pragma unroll
   for (int r = 0; r < 16; r += 2) {
-    const int kj = kb * kKB + 32 * w + 8 * (r >> 2) + 4 * hi + (r & 3) + (odd ? 1 : 0);
-    const size_t row = bh * a.Lk + kj;
-    const int col = li & ~1;
+    const uint32_t row = row0 + 8 * (r >> 2) + (r & 3);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      const float k0 = dk[nt][r] * a.scale, k1 = dk[nt][r + 1] * a.scale, v0 = dv[nt][r], v1 = dv[nt][r + 1];
-      const float kx = swap_pair(odd ? k0 : k1), vx = swap_pair(odd ? v0 : v1);
-      const uint32_t kp = odd ? pack_bf16x2(kx, k1) : pack_bf16x2(k0, kx);
-      const uint32_t vp = odd ? pack_bf16x2(vx, v1) : pack_bf16x2(v0, vx);
-      if (kj < a.Lk) {
-        *reinterpret_cast<uint32_t*>(a.dkn + row * kDn + 32 * nt + col) = kp;
-        *reinterpret_cast<uint32_t*>(a.dv + row * kDv + 32 * nt + col) = vp;
-      }
+      const uint32_t kown = pack_bf16x2(dk[nt][r] * a.scale, dk[nt][r + 1] * a.scale);
+      const uint32_t vown = pack_bf16x2(dv[nt][r], dv[nt][r + 1]);
+      const uint32_t kp = __builtin_amdgcn_perm(swap_pair(kown), kown, sel);
+      const uint32_t vp = __builtin_amdgcn_perm(swap_pair(vown), vown, sel);
+      __builtin_amdgcn_raw_buffer_store_b32(kp, r_dk, static_cast<int>(row * (kDn * 2) + (32 * nt + col) * 2), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(vp, r_dv, static_cast<int>(row * (kDv * 2) + (32 * nt + col) * 2), 0, 0);
     }
 #pragma unroll
     for (int nt = 4; nt < 6; ++nt) {
       const float k0 = dk[nt][r] * a.scale, k1 = dk[nt][r + 1] * a.scale;
-      const float kx = swap_pair(odd ? k0 : k1);
+      const float kx = __uint_as_float(swap_pair(__float_as_uint(odd ? k0 : k1)));
       const u32x2_t pr = odd ? u32x2_t{__float_as_uint(kx), __float_as_uint(k1)}
                              : u32x2_t{__float_as_uint(k0), __float_as_uint(kx)};
-      if (kj < a.Lk) *reinterpret_cast<u32x2_t*>(a.rope_part + row * kDr + 32 * (nt - 4) + col) = pr;
+      __builtin_amdgcn_raw_buffer_store_b64(pr, r_rp, static_cast<int>(row * (kDr * 4) + (32 * (nt - 4) + col) * 4), 0, 0);
     }
   }
 }
