@@ -839,37 +839,56 @@ attn_fwd_bf16(AttnBf16Args a) {
 // out = sum_s w_s o_s / sum_s w_s and lse = max + log(sum_s w_s), summed in split
 // order (deterministic).  A row whose runs are all empty gives 0 and -inf.
 // One thread per 4 output columns, 32 threads per row.
+constexpr int kMaxRuns = 8;          // key runs per row (the split heuristic's cap)
+
 __global__ void __launch_bounds__(256) attn_combine(AttnCombineArgs a) {
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
+  // 16 lanes per row, 8 dims (16 bytes) per lane.  Every run's normaliser and
+  // partial are loaded up front (one memory round trip), then merged in run
+  // order.
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
   if (row >= a.rows) return;
-  const int d = (threadIdx.x & 31) * 4;
+  const int d = (threadIdx.x & 15) * 8;
+  float ls[kMaxRuns];
+  u32x4_t ob[kMaxRuns];
+#pragma unroll
+  for (int sp = 0; sp < kMaxRuns; ++sp) {
+    ls[sp] = -INFINITY;
+    ob[sp] = u32x4_t{0u, 0u, 0u, 0u};
+    if (sp < a.nsplit) {
+      ls[sp] = a.part_lse[sp * a.rows + row];
+      ob[sp] = *reinterpret_cast<const u32x4_t*>(a.part_o + (sp * a.rows + row) * kDv + d);
+    }
+  }
   float mx = -INFINITY;
-  for (int sp = 0; sp < a.nsplit; ++sp) mx = fmaxf(mx, a.part_lse[sp * a.rows + row]);
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int sp = 0; sp < kMaxRuns; ++sp) mx = fmaxf(mx, ls[sp]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (mx != -INFINITY) {
-    for (int sp = 0; sp < a.nsplit; ++sp) {
-      const float ls = a.part_lse[sp * a.rows + row];
-      if (ls == -INFINITY) continue;
-      const float w = __builtin_amdgcn_exp2f((ls - mx) * kLog2e);
-      const u32x2_t ob = *reinterpret_cast<const u32x2_t*>(a.part_o + (sp * a.rows + row) * kDv + d);
-      const f32x4_t o = {__uint_as_float(ob[0] << 16), __uint_as_float(ob[0] & 0xFFFF0000u),
-                         __uint_as_float(ob[1] << 16), __uint_as_float(ob[1] & 0xFFFF0000u)};
+#pragma unroll
+    for (int sp = 0; sp < kMaxRuns; ++sp) {
+      if (ls[sp] == -INFINITY) continue;              // also every run past nsplit
+      const float w = __builtin_amdgcn_exp2f((ls[sp] - mx) * kLog2e);
       wsum += w;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[c] = __builtin_fmaf(w, o[c], acc[c]);
+      for (int c = 0; c < 4; ++c) {
+        acc[2 * c] = __builtin_fmaf(w, __uint_as_float(ob[sp][c] << 16), acc[2 * c]);
+        acc[2 * c + 1] = __builtin_fmaf(w, __uint_as_float(ob[sp][c] & 0xFFFF0000u), acc[2 * c + 1]);
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  const u32x2_t w2 = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
-  *reinterpret_cast<u32x2_t*>(a.out + row * kDv + d) = w2;
+  const u32x4_t w4 = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                      pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+  *reinterpret_cast<u32x4_t*>(a.out + row * kDv + d) = w4;
   if (a.lse && d == 0) a.lse[row] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
 }
 
 }  // namespace
 
 hipError_t launch_attn_combine(const AttnCombineArgs& a, hipStream_t s) {
-  const unsigned grid = static_cast<unsigned>((a.rows + 7) / 8);
+  if (a.nsplit < 1 || a.nsplit > kMaxRuns) return hipErrorInvalidValue;
+  const unsigned grid = static_cast<unsigned>((a.rows + 15) / 16);
   hipLaunchKernelGGL(attn_combine, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
