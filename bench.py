@@ -110,6 +110,7 @@ class SclkSampler:
         except Exception:
             self.source = "sysfs pp_dpm_sclk during the timed steps"
         self.period = period_s
+        self.smi_failures = 0
         self.samples = []
         self.stop = threading.Event()
         self.thread = threading.Thread(target=self._run, daemon=True)
@@ -125,15 +126,22 @@ class SclkSampler:
                     v = sum(cur) / len(cur) if cur else None
                 if v is not None:
                     self.source = "amdsmi GPU metrics GFX clock during warm-up and timed steps"
+                    self.smi_failures = 0
                     return float(v)
             except Exception:
                 pass
             try:
                 import amdsmi
                 info = amdsmi.amdsmi_get_clock_info(self.smi, amdsmi.AmdSmiClkType.GFX)
+                self.smi_failures = 0
                 return float(info["clk"])
             except Exception:
-                self.smi = None
+                # a failed read (seen right after initialisation) is retried on
+                # the next sample; amdsmi is given up only after many in a row
+                self.smi_failures += 1
+                if self.smi_failures >= 50:
+                    self.smi = None
+                return None
         for path in self.files:
             try:
                 for line in open(path):
