@@ -91,14 +91,14 @@ bool tile_layout(int64_t B, int64_t Lq, int64_t Lk, TileLayout* t) {
 // once and the longest item sets the kernel time; with a block mask the items'
 // tile counts differ widely (the last q-tile of a workload sees the whole
 // context, the first only its start).  While the items fit in that one round,
-// each item's tile list is cut into 2, 4 or 8 runs, each run keeping >= 8
-// k-tiles: the launch order (longest q-tiles first) then hands the short runs to
-// the units that finished a long one.
+// each item's tile list is cut into 2, 4 or 8 runs while a run of the whole key
+// range keeps >= 4 k-tiles: the launch order (longest q-tiles first) then hands
+// the short runs to the units that finished a long one.
 int attn_splits(int64_t B, int64_t H, int64_t Lq, int64_t Lk) {
   const int64_t items = B * ((Lq + DFLASH_TILE_M - 1) / DFLASH_TILE_M) * H;
   const int64_t nkt = (Lk + DFLASH_TILE_N - 1) / DFLASH_TILE_N;
   int sp = 1;
-  while (sp < 8 && items * sp <= 512 && nkt / (2 * sp) >= 8) sp *= 2;
+  while (sp < 8 && items * sp <= 512 && nkt / (2 * sp) >= 4) sp *= 2;
   return sp;
 }
 

@@ -325,10 +325,14 @@ def test_split_keys_workspace_bytes(lib):
     assert m2 + 2 * rows2 * (128 * 2 + 4) <= sb(1, 64, 1024, 9216) <= m2 + 2 * rows2 * (128 * 2 + 4) + 3 * 256
     assert sb(1, 32, 4096, 36864) == mb(1, 4096, 36864)    # 1024 items: no split, the map alone
     assert sb(1, 2, 32, 96) == mb(1, 32, 96)               # 2 k-tiles: too short to split
-    # 2 batches x 2 q-tiles x 16 heads = 64 items over 36 k-tiles: 4 runs
+    # 2 batches x 2 q-tiles x 16 heads = 64 items over 36 k-tiles: 8 runs (a run
+    # of the whole key range keeps 36 / 8 = 4.5 >= 4 k-tiles)
     rows, m = 2 * 16 * 256, mb(2, 256, 2304)
     n = sb(2, 16, 256, 2304)
-    assert m + 4 * rows * (128 * 2 + 4) <= n <= m + 4 * rows * (128 * 2 + 4) + 3 * 256
+    assert m + 8 * rows * (128 * 2 + 4) <= n <= m + 8 * rows * (128 * 2 + 4) + 3 * 256
+    # 64 items over 28 k-tiles: 4 runs (8 would leave 28 / 8 = 3.5 < 4 k-tiles per run)
+    n4 = sb(2, 16, 256, 1792)
+    assert mb(2, 256, 1792) + 4 * rows * (128 * 2 + 4) <= n4 <= mb(2, 256, 1792) + 4 * rows * (128 * 2 + 4) + 3 * 256
     # 1 x 1 q-tile x 8 heads over 129 k-tiles: 8 runs (the cap)
     n8 = sb(1, 8, 16, 8208)
     assert n8 >= mb(1, 16, 8208) + 8 * 8 * 16 * (128 * 2 + 4)
