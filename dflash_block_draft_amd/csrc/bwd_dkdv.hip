@@ -348,8 +348,15 @@ bwd_dkdv(AttnBwdArgs a) {
       int hv = 0;
 
       // ---- phase A: dV(i) (slots 0-7), S(i+1) (slots 8-19); dS(i), offsets(i+1)
+      // Every operand is read 8 slots ahead of its MFMA.  One wait per 4 slots,
+      // for the operands (and the words and normalisers) read 8 to 5 slots back,
+      // replaces a wait in front of every MFMA; N counts the LDS reads issued
+      // since (slot 0 of phase A reads 4 values, slots 1-7 two, the rest one).
       static_for<20>([&](auto K) __attribute__((always_inline)) {
         constexpr int k = decltype(K)::value;
+        if constexpr (k == 0 || k == 12 || k == 16) wait_lgkm<4>();
+        if constexpr (k == 4) wait_lgkm<10>();
+        if constexpr (k == 8) wait_lgkm<8>();
         if constexpr (k < 12) fq[k] = *(const lds_u32x4_t*)(f1 + ((k & 1) ? q_lane1 : q_lane0) + (k >> 1) * 1024);
         if constexpr (k == 0) {
           word = *(const lds_u32_t*)(f1 + w_lane);
@@ -388,6 +395,7 @@ bwd_dkdv(AttnBwdArgs a) {
       // ---- phase B: dP(i+1) (slots 0-7), dK(i) (slots 8-19); P(i+1)
       static_for<20>([&](auto K) __attribute__((always_inline)) {
         constexpr int k = decltype(K)::value;
+        if constexpr (k % 4 == 0) wait_lgkm<4>();   // one read per slot in this phase
         if constexpr (k < 12) ft[k] = *(const lds_u32x4_t*)(t0 + ((k & 1) ? t_lane1 : t_lane0) + (k >> 1) * 2048);
         else fo[k - 12] = *(const lds_u32x4_t*)(t1 + ((k & 1) ? t_lane1 : t_lane0) + ((k - 12) >> 1) * 2048);
         if constexpr (k < 8) mfma_dp<k == 0>(dpp, fd[k], vq[k], nd);

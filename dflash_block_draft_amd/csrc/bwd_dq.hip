@@ -306,8 +306,13 @@ bwd_dq(AttnBwdArgs a) {
       int hv = 0;
 
       // ---- slots 0-13: S^T(j+1), dP^T(j+1) begins; dS(j); offsets of step j+1
+      // Every operand is read 8 slots ahead of its MFMA, one read per slot (slot
+      // 0 also reads the visibility word and a list entry).  One wait per 4
+      // slots, for the 4 operands read 8 to 5 slots back, replaces a wait in
+      // front of every MFMA.
       static_for<14>([&](auto K) __attribute__((always_inline)) {
         constexpr int k = decltype(K)::value;
+        if constexpr (k % 4 == 0) wait_lgkm<k == 4 ? 6 : 4>();
         if constexpr (k < 4) fk[8 + k] = *(const lds_u32x4_t*)(f1 + k_off(8 + k));
         if constexpr (k >= 4 && k < 12) fv[k - 4] = *(const lds_u32x4_t*)(f1 + (((k - 4) & 1) ? v_lane1 : v_lane0) + ((k - 4) >> 1) * 1024);
         if constexpr (k >= 12) ft[k - 12] = *(const lds_u32x4_t*)(t0 + kt_off(k - 12));
@@ -344,6 +349,7 @@ bwd_dq(AttnBwdArgs a) {
       // ---- slots 14-31: dP^T(j+1) ends, dQ(j); P(j+1)
       static_for<18>([&](auto K0) __attribute__((always_inline)) {
         constexpr int k = decltype(K0)::value + 14;
+        if constexpr (k % 4 == 0) wait_lgkm<4>();
         if constexpr (k < 24) ft[k - 12] = *(const lds_u32x4_t*)(t0 + kt_off(k - 12));
         if constexpr (k >= 24) fk[k - 24] = *(const lds_u32x4_t*)(f2 + k_off(k - 24));
         if constexpr (k < 20) mfma_dp<false>(dpp, fv[k - 12], of[k - 12], nd);

@@ -14,6 +14,13 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// s_waitcnt lgkmcnt(N) with vmcnt/expcnt left at their no-wait maxima.
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));
+}
+
 // 16 bytes per lane from a buffer straight into LDS at lds_base + OFF + 16*lane; reads past
 // the descriptor's num_records return zeros.  Issued as inline asm so the compiler
 // does not treat the in-flight LDS write as a dependency of unrelated LDS reads
