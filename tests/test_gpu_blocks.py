@@ -130,8 +130,9 @@ def test_block_reuse_tile_map(dev):
     a = mla.mla_attn_blocks(q, kn, kr, v, ad, bs, ctx, workspace=ws)
     q2 = torch.flip(q, dims=[1]).contiguous()
     b = mla.mla_attn_blocks(q2, kn, kr, v, ad, bs, ctx, workspace=ws, reuse_tile_map=True)
-    c = mla.mla_attn_blocks(q2, kn, kr, v, ad, bs, ctx)
-    a2 = mla.mla_attn_blocks(q, kn, kr, v, ad, bs, ctx)
+    # (the map-only workspace gives unsplit calls; the fresh calls match that)
+    c = mla.mla_attn_blocks(q2, kn, kr, v, ad, bs, ctx, split_keys=False)
+    a2 = mla.mla_attn_blocks(q, kn, kr, v, ad, bs, ctx, split_keys=False)
     torch.cuda.synchronize()
     assert torch.equal(b, c)
     assert torch.equal(a, a2)
@@ -151,12 +152,14 @@ def test_block_structure_training_step(dev):
     ws = mla.new_bwd_workspace(B, H, Lq, Lk, dev)
     mla.block_occupancy(_i32(anchors, dev), bs, ctx, workspace=ws)
     lse = torch.empty((B, H, Lq), dtype=torch.float32, device=dev)
-    out = mla.mla_attn(q, kn, kr, v, None, lse=lse, workspace=ws, reuse_tile_map=True)
+    # (unsplit forwards throughout: whether a call may split its key list depends
+    # on its workspace, and split and unsplit outputs differ by bf16 rounding)
+    out = mla.mla_attn(q, kn, kr, v, None, lse=lse, workspace=ws, reuse_tile_map=True, split_keys=False)
     g = mla.mla_attn_bwd(q, kn, kr, v, None, out, dout, lse, workspace=ws, reuse_tile_map=True)
     lse_d = torch.empty_like(lse)
-    out_d = mla.mla_attn(q, kn, kr, v, mask, lse=lse_d)
+    out_d = mla.mla_attn(q, kn, kr, v, mask, lse=lse_d, split_keys=False)
     g_d = mla.mla_attn_bwd(q, kn, kr, v, mask, out_d, dout, lse_d)
-    blk = mla.mla_attn_blocks(q, kn, kr, v, _i32(anchors, dev), bs, ctx)
+    blk = mla.mla_attn_blocks(q, kn, kr, v, _i32(anchors, dev), bs, ctx, split_keys=False)
     torch.cuda.synchronize()
     assert torch.equal(out, out_d) and torch.equal(out, blk) and torch.equal(lse, lse_d)
     for x, y in zip(g, g_d):
