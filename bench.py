@@ -90,6 +90,24 @@ def kernel_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+_SMI = {"handle": None, "tried": 0}
+
+
+def _smi_handle():
+    """amdsmi's handle of the first GPU, initialised once per process; an
+    initialisation that fails (seen on the first attempt in a process) is tried
+    again, a few times, on later calls."""
+    while _SMI["handle"] is None and _SMI["tried"] < 5:
+        _SMI["tried"] += 1
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            _SMI["handle"] = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception:
+            time.sleep(0.1)
+    return _SMI["handle"]
+
+
 class SclkSampler:
     """Samples the shader clock the driver reports from a thread while the GPU
     runs the warm-up and the timed steps: amdsmi's GPU metrics (the SMU's average
@@ -101,14 +119,9 @@ class SclkSampler:
         import glob
         import threading
         self.files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
-        self.smi = None
-        try:                                   # the ROCm SMI library, when present
-            import amdsmi
-            amdsmi.amdsmi_init()
-            self.smi = amdsmi.amdsmi_get_processor_handles()[0]
-            self.source = "amdsmi GFX clock during the timed steps"
-        except Exception:
-            self.source = "sysfs pp_dpm_sclk during the timed steps"
+        self.smi = _smi_handle()               # the ROCm SMI library, when present
+        self.source = ("amdsmi GFX clock during the timed steps" if self.smi is not None
+                       else "sysfs pp_dpm_sclk during the timed steps")
         self.period = period_s
         self.smi_failures = 0
         self.samples = []
