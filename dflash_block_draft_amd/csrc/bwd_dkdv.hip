@@ -333,12 +333,16 @@ bwd_dkdv(AttnBwdArgs a) {
 
     // Step i.  Entering: sp, pkP = P(i); dpp = dP(i) - D(i); fo = dO^T(i) operands.
     // e1, e2, e3: entries of chunks i+1 .. i+3.
+    // ring slot offsets of steps i .. i+2 (F, 3 slots) and i .. i+3 (T, 4 slots),
+    // rotated once per step instead of recomputed modulo the ring sizes
+    int fs0 = f_slot(0), fs1 = f_slot(1), fs2 = f_slot(2);
+    int ts0 = t_slot(0), ts1 = t_slot(1), ts2 = t_slot(2), ts3 = t_slot(3);
     for (int i = 0; i < nch; ++i) {
-      const lds_char_t* const f1 = lds + f_slot(i + 1);                 // F(i+1)
-      const lds_char_t* const t0 = lds + t_slot(i);                     // T(i)
-      const lds_char_t* const t1 = lds + t_slot(i + 1) + (kT_OT - kT_QT);   // T(i+1), dO^T
-      const uint32_t fdst = lds0 + f_slot(i + 3);                       // F(i+3) <- copies
-      const uint32_t tdst = lds0 + t_slot(i + 3);                       // T(i+3) <- copies
+      const lds_char_t* const f1 = lds + fs1;                           // F(i+1)
+      const lds_char_t* const t0 = lds + ts0;                           // T(i)
+      const lds_char_t* const t1 = lds + ts1 + (kT_OT - kT_QT);         // T(i+1), dO^T
+      const uint32_t fdst = lds0 + fs0;                                 // F(i+3) (slot of F(i)) <- copies
+      const uint32_t tdst = lds0 + ts3;                                 // T(i+3) <- copies
       const bool live3 = (e3 >> 24) != 0;
       const uint32_t q3 = q0_of(e3, i + 3);
       const int cls1 = cls_of(e1);
@@ -421,6 +425,10 @@ bwd_dkdv(AttnBwdArgs a) {
       e1 = e2;
       e2 = e3;
       e3 = __builtin_amdgcn_readfirstlane(i + 4 < nch ? e4v : 0);
+      const int fr = fs0;
+      fs0 = fs1; fs1 = fs2; fs2 = fr;
+      const int tr = ts0;
+      ts0 = ts1; ts1 = ts2; ts2 = ts3; ts3 = tr;
     }
     // The last dK / dV MFMAs (inline asm, invisible to the hazard checks) must
     // finish before the vector unit reads their accumulators: 24 wait states

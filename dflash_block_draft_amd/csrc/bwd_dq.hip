@@ -295,12 +295,16 @@ bwd_dq(AttnBwdArgs a) {
 
     // Step j.  Entering: p = P(j), dpp = dP(j) - D, fk[0..7] = K operands 0-7 of
     // S^T(j+1).  e1 .. e4: entries of steps j+1 .. j+4.
+    // ring slot offsets of steps j .. j+3 (F, 4 slots) and j .. j+2 (T, 3 slots),
+    // rotated once per step instead of recomputed modulo the ring sizes
+    int fs0 = f_slot(0), fs1 = f_slot(1), fs2 = f_slot(2), fs3 = f_slot(3);
+    int ts0 = t_slot(0), ts1 = t_slot(1), ts2 = t_slot(2);
     for (int j = 0; j < nsteps; ++j) {
-      const lds_char_t* const f1 = lds + f_slot(j + 1);                 // F(j+1)
-      const lds_char_t* const f2 = lds + f_slot(j + 2);                 // F(j+2): next step's first K operands
-      const lds_char_t* const t0 = lds + t_slot(j);                     // T(j)
-      const uint32_t fdst = lds0 + f_slot(j + 4);                       // F(j+4) <- copies
-      const uint32_t tdst = lds0 + t_slot(j + 2);                       // T(j+2) <- copies
+      const lds_char_t* const f1 = lds + fs1;                           // F(j+1)
+      const lds_char_t* const f2 = lds + fs2;                           // F(j+2): next step's first K operands
+      const lds_char_t* const t0 = lds + ts0;                           // T(j)
+      const uint32_t fdst = lds0 + fs0;                                 // F(j+4) (slot of F(j)) <- copies
+      const uint32_t tdst = lds0 + ts2;                                 // T(j+2) <- copies
       int e5v = 0;
       uint64_t word = 0;
       int hv = 0;
@@ -371,6 +375,10 @@ bwd_dq(AttnBwdArgs a) {
       e2 = e3;
       e3 = e4;
       e4 = __builtin_amdgcn_readfirstlane(j + 5 < nsteps ? e5v : 0);
+      const int fr = fs0;
+      fs0 = fs1; fs1 = fs2; fs2 = fs3; fs3 = fr;
+      const int tr = ts0;
+      ts0 = ts1; ts1 = ts2; ts2 = tr;
     }
     wait_vmem<0>();
     __syncthreads();
