@@ -169,7 +169,7 @@ bwd_dkdv(AttnBwdArgs a) {
                       : reg == kSrcLD || reg == kSrcB ? q0 * 8 : q0 * 2;
     const u32x4_t d = reg == kSrcQ ? d_q : reg == kSrcO ? d_o : reg == kSrcLD ? d_ld : reg == kSrcB ? d_b
                     : reg == kSrcQT ? d_qt : d_ot;
-    dma16<0>(d, slot_base + static_cast<uint32_t>(dst_base(w, j)), vo[j], so);
+    dma16s(d, slot_base, static_cast<uint32_t>(dst_base(w, j)), vo[j], so);
   };
 
   // ---- per-lane LDS read offsets inside a slot (bwd_plan.h)

@@ -156,7 +156,7 @@ bwd_dq(AttnBwdArgs a) {
                       : reg == kSrcBits ? kt * 1024u : key0 * 2u;
     const u32x4_t d = reg == kSrcKN ? d_kn : reg == kSrcKR ? d_kr : reg == kSrcV ? d_v : reg == kSrcBits ? d_bits
                     : reg == kSrcKTN ? d_ktn : d_ktr;
-    dma16<0>(d, slot_base + static_cast<uint32_t>(q_dst_base(w, j)), vo[j], so);
+    dma16s(d, slot_base, static_cast<uint32_t>(q_dst_base(w, j)), vo[j], so);
   };
 
   // ---- per-lane LDS read offsets inside a slot (bwd_plan.h); chunk s of K at

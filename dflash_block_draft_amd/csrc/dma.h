@@ -34,6 +34,14 @@ __device__ __forceinline__ void dma16(u32x4_t rsrc, uint32_t lds_base, uint32_t 
                   "s"(__builtin_amdgcn_readfirstlane(lds_base)), "i"(OFF) : "scc");
 }
 
+// dma16 with the LDS address given as the sum of two scalar values (a ring slot
+// and a region offset): the one add into M0 forms it.
+__device__ __forceinline__ void dma16s(u32x4_t rsrc, uint32_t lds_a, uint32_t lds_b, uint32_t voff, uint32_t soff) {
+  asm volatile("s_add_u32 m0, %3, %4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                  "s"(__builtin_amdgcn_readfirstlane(lds_a)), "s"(__builtin_amdgcn_readfirstlane(lds_b)) : "scc");
+}
+
 __device__ __forceinline__ u32x4_t buffer_desc(const void* base, uint32_t bytes) {
   const uint64_t p = reinterpret_cast<uint64_t>(base);
   u32x4_t d = {static_cast<uint32_t>(p), static_cast<uint32_t>(p >> 32) & 0xFFFFu, bytes, 0x00020000u};
