@@ -149,11 +149,9 @@ class SclkSampler:
                 self.smi_failures = 0
                 return float(info["clk"])
             except Exception:
-                # a failed read (seen right after initialisation) is retried on
-                # the next sample; amdsmi is given up only after many in a row
+                # a failed read (seen for a while after initialisation) is retried
+                # on the next sample, for as long as the sampler runs
                 self.smi_failures += 1
-                if self.smi_failures >= 50:
-                    self.smi = None
                 return None
         for path in self.files:
             try:
@@ -183,7 +181,9 @@ class SclkSampler:
 
     def summary(self):
         if not self.samples:
-            return None
+            if self.smi is None and not self.files:
+                return None
+            return {"samples": 0, "failed_reads": self.smi_failures, "source": self.source}
         s = self.samples
         return {"mean_MHz": round(sum(s) / len(s)), "min_MHz": round(min(s)), "max_MHz": round(max(s)),
                 "samples": len(s), "source": self.source}
